@@ -1,0 +1,554 @@
+"""CPU oracle for ClusterAttention's forward path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the package smoke check and the bench's CPU-baseline leg
+may import this module. The HIP product path never imports, links or calls it,
+and it shares no code, tables or constants with the HIP sources.
+
+It is a plain, slow fp64 NumPy implementation of what the method computes,
+written step by step from the paper "ClusterAttention: A training-free speedup
+of bidirectional attention" (arXiv 2608.26965; cited below as "v1" for the
+arXiv HTML of version 1 and "rev" for the later revision's text). Inputs are
+the exact values the GPU sees (bf16-rounded numbers widened to fp64).
+
+Where the paper leaves a step open, the reading taken here is stated at the
+function that implements it. Summary of those readings:
+
+* splitting variant: basic recursive splitting (PDDP) with the attention
+  metric injected into the power iteration (v1 §3.2.1 "Basic recursive
+  splitting"; v1 §6.1 notes the metric can be injected so no
+  eigendecomposition is needed);
+* the subsample of min(a d, |S|) vectors is a Bernoulli sample at rate
+  min(1, a d / |S|) decided by a 64-bit content hash of each token's raw
+  input bits (so it is deterministic, identical on CPU and GPU, and
+  independent of token order); fewer than 2 sampled rows -> the whole node;
+* principal component of the centred sample covariance; p power iterations
+  (default 8), warm start = normalise(parent estimate + unit random vector),
+  random vector = Irwin-Hall(4) normals from a splitmix64 stream;
+* split threshold at the multiple of c closest to |S|/2 (equidistant ->
+  the smaller); values equal at the threshold go left in token-id order;
+* top-k selection is exact with ties to the lower key-cluster index;
+* striped mean-compensation is per query, with the cluster's valid count as
+  weight and the original (untransformed) key and value centroids.
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+against closed forms, invariants, library routines, published generator
+outputs or brute force, except ``cluster_agreement`` (a reporting helper).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+MASK64 = (1 << 64) - 1
+GOLDEN = 0x9E3779B97F4A7C15          # splitmix64 increment (Steele, Lea, Flood 2014)
+MIX1 = 0xBF58476D1CE4E5B9            # splitmix64 finaliser multipliers
+MIX2 = 0x94D049BB133111EB
+
+DOMAIN_SAMPLE = 0x53   # salt domains of the two random draws of the method
+DOMAIN_WARM = 0x57
+
+TENSOR_Q = 0
+TENSOR_K = 1
+
+
+# ---------------------------------------------------------------------------
+# Counter-based random numbers: splitmix64 (Steele, Lea & Flood, "Fast
+# splittable pseudorandom number generators", OOPSLA 2014).
+# ---------------------------------------------------------------------------
+
+def fmix64(z):
+    """splitmix64 output finaliser on Python ints or uint64 numpy arrays."""
+    if isinstance(z, (int, np.integer)) and not isinstance(z, np.ndarray):
+        z = int(z) & MASK64
+        z = ((z ^ (z >> 30)) * MIX1) & MASK64
+        z = ((z ^ (z >> 27)) * MIX2) & MASK64
+        return z ^ (z >> 31)
+    z = np.asarray(z, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(MIX1)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(MIX2)
+        return z ^ (z >> np.uint64(31))
+
+
+def splitmix64_stream(seed: int, count: int) -> list[int]:
+    """The first ``count`` outputs of splitmix64 seeded with ``seed``."""
+    out, s = [], seed & MASK64
+    for _ in range(count):
+        s = (s + GOLDEN) & MASK64
+        out.append(fmix64(s))
+    return out
+
+
+def chain(*vals: int) -> int:
+    """Fold small integers into one 64-bit key: z <- fmix64((z ^ v) + golden)."""
+    z = 0
+    for v in vals:
+        z = fmix64(((z ^ (int(v) & MASK64)) + GOLDEN) & MASK64)
+    return z
+
+
+def row_hash(words: np.ndarray) -> np.ndarray:
+    """64-bit content hash of each row of 32-bit words, shape [N, W] -> [N].
+
+    h = fmix64( sum_j fmix64((j << 32 | w_j) + golden)  mod 2^64 ).
+    """
+    words = np.asarray(words, dtype=np.uint64)
+    j = np.arange(words.shape[1], dtype=np.uint64)[None, :]
+    with np.errstate(over="ignore"):
+        per = fmix64(((j << np.uint64(32)) | words) + np.uint64(GOLDEN))
+        s = per.sum(axis=1, dtype=np.uint64)
+    return fmix64(s)
+
+
+def row_words(X: np.ndarray, dtype: str) -> np.ndarray:
+    """The raw 32-bit words of each token row as stored on the device.
+
+    bf16 rows: word j packs elements 2j (low half) and 2j+1 (high half);
+    fp32 rows: word j is the bit pattern of element j.
+    """
+    X32 = np.ascontiguousarray(X, dtype=np.float32)
+    u = X32.view(np.uint32)
+    if dtype == "f32":
+        return u.astype(np.uint64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    if np.any(u & np.uint32(0xFFFF)):
+        raise ValueError("values are not exact bfloat16")
+    b = (u >> np.uint32(16)).astype(np.uint64)
+    return b[:, 0::2] | (b[:, 1::2] << np.uint64(16))
+
+
+def warm_vector(seed: int, head: int, tensor: int, level: int, node: int, d: int) -> np.ndarray:
+    """Random normal-like vector for the power-iteration warm start.
+
+    Component j takes the (j+1)-th output of a splitmix64 stream keyed by
+    (seed, head, tensor, level, node); its four 16-bit fields f_0..f_3 give an
+    Irwin-Hall(4) variate sum_k (f_k + 1/2)/65536 - 2 (mean 0, variance 1/3;
+    the scale is irrelevant because the vector is normalised).
+    """
+    base = chain(seed, DOMAIN_WARM, head, tensor, level, node)
+    r = np.empty(d, np.float64)
+    for j, z in enumerate(splitmix64_stream(base, d)):
+        s = 0.0
+        for k in range(4):
+            s += (((z >> (16 * k)) & 0xFFFF) + 0.5) / 65536.0
+        r[j] = s - 2.0
+    return r
+
+
+# ---------------------------------------------------------------------------
+# Tree layout (v1 §3.1 and §3.2.1; rev §4.1.1)
+# ---------------------------------------------------------------------------
+
+def split_size(n: int, c: int) -> int:
+    """Left-child size of a node with n > c members.
+
+    The split leaves the multiple of c closest to n/2 below the threshold
+    (v1 §3.2.1): t = j c with j >= 1 and t < n; when two multiples are equally
+    close (n an odd multiple of c) the smaller one is taken.
+    """
+    if n <= c:
+        raise ValueError("a node of size <= c is a leaf")
+    best = None
+    for j in range(1, (n - 1) // c + 1):
+        t = j * c
+        if best is None or abs(2 * t - n) < abs(2 * best - n):
+            best = t
+    return best
+
+
+@dataclass
+class Node:
+    level: int
+    index: int      # position of the node among the 2^level slots of its level
+    off: int
+    n: int
+
+
+def tree_levels(N: int, c: int) -> list[list[Node]]:
+    """Nodes of the recursive split, grouped by depth.
+
+    The layout depends only on N and c. A node with n > c members splits into
+    [off, off+t) and [off+t, off+n), t = split_size(n, c); nodes with n <= c are
+    leaves (v1 §3.1: at most one cluster differs from c, the one that absorbs
+    the remainder). Children of slot j are slots 2j and 2j+1.
+    """
+    levels: list[list[Node]] = []
+    cur = [Node(0, 0, 0, N)]
+    while cur:
+        levels.append(cur)
+        nxt = []
+        for nd in cur:
+            if nd.n > c:
+                t = split_size(nd.n, c)
+                nxt.append(Node(nd.level + 1, 2 * nd.index, nd.off, t))
+                nxt.append(Node(nd.level + 1, 2 * nd.index + 1, nd.off + t, nd.n - t))
+        cur = nxt
+    return levels
+
+
+def leaf_sizes(N: int, c: int) -> list[int]:
+    """Cluster sizes in leaf order (left first)."""
+    out = []
+
+    def rec(n):
+        if n <= c:
+            out.append(n)
+            return
+        t = split_size(n, c)
+        rec(t)
+        rec(n - t)
+    rec(N)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Transforms (v1 §3.2.2, Eq. 12-16; App. B Eq. 37-47; App. C Eq. 48-49)
+# ---------------------------------------------------------------------------
+
+def metric_matrices(Q: np.ndarray, K: np.ndarray):
+    """M_q = Q^T Q / n (Eq. 12), key mean, M_k = K_c^T K_c / n (Eq. 15)."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    n = Q.shape[0]
+    Mq = Q.T @ Q / n
+    kbar = K.mean(axis=0)
+    Kc = K - kbar
+    Mk = Kc.T @ Kc / K.shape[0]
+    return Mq, Mk, kbar
+
+
+def root_matrix(M: np.ndarray) -> np.ndarray:
+    """Symmetric PSD root of a metric matrix via eigendecomposition, negative
+    eigenvalues clamped to zero (v1 §3.2.2 "Key clustering")."""
+    w, V = np.linalg.eigh(M)
+    w = np.clip(w, 0.0, None)
+    return (V * np.sqrt(w)) @ V.T
+
+
+def query_normalisers(Q: np.ndarray, G: np.ndarray) -> np.ndarray:
+    """s_i = (q_i^T G q_i)^{-1/2}, so that s_i q_i represents R q / |R q| with
+    R^T R = G (Eq. 16 / Eq. 47). A query with q^T G q <= 0 gets s_i = 0."""
+    Q = np.asarray(Q, np.float64)
+    v = np.einsum("ij,jk,ik->i", Q, G, Q)
+    s = np.zeros_like(v)
+    pos = v > 0
+    s[pos] = 1.0 / np.sqrt(v[pos])
+    return s
+
+
+# ---------------------------------------------------------------------------
+# Recursive splitting (v1 §3.2.1 "Basic recursive splitting"; rev §4.1.1)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class ClusterOpts:
+    transform: bool = True          # attention-aware metrics (v1 §3.2.2)
+    query_normalize: bool = True    # top-k query representation (Eq. 16)
+    power_iters: int = 8            # p
+    sample_factor: int = 1          # a
+    seed: int = 0
+
+
+def sample_threshold(n: int, d: int, a: int) -> int:
+    """Integer acceptance threshold floor(2^32 min(1, a d / n))."""
+    if a * d >= n:
+        return 1 << 32
+    return ((a * d) << 32) // n
+
+
+def sample_members(members: np.ndarray, hashes: np.ndarray, level: int, tensor: int,
+                   d: int, a: int, seed: int) -> np.ndarray:
+    """The node's subsample (reading: Bernoulli at rate min(1, a d / n) on a
+    content hash; fewer than two rows -> the whole node)."""
+    n = members.shape[0]
+    thr = sample_threshold(n, d, a)
+    salt = chain(seed, DOMAIN_SAMPLE, tensor, level)
+    top = fmix64(hashes[members] ^ np.uint64(salt)) >> np.uint64(32)
+    T = members[top.astype(np.uint64) < np.uint64(thr)] if thr < (1 << 32) else members
+    if T.shape[0] < 2:
+        T = members
+    return T
+
+
+def principal_direction(Xs: np.ndarray, M: np.ndarray, u0: np.ndarray, p: int) -> np.ndarray:
+    """p power iterations u <- M C u / |M C u| from u0, C the centred sample
+    covariance. With M = R^T R this is the power iteration on R C R^T written
+    for u = R^T v, so u . x = v . (R x): the metric is injected and no root
+    matrix is formed. If an iterate vanishes the warm start is kept."""
+    Xs = np.asarray(Xs, np.float64)
+    xbar = Xs.mean(axis=0)
+    Xc = Xs - xbar
+    C = Xc.T @ Xc / Xs.shape[0]
+    u = u0.copy()
+    for _ in range(p):
+        w = M @ (C @ u)
+        nrm = math.sqrt(float(w @ w))
+        if nrm == 0.0:
+            return u0.copy()
+        u = w / nrm
+    return u
+
+
+def split_by_scores(members: np.ndarray, scores: np.ndarray, t: int):
+    """Members ordered by (score, token id); the first t go left. Both halves
+    keep the node's order (ascending token id). Scores that compare equal
+    (including -0.0 and +0.0) are ordered by token id."""
+    scores = np.asarray(scores, np.float64) + 0.0   # -0.0 -> +0.0
+    order = np.lexsort((members, scores))
+    left_pos = np.sort(order[:t])
+    mask = np.zeros(members.shape[0], bool)
+    mask[left_pos] = True
+    return members[mask], members[~mask]
+
+
+@dataclass
+class TreeTrace:
+    """Per-level state of one clustering tree (for stage-isolated checks)."""
+    perms: list = field(default_factory=list)    # perm before level l (and final)
+    scores: list = field(default_factory=list)   # projection per position at level l
+    dirs: dict = field(default_factory=dict)     # (level, index) -> u
+
+
+def cluster_tree(X: np.ndarray, M: np.ndarray, hashes: np.ndarray, c: int, opts: ClusterOpts,
+                 head: int, tensor: int, trace: TreeTrace | None = None) -> np.ndarray:
+    """Recursive PDDP splitting of the rows of X under geometry M.
+
+    Returns perm with perm[p] = token at cluster-major position p; cluster j
+    occupies [j c, j c + n_j). At each node: subsample, centred covariance,
+    warm-started power iteration with the metric injected, projection of all
+    members, split at the multiple of c closest to half.
+    """
+    X = np.asarray(X, np.float64)
+    N, d = X.shape
+    perm = np.arange(N, dtype=np.int64)
+    parent_dir: dict = {}
+    for level, nodes in enumerate(tree_levels(N, c)):
+        if not any(nd.n > c for nd in nodes):
+            break
+        new = perm.copy()
+        sc = np.full(N, np.nan)
+        for nd in nodes:
+            if nd.n <= c:
+                continue
+            members = perm[nd.off:nd.off + nd.n]
+            T = sample_members(members, hashes, level, tensor, d, opts.sample_factor, opts.seed)
+            r = warm_vector(opts.seed, head, tensor, level, nd.index, d)
+            r = r / np.linalg.norm(r)
+            par = parent_dir.get((level - 1, nd.index // 2))
+            if par is None:
+                u0 = r
+            else:
+                s = par + r
+                ns = np.linalg.norm(s)
+                u0 = s / ns if ns > 0 else r
+            u = principal_direction(X[T], M, u0, opts.power_iters)
+            parent_dir[(level, nd.index)] = u
+            scores = X[members] @ u
+            sc[nd.off:nd.off + nd.n] = scores
+            t = split_size(nd.n, c)
+            left, right = split_by_scores(members, scores, t)
+            new[nd.off:nd.off + t] = left
+            new[nd.off + t:nd.off + nd.n] = right
+        if trace is not None:
+            trace.perms.append(perm.copy())
+            trace.scores.append(sc)
+        perm = new
+    if trace is not None:
+        trace.perms.append(perm.copy())
+        trace.dirs = parent_dir
+    return perm
+
+
+def head_representations(Q: np.ndarray, K: np.ndarray, opts: ClusterOpts):
+    """Vectors and geometry to split for one head.
+
+    Keys: x = k under M_q (Eq. 11-14). Queries: x = s q under M_k with
+    s = (q^T M_k q)^{-1/2} (Eq. 15-16, Eq. 47). Without the transform both
+    geometries are the identity.
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    d = Q.shape[1]
+    if opts.transform:
+        Mq, Mk, _ = metric_matrices(Q, K)
+    else:
+        Mq = Mk = np.eye(d)
+    s = query_normalisers(Q, Mk) if opts.query_normalize else np.ones(Q.shape[0])
+    return s[:, None] * Q, Mk, K, Mq
+
+
+def cluster(Q: np.ndarray, K: np.ndarray, c: int, opts: ClusterOpts | None = None,
+            dtype: str = "bf16", traces: dict | None = None):
+    """Cluster queries and keys of every (batch, head) separately (v1 §3.1).
+
+    Q, K: [B, H, N, D]. Returns perm_q, perm_k of shape [B, H, N] (int64).
+    The flattened head index b*H + h keys the random draws.
+    """
+    opts = opts or ClusterOpts()
+    B, H, N, D = Q.shape
+    pq = np.empty((B, H, N), np.int64)
+    pk = np.empty((B, H, N), np.int64)
+    for b in range(B):
+        for h in range(H):
+            head = b * H + h
+            Xq, Gq, Xk, Gk = head_representations(Q[b, h], K[b, h], opts)
+            hq = row_hash(row_words(Q[b, h], dtype))
+            hk = row_hash(row_words(K[b, h], dtype))
+            tq = TreeTrace() if traces is not None else None
+            tk = TreeTrace() if traces is not None else None
+            pq[b, h] = cluster_tree(Xq, Gq, hq, c, opts, head, TENSOR_Q, tq)
+            pk[b, h] = cluster_tree(Xk, Gk, hk, c, opts, head, TENSOR_K, tk)
+            if traces is not None:
+                traces[(b, h, TENSOR_Q)] = tq
+                traces[(b, h, TENSOR_K)] = tk
+    return pq, pk
+
+
+# ---------------------------------------------------------------------------
+# Centroids and assignment (v1 §3.3, Eq. 18-20; rev §4.2)
+# ---------------------------------------------------------------------------
+
+def centroids(X: np.ndarray, perm: np.ndarray, c: int):
+    """Means of the original vectors over each cluster's valid members, and
+    the member counts. X: [N, D], perm: [N]. Returns ([n_c, D], [n_c])."""
+    X = np.asarray(X, np.float64)
+    sizes = leaf_sizes(X.shape[0], c)
+    cent = np.empty((len(sizes), X.shape[1]))
+    for j, nj in enumerate(sizes):
+        cent[j] = X[perm[j * c:j * c + nj]].mean(axis=0)
+    return cent, np.asarray(sizes, np.int64)
+
+
+def cluster_scores(cq: np.ndarray, ck: np.ndarray) -> np.ndarray:
+    """A[a, j] = qbar_a . kbar_j: the mean logit between the clusters (Eq. 18;
+    the 1/sqrt(d) temperature does not change the ranking)."""
+    return np.asarray(cq, np.float64) @ np.asarray(ck, np.float64).T
+
+
+def topk_row(scores: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores, ties to the lower index, ascending."""
+    scores = np.asarray(scores, np.float64) + 0.0
+    idx = np.arange(scores.shape[0])
+    order = np.lexsort((idx, -scores))
+    return np.sort(order[:k])
+
+
+def route(cq: np.ndarray, ck: np.ndarray, k: int, scores: np.ndarray | None = None) -> np.ndarray:
+    """Top-k key clusters per query cluster (v1 §3.3.2). cq: [n_qc, D],
+    ck: [n_kc, D] (or a given score matrix). Returns [n_qc, k] ascending."""
+    A = cluster_scores(cq, ck) if scores is None else np.asarray(scores, np.float64)
+    return np.stack([topk_row(A[a], k) for a in range(A.shape[0])])
+
+
+# ---------------------------------------------------------------------------
+# Attention (v1 §1.2 Eq. 1-2; App. A Eq. 21-22)
+# ---------------------------------------------------------------------------
+
+def _softmax_combine(logits: np.ndarray, values: np.ndarray):
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    l = e.sum(axis=1, keepdims=True)
+    o = (e @ values) / l
+    return o, (m + np.log(l))[:, 0]
+
+
+def dense_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float | None = None):
+    """o_i = sum_j softmax_j(tau q_i . k_j) v_j and LSE_i = log sum_j exp(.)
+    for one head (Eq. 1). Q, K, V: [N, D]."""
+    Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
+    tau = 1.0 / math.sqrt(Q.shape[1]) if not scale else float(scale)
+    return _softmax_combine(tau * (Q @ K.T), V)
+
+
+def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
+                     scale: float | None = None):
+    """Block-sparse attention of one head with optional striped
+    mean-compensation.
+
+    Query i of cluster a attends with token resolution to every key of the
+    selected clusters Sel(a) (Eq. 2). With compensation, every excluded key
+    cluster enters once through its centroid: logit tau q_i . kbar_c +
+    ln|c| and value vbar_c, which is Eq. 21-22 (the centroid weight w_c
+    counted |c| times). Returns O in original token order and LSE.
+    """
+    Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
+    N, D = Q.shape
+    tau = 1.0 / math.sqrt(D) if not scale else float(scale)
+    qs = leaf_sizes(N, c)
+    ks = leaf_sizes(K.shape[0], c)
+    kbar, cnt = centroids(K, perm_k, c)
+    vbar, _ = centroids(V, perm_k, c)
+    O = np.empty((N, V.shape[1]))
+    L = np.empty(N)
+    for a, na in enumerate(qs):
+        qi = perm_q[a * c:a * c + na]
+        sel = np.asarray(blocks[a], np.int64)
+        keys = np.concatenate([perm_k[j * c:j * c + ks[j]] for j in sel])
+        logits = tau * (Q[qi] @ K[keys].T)
+        vals = V[keys]
+        if compensate:
+            mask = np.ones(len(ks), bool)
+            mask[sel] = False
+            ex = np.nonzero(mask)[0]
+            if ex.size:
+                cl = tau * (Q[qi] @ kbar[ex].T) + np.log(cnt[ex].astype(np.float64))[None, :]
+                logits = np.concatenate([logits, cl], axis=1)
+                vals = np.concatenate([vals, vbar[ex]], axis=0)
+        o, lse = _softmax_combine(logits, vals)
+        O[qi] = o
+        L[qi] = lse
+    return O, L
+
+
+def attend(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool, scale=None):
+    """sparse_attention over every (batch, head): Q,K,V [B,H,N,D]."""
+    B, H, N, D = Q.shape
+    O = np.empty((B, H, N, V.shape[-1]))
+    L = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            O[b, h], L[b, h] = sparse_attention(Q[b, h], K[b, h], V[b, h], perm_q[b, h],
+                                                perm_k[b, h], c, blocks[b, h], compensate, scale)
+    return O, L
+
+
+def dense(Q, K, V, scale=None):
+    """dense_attention over every (batch, head)."""
+    B, H, N, D = Q.shape
+    O = np.empty((B, H, N, V.shape[-1]))
+    L = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            O[b, h], L[b, h] = dense_attention(Q[b, h], K[b, h], V[b, h], scale)
+    return O, L
+
+
+def forward(Q, K, V, c: int, topk: int, compensate: bool = True, opts: ClusterOpts | None = None,
+            dtype: str = "bf16", scale=None):
+    """The whole path: cluster -> centroids -> route -> attend (v1 §1.1)."""
+    pq, pk = cluster(Q, K, c, opts, dtype)
+    B, H, N, D = Q.shape
+    blocks = np.empty((B, H, len(leaf_sizes(N, c)), topk), np.int64)
+    for b in range(B):
+        for h in range(H):
+            cq, _ = centroids(Q[b, h], pq[b, h], c)
+            ck, _ = centroids(K[b, h], pk[b, h], c)
+            blocks[b, h] = route(cq, ck, topk)
+    O, L = attend(Q, K, V, pq, pk, c, blocks, compensate, scale)
+    return O, L, pq, pk, blocks
+
+
+# ---------------------------------------------------------------------------
+# Reporting helper
+# ---------------------------------------------------------------------------
+
+def cluster_agreement(perm_a: np.ndarray, perm_b: np.ndarray, c: int) -> float:
+    """Fraction of tokens whose cluster id is the same under two perms."""
+    N = perm_a.shape[-1]
+    ida = np.empty(N, np.int64); idb = np.empty(N, np.int64)
+    ida[perm_a] = np.arange(N) // c
+    idb[perm_b] = np.arange(N) // c
+    return float(np.mean(ida == idb))

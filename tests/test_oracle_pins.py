@@ -1,0 +1,631 @@
+"""Pins of the CPU oracle against what the paper and mathematics fix.
+
+Each ``check_*`` function raises AssertionError when the oracle disagrees with
+an identity, invariant, library routine, brute force or published value; the
+tests call them on the oracle as written, and ``test_planted_mistakes`` plants
+plausible mistakes into the oracle (on the CPU) and requires a pin to fail.
+Paper: "ClusterAttention: A training-free speedup of bidirectional attention"
+(arXiv 2608.26965 v1).
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle.clusterattn as o
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _random_head(seed, N=256, D=16, scale=1.0):
+    r = _rng(seed)
+    Q = r.standard_normal((N, D)) * scale
+    K = r.standard_normal((N, D)) * scale + 0.3 * r.standard_normal(D)
+    V = r.standard_normal((N, D))
+    return Q, K, V
+
+
+def _dense_weights(Q, K, tau):
+    return scipy.special.softmax(tau * (Q @ K.T), axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Random numbers and hashing (build-defined draws; published generator)
+# ---------------------------------------------------------------------------
+
+def check_splitmix64_published():
+    vals = [int(l, 16) for l in open(os.path.join(GOLDEN, "splitmix64_seed0.txt"))
+            if l.strip() and not l.startswith("#")]
+    got = o.splitmix64_stream(0, len(vals))
+    assert got == vals, (got, vals)
+    arr = o.fmix64(np.array([0x9E3779B97F4A7C15 * (i + 1) & o.MASK64 for i in range(3)],
+                            dtype=np.uint64))
+    assert [int(x) for x in arr] == vals
+
+
+def test_splitmix64_published_outputs():
+    check_splitmix64_published()
+
+
+def test_row_words_match_device_layout():
+    import torch
+    r = _rng(1)
+    X = r.standard_normal((5, 8)).astype(np.float32)
+    Xb = torch.from_numpy(X).to(torch.bfloat16)
+    dev_words = Xb.contiguous().view(torch.int32).numpy().astype(np.uint32)
+    got = o.row_words(Xb.float().numpy(), "bf16").astype(np.uint32)
+    assert np.array_equal(got, dev_words)
+    got32 = o.row_words(X, "f32").astype(np.uint32)
+    assert np.array_equal(got32, X.view(np.uint32))
+
+
+def test_row_hash_properties():
+    r = _rng(2)
+    W = r.integers(0, 2**32, size=(50, 32), dtype=np.uint64)
+    h = o.row_hash(W)
+    assert len(set(h.tolist())) == 50
+    W2 = W.copy()
+    W2[:, [3, 4]] = W2[:, [4, 3]]          # the hash depends on word position
+    assert np.all(o.row_hash(W2) != h)
+    assert np.array_equal(o.row_hash(W[[7, 7, 3]]), h[[7, 7, 3]])
+    # scalar and vector finalisers agree
+    for z in W[:5, 0]:
+        assert o.fmix64(int(z)) == int(o.fmix64(np.array([z], np.uint64))[0])
+
+
+def test_warm_vector_statistics():
+    vals = np.concatenate([o.warm_vector(5, h, t, l, n, 64)
+                           for h in range(4) for t in range(2) for l in range(3) for n in range(4)])
+    assert abs(vals.mean()) < 0.02
+    assert abs(vals.var() - 1.0 / 3.0) < 0.02
+    assert np.all(np.abs(vals) <= 2.0)
+    a = o.warm_vector(5, 0, 0, 1, 0, 64)
+    b = o.warm_vector(5, 0, 0, 1, 1, 64)
+    assert not np.array_equal(a, b)
+    assert np.array_equal(a, o.warm_vector(5, 0, 0, 1, 0, 64))
+
+
+# ---------------------------------------------------------------------------
+# Tree layout (v1 §3.1, §3.2.1)
+# ---------------------------------------------------------------------------
+
+def check_tree_layout():
+    lines = [l.split() for l in open(os.path.join(GOLDEN, "tree_video_32760_c128.txt"))
+             if l.strip() and not l.startswith("#")]
+    spine = [int(x) for x in lines[0]]
+    ncl, last, nlev = (int(x) for x in lines[1])
+    levels = o.tree_levels(32760, 128)
+    got_spine = [lv[-1].n for lv in levels]
+    assert got_spine == spine, got_spine
+    sizes = o.leaf_sizes(32760, 128)
+    assert len(sizes) == ncl and sizes[-1] == last and all(s == 128 for s in sizes[:-1])
+    assert sum(1 for lv in levels if any(nd.n > 128 for nd in lv)) == nlev
+    for N, c in [(1024, 64), (65536, 128), (262144, 256), (1000, 64), (3 * 64, 64),
+                 (5 * 128, 128), (7 * 64 + 1, 64), (130, 64), (65, 64), (64, 64), (17, 1)]:
+        sizes = o.leaf_sizes(N, c)
+        assert sum(sizes) == N
+        assert len(sizes) == -(-N // c)
+        assert all(s == c for s in sizes[:-1]) and 0 < sizes[-1] <= c
+        for lv in o.tree_levels(N, c):
+            for nd in lv:
+                if nd.n > c:
+                    t = o.split_size(nd.n, c)
+                    cands = [j * c for j in range(1, nd.n) if j * c < nd.n]
+                    best = min(abs(x - nd.n / 2) for x in cands)
+                    ok = [x for x in cands if abs(x - nd.n / 2) == best]
+                    assert t == min(ok), (nd.n, c, t, ok)
+
+
+def test_tree_layout():
+    check_tree_layout()
+
+
+# ---------------------------------------------------------------------------
+# Transforms (v1 §3.2.2, App. B, App. C)
+# ---------------------------------------------------------------------------
+
+def check_metrics():
+    r = _rng(3)
+    n, d = 11, 4
+    Q = r.standard_normal((n, d))
+    K = r.standard_normal((n, d)) + 2.0
+    Mq, Mk, kbar = o.metric_matrices(Q, K)
+    # Eq. 10-11: (k1-k2)^T M (k1-k2) is the mean squared logit difference.
+    for a, b in [(0, 1), (2, 5), (7, 3)]:
+        dk = K[a] - K[b]
+        assert math.isclose(dk @ Mq @ dk, np.sum((Q @ K[a] - Q @ K[b]) ** 2) / n, rel_tol=1e-12)
+    # Eq. 43-46: D^T D over all ordered key pairs = 2 n K_c^T K_c = 2 n^2 M_k.
+    D = np.array([K[a] - K[b] for a in range(n) for b in range(n)])
+    assert np.allclose(D.T @ D, 2 * n * n * Mk, rtol=1e-12, atol=1e-10)
+    assert np.allclose(kbar, [np.mean(K[:, j]) for j in range(d)])
+    # Eq. 39: the entries of K_c q sum to zero for every q.
+    q = r.standard_normal(d)
+    assert abs(np.sum((K - kbar) @ q)) < 1e-10
+
+
+def test_metrics_closed_forms():
+    check_metrics()
+
+
+def test_query_representation_shift_invariance():
+    # Eq. 36-38: shifts delta with K delta = const * 1 leave the representation.
+    r = _rng(4)
+    n, d = 40, 5
+    e = np.zeros(d); e[2] = 1.0
+    K = r.standard_normal((n, d)); K[:, 2] = 1.5            # zero variance along e
+    Q = r.standard_normal((n, d))
+    Mq, Mk, _ = o.metric_matrices(Q, K)
+    assert np.allclose(Mk @ e, 0, atol=1e-12)
+    s1 = o.query_normalisers(Q, Mk)
+    s2 = o.query_normalisers(Q + 0.7 * e, Mk)
+    assert np.allclose(s1, s2, rtol=1e-12)
+
+
+def check_query_normalisers():
+    # Eq. 16/47: s q represents R_k q / |R_k q|, so |R_k (s q)| = 1.
+    r = _rng(5)
+    Q = r.standard_normal((30, 6))
+    K = r.standard_normal((30, 6)) @ np.diag([3, 1, 1, 0.5, 0.1, 0.0]) + 1.0
+    _, Mk, _ = o.metric_matrices(Q, K)
+    R = o.root_matrix(Mk)
+    assert np.allclose(R.T @ R, Mk, atol=1e-12)
+    s = o.query_normalisers(Q, Mk)
+    assert np.allclose(np.linalg.norm((s[:, None] * Q) @ R.T, axis=1), 1.0, rtol=1e-10)
+    assert np.all(o.query_normalisers(np.zeros((2, 6)), Mk) == 0.0)
+
+
+def test_query_normalisers():
+    check_query_normalisers()
+
+
+# ---------------------------------------------------------------------------
+# Principal direction with the metric injected (v1 §3.2.1, §3.2.2, §6.1)
+# ---------------------------------------------------------------------------
+
+def check_power_iteration_matches_eigh():
+    r = _rng(6)
+    d = 6
+    A = r.standard_normal((d, d))
+    M = A @ np.diag([4, 2, 1, 0.5, 0.2, 0.0]) @ A.T          # PSD, rank deficient
+    X = r.standard_normal((80, d)) @ np.diag([3, 2, 1.5, 1, 0.5, 0.2]) @ r.standard_normal((d, d))
+    R = o.root_matrix(M)
+    Y = X @ R.T                                              # explicit transform R x
+    Yc = Y - Y.mean(0)
+    w, Vv = np.linalg.eigh(Yc.T @ Yc / len(Y))
+    assert w[-1] - w[-2] > 1e-3
+    vstar = Vv[:, -1]
+    u0 = r.standard_normal(d); u0 /= np.linalg.norm(u0)
+    u = o.principal_direction(X, M, u0, 200)
+    target = R.T @ vstar
+    cos = abs(u @ target) / np.linalg.norm(u) / np.linalg.norm(target)
+    assert cos >= 1 - 1e-9, cos
+    # the same split as PDDP run explicitly on R x
+    sgn = np.sign(u @ target)
+    members = np.arange(len(X))
+    l1, _ = o.split_by_scores(members, X @ u, 40)
+    l2, _ = o.split_by_scores(members, sgn * (Y @ vstar), 40)
+    assert np.array_equal(l1, l2)
+
+
+def test_power_iteration_matches_eigh():
+    check_power_iteration_matches_eigh()
+
+
+def test_power_iteration_zero_covariance_keeps_warm_start():
+    u0 = np.ones(4) / 2.0
+    X = np.tile(np.arange(4.0), (10, 1))
+    assert np.array_equal(o.principal_direction(X, np.eye(4), u0, 8), u0)
+
+
+# ---------------------------------------------------------------------------
+# Split and sampling (v1 §3.2.1; rev §4.1.1)
+# ---------------------------------------------------------------------------
+
+def check_split_by_scores_bruteforce():
+    r = _rng(7)
+    for trial in range(200):
+        n = int(r.integers(2, 12))
+        members = np.sort(r.choice(1000, n, replace=False))
+        scores = r.integers(0, 4, n).astype(np.float64)     # many exact ties
+        if trial % 3 == 0:
+            scores = np.where(scores == 0, -0.0, scores)
+        t = int(r.integers(1, n))
+        left, right = o.split_by_scores(members, scores, t)
+        assert len(left) == t and len(right) == n - t
+        assert np.all(np.diff(left) > 0) and np.all(np.diff(right) > 0)
+        sc = dict(zip(members.tolist(), (scores + 0.0).tolist()))
+        for a in left:
+            for b in right:
+                assert (sc[a], a) < (sc[b], b)
+
+
+def test_split_by_scores_bruteforce():
+    check_split_by_scores_bruteforce()
+
+
+def test_cluster_tree_tiny_bruteforce():
+    # Every node of a tiny tree (c = 1 and 2) splits its members exactly at
+    # the (score, id) order statistic, and the result is a bijection.
+    r = _rng(8)
+    for c in (1, 2):
+        for N in (5, 9, 16):
+            X = r.standard_normal((N, 3))
+            hashes = o.row_hash(o.row_words(X.astype(np.float32), "f32"))
+            tr = o.TreeTrace()
+            perm = o.cluster_tree(X, np.eye(3), hashes, c, o.ClusterOpts(seed=3), 0, 1, tr)
+            assert sorted(perm.tolist()) == list(range(N))
+            for lvl, nodes in enumerate(o.tree_levels(N, c)[:len(tr.scores)]):
+                before, after, sc = tr.perms[lvl], tr.perms[lvl + 1], tr.scores[lvl]
+                for nd in nodes:
+                    if nd.n <= c:
+                        continue
+                    mem = before[nd.off:nd.off + nd.n]
+                    s = sc[nd.off:nd.off + nd.n]
+                    t = o.split_size(nd.n, c)
+                    order = sorted(zip(s.tolist(), mem.tolist()))
+                    want_left = sorted(m for _, m in order[:t])
+                    assert after[nd.off:nd.off + t].tolist() == want_left
+                    assert sorted(after[nd.off + t:nd.off + nd.n].tolist()) == \
+                        sorted(m for _, m in order[t:])
+
+
+def test_sample_members_properties():
+    r = _rng(9)
+    N, d = 20000, 64
+    W = r.integers(0, 2**32, size=(N, 8), dtype=np.uint64)
+    hashes = o.row_hash(W)
+    members = np.arange(N)
+    counts = []
+    for level in range(40):
+        T = o.sample_members(members, hashes, level, 1, d, 1, 11)
+        assert np.all(np.isin(T, members))
+        counts.append(len(T))
+    assert abs(np.mean(counts) - d) < 3 * math.sqrt(d / 40) + 1
+    # independent of the order of the members
+    T = o.sample_members(members, hashes, 3, 0, d, 1, 11)
+    T2 = o.sample_members(members[::-1].copy(), hashes, 3, 0, d, 1, 11)
+    assert np.array_equal(np.sort(T), np.sort(T2))
+    # whole node when a d >= n, and duplicates are sampled all-or-none
+    assert np.array_equal(o.sample_members(members[:50], hashes, 0, 0, d, 1, 11), members[:50])
+    dup = np.repeat(hashes[:400], 5)
+    T = o.sample_members(np.arange(2000), dup, 2, 0, d, 1, 11)
+    groups = np.bincount(T // 5, minlength=400)
+    assert set(groups.tolist()) <= {0, 5}
+
+
+# ---------------------------------------------------------------------------
+# Assignment (v1 §3.3, Eq. 18-19)
+# ---------------------------------------------------------------------------
+
+def check_centroid_scores():
+    r = _rng(10)
+    N, D, c = 200, 8, 32
+    Q = r.standard_normal((N, D)); K = r.standard_normal((N, D))
+    pq = r.permutation(N); pk = r.permutation(N)
+    cq, nq = o.centroids(Q, pq, c)
+    ck, nk = o.centroids(K, pk, c)
+    assert nq.tolist() == [32] * 6 + [8]
+    A = o.cluster_scores(cq, ck)
+    for a in range(len(nq)):
+        qa = Q[pq[a * c:a * c + nq[a]]]
+        for j in range(len(nk)):
+            kj = K[pk[j * c:j * c + nk[j]]]
+            # Eq. 18: the centroid product is the mean pairwise logit
+            assert math.isclose(A[a, j], np.mean(qa @ kj.T), rel_tol=1e-10, abs_tol=1e-12)
+            # Eq. 19: Jensen, the mean of exp is at least exp of the mean
+            tau = 1 / math.sqrt(D)
+            assert np.mean(np.exp(tau * qa @ kj.T)) >= math.exp(tau * A[a, j]) * (1 - 1e-12)
+
+
+def test_centroid_scores():
+    check_centroid_scores()
+
+
+def check_topk_bruteforce():
+    r = _rng(11)
+    for _ in range(300):
+        n = int(r.integers(1, 12))
+        k = int(r.integers(1, n + 1))
+        s = r.integers(-3, 3, n).astype(np.float64)
+        got = o.topk_row(s, k)
+        best = max(itertools.combinations(range(n), k),
+                   key=lambda sub: (sum(s[list(sub)]), tuple(-x for x in sub)))
+        assert tuple(got.tolist()) == best, (s, k, got, best)
+
+
+def test_topk_bruteforce():
+    check_topk_bruteforce()
+
+
+# ---------------------------------------------------------------------------
+# Attention (v1 §1.2 Eq. 1-6; App. A Eq. 21-33)
+# ---------------------------------------------------------------------------
+
+def check_dense_against_libraries():
+    import torch
+    Q, K, V = _random_head(12, N=96, D=16)
+    O, L = o.dense_attention(Q, K, V)
+    tau = 1 / 4.0
+    W = _dense_weights(Q, K, tau)
+    assert np.allclose(O, W @ V, rtol=1e-12, atol=1e-13)
+    assert np.allclose(L, scipy.special.logsumexp(tau * Q @ K.T, axis=1), rtol=1e-13)
+    t = lambda x: torch.from_numpy(x)[None, None]
+    Ot = torch.nn.functional.scaled_dot_product_attention(t(Q), t(K), t(V))[0, 0].numpy()
+    assert np.allclose(O, Ot, rtol=1e-12, atol=1e-13)
+    O2, _ = o.dense_attention(Q, K, V, scale=0.37)
+    assert np.allclose(O2, _dense_weights(Q, K, 0.37) @ V, rtol=1e-12, atol=1e-13)
+
+
+def test_dense_against_libraries():
+    check_dense_against_libraries()
+
+
+def _sparse_case(seed, N=256, D=16, c=32, k=3, remainder=0):
+    N = N - remainder
+    Q, K, V = _random_head(seed, N=N, D=D)
+    r = _rng(seed + 100)
+    pq = r.permutation(N); pk = r.permutation(N)
+    nc = -(-N // c)
+    blocks = np.stack([np.sort(r.choice(nc, k, replace=False)) for _ in range(nc)])
+    return Q, K, V, pq, pk, blocks, c
+
+
+def _token_set(pk, blocks_row, c, N):
+    sizes = o.leaf_sizes(N, c)
+    return np.concatenate([pk[j * c:j * c + sizes[j]] for j in blocks_row])
+
+
+def check_sparse_error_identity():
+    # Eq. 3-4: o - o_S = (1 - w_S)(o_Sbar - o_S), w from dense attention.
+    for rem in (0, 13):
+        Q, K, V, pq, pk, blocks, c = _sparse_case(13, remainder=rem)
+        N, D = Q.shape
+        tau = 1 / math.sqrt(D)
+        OS, _ = o.sparse_attention(Q, K, V, pq, pk, c, blocks, compensate=False)
+        W = _dense_weights(Q, K, tau)
+        Od = W @ V
+        qsz = o.leaf_sizes(N, c)
+        for a in range(len(qsz)):
+            S = _token_set(pk, blocks[a], c, N)
+            Sb = np.setdiff1d(np.arange(N), S)
+            for i in pq[a * c:a * c + qsz[a]]:
+                wS = W[i, S].sum()
+                oSb = W[i, Sb] @ V[Sb] / W[i, Sb].sum()
+                assert np.allclose(Od[i] - OS[i], (1 - wS) * (oSb - OS[i]), rtol=1e-9, atol=1e-12)
+
+
+def test_sparse_error_identity():
+    check_sparse_error_identity()
+
+
+def check_smc_error_identity():
+    # Eq. 21-33 with dense-normalised weights w_i and w_c = exp(tau q.kbar_c)/Z.
+    for rem in (0, 13):
+        Q, K, V, pq, pk, blocks, c = _sparse_case(14, remainder=rem)
+        N, D = Q.shape
+        tau = 1 / math.sqrt(D)
+        Oh, Lh = o.sparse_attention(Q, K, V, pq, pk, c, blocks, compensate=True)
+        logits = tau * Q @ K.T
+        Z = np.exp(logits).sum(1)
+        W = np.exp(logits) / Z[:, None]
+        Od = W @ V
+        ksz = o.leaf_sizes(N, c)
+        qsz = o.leaf_sizes(N, c)
+        for a in range(len(qsz)):
+            sel = set(blocks[a].tolist())
+            S = _token_set(pk, blocks[a], c, N)
+            for i in pq[a * c:a * c + qsz[a]]:
+                wS = W[i, S].sum()
+                rhs = np.zeros(D)
+                dhat = wS
+                for cl in range(len(ksz)):
+                    if cl in sel:
+                        continue
+                    mem = pk[cl * c:cl * c + ksz[cl]]
+                    kb = K[mem].mean(0); vb = V[mem].mean(0)
+                    wc = math.exp(tau * Q[i] @ kb) / Z[i]
+                    wbar = W[i, mem].mean()
+                    delta = wbar - wc
+                    assert delta >= -1e-15          # Eq. 19/25: Jensen
+                    cov = ((W[i, mem] - wbar)[:, None] * (V[mem] - vb)).mean(0)
+                    rhs += len(mem) * (delta * (vb - Od[i]) + cov)
+                    dhat += len(mem) * wc
+                assert dhat <= 1 + 1e-12             # Eq. 28: d_hat <= 1
+                assert np.allclose(Od[i] - Oh[i], rhs / dhat, rtol=1e-8, atol=1e-12)   # Eq. 33
+                # LSE of the compensated softmax is log(Z d_hat) + the row's log scale
+                assert math.isclose(Lh[i], math.log(Z[i] * dhat), rel_tol=1e-12)
+
+
+def test_smc_error_identity():
+    check_smc_error_identity()
+
+
+def check_special_cases_equal_dense():
+    Q, K, V, pq, pk, blocks, c = _sparse_case(15, N=200, c=32)
+    N = Q.shape[0]
+    Od, Ld = o.dense_attention(Q, K, V)
+    nc = -(-N // c)
+    allb = np.tile(np.arange(nc), (nc, 1))
+    for comp in (False, True):
+        O, L = o.sparse_attention(Q, K, V, pq, pk, c, allb, comp)
+        assert np.allclose(O, Od, rtol=1e-12, atol=1e-12) and np.allclose(L, Ld, rtol=1e-12)
+    # c = 1 with compensation equals dense for any k (each centroid is a token)
+    N = 24
+    Q, K, V = Q[:N], K[:N], V[:N]
+    Od, _ = o.dense_attention(Q, K, V)
+    for k in (1, 5, 24):
+        Os, _, _, _, _ = o.forward(Q[None, None], K[None, None], V[None, None], 1, k, True,
+                                   o.ClusterOpts(seed=2), dtype="f32")
+        assert np.allclose(Os[0, 0], Od, rtol=1e-10, atol=1e-12)
+
+
+def test_special_cases_equal_dense():
+    check_special_cases_equal_dense()
+
+
+def check_piecewise_constant_keys():
+    # Keys with n_c distinct rows, each repeated c times (shuffled): every split
+    # keeps the copies together, so each cluster is one distinct key, delta_c = 0
+    # and Cov_c = 0 (Eq. 27) and compensated attention equals dense for any k.
+    r = _rng(16)
+    c, nc, D = 8, 12, 16
+    N = c * nc
+    base = r.standard_normal((nc, D)).astype(np.float32)
+    K = np.repeat(base, c, axis=0)
+    sh = r.permutation(N)
+    K = K[sh].astype(np.float64)
+    Q = r.standard_normal((N, D)).astype(np.float32).astype(np.float64)
+    V = r.standard_normal((N, D))
+    Od, _ = o.dense_attention(Q, K, V)
+    for k in (1, 3, 7):
+        Os, _, pq, pk, _ = o.forward(Q[None, None], K[None, None], V[None, None], c, k, True,
+                                     o.ClusterOpts(seed=4), dtype="f32")
+        for j in range(nc):
+            assert len({tuple(x) for x in K[pk[0, 0, j * c:(j + 1) * c]]}) == 1
+        assert np.allclose(Os[0, 0], Od, rtol=1e-10, atol=1e-12)
+
+
+def test_piecewise_constant_keys():
+    check_piecewise_constant_keys()
+
+
+def check_permutation_equivariance():
+    r = _rng(17)
+    N, D, c = 256, 16, 32
+    Q = r.standard_normal((N, D)).astype(np.float32).astype(np.float64)
+    K = r.standard_normal((N, D)).astype(np.float32).astype(np.float64)
+    V = r.standard_normal((N, D))
+    P = r.permutation(N)
+    args = dict(c=c, topk=3, compensate=True, opts=o.ClusterOpts(seed=9), dtype="f32")
+    O1, L1, *_ = o.forward(Q[None, None], K[None, None], V[None, None], **args)
+    O2, L2, *_ = o.forward(Q[P][None, None], K[P][None, None], V[P][None, None], **args)
+    assert np.allclose(O2[0, 0], O1[0, 0][P], rtol=1e-12, atol=1e-12)
+    assert np.allclose(L2[0, 0], L1[0, 0][P], rtol=1e-12)
+
+
+def test_permutation_equivariance():
+    check_permutation_equivariance()
+
+
+def test_power_of_two_scaling_invariance():
+    # Full-sample mode (a d >= N): scaling Q by 2^alpha and K by 2^beta scales
+    # every intermediate exactly, so perms and blocks are identical.
+    r = _rng(18)
+    N, D, c = 64, 16, 4
+    Q = r.standard_normal((N, D)).astype(np.float32).astype(np.float64)
+    K = r.standard_normal((N, D)).astype(np.float32).astype(np.float64)
+    V = r.standard_normal((N, D))
+    opts = o.ClusterOpts(seed=1, sample_factor=4)
+    _, _, pq, pk, bl = o.forward(Q[None, None], K[None, None], V[None, None], c, 3, True, opts, "f32")
+    _, _, pq2, pk2, bl2 = o.forward(8 * Q[None, None], 0.25 * K[None, None], V[None, None], c, 3,
+                                    True, opts, "f32")
+    assert np.array_equal(pq, pq2) and np.array_equal(pk, pk2) and np.array_equal(bl, bl2)
+
+
+def test_random_cluster_control_all_selected_is_dense():
+    import synth
+    Q, K, V = _random_head(19, N=192, D=16)
+    pq = synth.random_perm(1, 1, 1, 192)[0, 0]
+    pk = synth.random_perm(2, 1, 1, 192)[0, 0]
+    nc = 192 // 32
+    O, _ = o.sparse_attention(Q, K, V, pq, pk, 32, np.tile(np.arange(nc), (nc, 1)), True)
+    assert np.allclose(O, o.dense_attention(Q, K, V)[0], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each plausible slip in the oracle must fail some pin.
+# ---------------------------------------------------------------------------
+
+def _fails(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+def _no_log_count(Q, K, V, perm_q, perm_k, c, blocks, compensate, scale=None):
+    # compensation without the ln|c| cluster-size weight
+    real_log = np.log
+    try:
+        o.np.log = lambda x: np.zeros_like(np.asarray(x, np.float64))
+        return _orig["sparse_attention"](Q, K, V, perm_q, perm_k, c, blocks, compensate, scale)
+    finally:
+        o.np.log = real_log
+
+
+_orig = {name: getattr(o, name) for name in
+         ["sparse_attention", "split_size", "metric_matrices", "principal_direction", "topk_row",
+          "centroids", "dense_attention", "split_by_scores", "fmix64"]}
+
+
+def _split_size_larger(n, c):
+    t = _orig["split_size"](n, c)
+    if (n // c) % 2 == 1 and n % c == 0:
+        t += c
+    return t
+
+
+def _metric_uncentred(Q, K):
+    Mq, _, kbar = _orig["metric_matrices"](Q, K)
+    K = np.asarray(K, np.float64)
+    return Mq, K.T @ K / K.shape[0], kbar
+
+
+def _power_without_metric(Xs, M, u0, p):
+    return _orig["principal_direction"](Xs, np.eye(M.shape[0]), u0, p)
+
+
+def _topk_ties_high(scores, k):
+    s = np.asarray(scores, np.float64)
+    idx = np.arange(s.shape[0])
+    return np.sort(np.lexsort((-idx, -s))[:k])
+
+
+def _centroids_divide_by_c(X, perm, c):
+    cent, cnt = _orig["centroids"](X, perm, c)
+    return cent * cnt[:, None] / c, cnt
+
+
+def _dense_no_scale(Q, K, V, scale=None):
+    return _orig["dense_attention"](Q, K, V, scale=1.0)
+
+
+def _split_reversed(members, scores, t):
+    return _orig["split_by_scores"](members, -np.asarray(scores), t)
+
+
+def _fmix_wrong_shift(z):
+    if isinstance(z, (int, np.integer)) and not isinstance(z, np.ndarray):
+        z = int(z) & o.MASK64
+        z = ((z ^ (z >> 31)) * o.MIX1) & o.MASK64
+        z = ((z ^ (z >> 27)) * o.MIX2) & o.MASK64
+        return z ^ (z >> 31)
+    return _orig["fmix64"](z)
+
+
+PLANTED = [
+    ("sparse_attention", _no_log_count, check_smc_error_identity),
+    ("split_size", _split_size_larger, check_tree_layout),
+    ("metric_matrices", _metric_uncentred, check_metrics),
+    ("principal_direction", _power_without_metric, check_power_iteration_matches_eigh),
+    ("topk_row", _topk_ties_high, check_topk_bruteforce),
+    ("centroids", _centroids_divide_by_c, check_smc_error_identity),
+    ("dense_attention", _dense_no_scale, check_dense_against_libraries),
+    ("split_by_scores", _split_reversed, check_split_by_scores_bruteforce),
+    ("fmix64", _fmix_wrong_shift, check_splitmix64_published),
+]
+
+
+@pytest.mark.parametrize("name,mutant,check", PLANTED, ids=[p[0] for p in PLANTED])
+def test_planted_mistakes(monkeypatch, name, mutant, check):
+    check()                                   # the pin passes on the real oracle
+    monkeypatch.setattr(o, name, mutant)
+    assert _fails(check), f"planted mistake in {name} was not caught"
