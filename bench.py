@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the ClusterAttention forward hot path on one MI355X (gfx950).
+
+One step is one pass of the whole path over one batch of synthetic input:
+ca_cluster (metrics, recursive PDDP splitting of queries and keys, centroids)
+-> ca_route (centroid scores, top-k) -> ca_attend (key/value tiles and
+centroids, block-sparse attention with striped mean-compensation).
+
+Default workload: the Wan-2.1-14B-like video self-attention shape, 40 heads,
+N = 32760 tokens (21x30x52 latent grid), head_dim 128, bf16, cluster size 128,
+top 1/8 of key clusters (32), compensation on. Inputs are generated on the host
+(seeded), uploaded once, and resident in HBM before the timed region.
+
+Prints one JSON line:
+  value      dense-equivalent effective TFLOP/s = 4 d N^2 H / step time
+  roofline   the block-sparse attention kernel against the bf16 MFMA peak,
+             counting 4 d FLOP per performed token or centroid interaction,
+             timed with HIP events recorded around that kernel alone
+  cpu_baseline  the CPU oracle on a bounded sample of heads of the same input
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ClusterAttention fwd latency, eff. TFLOP/s & speedup vs dense at N=32k, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video_32760")
+    ap.add_argument("--topk", type=int, default=0, help="override top-k")
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--verbose", action="store_true")
+    return ap.parse_args()
+
+
+def gen_inputs(w):
+    import synth
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+        parts = list(ex.map(lambda h: synth.generate(w, heads=slice(h, h + 1)), range(w.H)))
+    Q = np.concatenate([p[0] for p in parts], axis=1)
+    K = np.concatenate([p[1] for p in parts], axis=1)
+    V = np.concatenate([p[2] for p in parts], axis=1)
+    return Q, K, V
+
+
+def cpu_baseline(w, Q, K, V, topk, heads):
+    """The oracle, untuned, on the first `heads` heads of the same input."""
+    import oracle.clusterattn as o
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    opts = o.ClusterOpts(seed=w.cluster_seed)
+    t0 = time.perf_counter()
+    o.forward(Q[:, :heads], K[:, :heads], V[:, :heads], w.c, topk, w.compensate, opts, w.dtype)
+    t = time.perf_counter() - t0
+    flops = 4.0 * w.D * w.N * w.N * heads * w.B
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{heads} of {w.H} heads of the same workload, full N={w.N}; "
+                  f"{t:.2f} s wall for cluster+route+attend in fp64 NumPy "
+                  f"(BLAS threads={cores}; PDDP and top-k loops single-threaded Python)",
+        "seconds": t,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no communication); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import free_clustered_block_amd as ca
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ca.load()
+    w = synth.WORKLOADS[args.workload]
+    topk = args.topk or w.topk
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    Qn, Kn, Vn = gen_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    Q = torch.from_numpy(Qn).to(tdt).to(dev).contiguous()
+    K = torch.from_numpy(Kn).to(tdt).to(dev).contiguous()
+    V = torch.from_numpy(Vn).to(tdt).to(dev).contiguous()
+    if args.verbose:
+        print(f"inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    B, H, N, D = Q.shape
+    c = w.c
+    ws_c = torch.empty(ca.workspace_size(ca.OP_CLUSTER, B, H, N, D, c), dtype=torch.uint8, device=dev)
+    n_c = -(-N // c)
+    ws_r = torch.empty(max(1, ca.workspace_size(ca.OP_ROUTE, B, H, n_c, D, n_c, topk)),
+                       dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(ca.workspace_size(ca.OP_ATTEND, B, H, N, D, c, topk), dtype=torch.uint8,
+                       device=dev)
+
+    def step(evs=None, kev=None):
+        if evs:
+            evs[0].record()
+        cr = ca.cluster(Q, K, c, seed=w.cluster_seed, workspace=ws_c)
+        if evs:
+            evs[1].record()
+        blocks = ca.route(cr.cent_q, cr.cent_k, topk, workspace=ws_r)
+        if evs:
+            evs[2].record()
+            ca.profile_events(kev[0].handle, kev[1].handle)
+        O = ca.attend(Q, K, V, cr.perm_q, cr.perm_k, c, blocks, compensate=w.compensate,
+                      workspace=ws_a)
+        if evs:
+            ca.profile_events(None, None)
+            evs[3].record()
+        return O, cr, blocks
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    kevs = [(ca.HipEvent(), ca.HipEvent()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        O, cr, blocks = step(evs[i], kevs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    if args.verbose:
+        print(f"timed {args.steps} steps: {wall * 1e3:.3f} ms/step", file=sys.stderr, flush=True)
+    st_cluster = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    st_route = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    st_attend = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    t_attn_kernel = np.mean([a.elapsed_ms(b) for a, b in kevs])
+    gpu_step = np.mean([e[0].elapsed_time(e[3]) for e in evs])
+
+    # performed interactions of the attention kernel (valid keys and centroids)
+    bl = blocks.cpu().numpy().astype(np.int64)
+    sizes = np.full(n_c, c, np.int64)
+    sizes[-1] = N - (n_c - 1) * c
+    tok_inter = float(np.sum(sizes[None, None, :] * sizes[bl].sum(-1)))
+    cen_inter = float(np.sum(sizes) * (n_c - topk) * B * H) if w.compensate else 0.0
+    flops_attn = 4.0 * D * (tok_inter + cen_inter)
+    achieved = flops_attn / (t_attn_kernel * 1e-3) / 1e12
+
+    eff = 4.0 * D * N * N * B * H / (wall) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(eff, 3),
+        "unit": "TFLOP/s (dense-equivalent, 4 d N^2 H per step)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "N": N, "head_dim": D,
+                   "cluster_size": c, "topk": topk, "compensate": w.compensate},
+        "stage_ms": {"cluster": round(float(st_cluster), 4), "route": round(float(st_route), 4),
+                     "attend": round(float(st_attend), 4),
+                     "attend_kernel": round(float(t_attn_kernel), 4),
+                     "gpu_step_events": round(float(gpu_step), 4)},
+        "roofline": {
+            "kernel": "attn_fwd (block-sparse attention + SMC)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": flops_attn,
+        },
+    }
+
+    if not args.no_dense:
+        ws_d = torch.empty(ca.workspace_size(ca.OP_DENSE, B, H, N, D), dtype=torch.uint8, device=dev)
+        Od = ca.dense(Q, K, V, workspace=ws_d)
+        torch.cuda.synchronize()
+        de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.dense_steps)]
+        for a, b in de:
+            a.record()
+            Od = ca.dense(Q, K, V, workspace=ws_d)
+            b.record()
+        torch.cuda.synchronize()
+        dense_ms = float(np.mean([a.elapsed_time(b) for a, b in de]))
+        cos = torch.nn.functional.cosine_similarity(O.float(), Od.float(), dim=-1).mean().item()
+        result["dense_ms"] = round(dense_ms, 4)
+        result["speedup_vs_dense"] = round(dense_ms / (wall * 1e3), 3)
+        result["dense_tflops"] = round(4.0 * D * N * N * B * H / (dense_ms * 1e-3) / 1e12, 2)
+        result["cos_vs_dense"] = round(cos, 5)
+
+    if not args.no_cpu_baseline:
+        heads = max(1, min(args.cpu_heads, H))
+        result["cpu_baseline"] = cpu_baseline(w, Qn, Kn, Vn, topk, heads)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

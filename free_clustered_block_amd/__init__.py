@@ -1,0 +1,274 @@
+"""Python binding of the gfx950 ClusterAttention library (libca.so, include/ca.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI. PyTorch supplies device memory (outputs, workspace) and the
+current HIP stream. The library must have been built in-tree
+(``python -m free_clustered_block_amd.build``); nothing here falls back to a
+CPU or framework implementation.
+
+Paper: "ClusterAttention: A training-free speedup of bidirectional attention"
+(arXiv 2608.26965).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+__all__ = [
+    "CAError", "load", "LIB_PATH", "EXPORTS", "profile_events", "HipEvent", "tree_levels",
+    "workspace_size", "cluster", "route", "attend", "dense", "forward", "ClusterResult",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libca.so")
+EXPORTS = ["ca_tree_levels", "ca_workspace_size", "ca_cluster", "ca_route", "ca_attend",
+           "ca_dense", "ca_profile_events", "ca_status_string", "ca_last_error"]
+
+CA_BF16, CA_F32 = 0, 1
+OP_CLUSTER, OP_ROUTE, OP_ATTEND, OP_DENSE = 0, 1, 2, 3
+
+_lib = None
+
+
+class CAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [("transform", ctypes.c_int), ("query_normalize", ctypes.c_int),
+                ("power_iters", ctypes.c_int), ("sample_factor", ctypes.c_int),
+                ("seed", ctypes.c_uint64), ("trace_perm", ctypes.c_void_p),
+                ("trace_score", ctypes.c_void_p)]
+
+
+def load() -> ctypes.CDLL:
+    """Load libca.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m free_clustered_block_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, S, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    lib.ca_tree_levels.argtypes = [I, I]
+    lib.ca_tree_levels.restype = I
+    lib.ca_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.ca_workspace_size.restype = S
+    lib.ca_cluster.argtypes = [P, P, I, I, I, I, I, I, ctypes.POINTER(_Opts), P, P, P, P, P, P, S, P]
+    lib.ca_cluster.restype = I
+    lib.ca_route.argtypes = [P, P, I, I, I, I, I, I, P, P, P, S, P]
+    lib.ca_route.restype = I
+    lib.ca_attend.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, I, I, F, P, P, P, S, P]
+    lib.ca_attend.restype = I
+    lib.ca_dense.argtypes = [P, P, P, I, I, I, I, I, F, P, P, P, S, P]
+    lib.ca_dense.restype = I
+    lib.ca_profile_events.argtypes = [P, P]
+    lib.ca_profile_events.restype = I
+    lib.ca_status_string.argtypes = [I]
+    lib.ca_status_string.restype = ctypes.c_char_p
+    lib.ca_last_error.argtypes = []
+    lib.ca_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load()
+        msg = lib.ca_status_string(status).decode()
+        detail = lib.ca_last_error().decode()
+        raise CAError(status, f"{msg}: {detail}")
+
+
+def profile_events(start=None, stop=None) -> None:
+    """Record two raw hipEvent_t handles (ints, see ``HipEvent``) around the
+    attention kernel of the following attend/dense calls on this thread;
+    None, None switches it off."""
+    load().ca_profile_events(start, stop)
+
+
+class HipEvent:
+    """A raw timing hipEvent_t from the process's HIP runtime (the library
+    records these itself, which torch.cuda.Event does not allow)."""
+    _hip = None
+
+    @classmethod
+    def _rt(cls):
+        if cls._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        if self._rt().hipEventCreate(ctypes.byref(self.handle)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        if self._rt().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.handle:
+            self._hip.hipEventDestroy(self.handle)
+
+
+def tree_levels(N: int, c: int) -> int:
+    return load().ca_tree_levels(N, c)
+
+
+def workspace_size(op: int, B: int, H: int, N: int, D: int, c: int = 0, topk: int = 0) -> int:
+    return int(load().ca_workspace_size(op, B, H, N, D, c, topk))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return CA_BF16
+    if t.dtype == torch.float32:
+        return CA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_ptr(dev) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _ws(nbytes: int, dev, workspace=None):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if workspace is not None and workspace.numel() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+def _bhnd(*ts):
+    for t in ts:
+        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("tensors must be contiguous [B, H, N, D] device tensors")
+
+
+@dataclass
+class ClusterResult:
+    perm_q: object
+    perm_k: object
+    cent_q: object
+    cent_k: object
+    counts: object
+    trace_perm: object = None
+    trace_score: object = None
+
+
+def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = True,
+            power_iters: int = 8, sample_factor: int = 1, seed: int = 0, trace: bool = False,
+            workspace=None) -> ClusterResult:
+    """ca_cluster: permutations into clusters of size c and the cluster centroids."""
+    torch = _torch()
+    _bhnd(Q, K)
+    B, H, N, D = Q.shape
+    dev = Q.device
+    n_c = -(-N // c)
+    perm_q = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    perm_k = torch.empty_like(perm_q)
+    cent_q = torch.empty((B, H, n_c, D), dtype=torch.float32, device=dev)
+    cent_k = torch.empty_like(cent_q)
+    counts = torch.empty((B, H, n_c), dtype=torch.int32, device=dev)
+    tp = ts = None
+    if trace:
+        L = tree_levels(N, c)
+        tp = torch.full((L + 1, B * H, 2, N), -1, dtype=torch.int32, device=dev)
+        ts = torch.full((max(L, 1), B * H, 2, N), float("nan"), dtype=torch.float32, device=dev)
+    opts = _Opts(int(transform), int(query_normalize), power_iters, sample_factor,
+                 seed & ((1 << 64) - 1), _ptr(tp), _ptr(ts))
+    nbytes = workspace_size(OP_CLUSTER, B, H, N, D, c)
+    ws = _ws(nbytes, dev, workspace)
+    st = load().ca_cluster(Q.data_ptr(), K.data_ptr(), _dtype_code(Q), B, H, N, D, c,
+                           ctypes.byref(opts), perm_q.data_ptr(), perm_k.data_ptr(),
+                           cent_q.data_ptr(), cent_k.data_ptr(), counts.data_ptr(),
+                           _ptr(ws), nbytes, _stream_ptr(dev))
+    _check(st)
+    return ClusterResult(perm_q, perm_k, cent_q, cent_k, counts, tp, ts)
+
+
+def route(cent_q, cent_k, topk: int, *, return_scores: bool = False, workspace=None):
+    """ca_route: top-k key clusters per query cluster (ascending indices)."""
+    torch = _torch()
+    B, H, nq, D = cent_q.shape
+    nk = cent_k.shape[2]
+    dev = cent_q.device
+    blocks = torch.empty((B, H, nq, topk), dtype=torch.int32, device=dev)
+    scores = torch.empty((B, H, nq, nk), dtype=torch.float32, device=dev) if return_scores else None
+    nbytes = 0 if return_scores else workspace_size(OP_ROUTE, B, H, nq, D, nk, topk)
+    ws = _ws(nbytes, dev, workspace)
+    st = load().ca_route(cent_q.data_ptr(), cent_k.data_ptr(), B, H, nq, nk, D, topk,
+                         blocks.data_ptr(), _ptr(scores), _ptr(ws), nbytes, _stream_ptr(dev))
+    _check(st)
+    return (blocks, scores) if return_scores else blocks
+
+
+def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
+           scale: float = 0.0, return_lse: bool = False, workspace=None):
+    """ca_attend: block-sparse attention with optional mean-compensation."""
+    torch = _torch()
+    _bhnd(Q, K, V)
+    B, H, N, D = Q.shape
+    dev = Q.device
+    O = torch.empty_like(Q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
+    topk = blocks.shape[-1]
+    nbytes = workspace_size(OP_ATTEND, B, H, N, D, c, topk)
+    ws = _ws(nbytes, dev, workspace)
+    st = load().ca_attend(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, D,
+                          perm_q.data_ptr(), perm_k.data_ptr(), c, blocks.data_ptr(), topk,
+                          int(compensate), float(scale), O.data_ptr(), _ptr(lse), _ptr(ws),
+                          nbytes, _stream_ptr(dev))
+    _check(st)
+    return (O, lse) if return_lse else O
+
+
+def dense(Q, K, V, *, scale: float = 0.0, return_lse: bool = False, workspace=None):
+    """ca_dense: dense attention baseline."""
+    torch = _torch()
+    _bhnd(Q, K, V)
+    B, H, N, D = Q.shape
+    dev = Q.device
+    O = torch.empty_like(Q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
+    nbytes = workspace_size(OP_DENSE, B, H, N, D)
+    ws = _ws(nbytes, dev, workspace)
+    st = load().ca_dense(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, D,
+                         float(scale), O.data_ptr(), _ptr(lse), _ptr(ws), nbytes, _stream_ptr(dev))
+    _check(st)
+    return (O, lse) if return_lse else O
+
+
+def forward(Q, K, V, c: int, topk: int, *, compensate: bool = True, seed: int = 0,
+            return_all: bool = False, **cluster_kw):
+    """The whole path: cluster -> route -> attend."""
+    cr = cluster(Q, K, c, seed=seed, **cluster_kw)
+    blocks = route(cr.cent_q, cr.cent_k, topk)
+    O = attend(Q, K, V, cr.perm_q, cr.perm_k, c, blocks, compensate=compensate)
+    return (O, cr, blocks) if return_all else O

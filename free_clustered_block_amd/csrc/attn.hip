@@ -1,0 +1,493 @@
+// Block-sparse attention with striped mean-compensation (paper v1 §1.2
+// Eq. 2 and 5-6, App. A Eq. 21-22; the kernel returns the softmax denominator
+// as in §3.1) and the dense baseline (Eq. 1), on gfx950 bf16 MFMA.
+//
+// bf16 path:
+//   permute_kv   one workgroup per key cluster: gathers the cluster's K rows
+//                into a contiguous zero-padded tile [c][D], its V rows into a
+//                transposed tile [D][c] (key order swizzled to the MFMA operand
+//                order), and forms the key/value centroids and ln n_c.
+//   attn_fwd     one workgroup per query cluster (c/32 waves, 32 queries per
+//                wave): for every selected key cluster the K and V tiles are
+//                staged in LDS, S^T = K Q^T and O^T += V^T P^T run on
+//                v_mfma_f32_32x32x16_bf16 with an fp32 online softmax (exp2);
+//                the excluded clusters then enter through their centroids
+//                (logit scale q.kbar + ln n_c, value vbar) in the same running
+//                maximum and sum. O is scattered back to token order.
+// fp32 path: the same computation on VALU, one thread per query.
+#include "kernels.h"
+#include "mfma.h"
+
+namespace ca {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Token indices come from caller-supplied permutations: out-of-range values
+// read row 0 instead of faulting (the result is then meaningless).
+CA_DEV int clamp_tok(int t, int N) { return (unsigned)t < (unsigned)N ? t : 0; }
+
+// Storage slot of key k (0..15) inside a 16-key group of a transposed V tile:
+// the middle two quads are swapped so that the 8 keys a lane contributes to
+// the P.V contraction are contiguous.
+CA_HD int vslot(int k) {
+  const int q = (k >> 2) & 3;
+  const int qs = q == 1 ? 2 : (q == 2 ? 1 : q);
+  return (k & ~15) | (qs << 2) | (k & 3);
+}
+
+// ----------------------------------------------------------------------------
+// Cluster-major K / transposed V tiles and centroids (bf16 path)
+// ----------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
+  constexpr int RB = 64;                    // rows per LDS block
+  __shared__ __attribute__((aligned(16))) uint16_t sv[RB][D + 8];
+  __shared__ float sk[256 / D][D], sm[256 / D][D];
+  const int j = blockIdx.x, bh = blockIdx.y;
+  const int c = a.c, nc = a.nc, ncp = attn_ncp(nc);
+  const int tid = threadIdx.x;
+  if (j >= nc) {
+    // centroid padding up to a multiple of 32: zero vectors with ln n = -inf
+    for (int d = tid; d < D; d += 256) {
+      a.kbar_hi[((int64_t)bh * ncp + j) * D + d] = 0;
+      a.kbar_lo[((int64_t)bh * ncp + j) * D + d] = 0;
+      a.vbar_t[((int64_t)bh * D + d) * ncp + vslot(j)] = 0;
+      a.kbar32[((int64_t)bh * ncp + j) * D + d] = 0.0f;
+      a.vbar32[((int64_t)bh * ncp + j) * D + d] = 0.0f;
+    }
+    if (tid == 0) a.logn[(int64_t)bh * ncp + j] = kNegInf;
+    return;
+  }
+  const int nj = min(c, a.N - j * c);
+  const int32_t* perm = a.perm_k ? a.perm_k + (int64_t)bh * a.N + (int64_t)j * c : nullptr;
+  const uint16_t* K = (const uint16_t*)a.K + (int64_t)bh * a.N * D;
+  const uint16_t* V = (const uint16_t*)a.V + (int64_t)bh * a.N * D;
+  uint16_t* kc = a.kc + ((int64_t)bh * nc + j) * c * D;
+  uint16_t* vt = a.vt + ((int64_t)bh * nc + j) * (int64_t)D * c;
+
+  // K rows: 16-byte chunks, zero padded
+  constexpr int CPR = D / 8;
+  for (int e = tid; e < c * CPR; e += 256) {
+    const int r = e / CPR, g = e % CPR;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r < nj) {
+      const int tok = perm ? clamp_tok(perm[r], a.N) : j * c + r;
+      v = *reinterpret_cast<const u32x4_t*>(K + (int64_t)tok * D + 8 * g);
+    }
+    *reinterpret_cast<u32x4_t*>(kc + (int64_t)r * D + 8 * g) = v;
+  }
+  // centroid sums in row order: thread (grp, d) sums rows grp, grp+G, ...
+  constexpr int G = 256 / D;
+  const int d = tid % D, grp = tid / D;
+  float ksum = 0.0f, vsum = 0.0f;
+  for (int r = grp; r < nj; r += G) {
+    const int tok = perm ? clamp_tok(perm[r], a.N) : j * c + r;
+    ksum += bf16_to_f32(K[(int64_t)tok * D + d]);
+  }
+  // V: through LDS in blocks of 64 rows, written transposed [D][c]
+  for (int r0 = 0; r0 < c; r0 += RB) {
+    for (int e = tid; e < RB * CPR; e += 256) {
+      const int r = e / CPR, g = e % CPR;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (r0 + r < nj) {
+        const int tok = perm ? clamp_tok(perm[r0 + r], a.N) : j * c + r0 + r;
+        v = *reinterpret_cast<const u32x4_t*>(V + (int64_t)tok * D + 8 * g);
+      }
+      *reinterpret_cast<u32x4_t*>(&sv[r][8 * g]) = v;
+    }
+    __syncthreads();
+    for (int r = grp; r < RB; r += G)
+      if (r0 + r < nj) vsum += bf16_to_f32(sv[r][d]);
+    // each thread writes 8 consecutive storage slots of one dim
+    for (int e = tid; e < D * (RB / 8); e += 256) {
+      const int dd = e / (RB / 8), s8 = e % (RB / 8);
+      uint16_t vals[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        // storage slot s8*8+q holds key vslot^-1(slot); vslot is an involution
+        const int key = vslot(s8 * 8 + q);
+        vals[q] = sv[key][dd];
+      }
+      u32x4_t pk;
+      pk.x = vals[0] | ((uint32_t)vals[1] << 16);
+      pk.y = vals[2] | ((uint32_t)vals[3] << 16);
+      pk.z = vals[4] | ((uint32_t)vals[5] << 16);
+      pk.w = vals[6] | ((uint32_t)vals[7] << 16);
+      *reinterpret_cast<u32x4_t*>(vt + (int64_t)dd * c + r0 + s8 * 8) = pk;
+    }
+    __syncthreads();
+  }
+  sk[grp][d] = ksum;
+  sm[grp][d] = vsum;
+  __syncthreads();
+  if (grp == 0) {
+    float ks = 0.0f, vs = 0.0f;
+#pragma unroll
+    for (int q = 0; q < G; ++q) { ks += sk[q][d]; vs += sm[q][d]; }
+    const float inv = 1.0f / (float)nj;
+    const float kb = ks * inv, vb = vs * inv;
+    const uint16_t hi = f32_to_bf16(kb);
+    a.kbar_hi[((int64_t)bh * ncp + j) * D + d] = hi;
+    a.kbar_lo[((int64_t)bh * ncp + j) * D + d] = f32_to_bf16(kb - bf16_to_f32(hi));
+    a.vbar_t[((int64_t)bh * D + d) * ncp + vslot(j)] = f32_to_bf16(vb);
+    a.kbar32[((int64_t)bh * ncp + j) * D + d] = kb;
+    a.vbar32[((int64_t)bh * ncp + j) * D + d] = vb;
+    if (d == 0) a.logn[(int64_t)bh * ncp + j] = logf((float)nj);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Attention (bf16 MFMA)
+// ----------------------------------------------------------------------------
+
+template <int D, int C>
+struct AttnSmem {
+  static constexpr int KP = D + 8;     // padded K row (bf16)
+  static constexpr int VP = C + 8;     // padded V^T row (bf16)
+  static constexpr size_t k_bytes = (size_t)C * KP * 2;
+  static constexpr size_t v_bytes = (size_t)D * VP * 2;
+  static constexpr size_t bytes = k_bytes + v_bytes + 8192 / 8 + 64;
+};
+
+template <int D, int C, bool DENSE>
+__global__ __launch_bounds__(2 * C) void attn_fwd(AttnArgs a) {
+  using SM = AttnSmem<D, C>;
+  constexpr int NT = 2 * C;            // threads
+  constexpr int KS = D / 16;           // k-steps over the head dim
+  constexpr int NB = D / 32;           // 32-row blocks of O^T
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint16_t* sK = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + SM::k_bytes);
+  uint32_t* sSel = reinterpret_cast<uint32_t*>(smem + SM::k_bytes + SM::v_bytes);
+
+  const int qa = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
+  const int N = a.N, nc = a.nc;
+  const int qpos = qa * C + w * 32 + r;            // cluster-major position of this lane's query
+  const bool qvalid = qpos < N;
+  const int qtok =
+      qvalid ? (DENSE || !a.perm_q ? qpos : clamp_tok(a.perm_q[(int64_t)bh * N + qpos], N)) : 0;
+  const uint16_t* Qh = (const uint16_t*)a.Q + (int64_t)bh * N * D;
+
+  bf16x8_t qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (qvalid) v = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)qtok * D + s * 16 + h * 8);
+    qf[s] = as_bf16x8(v);
+  }
+  floatx16_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = zero16();
+  float m = kNegInf, lsum = 0.0f;
+  const float sl2 = a.scale * kLog2e;
+
+  // online-softmax update of this lane's query with 16 logits (log2 units)
+  auto absorb = [&](float (&t)[16], const uint16_t* vsrc, int vpitch, int vcol0) {
+    float bm = t[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) bm = fmaxf(bm, t[i]);
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float mn = fmaxf(m, bm);
+    const float mref = mn == kNegInf ? 0.0f : mn;
+    const float alpha = exp2f(m - mref);
+    float p[16], ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { p[i] = exp2f(t[i] - mref); ps += p[i]; }
+    ps += __shfl_xor(ps, 32, 64);
+    lsum = lsum * alpha + ps;
+    m = mn;
+    const bf16x8_t p0 = as_bf16x8(pack8(p));
+    const bf16x8_t p1 = as_bf16x8(pack8(p + 8));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
+      const uint16_t* row = vsrc + (int64_t)(nb * 32 + r) * vpitch + vcol0 + h * 8;
+      const bf16x8_t v0 = *reinterpret_cast<const bf16x8_t*>(row);
+      const bf16x8_t v1 = *reinterpret_cast<const bf16x8_t*>(row + 16);
+      acc[nb] = mfma32(v0, p0, acc[nb]);
+      acc[nb] = mfma32(v1, p1, acc[nb]);
+    }
+  };
+
+  const int nsel = DENSE ? nc : a.topk;
+  const int32_t* blk = DENSE ? nullptr : a.blocks + ((int64_t)bh * nc + qa) * a.topk;
+  for (int bi = 0; bi < nsel; ++bi) {
+    const int j = DENSE ? bi : blk[bi];
+    if (j < 0 || j >= nc) continue;   // out-of-range entries are ignored (uniform per block)
+    const int nvalid = min(C, N - j * C);
+    const uint16_t* kc = a.kc + ((int64_t)bh * nc + j) * C * D;
+    const uint16_t* vt = a.vt + ((int64_t)bh * nc + j) * (int64_t)D * C;
+    __syncthreads();
+    for (int e = tid; e < C * D / 8; e += NT) {
+      const int rr = e / (D / 8), g = e % (D / 8);
+      *reinterpret_cast<u32x4_t*>(sK + rr * SM::KP + 8 * g) =
+          *reinterpret_cast<const u32x4_t*>(kc + (int64_t)rr * D + 8 * g);
+    }
+    for (int e = tid; e < D * C / 8; e += NT) {
+      const int rr = e / (C / 8), g = e % (C / 8);
+      *reinterpret_cast<u32x4_t*>(sV + rr * SM::VP + 8 * g) =
+          *reinterpret_cast<const u32x4_t*>(vt + (int64_t)rr * C + 8 * g);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int kb = 0; kb < C / 32; ++kb) {
+      floatx16_t sacc = zero16();
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t*>(sK + (kb * 32 + r) * SM::KP + s * 16 + h * 8);
+        sacc = mfma32(kf, qf[s], sacc);
+      }
+      float t[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb * 32 + c_row(i, h);
+        t[i] = key < nvalid ? sacc[i] * sl2 : kNegInf;
+      }
+      absorb(t, sV, SM::VP, kb * 32);
+    }
+  }
+
+  if (!DENSE && a.compensate) {
+    const int ncp = attn_ncp(nc);
+    __syncthreads();
+    for (int e = tid; e < ncp / 32; e += NT) sSel[e] = 0u;
+    __syncthreads();
+    for (int e = tid; e < a.topk; e += NT) {
+      const int j = blk[e];
+      if (j >= 0 && j < nc) atomicOr(&sSel[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    const uint16_t* khi = a.kbar_hi + (int64_t)bh * ncp * D;
+    const uint16_t* klo = a.kbar_lo + (int64_t)bh * ncp * D;
+    const uint16_t* vbt = a.vbar_t + (int64_t)bh * D * ncp;
+    const float* logn = a.logn + (int64_t)bh * ncp;
+#pragma unroll 1
+    for (int cb = 0; cb < ncp / 32; ++cb) {
+      floatx16_t sacc = zero16();
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int64_t o = (int64_t)(cb * 32 + r) * D + s * 16 + h * 8;
+        sacc = mfma32(*reinterpret_cast<const bf16x8_t*>(khi + o), qf[s], sacc);
+        sacc = mfma32(*reinterpret_cast<const bf16x8_t*>(klo + o), qf[s], sacc);
+      }
+      const uint32_t selw = sSel[cb];
+      float t[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int cr = c_row(i, h);
+        const bool excluded = !((selw >> cr) & 1u);
+        const float ln = logn[cb * 32 + cr];
+        t[i] = excluded ? (sacc[i] * sl2 + ln * kLog2e) : kNegInf;
+      }
+      absorb(t, vbt, ncp, cb * 32);
+    }
+  }
+
+  if (!qvalid) return;
+  const float inv = 1.0f / lsum;
+  uint16_t* Oh = (uint16_t*)a.O + ((int64_t)bh * N + qtok) * D;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = nb * 32 + 8 * g + 4 * h;
+      u32x2_t v;
+      v.x = pack_bf16x2(acc[nb][4 * g] * inv, acc[nb][4 * g + 1] * inv);
+      v.y = pack_bf16x2(acc[nb][4 * g + 2] * inv, acc[nb][4 * g + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(Oh + d0) = v;
+    }
+  }
+  if (a.lse && h == 0) a.lse[(int64_t)bh * N + qtok] = (m + log2f(lsum)) * kLn2;
+}
+
+// ----------------------------------------------------------------------------
+// fp32 path
+// ----------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void centroids_kv_f32(AttnArgs a) {
+  const int j = blockIdx.x, bh = blockIdx.y;
+  const int ncp = attn_ncp(a.nc);
+  const int d = threadIdx.x;
+  if (d >= D) return;
+  float* kb = a.kbar32 + ((int64_t)bh * ncp + j) * D;
+  float* vb = a.vbar32 + ((int64_t)bh * ncp + j) * D;
+  if (j >= a.nc) {
+    kb[d] = 0.0f; vb[d] = 0.0f;
+    if (d == 0) a.logn[(int64_t)bh * ncp + j] = kNegInf;
+    return;
+  }
+  const int nj = min(a.c, a.N - j * a.c);
+  const int32_t* perm = a.perm_k + (int64_t)bh * a.N + (int64_t)j * a.c;
+  const float* K = (const float*)a.K + (int64_t)bh * a.N * D;
+  const float* V = (const float*)a.V + (int64_t)bh * a.N * D;
+  float ks = 0.0f, vs = 0.0f;
+  for (int r = 0; r < nj; ++r) {
+    const int tok = clamp_tok(perm[r], a.N);
+    ks += K[(int64_t)tok * D + d];
+    vs += V[(int64_t)tok * D + d];
+  }
+  kb[d] = ks / (float)nj;
+  vb[d] = vs / (float)nj;
+  if (d == 0) a.logn[(int64_t)bh * ncp + j] = logf((float)nj);
+}
+
+template <int D, bool DENSE>
+__global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
+  __shared__ float skv[2][32][D];
+  __shared__ uint32_t sSel[8192 / 32];
+  const int qa = blockIdx.x, bh = blockIdx.y;
+  const int N = a.N, nc = a.nc, c = a.c;
+  const int tid = threadIdx.x;
+  const int qpos = qa * 256 + tid;                   // DENSE: 256 queries per block
+  int qtok = 0;
+  bool qvalid;
+  if (DENSE) {
+    qvalid = qpos < N;
+    qtok = qpos;
+  } else {
+    const int nq = min(c, N - qa * c);
+    qvalid = tid < nq;
+    if (qvalid) qtok = clamp_tok(a.perm_q[(int64_t)bh * N + qa * c + tid], N);
+  }
+  const float* Qh = (const float*)a.Q + (int64_t)bh * N * D;
+  const float* Kh = (const float*)a.K + (int64_t)bh * N * D;
+  const float* Vh = (const float*)a.V + (int64_t)bh * N * D;
+  float q[D], o[D];
+  for (int d = 0; d < D; ++d) { q[d] = qvalid ? Qh[(int64_t)qtok * D + d] : 0.0f; o[d] = 0.0f; }
+  float m = kNegInf, lsum = 0.0f;
+  auto absorb = [&](float logit, const float* v) {
+    const float mn = fmaxf(m, logit);
+    const float alpha = __expf(m - mn);
+    const float p = __expf(logit - mn);
+    lsum = lsum * alpha + p;
+    for (int d = 0; d < D; ++d) o[d] = o[d] * alpha + p * v[d];
+    m = mn;
+  };
+  // key tokens, 32 at a time through LDS
+  const int nsel = DENSE ? 1 : a.topk;
+  for (int bi = 0; bi < nsel; ++bi) {
+    const int j = DENSE ? 0 : a.blocks[((int64_t)bh * nc + qa) * a.topk + bi];
+    if (j < 0 || j >= nc) continue;
+    const int kbeg = DENSE ? 0 : j * c;
+    const int kcnt = DENSE ? N : min(c, N - j * c);
+    for (int k0 = 0; k0 < kcnt; k0 += 32) {
+      __syncthreads();
+      for (int e = tid; e < 32 * D; e += 256) {
+        const int rr = e / D, d = e % D;
+        if (k0 + rr < kcnt) {
+          const int pos = kbeg + k0 + rr;
+          const int tok = DENSE ? pos : clamp_tok(a.perm_k[(int64_t)bh * N + pos], N);
+          skv[0][rr][d] = Kh[(int64_t)tok * D + d];
+          skv[1][rr][d] = Vh[(int64_t)tok * D + d];
+        }
+      }
+      __syncthreads();
+      const int kn = min(32, kcnt - k0);
+      for (int rr = 0; rr < kn; ++rr) {
+        float s = 0.0f;
+        for (int d = 0; d < D; ++d) s += q[d] * skv[0][rr][d];
+        absorb(s * a.scale, skv[1][rr]);
+      }
+    }
+  }
+  if (!DENSE && a.compensate) {
+    const int ncp = attn_ncp(nc);
+    __syncthreads();
+    for (int e = tid; e < ncp / 32; e += 256) sSel[e] = 0u;
+    __syncthreads();
+    for (int e = tid; e < a.topk; e += 256) {
+      const int j = a.blocks[((int64_t)bh * nc + qa) * a.topk + e];
+      if (j >= 0 && j < nc) atomicOr(&sSel[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    for (int j = 0; j < nc; ++j) {
+      if ((sSel[j >> 5] >> (j & 31)) & 1u) continue;
+      const float* kb = a.kbar32 + ((int64_t)bh * ncp + j) * D;
+      const float* vb = a.vbar32 + ((int64_t)bh * ncp + j) * D;
+      float s = 0.0f;
+      for (int d = 0; d < D; ++d) s += q[d] * kb[d];
+      absorb(s * a.scale + a.logn[(int64_t)bh * ncp + j], vb);
+    }
+  }
+  if (!qvalid) return;
+  float* Oh = (float*)a.O + ((int64_t)bh * N + qtok) * D;
+  const float inv = 1.0f / lsum;
+  for (int d = 0; d < D; ++d) Oh[d] = o[d] * inv;
+  if (a.lse) a.lse[(int64_t)bh * N + qtok] = m + logf(lsum);
+}
+
+template <int D, int C, bool DENSE>
+void launch_mfma(const AttnArgs& a, hipStream_t st) {
+  const size_t sm = AttnSmem<D, C>::bytes;
+  static bool attr_set = false;   // raise the dynamic-LDS limit once per instantiation
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd<D, C, DENSE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    attr_set = true;
+  }
+  dim3 g(a.nc, a.BH);
+  if (a.ev_start) (void)hipEventRecord(a.ev_start, st);
+  attn_fwd<D, C, DENSE><<<g, 2 * C, sm, st>>>(a);
+  if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);
+}
+
+template <int D>
+void launch_bf16(const AttnArgs& a, bool dense, hipStream_t st) {
+  dim3 gp(attn_ncp(a.nc), a.BH);
+  permute_kv<D><<<gp, 256, 0, st>>>(a);
+  if (dense) {
+    launch_mfma<D, 128, true>(a, st);
+    return;
+  }
+  switch (a.c) {
+    case 64: launch_mfma<D, 64, false>(a, st); break;
+    case 128: launch_mfma<D, 128, false>(a, st); break;
+    default: launch_mfma<D, 256, false>(a, st); break;
+  }
+}
+
+template <int D>
+void launch_f32(const AttnArgs& a, bool dense, hipStream_t st) {
+  if (dense) {
+    dim3 g((a.N + 255) / 256, a.BH);
+    if (a.ev_start) (void)hipEventRecord(a.ev_start, st);
+    attn_f32<D, true><<<g, 256, 0, st>>>(a);
+    if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);
+    return;
+  }
+  dim3 gc(attn_ncp(a.nc), a.BH);
+  centroids_kv_f32<D><<<gc, 256, 0, st>>>(a);
+  dim3 g(a.nc, a.BH);
+  if (a.ev_start) (void)hipEventRecord(a.ev_start, st);
+  attn_f32<D, false><<<g, 256, 0, st>>>(a);
+  if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);
+}
+
+}  // namespace
+
+void launch_attend(const AttnArgs& a, hipStream_t st) {
+  if (a.dtype == 0) {
+    if (a.D == 64) launch_bf16<64>(a, false, st); else launch_bf16<128>(a, false, st);
+  } else {
+    if (a.D == 64) launch_f32<64>(a, false, st); else launch_f32<128>(a, false, st);
+  }
+}
+
+void launch_dense(const AttnArgs& a, hipStream_t st) {
+  if (a.dtype == 0) {
+    if (a.D == 64) launch_bf16<64>(a, true, st); else launch_bf16<128>(a, true, st);
+  } else {
+    if (a.D == 64) launch_f32<64>(a, true, st); else launch_f32<128>(a, true, st);
+  }
+}
+
+}  // namespace ca

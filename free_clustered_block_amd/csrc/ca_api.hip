@@ -1,0 +1,314 @@
+// Host side of the C ABI declared in include/ca.h: argument validation,
+// workspace layout and launch sequencing. No call allocates memory or
+// synchronises with the device.
+#include <cmath>
+#include <string>
+
+#include "ca.h"
+#include "kernels.h"
+
+namespace ca {
+
+static thread_local std::string g_last_error;
+static thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+void set_error(const std::string& s) { g_last_error = s; }
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+// Carves typed, 256-byte aligned sub-buffers out of the workspace. With a null
+// base it only measures, so sizing and carving share one layout.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+  size_t size() const { return (off + kAlign - 1) / kAlign * kAlign; }
+};
+
+struct ClusterWs {
+  float* partial;
+  uint64_t* hash;
+  float *Mq, *Mk, *kbar;
+  uint16_t* gsplit;
+  float* s;
+  int32_t *permA, *permB;
+  uint32_t* keys;
+  float *dirA, *dirB;
+  int32_t* sample;
+  float* zbuf;
+};
+
+ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c) {
+  ClusterWs w;
+  const size_t T = 2 * (size_t)BH;
+  const int rows = metric_rows_per_chunk(N);
+  const size_t nchunks = (N + rows - 1) / rows;
+  const int L = tree_levels_host(N, c);
+  const size_t slots = L > 0 ? ((size_t)1 << (L - 1)) : 1;
+  w.partial = cv.take<float>((size_t)BH * nchunks * (2 * (size_t)D * D + D));
+  w.hash = cv.take<uint64_t>(T * N);
+  w.Mq = cv.take<float>((size_t)BH * D * D);
+  w.Mk = cv.take<float>((size_t)BH * D * D);
+  w.kbar = cv.take<float>((size_t)BH * D);
+  w.gsplit = cv.take<uint16_t>((size_t)BH * 3 * D * D);
+  w.s = cv.take<float>((size_t)BH * N);
+  w.permA = cv.take<int32_t>(T * N);
+  w.permB = cv.take<int32_t>(T * N);
+  w.keys = cv.take<uint32_t>(T * N);
+  w.dirA = cv.take<float>(T * slots * D);
+  w.dirB = cv.take<float>(T * slots * D);
+  w.sample = cv.take<int32_t>(T * N);
+  w.zbuf = cv.take<float>(T * N);
+  return w;
+}
+
+void plan_attend(Carver& cv, AttnArgs& a, bool with_tiles) {
+  const size_t BH = a.BH, nc = a.nc, ncp = attn_ncp(a.nc), D = a.D, c = a.c;
+  if (with_tiles) {
+    a.kc = cv.take<uint16_t>(BH * nc * c * D);
+    a.vt = cv.take<uint16_t>(BH * nc * c * D);
+    a.kbar_hi = cv.take<uint16_t>(BH * ncp * D);
+    a.kbar_lo = cv.take<uint16_t>(BH * ncp * D);
+    a.vbar_t = cv.take<uint16_t>(BH * ncp * D);
+  } else {
+    a.kc = a.vt = a.kbar_hi = a.kbar_lo = a.vbar_t = nullptr;
+  }
+  a.logn = cv.take<float>(BH * ncp);
+  a.kbar32 = cv.take<float>(BH * ncp * D);
+  a.vbar32 = cv.take<float>(BH * ncp * D);
+}
+
+constexpr int kDenseTile = 128;
+
+bool supported_c(int c) { return c == 64 || c == 128 || c == 256; }
+bool supported_d(int d) { return d == 64 || d == 128; }
+
+int fail(int code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return 0;
+  if (!ws) return fail(CA_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(CA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(CA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +
+                                      " bytes, got " + std::to_string(ws_bytes));
+  return 0;
+}
+
+int after_launch() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return CA_OK;
+}
+
+int check_common(int dt, int B, int H, int N, int D) {
+  if (dt != CA_BF16 && dt != CA_F32) return fail(CA_ERR_INVALID_ARG, "unknown dtype");
+  if (B < 1 || H < 1 || N < 1 || D < 1) return fail(CA_ERR_INVALID_ARG, "B, H, N, D must be >= 1");
+  if ((int64_t)B * H > 32767) return fail(CA_ERR_UNSUPPORTED, "B*H must be <= 32767");
+  if ((int64_t)B * H * N >= (int64_t)1 << 31) return fail(CA_ERR_INVALID_ARG, "B*H*N must be < 2^31");
+  if (!supported_d(D)) return fail(CA_ERR_UNSUPPORTED, "D must be 64 or 128");
+  return 0;
+}
+
+}  // namespace
+}  // namespace ca
+
+using namespace ca;
+
+extern "C" {
+
+int ca_tree_levels(int N, int cluster_size) {
+  if (N < 1 || cluster_size < 1) return -1;
+  return tree_levels_host(N, cluster_size);
+}
+
+size_t ca_workspace_size(ca_op op, int B, int H, int N, int D, int cluster_size, int topk) {
+  if (B < 1 || H < 1 || N < 1 || D < 1) return SIZE_MAX;
+  const int BH = B * H;
+  Carver cv(nullptr);
+  switch (op) {
+    case CA_OP_CLUSTER:
+      if (cluster_size < 1 || N < cluster_size) return SIZE_MAX;
+      plan_cluster(cv, BH, N, D, cluster_size);
+      return cv.size();
+    case CA_OP_ROUTE: {
+      // N = n_qc and cluster_size = n_kc for this op
+      const size_t nq = N, nk = cluster_size;
+      (void)cv.take<float>((size_t)BH * nq * nk);
+      return cv.size();
+    }
+    case CA_OP_ATTEND: {
+      if (cluster_size < 1 || N < cluster_size) return SIZE_MAX;
+      AttnArgs a{};
+      a.BH = BH; a.N = N; a.D = D; a.c = cluster_size; a.nc = (N + cluster_size - 1) / cluster_size;
+      plan_attend(cv, a, true);
+      return cv.size();
+    }
+    case CA_OP_DENSE: {
+      AttnArgs a{};
+      a.BH = BH; a.N = N; a.D = D; a.c = kDenseTile; a.nc = (N + kDenseTile - 1) / kDenseTile;
+      plan_attend(cv, a, true);
+      return cv.size();
+    }
+  }
+  (void)topk;
+  return SIZE_MAX;
+}
+
+int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, int D,
+               int cluster_size, const ca_cluster_opts* opts, int32_t* perm_q, int32_t* perm_k,
+               float* cent_q, float* cent_k, int32_t* counts, void* ws, size_t ws_bytes,
+               void* stream) {
+  set_error("");
+  if (!Q || !K || !perm_q || !perm_k || !cent_q || !cent_k)
+    return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
+  if (int e = check_common(dt, B, H, N, D)) return e;
+  const int c = cluster_size;
+  if (!supported_c(c)) return fail(CA_ERR_UNSUPPORTED, "cluster_size must be 64, 128 or 256");
+  if (N < c) return fail(CA_ERR_INVALID_ARG, "N must be >= cluster_size");
+  ca_cluster_opts o = {1, 1, 8, 1, 0, nullptr, nullptr};
+  if (opts) o = *opts;
+  if (o.power_iters < 1 || o.power_iters > 1000)
+    return fail(CA_ERR_INVALID_ARG, "power_iters must be in [1, 1000]");
+  if (o.sample_factor < 1 || o.sample_factor > 4096)
+    return fail(CA_ERR_INVALID_ARG, "sample_factor must be in [1, 4096]");
+  if ((2 * B * H) > 65535) return fail(CA_ERR_UNSUPPORTED, "2*B*H must be <= 65535");
+  const int BH = B * H;
+  Carver cv(ws);
+  ClusterWs w = plan_cluster(cv, BH, N, D, c);
+  if (int e = check_ws(ws, ws_bytes, cv.size())) return e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int L = tree_levels_host(N, c);
+  const size_t TN = 2 * (size_t)BH * N;
+
+  launch_metric(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, o.transform, o.query_normalize, w.partial,
+                w.hash, w.Mq, w.Mk, w.kbar, w.gsplit, w.s, st);
+  launch_perm_init(w.permA, 2 * BH, N, st);
+  int32_t* cur = w.permA;
+  int32_t* nxt = w.permB;
+  for (int level = 0; level < L; ++level) {
+    if (o.trace_perm)
+      CA_HIP_CHECK(hipMemcpyAsync(o.trace_perm + level * TN, cur, TN * 4, hipMemcpyDeviceToDevice, st));
+    LevelArgs a;
+    a.Q = Q; a.K = K; a.dtype = dt == CA_BF16 ? 0 : 1;
+    a.BH = BH; a.N = N; a.D = D; a.c = c; a.level = level;
+    a.transform = o.transform; a.power_iters = o.power_iters; a.sample_factor = o.sample_factor;
+    a.seed = o.seed;
+    a.perm_in = cur; a.perm_out = nxt;
+    a.hash = w.hash; a.s = w.s; a.Mq = w.Mq; a.Mk = w.Mk;
+    a.dir_prev = (level & 1) ? w.dirA : w.dirB;
+    a.dir_cur = (level & 1) ? w.dirB : w.dirA;
+    a.sample_buf = w.sample; a.zbuf = w.zbuf; a.keys = w.keys;
+    a.trace_score = o.trace_score ? o.trace_score + level * TN : nullptr;
+    launch_level(a, st);
+    int32_t* t = cur; cur = nxt; nxt = t;
+  }
+  if (o.trace_perm)
+    CA_HIP_CHECK(hipMemcpyAsync(o.trace_perm + (size_t)L * TN, cur, TN * 4, hipMemcpyDeviceToDevice, st));
+  launch_perm_out(cur, BH, N, perm_q, perm_k, st);
+  launch_centroids(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, c, perm_q, perm_k, cent_q, cent_k,
+                   counts, st);
+  return after_launch();
+}
+
+int ca_route(const float* cent_q, const float* cent_k, int B, int H, int n_qc, int n_kc, int D,
+             int topk, int32_t* blocks, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  set_error("");
+  if (!cent_q || !cent_k || !blocks) return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
+  if (B < 1 || H < 1 || n_qc < 1 || n_kc < 1) return fail(CA_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (!supported_d(D)) return fail(CA_ERR_UNSUPPORTED, "D must be 64 or 128");
+  if (topk < 1 || topk > n_kc) return fail(CA_ERR_INVALID_ARG, "topk must be in [1, n_kc]");
+  if (n_kc > 8192) return fail(CA_ERR_UNSUPPORTED, "n_kc must be <= 8192");
+  if ((int64_t)B * H > 32767 || n_qc > 65535) return fail(CA_ERR_UNSUPPORTED, "too many heads or query clusters");
+  const int BH = B * H;
+  Carver cv(ws);
+  float* sc = scores;
+  if (!sc) {
+    sc = cv.take<float>((size_t)BH * n_qc * n_kc);
+    if (int e = check_ws(ws, ws_bytes, cv.size())) return e;
+  }
+  launch_route(cent_q, cent_k, BH, n_qc, n_kc, D, topk, sc, blocks, static_cast<hipStream_t>(stream));
+  return after_launch();
+}
+
+int ca_attend(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N, int D,
+              const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
+              const int32_t* blocks, int topk, int compensate, float scale, void* O, float* lse,
+              void* ws, size_t ws_bytes, void* stream) {
+  set_error("");
+  if (!Q || !K || !V || !perm_q || !perm_k || !blocks || !O)
+    return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
+  if (int e = check_common(dt, B, H, N, D)) return e;
+  const int c = cluster_size;
+  if (!supported_c(c)) return fail(CA_ERR_UNSUPPORTED, "cluster_size must be 64, 128 or 256");
+  if (N < c) return fail(CA_ERR_INVALID_ARG, "N must be >= cluster_size");
+  const int nc = (N + c - 1) / c;
+  if (nc > 8192) return fail(CA_ERR_UNSUPPORTED, "at most 8192 clusters");
+  if (topk < 1 || topk > nc) return fail(CA_ERR_INVALID_ARG, "topk must be in [1, n_c]");
+  if (!(scale >= 0.0f) || !std::isfinite(scale)) return fail(CA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  AttnArgs a{};
+  a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : 1;
+  a.BH = B * H; a.N = N; a.D = D; a.c = c; a.nc = nc; a.topk = topk;
+  a.compensate = compensate ? 1 : 0;
+  a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
+  a.perm_q = perm_q; a.perm_k = perm_k; a.blocks = blocks; a.O = O; a.lse = lse;
+  a.ev_start = g_prof_start; a.ev_stop = g_prof_stop;
+  Carver cv(ws);
+  plan_attend(cv, a, true);
+  if (int e = check_ws(ws, ws_bytes, cv.size())) return e;
+  launch_attend(a, static_cast<hipStream_t>(stream));
+  return after_launch();
+}
+
+int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N, int D,
+             float scale, void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  set_error("");
+  if (!Q || !K || !V || !O) return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
+  if (int e = check_common(dt, B, H, N, D)) return e;
+  if (!(scale >= 0.0f) || !std::isfinite(scale)) return fail(CA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  AttnArgs a{};
+  a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : 1;
+  a.BH = B * H; a.N = N; a.D = D; a.c = kDenseTile; a.nc = (N + kDenseTile - 1) / kDenseTile;
+  a.topk = a.nc; a.compensate = 0;
+  a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
+  a.O = O; a.lse = lse;
+  a.ev_start = g_prof_start; a.ev_stop = g_prof_stop;
+  Carver cv(ws);
+  plan_attend(cv, a, true);
+  if (int e = check_ws(ws, ws_bytes, cv.size())) return e;
+  launch_dense(a, static_cast<hipStream_t>(stream));
+  return after_launch();
+}
+
+int ca_profile_events(void* start, void* stop) {
+  g_prof_start = (start && stop) ? static_cast<hipEvent_t>(start) : nullptr;
+  g_prof_stop = (start && stop) ? static_cast<hipEvent_t>(stop) : nullptr;
+  return CA_OK;
+}
+
+const char* ca_status_string(int status) {
+  switch (status) {
+    case CA_OK: return "ok";
+    case CA_ERR_INVALID_ARG: return "invalid argument";
+    case CA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case CA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* ca_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

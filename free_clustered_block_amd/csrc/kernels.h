@@ -1,0 +1,79 @@
+// Launch wrappers of the gfx950 kernels (host side, called by ca_api.hip).
+#pragma once
+
+#include "common.h"
+
+namespace ca {
+
+// metric.hip -----------------------------------------------------------------
+int metric_rows_per_chunk(int N);
+// dtype: 0 = bf16, 1 = fp32. partial: [BH][nchunks][2 D D + D] fp32 scratch.
+void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D, int transform,
+                   int query_normalize, float* partial, uint64_t* hash, float* Mq, float* Mk,
+                   float* kbar, uint16_t* gsplit, float* s, hipStream_t st);
+
+// cluster.hip ----------------------------------------------------------------
+struct LevelArgs {
+  const void* Q;
+  const void* K;
+  int dtype;
+  int BH, N, D, c, level;
+  int transform, power_iters, sample_factor;
+  uint64_t seed;
+  const int32_t* perm_in;   // [2 BH][N]
+  int32_t* perm_out;        // [2 BH][N]
+  const uint64_t* hash;     // [2 BH][N] by token
+  const float* s;           // [BH][N]
+  const float* Mq;          // [BH][D][D]
+  const float* Mk;          // [BH][D][D]
+  const float* dir_prev;    // [2 BH][slots/2][D]
+  float* dir_cur;           // [2 BH][slots][D]
+  int32_t* sample_buf;      // [2 BH][N]
+  float* zbuf;              // [2 BH][N]
+  uint32_t* keys;           // [2 BH][N]
+  float* trace_score;       // [2 BH][N] or null
+};
+void launch_level(const LevelArgs& a, hipStream_t st);
+void launch_perm_init(int32_t* perm, int trees, int N, hipStream_t st);
+void launch_perm_out(const int32_t* perm, int BH, int N, int32_t* perm_q, int32_t* perm_k,
+                     hipStream_t st);
+void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, int D, int c,
+                      const int32_t* perm_q, const int32_t* perm_k, float* cent_q, float* cent_k,
+                      int32_t* counts, hipStream_t st);
+
+// route.hip ------------------------------------------------------------------
+void launch_route(const float* cq, const float* ck, int BH, int nq, int nk, int D, int topk,
+                  float* scores, int32_t* blocks, hipStream_t st);
+
+// attn.hip -------------------------------------------------------------------
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  int dtype;
+  int BH, N, D, c, nc, topk, compensate;
+  float scale;
+  const int32_t* perm_q;
+  const int32_t* perm_k;
+  const int32_t* blocks;
+  void* O;
+  float* lse;
+  // scratch (bf16 path)
+  uint16_t* kc;       // [BH][nc][c][D]   keys, cluster-major, zero padded
+  uint16_t* vt;       // [BH][nc][D][c]   values, cluster-major, transposed
+  uint16_t* kbar_hi;  // [BH][ncp][D]
+  uint16_t* kbar_lo;  // [BH][ncp][D]
+  uint16_t* vbar_t;   // [BH][D][ncp]
+  float* logn;        // [BH][ncp]
+  float* kbar32;      // [BH][ncp][D]
+  float* vbar32;      // [BH][ncp][D]
+  // optional events recorded around the main attention kernel
+  hipEvent_t ev_start;
+  hipEvent_t ev_stop;
+};
+// centroid count padded to whole 32-blocks
+CA_HD int attn_ncp(int nc) { return (nc + 31) / 32 * 32; }
+void launch_attend(const AttnArgs& a, hipStream_t st);
+void launch_dense(const AttnArgs& a, hipStream_t st);
+
+}  // namespace ca

@@ -1,0 +1,353 @@
+// Metric pass of the clustering (paper v1 §3.2.2, Eq. 12, 15 and 16):
+//   M_q = Q^T Q / N,  kbar = mean(K),  M_k = K^T K / N - kbar kbar^T,
+//   s_i = (q_i^T G q_i)^{-1/2} with G the query geometry (M_k or I),
+// plus a 64-bit content hash of every token row of Q and K that decides the
+// node subsamples. Second moments and q^T G q run on bf16 MFMA with fp32
+// accumulation (G is split into three bf16 terms so q^T G q keeps fp32
+// accuracy); fp32 inputs take a VALU path.
+#include "kernels.h"
+#include "mfma.h"
+
+namespace ca {
+
+namespace {
+
+constexpr int kMetricTile = 64;   // tokens per LDS tile
+
+// Hash word j of a row: fmix64((j << 32 | w_j) + golden), summed mod 2^64.
+CA_DEV uint64_t hash_word(uint32_t j, uint32_t w) {
+  return fmix64((((uint64_t)j << 32) | (uint64_t)w) + kGolden);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void metric_partial_bf16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int N, int rows_per_chunk,
+    int nchunks, float* __restrict__ partial, uint64_t* __restrict__ hash) {
+  constexpr int TT = kMetricTile;
+  constexpr int NB = D / 32;
+  constexpr int BPW = NB * NB / 4;          // 32x32 blocks per wave
+  constexpr int LDT = TT + 8;               // padded token stride in LDS
+  constexpr int GROUPS = D / 8;             // 16-byte groups per row
+  constexpr int GPT = GROUPS / 4;           // groups per thread
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][D][LDT];
+  __shared__ uint64_t shash[2][4][TT];
+
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int r0 = chunk * rows_per_chunk;
+  const int r1 = min(N, r0 + rows_per_chunk);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
+  const uint16_t* X[2] = {Q + (int64_t)bh * N * D, K + (int64_t)bh * N * D};
+
+  floatx16_t acc[2][BPW];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) acc[t][i] = zero16();
+  float ksum[GPT][8];
+#pragma unroll
+  for (int i = 0; i < GPT; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ksum[i][e] = 0.0f;
+
+  for (int base = r0; base < r1; base += TT) {
+    const int tok = base + l;
+    const bool valid = tok < r1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      uint64_t hp = 0;
+#pragma unroll
+      for (int i = 0; i < GPT; ++i) {
+        const int g = w + 4 * i;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (valid) v = *reinterpret_cast<const u32x4_t*>(X[t] + (int64_t)tok * D + 8 * g);
+        const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sx[t][8 * g + 2 * q][l] = (uint16_t)(ws[q] & 0xFFFFu);
+          sx[t][8 * g + 2 * q + 1][l] = (uint16_t)(ws[q] >> 16);
+          hp += hash_word((uint32_t)(4 * g + q), ws[q]);
+          if (t == 1) {
+            ksum[i][2 * q] += bf16_to_f32((uint16_t)(ws[q] & 0xFFFFu));
+            ksum[i][2 * q + 1] += bf16_to_f32((uint16_t)(ws[q] >> 16));
+          }
+        }
+      }
+      shash[t][w][l] = hp;
+    }
+    __syncthreads();
+    if (tid < 2 * TT) {
+      const int t = tid / TT, j = tid % TT;
+      if (base + j < r1) {
+        uint64_t s = shash[t][0][j] + shash[t][1][j] + shash[t][2][j] + shash[t][3][j];
+        hash[((int64_t)bh * 2 + t) * N + base + j] = fmix64(s);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < TT / 16; ++s) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) {
+          const int b = w * BPW + i, bm = b / NB, bn = b % NB;
+          bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sx[t][bm * 32 + r][s * 16 + h * 8]);
+          bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sx[t][bn * 32 + r][s * 16 + h * 8]);
+          acc[t][i] = mfma32(a, bb, acc[t][i]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  float* out = partial + ((int64_t)bh * nchunks + chunk) * (2 * D * D + D);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int b = w * BPW + i, bm = b / NB, bn = b % NB;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        out[t * D * D + (bm * 32 + c_row(e, h)) * D + bn * 32 + r] = acc[t][i][e];
+    }
+  // key sums: reduce the 64 lanes of each wave (fixed butterfly order)
+#pragma unroll
+  for (int i = 0; i < GPT; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = wave_sum(ksum[i][e]);
+      if (l == 0) out[2 * D * D + 8 * (w + 4 * i) + e] = v;
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void metric_partial_f32(
+    const T* __restrict__ Q, const T* __restrict__ K, int N, int rows_per_chunk, int nchunks,
+    float* __restrict__ partial, uint64_t* __restrict__ hash) {
+  // Plain VALU path: thread e accumulates entries e, e+256, ... of Q^T Q and K^T K.
+  constexpr int TT = 32;
+  __shared__ float sx[2][TT][D];
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int r0 = chunk * rows_per_chunk;
+  const int r1 = min(N, r0 + rows_per_chunk);
+  const int tid = threadIdx.x;
+  const T* X[2] = {Q + (int64_t)bh * N * D, K + (int64_t)bh * N * D};
+  constexpr int PER = (D * D + 255) / 256;
+  float aq[PER], ak[PER];
+  for (int i = 0; i < PER; ++i) aq[i] = ak[i] = 0.0f;
+  float ks = 0.0f;
+  for (int base = r0; base < r1; base += TT) {
+    for (int e = tid; e < 2 * TT * D; e += 256) {
+      const int t = e / (TT * D), rr = (e / D) % TT, dd = e % D;
+      sx[t][rr][dd] = (base + rr < r1) ? load_elem(X[t], (int64_t)(base + rr) * D + dd) : 0.0f;
+    }
+    __syncthreads();
+    if (tid < 2 * TT) {
+      const int t = tid / TT, rr = tid % TT;
+      if (base + rr < r1) {
+        uint64_t s = 0;
+        const T* row = X[t] + (int64_t)(base + rr) * D;
+        const uint32_t* wrow = reinterpret_cast<const uint32_t*>(row);
+        constexpr int W = D * (int)sizeof(T) / 4;
+        for (int j = 0; j < W; ++j) s += hash_word((uint32_t)j, wrow[j]);
+        hash[((int64_t)bh * 2 + t) * N + base + rr] = fmix64(s);
+      }
+    }
+    for (int rr = 0; rr < TT; ++rr) {
+      for (int i = 0; i < PER; ++i) {
+        const int e = tid + 256 * i;
+        if (e < D * D) {
+          const int a = e / D, b = e % D;
+          aq[i] += sx[0][rr][a] * sx[0][rr][b];
+          ak[i] += sx[1][rr][a] * sx[1][rr][b];
+        }
+      }
+      if (tid < D) ks += sx[1][rr][tid];
+    }
+    __syncthreads();
+  }
+  float* out = partial + ((int64_t)bh * nchunks + chunk) * (2 * D * D + D);
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + 256 * i;
+    if (e < D * D) {
+      out[e] = aq[i];
+      out[D * D + e] = ak[i];
+    }
+  }
+  if (tid < D) out[2 * D * D + tid] = ks;
+}
+
+// Sum the chunk partials in chunk order; write M_q, M_k (fp32), kbar and the
+// three-term bf16 split of the query geometry G (M_k, or I without transform).
+template <int D>
+__global__ __launch_bounds__(256) void metric_reduce(const float* __restrict__ partial,
+                                                     int nchunks, int N, int transform,
+                                                     float* __restrict__ Mq,
+                                                     float* __restrict__ Mk,
+                                                     float* __restrict__ kbar,
+                                                     uint16_t* __restrict__ gsplit) {
+  const int bh = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= D * D) return;
+  const int a = e / D, b = e % D;
+  const float* p = partial + (int64_t)bh * nchunks * (2 * D * D + D);
+  float sq = 0.0f, sk = 0.0f, ka = 0.0f, kb = 0.0f;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const float* pc = p + (int64_t)ch * (2 * D * D + D);
+    sq += pc[e];
+    sk += pc[D * D + e];
+    ka += pc[2 * D * D + a];
+    kb += pc[2 * D * D + b];
+  }
+  const float invN = 1.0f / (float)N;
+  const float mq = sq * invN;
+  const float kma = ka * invN, kmb = kb * invN;
+  const float mk = sk * invN - kma * kmb;
+  Mq[(int64_t)bh * D * D + e] = mq;
+  Mk[(int64_t)bh * D * D + e] = mk;
+  if (a == 0) kbar[(int64_t)bh * D + b] = kmb;
+  const float g = transform ? mk : (a == b ? 1.0f : 0.0f);
+  const uint16_t hi = f32_to_bf16(g);
+  const float r1 = g - bf16_to_f32(hi);
+  const uint16_t mid = f32_to_bf16(r1);
+  const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+  uint16_t* gs = gsplit + (int64_t)bh * 3 * D * D;
+  gs[e] = hi;
+  gs[D * D + e] = mid;
+  gs[2 * D * D + e] = lo;
+}
+
+// s_i = (q_i^T G q_i)^{-1/2} (0 if q^T G q <= 0). Y = Q G^T on MFMA with G as
+// hi + mid + lo bf16 terms, then t_i = sum_n Y[i][n] Q[i][n].
+template <int D>
+__global__ __launch_bounds__(256) void qnorm_bf16(const uint16_t* __restrict__ Q, int N,
+                                                  const uint16_t* __restrict__ gsplit,
+                                                  float* __restrict__ s_out) {
+  constexpr int NB = D / 32;
+  constexpr int KS = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t sq[4][32][D + 8];
+  const int bh = blockIdx.y;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, r = l & 31;
+  const int t0 = blockIdx.x * 128 + w * 32;
+  const uint16_t* Qh = Q + (int64_t)bh * N * D;
+  const uint16_t* G = gsplit + (int64_t)bh * 3 * D * D;
+
+  bf16x8_t qa[KS];
+  const int tok = t0 + r;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (tok < N) v = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)tok * D + s * 16 + h * 8);
+    qa[s] = as_bf16x8(v);
+    *reinterpret_cast<u32x4_t*>(&sq[w][r][s * 16 + h * 8]) = v;
+  }
+  __syncthreads();
+  float part[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) part[i] = 0.0f;
+#pragma unroll
+  for (int bn = 0; bn < NB; ++bn) {
+    floatx16_t y = zero16();
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        bf16x8_t gb = *reinterpret_cast<const bf16x8_t*>(
+            G + (int64_t)p * D * D + (int64_t)(bn * 32 + r) * D + s * 16 + h * 8);
+        y = mfma32(qa[s], gb, y);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[i] += y[i] * bf16_to_f32(sq[w][c_row(i, h)][bn * 32 + r]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float v = part[i];
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, 64);
+    part[i] = v;
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tk = t0 + c_row(i, h);
+      if (tk < N) {
+        const float t = part[i];
+        s_out[(int64_t)bh * N + tk] = t > 0.0f ? 1.0f / sqrtf(t) : 0.0f;
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void qnorm_f32(const T* __restrict__ Q, int N,
+                                                 const float* __restrict__ Mk, int transform,
+                                                 float* __restrict__ s_out) {
+  __shared__ float G[D][D];
+  const int bh = blockIdx.y;
+  for (int e = threadIdx.x; e < D * D; e += 256)
+    G[e / D][e % D] = transform ? Mk[(int64_t)bh * D * D + e] : ((e / D) == (e % D) ? 1.0f : 0.0f);
+  __syncthreads();
+  const int tok = blockIdx.x * 256 + threadIdx.x;
+  if (tok >= N) return;
+  const T* q = Q + ((int64_t)bh * N + tok) * D;
+  float qv[D];
+  for (int j = 0; j < D; ++j) qv[j] = load_elem(q, j);
+  float t = 0.0f;
+  for (int j = 0; j < D; ++j) {
+    float y = 0.0f;
+    for (int k = 0; k < D; ++k) y += G[j][k] * qv[k];
+    t += qv[j] * y;
+  }
+  s_out[(int64_t)bh * N + tok] = t > 0.0f ? 1.0f / sqrtf(t) : 0.0f;
+}
+
+__global__ void fill_f32(float* p, int64_t n, float v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+}  // namespace
+
+int metric_rows_per_chunk(int N) {
+  // ~4096 rows per workgroup, a multiple of the 64-token tile
+  int chunks = (N + 4095) / 4096;
+  int rows = (N + chunks - 1) / chunks;
+  return (rows + kMetricTile - 1) / kMetricTile * kMetricTile;
+}
+
+void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D, int transform,
+                   int query_normalize, float* partial, uint64_t* hash, float* Mq, float* Mk,
+                   float* kbar, uint16_t* gsplit, float* s, hipStream_t st) {
+  const int rows = metric_rows_per_chunk(N);
+  const int nchunks = (N + rows - 1) / rows;
+  dim3 gp(nchunks, BH);
+  if (dtype == 0) {
+    const uint16_t* q = (const uint16_t*)Q;
+    const uint16_t* k = (const uint16_t*)K;
+    if (D == 64) metric_partial_bf16<64><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash);
+    else metric_partial_bf16<128><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash);
+  } else {
+    const float* q = (const float*)Q;
+    const float* k = (const float*)K;
+    if (D == 64) metric_partial_f32<float, 64><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash);
+    else metric_partial_f32<float, 128><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash);
+  }
+  dim3 gr((D * D + 255) / 256, BH);
+  if (D == 64) metric_reduce<64><<<gr, 256, 0, st>>>(partial, nchunks, N, transform, Mq, Mk, kbar, gsplit);
+  else metric_reduce<128><<<gr, 256, 0, st>>>(partial, nchunks, N, transform, Mq, Mk, kbar, gsplit);
+  if (!query_normalize) {
+    int64_t n = (int64_t)BH * N;
+    fill_f32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(s, n, 1.0f);
+    return;
+  }
+  if (dtype == 0) {
+    dim3 gq((N + 127) / 128, BH);
+    if (D == 64) qnorm_bf16<64><<<gq, 256, 0, st>>>((const uint16_t*)Q, N, gsplit, s);
+    else qnorm_bf16<128><<<gq, 256, 0, st>>>((const uint16_t*)Q, N, gsplit, s);
+  } else {
+    dim3 gq((N + 255) / 256, BH);
+    if (D == 64) qnorm_f32<float, 64><<<gq, 256, 0, st>>>((const float*)Q, N, Mk, transform, s);
+    else qnorm_f32<float, 128><<<gq, 256, 0, st>>>((const float*)Q, N, Mk, transform, s);
+  }
+}
+
+}  // namespace ca

@@ -1,0 +1,199 @@
+/*
+ * ca.h -- C ABI of the ClusterAttention forward path for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method is the one of "ClusterAttention: A training-free speedup of
+ * bidirectional attention" (arXiv 2608.26965): per head, queries and keys are
+ * clustered separately by recursive principal-direction splitting into
+ * clusters of a fixed size c (v1 §3.1, §3.2); every query cluster selects the
+ * top-k key clusters by centroid score (§3.3); queries attend with token
+ * resolution to the selected clusters and, optionally, to every excluded
+ * cluster through its key and value centroids with weight |c|
+ * ("striped mean-compensation", §1.2 Eq. 5-6, App. A Eq. 21-22).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are contiguous, row-major [B, H, N, D] (batch, head, token, dim),
+ *    element type given by ca_dtype. D must be 64 or 128.
+ *  - Every pointer argument is a device pointer owned by the caller unless it
+ *    is documented as a host pointer. The library never allocates device or
+ *    host memory, never frees caller memory and keeps no state between calls
+ *    except a thread-local error string.
+ *  - Scratch memory is passed in as `ws` (device, 256-byte aligned) of
+ *    `ws_bytes` bytes; ca_workspace_size() gives the bytes a call needs.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream): they enqueue kernels and return. The caller synchronises before
+ *    reading outputs. No call performs a device-to-host copy or a host sync,
+ *    so the sequence can be captured in a HIP graph.
+ *  - Inputs are never written. Outputs are completely overwritten.
+ *  - Arguments are validated on the host before anything is enqueued: a
+ *    non-CA_OK return means nothing was launched and no output was touched.
+ *    Errors are reported by return code (no exceptions, no abort); a detail
+ *    string is available from ca_last_error().
+ *  - Results are deterministic: the same inputs give bitwise identical outputs
+ *    (no floating-point atomics; all reductions run in a fixed order).
+ */
+#ifndef CLUSTERATTN_CA_H
+#define CLUSTERATTN_CA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CA_OK = 0,
+  CA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, k out of range, ...   */
+  CA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (D, c, dtype combo) */
+  CA_ERR_WORKSPACE = 3,    /* ws is NULL, misaligned or smaller than needed */
+  CA_ERR_HIP = 4           /* a HIP runtime call failed (see ca_last_error) */
+} ca_status;
+
+typedef enum {
+  CA_BF16 = 0,             /* bfloat16 inputs and outputs, fp32 accumulation */
+  CA_F32 = 1               /* float32 throughout                             */
+} ca_dtype;
+
+typedef enum {
+  CA_OP_CLUSTER = 0,
+  CA_OP_ROUTE = 1,
+  CA_OP_ATTEND = 2,
+  CA_OP_DENSE = 3
+} ca_op;
+
+/*
+ * Options of the clustering (v1 §3.2). Pass NULL for the defaults
+ * {transform=1, query_normalize=1, power_iters=8, sample_factor=1, seed=0,
+ *  trace_perm=NULL, trace_score=NULL}.
+ *
+ *  transform        1: keys are split under the query metric M_q = Q^T Q / N
+ *                   (Eq. 12-14) and queries under the centred key metric
+ *                   M_k = K_c^T K_c / N (Eq. 15); the metric is injected into
+ *                   the power iteration, so no root matrix is formed.
+ *                   0: Euclidean geometry for both.
+ *  query_normalize  1: queries are split as s_i q_i, s_i = (q_i^T G q_i)^-1/2
+ *                   with G the query geometry (the top-k representation of
+ *                   Eq. 16); a query with q^T G q <= 0 gets s_i = 0.
+ *  power_iters      p >= 1, power iterations per split (v1 §3.2.1).
+ *  sample_factor    a >= 1: each node estimates its direction from a
+ *                   Bernoulli sample of expected size min(a D, n) chosen by a
+ *                   64-bit hash of each token's raw input row.
+ *  seed             salt of the sample and of the warm-start vectors.
+ *  trace_perm       optional device buffer int32 [L+1][B*H][2][N]: the
+ *                   permutation before each of the L split levels and the
+ *                   final one (tensor index 0 = queries, 1 = keys). L is
+ *                   ca_tree_levels(N, c).
+ *  trace_score      optional device buffer float [L][B*H][2][N]: the
+ *                   projection of the token at each position at each level;
+ *                   positions inside leaves are left untouched.
+ */
+typedef struct {
+  int transform;
+  int query_normalize;
+  int power_iters;
+  int sample_factor;
+  uint64_t seed;
+  int32_t* trace_perm;
+  float* trace_score;
+} ca_cluster_opts;
+
+/* Number of split levels of the data-independent tree for (N, c): the tree
+ * splits a node of n > c members at the multiple of c closest to n/2 (ties to
+ * the smaller), v1 §3.2.1. Returns -1 for invalid arguments. Host only. */
+int ca_tree_levels(int N, int cluster_size);
+
+/* Bytes of workspace `op` needs for the given sizes (0 if none, SIZE_MAX if
+ * the arguments are invalid). For CA_OP_ROUTE pass N = n_qc and
+ * cluster_size = n_kc (the bytes are only needed when `scores` is NULL);
+ * CA_OP_DENSE ignores cluster_size and topk. Host only. */
+size_t ca_workspace_size(ca_op op, int B, int H, int N, int D, int cluster_size, int topk);
+
+/*
+ * ca_cluster -- recursive PDDP clustering of queries and keys (v1 §3.2.1
+ * "Basic recursive splitting" with the transforms of §3.2.2; the later
+ * revision's §4.1.1 gives the radix split).
+ *
+ * Q, K      [B,H,N,D] of type dt (device, read only).
+ * cluster_size  c in {64, 128, 256}; N >= c; B*H*N < 2^31.
+ * perm_q, perm_k  out int32 [B,H,N]: perm[p] = index of the token at
+ *           cluster-major position p. Cluster j occupies positions
+ *           [j c, j c + n_j); every n_j = c except the last, which holds
+ *           N - (n_c - 1) c (v1 §3.1). Members of a cluster are in ascending
+ *           token order.
+ * cent_q, cent_k  out float [B,H,n_c,D], n_c = ceil(N/c): means of the
+ *           original (untransformed) query / key rows of each cluster.
+ * counts    out int32 [B,H,n_c] or NULL: n_j.
+ */
+int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, int D,
+               int cluster_size, const ca_cluster_opts* opts, int32_t* perm_q,
+               int32_t* perm_k, float* cent_q, float* cent_k, int32_t* counts, void* ws,
+               size_t ws_bytes, void* stream);
+
+/*
+ * ca_route -- centroid scoring and top-k selection (v1 §3.3, Eq. 18).
+ *
+ * cent_q    float [B,H,n_qc,D], cent_k float [B,H,n_kc,D] (device).
+ * topk      1 <= topk <= n_kc; n_kc <= 8192.
+ * blocks    out int32 [B,H,n_qc,topk]: for each query cluster, the indices of
+ *           the topk key clusters with the largest score qbar . kbar (ties to
+ *           the lower index), in ascending order.
+ * scores    out float [B,H,n_qc,n_kc] or NULL: the fp32 score matrix.
+ */
+int ca_route(const float* cent_q, const float* cent_k, int B, int H, int n_qc, int n_kc,
+             int D, int topk, int32_t* blocks, float* scores, void* ws, size_t ws_bytes,
+             void* stream);
+
+/*
+ * ca_attend -- block-sparse attention over the selected clusters with
+ * optional striped mean-compensation (v1 §1.2 Eq. 2 and Eq. 5-6; App. A
+ * Eq. 21-22; v1 §3.1 on the padded remainder cluster).
+ *
+ * Q, K, V   [B,H,N,D] of type dt (device, read only).
+ * perm_q, perm_k  int32 [B,H,N]: cluster-major permutations as produced by
+ *           ca_cluster (any permutation is accepted: e.g. random clusters).
+ * blocks    int32 [B,H,n_c,topk]: selected key clusters per query cluster,
+ *           each in [0, n_c), distinct within a row (as produced by ca_route).
+ * compensate  nonzero: every key cluster not selected by a query's cluster
+ *           enters the query's softmax once, with logit scale*q.kbar_c +
+ *           ln n_c and value vbar_c (centroids of the original K and V rows).
+ * scale     softmax temperature; 0 means 1/sqrt(D).
+ * O         out [B,H,N,D] of type dt, original token order.
+ * lse       out float [B,H,N] or NULL: natural log of the softmax denominator
+ *           (the "attention denominator" of v1 §3.1) including the running
+ *           maximum, i.e. log sum over the attended terms of exp(logit).
+ */
+int ca_attend(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
+              int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
+              const int32_t* blocks, int topk, int compensate, float scale, void* O,
+              float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ca_dense -- dense attention baseline, o_i = sum_j softmax_j(scale q_i.k_j) v_j
+ * (v1 §1.2 Eq. 1). Same layouts and conventions as ca_attend.
+ */
+int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
+             int D, float scale, void* O, float* lse, void* ws, size_t ws_bytes,
+             void* stream);
+
+/*
+ * Profiling hook. When start and stop are non-NULL hipEvent_t handles,
+ * subsequent ca_attend and ca_dense calls made by the calling thread record
+ * `start` on their stream immediately before their main attention kernel and
+ * `stop` immediately after it, so the caller can time that kernel alone with
+ * hipEventElapsedTime. Pass NULL, NULL to switch it off. Returns CA_OK.
+ */
+int ca_profile_events(void* start, void* stop);
+
+/* Static description of a status code. */
+const char* ca_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* ca_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CLUSTERATTN_CA_H */

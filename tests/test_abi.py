@@ -1,0 +1,116 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every
+symbol include/ca.h declares, lays out the same tree as the oracle, sizes its
+workspace, and rejects bad arguments on the host before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle.clusterattn as o
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ca.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import free_clustered_block_amd as ca
+    return ca.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ca_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    import free_clustered_block_amd as ca
+    names = declared_functions()
+    assert set(names) == set(ca.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_tree_levels_match_oracle(lib):
+    for N, c in [(1024, 64), (65536, 128), (32760, 128), (262144, 256), (16384, 64),
+                 (1000, 64), (64, 64), (65, 64), (3 * 64, 64), (7 * 128 + 5, 128)]:
+        levels = o.tree_levels(N, c)
+        want = sum(1 for lv in levels if any(nd.n > c for nd in lv))
+        assert lib.ca_tree_levels(N, c) == want, (N, c)
+    assert lib.ca_tree_levels(0, 64) == -1
+
+
+def test_workspace_sizes(lib):
+    import free_clustered_block_amd as ca
+    SIZE_MAX = 2**64 - 1
+    for op in (ca.OP_CLUSTER, ca.OP_ATTEND, ca.OP_DENSE):
+        n = ca.workspace_size(op, 1, 8, 65536, 64, 128, 64)
+        assert 0 < n < 2**40 and n % 256 == 0
+    assert ca.workspace_size(ca.OP_ROUTE, 1, 8, 512, 64, 512, 64) == 8 * 512 * 512 * 4
+    assert ca.workspace_size(ca.OP_CLUSTER, 1, 1, 10, 64, 64, 1) == SIZE_MAX
+    assert ca.workspace_size(ca.OP_ATTEND, 0, 1, 1024, 64, 64, 1) == SIZE_MAX
+
+
+FAKE = 0x10000   # never dereferenced: every call below fails validation first
+
+
+def _cluster(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, dt=0, B=1, H=1, N=1024, D=64, c=64, opts=None, pq=FAKE, pk=FAKE,
+             cq=FAKE, ck=FAKE, counts=None, ws=FAKE, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.ca_cluster(a["Q"], a["K"], a["dt"], a["B"], a["H"], a["N"], a["D"], a["c"], a["opts"],
+                          a["pq"], a["pk"], a["cq"], a["ck"], a["counts"], a["ws"], a["ws_bytes"],
+                          a["stream"])
+
+
+def _attend(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dt=0, B=1, H=1, N=1024, D=64, pq=FAKE, pk=FAKE, c=64,
+             blocks=FAKE, topk=4, comp=1, scale=0.0, O=FAKE, lse=None, ws=FAKE, ws_bytes=0,
+             stream=None)
+    a.update(kw)
+    return lib.ca_attend(a["Q"], a["K"], a["V"], a["dt"], a["B"], a["H"], a["N"], a["D"], a["pq"],
+                         a["pk"], a["c"], a["blocks"], a["topk"], a["comp"], a["scale"], a["O"],
+                         a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_cluster_rejects_bad_arguments(lib):
+    import free_clustered_block_amd as ca
+    assert _cluster(lib, Q=None) == 1
+    assert _cluster(lib, dt=7) == 1
+    assert _cluster(lib, D=96) == 2
+    assert _cluster(lib, c=100) == 2
+    assert _cluster(lib, N=32) == 1
+    assert _cluster(lib, B=0) == 1
+    assert _cluster(lib, B=2**16, H=2**16) == 2
+    opts = ca._Opts(1, 1, 0, 1, 0, None, None)
+    assert _cluster(lib, opts=ctypes.byref(opts)) == 1
+    opts = ca._Opts(1, 1, 8, 0, 0, None, None)
+    assert _cluster(lib, opts=ctypes.byref(opts)) == 1
+    assert _cluster(lib, ws=None, ws_bytes=0) == 3
+    assert _cluster(lib, ws=FAKE + 8, ws_bytes=2**30) == 3
+    assert _cluster(lib, ws_bytes=100) == 3
+    assert b"workspace" in lib.ca_last_error()
+    assert lib.ca_status_string(3) == b"workspace missing, misaligned or too small"
+
+
+def test_attend_rejects_bad_arguments(lib):
+    assert _attend(lib, blocks=None) == 1
+    assert _attend(lib, topk=0) == 1
+    assert _attend(lib, topk=17) == 1          # n_c = 16
+    assert _attend(lib, scale=-1.0) == 1
+    assert _attend(lib, scale=float("nan")) == 1
+    assert _attend(lib, D=32) == 2
+    assert _attend(lib, c=32) == 2
+    assert _attend(lib, ws_bytes=10) == 3
+
+
+def test_route_and_dense_reject_bad_arguments(lib):
+    assert lib.ca_route(FAKE, FAKE, 1, 1, 8, 8, 64, 9, FAKE, None, FAKE, 0, None) == 1
+    assert lib.ca_route(FAKE, FAKE, 1, 1, 8, 8, 64, 0, FAKE, None, FAKE, 0, None) == 1
+    assert lib.ca_route(FAKE, FAKE, 1, 1, 8, 9000, 64, 4, FAKE, None, FAKE, 0, None) == 2
+    assert lib.ca_route(FAKE, FAKE, 1, 1, 8, 8, 64, 4, FAKE, None, FAKE, 16, None) == 3
+    assert lib.ca_dense(FAKE, FAKE, None, 0, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 0, None) == 1
+    assert lib.ca_dense(FAKE, FAKE, FAKE, 0, 1, 1, 128, 80, 0.0, FAKE, None, FAKE, 0, None) == 2
+    assert lib.ca_dense(FAKE, FAKE, FAKE, 0, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 8, None) == 3
