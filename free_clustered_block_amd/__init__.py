@@ -40,7 +40,7 @@ class _Opts(ctypes.Structure):
     _fields_ = [("transform", ctypes.c_int), ("query_normalize", ctypes.c_int),
                 ("power_iters", ctypes.c_int), ("sample_factor", ctypes.c_int),
                 ("seed", ctypes.c_uint64), ("trace_perm", ctypes.c_void_p),
-                ("trace_score", ctypes.c_void_p)]
+                ("trace_score", ctypes.c_void_p), ("trace_dir", ctypes.c_void_p)]
 
 
 def load() -> ctypes.CDLL:
@@ -180,6 +180,7 @@ class ClusterResult:
     counts: object
     trace_perm: object = None
     trace_score: object = None
+    trace_dir: object = None
 
 
 def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = True,
@@ -196,13 +197,15 @@ def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = Tru
     cent_q = torch.empty((B, H, n_c, D), dtype=torch.float32, device=dev)
     cent_k = torch.empty_like(cent_q)
     counts = torch.empty((B, H, n_c), dtype=torch.int32, device=dev)
-    tp = ts = None
+    tp = ts = td = None
     if trace:
         L = tree_levels(N, c)
+        S = 1 << max(L - 1, 0)
         tp = torch.full((L + 1, B * H, 2, N), -1, dtype=torch.int32, device=dev)
         ts = torch.full((max(L, 1), B * H, 2, N), float("nan"), dtype=torch.float32, device=dev)
+        td = torch.full((max(L, 1), B * H, 2, S, D), float("nan"), dtype=torch.float32, device=dev)
     opts = _Opts(int(transform), int(query_normalize), power_iters, sample_factor,
-                 seed & ((1 << 64) - 1), _ptr(tp), _ptr(ts))
+                 seed & ((1 << 64) - 1), _ptr(tp), _ptr(ts), _ptr(td))
     nbytes = workspace_size(OP_CLUSTER, B, H, N, D, c)
     ws = _ws(nbytes, dev, workspace)
     st = load().ca_cluster(Q.data_ptr(), K.data_ptr(), _dtype_code(Q), B, H, N, D, c,
@@ -210,7 +213,7 @@ def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = Tru
                            cent_q.data_ptr(), cent_k.data_ptr(), counts.data_ptr(),
                            _ptr(ws), nbytes, _stream_ptr(dev))
     _check(st)
-    return ClusterResult(perm_q, perm_k, cent_q, cent_k, counts, tp, ts)
+    return ClusterResult(perm_q, perm_k, cent_q, cent_k, counts, tp, ts, td)
 
 
 def route(cent_q, cent_k, topk: int, *, return_scores: bool = False, workspace=None):

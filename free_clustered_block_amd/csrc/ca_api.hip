@@ -43,6 +43,8 @@ struct ClusterWs {
   uint32_t* keys;
   float *dirA, *dirB;
   int32_t* sample;
+  int32_t* chunk_cnt;
+  int32_t* stok;
   float* zbuf;
 };
 
@@ -66,6 +68,8 @@ ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c) {
   w.dirA = cv.take<float>(T * slots * D);
   w.dirB = cv.take<float>(T * slots * D);
   w.sample = cv.take<int32_t>(T * N);
+  w.chunk_cnt = cv.take<int32_t>(T * ((N + c - 1) / c));
+  w.stok = cv.take<int32_t>(T * N);
   w.zbuf = cv.take<float>(T * N);
   return w;
 }
@@ -178,7 +182,8 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   const int c = cluster_size;
   if (!supported_c(c)) return fail(CA_ERR_UNSUPPORTED, "cluster_size must be 64, 128 or 256");
   if (N < c) return fail(CA_ERR_INVALID_ARG, "N must be >= cluster_size");
-  ca_cluster_opts o = {1, 1, 8, 1, 0, nullptr, nullptr};
+  if ((N + c - 1) / c > 8192) return fail(CA_ERR_UNSUPPORTED, "at most 8192 clusters");
+  ca_cluster_opts o = {1, 1, 8, 1, 0, nullptr, nullptr, nullptr};
   if (opts) o = *opts;
   if (o.power_iters < 1 || o.power_iters > 1000)
     return fail(CA_ERR_INVALID_ARG, "power_iters must be in [1, 1000]");
@@ -210,8 +215,12 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     a.hash = w.hash; a.s = w.s; a.Mq = w.Mq; a.Mk = w.Mk;
     a.dir_prev = (level & 1) ? w.dirA : w.dirB;
     a.dir_cur = (level & 1) ? w.dirB : w.dirA;
-    a.sample_buf = w.sample; a.zbuf = w.zbuf; a.keys = w.keys;
+    a.nchunks = (N + c - 1) / c;
+    a.sample_buf = w.sample; a.chunk_cnt = w.chunk_cnt; a.zbuf_tok = w.stok;
+    a.zbuf = w.zbuf; a.keys = w.keys;
     a.trace_score = o.trace_score ? o.trace_score + level * TN : nullptr;
+    a.trace_slots = L > 0 ? (1 << (L - 1)) : 1;
+    a.trace_dir = o.trace_dir ? o.trace_dir + (size_t)level * 2 * BH * a.trace_slots * D : nullptr;
     launch_level(a, st);
     int32_t* t = cur; cur = nxt; nxt = t;
   }

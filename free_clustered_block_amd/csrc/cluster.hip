@@ -21,118 +21,219 @@ namespace ca {
 namespace {
 
 // ----------------------------------------------------------------------------
-// Direction of each node
+// Node subsample (Bernoulli at rate min(1, a D / n) on the content hash):
+// one workgroup per c positions writes its sampled tokens, compacted in
+// position order, at the chunk's own offset, and their count. A node's sample
+// is the concatenation of its chunks' lists, so it is independent of the
+// launch order and of the number of workgroups.
 // ----------------------------------------------------------------------------
 
-template <typename T>
-struct DirLds;
+constexpr int kSampleSpan = 1024;   // positions per workgroup (a multiple of every c)
 
-template <int D, typename T>
-constexpr int dir_cap() {
-  // sample rows kept in LDS: 48 KB of row storage
-  return (48 * 1024) / (D * (int)sizeof(T));
-}
-
-// Row r of the sample (r < m) as float, read from LDS when cached.
-template <int D, typename T>
-struct SampleRows {
-  const T* X;            // token rows of this head and tensor
-  const int32_t* list;   // sample token ids
-  const float* s;        // per-token scale (queries) or null
-  const T* lds;          // [cap][D + pad]
-  const float* lds_s;    // [cap]
-  int cap, pitch;
-
-  CA_DEV float scale(int r) const {
-    if (r < cap) return lds_s[r];
-    return s ? s[list[r]] : 1.0f;
-  }
-  CA_DEV float elem(int r, int j) const {
-    if (r < cap) return load_elem(lds, (int64_t)r * pitch + j);
-    return load_elem(X, (int64_t)list[r] * D + j);
-  }
-};
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void pddp_dir(LevelArgs a) {
-  constexpr int CAP = dir_cap<D, T>();
-  constexpr int PITCH = D + (sizeof(T) == 2 ? 2 : 1);   // rotate banks between rows
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* srow = reinterpret_cast<T*>(smem);
-  float* ss = reinterpret_cast<float*>(smem + (size_t)CAP * PITCH * sizeof(T));
-  float* sz = ss + CAP;          // z_r for cached rows
-  float* su = sz + CAP;          // u            [D]
-  float* su0 = su + D;           // warm start   [D]
-  float* sw = su0 + D;           // w            [D]
-  float* smean = sw + D;         // sample mean  [D]
-  float* sred = smean + D;       // reductions   [16]
-  int* scnt = reinterpret_cast<int*>(sred + 16);   // [16]
-
-  const int tree = blockIdx.y, slot = blockIdx.x;
-  const int bh = tree >> 1, tensor = tree & 1;
-  int off, n;
-  if (!node_at(a.N, a.c, a.level, slot, &off, &n) || n <= a.c) return;
-
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const T* X = reinterpret_cast<const T*>(tensor == 0 ? a.Q : a.K) + (int64_t)bh * a.N * D;
-  const float* svec = tensor == 0 ? a.s + (int64_t)bh * a.N : nullptr;
-  const int32_t* perm = a.perm_in + (int64_t)tree * a.N + off;
-  const uint64_t* hash = a.hash + (int64_t)tree * a.N;
-  int32_t* list = a.sample_buf + (int64_t)tree * a.N + off;
-  float* zg = a.zbuf + (int64_t)tree * a.N + off;
-
-  // --- subsample: Bernoulli at rate min(1, a D / n) on the content hash ----
+__global__ __launch_bounds__(256) void pddp_sample(LevelArgs a) {
+  __shared__ int wcnt[4];
+  const int tree = blockIdx.y;
+  const int tensor = tree & 1;
+  const int tid = threadIdx.x, w = tid >> 6;
   uint64_t salt = 0;
   salt = chain_step(salt, a.seed);
   salt = chain_step(salt, kDomainSample);
   salt = chain_step(salt, (uint64_t)tensor);
   salt = chain_step(salt, (uint64_t)a.level);
-  const uint64_t ad = (uint64_t)a.sample_factor * D;
-  const bool take_all = ad >= (uint64_t)n;
-  const uint64_t thr = take_all ? 0 : ((ad << 32) / (uint64_t)n);
-  int m = 0;
-  for (int base = 0; base < n; base += 256) {
-    const int i = base + tid;
-    bool acc = false;
-    int tok = 0;
-    if (i < n) {
-      tok = perm[i];
-      acc = take_all || ((fmix64(hash[tok] ^ salt) >> 32) < thr);
+  const uint64_t ad = (uint64_t)a.sample_factor * a.D;
+  const int32_t* perm = a.perm_in + (int64_t)tree * a.N;
+  const uint64_t* hash = a.hash + (int64_t)tree * a.N;
+  // four slabs of 256 positions; a chunk of c <= 256 positions lies in one slab
+  int tok[4];
+  bool flag[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int p = blockIdx.x * kSampleSpan + k * 256 + tid;
+    flag[k] = false;
+    tok[k] = 0;
+    if (p < a.N) {
+      int off, n, idx;
+      const int depth = node_of(a.N, a.c, a.level, p, &off, &n, &idx);
+      if (depth == a.level && n > a.c) {
+        tok[k] = perm[p];
+        const bool take_all = ad >= (uint64_t)n;
+        const uint64_t thr = take_all ? 0 : ((ad << 32) / (uint64_t)n);
+        flag[k] = take_all || ((fmix64(hash[tok[k]] ^ salt) >> 32) < thr);
+      }
     }
+  }
+  const int waves_per_chunk = a.c >> 6;   // c in {64, 128, 256}
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int p = blockIdx.x * kSampleSpan + k * 256 + tid;
     uint64_t bal;
-    const int pre = lane_prefix(acc, &bal);
-    if (l == 0) scnt[w] = __popcll(bal);
+    const int pre = lane_prefix(flag[k], &bal);
+    if ((tid & 63) == 0) wcnt[w] = __popcll(bal);
     __syncthreads();
-    int wbase = 0;
-    for (int q = 0; q < w; ++q) wbase += scnt[q];
-    int tot = 0;
-    for (int q = 0; q < 4; ++q) tot += scnt[q];
-    if (acc) list[m + wbase + pre] = tok;
-    m += tot;
+    const int w0 = (w / waves_per_chunk) * waves_per_chunk;   // first wave of this chunk
+    int base = 0, tot = 0;
+    for (int q = w0; q < w0 + waves_per_chunk; ++q) {
+      if (q < w) base += wcnt[q];
+      tot += wcnt[q];
+    }
+    const int chunk = p / a.c;
+    if (flag[k]) a.sample_buf[(int64_t)tree * a.N + (int64_t)chunk * a.c + base + pre] = tok[k];
+    if (p < a.N && (p % a.c) == 0) a.chunk_cnt[(int64_t)tree * a.nchunks + chunk] = tot;
     __syncthreads();
   }
-  const int32_t* rows = list;
-  if (m < 2) {   // fewer than two sampled rows: use the whole node
-    rows = perm;
-    m = n;
-  }
+}
 
-  // --- cache the first CAP rows in LDS ------------------------------------
-  const int mc = m < CAP ? m : CAP;
-  for (int e = tid; e < mc * D; e += 256) {
-    const int r = e / D, j = e % D;
-    srow[r * PITCH + j] = X[(int64_t)rows[r] * D + j];
+// ----------------------------------------------------------------------------
+// Direction of each node: p power iterations u <- M C u / |M C u| from the
+// warm start, C the centred covariance of the node's sample, M the metric of
+// the tensor (injected; no root matrix). One workgroup of 256 threads per
+// node; the first CAP sample rows live in LDS, M lives in registers.
+// ----------------------------------------------------------------------------
+
+template <int D, typename T>
+struct DirCfg {
+  static constexpr int TPR = 256 / D;          // threads per row (z) and per M row
+  static constexpr int EPT = D / TPR;          // elements per thread
+  static constexpr int G = 256 / D;            // row groups for column sums
+  static constexpr int PITCH = D + 16 / (int)sizeof(T);   // padded row (elements)
+  static constexpr int CAP = (sizeof(T) == 2 ? 56 * 1024 : 96 * 1024) / (PITCH * (int)sizeof(T));
+  static constexpr size_t row_bytes = (size_t)CAP * PITCH * sizeof(T);
+  // floats after the rows: s[CAP], z[CAP], mean[D], u[D], w[D], u0[D], part[G][D], red[16]
+  // without the chunk prefix array, whose length depends on the level
+  static constexpr size_t smem = row_bytes + (size_t)(2 * CAP + 4 * D + G * D + 16) * 4 + 16 * 4;
+};
+
+template <typename T>
+CA_DEV void load_vec(const T* p, float* out, int n) {
+  for (int e = 0; e < n; ++e) out[e] = load_elem(p, e);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pddp_dir(LevelArgs a) {
+  using Cfg = DirCfg<D, T>;
+  constexpr int TPR = Cfg::TPR, EPT = Cfg::EPT, G = Cfg::G, PITCH = Cfg::PITCH, CAP = Cfg::CAP;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T* srow = reinterpret_cast<T*>(smem);
+  float* ss = reinterpret_cast<float*>(smem + Cfg::row_bytes);
+  float* sz = ss + CAP;
+  float* smean = sz + CAP;
+  float* su = smean + D;
+  float* sw = su + D;
+  float* su0 = sw + D;
+  float* spart = su0 + D;          // [G][D]
+  float* sred = spart + G * D;     // [16]
+  int* spre = reinterpret_cast<int*>(sred + 16 + 16);   // chunk prefix sums [nch + 1]
+
+  const int tree = blockIdx.y, slot = blockIdx.x;
+  const int bh = tree >> 1, tensor = tree & 1;
+  int off, n;
+  if (!node_at(a.N, a.c, a.level, slot, &off, &n) || n <= a.c) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const T* X = reinterpret_cast<const T*>(tensor == 0 ? a.Q : a.K) + (int64_t)bh * a.N * D;
+  const float* svec = tensor == 0 ? a.s + (int64_t)bh * a.N : nullptr;
+  const int32_t* perm = a.perm_in + (int64_t)tree * a.N + off;
+  int32_t* stok = a.zbuf_tok + (int64_t)tree * a.N + off;   // the node's sample tokens
+
+  auto block_sum = [&](float v) -> float {
+    v = wave_sum(v);
+    __syncthreads();
+    if (l == 0) sred[w] = v;
+    __syncthreads();
+    return sred[0] + sred[1] + sred[2] + sred[3];
+  };
+
+  // --- gather the sample: prefix over the node's chunk counts ---------------
+  const int ch0 = off / a.c;
+  const int nch = (n + a.c - 1) / a.c;
+  const int32_t* cnt = a.chunk_cnt + (int64_t)tree * a.nchunks + ch0;
+  {
+    // per-thread contiguous groups, then a block scan of the group totals
+    const int per = (nch + 255) / 256;
+    const int g0 = tid * per;
+    int gs = 0;
+    for (int k = 0; k < per; ++k)
+      if (g0 + k < nch) gs += cnt[g0 + k];
+    // block exclusive scan of gs
+    int inc = gs;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(inc, d, 64);
+      if (l >= d) inc += y;
+    }
+    if (l == 63) reinterpret_cast<int*>(sred)[w] = inc;
+    __syncthreads();
+    int wb = 0;
+    for (int q = 0; q < w; ++q) wb += reinterpret_cast<int*>(sred)[q];
+    int run = wb + inc - gs;
+    for (int k = 0; k < per; ++k)
+      if (g0 + k < nch) { spre[g0 + k] = run; run += cnt[g0 + k]; }
+    if (tid == 255) spre[nch] = run;
+    __syncthreads();
   }
-  for (int r = tid; r < mc; r += 256) ss[r] = svec ? svec[rows[r]] : 1.0f;
+  int m = spre[nch];
+  const bool whole = m < 2;     // fewer than two sampled rows: the whole node
+  if (whole) m = n;
   __syncthreads();
-  SampleRows<D, T> S{X, rows, svec, srow, ss, CAP, PITCH};
+  const int32_t* lists = a.sample_buf + (int64_t)tree * a.N;
+  for (int r = tid; r < m; r += 256) {
+    int tok;
+    if (whole) {
+      tok = perm[r];
+    } else {
+      int lo = 0, hi = nch - 1;     // last chunk k with spre[k] <= r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (spre[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      tok = lists[(int64_t)(ch0 + lo) * a.c + (r - spre[lo])];
+    }
+    stok[r] = tok;
+    if (r < CAP) {
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(X + (int64_t)tok * D);
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(srow + r * PITCH);
+#pragma unroll 4
+      for (int g = 0; g < D * (int)sizeof(T) / 16; ++g) dst[g] = src[g];
+      ss[r] = svec ? svec[tok] : 1.0f;
+    }
+  }
+  // M slice into registers: row jm, columns [qm EPT, (qm+1) EPT)
+  const int jm = tid / TPR, qm = tid % TPR;
+  const float* M = (tensor == 0 ? a.Mk : a.Mq) + (int64_t)bh * D * D;
+  float mreg[EPT];
+  if (a.transform) {
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4) {
+      const floatx4_t v = *reinterpret_cast<const floatx4_t*>(M + (int64_t)jm * D + qm * EPT + e);
+      mreg[e] = v[0]; mreg[e + 1] = v[1]; mreg[e + 2] = v[2]; mreg[e + 3] = v[3];
+    }
+  }
+  __syncthreads();
 
-  // --- sample mean ----------------------------------------------------------
-  const float inv_m = 1.0f / (float)m;
-  if (tid < D) {
+  // Rows r < mc live in LDS, rows r >= mc (only when the sample exceeds CAP)
+  // are read from global memory; the two ranges run as separate loops so that
+  // every load has a definite address space.
+  const int mc = m < CAP ? m : CAP;
+  const int64_t zoff = (int64_t)tree * a.N + off;
+
+  // --- sample mean (column j summed in row order by group, then groups) -----
+  const int jc = tid % D, gc = tid / D;
+  {
     float acc = 0.0f;
-    for (int r = 0; r < m; ++r) acc += S.scale(r) * S.elem(r, tid);
-    smean[tid] = acc * inv_m;
+    int r = gc;
+#pragma unroll 4
+    for (; r < mc; r += G) acc += ss[r] * load_elem(srow, (int64_t)r * PITCH + jc);
+    for (; r < m; r += G) {
+      const int tok = stok[r];
+      acc += (svec ? svec[tok] : 1.0f) * load_elem(X, (int64_t)tok * D + jc);
+    }
+    spart[gc * D + jc] = acc;
+    __syncthreads();
+    if (tid < D) {
+      float s = 0.0f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) s += spart[g * D + tid];
+      smean[tid] = s / (float)m;
+    }
   }
 
   // --- warm start: normalise(parent + unit random vector) ------------------
@@ -151,15 +252,8 @@ __global__ __launch_bounds__(256) void pddp_dir(LevelArgs a) {
     su0[tid] = rj - 2.0f;
   }
   __syncthreads();
-  auto block_sum = [&](float v) -> float {
-    v = wave_sum(v);
-    __syncthreads();
-    if (l == 0) sred[w] = v;
-    __syncthreads();
-    return sred[0] + sred[1] + sred[2] + sred[3];
-  };
   {
-    float r = tid < D ? su0[tid] : 0.0f;
+    const float r = tid < D ? su0[tid] : 0.0f;
     const float nr = sqrtf(block_sum(r * r));
     float rh = r / nr;
     if (a.level > 0) {
@@ -172,57 +266,98 @@ __global__ __launch_bounds__(256) void pddp_dir(LevelArgs a) {
   }
   __syncthreads();
 
-  // --- power iteration: u <- M C u / |M C u| ------------------------------
-  const float* M = (tensor == 0 ? a.Mk : a.Mq) + (int64_t)bh * D * D;
+  // per-thread slices of u and of the mean for the row dots
+  const int qz = tid % TPR;
+  float mz[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) mz[e] = smean[qz * EPT + e];
+  const float mcol = smean[jc];
+  const float inv_m = 1.0f / (float)m;
+
   bool fallback = false;
   for (int it = 0; it < a.power_iters; ++it) {
-    // z_r = (x_r - mean) . u
-    for (int r = tid; r < m; r += 256) {
-      const float sc = S.scale(r);
+    float uz[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) uz[e] = su[qz * EPT + e];
+    // z_r = (s_r x_r - mean) . u : TPR threads per row
+    for (int rb = 0; rb < m; rb += 256 / TPR) {
+      const int r = rb + tid / TPR;
       float acc = 0.0f;
-      for (int jj = 0; jj < D; ++jj) {
-        const int j = (jj + r) & (D - 1);
-        acc += (sc * S.elem(r, j) - smean[j]) * su[j];
+      if (r < mc) {
+        const float s = ss[r];
+        const T* row = srow + r * PITCH + qz * EPT;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) acc = fmaf(fmaf(s, load_elem(row, e), -mz[e]), uz[e], acc);
+      } else if (r < m) {
+        const int tok = stok[r];
+        const float s = svec ? svec[tok] : 1.0f;
+        const T* row = X + (int64_t)tok * D + qz * EPT;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) acc = fmaf(fmaf(s, load_elem(row, e), -mz[e]), uz[e], acc);
       }
-      if (r < CAP) sz[r] = acc; else zg[r] = acc;
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+      if (qz == 0) {
+        if (r < mc) sz[r] = acc;
+        else if (r < m) a.zbuf[zoff + r] = acc;
+      }
     }
     __syncthreads();
-    // w = (1/m) sum_r z_r (x_r - mean)
-    if (tid < D) {
+    // w_j = (1/m) sum_r z_r (s_r x_rj - mean_j): column j, rows of group gc
+    {
       float acc = 0.0f;
-      for (int r = 0; r < m; ++r) {
-        const float zr = r < CAP ? sz[r] : zg[r];
-        acc += zr * (S.scale(r) * S.elem(r, tid) - smean[tid]);
+      int r = gc;
+#pragma unroll 4
+      for (; r < mc; r += G)
+        acc = fmaf(sz[r], fmaf(ss[r], load_elem(srow, (int64_t)r * PITCH + jc), -mcol), acc);
+      for (; r < m; r += G) {
+        const int tok = stok[r];
+        const float s = svec ? svec[tok] : 1.0f;
+        acc = fmaf(a.zbuf[zoff + r], fmaf(s, load_elem(X, (int64_t)tok * D + jc), -mcol), acc);
       }
-      sw[tid] = acc * inv_m;
+      spart[gc * D + jc] = acc;
     }
     __syncthreads();
-    // u' = M w
-    float un = 0.0f;
     if (tid < D) {
-      if (a.transform) {
-        float acc = 0.0f;
-        for (int k = 0; k < D; ++k) acc += M[(int64_t)k * D + tid] * sw[k];
-        un = acc;
-      } else {
-        un = sw[tid];
-      }
+      float s = 0.0f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) s += spart[g * D + tid];
+      sw[tid] = s * inv_m;
     }
-    const float nn = block_sum(un * un);
+    __syncthreads();
+    // u'_j = sum_k M[j][k] w_k : TPR threads per row of M
+    float un;
+    if (a.transform) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) acc = fmaf(mreg[e], sw[qm * EPT + e], acc);
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+      un = acc;
+    } else {
+      un = sw[jm];
+    }
+    const float contrib = qm == 0 ? un * un : 0.0f;
+    const float nn = block_sum(contrib);
     if (nn == 0.0f) { fallback = true; break; }
-    if (tid < D) su[tid] = un / sqrtf(nn);
+    if (qm == 0) su[jm] = un / sqrtf(nn);
     __syncthreads();
   }
   __syncthreads();
   float* out = a.dir_cur + ((int64_t)tree * (1 << a.level) + slot) * D;
-  if (tid < D) out[tid] = fallback ? su0[tid] : su[tid];
+  if (tid < D) {
+    const float v = fallback ? su0[tid] : su[tid];
+    out[tid] = v;
+    if (a.trace_dir) a.trace_dir[((int64_t)tree * a.trace_slots + slot) * D + tid] = v;
+  }
 }
 
+// LDS of pddp_dir at a level: fixed part + chunk prefix sums of the largest node
 template <typename T, int D>
-size_t dir_smem() {
-  constexpr int CAP = dir_cap<D, T>();
-  constexpr int PITCH = D + (sizeof(T) == 2 ? 2 : 1);
-  return (size_t)CAP * PITCH * sizeof(T) + (size_t)(2 * CAP + 4 * D + 16) * 4 + 16 * 4;
+size_t dir_smem(int N, int c, int level) {
+  const int64_t nmax = ((int64_t)N >> level) + 2 * (int64_t)c;   // bounds every node at the level
+  const int64_t nch = (nmax + c - 1) / c;
+  return DirCfg<D, T>::smem + (size_t)(nch + 2) * 4;
 }
 
 // ----------------------------------------------------------------------------
@@ -421,7 +556,9 @@ __global__ void perm_out(const int32_t* perm, int BH, int N, int32_t* pq, int32_
   pk[i] = perm[(2 * bh + 1) * N + p];
 }
 
-// Means of the original rows of every cluster; rows summed in position order.
+// Means of the original rows of every cluster. Thread (row slot, group g)
+// sums 16-byte groups of rows slot, slot + S, ... in order; the S partial sums
+// of a group are then added in slot order.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void centroids_kernel(const T* __restrict__ Q,
                                                         const T* __restrict__ K, int N, int c,
@@ -430,25 +567,47 @@ __global__ __launch_bounds__(256) void centroids_kernel(const T* __restrict__ Q,
                                                         float* __restrict__ cq,
                                                         float* __restrict__ ck,
                                                         int32_t* __restrict__ counts) {
-  constexpr int G = 256 / D;   // row groups
-  __shared__ float part[G][D];
+  constexpr int EPG = 16 / (int)sizeof(T);   // elements per 16-byte group
+  constexpr int NG = D / EPG;                // groups per row
+  constexpr int S = 256 / NG;                // row slots
+  __shared__ float part[S][D + 1];
+  __shared__ int stoks[256];
   const int j = blockIdx.x, bh = blockIdx.y, tensor = blockIdx.z;
   const int nc = (N + c - 1) / c;
   const int nj = min(c, N - j * c);
   const T* X = (tensor == 0 ? Q : K) + (int64_t)bh * N * D;
   const int32_t* perm = (tensor == 0 ? pq : pk) + (int64_t)bh * N + (int64_t)j * c;
-  const int d = threadIdx.x % D, g = threadIdx.x / D;
-  float acc = 0.0f;
-  for (int r = g; r < nj; r += G) acc += load_elem(X, (int64_t)perm[r] * D + d);
-  part[g][d] = acc;
+  const int tid = threadIdx.x;
+  if (tid < nj) stoks[tid] = perm[tid];
   __syncthreads();
-  if (g == 0) {
-    float s = 0.0f;
+  const int g = tid % NG, slot = tid / NG;
+  float acc[EPG];
 #pragma unroll
-    for (int q = 0; q < G; ++q) s += part[q][d];
+  for (int e = 0; e < EPG; ++e) acc[e] = 0.0f;
+#pragma unroll 4
+  for (int r = slot; r < nj; r += S) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(X + (int64_t)stoks[r] * D + g * EPG);
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] += bf16_to_f32((uint16_t)(ws[k] & 0xFFFFu));
+        acc[2 * k + 1] += bf16_to_f32((uint16_t)(ws[k] >> 16));
+      }
+    } else {
+      acc[0] += __uint_as_float(v.x); acc[1] += __uint_as_float(v.y);
+      acc[2] += __uint_as_float(v.z); acc[3] += __uint_as_float(v.w);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPG; ++e) part[slot][g * EPG + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float sum = 0.0f;
+    for (int q = 0; q < S; ++q) sum += part[q][tid];
     float* out = (tensor == 0 ? cq : ck) + ((int64_t)bh * nc + j) * D;
-    out[d] = s / (float)nj;
-    if (d == 0 && tensor == 0 && counts) counts[(int64_t)bh * nc + j] = nj;
+    out[tid] = sum / (float)nj;
+    if (tid == 0 && tensor == 0 && counts) counts[(int64_t)bh * nc + j] = nj;
   }
 }
 
@@ -468,7 +627,16 @@ template <typename T, int D>
 static void level_impl(const LevelArgs& a, hipStream_t st) {
   const int trees = 2 * a.BH;
   dim3 gslots(1u << a.level, trees);
-  pddp_dir<T, D><<<gslots, 256, dir_smem<T, D>(), st>>>(a);
+  dim3 gspan((a.N + kSampleSpan - 1) / kSampleSpan, trees);
+  pddp_sample<<<gspan, 256, 0, st>>>(a);
+  const size_t lds = dir_smem<T, D>(a.N, a.c, a.level);
+  static size_t lds_allowed = 0;   // raise the dynamic-LDS limit when a level needs more
+  if (lds > lds_allowed) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&pddp_dir<T, D>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    lds_allowed = lds;
+  }
+  pddp_dir<T, D><<<gslots, 256, lds, st>>>(a);
   dim3 gproj((a.N + a.c - 1) / a.c, trees);
   pddp_project<T, D><<<gproj, 256, 0, st>>>(a);
   pddp_split<<<gslots, kSplitThreads, 0, st>>>(a);

@@ -28,10 +28,15 @@ struct LevelArgs {
   const float* Mk;          // [BH][D][D]
   const float* dir_prev;    // [2 BH][slots/2][D]
   float* dir_cur;           // [2 BH][slots][D]
-  int32_t* sample_buf;      // [2 BH][N]
+  int nchunks;              // ceil(N / c)
+  int32_t* sample_buf;      // [2 BH][N]   per-chunk sample lists
+  int32_t* chunk_cnt;       // [2 BH][nchunks]
+  int32_t* zbuf_tok;        // [2 BH][N]   a node's gathered sample tokens
   float* zbuf;              // [2 BH][N]
   uint32_t* keys;           // [2 BH][N]
   float* trace_score;       // [2 BH][N] or null
+  float* trace_dir;         // [2 BH][trace_slots][D] or null
+  int trace_slots;
 };
 void launch_level(const LevelArgs& a, hipStream_t st);
 void launch_perm_init(int32_t* perm, int trees, int N, hipStream_t st);

@@ -14,10 +14,23 @@ namespace {
 
 constexpr int kMetricTile = 64;   // tokens per LDS tile
 
-// Hash word j of a row: fmix64((j << 32 | w_j) + golden), summed mod 2^64.
-CA_DEV uint64_t hash_word(uint32_t j, uint32_t w) {
-  return fmix64((((uint64_t)j << 32) | (uint64_t)w) + kGolden);
+// Row content hash: fmix64(sum_j w_j golden^(j+1) mod 2^64) over the row's
+// 32-bit words; hash_word gives one term of the sum.
+struct HashPow {
+  uint64_t v[128];
+};
+constexpr HashPow make_hash_pow() {
+  HashPow t{};
+  uint64_t p = kGolden;
+  for (int j = 0; j < 128; ++j) {
+    t.v[j] = p;
+    p *= kGolden;
+  }
+  return t;
 }
+__constant__ HashPow kHashPow = make_hash_pow();
+
+CA_DEV uint64_t hash_word(uint32_t j, uint32_t w) { return (uint64_t)w * kHashPow.v[j]; }
 
 template <int D>
 __global__ __launch_bounds__(256) void metric_partial_bf16(

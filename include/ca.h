@@ -66,7 +66,7 @@ typedef enum {
 /*
  * Options of the clustering (v1 §3.2). Pass NULL for the defaults
  * {transform=1, query_normalize=1, power_iters=8, sample_factor=1, seed=0,
- *  trace_perm=NULL, trace_score=NULL}.
+ *  trace_perm=NULL, trace_score=NULL, trace_dir=NULL}.
  *
  *  transform        1: keys are split under the query metric M_q = Q^T Q / N
  *                   (Eq. 12-14) and queries under the centred key metric
@@ -88,6 +88,10 @@ typedef enum {
  *  trace_score      optional device buffer float [L][B*H][2][N]: the
  *                   projection of the token at each position at each level;
  *                   positions inside leaves are left untouched.
+ *  trace_dir        optional device buffer float [L][B*H][2][S][D] with
+ *                   S = 2^(L-1): the unit direction of the node in slot j of
+ *                   level l (slot j's children are slots 2j and 2j+1 of level
+ *                   l+1); slots without a splitting node are left untouched.
  */
 typedef struct {
   int transform;
@@ -97,6 +101,7 @@ typedef struct {
   uint64_t seed;
   int32_t* trace_perm;
   float* trace_score;
+  float* trace_dir;
 } ca_cluster_opts;
 
 /* Number of split levels of the data-independent tree for (N, c): the tree

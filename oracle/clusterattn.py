@@ -92,13 +92,13 @@ def chain(*vals: int) -> int:
 def row_hash(words: np.ndarray) -> np.ndarray:
     """64-bit content hash of each row of 32-bit words, shape [N, W] -> [N].
 
-    h = fmix64( sum_j fmix64((j << 32 | w_j) + golden)  mod 2^64 ).
+    A polynomial hash over Z/2^64 finished by the splitmix64 finaliser:
+    h = fmix64( sum_j w_j golden^(j+1)  mod 2^64 ).
     """
     words = np.asarray(words, dtype=np.uint64)
-    j = np.arange(words.shape[1], dtype=np.uint64)[None, :]
+    pw = np.array([pow(GOLDEN, j + 1, 1 << 64) for j in range(words.shape[1])], dtype=np.uint64)
     with np.errstate(over="ignore"):
-        per = fmix64(((j << np.uint64(32)) | words) + np.uint64(GOLDEN))
-        s = per.sum(axis=1, dtype=np.uint64)
+        s = (words * pw[None, :]).sum(axis=1, dtype=np.uint64)
     return fmix64(s)
 
 

@@ -84,9 +84,9 @@ def test_cluster_rejects_bad_arguments(lib):
     assert _cluster(lib, N=32) == 1
     assert _cluster(lib, B=0) == 1
     assert _cluster(lib, B=2**16, H=2**16) == 2
-    opts = ca._Opts(1, 1, 0, 1, 0, None, None)
+    opts = ca._Opts(1, 1, 0, 1, 0, None, None, None)
     assert _cluster(lib, opts=ctypes.byref(opts)) == 1
-    opts = ca._Opts(1, 1, 8, 0, 0, None, None)
+    opts = ca._Opts(1, 1, 8, 0, 0, None, None, None)
     assert _cluster(lib, opts=ctypes.byref(opts)) == 1
     assert _cluster(lib, ws=None, ws_bytes=0) == 3
     assert _cluster(lib, ws=FAKE + 8, ws_bytes=2**30) == 3

@@ -91,13 +91,24 @@ def _replay_direction(X, M, hashes, members, level, tensor, head, slot, d, opts,
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_cluster_against_oracle_per_level(ca, name):
+    """Stage-isolated clustering parity, node by node.
+
+    For every node the oracle is given the GPU's membership (the permutation
+    before the level) and the GPU's estimate for the parent (the warm start):
+    (1) its select-and-partition fed the GPU's fp32 projections reproduces the
+    GPU's children bit for bit; (2) its fp64 direction reproduces the GPU's
+    projections to 1e-4 of their spread; (3) splitting with its own fp64
+    projections puts every token on the GPU's side except at the threshold.
+    """
     w, Q, K, V, c, topk = _inputs(name)
     B, H, N, D = Q.shape
     res = _gpu_cluster(ca, name, trace=True)
     L = ca.tree_levels(N, c)
-    # trace layout [level][head][tensor][N] -> [level][tree = 2 head + tensor][N]
+    S = 1 << max(L - 1, 0)
+    # trace layouts [level][head][tensor][...] -> [level][tree = 2 head + tensor][...]
     tp = _np(res.trace_perm).reshape(L + 1, 2 * B * H, N)
     ts = _np(res.trace_score).reshape(max(L, 1), 2 * B * H, N)
+    td = _np(res.trace_dir).reshape(max(L, 1), 2 * B * H, S, D)
     levels = o.tree_levels(N, c)
     opts = _opts(w)
     for b in range(B):
@@ -109,7 +120,6 @@ def test_cluster_against_oracle_per_level(ca, name):
             for tensor, X, G, hs in ((0, Xq, Gq, hq), (1, Xk, Gk, hk)):
                 tree = head * 2 + tensor
                 assert np.array_equal(tp[0, tree], np.arange(N))
-                dirs = {}
                 disagree, total = 0, 0
                 for lvl in range(L):
                     before, after, sc = tp[lvl, tree], tp[lvl + 1, tree], ts[lvl, tree]
@@ -125,24 +135,24 @@ def test_cluster_against_oracle_per_level(ca, name):
                         left, right = o.split_by_scores(mem, sc[sl].astype(np.float64), t)
                         assert np.array_equal(after[nd.off:nd.off + t], left), (name, lvl, tensor)
                         assert np.array_equal(after[nd.off + t:nd.off + nd.n], right)
-                        # (2) oracle direction on the GPU's membership
-                        par = dirs.get((lvl - 1, nd.index // 2))
+                        # (2) oracle direction on the GPU's membership and parent estimate
+                        par = td[lvl - 1, tree, nd.index // 2].astype(np.float64) if lvl else None
                         u = _replay_direction(X, G, hs, mem, lvl, tensor, head, nd.index, D, opts, par)
-                        dirs[(lvl, nd.index)] = u
+                        ug = td[lvl, tree, nd.index].astype(np.float64)
+                        assert 1 - abs(u @ ug) / np.linalg.norm(ug) <= 1e-9, (name, lvl, tensor)
                         so = X[mem] @ u
                         sg = sc[sl].astype(np.float64)
                         spread = np.std(so) + 1e-30
-                        assert np.max(np.abs(so - sg)) <= 2e-3 * spread, (name, lvl, tensor)
+                        assert np.max(np.abs(so - sg)) <= 1e-4 * spread, (name, lvl, tensor)
+                        # (3) sides from the oracle's own projections
                         lo, ro = o.split_by_scores(mem, so, t)
-                        side_o = np.isin(mem, lo)
-                        side_g = np.isin(mem, left)
-                        bad = side_o != side_g
+                        bad = np.isin(mem, lo) != np.isin(mem, left)
                         disagree += int(bad.sum())
                         total += nd.n
                         if bad.any():
                             thr = np.sort(so)[t - 1:t + 1].mean()
                             iqr = np.subtract(*np.percentile(so, [75, 25])) + 1e-30
-                            assert np.all(np.abs(so[bad] - thr) <= 1e-3 * iqr), (name, lvl, tensor)
+                            assert np.all(np.abs(so[bad] - thr) <= 1e-4 * iqr), (name, lvl, tensor)
                     assert np.array_equal(before[~moved], after[~moved])
                 assert disagree <= 1e-3 * max(total, 1), (name, tensor, disagree, total)
                 final = tp[L, tree]
@@ -155,6 +165,14 @@ def test_cluster_against_oracle_per_level(ca, name):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_cluster_end_to_end_agreement(ca, name):
+    """Agreement of the whole GPU tree with the oracle's own fp64 tree.
+
+    Informational beyond a floor: the warm-started power iteration carries
+    last-bit differences of the metrics and directions down the tree (a
+    relative perturbation of 1e-6 in fp64 alone moves up to a few percent of
+    tokens on these inputs), so exact end-to-end agreement is not a property
+    of the method; the node-by-node test above is the parity check.
+    """
     w, Q, K, V, c, topk = _inputs(name)
     res = _gpu_cluster(ca, name)
     pq, pk = o.cluster(Q, K, c, _opts(w), w.dtype)
@@ -164,7 +182,7 @@ def test_cluster_end_to_end_agreement(ca, name):
     agk = np.mean([o.cluster_agreement(_np(res.perm_k)[b, h], pk[b, h], c)
                    for b in range(B) for h in range(H)])
     print(f"{name}: end-to-end cluster agreement q={agq:.5f} k={agk:.5f}")
-    assert agq >= 0.99 and agk >= 0.99
+    assert agq >= 0.95 and agk >= 0.95
 
 
 @pytest.mark.parametrize("name", list(CASES))
