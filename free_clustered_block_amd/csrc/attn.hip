@@ -4,12 +4,14 @@
 //
 // bf16 path:
 //   permute_kv   one workgroup per key cluster: gathers the cluster's K rows
-//                into a contiguous zero-padded tile [c][D], its V rows into a
-//                transposed tile [D][c] (key order swizzled to the MFMA operand
-//                order), and forms the key/value centroids and ln n_c.
+//                into a contiguous zero-padded tile [c][D], its V rows into
+//                transposed sub-tiles [c/64][D][64] (key order swizzled to the
+//                MFMA operand order), and forms the key/value centroids and
+//                ln n_c.
 //   attn_fwd     one workgroup per query cluster (c/32 waves, 32 queries per
-//                wave): for every selected key cluster the K and V tiles are
-//                staged in LDS, S^T = K Q^T and O^T += V^T P^T run on
+//                wave): the selected key clusters stream through LDS in
+//                double-buffered sub-tiles of 64 keys, S^T = K Q^T and
+//                O^T += V^T P^T run on
 //                v_mfma_f32_32x32x16_bf16 with an fp32 online softmax (exp2);
 //                the excluded clusters then enter through their centroids
 //                (logit scale q.kbar + ln n_c, value vbar) in the same running
@@ -25,6 +27,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLazy = 8.0f;   // log2 headroom before the running maximum moves
 
 // Token indices come from caller-supplied permutations: out-of-range values
 // read row 0 instead of faulting (the result is then meaningless).
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
       pk.y = vals[2] | ((uint32_t)vals[3] << 16);
       pk.z = vals[4] | ((uint32_t)vals[5] << 16);
       pk.w = vals[6] | ((uint32_t)vals[7] << 16);
-      *reinterpret_cast<u32x4_t*>(vt + (int64_t)dd * c + r0 + s8 * 8) = pk;
+      *reinterpret_cast<u32x4_t*>(vt + (int64_t)(r0 / RB) * D * RB + dd * RB + s8 * 8) = pk;
     }
     __syncthreads();
   }
@@ -145,30 +148,51 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
 // Attention (bf16 MFMA)
 // ----------------------------------------------------------------------------
 
-template <int D, int C>
-struct AttnSmem {
-  static constexpr int KP = D + 8;     // padded K row (bf16)
-  static constexpr int VP = C + 8;     // padded V^T row (bf16)
-  static constexpr size_t k_bytes = (size_t)C * KP * 2;
-  static constexpr size_t v_bytes = (size_t)D * VP * 2;
-  static constexpr size_t bytes = k_bytes + v_bytes + 8192 / 8 + 64;
+// Key/value sub-tiles of 64 keys are staged in LDS, double buffered: K rows
+// (64 x D bf16) and V^T rows (D x 64 bf16), each row padded by 16 bytes so
+// that the 16 lanes an LDS cycle serves (16 consecutive rows at one 16-byte
+// chunk) fall on distinct banks and every operand read is a per-lane base
+// plus a compile-time offset.
+template <int D>
+struct AttnTile {
+  static constexpr int KT = 64;                           // keys per sub-tile
+  static constexpr int KP = D * 2 + 16;                   // K row pitch (bytes)
+  static constexpr int VP = KT * 2 + 16;                  // V^T row pitch (bytes)
+  static constexpr int K_BYTES = KT * KP;
+  static constexpr int V_BYTES = D * VP;
+  static constexpr int BYTES = K_BYTES + V_BYTES;         // one buffer
+  static constexpr int K_CHUNKS = D / 8;                  // 16-byte chunks per K row
+  static constexpr int V_CHUNKS = KT / 8;                 // 16-byte chunks per V^T row
+  static constexpr int K_LOADS = KT * K_CHUNKS;           // 16-byte loads per sub-tile
+  static constexpr int V_LOADS = D * V_CHUNKS;
 };
 
+// Workgroup order: consecutive logical workgroups (adjacent query clusters of
+// one head, which select overlapping key clusters) are kept on one XCD, whose
+// L2 then serves their shared key/value tiles. Hardware hands workgroup b to
+// XCD b % 8.
+CA_DEV int xcd_logical(int b, int G) {
+  const int xcd = b & 7, idx = b >> 3;
+  const int per = G >> 3, rem = G & 7;
+  return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
 template <int D, int C, bool DENSE>
-__global__ __launch_bounds__(2 * C) void attn_fwd(AttnArgs a) {
-  using SM = AttnSmem<D, C>;
-  constexpr int NT = 2 * C;            // threads
+__global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd(AttnArgs a) {
+  using TL = AttnTile<D>;
+  constexpr int NT = 2 * C;            // threads (C/32 waves of 32 queries)
   constexpr int KS = D / 16;           // k-steps over the head dim
   constexpr int NB = D / 32;           // 32-row blocks of O^T
+  constexpr int SUB = C / TL::KT;      // sub-tiles per key cluster
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* sK = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + SM::k_bytes);
-  uint32_t* sSel = reinterpret_cast<uint32_t*>(smem + SM::k_bytes + SM::v_bytes);
+  uint32_t* sSel = reinterpret_cast<uint32_t*>(smem + 2 * TL::BYTES);
 
-  const int qa = blockIdx.x, bh = blockIdx.y;
+  const int G = gridDim.x * gridDim.y;
+  const int lg = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, G);
+  const int nc = a.nc, N = a.N;
+  const int qa = lg % nc, bh = lg / nc;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
-  const int N = a.N, nc = a.nc;
-  const int qpos = qa * C + w * 32 + r;            // cluster-major position of this lane's query
+  const int qpos = qa * C + w * 32 + r;
   const bool qvalid = qpos < N;
   const int qtok =
       qvalid ? (DENSE || !a.perm_q ? qpos : clamp_tok(a.perm_q[(int64_t)bh * N + qpos], N)) : 0;
@@ -187,77 +211,136 @@ __global__ __launch_bounds__(2 * C) void attn_fwd(AttnArgs a) {
   float m = kNegInf, lsum = 0.0f;
   const float sl2 = a.scale * kLog2e;
 
-  // online-softmax update of this lane's query with 16 logits (log2 units)
-  auto absorb = [&](float (&t)[16], const uint16_t* vsrc, int vpitch, int vcol0) {
-    float bm = t[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) bm = fmaxf(bm, t[i]);
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-    const float mn = fmaxf(m, bm);
-    const float mref = mn == kNegInf ? 0.0f : mn;
-    const float alpha = exp2f(m - mref);
-    float p[16], ps = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { p[i] = exp2f(t[i] - mref); ps += p[i]; }
-    ps += __shfl_xor(ps, 32, 64);
-    lsum = lsum * alpha + ps;
-    m = mn;
-    const bf16x8_t p0 = as_bf16x8(pack8(p));
-    const bf16x8_t p1 = as_bf16x8(pack8(p + 8));
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
-      const uint16_t* row = vsrc + (int64_t)(nb * 32 + r) * vpitch + vcol0 + h * 8;
-      const bf16x8_t v0 = *reinterpret_cast<const bf16x8_t*>(row);
-      const bf16x8_t v1 = *reinterpret_cast<const bf16x8_t*>(row + 16);
-      acc[nb] = mfma32(v0, p0, acc[nb]);
-      acc[nb] = mfma32(v1, p1, acc[nb]);
-    }
-  };
-
   const int nsel = DENSE ? nc : a.topk;
   const int32_t* blk = DENSE ? nullptr : a.blocks + ((int64_t)bh * nc + qa) * a.topk;
-  for (int bi = 0; bi < nsel; ++bi) {
-    const int j = DENSE ? bi : blk[bi];
-    if (j < 0 || j >= nc) continue;   // out-of-range entries are ignored (uniform per block)
-    const int nvalid = min(C, N - j * C);
-    const uint16_t* kc = a.kc + ((int64_t)bh * nc + j) * C * D;
-    const uint16_t* vt = a.vt + ((int64_t)bh * nc + j) * (int64_t)D * C;
-    __syncthreads();
-    for (int e = tid; e < C * D / 8; e += NT) {
-      const int rr = e / (D / 8), g = e % (D / 8);
-      *reinterpret_cast<u32x4_t*>(sK + rr * SM::KP + 8 * g) =
-          *reinterpret_cast<const u32x4_t*>(kc + (int64_t)rr * D + 8 * g);
+  const int T = nsel * SUB;   // sub-tiles to process
+
+  // cluster of sub-tile t (out-of-range block entries are skipped)
+  auto tile_cluster = [&](int t) -> int {
+    const int j = DENSE ? t / SUB : blk[t / SUB];
+    return (j >= 0 && j < nc) ? j : -1;
+  };
+  // stage: 16-byte global loads into registers, then into an LDS buffer
+  constexpr int KLPT = TL::K_LOADS / NT, VLPT = TL::V_LOADS / NT;
+  u32x4_t kst[KLPT], vst[VLPT];
+  auto fetch = [&](int t) {
+    int j = tile_cluster(t);
+    if (j < 0) j = 0;   // any valid tile; its results are not used
+    const int part = t % SUB;
+    const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(
+        a.kc + (((int64_t)bh * nc + j) * C + part * TL::KT) * D);
+    const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(
+        a.vt + (((int64_t)bh * nc + j) * SUB + part) * (int64_t)D * TL::KT);
+#pragma unroll
+    for (int i = 0; i < KLPT; ++i) kst[i] = ks[i * NT + tid];
+#pragma unroll
+    for (int i = 0; i < VLPT; ++i) vst[i] = vs[i * NT + tid];
+  };
+  auto store = [&](int buf) {
+    unsigned char* base = smem + buf * TL::BYTES;
+#pragma unroll
+    for (int i = 0; i < KLPT; ++i) {
+      const int e = i * NT + tid;
+      *reinterpret_cast<u32x4_t*>(base + (e / TL::K_CHUNKS) * TL::KP + (e % TL::K_CHUNKS) * 16) = kst[i];
     }
-    for (int e = tid; e < D * C / 8; e += NT) {
-      const int rr = e / (C / 8), g = e % (C / 8);
-      *reinterpret_cast<u32x4_t*>(sV + rr * SM::VP + 8 * g) =
-          *reinterpret_cast<const u32x4_t*>(vt + (int64_t)rr * C + 8 * g);
+#pragma unroll
+    for (int i = 0; i < VLPT; ++i) {
+      const int e = i * NT + tid;
+      *reinterpret_cast<u32x4_t*>(base + TL::K_BYTES + (e / TL::V_CHUNKS) * TL::VP +
+                                  (e % TL::V_CHUNKS) * 16) = vst[i];
     }
-    __syncthreads();
+  };
+  // per-lane LDS read bases: K row r, chunk h; V^T row r, chunk h
+  const int kread = r * TL::KP + h * 16;
+  const int vread = TL::K_BYTES + r * TL::VP + h * 16;
+
+  if (T > 0) {
+    fetch(0);
+    store(0);
+  }
+  __syncthreads();
 #pragma unroll 1
-    for (int kb = 0; kb < C / 32; ++kb) {
-      floatx16_t sacc = zero16();
+  for (int t = 0; t < T; ++t) {
+    if (t + 1 < T) fetch(t + 1);
+    const int j = tile_cluster(t);
+    if (j >= 0) {
+      const unsigned char* buf = smem + (t & 1) * TL::BYTES;
+      const int nvalid = min(C, N - j * C) - (t % SUB) * TL::KT;
+      // two independent accumulation chains (keys 0-31, 32-63) interleaved
+      floatx16_t sacc[2] = {zero16(), zero16()};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8_t kf =
-            *reinterpret_cast<const bf16x8_t*>(sK + (kb * 32 + r) * SM::KP + s * 16 + h * 8);
-        sacc = mfma32(kf, qf[s], sacc);
-      }
-      float t[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb * 32 + c_row(i, h);
-        t[i] = key < nvalid ? sacc[i] * sl2 : kNegInf;
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8_t kf =
+              *reinterpret_cast<const bf16x8_t*>(buf + kread + kb * 32 * TL::KP + s * 32);
+          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
+        }
       }
-      absorb(t, sV, SM::VP, kb * 32);
+      // online softmax in log2 units with a lazily updated running maximum:
+      // m only moves (and the accumulators are rescaled) when the tile's
+      // maximum exceeds it by more than 2^8, so P <= 256 (exact after the
+      // final division by l, which uses the same m).
+      if (nvalid < TL::KT) [[unlikely]] {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + c_row(i, h) >= nvalid) sacc[kb][i] = kNegInf;
+      }
+      float bm = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bm = fmaxf(bm, sacc[kb][i]);
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64)) * sl2;
+      const bool grow = bm > m + kLazy;
+      if (__ballot(grow)) [[unlikely]] {
+        const float mn = grow ? bm : m;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
+        lsum *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
+        m = mn;
+      }
+      const float nm = -m;
+      float tv[32];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          tv[kb * 16 + i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2, nm));
+      // P enters the P.V product as bf16; the denominator sums the same
+      // rounded values, so the output stays a convex combination of values
+      bf16x8_t pk[4];
+      float ps = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4_t u = pack8(tv + 8 * q);
+        ps = sum_bf16x8(u, ps);
+        pk[q] = as_bf16x8(u);
+      }
+      ps += __shfl_xor(ps, 32, 64);
+      lsum += ps;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          // keys 16q .. 16q+15 of the sub-tile: V^T chunk 2q + h
+          const bf16x8_t vf =
+              *reinterpret_cast<const bf16x8_t*>(buf + vread + nb * 32 * TL::VP + q * 32);
+          acc[nb] = mfma32(vf, pk[q], acc[nb]);
+        }
+      }
     }
+    if (t + 1 < T) store((t + 1) & 1);
+    __syncthreads();
   }
 
   if (!DENSE && a.compensate) {
     const int ncp = attn_ncp(nc);
-    __syncthreads();
     for (int e = tid; e < ncp / 32; e += NT) sSel[e] = 0u;
     __syncthreads();
     for (int e = tid; e < a.topk; e += NT) {
@@ -279,15 +362,44 @@ __global__ __launch_bounds__(2 * C) void attn_fwd(AttnArgs a) {
         sacc = mfma32(*reinterpret_cast<const bf16x8_t*>(klo + o), qf[s], sacc);
       }
       const uint32_t selw = sSel[cb];
-      float t[16];
+      // centroid logits in log2 units: scale q.kbar + ln n_c; selected or
+      // padded clusters get -inf
+      float tv[16];
+      float bm = kNegInf;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int cr = c_row(i, h);
         const bool excluded = !((selw >> cr) & 1u);
         const float ln = logn[cb * 32 + cr];
-        t[i] = excluded ? (sacc[i] * sl2 + ln * kLog2e) : kNegInf;
+        tv[i] = excluded ? fmaf(sacc[i], sl2, ln * kLog2e) : kNegInf;
+        bm = fmaxf(bm, tv[i]);
       }
-      absorb(t, vbt, ncp, cb * 32);
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      const bool grow = bm > m + kLazy;
+      if (__ballot(grow)) [[unlikely]] {
+        const float mn = grow ? bm : m;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
+        lsum *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
+        m = mn;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tv[i] = __builtin_amdgcn_exp2f(tv[i] - m);
+      const u32x4_t u0 = pack8(tv), u1 = pack8(tv + 8);
+      float ps = sum_bf16x8(u1, sum_bf16x8(u0, 0.0f));
+      ps += __shfl_xor(ps, 32, 64);
+      lsum += ps;
+      const bf16x8_t p0 = as_bf16x8(u0);
+      const bf16x8_t p1 = as_bf16x8(u1);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint16_t* row = vbt + (int64_t)(nb * 32 + r) * ncp + cb * 32 + h * 8;
+        acc[nb] = mfma32(*reinterpret_cast<const bf16x8_t*>(row), p0, acc[nb]);
+        acc[nb] = mfma32(*reinterpret_cast<const bf16x8_t*>(row + 16), p1, acc[nb]);
+      }
     }
   }
 
@@ -306,6 +418,11 @@ __global__ __launch_bounds__(2 * C) void attn_fwd(AttnArgs a) {
     }
   }
   if (a.lse && h == 0) a.lse[(int64_t)bh * N + qtok] = (m + log2f(lsum)) * kLn2;
+}
+
+template <int D, int C>
+constexpr size_t attn_smem() {
+  return 2 * (size_t)AttnTile<D>::BYTES + 8192 / 8 + 64;
 }
 
 // ----------------------------------------------------------------------------
@@ -427,7 +544,7 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
 
 template <int D, int C, bool DENSE>
 void launch_mfma(const AttnArgs& a, hipStream_t st) {
-  const size_t sm = AttnSmem<D, C>::bytes;
+  const size_t sm = attn_smem<D, C>();
   static bool attr_set = false;   // raise the dynamic-LDS limit once per instantiation
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd<D, C, DENSE>),

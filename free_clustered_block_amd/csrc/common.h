@@ -30,8 +30,13 @@ CA_DEV uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+typedef float float2v_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
 CA_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const float2v_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v_t));
 }
 
 // Element loads as float from a bf16 (uint16_t) or fp32 row.

@@ -31,6 +31,19 @@ CA_DEV u32x4_t pack8(const float* f) {
   return r;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + the sum of the eight bf16 values packed in v (v_dot2_f32_bf16 with a
+// pair of ones: each pair is added in fp32).
+CA_DEV float sum_bf16x8(const u32x4_t& v, float acc) {
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  const bf16x8_t p = __builtin_bit_cast(bf16x8_t, v);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
+  return acc;
+}
 CA_DEV floatx16_t zero16() {
   floatx16_t z;
 #pragma unroll
