@@ -189,10 +189,14 @@ __global__ __launch_bounds__(256) void pddp_dir(LevelArgs a) {
     }
     stok[r] = tok;
     if (r < CAP) {
+      constexpr int NG = D * (int)sizeof(T) / 16;
       const u32x4_t* src = reinterpret_cast<const u32x4_t*>(X + (int64_t)tok * D);
       u32x4_t* dst = reinterpret_cast<u32x4_t*>(srow + r * PITCH);
-#pragma unroll 4
-      for (int g = 0; g < D * (int)sizeof(T) / 16; ++g) dst[g] = src[g];
+      u32x4_t v[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) v[g] = src[g];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) dst[g] = v[g];
       ss[r] = svec ? svec[tok] : 1.0f;
     }
   }
@@ -279,63 +283,74 @@ __global__ __launch_bounds__(256) void pddp_dir(LevelArgs a) {
     float uz[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) uz[e] = su[qz * EPT + e];
-    // z_r = (s_r x_r - mean) . u : TPR threads per row
+    // z_r = (s_r x_r - mean) . u : TPR threads per row, four partial sums.
+    // y_r = s_r z_r is kept for w, and Z = sum_r z_r per row group.
+    float zpart = 0.0f;
     for (int rb = 0; rb < m; rb += 256 / TPR) {
       const int r = rb + tid / TPR;
-      float acc = 0.0f;
+      float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float sr = 1.0f;
       if (r < mc) {
-        const float s = ss[r];
+        sr = ss[r];
         const T* row = srow + r * PITCH + qz * EPT;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) acc = fmaf(fmaf(s, load_elem(row, e), -mz[e]), uz[e], acc);
+        for (int e = 0; e < EPT; ++e) a4[e & 3] = fmaf(fmaf(sr, load_elem(row, e), -mz[e]), uz[e], a4[e & 3]);
       } else if (r < m) {
         const int tok = stok[r];
-        const float s = svec ? svec[tok] : 1.0f;
+        sr = svec ? svec[tok] : 1.0f;
         const T* row = X + (int64_t)tok * D + qz * EPT;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) acc = fmaf(fmaf(s, load_elem(row, e), -mz[e]), uz[e], acc);
+        for (int e = 0; e < EPT; ++e) a4[e & 3] = fmaf(fmaf(sr, load_elem(row, e), -mz[e]), uz[e], a4[e & 3]);
       }
+      float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
 #pragma unroll
       for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
-      if (qz == 0) {
-        if (r < mc) sz[r] = acc;
-        else if (r < m) a.zbuf[zoff + r] = acc;
+      if (qz == 0 && r < m) {
+        zpart += acc;
+        if (r < mc) sz[r] = acc * sr;
+        else a.zbuf[zoff + r] = acc * sr;
       }
     }
-    __syncthreads();
-    // w_j = (1/m) sum_r z_r (s_r x_rj - mean_j): column j, rows of group gc
     {
-      float acc = 0.0f;
+      // Z = sum_r z_r over the block (rows are owned by the qz == 0 lanes)
+      const float zsum = block_sum(zpart);
+      // w_j = (1/m) sum_r z_r (s_r x_rj - mean_j) = (1/m)(sum_r y_r x_rj - mean_j Z),
+      // column j by row group gc with four partial sums; the G groups are added
+      // when w is read below
+      float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
       int r = gc;
-#pragma unroll 4
-      for (; r < mc; r += G)
-        acc = fmaf(sz[r], fmaf(ss[r], load_elem(srow, (int64_t)r * PITCH + jc), -mcol), acc);
-      for (; r < m; r += G) {
-        const int tok = stok[r];
-        const float s = svec ? svec[tok] : 1.0f;
-        acc = fmaf(a.zbuf[zoff + r], fmaf(s, load_elem(X, (int64_t)tok * D + jc), -mcol), acc);
+      for (; r + 3 * G < mc; r += 4 * G) {
+        a0 = fmaf(sz[r], load_elem(srow, (int64_t)r * PITCH + jc), a0);
+        a1 = fmaf(sz[r + G], load_elem(srow, (int64_t)(r + G) * PITCH + jc), a1);
+        a2 = fmaf(sz[r + 2 * G], load_elem(srow, (int64_t)(r + 2 * G) * PITCH + jc), a2);
+        a3 = fmaf(sz[r + 3 * G], load_elem(srow, (int64_t)(r + 3 * G) * PITCH + jc), a3);
       }
-      spart[gc * D + jc] = acc;
-    }
-    __syncthreads();
-    if (tid < D) {
-      float s = 0.0f;
-#pragma unroll
-      for (int g = 0; g < G; ++g) s += spart[g * D + tid];
-      sw[tid] = s * inv_m;
+      for (; r < mc; r += G) a0 = fmaf(sz[r], load_elem(srow, (int64_t)r * PITCH + jc), a0);
+      for (; r < m; r += G) a1 = fmaf(a.zbuf[zoff + r], load_elem(X, (int64_t)stok[r] * D + jc), a1);
+      float acc = (a0 + a1) + (a2 + a3);
+      if (gc == 0) acc -= mcol * zsum;
+      spart[gc * D + jc] = acc * inv_m;
     }
     __syncthreads();
     // u'_j = sum_k M[j][k] w_k : TPR threads per row of M
     float un;
     if (a.transform) {
-      float acc = 0.0f;
+      float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) acc = fmaf(mreg[e], sw[qm * EPT + e], acc);
+      for (int e = 0; e < EPT; ++e) {
+        float wk = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) wk += spart[g * D + qm * EPT + e];
+        a4[e & 3] = fmaf(mreg[e], wk, a4[e & 3]);
+      }
+      float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
 #pragma unroll
       for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
       un = acc;
     } else {
-      un = sw[jm];
+      un = 0.0f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) un += spart[g * D + jm];
     }
     const float contrib = qm == 0 ? un * un : 0.0f;
     const float nn = block_sum(contrib);
