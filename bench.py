@@ -17,10 +17,15 @@ Prints one JSON line:
              counting 4 d FLOP per performed token or centroid interaction,
              timed with HIP events recorded around that kernel alone
   cpu_baseline  the CPU oracle on a bounded sample of heads of the same input
+Also reported: per-step median/p10/p90 from HIP events, the same steps with
+the caches flushed before each one (cold), and the measured HBM copy and bf16
+GEMM rates of the box (a 1 GiB torch copy, which also serves as the plain-copy
+calibration of the HBM byte counters, and an 8192^3 torch.matmul).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -36,6 +41,37 @@ sys.path.insert(0, ROOT)
 METRIC = "ClusterAttention fwd latency, eff. TFLOP/s & speedup vs dense at N=32k, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+# HBM bytes per attention launch from rocprofv3 FETCH_SIZE + WRITE_SIZE runs,
+# scaled by the same counters on a plain copy; valid only for the kernel
+# sources whose digest the file records.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_video_32760_traffic.txt")
+ATTN_SOURCES = ["attn.hip", "mfma.h", "common.h", "kernels.h"]
+
+
+def attn_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "free_clustered_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str, topk: int):
+    """HBM bytes per attention launch recorded for this workload and these
+    kernel sources, or None."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith(("#", " ", "|")):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if (kv.get("workload") == workload and int(kv.get("topk", -1)) == topk
+                and kv.get("sources_sha256") == attn_source_digest()):
+            return float(kv["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def parse():
@@ -49,6 +85,10 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="steps timed one by one after a 512 MiB cache flush")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the copy and GEMM rate measurements")
     ap.add_argument("--verbose", action="store_true")
     return ap.parse_args()
 
@@ -86,6 +126,38 @@ def cpu_baseline(w, Q, K, V, topk, heads):
                   f"(BLAS threads={cores}; PDDP and top-k loops single-threaded Python)",
         "seconds": t,
     }
+
+
+def measure_peaks(torch, dev):
+    """Achievable rates of this machine: a plain 1 GiB bf16 copy (read + write
+    bytes over time; also the calibration kernel for the HBM byte counters)
+    and a bf16 8192^3 GEMM through torch.matmul."""
+    n = 1 << 29
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+    for a_ev, b_ev in ev:
+        a_ev.record()
+        dst.copy_(src)
+        b_ev.record()
+    torch.cuda.synchronize()
+    copy_ms = float(np.median([a_ev.elapsed_time(b_ev) for a_ev, b_ev in ev]))
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    torch.matmul(a, b)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+    for a_ev, b_ev in ev:
+        a_ev.record()
+        torch.matmul(a, b)
+        b_ev.record()
+    torch.cuda.synchronize()
+    gemm_ms = float(np.median([a_ev.elapsed_time(b_ev) for a_ev, b_ev in ev]))
+    return {"hbm_copy_GBs": round(2.0 * n * 2 / (copy_ms * 1e-3) / 1e9, 1),
+            "copy_bytes": 2 * n * 2,
+            "bf16_gemm_TFLOPs": round(2.0 * m ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
 
 
 def main():
@@ -155,6 +227,7 @@ def main():
     wall = (time.perf_counter() - t0) / args.steps
     if args.verbose:
         print(f"timed {args.steps} steps: {wall * 1e3:.3f} ms/step", file=sys.stderr, flush=True)
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     st_cluster = np.mean([e[0].elapsed_time(e[1]) for e in evs])
     st_route = np.mean([e[1].elapsed_time(e[2]) for e in evs])
     st_attend = np.mean([e[2].elapsed_time(e[3]) for e in evs])
@@ -170,6 +243,21 @@ def main():
     flops_attn = 4.0 * D * (tok_inter + cen_inter)
     achieved = flops_attn / (t_attn_kernel * 1e-3) / 1e12
 
+    # the same step with every cache flushed first (HIP events around the step only)
+    cold_ms = []
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for i in range(args.cold_steps):
+            flush.fill_(i & 0xFF)
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record()
+            step()
+            b_ev.record()
+            torch.cuda.synchronize()
+            cold_ms.append(a_ev.elapsed_time(b_ev))
+        del flush
+
+    traffic = recorded_traffic(w.name, topk) if B * H == w.B * w.H else None
     eff = 4.0 * D * N * N * B * H / (wall) / 1e12
     result = {
         "metric": METRIC,
@@ -189,7 +277,11 @@ def main():
         "stage_ms": {"cluster": round(float(st_cluster), 4), "route": round(float(st_route), 4),
                      "attend": round(float(st_attend), 4),
                      "attend_kernel": round(float(t_attn_kernel), 4),
-                     "gpu_step_events": round(float(gpu_step), 4)},
+                     "gpu_step_events": round(float(gpu_step), 4),
+                     "step_median": round(float(np.median(step_ms)), 4),
+                     "step_p10": round(float(np.percentile(step_ms, 10)), 4),
+                     "step_p90": round(float(np.percentile(step_ms, 90)), 4),
+                     "cold_step_median": round(float(np.median(cold_ms)), 4) if cold_ms else None},
         "roofline": {
             "kernel": "attn_fwd (block-sparse attention + SMC)",
             "bound": "mfma",
@@ -197,7 +289,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "flops_per_launch": flops_attn,
         },
     }
@@ -219,6 +311,9 @@ def main():
         result["speedup_vs_dense"] = round(dense_ms / (wall * 1e3), 3)
         result["dense_tflops"] = round(4.0 * D * N * N * B * H / (dense_ms * 1e-3) / 1e12, 2)
         result["cos_vs_dense"] = round(cos, 5)
+
+    if not args.no_peaks:
+        result["measured_peaks"] = measure_peaks(torch, dev)
 
     if not args.no_cpu_baseline:
         heads = max(1, min(args.cpu_heads, H))
