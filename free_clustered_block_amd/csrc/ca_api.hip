@@ -36,7 +36,7 @@ struct Carver {
 struct ClusterWs {
   float* partial;
   uint64_t* hash;
-  float *Mq, *Mk, *kbar;
+  float *Mq, *Mk, *kbar, *Mpk;
   uint16_t* gsplit;
   float* s;
   int32_t *permA, *permB;
@@ -60,6 +60,7 @@ ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c) {
   w.Mq = cv.take<float>((size_t)BH * D * D);
   w.Mk = cv.take<float>((size_t)BH * D * D);
   w.kbar = cv.take<float>((size_t)BH * D);
+  w.Mpk = cv.take<float>(T * D * D);
   w.gsplit = cv.take<uint16_t>((size_t)BH * 3 * D * D);
   w.s = cv.take<float>((size_t)BH * N);
   w.permA = cv.take<int32_t>(T * N);
@@ -199,7 +200,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   const size_t TN = 2 * (size_t)BH * N;
 
   launch_metric(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, o.transform, o.query_normalize, w.partial,
-                w.hash, w.Mq, w.Mk, w.kbar, w.gsplit, w.s, st);
+                w.hash, w.Mq, w.Mk, w.kbar, w.gsplit, w.s, w.Mpk, st);
   launch_perm_init(w.permA, 2 * BH, N, st);
   int32_t* cur = w.permA;
   int32_t* nxt = w.permB;
@@ -212,7 +213,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     a.transform = o.transform; a.power_iters = o.power_iters; a.sample_factor = o.sample_factor;
     a.seed = o.seed;
     a.perm_in = cur; a.perm_out = nxt;
-    a.hash = w.hash; a.s = w.s; a.Mq = w.Mq; a.Mk = w.Mk;
+    a.hash = w.hash; a.s = w.s; a.Mq = w.Mq; a.Mk = w.Mk; a.Mpk = w.Mpk;
     a.dir_prev = (level & 1) ? w.dirA : w.dirB;
     a.dir_cur = (level & 1) ? w.dirB : w.dirA;
     a.nchunks = (N + c - 1) / c;

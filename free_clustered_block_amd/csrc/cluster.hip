@@ -15,6 +15,7 @@
 // The node layout depends only on (N, c) and is recomputed on the device, so
 // no host synchronisation is needed between levels.
 #include "kernels.h"
+#include "mfma.h"
 
 namespace ca {
 
@@ -376,6 +377,334 @@ size_t dir_smem(int N, int c, int level) {
 }
 
 // ----------------------------------------------------------------------------
+// Direction of each node, bf16 rows: the sample's Gram matrix S = sum_r x_r x_r^T
+// is formed on the matrix cores (bf16 products are exact in the fp32
+// accumulator; a query row x = s q enters as q (s^2 q) with s^2 q split into
+// three bf16 parts), centred C = S/m - xbar xbar^T, and the p power iterations
+// u <- M C u / |M C u| then run as two d x d matrix-vector products on
+// registers. Wave w of the D/32 waves owns columns [32w, 32w + 32) of C and of
+// M, both held in the MFMA accumulator layout (C and M are symmetric, so a
+// column strip also serves as a row strip). The sample is gathered 128 rows at
+// a time in one round trip and stored transposed (dimension-major) in LDS.
+// ----------------------------------------------------------------------------
+
+template <int D>
+struct DirMma {
+  static constexpr int NW = D / 32;          // waves; wave w owns columns [32w, 32w + 32)
+  static constexpr int NT = 64 * NW;         // threads
+  static constexpr int RT = D / 32;          // 32-row tiles of C per column strip
+  static constexpr int SC = 160;             // sample rows per gather round (the sample
+                                             // averages a D rows; 160 covers it at +3 sd)
+  static constexpr int RPT = SC / 16;        // rows per thread and round
+  static constexpr int XP = SC + 8;          // padded transposed row (bf16): 336 B apart
+  static constexpr int TOKCAP = 4 * SC;      // sample tokens kept in LDS (whole rounds)
+};
+
+template <int D>
+__global__ __launch_bounds__(DirMma<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void pddp_dir_mma(LevelArgs a) {
+  using Cf = DirMma<D>;
+  constexpr int NW = Cf::NW, NT = Cf::NT, RT = Cf::RT, SC = Cf::SC, XP = Cf::XP, RPT = Cf::RPT;
+  constexpr int TOKCAP = Cf::TOKCAP;
+  __shared__ __attribute__((aligned(16))) uint16_t xt[D][XP];
+  __shared__ __attribute__((aligned(16))) float s2c[SC];
+  __shared__ int tokl[TOKCAP];
+  __shared__ __attribute__((aligned(16))) float xbar[D];
+  __shared__ __attribute__((aligned(16))) float su0[D];
+  __shared__ __attribute__((aligned(16))) float tbuf[D];
+  __shared__ __attribute__((aligned(16))) float vbuf[D];
+  __shared__ float red[3][NW];
+  __shared__ int ired[NW];
+  extern __shared__ int spre[];              // chunk prefix sums [nch + 1]
+
+  const int tree = blockIdx.y, slot = blockIdx.x;
+  const int bh = tree >> 1, tensor = tree & 1;
+  int off, n;
+  if (!node_at(a.N, a.c, a.level, slot, &off, &n) || n <= a.c) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 31, h = l >> 5;
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(tensor == 0 ? a.Q : a.K) + (int64_t)bh * a.N * D;
+  const float* svec = tensor == 0 ? a.s + (int64_t)bh * a.N : nullptr;
+  const int32_t* perm = a.perm_in + (int64_t)tree * a.N + off;
+  int32_t* stok = a.zbuf_tok + (int64_t)tree * a.N + off;
+
+  // warm start: component j of the random vector and of the parent direction
+  float rj = 0.0f, pj = 0.0f;
+  if (tid < D) {
+    if (a.level > 0)
+      pj = a.dir_prev[((int64_t)tree * (1 << (a.level - 1)) + (slot >> 1)) * D + tid];
+    uint64_t base = 0;
+    base = chain_step(base, a.seed);
+    base = chain_step(base, kDomainWarm);
+    base = chain_step(base, (uint64_t)bh);
+    base = chain_step(base, (uint64_t)tensor);
+    base = chain_step(base, (uint64_t)a.level);
+    base = chain_step(base, (uint64_t)slot);
+    const uint64_t z = fmix64(base + (uint64_t)(tid + 1) * kGolden);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rj += ((float)((z >> (16 * k)) & 0xFFFFu) + 0.5f) * (1.0f / 65536.0f);
+    rj -= 2.0f;
+  }
+
+  // sample size: prefix over the node's chunk counts
+  const int ch0 = off / a.c;
+  const int nch = (n + a.c - 1) / a.c;
+  const int32_t* cnt = a.chunk_cnt + (int64_t)tree * a.nchunks + ch0;
+  const int per = (nch + NT - 1) / NT;
+  const int g0 = tid * per;
+  int gs = 0;
+  for (int k = 0; k < per; ++k)
+    if (g0 + k < nch) gs += cnt[g0 + k];
+  {
+    const float srr = wave_sum(rj * rj), srp = wave_sum(rj * pj), spp = wave_sum(pj * pj);
+    if (l == 0) { red[0][w] = srr; red[1][w] = srp; red[2][w] = spp; }
+  }
+  int inc = gs;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d, 64);
+    if (l >= d) inc += y;
+  }
+  if (l == 63) ired[w] = inc;
+  __syncthreads();
+  {
+    int run = inc - gs;
+    for (int q = 0; q < w; ++q) run += ired[q];
+    for (int k = 0; k < per; ++k)
+      if (g0 + k < nch) { spre[g0 + k] = run; run += cnt[g0 + k]; }
+    if (tid == NT - 1) spre[nch] = run;
+    // u0 = normalise(parent + r / |r|), or r / |r| at the root
+    float srr = 0.0f, srp = 0.0f, spp = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) { srr += red[0][q]; srp += red[1][q]; spp += red[2][q]; }
+    const float nr = sqrtf(srr);
+    float u0 = rj / nr;
+    if (a.level > 0) {
+      const float ns = sqrtf(spp + 2.0f * (srp / nr) + srr / (nr * nr));
+      if (ns > 0.0f) u0 = (pj + rj / nr) / ns;
+    }
+    if (tid < D) su0[tid] = u0;
+  }
+  __syncthreads();
+  int m = spre[nch];
+  const bool whole = m < 2;     // fewer than two sampled rows: the whole node
+  if (whole) m = n;
+  const int32_t* lists = a.sample_buf + (int64_t)tree * a.N;
+  for (int rr = tid; rr < m; rr += NT) {
+    int tok;
+    if (whole) {
+      tok = perm[rr];
+    } else {
+      int lo = 0, hi = nch - 1;     // last chunk k with spre[k] <= rr
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (spre[mid] <= rr) lo = mid; else hi = mid - 1;
+      }
+      tok = lists[(int64_t)(ch0 + lo) * a.c + (rr - spre[lo])];
+    }
+    if (rr < TOKCAP) tokl[rr] = tok; else stok[rr] = tok;
+  }
+  __syncthreads();
+
+  // --- Gram matrix of the sample on the matrix cores -------------------------
+  // thread (rp, g) gathers rows 32 j + 2 rp + {0, 1} (j < RPT/2) of a round, dims [8g, 8g + 8)
+  const int rp = tid & 15, g = tid >> 4;
+  float msum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) msum[e] = 0.0f;
+  floatx16_t acc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = zero16();
+  // metric M[32 rt + c_row(i, h)][32 w + r], packed per lane by the metric pass
+  u32x4_t mv[RT * 4];
+
+  for (int base = 0;; base += SC) {
+    // sample tokens of the round: LDS for the first TOKCAP rows (whole rounds)
+    int tk[RPT];
+    if (base < TOKCAP) {
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        const int row = base + 32 * (q >> 1) + 2 * rp + (q & 1);
+        tk[q] = row < m ? tokl[row] : -1;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        const int row = base + 32 * (q >> 1) + 2 * rp + (q & 1);
+        tk[q] = row < m ? __builtin_nontemporal_load(stok + row) : -1;
+      }
+    }
+    u32x4_t v[RPT];
+    float sv[RPT];
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+      v[q] = u32x4_t{0u, 0u, 0u, 0u};
+      sv[q] = 0.0f;
+      if (tk[q] >= 0) {
+        v[q] = *reinterpret_cast<const u32x4_t*>(X + (int64_t)tk[q] * D + 8 * g);
+        sv[q] = svec ? svec[tk[q]] : 1.0f;
+      }
+    }
+    if (base > 0) __syncthreads();   // the previous round's operand reads are done
+#pragma unroll
+    for (int j = 0; j < RPT / 2; ++j) {
+      const uint32_t a0[4] = {v[2 * j].x, v[2 * j].y, v[2 * j].z, v[2 * j].w};
+      const uint32_t a1[4] = {v[2 * j + 1].x, v[2 * j + 1].y, v[2 * j + 1].z, v[2 * j + 1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t x0 = (a0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const uint32_t x1 = (a1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        *reinterpret_cast<uint32_t*>(&xt[8 * g + e][32 * j + 2 * rp]) = x0 | (x1 << 16);
+        msum[e] = fmaf(sv[2 * j], bf16_to_f32((uint16_t)x0), msum[e]);
+        msum[e] = fmaf(sv[2 * j + 1], bf16_to_f32((uint16_t)x1), msum[e]);
+      }
+      if (g == 0) {
+        s2c[32 * j + 2 * rp] = sv[2 * j] * sv[2 * j];
+        s2c[32 * j + 2 * rp + 1] = sv[2 * j + 1] * sv[2 * j + 1];
+      }
+    }
+    const bool last = base + SC >= m;
+    __syncthreads();
+    const int nks = min(SC, m - base + 15) >> 4;   // 16-row steps holding sample rows
+    for (int ks = 0; ks < nks; ++ks) {
+      const int k0 = 16 * ks + 8 * h;
+      const u32x4_t bw = *reinterpret_cast<const u32x4_t*>(&xt[32 * w + r][k0]);
+      if (tensor == 1) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const u32x4_t aw = *reinterpret_cast<const u32x4_t*>(&xt[32 * rt + r][k0]);
+          acc[rt] = mfma32(as_bf16x8(aw), as_bf16x8(bw), acc[rt]);
+        }
+      } else {
+        // B = s^2 x as hi + mid + lo bf16 parts (exact to fp32 rounding)
+        const floatx4_t sq0 = *reinterpret_cast<const floatx4_t*>(&s2c[k0]);
+        const floatx4_t sq1 = *reinterpret_cast<const floatx4_t*>(&s2c[k0 + 4]);
+        const float sq[8] = {sq0[0], sq0[1], sq0[2], sq0[3], sq1[0], sq1[1], sq1[2], sq1[3]};
+        const uint32_t bb[4] = {bw.x, bw.y, bw.z, bw.w};
+        float bh_[8], bm_[8], bl_[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float b = bf16_to_f32((uint16_t)((bb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu)) * sq[e];
+          const float hi = (float)(__bf16)b;
+          const float rem = b - hi;
+          const float mid = (float)(__bf16)rem;
+          bh_[e] = hi;
+          bm_[e] = mid;
+          bl_[e] = rem - mid;
+        }
+        const bf16x8_t ph = as_bf16x8(pack8(bh_)), pm = as_bf16x8(pack8(bm_)), pl = as_bf16x8(pack8(bl_));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const bf16x8_t aw = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&xt[32 * rt + r][k0]));
+          acc[rt] = mfma32(aw, ph, acc[rt]);
+          acc[rt] = mfma32(aw, pm, acc[rt]);
+          acc[rt] = mfma32(aw, pl, acc[rt]);
+        }
+      }
+    }
+    if (last) break;
+  }
+  if (a.transform) {   // in flight while the mean and C are formed
+    const u32x4_t* mp = reinterpret_cast<const u32x4_t*>(a.Mpk + ((int64_t)tree * D * D) +
+                                                         (int64_t)(w * 64 + l) * (RT * 16));
+#pragma unroll
+    for (int k = 0; k < RT * 4; ++k) mv[k] = mp[k];
+  }
+  // sample mean: the 16 lanes of a dimension group hold all row pairs
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float v = msum[e];
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+    msum[e] = v;
+  }
+  const float inv_m = 1.0f / (float)m;
+  if (rp == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xbar[8 * g + e] = msum[e] * inv_m;
+  }
+  __syncthreads();
+
+  // C = S / m - xbar xbar^T in place
+  {
+    const float xc = xbar[32 * w + r];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4_t xb = *reinterpret_cast<const floatx4_t*>(&xbar[32 * rt + 8 * q + 4 * h]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[rt][4 * q + k] = fmaf(acc[rt][4 * q + k], inv_m, -xb[k] * xc);
+      }
+  }
+  float mr[RT * 16];
+#pragma unroll
+  for (int k = 0; k < RT * 4; ++k) {
+    mr[4 * k] = __uint_as_float(mv[k].x);
+    mr[4 * k + 1] = __uint_as_float(mv[k].y);
+    mr[4 * k + 2] = __uint_as_float(mv[k].z);
+    mr[4 * k + 3] = __uint_as_float(mv[k].w);
+  }
+
+  // --- power iterations -------------------------------------------------------
+  // Each iteration reads the previous v (the warm start first) once: t = C v
+  // and |v|^2 come from the same values, then t is scaled by 1/|v| (u = v/|v|).
+  // vbuf is rewritten only after the next barrier.
+  bool fallback = false;
+  float inv_norm = 1.0f;
+  for (int it = 0;; ++it) {
+    const float* usrc = it == 0 ? su0 : vbuf;
+    floatx4_t ub[RT * 4];
+#pragma unroll
+    for (int k = 0; k < RT * 4; ++k)
+      ub[k] = *reinterpret_cast<const floatx4_t*>(&usrc[32 * (k >> 2) + 8 * (k & 3) + 4 * h]);
+    __builtin_amdgcn_sched_barrier(0);
+    float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, n4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < RT * 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t4[e] = fmaf(acc[k >> 2][4 * (k & 3) + e], ub[k][e], t4[e]);
+        n4[e] = fmaf(ub[k][e], ub[k][e], n4[e]);
+      }
+    float tp = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+    float nn = (n4[0] + n4[1]) + (n4[2] + n4[3]);
+    tp += __shfl_xor(tp, 32, 64);
+    nn += __shfl_xor(nn, 32, 64);   // the two half-waves' rows cover every index once
+    if (it > 0) {
+      if (nn == 0.0f) { fallback = true; break; }
+      inv_norm = 1.0f / sqrtf(nn);
+      if (it == a.power_iters) break;
+      tp *= inv_norm;
+    }
+    float vp = tp;
+    if (a.transform) {
+      if (h == 0) tbuf[32 * w + r] = tp;
+      __syncthreads();
+      floatx4_t tb[RT * 4];
+#pragma unroll
+      for (int k = 0; k < RT * 4; ++k)
+        tb[k] = *reinterpret_cast<const floatx4_t*>(&tbuf[32 * (k >> 2) + 8 * (k & 3) + 4 * h]);
+      __builtin_amdgcn_sched_barrier(0);
+      float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < RT * 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = fmaf(mr[4 * k + e], tb[k][e], v4[e]);
+      vp = (v4[0] + v4[1]) + (v4[2] + v4[3]);
+      vp += __shfl_xor(vp, 32, 64);
+    }
+    if (h == 0) vbuf[32 * w + r] = vp;
+    __syncthreads();
+  }
+  float* out = a.dir_cur + ((int64_t)tree * (1 << a.level) + slot) * D;
+  if (tid < D) {
+    const float v = fallback ? su0[tid] : vbuf[tid] * inv_norm;
+    out[tid] = v;
+    if (a.trace_dir) a.trace_dir[((int64_t)tree * a.trace_slots + slot) * D + tid] = v;
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Projection of every member of every splitting node
 // ----------------------------------------------------------------------------
 
@@ -644,14 +973,20 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
   dim3 gslots(1u << a.level, trees);
   dim3 gspan((a.N + kSampleSpan - 1) / kSampleSpan, trees);
   pddp_sample<<<gspan, 256, 0, st>>>(a);
-  const size_t lds = dir_smem<T, D>(a.N, a.c, a.level);
-  static size_t lds_allowed = 0;   // raise the dynamic-LDS limit when a level needs more
-  if (lds > lds_allowed) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&pddp_dir<T, D>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    lds_allowed = lds;
+  if constexpr (sizeof(T) == 2) {
+    const int64_t nmax = ((int64_t)a.N >> a.level) + 2 * (int64_t)a.c;   // bounds every node
+    const size_t lds = (size_t)((nmax + a.c - 1) / a.c + 2) * 4;
+    pddp_dir_mma<D><<<gslots, DirMma<D>::NT, lds, st>>>(a);
+  } else {
+    const size_t lds = dir_smem<T, D>(a.N, a.c, a.level);
+    static size_t lds_allowed = 0;   // raise the dynamic-LDS limit when a level needs more
+    if (lds > lds_allowed) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&pddp_dir<T, D>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      lds_allowed = lds;
+    }
+    pddp_dir<T, D><<<gslots, 256, lds, st>>>(a);
   }
-  pddp_dir<T, D><<<gslots, 256, lds, st>>>(a);
   dim3 gproj((a.N + a.c - 1) / a.c, trees);
   pddp_project<T, D><<<gproj, 256, 0, st>>>(a);
   pddp_split<<<gslots, kSplitThreads, 0, st>>>(a);

@@ -10,7 +10,7 @@ int metric_rows_per_chunk(int N);
 // dtype: 0 = bf16, 1 = fp32. partial: [BH][nchunks][2 D D + D] fp32 scratch.
 void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D, int transform,
                    int query_normalize, float* partial, uint64_t* hash, float* Mq, float* Mk,
-                   float* kbar, uint16_t* gsplit, float* s, hipStream_t st);
+                   float* kbar, uint16_t* gsplit, float* s, float* Mpk, hipStream_t st);
 
 // cluster.hip ----------------------------------------------------------------
 struct LevelArgs {
@@ -26,6 +26,8 @@ struct LevelArgs {
   const float* s;           // [BH][N]
   const float* Mq;          // [BH][D][D]
   const float* Mk;          // [BH][D][D]
+  const float* Mpk;         // [2 BH][D D]: metric of each tree (M_k for queries, M_q for
+                            // keys) packed in the per-lane order of the direction kernel
   const float* dir_prev;    // [2 BH][slots/2][D]
   float* dir_cur;           // [2 BH][slots][D]
   int nchunks;              // ceil(N / c)

@@ -196,7 +196,8 @@ __global__ __launch_bounds__(256) void metric_reduce(const float* __restrict__ p
                                                      float* __restrict__ Mq,
                                                      float* __restrict__ Mk,
                                                      float* __restrict__ kbar,
-                                                     uint16_t* __restrict__ gsplit) {
+                                                     uint16_t* __restrict__ gsplit,
+                                                     float* __restrict__ Mpk) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= D * D) return;
@@ -216,6 +217,15 @@ __global__ __launch_bounds__(256) void metric_reduce(const float* __restrict__ p
   const float mk = sk * invN - kma * kmb;
   Mq[(int64_t)bh * D * D + e] = mq;
   Mk[(int64_t)bh * D * D + e] = mk;
+  {
+    // element (a, b) sits in wave b/32, lane (b % 32) + 32 h, slot 16 (a/32) + i of
+    // the direction kernel, where a % 32 = 8 (i/4) + 4 h + i % 4 (the MFMA
+    // accumulator row order)
+    const int rr = a & 31, hh = (rr >> 2) & 1, ii = 4 * (rr >> 3) + (rr & 3);
+    const int64_t pk = (int64_t)((b >> 5) * 64 + (b & 31) + 32 * hh) * (D / 2) + 16 * (a >> 5) + ii;
+    Mpk[(int64_t)(2 * bh) * D * D + pk] = mk;
+    Mpk[(int64_t)(2 * bh + 1) * D * D + pk] = mq;
+  }
   if (a == 0) kbar[(int64_t)bh * D + b] = kmb;
   const float g = transform ? mk : (a == b ? 1.0f : 0.0f);
   const uint16_t hi = f32_to_bf16(g);
@@ -329,7 +339,7 @@ int metric_rows_per_chunk(int N) {
 
 void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D, int transform,
                    int query_normalize, float* partial, uint64_t* hash, float* Mq, float* Mk,
-                   float* kbar, uint16_t* gsplit, float* s, hipStream_t st) {
+                   float* kbar, uint16_t* gsplit, float* s, float* Mpk, hipStream_t st) {
   const int rows = metric_rows_per_chunk(N);
   const int nchunks = (N + rows - 1) / rows;
   dim3 gp(nchunks, BH);
@@ -345,8 +355,8 @@ void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D
     else metric_partial_f32<float, 128><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash);
   }
   dim3 gr((D * D + 255) / 256, BH);
-  if (D == 64) metric_reduce<64><<<gr, 256, 0, st>>>(partial, nchunks, N, transform, Mq, Mk, kbar, gsplit);
-  else metric_reduce<128><<<gr, 256, 0, st>>>(partial, nchunks, N, transform, Mq, Mk, kbar, gsplit);
+  if (D == 64) metric_reduce<64><<<gr, 256, 0, st>>>(partial, nchunks, N, transform, Mq, Mk, kbar, gsplit, Mpk);
+  else metric_reduce<128><<<gr, 256, 0, st>>>(partial, nchunks, N, transform, Mq, Mk, kbar, gsplit, Mpk);
   if (!query_normalize) {
     int64_t n = (int64_t)BH * N;
     fill_f32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(s, n, 1.0f);
