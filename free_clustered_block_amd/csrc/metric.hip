@@ -238,65 +238,93 @@ __global__ __launch_bounds__(256) void metric_reduce(const float* __restrict__ p
   gs[2 * D * D + e] = lo;
 }
 
-// s_i = (q_i^T G q_i)^{-1/2} (0 if q^T G q <= 0). Y = Q G^T on MFMA with G as
-// hi + mid + lo bf16 terms, then t_i = sum_n Y[i][n] Q[i][n].
+constexpr int kQnormSpan = 1024;   // queries per workgroup of qnorm_bf16
+
+// s_i = (q_i^T G q_i)^{-1/2} (0 if q^T G q <= 0). Y^T = G Q^T on the matrix
+// cores with G as hi + mid + lo bf16 terms held as A operands for the block's
+// lifetime; query tiles stream through LDS (double-buffered) as B operands,
+// then t_i = sum_n Y^T[n][i] q_i[n] from the accumulator rows. Wave w computes
+// rows [32 (w % NB), +32) of Y^T for query group w / NB of each tile.
 template <int D>
 __global__ __launch_bounds__(256) void qnorm_bf16(const uint16_t* __restrict__ Q, int N,
                                                   const uint16_t* __restrict__ gsplit,
                                                   float* __restrict__ s_out) {
-  constexpr int NB = D / 32;
-  constexpr int KS = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t sq[4][32][D + 8];
-  const int bh = blockIdx.y;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, r = l & 31;
-  const int t0 = blockIdx.x * 128 + w * 32;
+  constexpr int NB = D / 32;                 // 32-row blocks of Y^T
+  constexpr int QG = 4 / NB;                 // query groups of 32 per tile
+  constexpr int KS = D / 16;                 // MFMA k-steps
+  constexpr int QP = D + 8;                  // padded query row (bf16)
+  constexpr int TILE = 32 * QG;              // queries per step
+  constexpr int PPT = TILE * D / 8 / 256;    // 16-byte pieces per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t sq[2][TILE][QP];
+  __shared__ float tred[2][NB][TILE];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
+  const int bn = w % NB, qg = w / NB;
   const uint16_t* Qh = Q + (int64_t)bh * N * D;
   const uint16_t* G = gsplit + (int64_t)bh * 3 * D * D;
+  const int q0 = blockIdx.x * kQnormSpan;
+  const int qend = min(N, q0 + kQnormSpan);
 
-  bf16x8_t qa[KS];
-  const int tok = t0 + r;
+  u32x4_t st[PPT];
+  auto load_tile = [&](int t0) {
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (tok < N) v = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)tok * D + s * 16 + h * 8);
-    qa[s] = as_bf16x8(v);
-    *reinterpret_cast<u32x4_t*>(&sq[w][r][s * 16 + h * 8]) = v;
-  }
+    for (int k = 0; k < PPT; ++k) {
+      const int idx = tid + 256 * k, row = idx / (D / 8), pc = idx % (D / 8);
+      st[k] = u32x4_t{0u, 0u, 0u, 0u};
+      if (t0 + row < qend) st[k] = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)(t0 + row) * D + 8 * pc);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int idx = tid + 256 * k, row = idx / (D / 8), pc = idx % (D / 8);
+      *reinterpret_cast<u32x4_t*>(&sq[buf][row][8 * pc]) = st[k];
+    }
+  };
+  load_tile(q0);
+  // A operands: rows [32 bn, 32 bn + 32) of the three parts of G
+  bf16x8_t ga[3][KS];
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      ga[p][s] = *reinterpret_cast<const bf16x8_t*>(G + (int64_t)p * D * D +
+                                                    (int64_t)(32 * bn + r) * D + 16 * s + 8 * h);
+  store_tile(0);
   __syncthreads();
-  float part[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) part[i] = 0.0f;
-#pragma unroll
-  for (int bn = 0; bn < NB; ++bn) {
+  int buf = 0;
+  for (int t0 = q0; t0 < qend; t0 += TILE) {
+    const bool more = t0 + TILE < qend;
+    if (more) load_tile(t0 + TILE);
     floatx16_t y = zero16();
+    const uint16_t* qrow = &sq[buf][32 * qg + r][0];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8_t bq = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s + 8 * h);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        bf16x8_t gb = *reinterpret_cast<const bf16x8_t*>(
-            G + (int64_t)p * D * D + (int64_t)(bn * 32 + r) * D + s * 16 + h * 8);
-        y = mfma32(qa[s], gb, y);
-      }
+      for (int p = 0; p < 3; ++p) y = mfma32(ga[p][s], bq, y);
     }
+    // lane (r, h) holds Y^T[32 bn + c_row(i, h)][query r]
+    float tp = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) part[i] += y[i] * bf16_to_f32(sq[w][c_row(i, h)][bn * 32 + r]);
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float v = part[i];
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, 64);
-    part[i] = v;
-  }
-  if (r == 0) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tk = t0 + c_row(i, h);
-      if (tk < N) {
-        const float t = part[i];
-        s_out[(int64_t)bh * N + tk] = t > 0.0f ? 1.0f / sqrtf(t) : 0.0f;
-      }
+    for (int jq = 0; jq < 4; ++jq) {
+      const u32x2_t qv = *reinterpret_cast<const u32x2_t*>(qrow + 32 * bn + 8 * jq + 4 * h);
+      tp = fmaf(y[4 * jq + 0], bf16_to_f32((uint16_t)(qv.x & 0xFFFFu)), tp);
+      tp = fmaf(y[4 * jq + 1], bf16_to_f32((uint16_t)(qv.x >> 16)), tp);
+      tp = fmaf(y[4 * jq + 2], bf16_to_f32((uint16_t)(qv.y & 0xFFFFu)), tp);
+      tp = fmaf(y[4 * jq + 3], bf16_to_f32((uint16_t)(qv.y >> 16)), tp);
     }
+    tp += __shfl_xor(tp, 32, 64);
+    if (h == 0) tred[buf][bn][32 * qg + r] = tp;
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+    if (tid < TILE && t0 + tid < qend) {
+      float t = 0.0f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) t += tred[buf][b][tid];
+      s_out[(int64_t)bh * N + t0 + tid] = t > 0.0f ? 1.0f / sqrtf(t) : 0.0f;
+    }
+    buf ^= 1;
   }
 }
 
@@ -363,7 +391,7 @@ void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D
     return;
   }
   if (dtype == 0) {
-    dim3 gq((N + 127) / 128, BH);
+    dim3 gq((N + kQnormSpan - 1) / kQnormSpan, BH);
     if (D == 64) qnorm_bf16<64><<<gq, 256, 0, st>>>((const uint16_t*)Q, N, gsplit, s);
     else qnorm_bf16<128><<<gq, 256, 0, st>>>((const uint16_t*)Q, N, gsplit, s);
   } else {
