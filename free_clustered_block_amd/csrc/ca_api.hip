@@ -51,7 +51,7 @@ struct ClusterWs {
 ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c) {
   ClusterWs w;
   const size_t T = 2 * (size_t)BH;
-  const int rows = metric_rows_per_chunk(N);
+  const int rows = metric_rows_per_chunk(N, BH);
   const size_t nchunks = (N + rows - 1) / rows;
   const int L = tree_levels_host(N, c);
   const size_t slots = L > 0 ? ((size_t)1 << (L - 1)) : 1;

@@ -6,7 +6,7 @@
 namespace ca {
 
 // metric.hip -----------------------------------------------------------------
-int metric_rows_per_chunk(int N);
+int metric_rows_per_chunk(int N, int BH);
 // dtype: 0 = bf16, 1 = fp32. partial: [BH][nchunks][2 D D + D] fp32 scratch.
 void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D, int transform,
                    int query_normalize, float* partial, uint64_t* hash, float* Mq, float* Mk,

@@ -12,7 +12,7 @@ namespace ca {
 
 namespace {
 
-constexpr int kMetricTile = 64;   // tokens per LDS tile
+constexpr int kMetricTile = 128;  // tokens per LDS tile
 
 // Row content hash: fmix64(sum_j w_j golden^(j+1) mod 2^64) over the row's
 // 32-bit words; hash_word gives one term of the sum.
@@ -32,6 +32,10 @@ __constant__ HashPow kHashPow = make_hash_pow();
 
 CA_DEV uint64_t hash_word(uint32_t j, uint32_t w) { return (uint64_t)w * kHashPow.v[j]; }
 
+// One workgroup per (chunk of rows, head, tensor): tiles of 128 tokens are
+// read one round trip ahead as token pairs, stored transposed in LDS and fed
+// to the matrix cores; the row hashes and the key sums come from the same
+// registers.
 template <int D>
 __global__ __launch_bounds__(256) void metric_partial_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int N, int rows_per_chunk,
@@ -39,73 +43,86 @@ __global__ __launch_bounds__(256) void metric_partial_bf16(
   constexpr int TT = kMetricTile;
   constexpr int NB = D / 32;
   constexpr int BPW = NB * NB / 4;          // 32x32 blocks per wave
-  constexpr int LDT = TT + 8;               // padded token stride in LDS
+  constexpr int LDT = TT + 8;               // padded token stride in LDS (272 B)
+  constexpr int TP = TT / 2;                // token pairs per tile
+  constexpr int GI = 256 / TP;              // group slots
   constexpr int GROUPS = D / 8;             // 16-byte groups per row
-  constexpr int GPT = GROUPS / 4;           // groups per thread
-  __shared__ __attribute__((aligned(16))) uint16_t sx[2][D][LDT];
-  __shared__ uint64_t shash[2][4][TT];
+  constexpr int GPT = GROUPS / GI;          // groups per thread
+  __shared__ __attribute__((aligned(16))) uint16_t sx[D][LDT];
+  __shared__ uint64_t shash[GI][TT];
 
-  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int bh = blockIdx.y, chunk = blockIdx.x, t = blockIdx.z;
   const int r0 = chunk * rows_per_chunk;
   const int r1 = min(N, r0 + rows_per_chunk);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
-  const uint16_t* X[2] = {Q + (int64_t)bh * N * D, K + (int64_t)bh * N * D};
+  // thread (tp, gi): tokens 2 tp, 2 tp + 1 of each tile, groups gi + GI k
+  const int tp = tid % TP, gi = tid / TP;
+  const uint16_t* X = (t == 0 ? Q : K) + (int64_t)bh * N * D;
+  uint64_t hpow[GPT][4];
+#pragma unroll
+  for (int k = 0; k < GPT; ++k)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hpow[k][q] = kHashPow.v[4 * (gi + GI * k) + q];
 
-  floatx16_t acc[2][BPW];
+  floatx16_t acc[BPW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) acc[t][i] = zero16();
+  for (int i = 0; i < BPW; ++i) acc[i] = zero16();
   float ksum[GPT][8];
 #pragma unroll
-  for (int i = 0; i < GPT; ++i)
+  for (int k = 0; k < GPT; ++k)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ksum[i][e] = 0.0f;
+    for (int e = 0; e < 8; ++e) ksum[k][e] = 0.0f;
 
+  u32x4_t pre[GPT][2];
+  auto fetch = [&](int base) {
+#pragma unroll
+    for (int k = 0; k < GPT; ++k)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int tok = base + 2 * tp + q;
+        pre[k][q] = u32x4_t{0u, 0u, 0u, 0u};
+        if (tok < r1) pre[k][q] = *reinterpret_cast<const u32x4_t*>(X + (int64_t)tok * D + 8 * (gi + GI * k));
+      }
+  };
+  fetch(r0);
   for (int base = r0; base < r1; base += TT) {
-    const int tok = base + l;
-    const bool valid = tok < r1;
+    uint64_t hp0 = 0, hp1 = 0;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint64_t hp = 0;
+    for (int k = 0; k < GPT; ++k) {
+      const int g = gi + GI * k;
+      const uint32_t a0[4] = {pre[k][0].x, pre[k][0].y, pre[k][0].z, pre[k][0].w};
+      const uint32_t a1[4] = {pre[k][1].x, pre[k][1].y, pre[k][1].z, pre[k][1].w};
 #pragma unroll
-      for (int i = 0; i < GPT; ++i) {
-        const int g = w + 4 * i;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (valid) v = *reinterpret_cast<const u32x4_t*>(X[t] + (int64_t)tok * D + 8 * g);
-        const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          sx[t][8 * g + 2 * q][l] = (uint16_t)(ws[q] & 0xFFFFu);
-          sx[t][8 * g + 2 * q + 1][l] = (uint16_t)(ws[q] >> 16);
-          hp += hash_word((uint32_t)(4 * g + q), ws[q]);
-          if (t == 1) {
-            ksum[i][2 * q] += bf16_to_f32((uint16_t)(ws[q] & 0xFFFFu));
-            ksum[i][2 * q + 1] += bf16_to_f32((uint16_t)(ws[q] >> 16));
-          }
+      for (int q = 0; q < 4; ++q) {
+        hp0 += (uint64_t)a0[q] * hpow[k][q];
+        hp1 += (uint64_t)a1[q] * hpow[k][q];
+        // dims 8g + 2q (low halves) and 8g + 2q + 1 (high halves) of the two tokens
+        *reinterpret_cast<uint32_t*>(&sx[8 * g + 2 * q][2 * tp]) = (a0[q] & 0xFFFFu) | (a1[q] << 16);
+        *reinterpret_cast<uint32_t*>(&sx[8 * g + 2 * q + 1][2 * tp]) = (a0[q] >> 16) | (a1[q] & 0xFFFF0000u);
+        if (t == 1) {
+          ksum[k][2 * q] += bf16_to_f32((uint16_t)(a0[q] & 0xFFFFu)) + bf16_to_f32((uint16_t)(a1[q] & 0xFFFFu));
+          ksum[k][2 * q + 1] += bf16_to_f32((uint16_t)(a0[q] >> 16)) + bf16_to_f32((uint16_t)(a1[q] >> 16));
         }
       }
-      shash[t][w][l] = hp;
     }
+    shash[gi][2 * tp] = hp0;
+    shash[gi][2 * tp + 1] = hp1;
     __syncthreads();
-    if (tid < 2 * TT) {
-      const int t = tid / TT, j = tid % TT;
-      if (base + j < r1) {
-        uint64_t s = shash[t][0][j] + shash[t][1][j] + shash[t][2][j] + shash[t][3][j];
-        hash[((int64_t)bh * 2 + t) * N + base + j] = fmix64(s);
-      }
+    if (base + TT < r1) fetch(base + TT);   // next tile in flight during the products
+    if (tid < TT && base + tid < r1) {
+      uint64_t s = 0;
+#pragma unroll
+      for (int q = 0; q < GI; ++q) s += shash[q][tid];
+      hash[((int64_t)bh * 2 + t) * N + base + tid] = fmix64(s);
     }
 #pragma unroll
     for (int s = 0; s < TT / 16; ++s) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-          const int b = w * BPW + i, bm = b / NB, bn = b % NB;
-          bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sx[t][bm * 32 + r][s * 16 + h * 8]);
-          bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sx[t][bn * 32 + r][s * 16 + h * 8]);
-          acc[t][i] = mfma32(a, bb, acc[t][i]);
-        }
+      for (int i = 0; i < BPW; ++i) {
+        const int b = w * BPW + i, bm = b / NB, bn = b % NB;
+        bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sx[bm * 32 + r][s * 16 + h * 8]);
+        bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sx[bn * 32 + r][s * 16 + h * 8]);
+        acc[i] = mfma32(a, bb, acc[i]);
       }
     }
     __syncthreads();
@@ -113,22 +130,24 @@ __global__ __launch_bounds__(256) void metric_partial_bf16(
 
   float* out = partial + ((int64_t)bh * nchunks + chunk) * (2 * D * D + D);
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int i = 0; i < BPW; ++i) {
+    const int b = w * BPW + i, bm = b / NB, bn = b % NB;
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int b = w * BPW + i, bm = b / NB, bn = b % NB;
+    for (int e = 0; e < 16; ++e)
+      out[t * D * D + (bm * 32 + c_row(e, h)) * D + bn * 32 + r] = acc[i][e];
+  }
+  if (t == 1) {
+    // key sums: the TP token-pair lanes of a group (fixed butterfly order)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        out[t * D * D + (bm * 32 + c_row(e, h)) * D + bn * 32 + r] = acc[t][i][e];
-    }
-  // key sums: reduce the 64 lanes of each wave (fixed butterfly order)
+    for (int k = 0; k < GPT; ++k)
 #pragma unroll
-  for (int i = 0; i < GPT; ++i)
+      for (int e = 0; e < 8; ++e) {
+        float v = ksum[k][e];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = wave_sum(ksum[i][e]);
-      if (l == 0) out[2 * D * D + 8 * (w + 4 * i) + e] = v;
-    }
+        for (int o = 1; o < TP; o <<= 1) v += __shfl_xor(v, o, 64);
+        if (tp == 0) out[2 * D * D + 8 * (gi + GI * k) + e] = v;
+      }
+  }
 }
 
 template <typename T, int D>
@@ -358,22 +377,27 @@ __global__ void fill_f32(float* p, int64_t n, float v) {
 
 }  // namespace
 
-int metric_rows_per_chunk(int N) {
-  // ~4096 rows per workgroup, a multiple of the 64-token tile
-  int chunks = (N + 4095) / 4096;
-  int rows = (N + chunks - 1) / chunks;
-  return (rows + kMetricTile - 1) / kMetricTile * kMetricTile;
+int metric_rows_per_chunk(int N, int BH) {
+  // about 384 chunks over all heads (768 workgroups with the two tensors,
+  // three per CU), at least 256 rows each,
+  // a multiple of the 64-token tile
+  const int64_t want = (384 + BH - 1) / BH;
+  const int64_t most = ((int64_t)N + 255) / 256;
+  const int64_t chunks = want < most ? want : most;
+  const int64_t rows = ((int64_t)N + chunks - 1) / chunks;
+  return (int)((rows + kMetricTile - 1) / kMetricTile * kMetricTile);
 }
 
 void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D, int transform,
                    int query_normalize, float* partial, uint64_t* hash, float* Mq, float* Mk,
                    float* kbar, uint16_t* gsplit, float* s, float* Mpk, hipStream_t st) {
-  const int rows = metric_rows_per_chunk(N);
+  const int rows = metric_rows_per_chunk(N, BH);
   const int nchunks = (N + rows - 1) / rows;
   dim3 gp(nchunks, BH);
   if (dtype == 0) {
     const uint16_t* q = (const uint16_t*)Q;
     const uint16_t* k = (const uint16_t*)K;
+    gp.z = 2;
     if (D == 64) metric_partial_bf16<64><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash);
     else metric_partial_bf16<128><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash);
   } else {
