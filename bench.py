@@ -155,9 +155,27 @@ def measure_peaks(torch, dev):
         b_ev.record()
     torch.cuda.synchronize()
     gemm_ms = float(np.median([a_ev.elapsed_time(b_ev) for a_ev, b_ev in ev]))
+    del a, b
+    # matrix-core and LDS probes of the library: 2 workgroups of 4 waves per CU
+    import free_clustered_block_amd as ca
+    blocks, iters = 512, 20000
+    out = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
+    rates = {}
+    for kind, name in ((0, "mfma"), (1, "lds")):
+        ca.peak_probe(kind, blocks, 100, out)
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record()
+        ca.peak_probe(kind, blocks, iters, out)
+        b_ev.record()
+        torch.cuda.synchronize()
+        rates[name] = a_ev.elapsed_time(b_ev) * 1e-3
+    mfma_tf = blocks * 4 * 4 * iters * 32768.0 / rates["mfma"] / 1e12
+    lds_tbs = blocks * 4 * 8 * iters * 1024.0 / rates["lds"] / 1e12
     return {"hbm_copy_GBs": round(2.0 * n * 2 / (copy_ms * 1e-3) / 1e9, 1),
             "copy_bytes": 2 * n * 2,
-            "bf16_gemm_TFLOPs": round(2.0 * m ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
+            "bf16_gemm_TFLOPs": round(2.0 * m ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "mfma_loop_TFLOPs": round(mfma_tf, 1),
+            "lds_read_TBs": round(lds_tbs, 2)}
 
 
 def main():

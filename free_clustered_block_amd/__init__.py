@@ -16,13 +16,13 @@ import os
 from dataclasses import dataclass
 
 __all__ = [
-    "CAError", "load", "LIB_PATH", "EXPORTS", "profile_events", "HipEvent", "tree_levels",
+    "CAError", "load", "LIB_PATH", "EXPORTS", "profile_events", "peak_probe", "HipEvent", "tree_levels",
     "workspace_size", "cluster", "route", "attend", "dense", "forward", "ClusterResult",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libca.so")
 EXPORTS = ["ca_tree_levels", "ca_workspace_size", "ca_cluster", "ca_route", "ca_attend",
-           "ca_dense", "ca_profile_events", "ca_status_string", "ca_last_error"]
+           "ca_dense", "ca_profile_events", "ca_peak_probe", "ca_status_string", "ca_last_error"]
 
 CA_BF16, CA_F32 = 0, 1
 OP_CLUSTER, OP_ROUTE, OP_ATTEND, OP_DENSE = 0, 1, 2, 3
@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
     lib.ca_attend.restype = I
     lib.ca_dense.argtypes = [P, P, P, I, I, I, I, I, F, P, P, P, S, P]
     lib.ca_dense.restype = I
+    lib.ca_peak_probe.argtypes = [I, I, I, P, P]
+    lib.ca_peak_probe.restype = I
     lib.ca_profile_events.argtypes = [P, P]
     lib.ca_profile_events.restype = I
     lib.ca_status_string.argtypes = [I]
@@ -87,6 +89,15 @@ def profile_events(start=None, stop=None) -> None:
     attention kernel of the following attend/dense calls on this thread;
     None, None switches it off."""
     load().ca_profile_events(start, stop)
+
+
+def peak_probe(kind: int, blocks: int, iters: int, out) -> None:
+    """Launch the matrix-core (kind 0) or LDS (kind 1) peak-rate probe on the
+    current stream; ``out`` is a float32 device tensor of blocks * 4 elements."""
+    import torch
+    if out.dtype != torch.float32 or out.numel() < blocks * 4 or not out.is_cuda:
+        raise ValueError("out must be a float32 device tensor of at least blocks * 4 elements")
+    _check(load().ca_peak_probe(kind, blocks, iters, out.data_ptr(), _stream_ptr(out.device)))
 
 
 class HipEvent:

@@ -302,6 +302,16 @@ int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, in
   return after_launch();
 }
 
+int ca_peak_probe(int kind, int blocks, int iters, float* out, void* stream) {
+  if ((kind != 0 && kind != 1) || blocks < 1 || blocks > 65535 || iters < 1 || !out)
+    return fail(CA_ERR_INVALID_ARG, "ca_peak_probe: kind must be 0 or 1, blocks in [1, 65535], iters >= 1, out non-null");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (kind == 0) launch_peak_mfma(blocks, iters, out, st);
+  else launch_peak_lds(blocks, iters, out, st);
+  CA_HIP_CHECK(hipGetLastError());
+  return CA_OK;
+}
+
 int ca_profile_events(void* start, void* stop) {
   g_prof_start = (start && stop) ? static_cast<hipEvent_t>(start) : nullptr;
   g_prof_stop = (start && stop) ? static_cast<hipEvent_t>(stop) : nullptr;

@@ -81,6 +81,10 @@ struct AttnArgs {
 // centroid count padded to whole 32-blocks
 CA_HD int attn_ncp(int nc) { return (nc + 31) / 32 * 32; }
 void launch_attend(const AttnArgs& a, hipStream_t st);
+
+// peak.hip -------------------------------------------------------------------
+void launch_peak_mfma(int blocks, int iters, float* out, hipStream_t st);
+void launch_peak_lds(int blocks, int iters, float* out, hipStream_t st);
 void launch_dense(const AttnArgs& a, hipStream_t st);
 
 }  // namespace ca

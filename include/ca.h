@@ -191,6 +191,19 @@ int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, in
  */
 int ca_profile_events(void* start, void* stop);
 
+/*
+ * Peak-rate probe (a measurement utility beside the path, not part of it).
+ * kind 0: `blocks` workgroups of 4 waves each issue 4 x iters independent
+ *         v_mfma_f32_32x32x16_bf16 (32768 FLOP each) from registers.
+ * kind 1: `blocks` workgroups of 4 waves each issue 8 x iters conflict-free
+ *         ds_read_b128 (1 KB per wave instruction) from LDS.
+ * out: device float [blocks * 4], written with a checksum per wave.
+ * The caller times the call with events on `stream`. Returns
+ * CA_ERR_INVALID_ARG for a bad kind, blocks outside [1, 65535], iters < 1 or
+ * a null out.
+ */
+int ca_peak_probe(int kind, int blocks, int iters, float* out, void* stream);
+
 /* Static description of a status code. */
 const char* ca_status_string(int status);
 

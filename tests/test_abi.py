@@ -114,3 +114,10 @@ def test_route_and_dense_reject_bad_arguments(lib):
     assert lib.ca_dense(FAKE, FAKE, None, 0, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 0, None) == 1
     assert lib.ca_dense(FAKE, FAKE, FAKE, 0, 1, 1, 128, 80, 0.0, FAKE, None, FAKE, 0, None) == 2
     assert lib.ca_dense(FAKE, FAKE, FAKE, 0, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 8, None) == 3
+
+
+def test_peak_probe_rejects_bad_arguments(lib):
+    assert lib.ca_peak_probe(2, 1, 1, FAKE, None) == 1
+    assert lib.ca_peak_probe(0, 0, 1, FAKE, None) == 1
+    assert lib.ca_peak_probe(1, 1, 0, FAKE, None) == 1
+    assert lib.ca_peak_probe(0, 1, 1, None, None) == 1
