@@ -13,9 +13,11 @@
 //                double-buffered sub-tiles of 64 keys, S^T = K Q^T and
 //                O^T += V^T P^T run on
 //                v_mfma_f32_32x32x16_bf16 with an fp32 online softmax (exp2);
-//                the excluded clusters then enter through their centroids
-//                (logit scale q.kbar + ln n_c, value vbar) in the same running
-//                maximum and sum. O is scattered back to token order.
+//                the excluded clusters then enter through their centroids,
+//                streamed the same way as sub-tiles of 64 centroids (bf16
+//                kbar rows as keys, vbar as values, logit scale q.kbar +
+//                ln n_c, -inf for selected or padding clusters) in the same
+//                running maximum and sum. O is scattered back to token order.
 // fp32 path: the same computation on VALU, one thread per query.
 #include "kernels.h"
 #include "mfma.h"
@@ -55,13 +57,10 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
   const int c = a.c, nc = a.nc, ncp = attn_ncp(nc);
   const int tid = threadIdx.x;
   if (j >= nc) {
-    // centroid padding up to a multiple of 32: zero vectors with ln n = -inf
+    // centroid padding up to a whole sub-tile: zero vectors with ln n = -inf
     for (int d = tid; d < D; d += 256) {
       a.kbar_hi[((int64_t)bh * ncp + j) * D + d] = 0;
-      a.kbar_lo[((int64_t)bh * ncp + j) * D + d] = 0;
       a.vbar_t[((int64_t)bh * D + d) * ncp + vslot(j)] = 0;
-      a.kbar32[((int64_t)bh * ncp + j) * D + d] = 0.0f;
-      a.vbar32[((int64_t)bh * ncp + j) * D + d] = 0.0f;
     }
     if (tid == 0) a.logn[(int64_t)bh * ncp + j] = kNegInf;
     return;
@@ -134,12 +133,8 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
     for (int q = 0; q < G; ++q) { ks += sk[q][d]; vs += sm[q][d]; }
     const float inv = 1.0f / (float)nj;
     const float kb = ks * inv, vb = vs * inv;
-    const uint16_t hi = f32_to_bf16(kb);
-    a.kbar_hi[((int64_t)bh * ncp + j) * D + d] = hi;
-    a.kbar_lo[((int64_t)bh * ncp + j) * D + d] = f32_to_bf16(kb - bf16_to_f32(hi));
+    a.kbar_hi[((int64_t)bh * ncp + j) * D + d] = f32_to_bf16(kb);
     a.vbar_t[((int64_t)bh * D + d) * ncp + vslot(j)] = f32_to_bf16(vb);
-    a.kbar32[((int64_t)bh * ncp + j) * D + d] = kb;
-    a.vbar32[((int64_t)bh * ncp + j) * D + d] = vb;
     if (d == 0) a.logn[(int64_t)bh * ncp + j] = logf((float)nj);
   }
 }
@@ -213,9 +208,25 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 
   const int nsel = DENSE ? nc : a.topk;
   const int32_t* blk = DENSE ? nullptr : a.blocks + ((int64_t)bh * nc + qa) * a.topk;
-  const int T = nsel * SUB;   // sub-tiles to process
+  // Token sub-tiles of the selected clusters come first; with compensation the
+  // centroids follow as ncp / 64 more sub-tiles of 64 (kbar rows as keys,
+  // vbar as values) whose logits get + ln n_c, or -inf for a selected or
+  // padding cluster, in the same running maximum and sum.
+  const int Tm = nsel * SUB;
+  const int ncp = attn_ncp(nc);
+  const bool comp = !DENSE && a.compensate;
+  const int T = Tm + (comp ? ncp / TL::KT : 0);
+  if (comp) {
+    for (int e = tid; e < ncp / 32; e += NT) sSel[e] = 0u;
+    __syncthreads();
+    for (int e = tid; e < a.topk; e += NT) {
+      const int j = blk[e];
+      if (j >= 0 && j < nc) atomicOr(&sSel[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+  }
 
-  // cluster of sub-tile t (out-of-range block entries are skipped)
+  // cluster of token sub-tile t (out-of-range block entries are skipped)
   auto tile_cluster = [&](int t) -> int {
     const int j = DENSE ? t / SUB : blk[t / SUB];
     return (j >= 0 && j < nc) ? j : -1;
@@ -224,17 +235,31 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   constexpr int KLPT = TL::K_LOADS / NT, VLPT = TL::V_LOADS / NT;
   u32x4_t kst[KLPT], vst[VLPT];
   auto fetch = [&](int t) {
-    int j = tile_cluster(t);
-    if (j < 0) j = 0;   // any valid tile; its results are not used
-    const int part = t % SUB;
-    const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(
-        a.kc + (((int64_t)bh * nc + j) * C + part * TL::KT) * D);
-    const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(
-        a.vt + (((int64_t)bh * nc + j) * SUB + part) * (int64_t)D * TL::KT);
+    const u32x4_t* ks;
+    const unsigned char* vs;
+    int vstride;   // bytes between V^T rows of the sub-tile
+    if (t < Tm) {
+      int j = tile_cluster(t);
+      if (j < 0) j = 0;   // any valid tile; its results are not used
+      const int part = t % SUB;
+      ks = reinterpret_cast<const u32x4_t*>(a.kc + (((int64_t)bh * nc + j) * C + part * TL::KT) * D);
+      vs = reinterpret_cast<const unsigned char*>(
+          a.vt + (((int64_t)bh * nc + j) * SUB + part) * (int64_t)D * TL::KT);
+      vstride = TL::KT * 2;
+    } else {
+      const int ct = t - Tm;
+      ks = reinterpret_cast<const u32x4_t*>(a.kbar_hi + ((int64_t)bh * ncp + ct * TL::KT) * D);
+      vs = reinterpret_cast<const unsigned char*>(a.vbar_t + (int64_t)bh * D * ncp + ct * TL::KT);
+      vstride = ncp * 2;
+    }
 #pragma unroll
     for (int i = 0; i < KLPT; ++i) kst[i] = ks[i * NT + tid];
 #pragma unroll
-    for (int i = 0; i < VLPT; ++i) vst[i] = vs[i * NT + tid];
+    for (int i = 0; i < VLPT; ++i) {
+      const int e = i * NT + tid;
+      vst[i] = *reinterpret_cast<const u32x4_t*>(vs + (int64_t)(e / TL::V_CHUNKS) * vstride +
+                                                 (e % TL::V_CHUNKS) * 16);
+    }
   };
   auto store = [&](int buf) {
     unsigned char* base = smem + buf * TL::BYTES;
@@ -253,6 +278,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   // per-lane LDS read bases: K row r, chunk h; V^T row r, chunk h
   const int kread = r * TL::KP + h * 16;
   const int vread = TL::K_BYTES + r * TL::VP + h * 16;
+  const float* logn = a.logn + (int64_t)bh * ncp;
 
   if (T > 0) {
     fetch(0);
@@ -262,10 +288,11 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll 1
   for (int t = 0; t < T; ++t) {
     if (t + 1 < T) fetch(t + 1);
-    const int j = tile_cluster(t);
+    const bool cen = t >= Tm;
+    const int j = cen ? 0 : tile_cluster(t);
     if (j >= 0) {
       const unsigned char* buf = smem + (t & 1) * TL::BYTES;
-      const int nvalid = min(C, N - j * C) - (t % SUB) * TL::KT;
+      const int nvalid = cen ? TL::KT : min(C, N - j * C) - (t % SUB) * TL::KT;
       // two independent accumulation chains (keys 0-31, 32-63) interleaved
       floatx16_t sacc[2] = {zero16(), zero16()};
 #pragma unroll
@@ -277,23 +304,46 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
           sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
         }
       }
-      // online softmax in log2 units with a lazily updated running maximum:
-      // m only moves (and the accumulators are rescaled) when the tile's
-      // maximum exceeds it by more than 2^8, so P <= 256 (exact after the
-      // final division by l, which uses the same m).
-      if (nvalid < TL::KT) [[unlikely]] {
+      // logits in log2 units: scale q.k, or for a centroid tile
+      // scale q.kbar + ln n_c (-inf for selected and padding clusters)
+      float tv[32];
+      if (cen) [[unlikely]] {
+        const int c0 = (t - Tm) * TL::KT;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (kb * 32 + c_row(i, h) >= nvalid) sacc[kb][i] = kNegInf;
+          for (int q = 0; q < 4; ++q) {
+            const int k0 = c0 + kb * 32 + 8 * q + 4 * h;
+            const floatx4_t ln = *reinterpret_cast<const floatx4_t*>(logn + k0);
+            const uint32_t selw = sSel[k0 >> 5];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool excluded = !((selw >> ((k0 + e) & 31)) & 1u);
+              tv[kb * 16 + 4 * q + e] =
+                  excluded ? fmaf(sacc[kb][4 * q + e], sl2, ln[e] * kLog2e) : kNegInf;
+            }
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) tv[kb * 16 + i] = sacc[kb][i] * sl2;
+        if (nvalid < TL::KT) [[unlikely]] {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (kb * 32 + c_row(i, h) >= nvalid) tv[kb * 16 + i] = kNegInf;
+        }
       }
+      // online softmax with a lazily updated running maximum: m only moves
+      // (and the accumulators are rescaled) when the tile's maximum exceeds
+      // it by more than 2^8, so P <= 256 (exact after the final division by
+      // l, which uses the same m)
       float bm = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) bm = fmaxf(bm, sacc[kb][i]);
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64)) * sl2;
+      for (int i = 0; i < 32; ++i) bm = fmaxf(bm, tv[i]);
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
       const bool grow = bm > m + kLazy;
       if (__ballot(grow)) [[unlikely]] {
         const float mn = grow ? bm : m;
@@ -305,13 +355,9 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
           for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
         m = mn;
       }
-      const float nm = -m;
-      float tv[32];
+      const float nm = m == kNegInf ? 0.0f : -m;   // nothing valid yet: P = 0
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          tv[kb * 16 + i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2, nm));
+      for (int i = 0; i < 32; ++i) tv[i] = __builtin_amdgcn_exp2f(tv[i] + nm);
       // P enters the P.V product as bf16; the denominator sums the same
       // rounded values, so the output stays a convex combination of values
       bf16x8_t pk[4];
@@ -339,70 +385,6 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     __syncthreads();
   }
 
-  if (!DENSE && a.compensate) {
-    const int ncp = attn_ncp(nc);
-    for (int e = tid; e < ncp / 32; e += NT) sSel[e] = 0u;
-    __syncthreads();
-    for (int e = tid; e < a.topk; e += NT) {
-      const int j = blk[e];
-      if (j >= 0 && j < nc) atomicOr(&sSel[j >> 5], 1u << (j & 31));
-    }
-    __syncthreads();
-    const uint16_t* khi = a.kbar_hi + (int64_t)bh * ncp * D;
-    const uint16_t* klo = a.kbar_lo + (int64_t)bh * ncp * D;
-    const uint16_t* vbt = a.vbar_t + (int64_t)bh * D * ncp;
-    const float* logn = a.logn + (int64_t)bh * ncp;
-#pragma unroll 1
-    for (int cb = 0; cb < ncp / 32; ++cb) {
-      floatx16_t sacc = zero16();
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int64_t o = (int64_t)(cb * 32 + r) * D + s * 16 + h * 8;
-        sacc = mfma32(*reinterpret_cast<const bf16x8_t*>(khi + o), qf[s], sacc);
-        sacc = mfma32(*reinterpret_cast<const bf16x8_t*>(klo + o), qf[s], sacc);
-      }
-      const uint32_t selw = sSel[cb];
-      // centroid logits in log2 units: scale q.kbar + ln n_c; selected or
-      // padded clusters get -inf
-      float tv[16];
-      float bm = kNegInf;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int cr = c_row(i, h);
-        const bool excluded = !((selw >> cr) & 1u);
-        const float ln = logn[cb * 32 + cr];
-        tv[i] = excluded ? fmaf(sacc[i], sl2, ln * kLog2e) : kNegInf;
-        bm = fmaxf(bm, tv[i]);
-      }
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-      const bool grow = bm > m + kLazy;
-      if (__ballot(grow)) [[unlikely]] {
-        const float mn = grow ? bm : m;
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
-        lsum *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
-        m = mn;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tv[i] = __builtin_amdgcn_exp2f(tv[i] - m);
-      const u32x4_t u0 = pack8(tv), u1 = pack8(tv + 8);
-      float ps = sum_bf16x8(u1, sum_bf16x8(u0, 0.0f));
-      ps += __shfl_xor(ps, 32, 64);
-      lsum += ps;
-      const bf16x8_t p0 = as_bf16x8(u0);
-      const bf16x8_t p1 = as_bf16x8(u1);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const uint16_t* row = vbt + (int64_t)(nb * 32 + r) * ncp + cb * 32 + h * 8;
-        acc[nb] = mfma32(*reinterpret_cast<const bf16x8_t*>(row), p0, acc[nb]);
-        acc[nb] = mfma32(*reinterpret_cast<const bf16x8_t*>(row + 16), p1, acc[nb]);
-      }
-    }
-  }
-
   if (!qvalid) return;
   const float inv = 1.0f / lsum;
   uint16_t* Oh = (uint16_t*)a.O + ((int64_t)bh * N + qtok) * D;
@@ -422,7 +404,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 
 template <int D, int C>
 constexpr size_t attn_smem() {
-  return 2 * (size_t)AttnTile<D>::BYTES + 8192 / 8 + 64;
+  return 2 * (size_t)AttnTile<D>::BYTES + 8192 / 8 + 64;   // two buffers, selection bits
 }
 
 // ----------------------------------------------------------------------------

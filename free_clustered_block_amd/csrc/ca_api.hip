@@ -81,10 +81,9 @@ void plan_attend(Carver& cv, AttnArgs& a, bool with_tiles) {
     a.kc = cv.take<uint16_t>(BH * nc * c * D);
     a.vt = cv.take<uint16_t>(BH * nc * c * D);
     a.kbar_hi = cv.take<uint16_t>(BH * ncp * D);
-    a.kbar_lo = cv.take<uint16_t>(BH * ncp * D);
     a.vbar_t = cv.take<uint16_t>(BH * ncp * D);
   } else {
-    a.kc = a.vt = a.kbar_hi = a.kbar_lo = a.vbar_t = nullptr;
+    a.kc = a.vt = a.kbar_hi = a.vbar_t = nullptr;
   }
   a.logn = cv.take<float>(BH * ncp);
   a.kbar32 = cv.take<float>(BH * ncp * D);

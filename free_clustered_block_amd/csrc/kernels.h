@@ -68,9 +68,8 @@ struct AttnArgs {
   // scratch (bf16 path)
   uint16_t* kc;       // [BH][nc][c][D]   keys, cluster-major, zero padded
   uint16_t* vt;       // [BH][nc][D][c]   values, cluster-major, transposed
-  uint16_t* kbar_hi;  // [BH][ncp][D]
-  uint16_t* kbar_lo;  // [BH][ncp][D]
-  uint16_t* vbar_t;   // [BH][D][ncp]
+  uint16_t* kbar_hi;  // [BH][ncp][D]   key centroids rounded to bf16
+  uint16_t* vbar_t;   // [BH][D][ncp]   value centroids, transposed
   float* logn;        // [BH][ncp]
   float* kbar32;      // [BH][ncp][D]
   float* vbar32;      // [BH][ncp][D]
@@ -78,8 +77,8 @@ struct AttnArgs {
   hipEvent_t ev_start;
   hipEvent_t ev_stop;
 };
-// centroid count padded to whole 32-blocks
-CA_HD int attn_ncp(int nc) { return (nc + 31) / 32 * 32; }
+// centroid count padded to whole 64-centroid sub-tiles
+CA_HD int attn_ncp(int nc) { return (nc + 63) / 64 * 64; }
 void launch_attend(const AttnArgs& a, hipStream_t st);
 
 // peak.hip -------------------------------------------------------------------
