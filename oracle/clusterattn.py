@@ -464,7 +464,7 @@ def dense_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float | 
 
 
 def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
-                     scale: float | None = None):
+                     scale: float | None = None, clusters=None):
     """Block-sparse attention of one head with optional striped
     mean-compensation.
 
@@ -473,6 +473,8 @@ def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
     cluster enters once through its centroid: logit tau q_i . kbar_c +
     ln|c| and value vbar_c, which is Eq. 21-22 (the centroid weight w_c
     counted |c| times). Returns O in original token order and LSE.
+    ``clusters`` restricts the work to those query clusters (the rows of the
+    other queries are NaN).
     """
     Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
     N, D = Q.shape
@@ -481,9 +483,10 @@ def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
     ks = leaf_sizes(K.shape[0], c)
     kbar, cnt = centroids(K, perm_k, c)
     vbar, _ = centroids(V, perm_k, c)
-    O = np.empty((N, V.shape[1]))
-    L = np.empty(N)
-    for a, na in enumerate(qs):
+    O = np.full((N, V.shape[1]), np.nan)
+    L = np.full(N, np.nan)
+    for a in (range(len(qs)) if clusters is None else clusters):
+        na = qs[a]
         qi = perm_q[a * c:a * c + na]
         sel = np.asarray(blocks[a], np.int64)
         keys = np.concatenate([perm_k[j * c:j * c + ks[j]] for j in sel])
