@@ -35,7 +35,8 @@ struct Carver {
 
 struct ClusterWs {
   float* partial;
-  uint64_t* hash;
+  uint64_t* hash;      // by token (= by position before the first split)
+  uint64_t* hashB;     // by position, ping-pong with hash
   float *Mq, *Mk, *kbar, *Mpk;
   uint16_t* gsplit;
   float* s;
@@ -57,6 +58,7 @@ ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c) {
   const size_t slots = L > 0 ? ((size_t)1 << (L - 1)) : 1;
   w.partial = cv.take<float>((size_t)BH * nchunks * (2 * (size_t)D * D + D));
   w.hash = cv.take<uint64_t>(T * N);
+  w.hashB = cv.take<uint64_t>(T * N);
   w.Mq = cv.take<float>((size_t)BH * D * D);
   w.Mk = cv.take<float>((size_t)BH * D * D);
   w.kbar = cv.take<float>((size_t)BH * D);
@@ -203,6 +205,8 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   launch_perm_init(w.permA, 2 * BH, N, st);
   int32_t* cur = w.permA;
   int32_t* nxt = w.permB;
+  uint64_t* hcur = w.hash;
+  uint64_t* hnxt = w.hashB;
   for (int level = 0; level < L; ++level) {
     if (o.trace_perm)
       CA_HIP_CHECK(hipMemcpyAsync(o.trace_perm + level * TN, cur, TN * 4, hipMemcpyDeviceToDevice, st));
@@ -212,7 +216,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     a.transform = o.transform; a.power_iters = o.power_iters; a.sample_factor = o.sample_factor;
     a.seed = o.seed;
     a.perm_in = cur; a.perm_out = nxt;
-    a.hash = w.hash; a.s = w.s; a.Mq = w.Mq; a.Mk = w.Mk; a.Mpk = w.Mpk;
+    a.hpos_in = hcur; a.hpos_out = hnxt; a.s = w.s; a.Mq = w.Mq; a.Mk = w.Mk; a.Mpk = w.Mpk;
     a.dir_prev = (level & 1) ? w.dirA : w.dirB;
     a.dir_cur = (level & 1) ? w.dirB : w.dirA;
     a.nchunks = (N + c - 1) / c;
@@ -223,6 +227,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     a.trace_dir = o.trace_dir ? o.trace_dir + (size_t)level * 2 * BH * a.trace_slots * D : nullptr;
     launch_level(a, st);
     int32_t* t = cur; cur = nxt; nxt = t;
+    uint64_t* th = hcur; hcur = hnxt; hnxt = th;
   }
   if (o.trace_perm)
     CA_HIP_CHECK(hipMemcpyAsync(o.trace_perm + (size_t)L * TN, cur, TN * 4, hipMemcpyDeviceToDevice, st));

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void pddp_sample(LevelArgs a) {
   salt = chain_step(salt, (uint64_t)a.level);
   const uint64_t ad = (uint64_t)a.sample_factor * a.D;
   const int32_t* perm = a.perm_in + (int64_t)tree * a.N;
-  const uint64_t* hash = a.hash + (int64_t)tree * a.N;
+  const uint64_t* hpos = a.hpos_in + (int64_t)tree * a.N;
   // four slabs of 256 positions; a chunk of c <= 256 positions lies in one slab
   int tok[4];
   bool flag[4];
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void pddp_sample(LevelArgs a) {
         tok[k] = perm[p];
         const bool take_all = ad >= (uint64_t)n;
         const uint64_t thr = take_all ? 0 : ((ad << 32) / (uint64_t)n);
-        flag[k] = take_all || ((fmix64(hash[tok[k]] ^ salt) >> 32) < thr);
+        flag[k] = take_all || ((fmix64(hpos[p] ^ salt) >> 32) < thr);
       }
     }
   }
@@ -768,10 +768,19 @@ __global__ __launch_bounds__(256) void pddp_project(LevelArgs a) {
 
 constexpr int kSplitThreads = 512;
 constexpr int kSplitWaves = kSplitThreads / 64;
-constexpr int kSplitCache = 8192;   // keys kept in LDS
+constexpr int kSplitCache = 16384;           // keys kept in LDS
 
+CA_DEV int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Split of one node: the members are ordered by (key, position), strictly;
+// the first t go left and the rest right, both keeping position order (a
+// stable partition). The token's content hash moves with it.
 __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
-  __shared__ uint32_t skeys[kSplitCache];
+  __shared__ __attribute__((aligned(16))) uint32_t skeys[kSplitCache];
   __shared__ int hist[kSplitWaves][256];
   __shared__ int wtot[2][kSplitWaves];
   __shared__ uint32_t sel[4];
@@ -787,31 +796,63 @@ __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
   }
   const int32_t* pin = a.perm_in + (int64_t)tree * a.N;
   int32_t* pout = a.perm_out + (int64_t)tree * a.N;
+  const uint64_t* hin = a.hpos_in + (int64_t)tree * a.N;
+  uint64_t* hout = a.hpos_out + (int64_t)tree * a.N;
   if (depth < a.level || m <= a.c) {
     // leaf: copied once, by the slot whose remaining path bits are all zero
     const int below = a.level - depth;
     if (below > 0 && (slot & ((1 << below) - 1)) != 0) return;
-    for (int i = tid; i < m; i += kSplitThreads) pout[o + i] = pin[o + i];
+    for (int i = tid; i < m; i += kSplitThreads) {
+      pout[o + i] = pin[o + i];
+      hout[o + i] = hin[o + i];
+    }
     return;
   }
   const int off = o, n = m;
   const int t = split_size(n, a.c);
   const uint32_t* gkeys = a.keys + (int64_t)tree * a.N + off;
+
+  // radix select of the rank-t key over LDS histograms, 8-bit digits from the
+  // highest bit in which the node's keys differ (the bits above it are common
+  // to every key and would put every member in one bucket)
   const bool cached = n <= kSplitCache;
-  if (cached)
-    for (int i = tid; i < n; i += kSplitThreads) skeys[i] = gkeys[i];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int i = tid; i < n; i += kSplitThreads) {
+    const uint32_t k = gkeys[i];
+    if (cached) skeys[i] = k;
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d, 64));
+  }
+  if (l == 0) { wtot[0][w] = (int)kmin; wtot[1][w] = (int)kmax; }
   __syncthreads();
+  kmin = (uint32_t)wtot[0][0];
+  kmax = (uint32_t)wtot[1][0];
+  for (int q = 1; q < kSplitWaves; ++q) {
+    kmin = min(kmin, (uint32_t)wtot[0][q]);
+    kmax = max(kmax, (uint32_t)wtot[1][q]);
+  }
   auto key_at = [&](int i) -> uint32_t { return cached ? skeys[i] : gkeys[i]; };
 
-  uint32_t prefix = 0;
+  const uint32_t diff = kmin ^ kmax;
+  const int hb = diff ? 31 - __builtin_clz(diff) : -1;   // highest differing bit
+  uint32_t prefix = hb < 0 ? kmin : (hb == 31 ? 0u : kmin & (0xFFFFFFFFu << (hb + 1)));
   int want = t;   // 1-based rank still to locate among the candidates
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int hi = hb; hi >= 0;) {
+    const int lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dmask = (2u << (hi - lo)) - 1u;
+    const uint32_t hmask = hi == 31 ? 0u : (0xFFFFFFFFu << (hi + 1));
+    __syncthreads();   // the previous round's reads of hist and sel are done
     for (int i = tid; i < kSplitWaves * 256; i += kSplitThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+#pragma unroll 8
     for (int i = tid; i < n; i += kSplitThreads) {
       const uint32_t k = key_at(i);
-      if ((k & hmask) == (prefix & hmask)) atomicAdd(&hist[w][(k >> shift) & 255u], 1);
+      if ((k & hmask) == (prefix & hmask)) atomicAdd(&hist[w][(k >> lo) & dmask], 1);
     }
     __syncthreads();
     if (w == 0) {
@@ -841,50 +882,201 @@ __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
       }
     }
     __syncthreads();
-    prefix |= sel[0] << shift;
+    prefix |= sel[0] << lo;
     want -= (int)sel[1];
-    __syncthreads();
+    hi = lo - 1;
+  }
+  __syncthreads();
+  const uint32_t kstar = prefix;
+  const int eq_take = want;   // members equal to kstar that go left (lowest positions)
+
+  // stable partition: wave w owns a contiguous region of positions; the
+  // regions' counts give each wave its starting ranks, then each wave walks
+  // its region 64 members at a time with ballot prefixes
+  const int per_w = (n + kSplitWaves - 1) / kSplitWaves;
+  const int r0 = min(n, w * per_w), r1 = min(n, r0 + per_w);
+  int cl = 0, ce = 0;
+#pragma unroll 8
+  for (int i = r0 + l; i < r1; i += 64) {
+    const uint32_t k = key_at(i);
+    cl += k < kstar;
+    ce += k == kstar;
+  }
+  cl = wave_sum_int(cl);
+  ce = wave_sum_int(ce);
+  if (l == 0) { wtot[0][w] = cl; wtot[1][w] = ce; }
+  __syncthreads();
+  int lb = 0, eb = 0;
+  for (int q = 0; q < w; ++q) { lb += wtot[0][q]; eb += wtot[1][q]; }
+  int erun = eb;                        // equal members before the current step
+  int lrun = lb + min(eb, eq_take);     // left members before the current step
+  constexpr int BATCH = 8;   // 64-member steps whose loads are issued together
+  for (int base = r0; base < r1; base += 64 * BATCH) {
+    uint32_t k[BATCH];
+    int pv[BATCH];
+    uint64_t hv[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int i = base + 64 * b + l;
+      k[b] = 0u; pv[b] = 0; hv[b] = 0;
+      if (i < r1) { k[b] = key_at(i); pv[b] = pin[off + i]; hv[b] = hin[off + i]; }
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int i = base + 64 * b + l;
+      const bool valid = i < r1;
+      const bool less = valid && k[b] < kstar;
+      const bool eq = valid && k[b] == kstar;
+      uint64_t bal_e, bal_l;
+      const int eqpre = lane_prefix(eq, &bal_e);
+      const bool left = less || (eq && erun + eqpre < eq_take);
+      const int lpre = lane_prefix(left, &bal_l);
+      const int lrank = lrun + lpre;
+      if (valid) {
+        const int dest = left ? off + lrank : off + t + (i - lrank);
+        if (dest < off + n) {   // holds by construction; guards the slice
+          pout[dest] = pv[b];
+          hout[dest] = hv[b];
+        }
+      }
+      erun += __popcll(bal_e);
+      lrun += __popcll(bal_l);
+    }
+  }
+}
+
+// Split of nodes of at most kSmallNode members: one wave per node (four per
+// workgroup), the same radix select and stable partition with wave-wide
+// ballots and a per-wave LDS histogram, no workgroup barriers.
+constexpr int kSmallNode = 1024;
+
+CA_DEV void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(256) void pddp_split_small(LevelArgs a) {
+  constexpr int KPL = kSmallNode / 64;   // keys per lane
+  __shared__ int hist[4][256];
+  const int tree = blockIdx.y, w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int slot = blockIdx.x * 4 + w;
+  if (slot >= (1 << a.level)) return;   // the whole wave
+  int o = 0, m = a.N, depth = 0;
+  for (; depth < a.level; ++depth) {
+    if (m <= a.c) break;
+    const int t = split_size(m, a.c);
+    if ((slot >> (a.level - 1 - depth)) & 1) { o += t; m -= t; } else { m = t; }
+  }
+  const int32_t* pin = a.perm_in + (int64_t)tree * a.N;
+  int32_t* pout = a.perm_out + (int64_t)tree * a.N;
+  const uint64_t* hin = a.hpos_in + (int64_t)tree * a.N;
+  uint64_t* hout = a.hpos_out + (int64_t)tree * a.N;
+  if (depth < a.level || m <= a.c) {
+    const int below = a.level - depth;
+    if (below > 0 && (slot & ((1 << below) - 1)) != 0) return;
+    for (int i = l; i < m; i += 64) {
+      pout[o + i] = pin[o + i];
+      hout[o + i] = hin[o + i];
+    }
+    return;
+  }
+  const int off = o, n = m;   // n <= kSmallNode (checked by the launch)
+  const int t = split_size(n, a.c);
+  const uint32_t* gkeys = a.keys + (int64_t)tree * a.N + off;
+  uint32_t k[KPL];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int q = 0; q < KPL; ++q) {
+    const int i = l + 64 * q;
+    k[q] = i < n ? gkeys[i] : 0u;
+    if (i < n) { kmin = min(kmin, k[q]); kmax = max(kmax, k[q]); }
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d, 64));
+  }
+  const uint32_t diff = kmin ^ kmax;
+  const int hb = diff ? 31 - __builtin_clz(diff) : -1;
+  uint32_t prefix = hb < 0 ? kmin : (hb == 31 ? 0u : kmin & (0xFFFFFFFFu << (hb + 1)));
+  int want = t;
+  int* hw = hist[w];
+  for (int hi = hb; hi >= 0;) {
+    const int lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dmask = (2u << (hi - lo)) - 1u;
+    const uint32_t hmask = hi == 31 ? 0u : (0xFFFFFFFFu << (hi + 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hw[4 * l + j] = 0;
+    wave_sync();
+#pragma unroll
+    for (int q = 0; q < KPL; ++q)
+      if (l + 64 * q < n && (k[q] & hmask) == (prefix & hmask)) atomicAdd(&hw[(k[q] >> lo) & dmask], 1);
+    wave_sync();
+    int v[4], s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { v[j] = hw[4 * l + j]; s += v[j]; }
+    int inc = s;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(inc, d, 64);
+      if (l >= d) inc += y;
+    }
+    int before = inc - s, bsel = 0, bbefore = 0;
+    bool mine = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (before < want && want <= before + v[j]) { mine = true; bsel = 4 * l + j; bbefore = before; }
+      before += v[j];
+    }
+    const uint64_t owner = __ballot(mine);
+    const int src = owner ? __builtin_ctzll(owner) : 0;   // one lane owns rank `want`
+    bsel = __shfl(bsel, src, 64);
+    bbefore = __shfl(bbefore, src, 64);
+    prefix |= (uint32_t)bsel << lo;
+    want -= bbefore;
+    hi = lo - 1;
+    wave_sync();   // every lane has read the histogram before it is cleared again
   }
   const uint32_t kstar = prefix;
-  const int eq_take = want;   // elements equal to kstar that go left
-
-  int eq_base = 0, left_base = 0;
-  for (int base = 0; base < n; base += kSplitThreads) {
-    const int i = base + tid;
+  const int eq_take = want;
+  int erun = 0, lrun = 0;
+#pragma unroll
+  for (int q = 0; q < KPL; ++q) {
+    const int i = l + 64 * q;
+    if (64 * q >= n) break;   // uniform
     const bool valid = i < n;
-    uint32_t k = 0;
-    int pv = 0;
-    if (valid) { k = key_at(i); pv = pin[off + i]; }
-    const bool less = valid && k < kstar;
-    const bool eq = valid && k == kstar;
-    uint64_t bal;
-    const int eqpre = lane_prefix(eq, &bal);
-    if (l == 0) wtot[0][w] = __popcll(bal);
-    __syncthreads();
-    int eq_w = 0, eq_all = 0;
-    for (int q = 0; q < kSplitWaves; ++q) {
-      if (q < w) eq_w += wtot[0][q];
-      eq_all += wtot[0][q];
-    }
-    const int eq_rank = eq_base + eq_w + eqpre;
-    const bool left = less || (eq && eq_rank < eq_take);
-    const int lpre = lane_prefix(left, &bal);
-    if (l == 0) wtot[1][w] = __popcll(bal);
-    __syncthreads();
-    int l_w = 0, l_all = 0;
-    for (int q = 0; q < kSplitWaves; ++q) {
-      if (q < w) l_w += wtot[1][q];
-      l_all += wtot[1][q];
-    }
-    const int lrank = left_base + l_w + lpre;
+    const bool less = valid && k[q] < kstar;
+    const bool eq = valid && k[q] == kstar;
+    uint64_t bal_e, bal_l;
+    const int eqpre = lane_prefix(eq, &bal_e);
+    const bool left = less || (eq && erun + eqpre < eq_take);
+    const int lpre = lane_prefix(left, &bal_l);
+    const int lrank = lrun + lpre;
     if (valid) {
       const int dest = left ? off + lrank : off + t + (i - lrank);
-      if (dest < off + n) pout[dest] = pv;   // holds by construction; guards the slice
+      if (dest < off + n) {
+        pout[dest] = pin[off + i];
+        hout[dest] = hin[off + i];
+      }
     }
-    eq_base += eq_all;
-    left_base += l_all;
-    __syncthreads();
+    erun += __popcll(bal_e);
+    lrun += __popcll(bal_l);
   }
+}
+
+// Largest node that splits at a level (host).
+int max_split_node(int N, int c, int level) {
+  struct R {
+    static int rec(int n, int c, int l) {
+      if (n <= c) return 0;
+      if (l == 0) return n;
+      const int t = split_size(n, c);
+      const int x = rec(t, c, l - 1), y = rec(n - t, c, l - 1);
+      return x > y ? x : y;
+    }
+  };
+  return R::rec(N, c, level);
 }
 
 __global__ void perm_init(int32_t* perm, int trees, int N) {
@@ -989,7 +1181,12 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
   }
   dim3 gproj((a.N + a.c - 1) / a.c, trees);
   pddp_project<T, D><<<gproj, 256, 0, st>>>(a);
-  pddp_split<<<gslots, kSplitThreads, 0, st>>>(a);
+  if (max_split_node(a.N, a.c, a.level) <= kSmallNode) {
+    dim3 gsmall(((1u << a.level) + 3) / 4, trees);
+    pddp_split_small<<<gsmall, 256, 0, st>>>(a);
+  } else {
+    pddp_split<<<gslots, kSplitThreads, 0, st>>>(a);
+  }
 }
 
 void launch_level(const LevelArgs& a, hipStream_t st) {

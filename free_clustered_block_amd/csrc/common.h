@@ -72,11 +72,13 @@ constexpr uint64_t kDomainWarm = 0x57;    // salt domain of the warm-start vecto
 // ----------------------------------------------------------------------------
 // Tree layout: a node of n > c members splits at t = the multiple of c closest
 // to n/2 with 1 <= t/c and t < n; equidistant -> the smaller (paper v1 §3.2.1).
+// c is a power of two (64, 128 or 256).
 // ----------------------------------------------------------------------------
 
 CA_HD int split_size(int n, int c) {
-  int jmax = (n - 1) / c;
-  int jl = n / (2 * c);
+  const int lc = __builtin_ctz((unsigned)c);   // c is a power of two
+  int jmax = (n - 1) >> lc;
+  int jl = n >> (lc + 1);
   int jh = jl + 1;
   if (jl < 1) jl = 1;
   if (jl > jmax) jl = jmax;

@@ -22,7 +22,8 @@ struct LevelArgs {
   uint64_t seed;
   const int32_t* perm_in;   // [2 BH][N]
   int32_t* perm_out;        // [2 BH][N]
-  const uint64_t* hash;     // [2 BH][N] by token
+  const uint64_t* hpos_in;  // [2 BH][N] content hash of the token at each position
+  uint64_t* hpos_out;       // [2 BH][N] the same after this level's partition
   const float* s;           // [BH][N]
   const float* Mq;          // [BH][D][D]
   const float* Mk;          // [BH][D][D]
