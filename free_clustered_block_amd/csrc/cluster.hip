@@ -52,15 +52,13 @@ __global__ __launch_bounds__(256) void pddp_sample(LevelArgs a) {
     const int p = blockIdx.x * kSampleSpan + k * 256 + tid;
     flag[k] = false;
     tok[k] = 0;
-    if (p < a.N) {
-      int off, n, idx;
-      const int depth = node_of(a.N, a.c, a.level, p, &off, &n, &idx);
-      if (depth == a.level && n > a.c) {
-        tok[k] = perm[p];
-        const bool take_all = ad >= (uint64_t)n;
-        const uint64_t thr = take_all ? 0 : ((ad << 32) / (uint64_t)n);
-        flag[k] = take_all || ((fmix64(hpos[p] ^ salt) >> 32) < thr);
-      }
+    int off, n, idx;
+    const int depth = p < a.N ? node_of(a.N, a.c, a.level, p, &off, &n, &idx) : -1;
+    if (depth == a.level && n > a.c) {
+      tok[k] = perm[p];
+      const bool take_all = ad >= (uint64_t)n;
+      const uint64_t thr = take_all ? 0 : ((ad << 32) / (uint64_t)n);
+      flag[k] = take_all || ((fmix64(hpos[p] ^ salt) >> 32) < thr);
     }
   }
   const int waves_per_chunk = a.c >> 6;   // c in {64, 128, 256}
@@ -77,9 +75,9 @@ __global__ __launch_bounds__(256) void pddp_sample(LevelArgs a) {
       if (q < w) base += wcnt[q];
       tot += wcnt[q];
     }
-    const int chunk = p / a.c;
+    const int chunk = p >> __builtin_ctz((unsigned)a.c);   // c is a power of two
     if (flag[k]) a.sample_buf[(int64_t)tree * a.N + (int64_t)chunk * a.c + base + pre] = tok[k];
-    if (p < a.N && (p % a.c) == 0) a.chunk_cnt[(int64_t)tree * a.nchunks + chunk] = tot;
+    if (p < a.N && (p & (a.c - 1)) == 0) a.chunk_cnt[(int64_t)tree * a.nchunks + chunk] = tot;
     __syncthreads();
   }
 }
