@@ -295,14 +295,25 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       const int nvalid = cen ? TL::KT : min(C, N - j * C) - (t % SUB) * TL::KT;
       // two independent accumulation chains (keys 0-31, 32-63) interleaved
       floatx16_t sacc[2] = {zero16(), zero16()};
+      {
+        // operand reads issued PF ahead of their products (ring of PF
+        // registers); the schedule is pinned by scheduling barriers
+        constexpr int NQ = 2 * KS, PF = 4;
+        bf16x8_t ring[PF];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
+        for (int i = 0; i < PF; ++i)
+          ring[i] = *reinterpret_cast<const bf16x8_t*>(buf + kread + (i & 1) * 32 * TL::KP + (i >> 1) * 32);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8_t kf =
-              *reinterpret_cast<const bf16x8_t*>(buf + kread + kb * 32 * TL::KP + s * 32);
-          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
+        for (int i = 0; i < NQ; ++i) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int kb = i & 1, s = i >> 1;
+          sacc[kb] = mfma32(ring[i % PF], qf[s], sacc[kb]);
+          if (i + PF < NQ) {
+            const int j = i + PF;
+            ring[i % PF] = *reinterpret_cast<const bf16x8_t*>(buf + kread + (j & 1) * 32 * TL::KP + (j >> 1) * 32);
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       // logits in log2 units: scale q.k, or for a centroid tile
       // scale q.kbar + ln n_c (-inf for selected and padding clusters)
@@ -370,15 +381,25 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       }
       ps += __shfl_xor(ps, 32, 64);
       lsum += ps;
+      {
+        // keys 16q .. 16q+15 of the sub-tile: V^T chunk 2q + h; reads issued
+        // PF ahead of their products
+        constexpr int NV = 4 * NB, PF = 4;
+        bf16x8_t ring[PF];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+        for (int i = 0; i < PF; ++i)
+          ring[i] = *reinterpret_cast<const bf16x8_t*>(buf + vread + (i % NB) * 32 * TL::VP + (i / NB) * 32);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          // keys 16q .. 16q+15 of the sub-tile: V^T chunk 2q + h
-          const bf16x8_t vf =
-              *reinterpret_cast<const bf16x8_t*>(buf + vread + nb * 32 * TL::VP + q * 32);
-          acc[nb] = mfma32(vf, pk[q], acc[nb]);
+        for (int i = 0; i < NV; ++i) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int nb = i % NB, q = i / NB;
+          acc[nb] = mfma32(ring[i % PF], pk[q], acc[nb]);
+          if (i + PF < NV) {
+            const int j = i + PF;
+            ring[i % PF] = *reinterpret_cast<const bf16x8_t*>(buf + vread + (j % NB) * 32 * TL::VP + (j / NB) * 32);
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (t + 1 < T) store((t + 1) & 1);
