@@ -90,6 +90,9 @@ def parse():
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the copy and GEMM rate measurements")
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="quality/latency sweep over cluster size, selected fraction, SMC and "
+                         "clustering (the 16k peaked and flat workloads); one JSON line per point")
     return ap.parse_args()
 
 
@@ -178,6 +181,64 @@ def measure_peaks(torch, dev):
             "lds_read_TBs": round(lds_tbs, 2)}
 
 
+def sweep(args, torch, synth, ca):
+    """Error against dense attention and latency over cluster size c in {64, 128, 256},
+    selected fraction k/n_c in {1/4, 1/8, 1/16}, SMC off/on, for the learned
+    (PDDP) clusters and for seeded random clusters of the same sizes."""
+    dev = torch.device("cuda:0")
+
+    def timed(fn, reps=3):
+        out, ts = None, []
+        for _ in range(reps):
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record()
+            out = fn()
+            b_ev.record()
+            torch.cuda.synchronize()
+            ts.append(a_ev.elapsed_time(b_ev))
+        return out, float(np.median(ts))
+
+    for regime in ("peaked", "flat"):
+        w = synth.WORKLOADS[f"sweep_16k_{regime}"]
+        Qn, Kn, Vn = gen_inputs(w)
+        Q, K, V = (torch.from_numpy(x).to(torch.bfloat16).to(dev).contiguous() for x in (Qn, Kn, Vn))
+        B, H, N, D = Q.shape
+        Od, dense_ms = timed(lambda: ca.dense(Q, K, V))
+        Odf = Od.float()
+        nd = torch.linalg.vector_norm(Odf).item()
+        for c in (64, 128, 256):
+            n_c = N // c
+            # random clusters of the same sizes: seeded shuffles, centroids by mean
+            pq = torch.from_numpy(synth.random_perm(w.control_seed, B, H, N)).to(dev)
+            pk = torch.from_numpy(synth.random_perm(w.control_seed + 1, B, H, N)).to(dev)
+
+            def cent(X, perm):
+                Xg = torch.gather(X.float(), 2, perm.long()[..., None].expand(-1, -1, -1, D))
+                return Xg.view(B, H, n_c, c, D).mean(3).contiguous()
+            rq, rk = cent(Q, pq), cent(K, pk)
+            for f in (4, 8, 16):
+                k = n_c // f
+                for smc in (False, True):
+                    for kind in ("pddp", "random"):
+                        def run():
+                            if kind == "pddp":
+                                cr = ca.cluster(Q, K, c, seed=w.cluster_seed)
+                                bl = ca.route(cr.cent_q, cr.cent_k, k)
+                                return ca.attend(Q, K, V, cr.perm_q, cr.perm_k, c, bl, compensate=smc)
+                            bl = ca.route(rq, rk, k)
+                            return ca.attend(Q, K, V, pq, pk, c, bl, compensate=smc)
+                        O, ms = timed(run)
+                        Of = O.float()
+                        rel = torch.linalg.vector_norm(Of - Odf).item() / nd
+                        cos = torch.nn.functional.cosine_similarity(Of, Odf, dim=-1).mean().item()
+                        print(json.dumps({"sweep": w.name, "clusters": kind, "c": c, "k": k,
+                                          "fraction": f"1/{f}", "smc": smc,
+                                          "rel_err_vs_dense": round(rel, 5),
+                                          "cos_vs_dense": round(cos, 5), "ms": round(ms, 4),
+                                          "dense_ms": round(dense_ms, 4),
+                                          "speedup_vs_dense": round(dense_ms / ms, 3)}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -195,6 +256,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ca.load()
+    if args.sweep:
+        sweep(args, torch, synth, ca)
+        return
     w = synth.WORKLOADS[args.workload]
     topk = args.topk or w.topk
     dev = torch.device("cuda:0")
