@@ -166,6 +166,20 @@ struct AttnTile {
 // one head, which select overlapping key clusters) are kept on one XCD, whose
 // L2 then serves their shared key/value tiles. Hardware hands workgroup b to
 // XCD b % 8.
+CA_DEV int xcd_logical(int b, int G);
+
+// Reductions over the two wave halves (lane l with lane l ^ 32): with both
+// operands x, v_permlane32_swap leaves [x.lo, x.lo] in its first result and
+// [x.hi, x.hi] in its second (lanes 0-31 | 32-63).
+CA_DEV float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+CA_DEV float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 CA_DEV int xcd_logical(int b, int G) {
   const int xcd = b & 7, idx = b >> 3;
   const int per = G >> 3, rem = G & 7;
@@ -317,8 +331,12 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       }
       // logits in log2 units: scale q.k, or for a centroid tile
       // scale q.kbar + ln n_c (-inf for selected and padding clusters)
+      // scores in tv; the exponent below is fma(tv, scl, -m): token tiles keep
+      // raw q.k (scl = scale log2 e), centroid tiles are already in log2 units
       float tv[32];
+      float scl = sl2;
       if (cen) [[unlikely]] {
+        scl = 1.0f;
         const int c0 = (t - Tm) * TL::KT;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -338,7 +356,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) tv[kb * 16 + i] = sacc[kb][i] * sl2;
+          for (int i = 0; i < 16; ++i) tv[kb * 16 + i] = sacc[kb][i];
         if (nvalid < TL::KT) [[unlikely]] {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
@@ -354,7 +372,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       float bm = kNegInf;
 #pragma unroll
       for (int i = 0; i < 32; ++i) bm = fmaxf(bm, tv[i]);
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      bm = max_halves(bm) * scl;
       const bool grow = bm > m + kLazy;
       if (__ballot(grow)) [[unlikely]] {
         const float mn = grow ? bm : m;
@@ -368,7 +386,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       }
       const float nm = m == kNegInf ? 0.0f : -m;   // nothing valid yet: P = 0
 #pragma unroll
-      for (int i = 0; i < 32; ++i) tv[i] = __builtin_amdgcn_exp2f(tv[i] + nm);
+      for (int i = 0; i < 32; ++i) tv[i] = __builtin_amdgcn_exp2f(fmaf(tv[i], scl, nm));
       // P enters the P.V product as bf16; the denominator sums the same
       // rounded values, so the output stays a convex combination of values
       bf16x8_t pk[4];
@@ -379,8 +397,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         ps = sum_bf16x8(u, ps);
         pk[q] = as_bf16x8(u);
       }
-      ps += __shfl_xor(ps, 32, 64);
-      lsum += ps;
+      lsum += ps;   // this lane's keys; the halves are added at the end
       {
         // keys 16q .. 16q+15 of the sub-tile: V^T chunk 2q + h; reads issued
         // PF ahead of their products
@@ -406,6 +423,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     __syncthreads();
   }
 
+  lsum = sum_halves(lsum);
   if (!qvalid) return;
   const float inv = 1.0f / lsum;
   uint16_t* Oh = (uint16_t*)a.O + ((int64_t)bh * N + qtok) * D;
