@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
     // centroid padding up to a whole sub-tile: zero vectors with ln n = -inf
     for (int d = tid; d < D; d += 256) {
       a.kbar_hi[((int64_t)bh * ncp + j) * D + d] = 0;
-      a.vbar_t[((int64_t)bh * D + d) * ncp + vslot(j)] = 0;
+      a.vbar_t[(((int64_t)bh * (ncp / 64) + j / 64) * D + d) * 64 + vslot(j % 64)] = 0;
     }
     if (tid == 0) a.logn[(int64_t)bh * ncp + j] = kNegInf;
     return;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
     const float inv = 1.0f / (float)nj;
     const float kb = ks * inv, vb = vs * inv;
     a.kbar_hi[((int64_t)bh * ncp + j) * D + d] = f32_to_bf16(kb);
-    a.vbar_t[((int64_t)bh * D + d) * ncp + vslot(j)] = f32_to_bf16(vb);
+    a.vbar_t[(((int64_t)bh * (ncp / 64) + j / 64) * D + d) * 64 + vslot(j % 64)] = f32_to_bf16(vb);
     if (d == 0) a.logn[(int64_t)bh * ncp + j] = logf((float)nj);
   }
 }
@@ -248,32 +248,27 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   // stage: 16-byte global loads into registers, then into an LDS buffer
   constexpr int KLPT = TL::K_LOADS / NT, VLPT = TL::V_LOADS / NT;
   u32x4_t kst[KLPT], vst[VLPT];
+  // Every sub-tile is contiguous in HBM (K rows [64][D], V^T rows [D][64],
+  // token and centroid tiles alike), so each thread's 16-byte chunks sit at
+  // fixed offsets from a per-tile base.
   auto fetch = [&](int t) {
     const u32x4_t* ks;
-    const unsigned char* vs;
-    int vstride;   // bytes between V^T rows of the sub-tile
+    const u32x4_t* vs;
     if (t < Tm) {
       int j = tile_cluster(t);
       if (j < 0) j = 0;   // any valid tile; its results are not used
       const int part = t % SUB;
       ks = reinterpret_cast<const u32x4_t*>(a.kc + (((int64_t)bh * nc + j) * C + part * TL::KT) * D);
-      vs = reinterpret_cast<const unsigned char*>(
-          a.vt + (((int64_t)bh * nc + j) * SUB + part) * (int64_t)D * TL::KT);
-      vstride = TL::KT * 2;
+      vs = reinterpret_cast<const u32x4_t*>(a.vt + (((int64_t)bh * nc + j) * SUB + part) * (int64_t)D * TL::KT);
     } else {
       const int ct = t - Tm;
       ks = reinterpret_cast<const u32x4_t*>(a.kbar_hi + ((int64_t)bh * ncp + ct * TL::KT) * D);
-      vs = reinterpret_cast<const unsigned char*>(a.vbar_t + (int64_t)bh * D * ncp + ct * TL::KT);
-      vstride = ncp * 2;
+      vs = reinterpret_cast<const u32x4_t*>(a.vbar_t + ((int64_t)bh * (ncp / TL::KT) + ct) * D * TL::KT);
     }
 #pragma unroll
     for (int i = 0; i < KLPT; ++i) kst[i] = ks[i * NT + tid];
 #pragma unroll
-    for (int i = 0; i < VLPT; ++i) {
-      const int e = i * NT + tid;
-      vst[i] = *reinterpret_cast<const u32x4_t*>(vs + (int64_t)(e / TL::V_CHUNKS) * vstride +
-                                                 (e % TL::V_CHUNKS) * 16);
-    }
+    for (int i = 0; i < VLPT; ++i) vst[i] = vs[i * NT + tid];
   };
   auto store = [&](int buf) {
     unsigned char* base = smem + buf * TL::BYTES;
@@ -331,9 +326,8 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       }
       // logits in log2 units: scale q.k, or for a centroid tile
       // scale q.kbar + ln n_c (-inf for selected and padding clusters)
-      // scores in tv; the exponent below is fma(tv, scl, -m): token tiles keep
-      // raw q.k (scl = scale log2 e), centroid tiles are already in log2 units
-      float tv[32];
+      // the exponent below is fma(score, scl, -m): token tiles keep raw q.k
+      // (scl = scale log2 e), centroid tiles are turned into log2 units here
       float scl = sl2;
       if (cen) [[unlikely]] {
         scl = 1.0f;
@@ -348,22 +342,18 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const bool excluded = !((selw >> ((k0 + e) & 31)) & 1u);
-              tv[kb * 16 + 4 * q + e] =
-                  excluded ? fmaf(sacc[kb][4 * q + e], sl2, ln[e] * kLog2e) : kNegInf;
+              const float bias = excluded ? ln[e] * kLog2e : kNegInf;
+              sacc[kb][4 * q + e] = fmaf(sacc[kb][4 * q + e], sl2, bias);
             }
           }
-      } else {
+      } else if (nvalid < TL::KT) [[unlikely]] {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) tv[kb * 16 + i] = sacc[kb][i];
-        if (nvalid < TL::KT) [[unlikely]] {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (kb * 32 + c_row(i, h) >= nvalid) tv[kb * 16 + i] = kNegInf;
-        }
+          for (int i = 0; i < 16; ++i) {
+            const bool out = kb * 32 + c_row(i, h) >= nvalid;
+            sacc[kb][i] = out ? kNegInf : sacc[kb][i];
+          }
       }
       // online softmax with a lazily updated running maximum: m only moves
       // (and the accumulators are rescaled) when the tile's maximum exceeds
@@ -371,7 +361,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       // l, which uses the same m)
       float bm = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) bm = fmaxf(bm, tv[i]);
+      for (int i = 0; i < 32; ++i) bm = fmaxf(bm, sacc[i >> 4][i & 15]);
       bm = max_halves(bm) * scl;
       const bool grow = bm > m + kLazy;
       if (__ballot(grow)) [[unlikely]] {
@@ -385,8 +375,9 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         m = mn;
       }
       const float nm = m == kNegInf ? 0.0f : -m;   // nothing valid yet: P = 0
+      float tv[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) tv[i] = __builtin_amdgcn_exp2f(fmaf(tv[i], scl, nm));
+      for (int i = 0; i < 32; ++i) tv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 4][i & 15], scl, nm));
       // P enters the P.V product as bf16; the denominator sums the same
       // rounded values, so the output stays a convex combination of values
       bf16x8_t pk[4];

@@ -70,7 +70,7 @@ struct AttnArgs {
   uint16_t* kc;       // [BH][nc][c][D]   keys, cluster-major, zero padded
   uint16_t* vt;       // [BH][nc][D][c]   values, cluster-major, transposed
   uint16_t* kbar_hi;  // [BH][ncp][D]   key centroids rounded to bf16
-  uint16_t* vbar_t;   // [BH][D][ncp]   value centroids, transposed
+  uint16_t* vbar_t;   // [BH][ncp/64][D][64] value centroids, transposed per 64
   float* logn;        // [BH][ncp]
   float* kbar32;      // [BH][ncp][D]
   float* vbar32;      // [BH][ncp][D]
