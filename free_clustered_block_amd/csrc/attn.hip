@@ -324,8 +324,6 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // logits in log2 units: scale q.k, or for a centroid tile
-      // scale q.kbar + ln n_c (-inf for selected and padding clusters)
       // the exponent below is fma(score, scl, -m): token tiles keep raw q.k
       // (scl = scale log2 e), centroid tiles are turned into log2 units here
       float scl = sl2;
