@@ -51,6 +51,7 @@ CA_HD int vslot(int k) {
 template <int D>
 __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
   constexpr int RB = 64;                    // rows per LDS block
+  __shared__ __attribute__((aligned(16))) uint16_t skr[RB][D + 8];
   __shared__ __attribute__((aligned(16))) uint16_t sv[RB][D + 8];
   __shared__ float sk[256 / D][D], sm[256 / D][D];
   const int j = blockIdx.x, bh = blockIdx.y;
@@ -72,40 +73,47 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
   uint16_t* kc = a.kc + ((int64_t)bh * nc + j) * c * D;
   uint16_t* vt = a.vt + ((int64_t)bh * nc + j) * (int64_t)D * c;
 
-  // K rows: 16-byte chunks, zero padded
-  constexpr int CPR = D / 8;
-  for (int e = tid; e < c * CPR; e += 256) {
-    const int r = e / CPR, g = e % CPR;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (r < nj) {
-      const int tok = perm ? clamp_tok(perm[r], a.N) : j * c + r;
-      v = *reinterpret_cast<const u32x4_t*>(K + (int64_t)tok * D + 8 * g);
-    }
-    *reinterpret_cast<u32x4_t*>(kc + (int64_t)r * D + 8 * g) = v;
-  }
-  // centroid sums in row order: thread (grp, d) sums rows grp, grp+G, ...
+  // Blocks of 64 rows: the K and V chunks of block b + 1 are loaded while
+  // block b is summed and transposed out of LDS. K rows go to kc straight from
+  // registers (zero padded past the cluster's end).
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int LPT = RB * CPR / 256;       // chunks per thread and block
   constexpr int G = 256 / D;
   const int d = tid % D, grp = tid / D;
-  float ksum = 0.0f, vsum = 0.0f;
-  for (int r = grp; r < nj; r += G) {
-    const int tok = perm ? clamp_tok(perm[r], a.N) : j * c + r;
-    ksum += bf16_to_f32(K[(int64_t)tok * D + d]);
-  }
-  // V: through LDS in blocks of 64 rows, written transposed [D][c]
-  for (int r0 = 0; r0 < c; r0 += RB) {
-    for (int e = tid; e < RB * CPR; e += 256) {
-      const int r = e / CPR, g = e % CPR;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (r0 + r < nj) {
-        const int tok = perm ? clamp_tok(perm[r0 + r], a.N) : j * c + r0 + r;
-        v = *reinterpret_cast<const u32x4_t*>(V + (int64_t)tok * D + 8 * g);
+  const int nb = c / RB;
+  u32x4_t kr[LPT], vr[LPT];
+  auto load = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int e = i * 256 + tid, r = b * RB + e / CPR, g = e % CPR;
+      kr[i] = vr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (r < nj) {
+        const int tok = perm ? clamp_tok(perm[r], a.N) : j * c + r;
+        kr[i] = *reinterpret_cast<const u32x4_t*>(K + (int64_t)tok * D + 8 * g);
+        vr[i] = *reinterpret_cast<const u32x4_t*>(V + (int64_t)tok * D + 8 * g);
       }
-      *reinterpret_cast<u32x4_t*>(&sv[r][8 * g]) = v;
     }
+  };
+  // centroid sums in row order: thread (grp, d) sums rows grp, grp + G, ...
+  float ksum = 0.0f, vsum = 0.0f;
+  load(0);
+  for (int b = 0; b < nb; ++b) {
+    if (b > 0) __syncthreads();   // the previous block's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int e = i * 256 + tid, r = e / CPR, g = e % CPR;
+      *reinterpret_cast<u32x4_t*>(&skr[r][8 * g]) = kr[i];
+      *reinterpret_cast<u32x4_t*>(&sv[r][8 * g]) = vr[i];
+      *reinterpret_cast<u32x4_t*>(kc + (int64_t)(b * RB + r) * D + 8 * g) = kr[i];
+    }
+    if (b + 1 < nb) load(b + 1);
     __syncthreads();
-    for (int r = grp; r < RB; r += G)
-      if (r0 + r < nj) vsum += bf16_to_f32(sv[r][d]);
-    // each thread writes 8 consecutive storage slots of one dim
+    for (int r = grp; r < RB && b * RB + r < nj; r += G) {
+      ksum += bf16_to_f32(skr[r][d]);
+      vsum += bf16_to_f32(sv[r][d]);
+    }
+    // V written transposed [D][64] per block: each thread writes 8
+    // consecutive storage slots of one dim
     for (int e = tid; e < D * (RB / 8); e += 256) {
       const int dd = e / (RB / 8), s8 = e % (RB / 8);
       uint16_t vals[8];
@@ -120,9 +128,8 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
       pk.y = vals[2] | ((uint32_t)vals[3] << 16);
       pk.z = vals[4] | ((uint32_t)vals[5] << 16);
       pk.w = vals[6] | ((uint32_t)vals[7] << 16);
-      *reinterpret_cast<u32x4_t*>(vt + (int64_t)(r0 / RB) * D * RB + dd * RB + s8 * 8) = pk;
+      *reinterpret_cast<u32x4_t*>(vt + (int64_t)b * D * RB + dd * RB + s8 * 8) = pk;
     }
-    __syncthreads();
   }
   sk[grp][d] = ksum;
   sm[grp][d] = vsum;
