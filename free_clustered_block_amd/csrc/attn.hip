@@ -19,6 +19,8 @@
 //                ln n_c, -inf for selected or padding clusters) in the same
 //                running maximum and sum. O is scattered back to token order.
 // fp32 path: the same computation on VALU, one thread per query.
+#include <type_traits>
+
 #include "kernels.h"
 #include "mfma.h"
 
@@ -301,10 +303,26 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     store(0);
   }
   __syncthreads();
-#pragma unroll 1
-  for (int t = 0; t < T; ++t) {
+  // Sub-tiles that need no masking (full token tiles) run in loops of their
+  // own; the sub-tiles of the short last cluster, wherever the selection
+  // holds it, and the centroid tiles run in loops with the masking code.
+  int rpos = -1;   // position of the short cluster in the selection, if any
+  if (N % C != 0) {
+    if (DENSE) {
+      rpos = nc - 1;
+    } else {
+      int mine = -1;   // entries are distinct: at most one lane finds it
+      for (int e = l; e < nsel; e += 64)
+        if (blk[e] == nc - 1) mine = e;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mine = max(mine, __shfl_xor(mine, o, 64));
+      rpos = __builtin_amdgcn_readfirstlane(mine);
+    }
+  }
+  auto step = [&](int t, auto special_tag) __attribute__((always_inline)) {
+    constexpr bool SPECIAL = decltype(special_tag)::value;
     if (t + 1 < T) fetch(t + 1);
-    const bool cen = t >= Tm;
+    const bool cen = SPECIAL && t >= Tm;
     const int j = cen ? 0 : tile_cluster(t);
     if (j >= 0) {
       const unsigned char* buf = smem + (t & 1) * TL::BYTES;
@@ -334,7 +352,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       // the exponent below is fma(score, scl, -m): token tiles keep raw q.k
       // (scl = scale log2 e), centroid tiles are turned into log2 units here
       float scl = sl2;
-      if (cen) [[unlikely]] {
+      if (SPECIAL && cen) {
         scl = 1.0f;
         const int c0 = (t - Tm) * TL::KT;
 #pragma unroll
@@ -351,7 +369,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
               sacc[kb][4 * q + e] = fmaf(sacc[kb][4 * q + e], sl2, bias);
             }
           }
-      } else if (nvalid < TL::KT) [[unlikely]] {
+      } else if (SPECIAL && nvalid < TL::KT) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -417,7 +435,19 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     }
     if (t + 1 < T) store((t + 1) & 1);
     __syncthreads();
+  };
+  auto run = [&](int t0, int t1, auto special_tag) __attribute__((always_inline)) {
+#pragma unroll 1
+    for (int t = t0; t < t1; ++t) step(t, special_tag);
+  };
+  if (rpos < 0) {
+    run(0, Tm, std::false_type{});
+  } else {
+    run(0, rpos * SUB, std::false_type{});
+    run(rpos * SUB, rpos * SUB + SUB, std::true_type{});
+    run(rpos * SUB + SUB, Tm, std::false_type{});
   }
+  run(Tm, T, std::true_type{});
 
   lsum = sum_halves(lsum);
   if (!qvalid) return;
