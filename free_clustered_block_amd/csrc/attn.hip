@@ -175,20 +175,6 @@ struct AttnTile {
 // one head, which select overlapping key clusters) are kept on one XCD, whose
 // L2 then serves their shared key/value tiles. Hardware hands workgroup b to
 // XCD b % 8.
-CA_DEV int xcd_logical(int b, int G);
-
-// Reductions over the two wave halves (lane l with lane l ^ 32): with both
-// operands x, v_permlane32_swap leaves [x.lo, x.lo] in its first result and
-// [x.hi, x.hi] in its second (lanes 0-31 | 32-63).
-CA_DEV float max_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-CA_DEV float sum_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 CA_DEV int xcd_logical(int b, int G) {
   const int xcd = b & 7, idx = b >> 3;
   const int per = G >> 3, rem = G & 7;

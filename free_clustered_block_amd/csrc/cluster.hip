@@ -666,8 +666,8 @@ void pddp_dir_mma(LevelArgs a) {
       }
     float tp = (t4[0] + t4[1]) + (t4[2] + t4[3]);
     float nn = (n4[0] + n4[1]) + (n4[2] + n4[3]);
-    tp += __shfl_xor(tp, 32, 64);
-    nn += __shfl_xor(nn, 32, 64);   // the two half-waves' rows cover every index once
+    tp = sum_halves(tp);
+    nn = sum_halves(nn);   // the two half-waves' rows cover every index once
     if (it > 0) {
       if (nn == 0.0f) { fallback = true; break; }
       inv_norm = 1.0f / sqrtf(nn);
@@ -689,7 +689,7 @@ void pddp_dir_mma(LevelArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v4[e] = fmaf(mr[4 * k + e], tb[k][e], v4[e]);
       vp = (v4[0] + v4[1]) + (v4[2] + v4[3]);
-      vp += __shfl_xor(vp, 32, 64);
+      vp = sum_halves(vp);
     }
     if (h == 0) vbuf[32 * w + r] = vp;
     __syncthreads();

@@ -135,15 +135,29 @@ inline int tree_levels_host(int N, int c) {
 // Wave helpers (wave64)
 // ----------------------------------------------------------------------------
 
+// Reductions over the two wave halves (lane l with lane l ^ 32), on the VALU:
+// with both operands x, v_permlane32_swap leaves [x.lo, x.lo] in its first
+// result and [x.hi, x.hi] in its second (lanes 0-31 | 32-63).
+CA_DEV float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+CA_DEV float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 CA_DEV float wave_sum(float v) {
+  v = sum_halves(v);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 
 CA_DEV float wave_max(float v) {
+  v = max_halves(v);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
 

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void qnorm_bf16(const uint16_t* __restrict__ Q
       tp = fmaf(y[4 * jq + 2], bf16_to_f32((uint16_t)(qv.y & 0xFFFFu)), tp);
       tp = fmaf(y[4 * jq + 3], bf16_to_f32((uint16_t)(qv.y >> 16)), tp);
     }
-    tp += __shfl_xor(tp, 32, 64);
+    tp = sum_halves(tp);
     if (h == 0) tred[buf][bn][32 * qg + r] = tp;
     if (more) store_tile(buf ^ 1);
     __syncthreads();
