@@ -16,7 +16,12 @@ function that implements it. Summary of those readings:
 * splitting variant: basic recursive splitting (PDDP) with the attention
   metric injected into the power iteration (v1 §3.2.1 "Basic recursive
   splitting"; v1 §6.1 notes the metric can be injected so no
-  eigendecomposition is needed);
+  eigendecomposition is needed); optionally the diagonalized variant (v1
+  §3.2.1 "Diagonalized recursive splitting", rev §4.1.1): the vectors are
+  rotated once into the principal-component basis of the whole set (in the
+  transform's geometry, z = R x) and each node splits along the coordinate
+  of highest sample variance; basis columns are ordered by descending
+  eigenvalue, each with its largest-magnitude entry made positive;
 * the subsample of min(a d, |S|) vectors is a Bernoulli sample at rate
   min(1, a d / |S|) decided by a 64-bit content hash of each token's raw
   input bits (so it is deterministic, identical on CPU and GPU, and
@@ -250,6 +255,7 @@ class ClusterOpts:
     power_iters: int = 8            # p
     sample_factor: int = 1          # a
     seed: int = 0
+    split_mode: str = "power"       # "power" (basic) or "diag" (diagonalized)
 
 
 def sample_threshold(n: int, d: int, a: int) -> int:
@@ -292,6 +298,43 @@ def principal_direction(Xs: np.ndarray, M: np.ndarray, u0: np.ndarray, p: int) -
     return u
 
 
+def pc_basis(X: np.ndarray, M: np.ndarray):
+    """Principal-component basis of the whole set in the geometry M (v1
+    §3.2.1 "Diagonalized recursive splitting"; rev §4.1.1).
+
+    The vectors are represented as z = R x with R the root matrix of M (the
+    transforms of v1 §3.2.2); C is the centred covariance of the z over all
+    rows and C = W diag(lam) W^T its eigendecomposition. Returns A = R W and
+    lam: coordinate j of a vector is y_j = x . a_j (a_j column j of A).
+    Columns are ordered by descending eigenvalue; each column of W is signed
+    so that its largest-magnitude entry is positive (the first such entry on
+    ties), which fixes which child is "left" at a split.
+    """
+    X = np.asarray(X, np.float64)
+    R = root_matrix(M)
+    Z = X @ R
+    Zc = Z - Z.mean(axis=0)
+    C = Zc.T @ Zc / X.shape[0]
+    lam, W = np.linalg.eigh(C)
+    order = np.argsort(-lam, kind="stable")
+    lam, W = lam[order], W[:, order]
+    for j in range(W.shape[1]):
+        k = int(np.argmax(np.abs(W[:, j])))
+        if W[k, j] < 0:
+            W[:, j] = -W[:, j]
+    return R @ W, lam
+
+
+def diag_direction(Xs: np.ndarray, A: np.ndarray):
+    """Coordinate of highest variance over the sample rows Xs (population
+    variance of y_j = x . a_j; the lowest index on ties) and its column of A:
+    splitting along y_j is projecting onto a_j."""
+    Y = np.asarray(Xs, np.float64) @ A
+    var = ((Y - Y.mean(axis=0)) ** 2).mean(axis=0)
+    j = int(np.argmax(var))
+    return j, A[:, j].copy()
+
+
 def split_by_scores(members: np.ndarray, scores: np.ndarray, t: int):
     """Members ordered by (score, token id); the first t go left. Both halves
     keep the node's order (ascending token id). Scores that compare equal
@@ -313,18 +356,25 @@ class TreeTrace:
 
 
 def cluster_tree(X: np.ndarray, M: np.ndarray, hashes: np.ndarray, c: int, opts: ClusterOpts,
-                 head: int, tensor: int, trace: TreeTrace | None = None) -> np.ndarray:
+                 head: int, tensor: int, trace: TreeTrace | None = None,
+                 basis: np.ndarray | None = None) -> np.ndarray:
     """Recursive PDDP splitting of the rows of X under geometry M.
 
     Returns perm with perm[p] = token at cluster-major position p; cluster j
     occupies [j c, j c + n_j). At each node: subsample, centred covariance,
     warm-started power iteration with the metric injected, projection of all
-    members, split at the multiple of c closest to half.
+    members, split at the multiple of c closest to half. With
+    opts.split_mode == "diag" the direction is instead the basis column of
+    highest sample variance (``basis`` = A of pc_basis, computed here if not
+    given).
     """
     X = np.asarray(X, np.float64)
     N, d = X.shape
     perm = np.arange(N, dtype=np.int64)
     parent_dir: dict = {}
+    diag = opts.split_mode == "diag"
+    if diag and basis is None:
+        basis, _ = pc_basis(X, M)
     for level, nodes in enumerate(tree_levels(N, c)):
         if not any(nd.n > c for nd in nodes):
             break
@@ -335,16 +385,19 @@ def cluster_tree(X: np.ndarray, M: np.ndarray, hashes: np.ndarray, c: int, opts:
                 continue
             members = perm[nd.off:nd.off + nd.n]
             T = sample_members(members, hashes, level, tensor, d, opts.sample_factor, opts.seed)
-            r = warm_vector(opts.seed, head, tensor, level, nd.index, d)
-            r = r / np.linalg.norm(r)
-            par = parent_dir.get((level - 1, nd.index // 2))
-            if par is None:
-                u0 = r
+            if diag:
+                _, u = diag_direction(X[T], basis)
             else:
-                s = par + r
-                ns = np.linalg.norm(s)
-                u0 = s / ns if ns > 0 else r
-            u = principal_direction(X[T], M, u0, opts.power_iters)
+                r = warm_vector(opts.seed, head, tensor, level, nd.index, d)
+                r = r / np.linalg.norm(r)
+                par = parent_dir.get((level - 1, nd.index // 2))
+                if par is None:
+                    u0 = r
+                else:
+                    s = par + r
+                    ns = np.linalg.norm(s)
+                    u0 = s / ns if ns > 0 else r
+                u = principal_direction(X[T], M, u0, opts.power_iters)
             parent_dir[(level, nd.index)] = u
             scores = X[members] @ u
             sc[nd.off:nd.off + nd.n] = scores

@@ -225,6 +225,120 @@ def test_power_iteration_zero_covariance_keeps_warm_start():
 
 
 # ---------------------------------------------------------------------------
+# Diagonalized splitting (v1 §3.2.1 "Diagonalized recursive splitting";
+# rev §4.1.1): principal-component basis and highest-variance coordinate
+# ---------------------------------------------------------------------------
+
+def _orthonormal(r, n, d):
+    q, _ = np.linalg.qr(r.standard_normal((n, d)))
+    return q
+
+
+def check_pc_basis_known_axes():
+    # X built with covariance exactly U diag(sig^2) U^T: in the identity
+    # geometry the basis is U itself, columns by decreasing sig, signed so
+    # that the largest-magnitude entry is positive
+    r = _rng(40)
+    N, d = 300, 6
+    U = _orthonormal(r, d, d)
+    sig = np.array([5.0, 3.5, 2.0, 1.2, 0.7, 0.3])
+    H = r.standard_normal((N, d))
+    Hc, _ = np.linalg.qr(H - H.mean(0))
+    Hc = Hc - Hc.mean(0)   # centred columns, orthonormal up to rounding
+    X = math.sqrt(N) * (Hc * sig) @ U.T + r.standard_normal(d)
+    A, lam = o.pc_basis(X, np.eye(d))
+    assert np.allclose(lam, sig ** 2, rtol=1e-9)
+    for j in range(d):
+        u = U[:, j] * (1.0 if U[np.argmax(np.abs(U[:, j])), j] > 0 else -1.0)
+        assert np.allclose(A[:, j], u, atol=1e-9)
+
+
+def check_pc_basis_decorrelates():
+    # In a metric geometry (rank-deficient too) the coordinates y = x A are
+    # uncorrelated with variances lam in decreasing order, and A = R W with
+    # W orthonormal (A^T M^+ A = I on the range of M)
+    r = _rng(41)
+    N, d = 400, 7
+    X = r.standard_normal((N, d)) @ r.standard_normal((d, d)) + r.standard_normal(d)
+    for rank in (d, d - 2):
+        B = r.standard_normal((d, rank))
+        M = B @ B.T / rank
+        A, lam = o.pc_basis(X, M)
+        Y = X @ A
+        Yc = Y - Y.mean(0)
+        C = Yc.T @ Yc / N
+        assert np.allclose(C, np.diag(lam), atol=1e-9 * lam.max())
+        assert np.all(np.diff(lam) <= 1e-12 * lam.max())
+        R = o.root_matrix(M)
+        W = np.linalg.pinv(R) @ A
+        keep = lam > 1e-9 * lam.max()
+        Wk = W[:, keep]
+        assert np.allclose(Wk.T @ Wk, np.eye(keep.sum()), atol=1e-8)
+        for j in np.flatnonzero(keep):
+            k = np.argmax(np.abs(W[:, j]))
+            assert W[k, j] > 0
+
+
+def check_diag_direction_bruteforce():
+    r = _rng(42)
+    for trial in range(50):
+        m, d = int(r.integers(2, 9)), int(r.integers(2, 6))
+        Xs = r.standard_normal((m, d))
+        A = r.standard_normal((d, d))
+        if trial % 5 == 0:
+            A[:, 2 % d] = A[:, 0]       # an exact tie: the lower index wins
+        var = []
+        for j in range(d):
+            y = [sum(Xs[i, k] * A[k, j] for k in range(d)) for i in range(m)]
+            mu = sum(y) / m
+            var.append(sum((v - mu) ** 2 for v in y) / m)
+        best = max(var)
+        want = min(j for j in range(d) if var[j] >= best - 1e-12 * max(1.0, best))
+        j, u = o.diag_direction(Xs, A)
+        assert j == want and np.array_equal(u, A[:, j])
+
+
+def test_pc_basis_known_axes():
+    check_pc_basis_known_axes()
+
+
+def test_pc_basis_decorrelates():
+    check_pc_basis_decorrelates()
+
+
+def test_diag_direction_bruteforce():
+    check_diag_direction_bruteforce()
+
+
+def test_diag_cluster_tree_splits():
+    # Every node of the diagonalized tree splits at the (score, id) order
+    # statistic of the projections onto the basis column of highest sample
+    # variance, and the result is a bijection with the data-independent sizes
+    r = _rng(43)
+    for c in (2, 4):
+        for N in (13, 32):
+            X = r.standard_normal((N, 4)) @ np.diag([3.0, 2.0, 1.0, 0.5])
+            hashes = o.row_hash(o.row_words(X.astype(np.float32), "f32"))
+            opts = o.ClusterOpts(seed=5, split_mode="diag")
+            A, _ = o.pc_basis(X, np.eye(4))
+            tr = o.TreeTrace()
+            perm = o.cluster_tree(X, np.eye(4), hashes, c, opts, 0, 1, tr)
+            assert sorted(perm.tolist()) == list(range(N))
+            for lvl, nodes in enumerate(o.tree_levels(N, c)[:len(tr.scores)]):
+                before, after, sc = tr.perms[lvl], tr.perms[lvl + 1], tr.scores[lvl]
+                for nd in nodes:
+                    if nd.n <= c:
+                        continue
+                    mem = before[nd.off:nd.off + nd.n]
+                    T = o.sample_members(mem, hashes, lvl, 1, 4, 1, 5)
+                    j, u = o.diag_direction(X[T], A)
+                    assert np.allclose(sc[nd.off:nd.off + nd.n], X[mem] @ u, rtol=0, atol=0)
+                    t = o.split_size(nd.n, c)
+                    order = sorted(zip((X[mem] @ u).tolist(), mem.tolist()))
+                    assert after[nd.off:nd.off + t].tolist() == sorted(m for _, m in order[:t])
+
+
+# ---------------------------------------------------------------------------
 # Split and sampling (v1 §3.2.1; rev §4.1.1)
 # ---------------------------------------------------------------------------
 
@@ -563,7 +677,30 @@ def _no_log_count(Q, K, V, perm_q, perm_k, c, blocks, compensate, scale=None):
 
 _orig = {name: getattr(o, name) for name in
          ["sparse_attention", "split_size", "metric_matrices", "principal_direction", "topk_row",
-          "centroids", "dense_attention", "split_by_scores", "fmix64"]}
+          "centroids", "dense_attention", "split_by_scores", "fmix64", "pc_basis",
+          "diag_direction"]}
+
+
+def _basis_ascending(X, M):
+    A, lam = _orig["pc_basis"](X, M)
+    return A[:, ::-1].copy(), lam[::-1].copy()
+
+
+def _basis_without_root(X, M):
+    return _orig["pc_basis"](X, np.eye(M.shape[0]))
+
+
+def _direction_lowest_variance(Xs, A):
+    Y = np.asarray(Xs, np.float64) @ A
+    var = ((Y - Y.mean(axis=0)) ** 2).mean(axis=0)
+    j = int(np.argmin(var))
+    return j, A[:, j].copy()
+
+
+def _direction_uncentred(Xs, A):
+    Y = np.asarray(Xs, np.float64) @ A
+    j = int(np.argmax((Y ** 2).mean(axis=0)))
+    return j, A[:, j].copy()
 
 
 def _split_size_larger(n, c):
@@ -621,10 +758,15 @@ PLANTED = [
     ("dense_attention", _dense_no_scale, check_dense_against_libraries),
     ("split_by_scores", _split_reversed, check_split_by_scores_bruteforce),
     ("fmix64", _fmix_wrong_shift, check_splitmix64_published),
+    ("pc_basis", _basis_ascending, check_pc_basis_known_axes),
+    ("pc_basis", _basis_without_root, check_pc_basis_decorrelates),
+    ("diag_direction", _direction_lowest_variance, check_diag_direction_bruteforce),
+    ("diag_direction", _direction_uncentred, check_diag_direction_bruteforce),
 ]
 
 
-@pytest.mark.parametrize("name,mutant,check", PLANTED, ids=[p[0] for p in PLANTED])
+@pytest.mark.parametrize("name,mutant,check", PLANTED,
+                         ids=[f"{p[0]}-{p[1].__name__.lstrip('_')}" for p in PLANTED])
 def test_planted_mistakes(monkeypatch, name, mutant, check):
     check()                                   # the pin passes on the real oracle
     monkeypatch.setattr(o, name, mutant)
