@@ -89,6 +89,8 @@ def parse():
                     help="steps timed one by one after a 512 MiB cache flush")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the copy and GEMM rate measurements")
+    ap.add_argument("--split-mode", choices=["power", "diag"], default="power",
+                    help="basic (power iteration) or diagonalized recursive splitting")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="quality/latency sweep over cluster size, selected fraction, SMC and "
@@ -106,7 +108,7 @@ def gen_inputs(w):
     return Q, K, V
 
 
-def cpu_baseline(w, Q, K, V, topk, heads):
+def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power"):
     """The oracle, untuned, on the first `heads` heads of the same input."""
     import oracle.clusterattn as o
     try:
@@ -114,7 +116,7 @@ def cpu_baseline(w, Q, K, V, topk, heads):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = 1
-    opts = o.ClusterOpts(seed=w.cluster_seed)
+    opts = o.ClusterOpts(seed=w.cluster_seed, split_mode=split_mode)
     t0 = time.perf_counter()
     o.forward(Q[:, :heads], K[:, :heads], V[:, :heads], w.c, topk, w.compensate, opts, w.dtype)
     t = time.perf_counter() - t0
@@ -282,7 +284,7 @@ def main():
     def step(evs=None, kev=None):
         if evs:
             evs[0].record()
-        cr = ca.cluster(Q, K, c, seed=w.cluster_seed, workspace=ws_c)
+        cr = ca.cluster(Q, K, c, seed=w.cluster_seed, split_mode=args.split_mode, workspace=ws_c)
         if evs:
             evs[1].record()
         blocks = ca.route(cr.cent_q, cr.cent_k, topk, workspace=ws_r)
@@ -339,6 +341,16 @@ def main():
             cold_ms.append(a_ev.elapsed_time(b_ev))
         del flush
 
+    # clustering + routing against the HBM roofline: algorithmic bytes are, per
+    # split level, tensor and token, the row read for the projection plus the
+    # index read and write (2 D e + 8 B, e = element size), plus the
+    # compulsory metric pass (Q and K rows) and centroid pass (Q, K, V rows)
+    esz = 2 if w.dtype == "bf16" else 4
+    n_levels = ca.tree_levels(N, c)
+    clu_bytes = float(B * H) * (n_levels * 2 * N * (D * esz + 8) + 5 * N * D * esz)
+    clu_ms = float(st_cluster + st_route)
+    clu_gbs = clu_bytes / (clu_ms * 1e-3) / 1e9
+
     traffic = recorded_traffic(w.name, topk) if B * H == w.B * w.H else None
     eff = 4.0 * D * N * N * B * H / (wall) / 1e12
     result = {
@@ -355,7 +367,8 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "N": N, "head_dim": D,
-                   "cluster_size": c, "topk": topk, "compensate": w.compensate},
+                   "cluster_size": c, "topk": topk, "compensate": w.compensate,
+                   "split_mode": args.split_mode},
         "stage_ms": {"cluster": round(float(st_cluster), 4), "route": round(float(st_route), 4),
                      "attend": round(float(st_attend), 4),
                      "attend_kernel": round(float(t_attn_kernel), 4),
@@ -373,6 +386,10 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "flops_per_launch": flops_attn,
+        },
+        "cluster_route_hbm": {
+            "bytes": clu_bytes, "ms": round(clu_ms, 4), "achieved": round(clu_gbs, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(clu_gbs / PEAK_HBM_GBS, 4),
         },
     }
 
@@ -399,7 +416,7 @@ def main():
 
     if not args.no_cpu_baseline:
         heads = max(1, min(args.cpu_heads, H))
-        result["cpu_baseline"] = cpu_baseline(w, Qn, Kn, Vn, topk, heads)
+        result["cpu_baseline"] = cpu_baseline(w, Qn, Kn, Vn, topk, heads, args.split_mode)
 
     print(json.dumps(result), flush=True)
 

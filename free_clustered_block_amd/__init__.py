@@ -40,7 +40,10 @@ class _Opts(ctypes.Structure):
     _fields_ = [("transform", ctypes.c_int), ("query_normalize", ctypes.c_int),
                 ("power_iters", ctypes.c_int), ("sample_factor", ctypes.c_int),
                 ("seed", ctypes.c_uint64), ("trace_perm", ctypes.c_void_p),
-                ("trace_score", ctypes.c_void_p), ("trace_dir", ctypes.c_void_p)]
+                ("trace_score", ctypes.c_void_p), ("trace_dir", ctypes.c_void_p),
+                ("split_mode", ctypes.c_int), ("trace_basis", ctypes.c_void_p)]
+
+_SPLIT_MODES = {"power": 0, "diag": 1}
 
 
 def load() -> ctypes.CDLL:
@@ -192,12 +195,19 @@ class ClusterResult:
     trace_perm: object = None
     trace_score: object = None
     trace_dir: object = None
+    trace_basis: object = None
 
 
 def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = True,
-            power_iters: int = 8, sample_factor: int = 1, seed: int = 0, trace: bool = False,
-            workspace=None) -> ClusterResult:
-    """ca_cluster: permutations into clusters of size c and the cluster centroids."""
+            power_iters: int = 8, sample_factor: int = 1, seed: int = 0,
+            split_mode: str = "power", trace: bool = False, workspace=None) -> ClusterResult:
+    """ca_cluster: permutations into clusters of size c and the cluster centroids.
+
+    split_mode "power" is basic recursive splitting (power iteration per node),
+    "diag" diagonalized recursive splitting (one principal-component basis per
+    tree, each node splits along its highest-variance coordinate)."""
+    if split_mode not in _SPLIT_MODES:
+        raise ValueError(f"split_mode must be one of {sorted(_SPLIT_MODES)}")
     torch = _torch()
     _bhnd(Q, K)
     B, H, N, D = Q.shape
@@ -208,15 +218,18 @@ def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = Tru
     cent_q = torch.empty((B, H, n_c, D), dtype=torch.float32, device=dev)
     cent_k = torch.empty_like(cent_q)
     counts = torch.empty((B, H, n_c), dtype=torch.int32, device=dev)
-    tp = ts = td = None
+    tp = ts = td = tb = None
     if trace:
         L = tree_levels(N, c)
         S = 1 << max(L - 1, 0)
         tp = torch.full((L + 1, B * H, 2, N), -1, dtype=torch.int32, device=dev)
         ts = torch.full((max(L, 1), B * H, 2, N), float("nan"), dtype=torch.float32, device=dev)
         td = torch.full((max(L, 1), B * H, 2, S, D), float("nan"), dtype=torch.float32, device=dev)
+        if split_mode == "diag":
+            tb = torch.full((B * H, 2, D, D), float("nan"), dtype=torch.float32, device=dev)
     opts = _Opts(int(transform), int(query_normalize), power_iters, sample_factor,
-                 seed & ((1 << 64) - 1), _ptr(tp), _ptr(ts), _ptr(td))
+                 seed & ((1 << 64) - 1), _ptr(tp), _ptr(ts), _ptr(td),
+                 _SPLIT_MODES[split_mode], _ptr(tb))
     nbytes = workspace_size(OP_CLUSTER, B, H, N, D, c)
     ws = _ws(nbytes, dev, workspace)
     st = load().ca_cluster(Q.data_ptr(), K.data_ptr(), _dtype_code(Q), B, H, N, D, c,
@@ -224,7 +237,7 @@ def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = Tru
                            cent_q.data_ptr(), cent_k.data_ptr(), counts.data_ptr(),
                            _ptr(ws), nbytes, _stream_ptr(dev))
     _check(st)
-    return ClusterResult(perm_q, perm_k, cent_q, cent_k, counts, tp, ts, td)
+    return ClusterResult(perm_q, perm_k, cent_q, cent_k, counts, tp, ts, td, tb)
 
 
 def route(cent_q, cent_k, topk: int, *, return_scores: bool = False, workspace=None):

@@ -47,6 +47,7 @@ struct ClusterWs {
   int32_t* chunk_cnt;
   int32_t* stok;
   float* zbuf;
+  float *Cq, *Rbuf, *Zbuf, *At;   // diagonalized splitting: basis of each tree
 };
 
 ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c) {
@@ -74,6 +75,10 @@ ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c) {
   w.chunk_cnt = cv.take<int32_t>(T * ((N + c - 1) / c));
   w.stok = cv.take<int32_t>(T * N);
   w.zbuf = cv.take<float>(T * N);
+  w.Cq = cv.take<float>((size_t)BH * D * D);
+  w.Rbuf = cv.take<float>(T * D * D);
+  w.Zbuf = cv.take<float>(T * D * D);
+  w.At = cv.take<float>(T * D * D);
   return w;
 }
 
@@ -185,8 +190,10 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   if (!supported_c(c)) return fail(CA_ERR_UNSUPPORTED, "cluster_size must be 64, 128 or 256");
   if (N < c) return fail(CA_ERR_INVALID_ARG, "N must be >= cluster_size");
   if ((N + c - 1) / c > 8192) return fail(CA_ERR_UNSUPPORTED, "at most 8192 clusters");
-  ca_cluster_opts o = {1, 1, 8, 1, 0, nullptr, nullptr, nullptr};
+  ca_cluster_opts o = {1, 1, 8, 1, 0, nullptr, nullptr, nullptr, 0, nullptr};
   if (opts) o = *opts;
+  if (o.split_mode != 0 && o.split_mode != 1)
+    return fail(CA_ERR_INVALID_ARG, "split_mode must be 0 (power iteration) or 1 (diagonalized)");
   if (o.power_iters < 1 || o.power_iters > 1000)
     return fail(CA_ERR_INVALID_ARG, "power_iters must be in [1, 1000]");
   if (o.sample_factor < 1 || o.sample_factor > 4096)
@@ -202,6 +209,13 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
 
   launch_metric(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, o.transform, o.query_normalize, w.partial,
                 w.hash, w.Mq, w.Mk, w.kbar, w.gsplit, w.s, w.Mpk, st);
+  if (o.split_mode == 1) {
+    launch_basis(Q, dt == CA_BF16 ? 0 : 1, BH, N, D, o.transform, w.s, w.Mq, w.Mk, w.partial, w.Cq,
+                 w.Rbuf, w.Zbuf, w.At, st);
+    if (o.trace_basis)
+      CA_HIP_CHECK(hipMemcpyAsync(o.trace_basis, w.At, 2 * (size_t)BH * D * D * 4,
+                                  hipMemcpyDeviceToDevice, st));
+  }
   launch_perm_init(w.permA, 2 * BH, N, st);
   int32_t* cur = w.permA;
   int32_t* nxt = w.permB;
@@ -214,6 +228,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     a.Q = Q; a.K = K; a.dtype = dt == CA_BF16 ? 0 : 1;
     a.BH = BH; a.N = N; a.D = D; a.c = c; a.level = level;
     a.transform = o.transform; a.power_iters = o.power_iters; a.sample_factor = o.sample_factor;
+    a.split_mode = o.split_mode; a.basis = w.At;
     a.seed = o.seed;
     a.perm_in = cur; a.perm_out = nxt;
     a.hpos_in = hcur; a.hpos_out = hnxt; a.s = w.s; a.Mq = w.Mq; a.Mk = w.Mk; a.Mpk = w.Mpk;

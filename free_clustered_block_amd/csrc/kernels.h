@@ -19,6 +19,7 @@ struct LevelArgs {
   int dtype;
   int BH, N, D, c, level;
   int transform, power_iters, sample_factor;
+  int split_mode;           // 0 = power iteration, 1 = diagonalized (basis below)
   uint64_t seed;
   const int32_t* perm_in;   // [2 BH][N]
   int32_t* perm_out;        // [2 BH][N]
@@ -29,6 +30,7 @@ struct LevelArgs {
   const float* Mk;          // [BH][D][D]
   const float* Mpk;         // [2 BH][D D]: metric of each tree (M_k for queries, M_q for
                             // keys) packed in the per-lane order of the direction kernel
+  const float* basis;       // [2 BH][D][D]: row j = basis direction a_j (diagonalized)
   const float* dir_prev;    // [2 BH][slots/2][D]
   float* dir_cur;           // [2 BH][slots][D]
   int nchunks;              // ceil(N / c)
@@ -42,6 +44,14 @@ struct LevelArgs {
   int trace_slots;
 };
 void launch_level(const LevelArgs& a, hipStream_t st);
+
+// basis.hip ------------------------------------------------------------------
+// Principal-component basis of each tree for diagonalized splitting: At
+// [2 BH][D][D] (row j = a_j); partial as for launch_metric, Cq [BH][D][D],
+// Rbuf and Zbuf [2 BH][D][D] scratch.
+void launch_basis(const void* Q, int dtype, int BH, int N, int D, int transform, const float* s,
+                  const float* Mq, const float* Mk, float* partial, float* Cq, float* Rbuf,
+                  float* Zbuf, float* At, hipStream_t st);
 void launch_perm_init(int32_t* perm, int trees, int N, hipStream_t st);
 void launch_perm_out(const int32_t* perm, int BH, int N, int32_t* perm_q, int32_t* perm_k,
                      hipStream_t st);

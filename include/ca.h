@@ -66,7 +66,8 @@ typedef enum {
 /*
  * Options of the clustering (v1 §3.2). Pass NULL for the defaults
  * {transform=1, query_normalize=1, power_iters=8, sample_factor=1, seed=0,
- *  trace_perm=NULL, trace_score=NULL, trace_dir=NULL}.
+ *  trace_perm=NULL, trace_score=NULL, trace_dir=NULL, split_mode=0,
+ *  trace_basis=NULL}.
  *
  *  transform        1: keys are split under the query metric M_q = Q^T Q / N
  *                   (Eq. 12-14) and queries under the centred key metric
@@ -92,6 +93,22 @@ typedef enum {
  *                   S = 2^(L-1): the unit direction of the node in slot j of
  *                   level l (slot j's children are slots 2j and 2j+1 of level
  *                   l+1); slots without a splitting node are left untouched.
+ *  split_mode       0: basic recursive splitting, each node's direction by
+ *                   power iteration (v1 §3.2.1 "Basic recursive splitting").
+ *                   1: diagonalized recursive splitting (v1 §3.2.1
+ *                   "Diagonalized recursive splitting"; later revision
+ *                   §4.1.1): each tree first computes the principal-component
+ *                   basis A = R W of its whole set in the tree's geometry (R
+ *                   the symmetric root of the geometry with negative
+ *                   eigenvalues clamped, W the eigenvectors of R C R with C
+ *                   the centred covariance of the split vectors, by
+ *                   descending eigenvalue, each signed so that its largest-
+ *                   magnitude entry is positive); each node then splits along
+ *                   the basis coordinate y_j = x . a_j of highest population
+ *                   variance over its sample (lowest j on ties). power_iters
+ *                   is ignored. trace_dir then holds the chosen a_j.
+ *  trace_basis      optional device buffer float [B*H][2][D][D] (split_mode
+ *                   1 only): row j of tree (head, tensor) is a_j.
  */
 typedef struct {
   int transform;
@@ -102,6 +119,8 @@ typedef struct {
   int32_t* trace_perm;
   float* trace_score;
   float* trace_dir;
+  int split_mode;
+  float* trace_basis;
 } ca_cluster_opts;
 
 /* Number of split levels of the data-independent tree for (N, c): the tree

@@ -88,6 +88,9 @@ def test_cluster_rejects_bad_arguments(lib):
     assert _cluster(lib, opts=ctypes.byref(opts)) == 1
     opts = ca._Opts(1, 1, 8, 0, 0, None, None, None)
     assert _cluster(lib, opts=ctypes.byref(opts)) == 1
+    opts = ca._Opts(1, 1, 8, 1, 0, None, None, None, 2, None)
+    assert _cluster(lib, opts=ctypes.byref(opts)) == 1
+    assert b"split_mode" in lib.ca_last_error()
     assert _cluster(lib, ws=None, ws_bytes=0) == 3
     assert _cluster(lib, ws=FAKE + 8, ws_bytes=2**30) == 3
     assert _cluster(lib, ws_bytes=100) == 3

@@ -1,0 +1,207 @@
+"""GPU parity of diagonalized recursive splitting (paper: "ClusterAttention:
+A training-free speedup of bidirectional attention", arXiv 2608.26965 v1
+§3.2.1 "Diagonalized recursive splitting"; later revision §4.1.1).
+
+Acceptance:
+
+* the basis: A A^T equals the square of the geometry's root, the covariance
+  of the coordinates x . a_j is diagonal with the oracle's eigenvalues in
+  descending order, and every column whose eigenvalue is separated from its
+  neighbours by more than 1% of the largest matches the oracle's column,
+  sign included, to 1e-6 in cosine;
+* per node, given the GPU's membership and basis: the oracle's fp64 variances
+  of the sampled coordinates make the GPU's choice the maximum or within
+  1e-4 of it (a near tie); the select-and-partition fed the GPU's fp32
+  projections reproduces the GPU's children bit for bit; the projections
+  match the fp64 ones to 1e-4 of their spread and the sides agree except at
+  the threshold;
+* end to end, the whole tree agrees with the oracle's own fp64 tree on at
+  least 95% of co-memberships.
+"""
+import numpy as np
+import pytest
+
+import oracle.clusterattn as o
+import synth
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (workload, N, heads, c)
+    "gmm_f32_d64_c64": ("small_gmm_1k", 1024, 1, 64),
+    "video_bf16_d128_c128_ragged": ("video_32760", 4000, 2, 128),
+    "gmm_bf16_d64_c256_ragged": ("tabular_256k", 5000, 2, 256),
+    "peaked_bf16_d64_c64": ("sweep_16k_peaked", 2000, 2, 64),
+}
+
+_cache = {}
+
+
+def _inputs(name):
+    if name not in _cache:
+        wname, N, H, c = CASES[name]
+        w = synth.WORKLOADS[wname]
+        Q, K, _ = synth.generate(w, heads=slice(0, H), N=N)
+        _cache[name] = (w, Q, K, c)
+    return _cache[name]
+
+
+def _dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32))
+    t = t.to(torch.bfloat16) if dtype == "bf16" else t
+    return t.cuda().contiguous()
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy() if t.is_floating_point() else t.detach().cpu().numpy()
+
+
+def _opts(w):
+    return o.ClusterOpts(seed=w.cluster_seed, split_mode="diag")
+
+
+def _gpu(ca, name, trace=True):
+    w, Q, K, c = _inputs(name)
+    return ca.cluster(_dev(Q, w.dtype), _dev(K, w.dtype), c, seed=w.cluster_seed,
+                      split_mode="diag", trace=trace)
+
+
+def _trees(w, Q, K):
+    """(tree, tensor, head, X, G, hashes) for every tree of the batch."""
+    B, H = Q.shape[:2]
+    opts = _opts(w)
+    for b in range(B):
+        for h in range(H):
+            head = b * H + h
+            Xq, Gq, Xk, Gk = o.head_representations(Q[b, h], K[b, h], opts)
+            hq = o.row_hash(o.row_words(Q[b, h], w.dtype))
+            hk = o.row_hash(o.row_words(K[b, h], w.dtype))
+            yield head * 2, 0, head, Xq, Gq, hq
+            yield head * 2 + 1, 1, head, Xk, Gk, hk
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_basis_against_oracle(ca, name):
+    w, Q, K, c = _inputs(name)
+    B, H, N, D = Q.shape
+    res = _gpu(ca, name)
+    tb = _np(res.trace_basis).reshape(2 * B * H, D, D).astype(np.float64)
+    for tree, tensor, head, X, G, _ in _trees(w, Q, K):
+        Ag = tb[tree].T                       # column j = a_j
+        Ao, lam = o.pc_basis(X, G)
+        R = o.root_matrix(G)
+        RR = R @ R
+        assert np.linalg.norm(Ag @ Ag.T - RR) <= 1e-4 * np.linalg.norm(RR), (name, tree)
+        Y = X @ Ag
+        C = np.cov(Y, rowvar=False, bias=True)
+        scale = lam[0]
+        off = C - np.diag(np.diag(C))
+        assert np.max(np.abs(off)) <= 1e-4 * scale, (name, tree, np.max(np.abs(off)) / scale)
+        assert np.max(np.abs(np.diag(C) - lam)) <= 1e-4 * scale, (name, tree)
+        # well-separated columns: the oracle's column, sign included unless the
+        # sign rule's largest-magnitude entry is ambiguous
+        Z = X @ R
+        lw, W = np.linalg.eigh(np.cov(Z, rowvar=False, bias=True))
+        W = W[:, np.argsort(-lw, kind="stable")]
+        gaps = np.full(D, np.inf)
+        gaps[:-1] = np.minimum(gaps[:-1], lam[:-1] - lam[1:])
+        gaps[1:] = np.minimum(gaps[1:], lam[:-1] - lam[1:])
+        checked = 0
+        for j in range(D):
+            if gaps[j] <= 1e-2 * scale:
+                continue
+            cos = Ag[:, j] @ Ao[:, j] / (np.linalg.norm(Ag[:, j]) * np.linalg.norm(Ao[:, j]))
+            assert abs(cos) >= 1 - 1e-6, (name, tree, j, cos)
+            if cos < 0:
+                m = np.sort(np.abs(W[:, j]))[::-1]
+                assert m[0] - m[1] <= 1e-3 * m[0], (name, tree, j)
+            checked += 1
+        print(f"{name} tree {tree}: {checked} well-separated columns matched")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_diag_cluster_per_level(ca, name):
+    w, Q, K, c = _inputs(name)
+    B, H, N, D = Q.shape
+    res = _gpu(ca, name)
+    L = ca.tree_levels(N, c)
+    S = 1 << max(L - 1, 0)
+    tp = _np(res.trace_perm).reshape(L + 1, 2 * B * H, N)
+    ts = _np(res.trace_score).reshape(max(L, 1), 2 * B * H, N)
+    td = _np(res.trace_dir).reshape(max(L, 1), 2 * B * H, S, D)
+    tb = _np(res.trace_basis).reshape(2 * B * H, D, D)
+    levels = o.tree_levels(N, c)
+    opts = _opts(w)
+    near_ties = 0
+    for tree, tensor, head, X, G, hs in _trees(w, Q, K):
+        A = tb[tree].T.astype(np.float64)
+        assert np.array_equal(tp[0, tree], np.arange(N))
+        disagree, total = 0, 0
+        for lvl in range(L):
+            before, after, sc = tp[lvl, tree], tp[lvl + 1, tree], ts[lvl, tree]
+            moved = np.zeros(N, bool)
+            for nd in levels[lvl]:
+                if nd.n <= c:
+                    continue
+                sl = slice(nd.off, nd.off + nd.n)
+                moved[sl] = True
+                mem = before[sl].astype(np.int64)
+                t = o.split_size(nd.n, c)
+                left, right = o.split_by_scores(mem, sc[sl].astype(np.float64), t)
+                assert np.array_equal(after[nd.off:nd.off + t], left), (name, lvl, tensor)
+                assert np.array_equal(after[nd.off + t:nd.off + nd.n], right)
+                # the GPU's direction is one of its basis rows
+                hit = np.flatnonzero(np.all(tb[tree] == td[lvl, tree, nd.index], axis=1))
+                assert hit.size >= 1, (name, lvl, tensor, nd.index)
+                jg = int(hit[0])
+                # the oracle's choice on the GPU's membership and basis
+                T = o.sample_members(mem, hs, lvl, tensor, D, opts.sample_factor, opts.seed)
+                jo, _ = o.diag_direction(X[T], A)
+                if jg != jo:
+                    Y = X[T] @ A
+                    var = ((Y - Y.mean(axis=0)) ** 2).mean(axis=0)
+                    e2 = (Y ** 2).mean(axis=0)
+                    assert var[jg] >= var[jo] - 1e-4 * var[jo] - 1e-6 * e2[jo], (name, lvl, tensor)
+                    near_ties += 1
+                so = X[mem] @ A[:, jg]
+                sg = sc[sl].astype(np.float64)
+                spread = np.std(so) + 1e-30
+                assert np.max(np.abs(so - sg)) <= 1e-4 * spread, (name, lvl, tensor)
+                lo, _ = o.split_by_scores(mem, so, t)
+                bad = np.isin(mem, lo) != np.isin(mem, left)
+                disagree += int(bad.sum())
+                total += nd.n
+                if bad.any():
+                    thr = np.sort(so)[t - 1:t + 1].mean()
+                    iqr = np.subtract(*np.percentile(so, [75, 25])) + 1e-30
+                    assert np.all(np.abs(so[bad] - thr) <= 1e-4 * iqr), (name, lvl, tensor)
+            assert np.array_equal(before[~moved], after[~moved])
+        assert disagree <= 1e-3 * max(total, 1), (name, tensor, disagree, total)
+        perm = _np(res.perm_q if tensor == 0 else res.perm_k)[head // H, head % H]
+        assert np.array_equal(perm, tp[L, tree])
+        for j, nj in enumerate(o.leaf_sizes(N, c)):
+            assert np.all(np.diff(perm[j * c:j * c + nj]) > 0)
+    print(f"{name}: {near_ties} near-tie coordinate choices")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_diag_end_to_end_agreement(ca, name):
+    w, Q, K, c = _inputs(name)
+    B, H = Q.shape[:2]
+    res = _gpu(ca, name, trace=False)
+    pq, pk = o.cluster(Q, K, c, _opts(w), w.dtype)
+    agq = np.mean([o.cluster_agreement(_np(res.perm_q)[b, h], pq[b, h], c)
+                   for b in range(B) for h in range(H)])
+    agk = np.mean([o.cluster_agreement(_np(res.perm_k)[b, h], pk[b, h], c)
+                   for b in range(B) for h in range(H)])
+    print(f"{name}: diagonalized end-to-end agreement q={agq:.5f} k={agk:.5f}")
+    assert agq >= 0.95 and agk >= 0.95
+
+
+def test_diag_deterministic_and_no_trace_equal(ca):
+    name = "video_bf16_d128_c128_ragged"
+    a = _gpu(ca, name, trace=True)
+    b = _gpu(ca, name, trace=False)
+    assert np.array_equal(_np(a.perm_q), _np(b.perm_q))
+    assert np.array_equal(_np(a.perm_k), _np(b.perm_k))
