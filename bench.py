@@ -274,7 +274,8 @@ def main():
         print(f"inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     B, H, N, D = Q.shape
     c = w.c
-    ws_c = torch.empty(ca.workspace_size(ca.OP_CLUSTER, B, H, N, D, c), dtype=torch.uint8, device=dev)
+    op_c = ca.OP_CLUSTER_DIAG if args.split_mode == "diag" else ca.OP_CLUSTER
+    ws_c = torch.empty(ca.workspace_size(op_c, B, H, N, D, c), dtype=torch.uint8, device=dev)
     n_c = -(-N // c)
     ws_r = torch.empty(max(1, ca.workspace_size(ca.OP_ROUTE, B, H, n_c, D, n_c, topk)),
                        dtype=torch.uint8, device=dev)

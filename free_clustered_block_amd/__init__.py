@@ -25,7 +25,7 @@ EXPORTS = ["ca_tree_levels", "ca_workspace_size", "ca_cluster", "ca_route", "ca_
            "ca_dense", "ca_profile_events", "ca_peak_probe", "ca_status_string", "ca_last_error"]
 
 CA_BF16, CA_F32 = 0, 1
-OP_CLUSTER, OP_ROUTE, OP_ATTEND, OP_DENSE = 0, 1, 2, 3
+OP_CLUSTER, OP_ROUTE, OP_ATTEND, OP_DENSE, OP_CLUSTER_DIAG = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -230,7 +230,7 @@ def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = Tru
     opts = _Opts(int(transform), int(query_normalize), power_iters, sample_factor,
                  seed & ((1 << 64) - 1), _ptr(tp), _ptr(ts), _ptr(td),
                  _SPLIT_MODES[split_mode], _ptr(tb))
-    nbytes = workspace_size(OP_CLUSTER, B, H, N, D, c)
+    nbytes = workspace_size(OP_CLUSTER_DIAG if split_mode == "diag" else OP_CLUSTER, B, H, N, D, c)
     ws = _ws(nbytes, dev, workspace)
     st = load().ca_cluster(Q.data_ptr(), K.data_ptr(), _dtype_code(Q), B, H, N, D, c,
                            ctypes.byref(opts), perm_q.data_ptr(), perm_k.data_ptr(),

@@ -8,9 +8,9 @@
 //   qmoment_partial / qmoment_reduce   C_q = Cov(s q) over all queries (the
 //       query representation x = s q of Eq. 16); the key covariance is M_k of
 //       the metric pass.
-//   basis_kernel   one workgroup per tree: cyclic Jacobi eigendecomposition of
-//       the geometry M (-> symmetric root R, negative eigenvalues clamped),
-//       Z = R C_x R, Jacobi of Z (-> W, lam), columns ordered by descending
+//   basis_kernel   one workgroup per tree: eigendecomposition of the geometry
+//       M (-> symmetric root R, negative eigenvalues clamped), Z = R C_x R,
+//       eigendecomposition of Z (-> W, lam), columns ordered by descending
 //       eigenvalue and signed so that each column's largest-magnitude entry is
 //       positive; writes A^T with A = R W, so row j of the output is the
 //       direction whose projection x . a_j is coordinate j.
@@ -171,115 +171,404 @@ __global__ __launch_bounds__(256) void qmoment_reduce(const float* __restrict__ 
 }
 
 // ----------------------------------------------------------------------------
-// Cyclic Jacobi on a symmetric D x D matrix in LDS (row pitch D + 1), all 256
-// threads: each round applies D/2 disjoint rotations of the round-robin
-// (circle-method) pairing, rows first then columns; a rotation is skipped when
-// |a_pq| <= max(1e-7 sqrt(|a_pp a_qq|), 2^-26 tr|S|) with tr|S| the sum of the
-// diagonal magnitudes on entry (below the rounding of fp32 entries, so sweeps
-// end even where small eigenvalues sit next to large ones); sweeps stop when a
-// whole sweep skipped every rotation, after at most kMaxSweeps. V accumulates the
-// rotations (V <- V J): its columns are the eigenvectors, S's diagonal the
-// eigenvalues.
+// Symmetric eigendecomposition of a D x D matrix by one workgroup of 256
+// threads (the textbook pipeline: Householder tridiagonalization, bisection on
+// Sturm counts, inverse iteration, modified Gram-Schmidt, back-transform).
+//
+//   tridiagonalize  the matrix lives in registers, TPR = 256/D threads per row
+//                   (EPT contiguous columns each); for k = 0 .. D-3 the
+//                   reflector H_k = I - beta_k v_k v_k^T zeroes column k below
+//                   the subdiagonal of the trailing block; v_k goes to row k of
+//                   Hv (LDS, zero outside (k, D)); three barriers per step;
+//   bisection       PPE = 256/D lanes per eigenvalue evaluate Sturm counts at
+//                   PPE interior points, so each round shrinks the bracket by
+//                   PPE + 1, down to 2^-22 of the Gershgorin bound;
+//   inverse iter.   one lane per eigenvalue: three solves (T - lam I) x = b with
+//                   the LDL^T factors formed on the fly (pivots below
+//                   2^-23 |T| raised to it), L in registers, x in LDS;
+//   MGS             two passes in descending eigenvalue order, each vector
+//                   normalised, then removed from every vector after it;
+//   back-transform  x <- H_0 ... H_{D-3} x; each vector is signed so that its
+//                   largest-magnitude entry (the first on ties) is positive.
+//
+// Eigenvalues ascend in lam; row j of Xv (global, D x D) is the unit
+// eigenvector of lam[j].
 // ----------------------------------------------------------------------------
 
-constexpr int kMaxSweeps = 30;
-
 template <int D>
-struct JacobiLds {
+struct EigLds {
   static constexpr int P = D + 1;
-  float* S;      // [D][P]
-  float* V;      // [D][P]
-  float* cs;     // [D/2][2]
-  int* pq;       // [D/2][2]
-  int* flag;     // [0]: rotations done in the sweep; [1]: absolute threshold (float bits)
+  float* S;      // in: [D][P] (destroyed); then Hv [D][D]
+  float* Zw;     // [D][D]: inverse-iteration vectors, Zw[i D + j] = x_j[i]
+  float* d;      // [D] diagonal of T
+  float* e;      // [D] e[k] = T[k+1][k]
+  float* e2;     // [D] e^2
+  float* beta;   // [D]
+  float* pb;     // [2][D] p of the current reflector (by step parity)
+  float* red;    // [2][4]
+  float* xb;     // [2][D] vectors broadcast during MGS
 };
 
-// pair i of round r (0 <= r < D - 1) of the circle method on D players
-CA_DEV void jacobi_pair(int D, int r, int i, int* p, int* q) {
-  int a, b;
-  if (i == 0) {
-    a = D - 1;
-    b = r;
-  } else {
-    a = (r + i) % (D - 1);
-    b = (r - i + D - 1) % (D - 1);
+CA_DEV float ii_start(int i, int j) {
+  uint32_t h = (uint32_t)(i + 1) * 0x9E3779B1u ^ (uint32_t)(j + 1) * 0x85EBCA77u;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  return (float)(h >> 8) * 0x1p-24f - 0.5f;
+}
+
+CA_DEV float rcpf(float x) { return __builtin_amdgcn_rcpf(x); }
+
+template <int D>
+CA_DEV void eig_sym(const EigLds<D>& E, float* lam, float* __restrict__ Xv) {
+  constexpr int P = EigLds<D>::P, TPR = 256 / D, EPT = D / TPR;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+
+  // --- Householder tridiagonalization, rows in registers --------------------
+  {
+    const int r = tid / TPR, cb = (tid % TPR) * EPT;
+    const bool lead = (tid % TPR) == 0;
+    auto row_sum = [&](float v) __attribute__((always_inline)) {
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) v += __shfl_xor(v, o);
+      return v;
+    };
+    float sr[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) sr[i] = E.S[r * P + cb + i];
+    __syncthreads();
+    float* Hv = E.S;
+    for (int k = 0; k < D - 2; ++k) {
+      const int par = k & 1;
+      if (r == k) {   // row k (= column k) as it stands
+#pragma unroll
+        for (int i = 0; i < EPT; i += 4) {
+          floatx4_t v;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = sr[i + u];
+          *reinterpret_cast<floatx4_t*>(Hv + k * D + cb + i) = v;
+        }
+      }
+      __syncthreads();
+      if (w == 0) {   // the reflector of column k: v_k in place of row k
+        float* hv = Hv + k * D;
+        const float dk = hv[k], x0 = hv[k + 1];
+        float xa[D / 64], sig = 0.0f;
+#pragma unroll
+        for (int q = 0; q < D / 64; ++q) {
+          const int c = l + 64 * q;
+          xa[q] = hv[c];
+          sig = fmaf(c > k + 1 ? xa[q] : 0.0f, xa[q], sig);
+        }
+        sig = wave_sum(sig);
+        float alpha = x0, bet = 0.0f;
+        if (sig > 0.0f) {
+          const float nrm = sqrtf(fmaf(x0, x0, sig));
+          alpha = x0 >= 0.0f ? -nrm : nrm;
+          bet = 1.0f / (nrm * (nrm + fabsf(x0)));
+        }
+#pragma unroll
+        for (int q = 0; q < D / 64; ++q) {
+          const int c = l + 64 * q;
+          hv[c] = bet == 0.0f ? 0.0f : (c > k + 1 ? xa[q] : (c == k + 1 ? x0 - alpha : 0.0f));
+        }
+        if (l == 0) {
+          E.d[k] = dk;
+          E.e[k] = alpha;
+          E.beta[k] = bet;
+        }
+      }
+      __syncthreads();
+      const float bet = E.beta[k];
+      if (bet == 0.0f) continue;
+      const float* hv = Hv + k * D;
+      float pr = 0.0f;
+#pragma unroll
+      for (int i = 0; i < EPT; i += 4) {
+        const floatx4_t v = *reinterpret_cast<const floatx4_t*>(hv + cb + i);
+        pr = fmaf(sr[i], v[0], pr);
+        pr = fmaf(sr[i + 1], v[1], pr);
+        pr = fmaf(sr[i + 2], v[2], pr);
+        pr = fmaf(sr[i + 3], v[3], pr);
+      }
+      pr = bet * row_sum(pr);
+      const float vr = hv[r];
+      const float dv = wave_sum(lead ? vr * pr : 0.0f);
+      if (l == 0) E.red[par * 4 + w] = dv;
+      if (lead) E.pb[par * D + r] = pr;
+      __syncthreads();
+      const float K = 0.5f * bet * ((E.red[par * 4] + E.red[par * 4 + 1]) +
+                                    (E.red[par * 4 + 2] + E.red[par * 4 + 3]));
+      const float wr = fmaf(-K, vr, pr);
+      const float* pp = E.pb + par * D + cb;
+#pragma unroll
+      for (int i = 0; i < EPT; i += 4) {
+        const floatx4_t v = *reinterpret_cast<const floatx4_t*>(hv + cb + i);
+        const floatx4_t pv = *reinterpret_cast<const floatx4_t*>(pp + i);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float wc = fmaf(-K, v[u], pv[u]);
+          sr[i + u] -= fmaf(vr, wc, wr * v[u]);
+        }
+      }
+    }
+    if (r >= D - 2) {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const int c = cb + i;
+        if (c == r) E.d[r] = sr[i];
+        if (r == D - 1 && c == D - 2) E.e[D - 2] = sr[i];
+      }
+    }
+    if (tid == 0) {
+      E.e[D - 1] = 0.0f;
+      E.beta[D - 2] = 0.0f;
+      E.beta[D - 1] = 0.0f;
+    }
+    __syncthreads();
+    if (tid < D) E.e2[tid] = E.e[tid] * E.e[tid];
+    __syncthreads();
   }
-  *p = min(a, b);
-  *q = max(a, b);
+
+  // --- Gershgorin interval and the scale of T --------------------------------
+  float glo = INFINITY, ghi = -INFINITY, emax2 = 0.0f;
+  for (int i = 0; i < D; ++i) {
+    const float rad = (i > 0 ? fabsf(E.e[i - 1]) : 0.0f) + fabsf(E.e[i]);
+    glo = fminf(glo, E.d[i] - rad);
+    ghi = fmaxf(ghi, E.d[i] + rad);
+    emax2 = fmaxf(emax2, E.e2[i]);
+  }
+  const float tnorm = fmaxf(fmaxf(fabsf(glo), fabsf(ghi)), 1e-30f);
+  const float pivmin = 1.17549435e-38f * fmaxf(1.0f, emax2);
+
+  // --- multisection: PPE lanes per eigenvalue -------------------------------
+  {
+    constexpr int PPE = 256 / D, LPE = 64 / PPE;
+    const int j = w * LPE + l % LPE, m = l / LPE;
+    float a = glo - 0x1p-20f * tnorm - pivmin, b = ghi + 0x1p-20f * tnorm + pivmin;
+    const float tol = 0x1p-22f * tnorm;
+    for (int it = 0; it < 48; ++it) {
+      if (!(b - a > tol)) break;
+      const float step = (b - a) * (1.0f / (float)(PPE + 1));
+      const float x = fmaf((float)(m + 1), step, a);
+      int cnt = 0;
+      float q = E.d[0] - x;
+      if (fabsf(q) < pivmin) q = -pivmin;
+      cnt += q < 0.0f;
+#pragma unroll 4
+      for (int i = 1; i < D; ++i) {
+        q = (E.d[i] - x) - E.e2[i - 1] * rcpf(q);
+        if (fabsf(q) < pivmin) q = -pivmin;
+        cnt += q < 0.0f;
+      }
+      float na = a, nb = b;
+#pragma unroll
+      for (int mm = 0; mm < PPE; ++mm) {
+        const int cm = __shfl(cnt, (l % LPE) + mm * LPE);
+        const float xm = fmaf((float)(mm + 1), step, a);
+        if (cm > j) nb = fminf(nb, xm); else na = fmaxf(na, xm);
+      }
+      if (na == a && nb == b) break;
+      a = na;
+      b = nb;
+    }
+    if (m == 0) lam[j] = 0.5f * (a + b);
+  }
+  __syncthreads();
+
+  // --- inverse iteration: lane j < D, L in registers, x in LDS ---------------
+  if (tid < D) {
+    const int j = tid;
+    const float mu = lam[j];
+    const float piv = 0x1p-23f * tnorm;
+    float* Zw = E.Zw;
+    float Lr[D - 1];
+    for (int i = 0; i < D; ++i) Zw[i * D + j] = ii_start(i, j);
+#pragma unroll 1
+    for (int it = 0; it < 3; ++it) {
+      float dp = E.d[0] - mu;
+      if (fabsf(dp) < piv) dp = piv;
+      float rdp = rcpf(dp);
+      float y = Zw[j];
+      Zw[j] = y * rdp;
+#pragma unroll
+      for (int i = 0; i < D - 1; ++i) {
+        const float li = E.e[i] * rdp;
+        Lr[i] = li;
+        dp = (E.d[i + 1] - mu) - li * E.e[i];
+        if (fabsf(dp) < piv) dp = piv;
+        rdp = rcpf(dp);
+        const float bi = Zw[(i + 1) * D + j];
+        y = fmaf(-li, y, bi);
+        Zw[(i + 1) * D + j] = y * rdp;
+      }
+      float x = Zw[(D - 1) * D + j];
+      float n2 = x * x;
+#pragma unroll
+      for (int i = D - 2; i >= 0; --i) {
+        x = fmaf(-Lr[i], x, Zw[i * D + j]);
+        Zw[i * D + j] = x;
+        n2 = fmaf(x, x, n2);
+      }
+      const float inv = 1.0f / sqrtf(n2);
+      for (int i = 0; i < D; ++i) Zw[i * D + j] *= inv;
+    }
+  }
+  __syncthreads();
+
+  // --- MGS and back-transform, one vector over PARTS lanes -------------------
+  constexpr int PARTS = 256 / D, LPG = 64 / PARTS, CH = D / PARTS;
+  const int j = w * LPG + (l % LPG), part = l / LPG, c0 = part * CH;
+  auto reduce_parts = [&](float v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s2 = LPG; s2 < 64; s2 <<= 1) v += __shfl_xor(v, s2);
+    return v;
+  };
+  float x[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) x[c] = E.Zw[(c0 + c) * D + j];
+  for (int pass = 0; pass < 2; ++pass)   // twice: near-degenerate vectors leave the first
+  for (int i = D - 1; i >= 0; --i) {     // pass only roughly orthogonal
+    float* buf = E.xb + (i & 1) * D + c0;
+    if (w == i / LPG) {
+      float n2 = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) n2 = fmaf(x[c], x[c], n2);
+      const float inv = 1.0f / sqrtf(reduce_parts(n2));
+      if (j == i) {
+#pragma unroll
+        for (int c = 0; c < CH; c += 4) {
+          floatx4_t v;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            x[c + u] *= inv;
+            v[u] = x[c + u];
+          }
+          *reinterpret_cast<floatx4_t*>(buf + c) = v;
+        }
+      }
+    }
+    __syncthreads();
+    if (j < i) {
+      floatx4_t bv[CH / 4];
+      float dot = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CH; c += 4) {
+        bv[c / 4] = *reinterpret_cast<const floatx4_t*>(buf + c);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dot = fmaf(x[c + u], bv[c / 4][u], dot);
+      }
+      dot = reduce_parts(dot);
+#pragma unroll
+      for (int c = 0; c < CH; c += 4)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[c + u] = fmaf(-dot, bv[c / 4][u], x[c + u]);
+    }
+  }
+  for (int k = D - 3; k >= 0; --k) {
+    const float bet = E.beta[k];
+    if (bet == 0.0f) continue;
+    const float* v = E.S + k * D + c0;
+    floatx4_t vv[CH / 4];
+    float dot = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; c += 4) {
+      vv[c / 4] = *reinterpret_cast<const floatx4_t*>(v + c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dot = fmaf(vv[c / 4][u], x[c + u], dot);
+    }
+    dot = bet * reduce_parts(dot);
+#pragma unroll
+    for (int c = 0; c < CH; c += 4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[c + u] = fmaf(-dot, vv[c / 4][u], x[c + u]);
+  }
+  // sign: the largest-magnitude entry (the first on ties) positive
+  float best = -1.0f, sv = 1.0f;
+  int bi = 0;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+    if (fabsf(x[c]) > best) { best = fabsf(x[c]); bi = c0 + c; sv = x[c]; }
+#pragma unroll
+  for (int s2 = LPG; s2 < 64; s2 <<= 1) {
+    const float ob = __shfl_xor(best, s2);
+    const int oi = __shfl_xor(bi, s2);
+    const float os = __shfl_xor(sv, s2);
+    if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; sv = os; }
+  }
+  const float sg = sv < 0.0f ? -1.0f : 1.0f;
+#pragma unroll
+  for (int c = 0; c < CH; c += 4) {
+    floatx4_t v;
+    v[0] = sg * x[c]; v[1] = sg * x[c + 1]; v[2] = sg * x[c + 2]; v[3] = sg * x[c + 3];
+    *reinterpret_cast<floatx4_t*>(Xv + (int64_t)j * D + c0 + c) = v;
+  }
+  __threadfence_block();
+  __syncthreads();
+}
+
+// C = op(A) B on 256 threads, each a (D/16) x (D/16) block of C; op(A)(i, k)
+// is A[k lda + i] when TA, else A[i lda + k]. Output row i goes to row
+// (REV ? D - 1 - i : i) of C.
+template <int D, bool TA, bool REV>
+CA_DEV void matmul(const float* A, int lda, const float* B, int ldb, float* C, int ldc) {
+  constexpr int TM = D / 16;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  float acc[TM][TM];
+#pragma unroll
+  for (int m = 0; m < TM; ++m)
+#pragma unroll
+    for (int n = 0; n < TM; ++n) acc[m][n] = 0.0f;
+  for (int k = 0; k < D; ++k) {
+    float a[TM], b[TM];
+#pragma unroll
+    for (int m = 0; m < TM; ++m) a[m] = TA ? A[k * lda + ty + 16 * m] : A[(ty + 16 * m) * lda + k];
+#pragma unroll
+    for (int n = 0; n < TM; ++n) b[n] = B[k * ldb + tx + 16 * n];
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+      for (int n = 0; n < TM; ++n) acc[m][n] = fmaf(a[m], b[n], acc[m][n]);
+  }
+#pragma unroll
+  for (int m = 0; m < TM; ++m) {
+    const int i = ty + 16 * m;
+    const int orow = REV ? D - 1 - i : i;
+#pragma unroll
+    for (int n = 0; n < TM; ++n) C[(int64_t)orow * ldc + tx + 16 * n] = acc[m][n];
+  }
+}
+
+// dst[i][k] (pitch D + 1, LDS) = scale_i src[i][k] (pitch D)
+template <int D>
+CA_DEV void load_mat(float* dst, const float* src, const float* scale) {
+  constexpr int P = D + 1;
+  for (int e = threadIdx.x; e < D * D; e += 256) {
+    const int i = e / D, k = e % D;
+    dst[i * P + k] = scale ? scale[i] * src[e] : src[e];
+  }
+}
+
+CA_DEV void block_sync_global() {
+  __threadfence_block();
+  __syncthreads();
 }
 
 template <int D>
-CA_DEV void jacobi(const JacobiLds<D>& J) {
-  constexpr int P = JacobiLds<D>::P, H = D / 2;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < D * D; e += 256) J.V[(e / D) * P + e % D] = (e / D == e % D) ? 1.0f : 0.0f;
-  if (tid == 0) {
-    float tr = 0.0f;
-    for (int i = 0; i < D; ++i) tr += fabsf(J.S[i * P + i]);
-    J.flag[1] = __float_as_int(tr * 0x1p-26f);
-  }
-  __syncthreads();
-  const float tol_abs = __int_as_float(J.flag[1]);
-  for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-    if (tid == 0) *J.flag = 0;
-    __syncthreads();
-    for (int rd = 0; rd < D - 1; ++rd) {
-      if (tid < H) {
-        int p, q;
-        jacobi_pair(D, rd, tid, &p, &q);
-        const float app = J.S[p * P + p], aqq = J.S[q * P + q], apq = J.S[p * P + q];
-        float c = 1.0f, sn = 0.0f;
-        if (fabsf(apq) > fmaxf(1e-7f * sqrtf(fabsf(app) * fabsf(aqq)), tol_abs) && apq != 0.0f) {
-          const float th = (aqq - app) / (2.0f * apq);
-          const float t = (th >= 0.0f ? 1.0f : -1.0f) / (fabsf(th) + sqrtf(th * th + 1.0f));
-          c = 1.0f / sqrtf(t * t + 1.0f);
-          sn = t * c;
-          *J.flag = 1;
-        }
-        J.cs[2 * tid] = c;
-        J.cs[2 * tid + 1] = sn;
-        J.pq[2 * tid] = p;
-        J.pq[2 * tid + 1] = q;
-      }
-      __syncthreads();
-      // rows: S <- J^T S
-      for (int e = tid; e < H * D; e += 256) {
-        const int i = e / D, k = e % D;
-        const float c = J.cs[2 * i], sn = J.cs[2 * i + 1];
-        if (sn == 0.0f) continue;
-        const int p = J.pq[2 * i], q = J.pq[2 * i + 1];
-        const float sp = J.S[p * P + k], sq = J.S[q * P + k];
-        J.S[p * P + k] = c * sp - sn * sq;
-        J.S[q * P + k] = sn * sp + c * sq;
-      }
-      __syncthreads();
-      // columns: S <- S J, V <- V J; the rotated pair's off-diagonal is zero
-      for (int e = tid; e < H * D; e += 256) {
-        const int i = e / D, k = e % D;
-        const float c = J.cs[2 * i], sn = J.cs[2 * i + 1];
-        if (sn == 0.0f) continue;
-        const int p = J.pq[2 * i], q = J.pq[2 * i + 1];
-        const float sp = J.S[k * P + p], sq = J.S[k * P + q];
-        float np = c * sp - sn * sq, nq = sn * sp + c * sq;
-        if (k == q) np = 0.0f;
-        if (k == p) nq = 0.0f;
-        J.S[k * P + p] = np;
-        J.S[k * P + q] = nq;
-        const float vp = J.V[k * P + p], vq = J.V[k * P + q];
-        J.V[k * P + p] = c * vp - sn * vq;
-        J.V[k * P + q] = sn * vp + c * vq;
-      }
-      __syncthreads();
-    }
-    const int done = *J.flag == 0;
-    __syncthreads();
-    if (done) break;
-  }
-}
+struct BasisLds {
+  static constexpr int P = D + 1;
+  static constexpr int R1 = D * P;
+  static constexpr int R2 = D * P;
+  static constexpr int SMALL = 12 * D + 8;
+  static constexpr size_t bytes = (size_t)(R1 + R2 + SMALL) * 4;
+};
 
 // One workgroup per tree (2 bh + tensor; tensor 0 = queries, 1 = keys).
 // Geometry M: M_k for queries, M_q for keys (identity without the transform);
 // covariance C_x of the representation: C_q (queries), M_k (keys).
+//   R = V diag(sqrt(max(lam, 0))) V^T from eig(M);  Z = R C_x R;  eig(Z) -> W;
+//   row D-1-j of the output is R w_j (w_j the eigenvector of the (j+1)-th
+//   smallest eigenvalue of Z), i.e. the rows descend by eigenvalue.
 template <int D>
 __global__ __launch_bounds__(256) void basis_kernel(const float* __restrict__ Mq,
                                                     const float* __restrict__ Mk,
@@ -287,97 +576,66 @@ __global__ __launch_bounds__(256) void basis_kernel(const float* __restrict__ Mq
                                                     float* __restrict__ Rbuf,
                                                     float* __restrict__ Zbuf,
                                                     float* __restrict__ At) {
-  constexpr int P = D + 1;
+  using L = BasisLds<D>;
+  constexpr int P = L::P;
   extern __shared__ __attribute__((aligned(16))) float bsm[];
-  JacobiLds<D> J;
-  J.S = bsm;
-  J.V = bsm + D * P;
-  J.cs = bsm + 2 * D * P;
-  float* lam = J.cs + D;                     // [D]
-  float* sgn = lam + D;                      // [D]
-  int* rank = reinterpret_cast<int*>(sgn + D);
-  J.pq = rank + D;
-  J.flag = J.pq + D;
+  float* r1 = bsm;
+  float* r2 = bsm + L::R1;
+  float* sm = r2 + L::R2;
+  EigLds<D> E;
+  E.S = r1;
+  E.Zw = r2;
+  E.d = sm;
+  E.e = sm + D;
+  E.e2 = sm + 2 * D;
+  E.beta = sm + 3 * D;
+  E.pb = sm + 4 * D;            // [2 D]
+  E.xb = sm + 6 * D;            // [2 D]
+  float* lam = sm + 8 * D;
+  float* scl = sm + 9 * D;
+  E.red = sm + 10 * D;          // [8]
   const int tree = blockIdx.x, bh = tree >> 1, tensor = tree & 1;
   const int tid = threadIdx.x;
   const float* Cx = (tensor == 0 ? Cq : Mk) + (int64_t)bh * D * D;
   float* R = Rbuf + (int64_t)tree * D * D;
-  float* Z = Zbuf + (int64_t)tree * D * D;
+  float* Z = Zbuf + (int64_t)tree * D * D;   // scratch: eigenvectors, T, Z, W
+  float* out = At + (int64_t)tree * D * D;
 
-  // R: symmetric root of the geometry
   if (transform) {
     const float* M = (tensor == 0 ? Mk : Mq) + (int64_t)bh * D * D;
-    for (int e = tid; e < D * D; e += 256) J.S[(e / D) * P + e % D] = M[e];
+    load_mat<D>(r1, M, nullptr);
     __syncthreads();
-    jacobi<D>(J);
-    if (tid < D) lam[tid] = sqrtf(fmaxf(J.S[tid * P + tid], 0.0f));
+    eig_sym<D>(E, lam, Z);
+    if (tid < D) scl[tid] = sqrtf(fmaxf(lam[tid], 0.0f));
     __syncthreads();
-    for (int e = tid; e < D * D; e += 256) {
-      const int k = e / D, l = e % D;
-      float acc = 0.0f;
-      for (int i = 0; i < D; ++i) acc = fmaf(J.V[k * P + i] * lam[i], J.V[l * P + i], acc);
-      J.S[k * P + l] = acc;   // S is free after the eigenvalues were read
-    }
+    load_mat<D>(r1, Z, nullptr);
+    load_mat<D>(r2, Z, scl);
     __syncthreads();
-    for (int e = tid; e < D * D; e += 256) R[e] = J.S[(e / D) * P + e % D];
-    // T = C_x R into V, then Z = R T to global memory
-    for (int e = tid; e < D * D; e += 256) {
-      const int k = e / D, l = e % D;
-      float acc = 0.0f;
-      for (int i = 0; i < D; ++i) acc = fmaf(Cx[(int64_t)k * D + i], J.S[i * P + l], acc);
-      J.V[k * P + l] = acc;
-    }
+    matmul<D, true, false>(r1, P, r2, P, R, D);   // R = V^T diag(scl) V (rows of V: vectors)
+    block_sync_global();
+    load_mat<D>(r1, Cx, nullptr);
+    load_mat<D>(r2, R, nullptr);
     __syncthreads();
-    for (int e = tid; e < D * D; e += 256) {
-      const int k = e / D, l = e % D;
-      float acc = 0.0f;
-      for (int i = 0; i < D; ++i) acc = fmaf(J.S[k * P + i], J.V[i * P + l], acc);
-      Z[e] = acc;
-    }
-    __threadfence_block();
+    matmul<D, false, false>(r1, P, r2, P, Z, D);  // T = C_x R
+    block_sync_global();
+    load_mat<D>(r1, Z, nullptr);
     __syncthreads();
-    for (int e = tid; e < D * D; e += 256) J.S[(e / D) * P + e % D] = Z[e];
+    matmul<D, false, false>(r2, P, r1, P, Z, D);  // Z = R T
+    block_sync_global();
+    load_mat<D>(r1, Z, nullptr);
   } else {
-    for (int e = tid; e < D * D; e += 256) {
-      R[e] = (e / D == e % D) ? 1.0f : 0.0f;
-      J.S[(e / D) * P + e % D] = Cx[e];
-    }
-  }
-  __threadfence_block();
-  __syncthreads();
-  // W, lam of Z = R C_x R
-  jacobi<D>(J);
-  if (tid < D) lam[tid] = J.S[tid * P + tid];
-  __syncthreads();
-  if (tid < D) {
-    // descending eigenvalue order (ties to the lower index) and the sign that
-    // makes the column's largest-magnitude entry (the first on ties) positive
-    const float li = lam[tid];
-    int rk = 0;
-    for (int j = 0; j < D; ++j) rk += (lam[j] > li) || (lam[j] == li && j < tid);
-    rank[tid] = rk;
-    int kb = 0;
-    float best = -1.0f;
-    for (int k = 0; k < D; ++k) {
-      const float v = fabsf(J.V[k * P + tid]);
-      if (v > best) { best = v; kb = k; }
-    }
-    sgn[tid] = J.V[kb * P + tid] < 0.0f ? -1.0f : 1.0f;
+    load_mat<D>(r1, Cx, nullptr);
   }
   __syncthreads();
-  // A = R W: row rank[i] of A^T is sign_i (R w_i)
-  float* out = At + (int64_t)tree * D * D;
-  for (int e = tid; e < D * D; e += 256) {
-    const int i = e / D, k = e % D;   // eigenvector i, component k
-    float acc = 0.0f;
-    for (int l = 0; l < D; ++l) acc = fmaf(R[(int64_t)k * D + l], J.V[l * P + i], acc);
-    out[(int64_t)rank[i] * D + k] = sgn[i] * acc;
+  eig_sym<D>(E, lam, Z);   // W: row j = w_j
+  if (transform) {
+    load_mat<D>(r1, Z, nullptr);
+    load_mat<D>(r2, R, nullptr);
+    __syncthreads();
+    matmul<D, false, true>(r1, P, r2, P, out, D);   // row D-1-j = w_j^T R = (R w_j)^T
+  } else {
+    for (int e = tid; e < D * D; e += 256) out[(D - 1 - e / D) * D + e % D] = Z[e];
   }
-}
-
-template <int D>
-constexpr size_t basis_smem() {
-  return (size_t)(2 * D * (D + 1) + 3 * D + D) * 4 + (size_t)(D + D + 4) * 4;
 }
 
 template <int D>
@@ -393,7 +651,7 @@ void launch_basis_d(const void* Q, int dtype, int BH, int N, int transform, cons
     qmoment_partial_f32<D><<<gp, 256, 0, st>>>((const float*)Q, s, N, rows, nchunks, partial);
   dim3 gr((D * D + 255) / 256, BH);
   qmoment_reduce<D><<<gr, 256, 0, st>>>(partial, nchunks, N, Cq);
-  constexpr size_t sm = basis_smem<D>();
+  constexpr size_t sm = BasisLds<D>::bytes;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&basis_kernel<D>),
@@ -403,6 +661,123 @@ void launch_basis_d(const void* Q, int dtype, int BH, int N, int transform, cons
   basis_kernel<D><<<2 * BH, 256, sm, st>>>(Mq, Mk, Cq, transform, Rbuf, Zbuf, At);
 }
 
+// ----------------------------------------------------------------------------
+// Rotation of every vector into its tree's basis once (the diagonalized
+// splitting then only reads coordinates): Y[tree][t][j] = x_t . a_j, with
+// x = s q for queries and x = k for keys, fp32 [2 BH][N][D].
+// ----------------------------------------------------------------------------
+
+// Three-term bf16 split of At (hi + mid + lo carries 24 significant bits):
+// At3 [2 BH][3][D][D].
+template <int D>
+__global__ __launch_bounds__(256) void basis_split(const float* __restrict__ At, int trees,
+                                                   uint16_t* __restrict__ At3) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)trees * D * D) return;
+  const int64_t tree = e / (D * D), r = e % (D * D);
+  const float g = At[e];
+  const uint16_t hi = f32_to_bf16(g);
+  const float r1 = g - bf16_to_f32(hi);
+  const uint16_t mid = f32_to_bf16(r1);
+  const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+  uint16_t* o = At3 + tree * 3 * D * D + r;
+  o[0] = hi;
+  o[D * D] = mid;
+  o[2 * D * D] = lo;
+}
+
+constexpr int kRotTokens = 256;   // tokens per workgroup of the rotation
+
+// bf16 rows on MFMA: wave w owns coordinate block bn = w % (D/32) (its three
+// B-operand terms stay in registers) and token blocks of 32 in turn; the A
+// operand (the bf16 row, exact) is read straight from global memory.
+template <int D>
+__global__ __launch_bounds__(256) void rotate_bf16(const uint16_t* __restrict__ Q,
+                                                   const uint16_t* __restrict__ K,
+                                                   const float* __restrict__ s,
+                                                   const uint16_t* __restrict__ At3, int N,
+                                                   float* __restrict__ Y) {
+  constexpr int NB = D / 32, KS = D / 16, WPB = 4 / NB;   // waves per coordinate block
+  const int tree = blockIdx.y, bh = tree >> 1, tensor = tree & 1;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 31, h = l >> 5;
+  const int bn = w % NB, wg = w / NB;
+  const uint16_t* X = (tensor == 0 ? Q : K) + (int64_t)bh * N * D;
+  const float* sv = tensor == 0 ? s + (int64_t)bh * N : nullptr;
+  float* Yt = Y + (int64_t)tree * N * D;
+  bf16x8_t b[3][KS];
+  const uint16_t* B3 = At3 + (int64_t)tree * 3 * D * D + (int64_t)(32 * bn + r) * D + 8 * h;
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      b[t][ks] = *reinterpret_cast<const bf16x8_t*>(B3 + (int64_t)t * D * D + 16 * ks);
+  const int tend = min(N, (blockIdx.x + 1) * kRotTokens);
+  for (int t0 = blockIdx.x * kRotTokens + 32 * wg; t0 < tend; t0 += 32 * WPB) {
+    const int tok = t0 + r;
+    u32x4_t av[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      av[ks] = tok < N ? *reinterpret_cast<const u32x4_t*>(X + (int64_t)tok * D + 16 * ks + 8 * h)
+                       : u32x4_t{0u, 0u, 0u, 0u};
+    floatx16_t acc = zero16();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) acc = mfma32(as_bf16x8(av[ks]), b[t][ks], acc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tt = t0 + c_row(i, h);
+      if (tt < N) Yt[(int64_t)tt * D + 32 * bn + r] = (sv ? sv[tt] : 1.0f) * acc[i];
+    }
+  }
+}
+
+// fp32 rows on the VALU: thread (j, g) holds a_j and sums rows g, g + G, ...
+// of a 32-token tile staged in LDS.
+template <int D>
+__global__ __launch_bounds__(256) void rotate_f32(const float* __restrict__ Q,
+                                                  const float* __restrict__ K,
+                                                  const float* __restrict__ s,
+                                                  const float* __restrict__ At, int N,
+                                                  float* __restrict__ Y) {
+  constexpr int G = 256 / D, TT = 32;
+  __shared__ float sx[TT][D + 1];
+  const int tree = blockIdx.y, bh = tree >> 1, tensor = tree & 1;
+  const int tid = threadIdx.x, j = tid % D, g = tid / D;
+  const float* X = (tensor == 0 ? Q : K) + (int64_t)bh * N * D;
+  const float* sv = tensor == 0 ? s + (int64_t)bh * N : nullptr;
+  float aj[D];
+#pragma unroll
+  for (int k = 0; k < D; ++k) aj[k] = At[((int64_t)tree * D + j) * D + k];
+  const int t0 = blockIdx.x * TT;
+  for (int e = tid; e < TT * D; e += 256) {
+    const int t = e / D, k = e % D;
+    sx[t][k] = t0 + t < N ? X[(int64_t)(t0 + t) * D + k] : 0.0f;
+  }
+  __syncthreads();
+  for (int t = g; t < TT; t += G) {
+    if (t0 + t >= N) break;
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < D; ++k) acc = fmaf(sx[t][k], aj[k], acc);
+    Y[((int64_t)tree * N + t0 + t) * D + j] = (sv ? sv[t0 + t] : 1.0f) * acc;
+  }
+}
+
+template <int D>
+void launch_rotate_d(const void* Q, const void* K, int dtype, int BH, int N, const float* s,
+                     const float* At, uint16_t* At3, float* Y, hipStream_t st) {
+  const int trees = 2 * BH;
+  if (dtype == 0) {
+    basis_split<D><<<(unsigned)(((int64_t)trees * D * D + 255) / 256), 256, 0, st>>>(At, trees, At3);
+    dim3 g((N + kRotTokens - 1) / kRotTokens, trees);
+    rotate_bf16<D><<<g, 256, 0, st>>>((const uint16_t*)Q, (const uint16_t*)K, s, At3, N, Y);
+  } else {
+    dim3 g((N + 31) / 32, trees);
+    rotate_f32<D><<<g, 256, 0, st>>>((const float*)Q, (const float*)K, s, At, N, Y);
+  }
+}
+
 }  // namespace
 
 void launch_basis(const void* Q, int dtype, int BH, int N, int D, int transform, const float* s,
@@ -410,6 +785,12 @@ void launch_basis(const void* Q, int dtype, int BH, int N, int D, int transform,
                   float* Zbuf, float* At, hipStream_t st) {
   if (D == 64) launch_basis_d<64>(Q, dtype, BH, N, transform, s, Mq, Mk, partial, Cq, Rbuf, Zbuf, At, st);
   else launch_basis_d<128>(Q, dtype, BH, N, transform, s, Mq, Mk, partial, Cq, Rbuf, Zbuf, At, st);
+}
+
+void launch_rotate(const void* Q, const void* K, int dtype, int BH, int N, int D, const float* s,
+                   const float* At, uint16_t* At3, float* Y, hipStream_t st) {
+  if (D == 64) launch_rotate_d<64>(Q, K, dtype, BH, N, s, At, At3, Y, st);
+  else launch_rotate_d<128>(Q, K, dtype, BH, N, s, At, At3, Y, st);
 }
 
 }  // namespace ca

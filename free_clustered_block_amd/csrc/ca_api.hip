@@ -48,9 +48,12 @@ struct ClusterWs {
   int32_t* stok;
   float* zbuf;
   float *Cq, *Rbuf, *Zbuf, *At;   // diagonalized splitting: basis of each tree
+  uint16_t* At3;                  // its three-term bf16 split
+  int32_t* jsel;                  // chosen coordinate per node
+  float* Y;                       // coordinates of every vector (diagonalized only)
 };
 
-ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c) {
+ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c, bool diag) {
   ClusterWs w;
   const size_t T = 2 * (size_t)BH;
   const int rows = metric_rows_per_chunk(N, BH);
@@ -79,6 +82,9 @@ ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c) {
   w.Rbuf = cv.take<float>(T * D * D);
   w.Zbuf = cv.take<float>(T * D * D);
   w.At = cv.take<float>(T * D * D);
+  w.At3 = cv.take<uint16_t>(T * 3 * D * D);
+  w.jsel = cv.take<int32_t>(T * slots);
+  w.Y = diag ? cv.take<float>(T * N * D) : nullptr;
   return w;
 }
 
@@ -151,8 +157,9 @@ size_t ca_workspace_size(ca_op op, int B, int H, int N, int D, int cluster_size,
   Carver cv(nullptr);
   switch (op) {
     case CA_OP_CLUSTER:
+    case CA_OP_CLUSTER_DIAG:
       if (cluster_size < 1 || N < cluster_size) return SIZE_MAX;
-      plan_cluster(cv, BH, N, D, cluster_size);
+      plan_cluster(cv, BH, N, D, cluster_size, op == CA_OP_CLUSTER_DIAG);
       return cv.size();
     case CA_OP_ROUTE: {
       // N = n_qc and cluster_size = n_kc for this op
@@ -201,7 +208,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   if ((2 * B * H) > 65535) return fail(CA_ERR_UNSUPPORTED, "2*B*H must be <= 65535");
   const int BH = B * H;
   Carver cv(ws);
-  ClusterWs w = plan_cluster(cv, BH, N, D, c);
+  ClusterWs w = plan_cluster(cv, BH, N, D, c, o.split_mode == 1);
   if (int e = check_ws(ws, ws_bytes, cv.size())) return e;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int L = tree_levels_host(N, c);
@@ -215,6 +222,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     if (o.trace_basis)
       CA_HIP_CHECK(hipMemcpyAsync(o.trace_basis, w.At, 2 * (size_t)BH * D * D * 4,
                                   hipMemcpyDeviceToDevice, st));
+    launch_rotate(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, w.s, w.At, w.At3, w.Y, st);
   }
   launch_perm_init(w.permA, 2 * BH, N, st);
   int32_t* cur = w.permA;
@@ -228,7 +236,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     a.Q = Q; a.K = K; a.dtype = dt == CA_BF16 ? 0 : 1;
     a.BH = BH; a.N = N; a.D = D; a.c = c; a.level = level;
     a.transform = o.transform; a.power_iters = o.power_iters; a.sample_factor = o.sample_factor;
-    a.split_mode = o.split_mode; a.basis = w.At;
+    a.split_mode = o.split_mode; a.basis = w.At; a.Y = w.Y; a.jsel = w.jsel;
     a.seed = o.seed;
     a.perm_in = cur; a.perm_out = nxt;
     a.hpos_in = hcur; a.hpos_out = hnxt; a.s = w.s; a.Mq = w.Mq; a.Mk = w.Mk; a.Mpk = w.Mpk;

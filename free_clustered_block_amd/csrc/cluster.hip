@@ -367,39 +367,26 @@ __global__ __launch_bounds__(256) void pddp_dir(LevelArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Direction of each node for diagonalized splitting (v1 §3.2.1 "Diagonalized
-// recursive splitting"; later revision §4.1.1): the coordinate y_j = x . a_j
-// of the tree's principal-component basis with the highest variance over the
-// node's sample, the lowest index on ties; the direction is a_j itself, so the
-// projection kernel then computes exactly coordinate j. Thread (j, g) holds
-// a_j in registers and sums y and y^2 (fp64) over rows g, g + G, ... of the
-// sample; the same sample and LDS row staging as pddp_dir.
+// Diagonalized splitting (v1 §3.2.1 "Diagonalized recursive splitting"; later
+// revision §4.1.1). Every vector was rotated once into its tree's
+// principal-component basis (Y = coordinates x . a_j). A node splits along
+// the coordinate of highest population variance over its sample (the lowest
+// index on ties): thread (j, g) sums y_j and y_j^2 (fp64) over sample rows g,
+// g + G, ...; the projection is then the coordinate itself.
 // ----------------------------------------------------------------------------
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void pddp_dir_diag(LevelArgs a) {
-  using Cfg = DirCfg<D, T>;
-  constexpr int G = Cfg::G, PITCH = Cfg::PITCH, CAP = Cfg::CAP;
-  constexpr int EPV = 16 / (int)sizeof(T);   // elements per 16-byte vector
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* srow = reinterpret_cast<T*>(smem);
-  float* ss = reinterpret_cast<float*>(smem + Cfg::row_bytes);
-  double* sp1 = reinterpret_cast<double*>(ss + CAP + (CAP & 1));   // [G][D]
-  double* sp2 = sp1 + G * D;                                        // [G][D]
-  int* sred = reinterpret_cast<int*>(sp2 + G * D);                  // [16]
-  int* spre = sred + 16;                                            // [nch + 1]
-
+template <int D>
+__global__ __launch_bounds__(256) void pddp_dir_y(LevelArgs a) {
+  constexpr int G = 256 / D;
+  __shared__ double sp1[G * D], sp2[G * D];
+  __shared__ int sred[16];
+  extern __shared__ int spre[];   // [nch + 1]
   const int tree = blockIdx.y, slot = blockIdx.x;
-  const int bh = tree >> 1, tensor = tree & 1;
   int off, n;
   if (!node_at(a.N, a.c, a.level, slot, &off, &n) || n <= a.c) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const T* X = reinterpret_cast<const T*>(tensor == 0 ? a.Q : a.K) + (int64_t)bh * a.N * D;
-  const float* svec = tensor == 0 ? a.s + (int64_t)bh * a.N : nullptr;
   const int32_t* perm = a.perm_in + (int64_t)tree * a.N + off;
   int32_t* stok = a.zbuf_tok + (int64_t)tree * a.N + off;
-
-  // --- the node's sample (prefix over its chunk counts), rows into LDS ------
   const int ch0 = off / a.c;
   const int nch = (n + a.c - 1) / a.c;
   const int32_t* cnt = a.chunk_cnt + (int64_t)tree * a.nchunks + ch0;
@@ -428,7 +415,6 @@ __global__ __launch_bounds__(256) void pddp_dir_diag(LevelArgs a) {
   int m = spre[nch];
   const bool whole = m < 2;     // fewer than two sampled rows: the whole node
   if (whole) m = n;
-  __syncthreads();
   const int32_t* lists = a.sample_buf + (int64_t)tree * a.N;
   for (int r = tid; r < m; r += 256) {
     int tok;
@@ -443,62 +429,24 @@ __global__ __launch_bounds__(256) void pddp_dir_diag(LevelArgs a) {
       tok = lists[(int64_t)(ch0 + lo) * a.c + (r - spre[lo])];
     }
     stok[r] = tok;
-    if (r < CAP) {
-      constexpr int NG = D * (int)sizeof(T) / 16;
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(X + (int64_t)tok * D);
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(srow + r * PITCH);
-      u32x4_t v[NG];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) v[g] = src[g];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) dst[g] = v[g];
-      ss[r] = svec ? svec[tok] : 1.0f;
-    }
-  }
-  // basis vector a_j of this thread's coordinate
-  const int jc = tid % D, gc = tid / D;
-  float aj[D];
-  {
-    const floatx4_t* ab = reinterpret_cast<const floatx4_t*>(a.basis + ((int64_t)tree * D + jc) * D);
-#pragma unroll
-    for (int g = 0; g < D / 4; ++g) {
-      const floatx4_t v = ab[g];
-      aj[4 * g] = v[0]; aj[4 * g + 1] = v[1]; aj[4 * g + 2] = v[2]; aj[4 * g + 3] = v[3];
-    }
   }
   __syncthreads();
-
-  // --- sums of y_rj = s_r (x_r . a_j) and of its square over the sample -----
-  auto dot_row = [&](const T* row) __attribute__((always_inline)) -> float {
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int g = 0; g < D / EPV; ++g) {
-      const u32x4_t v = reinterpret_cast<const u32x4_t*>(row)[g];
-      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[q] = fmaf(bf16_to_f32((uint16_t)(wd[q] & 0xFFFFu)), aj[g * 8 + 2 * q], acc[q]);
-          acc[q] = fmaf(bf16_to_f32((uint16_t)(wd[q] >> 16)), aj[g * 8 + 2 * q + 1], acc[q]);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = fmaf(__uint_as_float(wd[q]), aj[g * 4 + q], acc[q]);
-      }
-    }
-    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  };
-  const int mc = m < CAP ? m : CAP;
+  const int jc = tid % D, gc = tid / D;
+  const float* Yt = a.Y + (int64_t)tree * a.N * D + jc;
   double s1 = 0.0, s2 = 0.0;
   int r = gc;
-  for (; r < mc; r += G) {
-    const float y = ss[r] * dot_row(srow + r * PITCH);
-    s1 += (double)y;
-    s2 = fma((double)y, (double)y, s2);
+  for (; r + 3 * G < m; r += 4 * G) {
+    float y[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) y[u] = Yt[(int64_t)stok[r + u * G] * D];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s1 += (double)y[u];
+      s2 = fma((double)y[u], (double)y[u], s2);
+    }
   }
   for (; r < m; r += G) {
-    const int tok = stok[r];
-    const float y = (svec ? svec[tok] : 1.0f) * dot_row(X + (int64_t)tok * D);
+    const float y = Yt[(int64_t)stok[r] * D];
     s1 += (double)y;
     s2 = fma((double)y, (double)y, s2);
   }
@@ -519,6 +467,7 @@ __global__ __launch_bounds__(256) void pddp_dir_diag(LevelArgs a) {
     for (int j = 1; j < D; ++j)
       if (sp1[j] > best) { best = sp1[j]; jb = j; }
     sred[0] = jb;
+    a.jsel[(int64_t)tree * (1 << a.level) + slot] = jb;
   }
   __syncthreads();
   const int jb = sred[0];
@@ -530,13 +479,20 @@ __global__ __launch_bounds__(256) void pddp_dir_diag(LevelArgs a) {
   }
 }
 
-template <typename T, int D>
-size_t dir_diag_smem(int N, int c, int level) {
-  using Cfg = DirCfg<D, T>;
-  const int64_t nmax = ((int64_t)N >> level) + 2 * (int64_t)c;
-  const int64_t nch = (nmax + c - 1) / c;
-  return Cfg::row_bytes + (size_t)(Cfg::CAP + 1) * 4 + (size_t)2 * Cfg::G * D * 8 + 16 * 4 +
-         (size_t)(nch + 2) * 4 + 16;
+// Projection of diagonalized splitting: the chosen coordinate of each member.
+__global__ __launch_bounds__(256) void pddp_project_y(LevelArgs a) {
+  const int tree = blockIdx.y;
+  const int p0 = blockIdx.x * a.c;
+  int off, n, idx;
+  const int depth = node_of(a.N, a.c, a.level, p0, &off, &n, &idx);
+  if (depth < a.level || n <= a.c) return;   // inside a leaf
+  const int j = a.jsel[(int64_t)tree * (1 << a.level) + idx];
+  const int p = p0 + (int)threadIdx.x;
+  if (p >= min(a.N, p0 + a.c)) return;
+  const int tok = a.perm_in[(int64_t)tree * a.N + p];
+  const float score = a.Y[((int64_t)tree * a.N + tok) * a.D + j];
+  a.keys[(int64_t)tree * a.N + p] = order_key(score);
+  if (a.trace_score) a.trace_score[(int64_t)tree * a.N + p] = score;
 }
 
 // LDS of pddp_dir at a level: fixed part + chunk prefix sums of the largest node
@@ -1337,14 +1293,9 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
   dim3 gspan((a.N + kSampleSpan - 1) / kSampleSpan, trees);
   pddp_sample<<<gspan, 256, 0, st>>>(a);
   if (a.split_mode == 1) {
-    const size_t lds = dir_diag_smem<T, D>(a.N, a.c, a.level);
-    static size_t lds_allowed = 0;   // raise the dynamic-LDS limit when a level needs more
-    if (lds > lds_allowed) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&pddp_dir_diag<T, D>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      lds_allowed = lds;
-    }
-    pddp_dir_diag<T, D><<<gslots, 256, lds, st>>>(a);
+    const int64_t nmax = ((int64_t)a.N >> a.level) + 2 * (int64_t)a.c;   // bounds every node
+    const size_t lds = (size_t)((nmax + a.c - 1) / a.c + 2) * 4;
+    pddp_dir_y<D><<<gslots, 256, lds, st>>>(a);
   } else if constexpr (sizeof(T) == 2) {
     const int64_t nmax = ((int64_t)a.N >> a.level) + 2 * (int64_t)a.c;   // bounds every node
     const size_t lds = (size_t)((nmax + a.c - 1) / a.c + 2) * 4;
@@ -1360,7 +1311,8 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
     pddp_dir<T, D><<<gslots, 256, lds, st>>>(a);
   }
   dim3 gproj((a.N + a.c - 1) / a.c, trees);
-  pddp_project<T, D><<<gproj, 256, 0, st>>>(a);
+  if (a.split_mode == 1) pddp_project_y<<<gproj, 256, 0, st>>>(a);
+  else pddp_project<T, D><<<gproj, 256, 0, st>>>(a);
   if (max_split_node(a.N, a.c, a.level) <= kSmallNode) {
     dim3 gsmall(((1u << a.level) + 3) / 4, trees);
     pddp_split_small<<<gsmall, 256, 0, st>>>(a);

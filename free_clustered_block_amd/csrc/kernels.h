@@ -31,6 +31,8 @@ struct LevelArgs {
   const float* Mpk;         // [2 BH][D D]: metric of each tree (M_k for queries, M_q for
                             // keys) packed in the per-lane order of the direction kernel
   const float* basis;       // [2 BH][D][D]: row j = basis direction a_j (diagonalized)
+  const float* Y;           // [2 BH][N][D]: coordinates x . a_j of every token (diagonalized)
+  int32_t* jsel;            // [2 BH][slots]: chosen coordinate of each node (diagonalized)
   const float* dir_prev;    // [2 BH][slots/2][D]
   float* dir_cur;           // [2 BH][slots][D]
   int nchunks;              // ceil(N / c)
@@ -52,6 +54,10 @@ void launch_level(const LevelArgs& a, hipStream_t st);
 void launch_basis(const void* Q, int dtype, int BH, int N, int D, int transform, const float* s,
                   const float* Mq, const float* Mk, float* partial, float* Cq, float* Rbuf,
                   float* Zbuf, float* At, hipStream_t st);
+// Y [2 BH][N][D] = coordinates of every query (s q) and key in its tree's
+// basis At; At3 [2 BH][3][D][D] bf16 scratch (bf16 inputs).
+void launch_rotate(const void* Q, const void* K, int dtype, int BH, int N, int D, const float* s,
+                   const float* At, uint16_t* At3, float* Y, hipStream_t st);
 void launch_perm_init(int32_t* perm, int trees, int N, hipStream_t st);
 void launch_perm_out(const int32_t* perm, int BH, int N, int32_t* perm_q, int32_t* perm_k,
                      hipStream_t st);

@@ -60,7 +60,8 @@ typedef enum {
   CA_OP_CLUSTER = 0,
   CA_OP_ROUTE = 1,
   CA_OP_ATTEND = 2,
-  CA_OP_DENSE = 3
+  CA_OP_DENSE = 3,
+  CA_OP_CLUSTER_DIAG = 4   /* ca_cluster with split_mode 1 (diagonalized)    */
 } ca_op;
 
 /*
@@ -131,7 +132,9 @@ int ca_tree_levels(int N, int cluster_size);
 /* Bytes of workspace `op` needs for the given sizes (0 if none, SIZE_MAX if
  * the arguments are invalid). For CA_OP_ROUTE pass N = n_qc and
  * cluster_size = n_kc (the bytes are only needed when `scores` is NULL);
- * CA_OP_DENSE ignores cluster_size and topk. Host only. */
+ * CA_OP_DENSE ignores cluster_size and topk. CA_OP_CLUSTER_DIAG is the
+ * workspace of ca_cluster with split_mode 1: it adds the coordinates of every
+ * query and key in its tree's basis (2 B H N D floats). Host only. */
 size_t ca_workspace_size(ca_op op, int B, int H, int N, int D, int cluster_size, int topk);
 
 /*

@@ -49,6 +49,10 @@ def test_workspace_sizes(lib):
         n = ca.workspace_size(op, 1, 8, 65536, 64, 128, 64)
         assert 0 < n < 2**40 and n % 256 == 0
     assert ca.workspace_size(ca.OP_ROUTE, 1, 8, 512, 64, 512, 64) == 8 * 512 * 512 * 4
+    # the diagonalized split adds the coordinates of every vector: 2 B H N D floats
+    extra = (ca.workspace_size(ca.OP_CLUSTER_DIAG, 1, 8, 65536, 64, 128, 64)
+             - ca.workspace_size(ca.OP_CLUSTER, 1, 8, 65536, 64, 128, 64))
+    assert 2 * 8 * 65536 * 64 * 4 <= extra < 2 * 8 * 65536 * 64 * 4 + 512
     assert ca.workspace_size(ca.OP_CLUSTER, 1, 1, 10, 64, 64, 1) == SIZE_MAX
     assert ca.workspace_size(ca.OP_ATTEND, 0, 1, 1024, 64, 64, 1) == SIZE_MAX
 

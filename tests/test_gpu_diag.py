@@ -205,3 +205,32 @@ def test_diag_deterministic_and_no_trace_equal(ca):
     b = _gpu(ca, name, trace=False)
     assert np.array_equal(_np(a.perm_q), _np(b.perm_q))
     assert np.array_equal(_np(a.perm_k), _np(b.perm_k))
+
+
+def test_basis_rank_deficient(ca):
+    """Queries and keys confined to a 24-dimensional subspace of D = 64: the
+    geometries are singular, the zero eigenvalues degenerate; the basis still
+    satisfies A A^T = R^2 and diagonalises the covariance."""
+    import torch
+    rng = np.random.default_rng(1234)
+    N, D, r = 1500, 64, 24
+    basis = rng.standard_normal((r, D))
+    Q = (rng.standard_normal((1, 1, N, r)) @ basis).astype(np.float32)
+    K = (rng.standard_normal((1, 1, N, r)) * np.linspace(2.0, 0.5, r) @ basis).astype(np.float32)
+    res = ca.cluster(torch.from_numpy(Q).cuda(), torch.from_numpy(K).cuda(), 64,
+                     split_mode="diag", trace=True)
+    tb = _np(res.trace_basis).reshape(2, D, D).astype(np.float64)
+    opts = o.ClusterOpts(split_mode="diag")
+    Xq, Gq, Xk, Gk = o.head_representations(Q[0, 0], K[0, 0], opts)
+    for tree, X, G in ((0, Xq, Gq), (1, Xk, Gk)):
+        Ag = tb[tree].T
+        _, lam = o.pc_basis(X, G)
+        R = o.root_matrix(G)
+        RR = R @ R
+        assert np.linalg.norm(Ag @ Ag.T - RR) <= 1e-4 * np.linalg.norm(RR), tree
+        C = np.cov(X @ Ag, rowvar=False, bias=True)
+        off = C - np.diag(np.diag(C))
+        assert np.max(np.abs(off)) <= 1e-4 * lam[0], tree
+        assert np.max(np.abs(np.diag(C) - lam)) <= 1e-4 * lam[0], tree
+    perm = _np(res.perm_k)[0, 0]
+    assert np.array_equal(np.sort(perm), np.arange(N))
