@@ -1,19 +1,19 @@
 // Principal-component basis for diagonalized recursive splitting (paper v1
 // §3.2.1 "Diagonalized recursive splitting"; later revision §4.1.1): the
 // vectors of each tree are rotated once into the principal-component basis of
-// the whole set, taken in the transform's geometry (z = R x, R the root matrix
-// of the metric, v1 §3.2.2), and every node then splits along the coordinate
-// of highest sample variance.
+// the whole set, taken in the transform's geometry (the metric M of v1 §3.2.2:
+// z = F^T x for any factor F F^T = M), and every node then splits along the
+// coordinate of highest sample variance.
 //
 //   qmoment_partial / qmoment_reduce   C_q = Cov(s q) over all queries (the
 //       query representation x = s q of Eq. 16); the key covariance is M_k of
 //       the metric pass.
-//   basis_kernel   one workgroup per tree: eigendecomposition of the geometry
-//       M (-> symmetric root R, negative eigenvalues clamped), Z = R C_x R,
-//       eigendecomposition of Z (-> W, lam), columns ordered by descending
-//       eigenvalue and signed so that each column's largest-magnitude entry is
-//       positive; writes A^T with A = R W, so row j of the output is the
-//       direction whose projection x . a_j is coordinate j.
+//   basis_kernel   one workgroup per tree: pivoted Cholesky factor F of the
+//       geometry M, Z = F^T C_x F, eigendecomposition of Z (-> W, lam), a_j = F w_j by
+//       descending eigenvalue, each signed so that its largest-magnitude entry
+//       is positive; writes A^T, so row j of the output is the direction whose
+//       projection x . a_j is coordinate j.
+//   basis_split / rotate_*   Y = the coordinates of every vector, once.
 #include "kernels.h"
 #include "mfma.h"
 
@@ -188,8 +188,7 @@ __global__ __launch_bounds__(256) void qmoment_reduce(const float* __restrict__ 
 //                   2^-23 |T| raised to it), L in registers, x in LDS;
 //   MGS             two passes in descending eigenvalue order, each vector
 //                   normalised, then removed from every vector after it;
-//   back-transform  x <- H_0 ... H_{D-3} x; each vector is signed so that its
-//                   largest-magnitude entry (the first on ties) is positive.
+//   back-transform  x <- H_0 ... H_{D-3} x.
 //
 // Eigenvalues ascend in lam; row j of Xv (global, D x D) is the unit
 // eigenvector of lam[j].
@@ -483,34 +482,20 @@ CA_DEV void eig_sym(const EigLds<D>& E, float* lam, float* __restrict__ Xv) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) x[c + u] = fmaf(-dot, vv[c / 4][u], x[c + u]);
   }
-  // sign: the largest-magnitude entry (the first on ties) positive
-  float best = -1.0f, sv = 1.0f;
-  int bi = 0;
-#pragma unroll
-  for (int c = 0; c < CH; ++c)
-    if (fabsf(x[c]) > best) { best = fabsf(x[c]); bi = c0 + c; sv = x[c]; }
-#pragma unroll
-  for (int s2 = LPG; s2 < 64; s2 <<= 1) {
-    const float ob = __shfl_xor(best, s2);
-    const int oi = __shfl_xor(bi, s2);
-    const float os = __shfl_xor(sv, s2);
-    if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; sv = os; }
-  }
-  const float sg = sv < 0.0f ? -1.0f : 1.0f;
 #pragma unroll
   for (int c = 0; c < CH; c += 4) {
     floatx4_t v;
-    v[0] = sg * x[c]; v[1] = sg * x[c + 1]; v[2] = sg * x[c + 2]; v[3] = sg * x[c + 3];
+    v[0] = x[c]; v[1] = x[c + 1]; v[2] = x[c + 2]; v[3] = x[c + 3];
     *reinterpret_cast<floatx4_t*>(Xv + (int64_t)j * D + c0 + c) = v;
   }
   __threadfence_block();
   __syncthreads();
 }
 
-// C = op(A) B on 256 threads, each a (D/16) x (D/16) block of C; op(A)(i, k)
-// is A[k lda + i] when TA, else A[i lda + k]. Output row i goes to row
-// (REV ? D - 1 - i : i) of C.
-template <int D, bool TA, bool REV>
+// C = op(A) op(B) on 256 threads, each a (D/16) x (D/16) block of C;
+// op(A)(i, k) is A[k lda + i] when TA, else A[i lda + k]; op(B)(k, n) is
+// B[n ldb + k] when TB, else B[k ldb + n].
+template <int D, bool TA, bool TB>
 CA_DEV void matmul(const float* A, int lda, const float* B, int ldb, float* C, int ldc) {
   constexpr int TM = D / 16;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
@@ -524,7 +509,7 @@ CA_DEV void matmul(const float* A, int lda, const float* B, int ldb, float* C, i
 #pragma unroll
     for (int m = 0; m < TM; ++m) a[m] = TA ? A[k * lda + ty + 16 * m] : A[(ty + 16 * m) * lda + k];
 #pragma unroll
-    for (int n = 0; n < TM; ++n) b[n] = B[k * ldb + tx + 16 * n];
+    for (int n = 0; n < TM; ++n) b[n] = TB ? B[(tx + 16 * n) * ldb + k] : B[k * ldb + tx + 16 * n];
 #pragma unroll
     for (int m = 0; m < TM; ++m)
 #pragma unroll
@@ -533,9 +518,8 @@ CA_DEV void matmul(const float* A, int lda, const float* B, int ldb, float* C, i
 #pragma unroll
   for (int m = 0; m < TM; ++m) {
     const int i = ty + 16 * m;
-    const int orow = REV ? D - 1 - i : i;
 #pragma unroll
-    for (int n = 0; n < TM; ++n) C[(int64_t)orow * ldc + tx + 16 * n] = acc[m][n];
+    for (int n = 0; n < TM; ++n) C[(int64_t)i * ldc + tx + 16 * n] = acc[m][n];
   }
 }
 
@@ -559,16 +543,122 @@ struct BasisLds {
   static constexpr int P = D + 1;
   static constexpr int R1 = D * P;
   static constexpr int R2 = D * P;
-  static constexpr int SMALL = 12 * D + 8;
+  static constexpr int SMALL = 12 * D + 16;
   static constexpr size_t bytes = (size_t)(R1 + R2 + SMALL) * 4;
 };
+
+// Pivoted Cholesky factor M = F F^T of a symmetric PSD D x D matrix (in LDS,
+// pitch D + 1), right-looking with the rows in registers (TPR threads per
+// row). Step k pivots on the largest remaining diagonal entry p_k (the lowest
+// index on ties), so a singular metric's range is taken first with large
+// pivots; the factor stops at the first pivot at or below 2^-20 of the
+// largest diagonal entry (what remains is rounding noise of the null space).
+// Column k of F (row k of F^T) is lsc[k] Lraw[k][c] for every c not pivoted
+// before step k (step_of[c] >= k), zero elsewhere; lsc[k] = 0 past the stop.
+template <int D>
+CA_DEV void cholesky_rows(const float* S, float* rb, float* diag, int* step_of, int* sel,
+                          float* lsc, float* __restrict__ Lraw) {
+  constexpr int P = D + 1, TPR = 256 / D, EPT = D / TPR, DL = D / 64;
+  const int tid = threadIdx.x, r = tid / TPR, cb = (tid % TPR) * EPT;
+  const int w = tid >> 6, l = tid & 63;
+  float sr[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) sr[i] = S[r * P + cb + i];
+  float dmax = 0.0f;
+  for (int i = 0; i < D; ++i) dmax = fmaxf(dmax, S[i * P + i]);
+  const float tolp = 0x1p-20f * dmax;
+  // wave 0: argmax of the remaining diagonal (the lowest index on ties)
+  auto pick = [&](int slot) __attribute__((always_inline)) {
+    float best = -INFINITY;
+    int bi = D;
+#pragma unroll
+    for (int q = 0; q < DL; ++q) {
+      const int c = l + 64 * q;
+      if (step_of[c] == D && diag[c] > best) { best = diag[c]; bi = c; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ob = __shfl_xor(best, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    }
+    if (l == 0) sel[slot] = bi;
+  };
+  if (w == 0) {
+#pragma unroll
+    for (int q = 0; q < DL; ++q) {
+      const int c = l + 64 * q;
+      diag[c] = S[c * P + c];
+      step_of[c] = D;
+    }
+    __builtin_amdgcn_wave_barrier();
+    pick(0);
+  }
+  if (tid < D) lsc[tid] = 0.0f;
+  __syncthreads();
+  for (int k = 0; k < D; ++k) {
+    const int p = sel[k & 1];
+    if (p >= D) break;
+    if (r == p) {
+#pragma unroll
+      for (int i = 0; i < EPT; i += 4) {
+        floatx4_t v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = sr[i + u];
+        *reinterpret_cast<floatx4_t*>(rb + cb + i) = v;
+        *reinterpret_cast<floatx4_t*>(Lraw + (int64_t)k * D + cb + i) = v;
+      }
+    }
+    __syncthreads();
+    const float piv = rb[p];
+    if (!(piv > tolp)) break;
+    const float rr = rb[r] / piv;
+#pragma unroll
+    for (int i = 0; i < EPT; i += 4) {
+      const floatx4_t v = *reinterpret_cast<const floatx4_t*>(rb + cb + i);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sr[i + u] = fmaf(-rr, v[u], sr[i + u]);
+    }
+    if (w == 0) {
+      if (l == 0) {
+        lsc[k] = 1.0f / sqrtf(piv);
+        step_of[p] = k;
+      }
+      const float ip = 1.0f / piv;
+#pragma unroll
+      for (int q = 0; q < DL; ++q) {
+        const int c = l + 64 * q;
+        const float v = rb[c];
+        diag[c] = fmaf(-v * ip, v, diag[c]);
+      }
+      __builtin_amdgcn_wave_barrier();
+      pick((k + 1) & 1);
+    }
+    __syncthreads();
+  }
+  __threadfence_block();
+  __syncthreads();
+}
+
+// dst[k][c] (pitch D + 1) = row k of F^T
+template <int D>
+CA_DEV void load_lt(float* dst, const float* Lraw, const float* lsc, const int* step_of) {
+  constexpr int P = D + 1;
+  for (int e = threadIdx.x; e < D * D; e += 256) {
+    const int k = e / D, c = e % D;
+    dst[k * P + c] = (lsc[k] != 0.0f && step_of[c] >= k) ? lsc[k] * Lraw[e] : 0.0f;
+  }
+}
 
 // One workgroup per tree (2 bh + tensor; tensor 0 = queries, 1 = keys).
 // Geometry M: M_k for queries, M_q for keys (identity without the transform);
 // covariance C_x of the representation: C_q (queries), M_k (keys).
-//   R = V diag(sqrt(max(lam, 0))) V^T from eig(M);  Z = R C_x R;  eig(Z) -> W;
-//   row D-1-j of the output is R w_j (w_j the eigenvector of the (j+1)-th
-//   smallest eigenvalue of Z), i.e. the rows descend by eigenvalue.
+//   M = F F^T (pivoted Cholesky);  Z = F^T C_x F;  eig(Z) -> W;  a_j = F w_j.
+// Any factor F F^T = M gives the same a_j up to sign (for invertible M the
+// eigenvectors of F^T C_x F are those of R C_x R, R the symmetric root,
+// rotated by the orthogonal F^T R^-1), so the root is not formed. Each a_j is signed so that its
+// largest-magnitude entry (the first on ties) is positive; output row D-1-j is
+// a_j for the (j+1)-th smallest eigenvalue, so the rows descend.
 template <int D>
 __global__ __launch_bounds__(256) void basis_kernel(const float* __restrict__ Mq,
                                                     const float* __restrict__ Mk,
@@ -592,49 +682,65 @@ __global__ __launch_bounds__(256) void basis_kernel(const float* __restrict__ Mq
   E.pb = sm + 4 * D;            // [2 D]
   E.xb = sm + 6 * D;            // [2 D]
   float* lam = sm + 8 * D;
-  float* scl = sm + 9 * D;
+  float* lsc = sm + 9 * D;
   E.red = sm + 10 * D;          // [8]
+  int* step_of = reinterpret_cast<int*>(sm + 11 * D);   // [D]
+  int* sel = reinterpret_cast<int*>(sm + 12 * D);       // [2]
   const int tree = blockIdx.x, bh = tree >> 1, tensor = tree & 1;
   const int tid = threadIdx.x;
   const float* Cx = (tensor == 0 ? Cq : Mk) + (int64_t)bh * D * D;
-  float* R = Rbuf + (int64_t)tree * D * D;
-  float* Z = Zbuf + (int64_t)tree * D * D;   // scratch: eigenvectors, T, Z, W
+  float* Lraw = Rbuf + (int64_t)tree * D * D;
+  float* Z = Zbuf + (int64_t)tree * D * D;   // scratch: F^T C_x, Z, then W, then the a_j
   float* out = At + (int64_t)tree * D * D;
 
   if (transform) {
     const float* M = (tensor == 0 ? Mk : Mq) + (int64_t)bh * D * D;
     load_mat<D>(r1, M, nullptr);
     __syncthreads();
-    eig_sym<D>(E, lam, Z);
-    if (tid < D) scl[tid] = sqrtf(fmaxf(lam[tid], 0.0f));
+    cholesky_rows<D>(r1, E.pb, E.d, step_of, sel, lsc, Lraw);
+    load_lt<D>(r1, Lraw, lsc, step_of);
+    load_mat<D>(r2, Cx, nullptr);
     __syncthreads();
-    load_mat<D>(r1, Z, nullptr);
-    load_mat<D>(r2, Z, scl);
-    __syncthreads();
-    matmul<D, true, false>(r1, P, r2, P, R, D);   // R = V^T diag(scl) V (rows of V: vectors)
+    matmul<D, false, false>(r1, P, r2, P, Z, D);   // T = F^T C_x
     block_sync_global();
-    load_mat<D>(r1, Cx, nullptr);
-    load_mat<D>(r2, R, nullptr);
+    load_mat<D>(r2, Z, nullptr);
     __syncthreads();
-    matmul<D, false, false>(r1, P, r2, P, Z, D);  // T = C_x R
-    block_sync_global();
-    load_mat<D>(r1, Z, nullptr);
-    __syncthreads();
-    matmul<D, false, false>(r2, P, r1, P, Z, D);  // Z = R T
+    matmul<D, false, true>(r2, P, r1, P, Z, D);    // Z = T F
     block_sync_global();
     load_mat<D>(r1, Z, nullptr);
   } else {
     load_mat<D>(r1, Cx, nullptr);
   }
   __syncthreads();
-  eig_sym<D>(E, lam, Z);   // W: row j = w_j
+  eig_sym<D>(E, lam, Z);   // row j of Z: w_j
   if (transform) {
     load_mat<D>(r1, Z, nullptr);
-    load_mat<D>(r2, R, nullptr);
+    load_lt<D>(r2, Lraw, lsc, step_of);
     __syncthreads();
-    matmul<D, false, true>(r1, P, r2, P, out, D);   // row D-1-j = w_j^T R = (R w_j)^T
-  } else {
-    for (int e = tid; e < D * D; e += 256) out[(D - 1 - e / D) * D + e % D] = Z[e];
+    matmul<D, false, false>(r1, P, r2, P, Z, D);   // row j: w_j^T F^T = (F w_j)^T
+    block_sync_global();
+  }
+  // sign and order: TPR threads per row
+  {
+    constexpr int TPR = 256 / D, EPT = D / TPR;
+    const int j = tid / TPR, cb = (tid % TPR) * EPT;
+    const float* zr = Z + (int64_t)j * D + cb;
+    float best = -1.0f, sv = 1.0f;
+    int bi = 0;
+    for (int i = 0; i < EPT; ++i) {
+      const float v = zr[i];
+      if (fabsf(v) > best) { best = fabsf(v); bi = cb + i; sv = v; }
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) {
+      const float ob = __shfl_xor(best, o);
+      const int oi = __shfl_xor(bi, o);
+      const float os = __shfl_xor(sv, o);
+      if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; sv = os; }
+    }
+    const float sg = sv < 0.0f ? -1.0f : 1.0f;
+    float* orow = out + (int64_t)(D - 1 - j) * D + cb;
+    for (int i = 0; i < EPT; ++i) orow[i] = sg * zr[i];
   }
 }
 
@@ -689,8 +795,10 @@ __global__ __launch_bounds__(256) void basis_split(const float* __restrict__ At,
 constexpr int kRotTokens = 256;   // tokens per workgroup of the rotation
 
 // bf16 rows on MFMA: wave w owns coordinate block bn = w % (D/32) (its three
-// B-operand terms stay in registers) and token blocks of 32 in turn; the A
-// operand (the bf16 row, exact) is read straight from global memory.
+// A-operand terms of the basis stay in registers) and token blocks of 32 in
+// turn; the B operand is the bf16 rows (exact), read straight from global
+// memory one block ahead. Lane (r, h) ends with coordinates 32 bn + 8 g + 4 h
+// + (0..3) of token t0 + r and stores them as four 16-byte vectors.
 template <int D>
 __global__ __launch_bounds__(256) void rotate_bf16(const uint16_t* __restrict__ Q,
                                                    const uint16_t* __restrict__ K,
@@ -712,22 +820,45 @@ __global__ __launch_bounds__(256) void rotate_bf16(const uint16_t* __restrict__ 
     for (int ks = 0; ks < KS; ++ks)
       b[t][ks] = *reinterpret_cast<const bf16x8_t*>(B3 + (int64_t)t * D * D + 16 * ks);
   const int tend = min(N, (blockIdx.x + 1) * kRotTokens);
-  for (int t0 = blockIdx.x * kRotTokens + 32 * wg; t0 < tend; t0 += 32 * WPB) {
+  auto load = [&](int t0, u32x4_t* av, float* sc) __attribute__((always_inline)) {
     const int tok = t0 + r;
-    u32x4_t av[KS];
+    const bool ok = tok < N;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      av[ks] = tok < N ? *reinterpret_cast<const u32x4_t*>(X + (int64_t)tok * D + 16 * ks + 8 * h)
-                       : u32x4_t{0u, 0u, 0u, 0u};
+      av[ks] = ok ? *reinterpret_cast<const u32x4_t*>(X + (int64_t)tok * D + 16 * ks + 8 * h)
+                  : u32x4_t{0u, 0u, 0u, 0u};
+    *sc = ok && sv ? sv[tok] : 1.0f;
+  };
+  int t0 = blockIdx.x * kRotTokens + 32 * wg;
+  if (t0 >= tend) return;
+  u32x4_t av[KS];
+  float sc;
+  load(t0, av, &sc);
+  for (; t0 < tend; t0 += 32 * WPB) {
+    u32x4_t nx[KS];
+    float nsc = 1.0f;
+    const bool more = t0 + 32 * WPB < tend;
+    if (more) load(t0 + 32 * WPB, nx, &nsc);
     floatx16_t acc = zero16();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int t = 0; t < 3; ++t) acc = mfma32(as_bf16x8(av[ks]), b[t][ks], acc);
+      for (int t = 0; t < 3; ++t) acc = mfma32(b[t][ks], as_bf16x8(av[ks]), acc);
+    const int tok = t0 + r;
+    if (tok < N) {
+      float* yr = Yt + (int64_t)tok * D + 32 * bn + 4 * h;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tt = t0 + c_row(i, h);
-      if (tt < N) Yt[(int64_t)tt * D + 32 * bn + r] = (sv ? sv[tt] : 1.0f) * acc[i];
+      for (int g = 0; g < 4; ++g) {
+        floatx4_t v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = sc * acc[4 * g + u];
+        *reinterpret_cast<floatx4_t*>(yr + 8 * g) = v;
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) av[ks] = nx[ks];
+      sc = nsc;
     }
   }
 }

@@ -306,9 +306,12 @@ def pc_basis(X: np.ndarray, M: np.ndarray):
     transforms of v1 §3.2.2); C is the centred covariance of the z over all
     rows and C = W diag(lam) W^T its eigendecomposition. Returns A = R W and
     lam: coordinate j of a vector is y_j = x . a_j (a_j column j of A).
-    Columns are ordered by descending eigenvalue; each column of W is signed
-    so that its largest-magnitude entry is positive (the first such entry on
-    ties), which fixes which child is "left" at a split.
+    Columns are ordered by descending eigenvalue; each column a_j of A is
+    signed so that its largest-magnitude entry is positive (the first such
+    entry on ties), which fixes which child is "left" at a split. The
+    coordinates do not depend on which root of M is used (any F with
+    F F^T = M gives the same a_j up to sign), so the sign is fixed on A
+    itself.
     """
     X = np.asarray(X, np.float64)
     R = root_matrix(M)
@@ -318,11 +321,12 @@ def pc_basis(X: np.ndarray, M: np.ndarray):
     lam, W = np.linalg.eigh(C)
     order = np.argsort(-lam, kind="stable")
     lam, W = lam[order], W[:, order]
-    for j in range(W.shape[1]):
-        k = int(np.argmax(np.abs(W[:, j])))
-        if W[k, j] < 0:
-            W[:, j] = -W[:, j]
-    return R @ W, lam
+    A = R @ W
+    for j in range(A.shape[1]):
+        k = int(np.argmax(np.abs(A[:, j])))
+        if A[k, j] < 0:
+            A[:, j] = -A[:, j]
+    return A, lam
 
 
 def diag_direction(Xs: np.ndarray, A: np.ndarray):

@@ -256,7 +256,8 @@ def check_pc_basis_known_axes():
 def check_pc_basis_decorrelates():
     # In a metric geometry (rank-deficient too) the coordinates y = x A are
     # uncorrelated with variances lam in decreasing order, and A = R W with
-    # W orthonormal (A^T M^+ A = I on the range of M)
+    # W orthonormal (A^T M^+ A = I on the range of M); each a_j has its
+    # largest-magnitude entry positive
     r = _rng(41)
     N, d = 400, 7
     X = r.standard_normal((N, d)) @ r.standard_normal((d, d)) + r.standard_normal(d)
@@ -275,8 +276,33 @@ def check_pc_basis_decorrelates():
         Wk = W[:, keep]
         assert np.allclose(Wk.T @ Wk, np.eye(keep.sum()), atol=1e-8)
         for j in np.flatnonzero(keep):
-            k = np.argmax(np.abs(W[:, j]))
-            assert W[k, j] > 0
+            k = np.argmax(np.abs(A[:, j]))
+            assert A[k, j] > 0
+
+
+def check_pc_basis_root_free():
+    # The same basis from a Cholesky factor of M instead of its symmetric
+    # root: with M = L L^T the vectors z = L^T x have covariance L^T C L,
+    # whose eigenvectors w' give a_j = L w'_j, equal to pc_basis's columns up
+    # to sign; with the sign fixed on a_j they agree exactly
+    r = _rng(43)
+    N, d = 500, 6
+    X = r.standard_normal((N, d)) @ r.standard_normal((d, d)) + r.standard_normal(d)
+    B = r.standard_normal((d, d))
+    M = B @ B.T / d + 0.1 * np.eye(d)
+    A, lam = o.pc_basis(X, M)
+    L = np.linalg.cholesky(M)
+    Z = X @ L
+    Zc = Z - Z.mean(0)
+    lw, Wp = np.linalg.eigh(Zc.T @ Zc / N)
+    idx = np.argsort(-lw)
+    A2 = L @ Wp[:, idx]
+    for j in range(d):
+        k = np.argmax(np.abs(A2[:, j]))
+        if A2[k, j] < 0:
+            A2[:, j] = -A2[:, j]
+    assert np.allclose(lam, lw[idx], rtol=1e-9)
+    assert np.allclose(A, A2, atol=1e-9 * np.abs(A).max())
 
 
 def check_diag_direction_bruteforce():
@@ -304,6 +330,10 @@ def test_pc_basis_known_axes():
 
 def test_pc_basis_decorrelates():
     check_pc_basis_decorrelates()
+
+
+def test_pc_basis_root_free():
+    check_pc_basis_root_free()
 
 
 def test_diag_direction_bruteforce():
@@ -686,6 +716,22 @@ def _basis_ascending(X, M):
     return A[:, ::-1].copy(), lam[::-1].copy()
 
 
+def _basis_sign_on_w(X, M):
+    # the former reading: each eigenvector w_j signed, not a_j = R w_j
+    X = np.asarray(X, np.float64)
+    R = o.root_matrix(M)
+    Z = X @ R
+    Zc = Z - Z.mean(0)
+    lam, W = np.linalg.eigh(Zc.T @ Zc / X.shape[0])
+    order = np.argsort(-lam, kind="stable")
+    lam, W = lam[order], W[:, order]
+    for j in range(W.shape[1]):
+        k = int(np.argmax(np.abs(W[:, j])))
+        if W[k, j] < 0:
+            W[:, j] = -W[:, j]
+    return R @ W, lam
+
+
 def _basis_without_root(X, M):
     return _orig["pc_basis"](X, np.eye(M.shape[0]))
 
@@ -760,6 +806,7 @@ PLANTED = [
     ("fmix64", _fmix_wrong_shift, check_splitmix64_published),
     ("pc_basis", _basis_ascending, check_pc_basis_known_axes),
     ("pc_basis", _basis_without_root, check_pc_basis_decorrelates),
+    ("pc_basis", _basis_sign_on_w, check_pc_basis_decorrelates),
     ("diag_direction", _direction_lowest_variance, check_diag_direction_bruteforce),
     ("diag_direction", _direction_uncentred, check_diag_direction_bruteforce),
 ]
