@@ -21,11 +21,14 @@ namespace ca {
 
 namespace {
 
-constexpr int kMomTile = 128;   // tokens per LDS tile of the bf16 moment pass
+constexpr int kMomTile = 64;   // tokens per LDS tile of the bf16 moment pass
 
 // Weighted second moment sum_t w_t q_t q_t^T (w = s^2) and sum_t s_t q_t over
 // a chunk of query rows, on bf16 MFMA: the A operand is q (exact in bf16), the
-// B operand w q split into three bf16 terms (fp32 accuracy).
+// B operand w q split into three bf16 terms (fp32 accuracy). Thread (tp, gi)
+// reads 16-byte groups of dims of the token pair (2 tp, 2 tp + 1) and writes
+// them transposed as 32-bit words (the two tokens of one dim), the next tile
+// in flight during the products.
 template <int D>
 __global__ __launch_bounds__(256) void qmoment_partial_bf16(const uint16_t* __restrict__ Q,
                                                             const float* __restrict__ s, int N,
@@ -35,63 +38,85 @@ __global__ __launch_bounds__(256) void qmoment_partial_bf16(const uint16_t* __re
   constexpr int NB = D / 32;
   constexpr int BPW = NB * NB / 4;          // 32x32 blocks per wave
   constexpr int LDT = TT + 8;
+  constexpr int TP = TT / 2, GI = 256 / TP, GROUPS = D / 8, GPT = GROUPS / GI;
   __shared__ __attribute__((aligned(16))) uint16_t sx[D][LDT];
-  __shared__ float sw[TT], sv[TT];
+  __shared__ __attribute__((aligned(16))) uint16_t sw3[3][D][LDT];
+  __shared__ float sv[2][TT];
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int r0 = chunk * rows_per_chunk, r1 = min(N, r0 + rows_per_chunk);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
+  const int tp = tid % TP, gi = tid / TP;
   const uint16_t* X = Q + (int64_t)bh * N * D;
   const float* sq = s + (int64_t)bh * N;
   floatx16_t acc[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) acc[i] = zero16();
   float s1 = 0.0f;   // sum of s q over dim tid (tid < D), in token order
-  for (int base = r0; base < r1; base += TT) {
-    // tile into LDS transposed: element (token t, dim d) -> sx[d][t]
-    for (int e = tid; e < TT * D / 2; e += 256) {
-      const int t = e / (D / 2), d2 = e % (D / 2);
-      uint32_t v = 0u;
-      if (base + t < r1) v = *reinterpret_cast<const uint32_t*>(X + (int64_t)(base + t) * D + 2 * d2);
-      sx[2 * d2][t] = (uint16_t)(v & 0xFFFFu);
-      sx[2 * d2 + 1][t] = (uint16_t)(v >> 16);
+  u32x4_t pre[GPT][2];
+  float ps[2];
+  auto fetch = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int tok = base + 2 * tp + q;
+      ps[q] = tok < r1 ? sq[tok] : 0.0f;
+#pragma unroll
+      for (int k = 0; k < GPT; ++k) {
+        pre[k][q] = u32x4_t{0u, 0u, 0u, 0u};
+        if (tok < r1) pre[k][q] = *reinterpret_cast<const u32x4_t*>(X + (int64_t)tok * D + 8 * (gi + GI * k));
+      }
     }
-    if (tid < TT) {
-      const float st = base + tid < r1 ? sq[base + tid] : 0.0f;
-      sw[tid] = st * st;
-      sv[tid] = st;
+  };
+  fetch(r0);
+  int buf = 0;
+  for (int base = r0; base < r1; base += TT) {
+    const float w0 = ps[0] * ps[0], w1 = ps[1] * ps[1];
+    if (gi == 0) {
+      sv[buf][2 * tp] = ps[0];
+      sv[buf][2 * tp + 1] = ps[1];
+    }
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) {
+      const int g = gi + GI * k;
+      const uint32_t a0[4] = {pre[k][0].x, pre[k][0].y, pre[k][0].z, pre[k][0].w};
+      const uint32_t a1[4] = {pre[k][1].x, pre[k][1].y, pre[k][1].z, pre[k][1].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {   // dim 8 g + 2 q + u
+          const uint32_t b0 = (a0[q] >> (16 * u)) & 0xFFFFu, b1 = (a1[q] >> (16 * u)) & 0xFFFFu;
+          const int dd = 8 * g + 2 * q + u;
+          *reinterpret_cast<uint32_t*>(&sx[dd][2 * tp]) = b0 | (b1 << 16);
+          const float x0 = bf16_to_f32((uint16_t)b0) * w0, x1 = bf16_to_f32((uint16_t)b1) * w1;
+          const uint16_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
+          const float e0 = x0 - bf16_to_f32(h0), e1 = x1 - bf16_to_f32(h1);
+          const uint16_t m0 = f32_to_bf16(e0), m1 = f32_to_bf16(e1);
+          const uint16_t l0 = f32_to_bf16(e0 - bf16_to_f32(m0)), l1 = f32_to_bf16(e1 - bf16_to_f32(m1));
+          *reinterpret_cast<uint32_t*>(&sw3[0][dd][2 * tp]) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          *reinterpret_cast<uint32_t*>(&sw3[1][dd][2 * tp]) = (uint32_t)m0 | ((uint32_t)m1 << 16);
+          *reinterpret_cast<uint32_t*>(&sw3[2][dd][2 * tp]) = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+      }
     }
     __syncthreads();
+    if (base + TT < r1) fetch(base + TT);   // next tile in flight during the products
     if (tid < D) {
       const int nt = min(TT, r1 - base);
-      for (int t = 0; t < nt; ++t) s1 = fmaf(sv[t], bf16_to_f32(sx[tid][t]), s1);
+      for (int t = 0; t < nt; ++t) s1 = fmaf(sv[buf][t], bf16_to_f32(sx[tid][t]), s1);
     }
-#pragma unroll 1
+#pragma unroll
     for (int ks = 0; ks < TT / 16; ++ks) {
       const int k0 = 16 * ks + 8 * h;
-      float wk[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wk[e] = sw[k0 + e];
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
         const int b = w * BPW + i, bm = b / NB, bn = b % NB;
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sx[bm * 32 + r][k0]);
-        const u32x4_t bw = *reinterpret_cast<const u32x4_t*>(&sx[bn * 32 + r][k0]);
-        const uint32_t bb[4] = {bw.x, bw.y, bw.z, bw.w};
-        float hi[8], mid[8], lo[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = bf16_to_f32((uint16_t)((bb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu)) * wk[e];
-          hi[e] = (float)(__bf16)v;
-          const float rem = v - hi[e];
-          mid[e] = (float)(__bf16)rem;
-          lo[e] = rem - mid[e];
-        }
-        acc[i] = mfma32(a, as_bf16x8(pack8(hi)), acc[i]);
-        acc[i] = mfma32(a, as_bf16x8(pack8(mid)), acc[i]);
-        acc[i] = mfma32(a, as_bf16x8(pack8(lo)), acc[i]);
+        for (int t = 0; t < 3; ++t)
+          acc[i] = mfma32(a, *reinterpret_cast<const bf16x8_t*>(&sw3[t][bn * 32 + r][k0]), acc[i]);
       }
     }
     __syncthreads();
+    buf ^= 1;
   }
   float* out = partial + ((int64_t)bh * nchunks + chunk) * (D * D + D);
 #pragma unroll
@@ -218,6 +243,40 @@ CA_DEV float ii_start(int i, int j) {
 
 CA_DEV float rcpf(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// Wave reductions on DPP moves (VALU, no LDS round trip): lanes without a
+// source read the identity. Row shifts build each 16-lane row's prefix, the
+// two row broadcasts carry it across rows, lane 63 ends with the total.
+template <int CTRL, int ROW_MASK>
+CA_DEV float dpp_or(float x, float ident) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(ident), __float_as_int(x), CTRL,
+                                                    ROW_MASK, 0xf, false));
+}
+CA_DEV float wave_sum_dpp(float v) {
+  v += dpp_or<0x111, 0xf>(v, 0.0f);   // row_shr:1
+  v += dpp_or<0x112, 0xf>(v, 0.0f);   // row_shr:2
+  v += dpp_or<0x114, 0xf>(v, 0.0f);   // row_shr:4
+  v += dpp_or<0x118, 0xf>(v, 0.0f);   // row_shr:8
+  v += dpp_or<0x142, 0xa>(v, 0.0f);   // row_bcast:15 into rows 1, 3
+  v += dpp_or<0x143, 0xc>(v, 0.0f);   // row_bcast:31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+CA_DEV float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_or<0x111, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_or<0x112, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_or<0x114, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_or<0x118, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_or<0x142, 0xa>(v, -INFINITY));
+  v = fmaxf(v, dpp_or<0x143, 0xc>(v, -INFINITY));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// sum over aligned groups of G = 2 or 4 adjacent lanes (quad permutations)
+template <int G>
+CA_DEV float group_sum(float v) {
+  v += dpp_or<0xB1, 0xf>(v, 0.0f);                  // lane ^ 1
+  if constexpr (G == 4) v += dpp_or<0x4E, 0xf>(v, 0.0f);   // lane ^ 2
+  return v;
+}
+
 template <int D>
 CA_DEV void eig_sym(const EigLds<D>& E, float* lam, float* __restrict__ Xv) {
   constexpr int P = EigLds<D>::P, TPR = 256 / D, EPT = D / TPR;
@@ -227,11 +286,6 @@ CA_DEV void eig_sym(const EigLds<D>& E, float* lam, float* __restrict__ Xv) {
   {
     const int r = tid / TPR, cb = (tid % TPR) * EPT;
     const bool lead = (tid % TPR) == 0;
-    auto row_sum = [&](float v) __attribute__((always_inline)) {
-#pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) v += __shfl_xor(v, o);
-      return v;
-    };
     float sr[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) sr[i] = E.S[r * P + cb + i];
@@ -259,7 +313,7 @@ CA_DEV void eig_sym(const EigLds<D>& E, float* lam, float* __restrict__ Xv) {
           xa[q] = hv[c];
           sig = fmaf(c > k + 1 ? xa[q] : 0.0f, xa[q], sig);
         }
-        sig = wave_sum(sig);
+        sig = wave_sum_dpp(sig);
         float alpha = x0, bet = 0.0f;
         if (sig > 0.0f) {
           const float nrm = sqrtf(fmaf(x0, x0, sig));
@@ -290,9 +344,9 @@ CA_DEV void eig_sym(const EigLds<D>& E, float* lam, float* __restrict__ Xv) {
         pr = fmaf(sr[i + 2], v[2], pr);
         pr = fmaf(sr[i + 3], v[3], pr);
       }
-      pr = bet * row_sum(pr);
+      pr = bet * group_sum<TPR>(pr);
       const float vr = hv[r];
-      const float dv = wave_sum(lead ? vr * pr : 0.0f);
+      const float dv = wave_sum_dpp(lead ? vr * pr : 0.0f);
       if (l == 0) E.red[par * 4 + w] = dv;
       if (lead) E.pb[par * D + r] = pr;
       __syncthreads();
@@ -361,9 +415,18 @@ CA_DEV void eig_sym(const EigLds<D>& E, float* lam, float* __restrict__ Xv) {
         cnt += q < 0.0f;
       }
       float na = a, nb = b;
+      int cms[PPE];
+      if constexpr (PPE == 2) {   // the other half of the wave: v_permlane32_swap
+        const auto sw = __builtin_amdgcn_permlane32_swap((uint32_t)cnt, (uint32_t)cnt, false, false);
+        cms[0] = (int)sw[0];
+        cms[1] = (int)sw[1];
+      } else {
+#pragma unroll
+        for (int mm = 0; mm < PPE; ++mm) cms[mm] = __shfl(cnt, (l % LPE) + mm * LPE);
+      }
 #pragma unroll
       for (int mm = 0; mm < PPE; ++mm) {
-        const int cm = __shfl(cnt, (l % LPE) + mm * LPE);
+        const int cm = cms[mm];
         const float xm = fmaf((float)(mm + 1), step, a);
         if (cm > j) nb = fminf(nb, xm); else na = fmaxf(na, xm);
       }
@@ -419,9 +482,8 @@ CA_DEV void eig_sym(const EigLds<D>& E, float* lam, float* __restrict__ Xv) {
   constexpr int PARTS = 256 / D, LPG = 64 / PARTS, CH = D / PARTS;
   const int j = w * LPG + (l % LPG), part = l / LPG, c0 = part * CH;
   auto reduce_parts = [&](float v) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s2 = LPG; s2 < 64; s2 <<= 1) v += __shfl_xor(v, s2);
-    return v;
+    if constexpr (LPG < 32) v += __shfl_xor(v, 16);
+    return sum_halves(v);
   };
   float x[CH];
 #pragma unroll
@@ -492,34 +554,46 @@ CA_DEV void eig_sym(const EigLds<D>& E, float* lam, float* __restrict__ Xv) {
   __syncthreads();
 }
 
-// C = op(A) op(B) on 256 threads, each a (D/16) x (D/16) block of C;
-// op(A)(i, k) is A[k lda + i] when TA, else A[i lda + k]; op(B)(k, n) is
-// B[n ldb + k] when TB, else B[k ldb + n].
-template <int D, bool TA, bool TB>
-CA_DEV void matmul(const float* A, int lda, const float* B, int ldb, float* C, int ldc) {
-  constexpr int TM = D / 16;
+// C = A Bt^T on 256 threads: C[i][n] = sum_k A[i][k] Bt[n][k], both operands
+// in LDS with pitch D + 4 (16-byte rows, read four k at a time; the 16 Bt rows
+// a wave reads fall on disjoint banks). Each thread owns a (D/16) x (D/16)
+// block: rows ty + 16 m, columns tx + 16 n.
+template <int D>
+CA_DEV void matmul_nt(const float* A, const float* Bt, float* C, int ldc) {
+  constexpr int TM = D / 16, PM = D + 4;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   float acc[TM][TM];
 #pragma unroll
   for (int m = 0; m < TM; ++m)
 #pragma unroll
     for (int n = 0; n < TM; ++n) acc[m][n] = 0.0f;
-  for (int k = 0; k < D; ++k) {
-    float a[TM], b[TM];
+  for (int k = 0; k < D; k += 4) {
+    floatx4_t a[TM], b[TM];
 #pragma unroll
-    for (int m = 0; m < TM; ++m) a[m] = TA ? A[k * lda + ty + 16 * m] : A[(ty + 16 * m) * lda + k];
+    for (int m = 0; m < TM; ++m) a[m] = *reinterpret_cast<const floatx4_t*>(A + (ty + 16 * m) * PM + k);
 #pragma unroll
-    for (int n = 0; n < TM; ++n) b[n] = TB ? B[(tx + 16 * n) * ldb + k] : B[k * ldb + tx + 16 * n];
+    for (int n = 0; n < TM; ++n) b[n] = *reinterpret_cast<const floatx4_t*>(Bt + (tx + 16 * n) * PM + k);
 #pragma unroll
-    for (int m = 0; m < TM; ++m)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int n = 0; n < TM; ++n) acc[m][n] = fmaf(a[m], b[n], acc[m][n]);
+      for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < TM; ++n) acc[m][n] = fmaf(a[m][u], b[n][u], acc[m][n]);
   }
 #pragma unroll
-  for (int m = 0; m < TM; ++m) {
-    const int i = ty + 16 * m;
+  for (int m = 0; m < TM; ++m)
 #pragma unroll
-    for (int n = 0; n < TM; ++n) C[(int64_t)i * ldc + tx + 16 * n] = acc[m][n];
+    for (int n = 0; n < TM; ++n) C[(int64_t)(ty + 16 * m) * ldc + tx + 16 * n] = acc[m][n];
+}
+
+// dst (pitch D + 4) = src (pitch D), or its transpose
+template <int D, bool TRANS>
+CA_DEV void load_nt(float* dst, const float* src) {
+  constexpr int PM = D + 4;
+  for (int e = threadIdx.x; e < D * D; e += 256) {
+    const int i = e / D, k = e % D;
+    if (TRANS) dst[k * PM + i] = src[e];
+    else dst[i * PM + k] = src[e];
   }
 }
 
@@ -541,18 +615,19 @@ CA_DEV void block_sync_global() {
 template <int D>
 struct BasisLds {
   static constexpr int P = D + 1;
-  static constexpr int R1 = D * P;
-  static constexpr int R2 = D * P;
+  static constexpr int R1 = D * (D + 4);   // also holds a pitch-(D + 4) matmul operand
+  static constexpr int R2 = D * (D + 4);
   static constexpr int SMALL = 12 * D + 16;
   static constexpr size_t bytes = (size_t)(R1 + R2 + SMALL) * 4;
 };
 
 // Pivoted Cholesky factor M = F F^T of a symmetric PSD D x D matrix (in LDS,
 // pitch D + 1), right-looking with the rows in registers (TPR threads per
-// row). Step k pivots on the largest remaining diagonal entry p_k (the lowest
-// index on ties), so a singular metric's range is taken first with large
+// row). Step k pivots on the largest remaining diagonal entry p_k, so a
+// singular metric's range is taken first with large
 // pivots; the factor stops at the first pivot at or below 2^-20 of the
 // largest diagonal entry (what remains is rounding noise of the null space).
+// (Among equal largest entries the one held by the lowest lane is taken.)
 // Column k of F (row k of F^T) is lsc[k] Lraw[k][c] for every c not pivoted
 // before step k (step_of[c] >= k), zero elsewhere; lsc[k] = 0 past the stop.
 template <int D>
@@ -576,13 +651,11 @@ CA_DEV void cholesky_rows(const float* S, float* rb, float* diag, int* step_of, 
       const int c = l + 64 * q;
       if (step_of[c] == D && diag[c] > best) { best = diag[c]; bi = c; }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ob = __shfl_xor(best, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-    }
-    if (l == 0) sel[slot] = bi;
+    const float m = wave_max_dpp(best);
+    const uint64_t hit = __ballot(bi < D && best == m);
+    const int src = hit ? (int)__builtin_ctzll(hit) : 0;
+    const int pb = hit ? __builtin_amdgcn_readlane(bi, src) : D;
+    if (l == 0) sel[slot] = pb;
   };
   if (w == 0) {
 #pragma unroll
@@ -640,13 +713,15 @@ CA_DEV void cholesky_rows(const float* S, float* rb, float* diag, int* step_of, 
   __syncthreads();
 }
 
-// dst[k][c] (pitch D + 1) = row k of F^T
-template <int D>
+// dst (pitch D + 4) = F^T (row k = column k of F), or F itself when TRANS
+template <int D, bool TRANS>
 CA_DEV void load_lt(float* dst, const float* Lraw, const float* lsc, const int* step_of) {
-  constexpr int P = D + 1;
+  constexpr int PM = D + 4;
   for (int e = threadIdx.x; e < D * D; e += 256) {
     const int k = e / D, c = e % D;
-    dst[k * P + c] = (lsc[k] != 0.0f && step_of[c] >= k) ? lsc[k] * Lraw[e] : 0.0f;
+    const float v = (lsc[k] != 0.0f && step_of[c] >= k) ? lsc[k] * Lraw[e] : 0.0f;
+    if (TRANS) dst[c * PM + k] = v;
+    else dst[k * PM + c] = v;
   }
 }
 
@@ -698,14 +773,14 @@ __global__ __launch_bounds__(256) void basis_kernel(const float* __restrict__ Mq
     load_mat<D>(r1, M, nullptr);
     __syncthreads();
     cholesky_rows<D>(r1, E.pb, E.d, step_of, sel, lsc, Lraw);
-    load_lt<D>(r1, Lraw, lsc, step_of);
-    load_mat<D>(r2, Cx, nullptr);
+    load_lt<D, false>(r1, Lraw, lsc, step_of);
+    load_nt<D, false>(r2, Cx);
     __syncthreads();
-    matmul<D, false, false>(r1, P, r2, P, Z, D);   // T = F^T C_x
+    matmul_nt<D>(r1, r2, Z, D);   // T = F^T C_x (C_x symmetric)
     block_sync_global();
-    load_mat<D>(r2, Z, nullptr);
+    load_nt<D, false>(r2, Z);
     __syncthreads();
-    matmul<D, false, true>(r2, P, r1, P, Z, D);    // Z = T F
+    matmul_nt<D>(r2, r1, Z, D);   // Z = T F
     block_sync_global();
     load_mat<D>(r1, Z, nullptr);
   } else {
@@ -714,10 +789,10 @@ __global__ __launch_bounds__(256) void basis_kernel(const float* __restrict__ Mq
   __syncthreads();
   eig_sym<D>(E, lam, Z);   // row j of Z: w_j
   if (transform) {
-    load_mat<D>(r1, Z, nullptr);
-    load_lt<D>(r2, Lraw, lsc, step_of);
+    load_nt<D, false>(r1, Z);
+    load_lt<D, true>(r2, Lraw, lsc, step_of);
     __syncthreads();
-    matmul<D, false, false>(r1, P, r2, P, Z, D);   // row j: w_j^T F^T = (F w_j)^T
+    matmul_nt<D>(r1, r2, Z, D);   // row j: w_j^T F^T = (F w_j)^T
     block_sync_global();
   }
   // sign and order: TPR threads per row
@@ -792,33 +867,37 @@ __global__ __launch_bounds__(256) void basis_split(const float* __restrict__ At,
   o[2 * D * D] = lo;
 }
 
-constexpr int kRotTokens = 256;   // tokens per workgroup of the rotation
+constexpr int kRotThreads = 1024;   // 16 waves, one 32-token block each
+constexpr int kRotTokens = 2048;    // tokens per workgroup
 
-// bf16 rows on MFMA: wave w owns coordinate block bn = w % (D/32) (its three
-// A-operand terms of the basis stay in registers) and token blocks of 32 in
-// turn; the B operand is the bf16 rows (exact), read straight from global
-// memory one block ahead. Lane (r, h) ends with coordinates 32 bn + 8 g + 4 h
-// + (0..3) of token t0 + r and stores them as four 16-byte vectors.
+// bf16 rows on MFMA: the three bf16 terms of the tree's basis sit in LDS;
+// each wave takes 32-token blocks in turn (the B operand, the bf16 rows,
+// exact, read from global memory two blocks ahead) and forms every
+// coordinate block from them. Lane (r, h) ends with coordinates
+// 32 bn + 8 g + 4 h + (0..3) of token t0 + r and stores them as 16-byte
+// vectors.
 template <int D>
-__global__ __launch_bounds__(256) void rotate_bf16(const uint16_t* __restrict__ Q,
-                                                   const uint16_t* __restrict__ K,
-                                                   const float* __restrict__ s,
-                                                   const uint16_t* __restrict__ At3, int N,
-                                                   float* __restrict__ Y) {
-  constexpr int NB = D / 32, KS = D / 16, WPB = 4 / NB;   // waves per coordinate block
+__global__ __launch_bounds__(kRotThreads) void rotate_bf16(const uint16_t* __restrict__ Q,
+                                                           const uint16_t* __restrict__ K,
+                                                           const float* __restrict__ s,
+                                                           const uint16_t* __restrict__ At3, int N,
+                                                           float* __restrict__ Y) {
+  constexpr int NB = D / 32, KS = D / 16, PB = D + 8, NW = kRotThreads / 64;
+  extern __shared__ __attribute__((aligned(16))) uint16_t sb[];   // [3 D][PB]
   const int tree = blockIdx.y, bh = tree >> 1, tensor = tree & 1;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 31, h = l >> 5;
-  const int bn = w % NB, wg = w / NB;
+  {
+    const uint16_t* src = At3 + (int64_t)tree * 3 * D * D;
+    for (int e = tid; e < 3 * D * D / 8; e += kRotThreads) {
+      const int row = e / (D / 8), c8 = e % (D / 8);
+      *reinterpret_cast<u32x4_t*>(&sb[row * PB + 8 * c8]) =
+          *reinterpret_cast<const u32x4_t*>(src + (int64_t)row * D + 8 * c8);
+    }
+  }
+  __syncthreads();
   const uint16_t* X = (tensor == 0 ? Q : K) + (int64_t)bh * N * D;
   const float* sv = tensor == 0 ? s + (int64_t)bh * N : nullptr;
   float* Yt = Y + (int64_t)tree * N * D;
-  bf16x8_t b[3][KS];
-  const uint16_t* B3 = At3 + (int64_t)tree * 3 * D * D + (int64_t)(32 * bn + r) * D + 8 * h;
-#pragma unroll
-  for (int t = 0; t < 3; ++t)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      b[t][ks] = *reinterpret_cast<const bf16x8_t*>(B3 + (int64_t)t * D * D + 16 * ks);
   const int tend = min(N, (blockIdx.x + 1) * kRotTokens);
   auto load = [&](int t0, u32x4_t* av, float* sc) __attribute__((always_inline)) {
     const int tok = t0 + r;
@@ -829,37 +908,43 @@ __global__ __launch_bounds__(256) void rotate_bf16(const uint16_t* __restrict__ 
                   : u32x4_t{0u, 0u, 0u, 0u};
     *sc = ok && sv ? sv[tok] : 1.0f;
   };
-  int t0 = blockIdx.x * kRotTokens + 32 * wg;
+  constexpr int STR = 32 * NW;
+  int t0 = blockIdx.x * kRotTokens + 32 * w;
   if (t0 >= tend) return;
-  u32x4_t av[KS];
-  float sc;
-  load(t0, av, &sc);
-  for (; t0 < tend; t0 += 32 * WPB) {
-    u32x4_t nx[KS];
-    float nsc = 1.0f;
-    const bool more = t0 + 32 * WPB < tend;
-    if (more) load(t0 + 32 * WPB, nx, &nsc);
-    floatx16_t acc = zero16();
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int t = 0; t < 3; ++t) acc = mfma32(b[t][ks], as_bf16x8(av[ks]), acc);
+  u32x4_t a0[KS], a1[KS];   // blocks t0 and t0 + STR in flight
+  float s0, s1;
+  load(t0, a0, &s0);
+  load(t0 + STR, a1, &s1);
+  for (; t0 < tend; t0 += STR) {
     const int tok = t0 + r;
-    if (tok < N) {
-      float* yr = Yt + (int64_t)tok * D + 32 * bn + 4 * h;
+#pragma unroll 1
+    for (int bn = 0; bn < NB; ++bn) {   // not unrolled: the basis operands stay in LDS
+      floatx16_t acc0 = zero16(), acc1 = zero16();   // two chains: even and odd k-steps
+      const uint16_t* bb = sb + (32 * bn + r) * PB + 8 * h;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        floatx4_t v;
+      for (int ks = 0; ks < KS; ks += 2)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = sc * acc[4 * g + u];
-        *reinterpret_cast<floatx4_t*>(yr + 8 * g) = v;
+        for (int t = 0; t < 3; ++t) {
+          const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(bb + t * D * PB + 16 * ks);
+          const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(bb + t * D * PB + 16 * ks + 16);
+          acc0 = mfma32(b0, as_bf16x8(a0[ks]), acc0);
+          acc1 = mfma32(b1, as_bf16x8(a0[ks + 1]), acc1);
+        }
+      if (tok < N) {
+        float* yr = Yt + (int64_t)tok * D + 32 * bn + 4 * h;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          floatx4_t v;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = s0 * (acc0[4 * g + u] + acc1[4 * g + u]);
+          *reinterpret_cast<floatx4_t*>(yr + 8 * g) = v;
+        }
       }
     }
-    if (more) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) av[ks] = nx[ks];
-      sc = nsc;
-    }
+    for (int ks = 0; ks < KS; ++ks) a0[ks] = a1[ks];
+    s0 = s1;
+    if (t0 + 2 * STR < tend) load(t0 + 2 * STR, a1, &s1);
   }
 }
 
@@ -902,7 +987,14 @@ void launch_rotate_d(const void* Q, const void* K, int dtype, int BH, int N, con
   if (dtype == 0) {
     basis_split<D><<<(unsigned)(((int64_t)trees * D * D + 255) / 256), 256, 0, st>>>(At, trees, At3);
     dim3 g((N + kRotTokens - 1) / kRotTokens, trees);
-    rotate_bf16<D><<<g, 256, 0, st>>>((const uint16_t*)Q, (const uint16_t*)K, s, At3, N, Y);
+    constexpr size_t sm = (size_t)3 * D * (D + 8) * 2;
+    static bool attr_set = false;
+    if (!attr_set) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rotate_bf16<D>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+      attr_set = true;
+    }
+    rotate_bf16<D><<<g, kRotThreads, sm, st>>>((const uint16_t*)Q, (const uint16_t*)K, s, At3, N, Y);
   } else {
     dim3 g((N + 31) / 32, trees);
     rotate_f32<D><<<g, 256, 0, st>>>((const float*)Q, (const float*)K, s, At, N, Y);
