@@ -231,3 +231,87 @@ def test_basis_rank_deficient(ca):
         assert np.max(np.abs(np.diag(C) - lam)) <= 1e-4 * lam[0], tree
     perm = _np(res.perm_k)[0, 0]
     assert np.array_equal(np.sort(perm), np.arange(N))
+
+
+def test_diag_full_size_video(ca):
+    """The video workload at full size (40 heads, N = 32760, D = 128) in the
+    launch configuration bench.py times with --split-mode diag: permutations
+    of every head are bijections with ascending clusters; for two sampled
+    heads the basis satisfies the bounds above against the oracle's metrics
+    and covariances at full N, every split of every level is bit-exact given
+    the GPU scores, and a sample of nodes per level has its coordinate choice
+    and scores checked against fp64."""
+    import os
+    import time
+    from concurrent.futures import ThreadPoolExecutor
+    import torch
+    w = synth.WORKLOADS["video_32760"]
+    t0 = time.time()
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+        parts = list(ex.map(lambda h: synth.generate(w, heads=slice(h, h + 1)), range(w.H)))
+    Q, K = (np.concatenate([p[i] for p in parts], axis=1) for i in range(2))
+    print(f"inputs {Q.shape} in {time.time() - t0:.1f}s", flush=True)
+    B, H, N, D = Q.shape
+    c = w.c
+    dev = torch.device("cuda:0")
+    tq, tk = (torch.from_numpy(x).to(torch.bfloat16).to(dev).contiguous() for x in (Q, K))
+    res = ca.cluster(tq, tk, c, seed=w.cluster_seed, split_mode="diag", trace=True)
+    torch.cuda.synchronize()
+    L = ca.tree_levels(N, c)
+    S = 1 << max(L - 1, 0)
+    tp = _np(res.trace_perm).reshape(L + 1, 2 * B * H, N)
+    ts = _np(res.trace_score).reshape(L, 2 * B * H, N)
+    td = _np(res.trace_dir).reshape(L, 2 * B * H, S, D)
+    tb = _np(res.trace_basis).reshape(2 * B * H, D, D)
+    pq, pk = _np(res.perm_q), _np(res.perm_k)
+    sizes = o.leaf_sizes(N, c)
+    for h in range(H):
+        for perm in (pq[0, h], pk[0, h]):
+            assert np.array_equal(np.sort(perm), np.arange(N))
+            for j, nj in enumerate(sizes):
+                assert np.all(np.diff(perm[j * c:j * c + nj]) > 0)
+    print(f"properties of {H} heads ok", flush=True)
+    opts = _opts(w)
+    levels = o.tree_levels(N, c)
+    rng = np.random.default_rng(12)
+    for h in (0, 33):
+        Xq, Gq, Xk, Gk = o.head_representations(Q[0, h], K[0, h], opts)
+        hq = o.row_hash(o.row_words(Q[0, h], w.dtype))
+        hk = o.row_hash(o.row_words(K[0, h], w.dtype))
+        for tensor, X, G, hs in ((0, Xq, Gq, hq), (1, Xk, Gk, hk)):
+            tree = 2 * h + tensor
+            A = tb[tree].T.astype(np.float64)
+            _, lam = o.pc_basis(X, G)
+            R = o.root_matrix(G)
+            RR = R @ R
+            assert np.linalg.norm(A @ A.T - RR) <= 1e-4 * np.linalg.norm(RR), (h, tensor)
+            C = np.cov(X @ A, rowvar=False, bias=True)
+            assert np.max(np.abs(C - np.diag(np.diag(C)))) <= 1e-4 * lam[0], (h, tensor)
+            assert np.max(np.abs(np.diag(C) - lam)) <= 1e-4 * lam[0], (h, tensor)
+            for lvl in range(L):
+                before, after, scl = tp[lvl, tree], tp[lvl + 1, tree], ts[lvl, tree]
+                splitting = [nd for nd in levels[lvl] if nd.n > c]
+                check = set(rng.choice(len(splitting), size=min(12, len(splitting)),
+                                       replace=False).tolist())
+                for k, nd in enumerate(splitting):
+                    sl = slice(nd.off, nd.off + nd.n)
+                    mem = before[sl].astype(np.int64)
+                    t = o.split_size(nd.n, c)
+                    left, right = o.split_by_scores(mem, scl[sl].astype(np.float64), t)
+                    assert np.array_equal(after[nd.off:nd.off + t], left), (h, lvl, tensor)
+                    assert np.array_equal(after[nd.off + t:nd.off + nd.n], right)
+                    if k not in check:
+                        continue
+                    hit = np.flatnonzero(np.all(tb[tree] == td[lvl, tree, nd.index], axis=1))
+                    assert hit.size >= 1, (h, lvl, tensor, nd.index)
+                    jg = int(hit[0])
+                    T = o.sample_members(mem, hs, lvl, tensor, D, opts.sample_factor, opts.seed)
+                    jo, _ = o.diag_direction(X[T], A)
+                    if jg != jo:
+                        Y = X[T] @ A
+                        var = ((Y - Y.mean(axis=0)) ** 2).mean(axis=0)
+                        e2 = (Y ** 2).mean(axis=0)
+                        assert var[jg] >= var[jo] - 1e-4 * var[jo] - 1e-6 * e2[jo], (h, lvl, tensor)
+                    so = X[mem] @ A[:, jg]
+                    assert np.max(np.abs(so - scl[sl])) <= 1e-4 * (np.std(so) + 1e-30), (h, lvl, tensor)
+            print(f"head {h} tensor {tensor}: basis, {L} levels ok", flush=True)
