@@ -500,6 +500,88 @@ def route(cq: np.ndarray, ck: np.ndarray, k: int, scores: np.ndarray | None = No
     return np.stack([topk_row(A[a], k) for a in range(A.shape[0])])
 
 
+def cluster_masses(scores: np.ndarray, counts: np.ndarray, tau: float) -> np.ndarray:
+    """Estimated attention mass of each key cluster for one query cluster:
+    every member of cluster c taken at the centroid logit, n_c exp(tau s_c)
+    (the same term that stands for an excluded cluster in Eq. 21), relative
+    to the largest score so that nothing overflows."""
+    s = np.asarray(scores, np.float64)
+    return np.asarray(counts, np.float64) * np.exp(tau * (s - s.max()))
+
+
+def adaptive_row(scores: np.ndarray, counts: np.ndarray, tau: float, recall: float,
+                 min_count: int, nbins: int = 128) -> np.ndarray:
+    """Adaptive selection for one query cluster (v1 §3.3.2 "Selection"; later
+    revision §4.2): the key clusters of highest centroid score until both an
+    estimated attention-mass recall and a minimum count are reached, found by
+    two histogram passes with shared edges for the two criteria.
+
+    Pass 1: n_bins bins spanning the lowest to the highest score; scanning
+    from the top bin, the cutoff bin of each criterion is the first at which
+    the cumulative count (mass) reaches min_count (recall x total mass); the
+    lower of the two is refined. Pass 2: n_bins sub-bins within it, the same
+    scan with the totals of the bins above carried in; the final cutoff is the
+    lower edge of the lower of the two cutoff sub-bins, and every cluster at
+    or above it is selected. Returns the selected indices, ascending.
+
+    The bin of a score decides membership, so it is computed in fp32 exactly
+    as the kernel does: u = (s - lo) * (n_bins / (hi - lo)), key =
+    min(n_bins^2 - 1, floor(u * n_bins)); coarse bin key // n_bins, sub-bin
+    key % n_bins. Masses are fp64, summed exactly as integers in units of
+    2^-40 (every mass is at most n_c <= 2^13, so sums fit in 62 bits); the
+    mass target is floor(recall * total) in fp64. All clusters are selected
+    when the scores are all equal or there are at most min_count clusters.
+    """
+    s32 = np.asarray(scores, np.float32)
+    n = s32.shape[0]
+    if n <= min_count:
+        return np.arange(n)
+    lo, hi = s32.min(), s32.max()
+    if not hi > lo:
+        return np.arange(n)
+    scale = np.float32(nbins) / (hi - lo)
+    u = (s32 - lo) * scale
+    key = np.minimum(nbins * nbins - 1, np.floor(u * np.float32(nbins)).astype(np.int64))
+    coarse, fine = key // nbins, key % nbins
+    mass = [int(v) for v in np.rint(cluster_masses(s32.astype(np.float64), counts, tau) * 2.0**40)]
+    total = sum(mass)
+    target = int(math.floor(recall * float(total)))
+    ones = [1] * n
+
+    def cutoff(members, bins, weights, carried, thr):
+        # highest bin b with carried + sum over bins >= b of weights >= thr
+        # (n_bins when the carried total already reaches it, 0 if none does)
+        if carried >= thr:
+            return nbins
+        hist = [0] * nbins
+        for i in members:
+            hist[bins[i]] += weights[i]
+        cum = carried
+        for b in range(nbins - 1, -1, -1):
+            cum += hist[b]
+            if cum >= thr:
+                return b
+        return 0
+
+    everyone = range(n)
+    b_star = min(cutoff(everyone, coarse, ones, 0, min_count),
+                 cutoff(everyone, coarse, mass, 0, target))
+    above = [i for i in everyone if coarse[i] > b_star]
+    inb = [i for i in everyone if coarse[i] == b_star]
+    f_c = cutoff(inb, fine, ones, len(above), min_count)
+    f_m = cutoff(inb, fine, mass, sum(mass[i] for i in above), target)
+    k_star = b_star * nbins + min(f_c, f_m)
+    return np.flatnonzero(key >= k_star)
+
+
+def route_adaptive(cq: np.ndarray, ck: np.ndarray, counts: np.ndarray, tau: float, recall: float,
+                   min_count: int = 16, scores: np.ndarray | None = None):
+    """Adaptive selection per query cluster: a list of ascending index
+    arrays (their lengths vary)."""
+    A = cluster_scores(cq, ck) if scores is None else np.asarray(scores, np.float64)
+    return [adaptive_row(A[a], counts, tau, recall, min_count) for a in range(A.shape[0])]
+
+
 # ---------------------------------------------------------------------------
 # Attention (v1 §1.2 Eq. 1-2; App. A Eq. 21-22)
 # ---------------------------------------------------------------------------
@@ -571,7 +653,7 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool, scale=None
     for b in range(B):
         for h in range(H):
             O[b, h], L[b, h] = sparse_attention(Q[b, h], K[b, h], V[b, h], perm_q[b, h],
-                                                perm_k[b, h], c, blocks[b, h], compensate, scale)
+                                                perm_k[b, h], c, blocks[b][h], compensate, scale)
     return O, L
 
 

@@ -488,6 +488,103 @@ def test_topk_bruteforce():
     check_topk_bruteforce()
 
 
+# Adaptive selection (v1 §3.3.2 "Selection"; later revision §4.2)
+
+def _adaptive_inputs(r, n):
+    s = r.standard_normal(n) * float(r.choice([0.3, 3.0, 30.0])) + float(r.normal(0, 5))
+    if r.random() < 0.3:
+        s = np.round(s, 1)                      # repeated scores
+    cnt = np.full(n, 64)
+    cnt[-1] = int(r.integers(1, 65))            # a short last cluster
+    return s.astype(np.float32).astype(np.float64), cnt, float(r.choice([0.05, 0.125, 0.5]))
+
+
+def _keys(s):
+    # the 16384 score bins of the selection, in fp32 as the kernel forms them
+    s32 = np.asarray(s, np.float32)
+    lo, hi = s32.min(), s32.max()
+    u = (s32 - lo) * (np.float32(128) / (hi - lo))
+    return np.minimum(16383, np.floor(u * np.float32(128)).astype(np.int64))
+
+
+def check_adaptive_direct_cutoff():
+    # The two passes equal a single pass over all n_bins^2 keys: the cutoff
+    # key is the lower of, per criterion, the largest key K with the total
+    # over keys >= K reaching the threshold
+    r = _rng(50)
+    for _ in range(400):
+        n = int(r.integers(1, 300))
+        s, cnt, tau = _adaptive_inputs(r, n)
+        recall = float(r.choice([0.0, 0.3, 0.9, 0.99, 1.0]))
+        mc = int(r.integers(1, 20))
+        got = o.adaptive_row(s, cnt, tau, recall, mc)
+        if n <= mc or s.max() == s.min():
+            assert np.array_equal(got, np.arange(n))
+            continue
+        key = _keys(s)
+        mass = np.rint(cnt * np.exp(tau * (s - s.max())) * 2.0**40).astype(np.int64)
+        cum_n = np.cumsum(np.bincount(key, minlength=16384)[::-1])[::-1]
+        per_key = np.zeros(16384, np.int64)
+        np.add.at(per_key, key, mass)
+        cum_m = np.cumsum(per_key[::-1])[::-1]
+        kc = int(np.flatnonzero(cum_n >= mc).max())
+        ok = np.flatnonzero(cum_m >= int(math.floor(recall * float(mass.sum()))))
+        km = int(ok.max()) if ok.size else 0
+        want = np.flatnonzero(key >= min(kc, km))
+        assert np.array_equal(got, want), (n, recall, mc)
+
+
+def check_adaptive_guarantees():
+    # count >= min_count; estimated mass >= recall x total; an upper set in
+    # score; dropping the members at the cutoff key breaks a criterion;
+    # monotone in the recall
+    r = _rng(51)
+    for _ in range(300):
+        n = int(r.integers(2, 200))
+        s, cnt, tau = _adaptive_inputs(r, n)
+        mc = int(r.integers(1, 20))
+        mass = cnt * np.exp(tau * (s - s.max()))
+        prev = None
+        for recall in (0.0, 0.5, 0.8, 0.95, 0.999):
+            sel = o.adaptive_row(s, cnt, tau, recall, mc)
+            assert len(sel) >= min(mc, n)
+            assert mass[sel].sum() >= recall * mass.sum() * (1 - 1e-9)
+            assert np.all(np.isin(np.flatnonzero(s > s[sel].min()), sel))
+            assert np.all(np.diff(sel) > 0)
+            if prev is not None:
+                assert np.all(np.isin(prev, sel))
+            prev = sel
+            if len(sel) < n and s.max() > s.min():
+                key = _keys(s)
+                rest = sel[key[sel] > key[sel].min()]
+                assert len(rest) < mc or mass[rest].sum() < recall * mass.sum() * (1 + 1e-9)
+
+
+def check_adaptive_topk_mode():
+    # recall 0 with min_count k on scores far apart (no two in one of the
+    # 16384 key bins) is exact top-k; recall 1 takes every cluster
+    r = _rng(52)
+    for _ in range(200):
+        n = int(r.integers(2, 120))
+        s = r.permutation(n).astype(np.float64) * 3.0 + r.uniform(0, 0.1)
+        cnt = np.full(n, 128)
+        k = int(r.integers(1, n + 1))
+        assert np.array_equal(o.adaptive_row(s, cnt, 0.1, 0.0, k), o.topk_row(s, k))
+        assert np.array_equal(o.adaptive_row(s, cnt, 1e-3, 1.0, 1), np.arange(n))
+
+
+def test_adaptive_direct_cutoff():
+    check_adaptive_direct_cutoff()
+
+
+def test_adaptive_guarantees():
+    check_adaptive_guarantees()
+
+
+def test_adaptive_topk_mode():
+    check_adaptive_topk_mode()
+
+
 # ---------------------------------------------------------------------------
 # Attention (v1 §1.2 Eq. 1-6; App. A Eq. 21-33)
 # ---------------------------------------------------------------------------
@@ -708,7 +805,7 @@ def _no_log_count(Q, K, V, perm_q, perm_k, c, blocks, compensate, scale=None):
 _orig = {name: getattr(o, name) for name in
          ["sparse_attention", "split_size", "metric_matrices", "principal_direction", "topk_row",
           "centroids", "dense_attention", "split_by_scores", "fmix64", "pc_basis",
-          "diag_direction"]}
+          "diag_direction", "adaptive_row", "cluster_masses"]}
 
 
 def _basis_ascending(X, M):
@@ -734,6 +831,18 @@ def _basis_sign_on_w(X, M):
 
 def _basis_without_root(X, M):
     return _orig["pc_basis"](X, np.eye(M.shape[0]))
+
+
+def _adaptive_higher_cutoff(scores, counts, tau, recall, min_count, nbins=128):
+    # the upper of the two criteria's cutoffs: one criterion left unmet
+    a = _orig["adaptive_row"](scores, counts, tau, recall, 1, nbins)
+    b = _orig["adaptive_row"](scores, counts, tau, 0.0, min_count, nbins)
+    return a if len(a) < len(b) else b
+
+
+def _masses_without_counts(scores, counts, tau):
+    s = np.asarray(scores, np.float64)
+    return np.exp(tau * (s - s.max()))
 
 
 def _direction_lowest_variance(Xs, A):
@@ -809,6 +918,8 @@ PLANTED = [
     ("pc_basis", _basis_sign_on_w, check_pc_basis_decorrelates),
     ("diag_direction", _direction_lowest_variance, check_diag_direction_bruteforce),
     ("diag_direction", _direction_uncentred, check_diag_direction_bruteforce),
+    ("adaptive_row", _adaptive_higher_cutoff, check_adaptive_guarantees),
+    ("cluster_masses", _masses_without_counts, check_adaptive_direct_cutoff),
 ]
 
 
