@@ -91,6 +91,10 @@ def parse():
                     help="skip the copy and GEMM rate measurements")
     ap.add_argument("--split-mode", choices=["power", "diag"], default="power",
                     help="basic (power iteration) or diagonalized recursive splitting")
+    ap.add_argument("--assign", choices=["topk", "adaptive"], default="topk",
+                    help="top-k selection, or adaptive selection to a mass recall")
+    ap.add_argument("--recall", type=float, default=0.9, help="mass recall of --assign adaptive")
+    ap.add_argument("--min-count", type=int, default=16, help="minimum count of --assign adaptive")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="quality/latency sweep over cluster size, selected fraction, SMC and "
@@ -108,7 +112,8 @@ def gen_inputs(w):
     return Q, K, V
 
 
-def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power"):
+def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power", assign="topk", recall=0.9,
+                 min_count=16):
     """The oracle, untuned, on the first `heads` heads of the same input."""
     import oracle.clusterattn as o
     try:
@@ -116,9 +121,22 @@ def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power"):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = 1
-    opts = o.ClusterOpts(seed=w.cluster_seed, split_mode=split_mode)
+    opts = o.ClusterOpts(seed=w.cluster_seed, split_mode=split_mode,
+                         query_normalize=assign == "topk")
     t0 = time.perf_counter()
-    o.forward(Q[:, :heads], K[:, :heads], V[:, :heads], w.c, topk, w.compensate, opts, w.dtype)
+    if assign == "topk":
+        o.forward(Q[:, :heads], K[:, :heads], V[:, :heads], w.c, topk, w.compensate, opts, w.dtype)
+    else:
+        Qs, Ks, Vs = Q[:, :heads], K[:, :heads], V[:, :heads]
+        pq, pk = o.cluster(Qs, Ks, w.c, opts, w.dtype)
+        tau = 1.0 / math.sqrt(w.D)
+        sel = [[None] * heads for _ in range(w.B)]
+        for b in range(w.B):
+            for h in range(heads):
+                cq, _ = o.centroids(Qs[b, h], pq[b, h], w.c)
+                ck, cnt = o.centroids(Ks[b, h], pk[b, h], w.c)
+                sel[b][h] = o.route_adaptive(cq, ck, cnt, tau, recall, min_count)
+        o.attend(Qs, Ks, Vs, pq, pk, w.c, sel, w.compensate)
     t = time.perf_counter() - t0
     flops = 4.0 * w.D * w.N * w.N * heads * w.B
     return {
@@ -282,22 +300,29 @@ def main():
     ws_a = torch.empty(ca.workspace_size(ca.OP_ATTEND, B, H, N, D, c, topk), dtype=torch.uint8,
                        device=dev)
 
+    adaptive = args.assign == "adaptive"
+
     def step(evs=None, kev=None):
         if evs:
             evs[0].record()
-        cr = ca.cluster(Q, K, c, seed=w.cluster_seed, split_mode=args.split_mode, workspace=ws_c)
+        cr = ca.cluster(Q, K, c, seed=w.cluster_seed, split_mode=args.split_mode,
+                        query_normalize=not adaptive, workspace=ws_c)
         if evs:
             evs[1].record()
-        blocks = ca.route(cr.cent_q, cr.cent_k, topk, workspace=ws_r)
+        if adaptive:
+            blocks, nsel = ca.route_adaptive(cr.cent_q, cr.cent_k, cr.counts, args.recall,
+                                             min_count=args.min_count, workspace=ws_r)
+        else:
+            blocks, nsel = ca.route(cr.cent_q, cr.cent_k, topk, workspace=ws_r), None
         if evs:
             evs[2].record()
             ca.profile_events(kev[0].handle, kev[1].handle)
         O = ca.attend(Q, K, V, cr.perm_q, cr.perm_k, c, blocks, compensate=w.compensate,
-                      workspace=ws_a)
+                      nsel=nsel, workspace=ws_a)
         if evs:
             ca.profile_events(None, None)
             evs[3].record()
-        return O, cr, blocks
+        return O, cr, (blocks, nsel)
 
     for _ in range(args.warmup):
         step()
@@ -320,11 +345,19 @@ def main():
     gpu_step = np.mean([e[0].elapsed_time(e[3]) for e in evs])
 
     # performed interactions of the attention kernel (valid keys and centroids)
+    blocks, nsel = blocks
     bl = blocks.cpu().numpy().astype(np.int64)
     sizes = np.full(n_c, c, np.int64)
     sizes[-1] = N - (n_c - 1) * c
-    tok_inter = float(np.sum(sizes[None, None, :] * sizes[bl].sum(-1)))
-    cen_inter = float(np.sum(sizes) * (n_c - topk) * B * H) if w.compensate else 0.0
+    if nsel is None:
+        ns = np.full(bl.shape[:3], topk, np.int64)
+    else:
+        ns = nsel.cpu().numpy().astype(np.int64)
+    take = np.arange(bl.shape[-1])[None, None, None, :] < ns[..., None]
+    sel_sizes = np.where(take, sizes[np.clip(bl, 0, n_c - 1)], 0).sum(-1)
+    tok_inter = float(np.sum(sizes[None, None, :] * sel_sizes))
+    cen_inter = float(np.sum(sizes[None, None, :] * (n_c - ns))) if w.compensate else 0.0
+    mean_sel = float(ns.mean())
     flops_attn = 4.0 * D * (tok_inter + cen_inter)
     achieved = flops_attn / (t_attn_kernel * 1e-3) / 1e12
 
@@ -352,7 +385,8 @@ def main():
     clu_ms = float(st_cluster + st_route)
     clu_gbs = clu_bytes / (clu_ms * 1e-3) / 1e9
 
-    traffic = recorded_traffic(w.name, topk) if B * H == w.B * w.H else None
+    traffic = (recorded_traffic(w.name, topk) if B * H == w.B * w.H and not adaptive
+               and args.split_mode == "power" else None)
     eff = 4.0 * D * N * N * B * H / (wall) / 1e12
     result = {
         "metric": METRIC,
@@ -369,7 +403,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "N": N, "head_dim": D,
                    "cluster_size": c, "topk": topk, "compensate": w.compensate,
-                   "split_mode": args.split_mode},
+                   "split_mode": args.split_mode, "assign": args.assign,
+                   **({"recall": args.recall, "min_count": args.min_count,
+                       "mean_selected": round(mean_sel, 2)} if adaptive else {})},
         "stage_ms": {"cluster": round(float(st_cluster), 4), "route": round(float(st_route), 4),
                      "attend": round(float(st_attend), 4),
                      "attend_kernel": round(float(t_attn_kernel), 4),
@@ -417,7 +453,8 @@ def main():
 
     if not args.no_cpu_baseline:
         heads = max(1, min(args.cpu_heads, H))
-        result["cpu_baseline"] = cpu_baseline(w, Qn, Kn, Vn, topk, heads, args.split_mode)
+        result["cpu_baseline"] = cpu_baseline(w, Qn, Kn, Vn, topk, heads, args.split_mode,
+                                              args.assign, args.recall, args.min_count)
 
     print(json.dumps(result), flush=True)
 

@@ -17,12 +17,14 @@ from dataclasses import dataclass
 
 __all__ = [
     "CAError", "load", "LIB_PATH", "EXPORTS", "profile_events", "peak_probe", "HipEvent", "tree_levels",
-    "workspace_size", "cluster", "route", "attend", "dense", "forward", "ClusterResult",
+    "workspace_size", "cluster", "route", "route_adaptive", "attend", "dense", "forward",
+    "ClusterResult",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libca.so")
-EXPORTS = ["ca_tree_levels", "ca_workspace_size", "ca_cluster", "ca_route", "ca_attend",
-           "ca_dense", "ca_profile_events", "ca_peak_probe", "ca_status_string", "ca_last_error"]
+EXPORTS = ["ca_tree_levels", "ca_workspace_size", "ca_cluster", "ca_route", "ca_route_adaptive",
+           "ca_attend", "ca_attend_var", "ca_dense", "ca_profile_events", "ca_peak_probe",
+           "ca_status_string", "ca_last_error"]
 
 CA_BF16, CA_F32 = 0, 1
 OP_CLUSTER, OP_ROUTE, OP_ATTEND, OP_DENSE, OP_CLUSTER_DIAG = 0, 1, 2, 3, 4
@@ -63,8 +65,12 @@ def load() -> ctypes.CDLL:
     lib.ca_cluster.restype = I
     lib.ca_route.argtypes = [P, P, I, I, I, I, I, I, P, P, P, S, P]
     lib.ca_route.restype = I
+    lib.ca_route_adaptive.argtypes = [P, P, P, I, I, I, I, I, F, F, I, P, P, P, P, S, P]
+    lib.ca_route_adaptive.restype = I
     lib.ca_attend.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, I, I, F, P, P, P, S, P]
     lib.ca_attend.restype = I
+    lib.ca_attend_var.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I, I, F, P, P, P, S, P]
+    lib.ca_attend_var.restype = I
     lib.ca_dense.argtypes = [P, P, P, I, I, I, I, I, F, P, P, P, S, P]
     lib.ca_dense.restype = I
     lib.ca_peak_probe.argtypes = [I, I, I, P, P]
@@ -256,9 +262,33 @@ def route(cent_q, cent_k, topk: int, *, return_scores: bool = False, workspace=N
     return (blocks, scores) if return_scores else blocks
 
 
+def route_adaptive(cent_q, cent_k, counts_k, recall: float, *, min_count: int = 16,
+                   scale: float = 0.0, return_scores: bool = False, workspace=None):
+    """ca_route_adaptive: per query cluster the key clusters above a histogram
+    cutoff that meets min_count and the estimated mass recall. Returns
+    (blocks [B,H,n_qc,n_kc] with the first nsel entries of a row selected,
+    nsel [B,H,n_qc]) and the scores if asked."""
+    torch = _torch()
+    B, H, nq, D = cent_q.shape
+    nk = cent_k.shape[2]
+    dev = cent_q.device
+    blocks = torch.empty((B, H, nq, nk), dtype=torch.int32, device=dev)
+    nsel = torch.empty((B, H, nq), dtype=torch.int32, device=dev)
+    scores = torch.empty((B, H, nq, nk), dtype=torch.float32, device=dev) if return_scores else None
+    nbytes = 0 if return_scores else workspace_size(OP_ROUTE, B, H, nq, D, nk, 1)
+    ws = _ws(nbytes, dev, workspace)
+    st = load().ca_route_adaptive(cent_q.data_ptr(), cent_k.data_ptr(), counts_k.data_ptr(), B, H,
+                                  nq, nk, D, float(scale), float(recall), int(min_count),
+                                  blocks.data_ptr(), nsel.data_ptr(), _ptr(scores), _ptr(ws),
+                                  nbytes, _stream_ptr(dev))
+    _check(st)
+    return (blocks, nsel, scores) if return_scores else (blocks, nsel)
+
+
 def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
-           scale: float = 0.0, return_lse: bool = False, workspace=None):
-    """ca_attend: block-sparse attention with optional mean-compensation."""
+           scale: float = 0.0, return_lse: bool = False, nsel=None, workspace=None):
+    """ca_attend: block-sparse attention with optional mean-compensation;
+    with `nsel` (selected count per row of `blocks`), ca_attend_var."""
     torch = _torch()
     _bhnd(Q, K, V)
     B, H, N, D = Q.shape
@@ -268,10 +298,16 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
     topk = blocks.shape[-1]
     nbytes = workspace_size(OP_ATTEND, B, H, N, D, c, topk)
     ws = _ws(nbytes, dev, workspace)
-    st = load().ca_attend(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, D,
-                          perm_q.data_ptr(), perm_k.data_ptr(), c, blocks.data_ptr(), topk,
-                          int(compensate), float(scale), O.data_ptr(), _ptr(lse), _ptr(ws),
-                          nbytes, _stream_ptr(dev))
+    if nsel is None:
+        st = load().ca_attend(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, D,
+                              perm_q.data_ptr(), perm_k.data_ptr(), c, blocks.data_ptr(), topk,
+                              int(compensate), float(scale), O.data_ptr(), _ptr(lse), _ptr(ws),
+                              nbytes, _stream_ptr(dev))
+    else:
+        st = load().ca_attend_var(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N,
+                                  D, perm_q.data_ptr(), perm_k.data_ptr(), c, blocks.data_ptr(),
+                                  nsel.data_ptr(), topk, int(compensate), float(scale),
+                                  O.data_ptr(), _ptr(lse), _ptr(ws), nbytes, _stream_ptr(dev))
     _check(st)
     return (O, lse) if return_lse else O
 

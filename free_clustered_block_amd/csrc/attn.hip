@@ -215,7 +215,8 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   float m = kNegInf, lsum = 0.0f;
   const float sl2 = a.scale * kLog2e;
 
-  const int nsel = DENSE ? nc : a.topk;
+  const int nsel = DENSE ? nc
+                  : (a.nsel ? min(max(a.nsel[(int64_t)bh * nc + qa], 0), a.topk) : a.topk);
   const int32_t* blk = DENSE ? nullptr : a.blocks + ((int64_t)bh * nc + qa) * a.topk;
   // Token sub-tiles of the selected clusters come first; with compensation the
   // centroids follow as ncp / 64 more sub-tiles of 64 (kbar rows as keys,
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   if (comp) {
     for (int e = tid; e < ncp / 32; e += NT) sSel[e] = 0u;
     __syncthreads();
-    for (int e = tid; e < a.topk; e += NT) {
+    for (int e = tid; e < nsel; e += NT) {
       const int j = blk[e];
       if (j >= 0 && j < nc) atomicOr(&sSel[j >> 5], 1u << (j & 31));
     }
@@ -523,7 +524,8 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
     m = mn;
   };
   // key tokens, 32 at a time through LDS
-  const int nsel = DENSE ? 1 : a.topk;
+  const int nsel = DENSE ? 1
+                  : (a.nsel ? min(max(a.nsel[(int64_t)bh * nc + qa], 0), a.topk) : a.topk);
   for (int bi = 0; bi < nsel; ++bi) {
     const int j = DENSE ? 0 : a.blocks[((int64_t)bh * nc + qa) * a.topk + bi];
     if (j < 0 || j >= nc) continue;
@@ -554,7 +556,7 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
     __syncthreads();
     for (int e = tid; e < ncp / 32; e += 256) sSel[e] = 0u;
     __syncthreads();
-    for (int e = tid; e < a.topk; e += 256) {
+    for (int e = tid; e < nsel; e += 256) {
       const int j = a.blocks[((int64_t)bh * nc + qa) * a.topk + e];
       if (j >= 0 && j < nc) atomicOr(&sSel[j >> 5], 1u << (j & 31));
     }

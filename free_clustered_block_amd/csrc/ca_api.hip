@@ -280,10 +280,38 @@ int ca_route(const float* cent_q, const float* cent_k, int B, int H, int n_qc, i
   return after_launch();
 }
 
-int ca_attend(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N, int D,
-              const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
-              const int32_t* blocks, int topk, int compensate, float scale, void* O, float* lse,
-              void* ws, size_t ws_bytes, void* stream) {
+int ca_route_adaptive(const float* cent_q, const float* cent_k, const int32_t* counts_k, int B,
+                      int H, int n_qc, int n_kc, int D, float scale, float recall, int min_count,
+                      int32_t* blocks, int32_t* nsel, float* scores, void* ws, size_t ws_bytes,
+                      void* stream) {
+  set_error("");
+  if (!cent_q || !cent_k || !counts_k || !blocks || !nsel)
+    return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
+  if (B < 1 || H < 1 || n_qc < 1 || n_kc < 1) return fail(CA_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (!supported_d(D)) return fail(CA_ERR_UNSUPPORTED, "D must be 64 or 128");
+  if (!(recall >= 0.0f && recall <= 1.0f)) return fail(CA_ERR_INVALID_ARG, "recall must be in [0, 1]");
+  if (min_count < 1) return fail(CA_ERR_INVALID_ARG, "min_count must be >= 1");
+  if (!(scale >= 0.0f) || !std::isfinite(scale)) return fail(CA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (n_kc > 8192) return fail(CA_ERR_UNSUPPORTED, "n_kc must be <= 8192");
+  if ((int64_t)B * H > 32767 || n_qc > 65535) return fail(CA_ERR_UNSUPPORTED, "too many heads or query clusters");
+  const int BH = B * H;
+  Carver cv(ws);
+  float* sc = scores;
+  if (!sc) {
+    sc = cv.take<float>((size_t)BH * n_qc * n_kc);
+    if (int e = check_ws(ws, ws_bytes, cv.size())) return e;
+  }
+  const float tau = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
+  launch_route_adaptive(cent_q, cent_k, counts_k, BH, n_qc, n_kc, D, tau, (double)recall, min_count,
+                        sc, blocks, nsel, static_cast<hipStream_t>(stream));
+  return after_launch();
+}
+
+namespace {
+int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
+                int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
+                const int32_t* blocks, const int32_t* nsel, int topk, int compensate, float scale,
+                void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
   set_error("");
   if (!Q || !K || !V || !perm_q || !perm_k || !blocks || !O)
     return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
@@ -300,13 +328,34 @@ int ca_attend(const void* Q, const void* K, const void* V, ca_dtype dt, int B, i
   a.BH = B * H; a.N = N; a.D = D; a.c = c; a.nc = nc; a.topk = topk;
   a.compensate = compensate ? 1 : 0;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
-  a.perm_q = perm_q; a.perm_k = perm_k; a.blocks = blocks; a.O = O; a.lse = lse;
+  a.perm_q = perm_q; a.perm_k = perm_k; a.blocks = blocks; a.nsel = nsel; a.O = O; a.lse = lse;
   a.ev_start = g_prof_start; a.ev_stop = g_prof_stop;
   Carver cv(ws);
   plan_attend(cv, a, true);
   if (int e = check_ws(ws, ws_bytes, cv.size())) return e;
   launch_attend(a, static_cast<hipStream_t>(stream));
   return after_launch();
+}
+}  // namespace
+
+int ca_attend(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N, int D,
+              const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
+              const int32_t* blocks, int topk, int compensate, float scale, void* O, float* lse,
+              void* ws, size_t ws_bytes, void* stream) {
+  return attend_impl(Q, K, V, dt, B, H, N, D, perm_q, perm_k, cluster_size, blocks, nullptr, topk,
+                     compensate, scale, O, lse, ws, ws_bytes, stream);
+}
+
+int ca_attend_var(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
+                  int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
+                  const int32_t* blocks, const int32_t* nsel, int max_sel, int compensate,
+                  float scale, void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!nsel) {
+    set_error("");
+    return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
+  }
+  return attend_impl(Q, K, V, dt, B, H, N, D, perm_q, perm_k, cluster_size, blocks, nsel, max_sel,
+                     compensate, scale, O, lse, ws, ws_bytes, stream);
 }
 
 int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N, int D,

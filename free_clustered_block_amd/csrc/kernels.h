@@ -68,6 +68,11 @@ void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, in
 // route.hip ------------------------------------------------------------------
 void launch_route(const float* cq, const float* ck, int BH, int nq, int nk, int D, int topk,
                   float* scores, int32_t* blocks, hipStream_t st);
+// adaptive selection: blocks [BH][nq][nk] (the first nsel entries of a row
+// are the selected clusters, ascending; the rest -1), nsel [BH][nq]
+void launch_route_adaptive(const float* cq, const float* ck, const int32_t* counts, int BH, int nq,
+                           int nk, int D, float tau, double recall, int min_count, float* scores,
+                           int32_t* blocks, int32_t* nsel, hipStream_t st);
 
 // attn.hip -------------------------------------------------------------------
 struct AttnArgs {
@@ -80,6 +85,7 @@ struct AttnArgs {
   const int32_t* perm_q;
   const int32_t* perm_k;
   const int32_t* blocks;
+  const int32_t* nsel;   // [BH][nc] selected clusters per row of blocks, or null (= topk)
   void* O;
   float* lse;
   // scratch (bf16 path)

@@ -1,7 +1,8 @@
 // Cluster assignment (paper v1 §3.3): score every query cluster against every
 // key cluster by the centroid product qbar . kbar (Eq. 18, the mean logit),
 // then keep the top-k key clusters per query cluster (§3.3.2), ties to the
-// lower index, written in ascending order.
+// lower index, written in ascending order; or, adaptively, the clusters above
+// a histogram cutoff that meets a minimum count and a mass recall.
 #include "kernels.h"
 
 namespace ca {
@@ -153,7 +154,177 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
   }
 }
 
+// ----------------------------------------------------------------------------
+// Adaptive selection (v1 §3.3.2 "Selection"; later revision §4.2): per query
+// cluster, the key clusters of highest score until both a minimum count and
+// an estimated attention-mass recall are reached. Two histogram passes with
+// shared edges for the two criteria: 128 bins over [lo, hi], the lower of the
+// two cutoff bins refined into 128 sub-bins; the cutoff is the lower edge of
+// the lower cutoff sub-bin. A score's bin is key >> 7 and its sub-bin key &
+// 127 with key = min(16383, floor(((s - lo) * (128 / (hi - lo))) * 128)) in
+// fp32 (round-to-nearest, no contraction). The mass of cluster j is
+// n_j exp(tau (s_j - hi)), held as an integer in units of 2^-40 so that sums
+// are exact and the passes deterministic; the target is
+// floor(recall * total) in double.
+// ----------------------------------------------------------------------------
+
+constexpr int kAdaBins = 128;
+
+__device__ __forceinline__ int ada_key(float s, float lo, float scale) {
+  const float u = __fmul_rn(__fsub_rn(s, lo), scale);
+  const float f = floorf(__fmul_rn(u, (float)kAdaBins));
+  return f >= 0.0f ? (int)fminf(f, (float)(kAdaBins * kAdaBins - 1)) : 0;   // NaN -> 0
+}
+
+__device__ __forceinline__ uint64_t ada_mass(float s, float hi, float tau, int cnt) {
+  const float m = (float)cnt * expf(__fmul_rn(tau, __fsub_rn(s, hi)));
+  return (uint64_t)rint((double)m * 0x1p40);
+}
+
+// Wave 0: highest bin b with carried + sum over bins >= b reaching thr
+// (kAdaBins when the carried total already does, 0 if no bin does). Lane l
+// holds bins 2l and 2l + 1; a suffix sum over the lanes gives every bin's
+// cumulative total, and since it only grows towards lower bins, the bins
+// that reach thr are 0 .. b: b + 1 of them.
+template <typename T>
+__device__ int ada_cutoff(const T* hist, T carried, T thr) {
+  const int l = threadIdx.x & 63;
+  if (carried >= thr) return kAdaBins;
+  const T h0 = hist[2 * l], h1 = hist[2 * l + 1];
+  T suf = h0 + h1;   // becomes the sum over bins >= 2 l
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const T y = __shfl_down(suf, d, 64);
+    if (l + d < 64) suf += y;
+  }
+  const T c0 = carried + suf, c1 = carried + suf - h0;   // cumulative at bins 2 l, 2 l + 1
+  const int n = __popcll(__ballot(c0 >= thr)) + __popcll(__ballot(c1 >= thr));
+  return n > 0 ? n - 1 : 0;
+}
+
+__global__ __launch_bounds__(kSelThreads) void adaptive_kernel(
+    const float* __restrict__ A, const int32_t* __restrict__ counts, int nq, int nk, float tau,
+    double recall, int min_count, int32_t* __restrict__ blocks, int32_t* __restrict__ nsel) {
+  __shared__ int skey[kMaxKeys];
+  __shared__ int hc[kAdaBins];
+  __shared__ unsigned long long hm[kAdaBins];
+  __shared__ float sred[2][kSelWaves];
+  __shared__ int wtot[kSelWaves];
+  __shared__ int sk[4];
+  __shared__ unsigned long long smass[2];
+  const int row = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const float* a = A + ((int64_t)bh * nq + row) * nk;
+  const int32_t* cn = counts + (int64_t)bh * nk;
+  int32_t* out = blocks + ((int64_t)bh * nq + row) * nk;
+
+  float lo = INFINITY, hi = -INFINITY;
+  for (int i = tid; i < nk; i += kSelThreads) {
+    const float v = a[i];
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  lo = -wave_max(-lo);
+  hi = wave_max(hi);
+  if (l == 0) { sred[0][w] = lo; sred[1][w] = hi; }
+  __syncthreads();
+  lo = sred[0][0]; hi = sred[1][0];
+  for (int q = 1; q < kSelWaves; ++q) { lo = fminf(lo, sred[0][q]); hi = fmaxf(hi, sred[1][q]); }
+
+  int kstar = 0;   // every key >= 0: all selected
+  if (nk > min_count && hi > lo) {
+    const float scale = __fdiv_rn((float)kAdaBins, __fsub_rn(hi, lo));
+    // pass 1: coarse bins
+    if (tid < kAdaBins) { hc[tid] = 0; hm[tid] = 0ull; }
+    __syncthreads();
+    for (int i = tid; i < nk; i += kSelThreads) {
+      const float v = a[i];
+      const int k = ada_key(v, lo, scale);
+      skey[i] = k;
+      atomicAdd(&hc[k >> 7], 1);
+      atomicAdd(&hm[k >> 7], (unsigned long long)ada_mass(v, hi, tau, cn[i]));
+    }
+    __syncthreads();
+    if (w == 0) {
+      unsigned long long tm = hm[2 * l] + hm[2 * l + 1];
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) tm += __shfl_xor(tm, d, 64);
+      const unsigned long long target = (unsigned long long)floor(recall * (double)tm);
+      const int bc = ada_cutoff<int>(hc, 0, min_count);
+      const int bm = ada_cutoff<unsigned long long>(hm, 0ull, target);
+      const int bs = min(bc, bm);
+      // totals of the bins above bs
+      int c0 = (2 * l > bs ? hc[2 * l] : 0) + (2 * l + 1 > bs ? hc[2 * l + 1] : 0);
+      unsigned long long m0 = (2 * l > bs ? hm[2 * l] : 0ull) + (2 * l + 1 > bs ? hm[2 * l + 1] : 0ull);
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) {
+        c0 += __shfl_xor(c0, d, 64);
+        m0 += __shfl_xor(m0, d, 64);
+      }
+      if (l == 0) {
+        sk[0] = bs;
+        sk[1] = c0;
+        smass[0] = m0;
+        smass[1] = target;
+      }
+    }
+    __syncthreads();
+    const int bs = sk[0];
+    // pass 2: the sub-bins of bin bs
+    if (tid < kAdaBins) { hc[tid] = 0; hm[tid] = 0ull; }
+    __syncthreads();
+    for (int i = tid; i < nk; i += kSelThreads) {
+      const int k = skey[i];
+      if ((k >> 7) == bs) {
+        atomicAdd(&hc[k & 127], 1);
+        atomicAdd(&hm[k & 127], (unsigned long long)ada_mass(a[i], hi, tau, cn[i]));
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      const int fc = ada_cutoff<int>(hc, sk[1], min_count);
+      const int fm = ada_cutoff<unsigned long long>(hm, smass[0], smass[1]);
+      if (l == 0) sk[2] = bs * kAdaBins + min(fc, fm);
+    }
+    __syncthreads();
+    kstar = sk[2];
+  } else {
+    for (int i = tid; i < nk; i += kSelThreads) skey[i] = 0;
+    __syncthreads();
+  }
+  // compaction in index order
+  int base = 0;
+  for (int b0 = 0; b0 < nk; b0 += kSelThreads) {
+    const int i = b0 + tid;
+    const bool take = i < nk && skey[i] >= kstar;
+    uint64_t bal;
+    const int pre = lane_prefix(take, &bal);
+    if (l == 0) wtot[w] = __popcll(bal);
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int q = 0; q < kSelWaves; ++q) {
+      if (q < w) before += wtot[q];
+      all += wtot[q];
+    }
+    if (take) out[base + before + pre] = i;
+    base += all;
+    __syncthreads();
+  }
+  for (int i = base + tid; i < nk; i += kSelThreads) out[i] = -1;
+  if (tid == 0) nsel[(int64_t)bh * nq + row] = base;
+}
+
 }  // namespace
+
+void launch_route_adaptive(const float* cq, const float* ck, const int32_t* counts, int BH, int nq,
+                           int nk, int D, float tau, double recall, int min_count, float* scores,
+                           int32_t* blocks, int32_t* nsel, hipStream_t st) {
+  dim3 gs((nk + kTile - 1) / kTile, (nq + kTile - 1) / kTile, BH);
+  scores_kernel<<<gs, 256, 0, st>>>(cq, ck, nq, nk, D, scores);
+  dim3 gt(nq, BH);
+  adaptive_kernel<<<gt, kSelThreads, 0, st>>>(scores, counts, nq, nk, tau, recall, min_count,
+                                               blocks, nsel);
+}
 
 void launch_route(const float* cq, const float* ck, int BH, int nq, int nk, int D, int topk,
                   float* scores, int32_t* blocks, hipStream_t st) {

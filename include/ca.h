@@ -173,6 +173,44 @@ int ca_route(const float* cent_q, const float* cent_k, int B, int H, int n_qc, i
              void* stream);
 
 /*
+ * ca_route_adaptive -- centroid scoring and adaptive selection (v1 §3.3.2
+ * "Selection"; later revision §4.2): for each query cluster, the key
+ * clusters of highest score until both min_count clusters and a fraction
+ * `recall` of the estimated attention mass are selected.
+ *
+ * The estimated mass of key cluster j for query cluster a is
+ * n_j exp(tau (s_aj - max_j s_aj)), every member taken at the centroid logit
+ * (the term that stands for an excluded cluster in Eq. 21). The cutoff is
+ * found by two histogram passes with shared edges for the two criteria:
+ * 128 bins spanning the row's lowest to highest score, then 128 sub-bins of
+ * the lower of the two cutoff bins; every cluster at or above the lower
+ * edge of the lower cutoff sub-bin is selected, so at least min_count
+ * clusters are taken and their estimated mass reaches recall x total. A
+ * score's bin is formed in fp32: key = min(16383, floor(((s - lo) * (128 /
+ * (hi - lo))) * 128)), bin key >> 7, sub-bin key & 127; masses are summed
+ * exactly as integers in units of 2^-40; the target is floor(recall x total).
+ * All clusters are taken when a row's scores are all equal or
+ * n_kc <= min_count.
+ *
+ * cent_q    float [B,H,n_qc,D], cent_k float [B,H,n_kc,D] (device).
+ * counts_k  int32 [B,H,n_kc]: key cluster sizes n_j (ca_cluster's counts).
+ * scale     tau of the mass estimate; 0 means 1/sqrt(D).
+ * recall    in [0, 1] (0: a pure count criterion).
+ * min_count >= 1 (16 in the pages' adaptive setting).
+ * blocks    out int32 [B,H,n_qc,n_kc]: row a holds its nsel[a] selected key
+ *           clusters in ascending order, then -1 up to n_kc.
+ * nsel      out int32 [B,H,n_qc]: the number selected.
+ * scores    out float [B,H,n_qc,n_kc] or NULL (then the workspace holds it;
+ *           its size is that of CA_OP_ROUTE).
+ * Errors as ca_route; CA_ERR_INVALID_ARG for recall outside [0, 1],
+ * min_count < 1, a negative or non-finite scale.
+ */
+int ca_route_adaptive(const float* cent_q, const float* cent_k, const int32_t* counts_k, int B,
+                      int H, int n_qc, int n_kc, int D, float scale, float recall, int min_count,
+                      int32_t* blocks, int32_t* nsel, float* scores, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
  * ca_attend -- block-sparse attention over the selected clusters with
  * optional striped mean-compensation (v1 §1.2 Eq. 2 and Eq. 5-6; App. A
  * Eq. 21-22; v1 §3.1 on the padded remainder cluster).
@@ -195,6 +233,23 @@ int ca_attend(const void* Q, const void* K, const void* V, ca_dtype dt, int B, i
               int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
               const int32_t* blocks, int topk, int compensate, float scale, void* O,
               float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ca_attend_var -- ca_attend with a variable number of selected clusters per
+ * query cluster (the output of ca_route_adaptive; v1 §3.3.2).
+ *
+ * blocks    int32 [B,H,n_c,max_sel]: row a holds nsel[a] distinct key
+ *           clusters in [0, n_c); entries past nsel[a] are not read.
+ * nsel      int32 [B,H,n_c] (device): 1 <= nsel[a] <= max_sel (values
+ *           outside [0, max_sel] are clamped to it).
+ * max_sel   row stride of blocks, 1 <= max_sel <= n_c.
+ * Every other argument, the workspace (CA_OP_ATTEND) and the errors are
+ * those of ca_attend; CA_ERR_INVALID_ARG also for a null nsel.
+ */
+int ca_attend_var(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
+                  int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
+                  const int32_t* blocks, const int32_t* nsel, int max_sel, int compensate,
+                  float scale, void* O, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * ca_dense -- dense attention baseline, o_i = sum_j softmax_j(scale q_i.k_j) v_j

@@ -123,6 +123,30 @@ def test_route_and_dense_reject_bad_arguments(lib):
     assert lib.ca_dense(FAKE, FAKE, FAKE, 0, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 8, None) == 3
 
 
+def test_adaptive_route_and_ragged_attend_reject_bad_arguments(lib):
+    ra = lib.ca_route_adaptive
+    # cent_q, cent_k, counts, B, H, n_qc, n_kc, D, scale, recall, min_count, blocks, nsel, scores, ws
+    assert ra(FAKE, FAKE, None, 1, 1, 8, 8, 64, 0.0, 0.9, 16, FAKE, FAKE, None, FAKE, 1 << 20, None) == 1
+    assert ra(FAKE, FAKE, FAKE, 1, 1, 8, 8, 64, 0.0, 1.5, 16, FAKE, FAKE, None, FAKE, 1 << 20, None) == 1
+    assert ra(FAKE, FAKE, FAKE, 1, 1, 8, 8, 64, 0.0, -0.1, 16, FAKE, FAKE, None, FAKE, 1 << 20, None) == 1
+    assert ra(FAKE, FAKE, FAKE, 1, 1, 8, 8, 64, 0.0, 0.9, 0, FAKE, FAKE, None, FAKE, 1 << 20, None) == 1
+    assert ra(FAKE, FAKE, FAKE, 1, 1, 8, 8, 64, -1.0, 0.9, 16, FAKE, FAKE, None, FAKE, 1 << 20, None) == 1
+    assert ra(FAKE, FAKE, FAKE, 1, 1, 8, 8, 96, 0.0, 0.9, 16, FAKE, FAKE, None, FAKE, 1 << 20, None) == 2
+    assert ra(FAKE, FAKE, FAKE, 1, 1, 8, 9000, 64, 0.0, 0.9, 16, FAKE, FAKE, None, FAKE, 1 << 20, None) == 2
+    assert ra(FAKE, FAKE, FAKE, 1, 1, 8, 8, 64, 0.0, 0.9, 16, FAKE, None, None, FAKE, 1 << 20, None) == 1
+    assert ra(FAKE, FAKE, FAKE, 1, 1, 8, 8, 64, 0.0, 0.9, 16, FAKE, FAKE, None, FAKE, 16, None) == 3
+    av = lib.ca_attend_var
+    # Q, K, V, dt, B, H, N, D, perm_q, perm_k, c, blocks, nsel, max_sel, comp, scale, O, lse, ws
+    assert av(FAKE, FAKE, FAKE, 0, 1, 1, 1024, 64, FAKE, FAKE, 64, FAKE, None, 4, 1, 0.0, FAKE, None,
+              FAKE, 1 << 30, None) == 1
+    assert av(FAKE, FAKE, FAKE, 0, 1, 1, 1024, 64, FAKE, FAKE, 64, FAKE, FAKE, 17, 1, 0.0, FAKE,
+              None, FAKE, 1 << 30, None) == 1
+    assert av(FAKE, FAKE, FAKE, 0, 1, 1, 1024, 64, FAKE, FAKE, 64, FAKE, FAKE, 0, 1, 0.0, FAKE,
+              None, FAKE, 1 << 30, None) == 1
+    assert av(FAKE, FAKE, FAKE, 0, 1, 1, 1024, 64, FAKE, FAKE, 64, FAKE, FAKE, 4, 1, 0.0, FAKE,
+              None, FAKE, 10, None) == 3
+
+
 def test_peak_probe_rejects_bad_arguments(lib):
     assert lib.ca_peak_probe(2, 1, 1, FAKE, None) == 1
     assert lib.ca_peak_probe(0, 0, 1, FAKE, None) == 1
