@@ -204,7 +204,9 @@ def measure_peaks(torch, dev):
 def sweep(args, torch, synth, ca):
     """Error against dense attention and latency over cluster size c in {64, 128, 256},
     selected fraction k/n_c in {1/4, 1/8, 1/16}, SMC off/on, for the learned
-    (PDDP) clusters and for seeded random clusters of the same sizes."""
+    (PDDP) clusters and for seeded random clusters of the same sizes; then
+    adaptive selection at mass recalls {0.6, 0.8, 0.9, 0.95, 0.99} (minimum
+    count 16), SMC off/on."""
     dev = torch.device("cuda:0")
 
     def timed(fn, reps=3):
@@ -257,6 +259,29 @@ def sweep(args, torch, synth, ca):
                                           "cos_vs_dense": round(cos, 5), "ms": round(ms, 4),
                                           "dense_ms": round(dense_ms, 4),
                                           "speedup_vs_dense": round(dense_ms / ms, 3)}), flush=True)
+            # adaptive selection to a mass recall (queries clustered unnormalised)
+            for recall in (0.6, 0.8, 0.9, 0.95, 0.99):
+                for smc in (False, True):
+                    sel = {}
+
+                    def run_ada():
+                        cr = ca.cluster(Q, K, c, seed=w.cluster_seed, query_normalize=False)
+                        bl, ns = ca.route_adaptive(cr.cent_q, cr.cent_k, cr.counts, recall,
+                                                   min_count=16)
+                        sel["n"] = ns
+                        return ca.attend(Q, K, V, cr.perm_q, cr.perm_k, c, bl, compensate=smc,
+                                         nsel=ns)
+                    O, ms = timed(run_ada)
+                    Of = O.float()
+                    rel = torch.linalg.vector_norm(Of - Odf).item() / nd
+                    cos = torch.nn.functional.cosine_similarity(Of, Odf, dim=-1).mean().item()
+                    frac = sel["n"].float().mean().item() / n_c
+                    print(json.dumps({"sweep": w.name, "clusters": "pddp", "assign": "adaptive",
+                                      "c": c, "recall": recall, "selected_fraction": round(frac, 4),
+                                      "smc": smc, "rel_err_vs_dense": round(rel, 5),
+                                      "cos_vs_dense": round(cos, 5), "ms": round(ms, 4),
+                                      "dense_ms": round(dense_ms, 4),
+                                      "speedup_vs_dense": round(dense_ms / ms, 3)}), flush=True)
 
 
 def main():
