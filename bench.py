@@ -91,6 +91,8 @@ def parse():
                     help="skip the copy and GEMM rate measurements")
     ap.add_argument("--split-mode", choices=["power", "diag"], default="power",
                     help="basic (power iteration) or diagonalized recursive splitting")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph and replayed")
     ap.add_argument("--assign", choices=["topk", "adaptive"], default="topk",
                     help="top-k selection, or adaptive selection to a mass recall")
     ap.add_argument("--recall", type=float, default=0.9, help="mass recall of --assign adaptive")
@@ -386,6 +388,27 @@ def main():
     flops_attn = 4.0 * D * (tok_inter + cen_inter)
     achieved = flops_attn / (t_attn_kernel * 1e-3) / 1e12
 
+    # the same step captured once in a HIP graph (fixed shapes) and replayed
+    graph_ms = None
+    if args.graph:
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            step()
+        torch.cuda.current_stream().wait_stream(gs)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - tg) / args.steps * 1e3
+        del graph
+
     # the same step with every cache flushed first (HIP events around the step only)
     cold_ms = []
     if args.cold_steps > 0:
@@ -438,7 +461,8 @@ def main():
                      "step_median": round(float(np.median(step_ms)), 4),
                      "step_p10": round(float(np.percentile(step_ms, 10)), 4),
                      "step_p90": round(float(np.percentile(step_ms, 90)), 4),
-                     "cold_step_median": round(float(np.median(cold_ms)), 4) if cold_ms else None},
+                     "cold_step_median": round(float(np.median(cold_ms)), 4) if cold_ms else None,
+                     "graph_replay": round(graph_ms, 4) if graph_ms is not None else None},
         "roofline": {
             "kernel": "attn_fwd (block-sparse attention + SMC)",
             "bound": "mfma",
