@@ -23,7 +23,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libca.so")
 EXPORTS = ["ca_tree_levels", "ca_workspace_size", "ca_cluster", "ca_route", "ca_route_adaptive",
-           "ca_attend", "ca_attend_var", "ca_dense", "ca_profile_events", "ca_peak_probe",
+           "ca_attend", "ca_attend_var", "ca_attend_ex", "ca_dense", "ca_profile_events", "ca_peak_probe",
            "ca_status_string", "ca_last_error"]
 
 CA_BF16, CA_F32 = 0, 1
@@ -43,7 +43,8 @@ class _Opts(ctypes.Structure):
                 ("power_iters", ctypes.c_int), ("sample_factor", ctypes.c_int),
                 ("seed", ctypes.c_uint64), ("trace_perm", ctypes.c_void_p),
                 ("trace_score", ctypes.c_void_p), ("trace_dir", ctypes.c_void_p),
-                ("split_mode", ctypes.c_int), ("trace_basis", ctypes.c_void_p)]
+                ("split_mode", ctypes.c_int), ("trace_basis", ctypes.c_void_p),
+                ("cluster_size_k", ctypes.c_int)]
 
 _SPLIT_MODES = {"power": 0, "diag": 1}
 
@@ -71,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.ca_attend.restype = I
     lib.ca_attend_var.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I, I, F, P, P, P, S, P]
     lib.ca_attend_var.restype = I
+    lib.ca_attend_ex.argtypes = [P, P, P, I, I, I, I, I, P, P, I, I, P, P, I, I, F, P, P, P, S, P]
+    lib.ca_attend_ex.restype = I
     lib.ca_dense.argtypes = [P, P, P, I, I, I, I, I, F, P, P, P, S, P]
     lib.ca_dense.restype = I
     lib.ca_peak_probe.argtypes = [I, I, I, P, P]
@@ -206,24 +209,27 @@ class ClusterResult:
 
 def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = True,
             power_iters: int = 8, sample_factor: int = 1, seed: int = 0,
-            split_mode: str = "power", trace: bool = False, workspace=None) -> ClusterResult:
+            split_mode: str = "power", cluster_size_k: int = 0, trace: bool = False,
+            workspace=None) -> ClusterResult:
     """ca_cluster: permutations into clusters of size c and the cluster centroids.
 
     split_mode "power" is basic recursive splitting (power iteration per node),
     "diag" diagonalized recursive splitting (one principal-component basis per
-    tree, each node splits along its highest-variance coordinate)."""
+    tree, each node splits along its highest-variance coordinate).
+    cluster_size_k (0: c) clusters the keys with their own size."""
     if split_mode not in _SPLIT_MODES:
         raise ValueError(f"split_mode must be one of {sorted(_SPLIT_MODES)}")
     torch = _torch()
     _bhnd(Q, K)
     B, H, N, D = Q.shape
     dev = Q.device
-    n_c = -(-N // c)
+    ck = cluster_size_k or c
+    n_c, n_kc = -(-N // c), -(-N // ck)
     perm_q = torch.empty((B, H, N), dtype=torch.int32, device=dev)
     perm_k = torch.empty_like(perm_q)
     cent_q = torch.empty((B, H, n_c, D), dtype=torch.float32, device=dev)
-    cent_k = torch.empty_like(cent_q)
-    counts = torch.empty((B, H, n_c), dtype=torch.int32, device=dev)
+    cent_k = torch.empty((B, H, n_kc, D), dtype=torch.float32, device=dev)
+    counts = torch.empty((B, H, n_kc), dtype=torch.int32, device=dev)
     tp = ts = td = tb = None
     if trace:
         L = tree_levels(N, c)
@@ -235,8 +241,9 @@ def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = Tru
             tb = torch.full((B * H, 2, D, D), float("nan"), dtype=torch.float32, device=dev)
     opts = _Opts(int(transform), int(query_normalize), power_iters, sample_factor,
                  seed & ((1 << 64) - 1), _ptr(tp), _ptr(ts), _ptr(td),
-                 _SPLIT_MODES[split_mode], _ptr(tb))
-    nbytes = workspace_size(OP_CLUSTER_DIAG if split_mode == "diag" else OP_CLUSTER, B, H, N, D, c)
+                 _SPLIT_MODES[split_mode], _ptr(tb), int(cluster_size_k))
+    nbytes = workspace_size(OP_CLUSTER_DIAG if split_mode == "diag" else OP_CLUSTER, B, H, N, D,
+                            min(c, ck))
     ws = _ws(nbytes, dev, workspace)
     st = load().ca_cluster(Q.data_ptr(), K.data_ptr(), _dtype_code(Q), B, H, N, D, c,
                            ctypes.byref(opts), perm_q.data_ptr(), perm_k.data_ptr(),
@@ -286,9 +293,11 @@ def route_adaptive(cent_q, cent_k, counts_k, recall: float, *, min_count: int = 
 
 
 def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
-           scale: float = 0.0, return_lse: bool = False, nsel=None, workspace=None):
+           scale: float = 0.0, return_lse: bool = False, nsel=None, c_k: int = 0,
+           workspace=None):
     """ca_attend: block-sparse attention with optional mean-compensation;
-    with `nsel` (selected count per row of `blocks`), ca_attend_var."""
+    with `nsel` (selected count per row of `blocks`), ca_attend_var; with key
+    clusters of another size c_k than the query clusters' c, ca_attend_ex."""
     torch = _torch()
     _bhnd(Q, K, V)
     B, H, N, D = Q.shape
@@ -296,9 +305,15 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
     O = torch.empty_like(Q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
     topk = blocks.shape[-1]
-    nbytes = workspace_size(OP_ATTEND, B, H, N, D, c, topk)
+    ck = c_k or c
+    nbytes = workspace_size(OP_ATTEND, B, H, N, D, ck, topk)
     ws = _ws(nbytes, dev, workspace)
-    if nsel is None:
+    if ck != c:
+        st = load().ca_attend_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N,
+                                 D, perm_q.data_ptr(), perm_k.data_ptr(), c, ck, blocks.data_ptr(),
+                                 _ptr(nsel), topk, int(compensate), float(scale), O.data_ptr(),
+                                 _ptr(lse), _ptr(ws), nbytes, _stream_ptr(dev))
+    elif nsel is None:
         st = load().ca_attend(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, D,
                               perm_q.data_ptr(), perm_k.data_ptr(), c, blocks.data_ptr(), topk,
                               int(compensate), float(scale), O.data_ptr(), _ptr(lse), _ptr(ws),

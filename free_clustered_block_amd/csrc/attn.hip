@@ -181,22 +181,22 @@ CA_DEV int xcd_logical(int b, int G) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
-template <int D, int C, bool DENSE>
-__global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd(AttnArgs a) {
+template <int D, int CQ, int CK, bool DENSE>
+__global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd(AttnArgs a) {
   using TL = AttnTile<D>;
-  constexpr int NT = 2 * C;            // threads (C/32 waves of 32 queries)
+  constexpr int NT = 2 * CQ;           // threads (CQ/32 waves of 32 queries)
   constexpr int KS = D / 16;           // k-steps over the head dim
   constexpr int NB = D / 32;           // 32-row blocks of O^T
-  constexpr int SUB = C / TL::KT;      // sub-tiles per key cluster
+  constexpr int SUB = CK / TL::KT;     // sub-tiles per key cluster
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint32_t* sSel = reinterpret_cast<uint32_t*>(smem + 2 * TL::BYTES);
 
   const int G = gridDim.x * gridDim.y;
   const int lg = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, G);
-  const int nc = a.nc, N = a.N;
-  const int qa = lg % nc, bh = lg / nc;
+  const int nc = a.nc, nqc = a.nqc, N = a.N;   // key clusters, query clusters
+  const int qa = lg % nqc, bh = lg / nqc;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
-  const int qpos = qa * C + w * 32 + r;
+  const int qpos = qa * CQ + w * 32 + r;
   const bool qvalid = qpos < N;
   const int qtok =
       qvalid ? (DENSE || !a.perm_q ? qpos : clamp_tok(a.perm_q[(int64_t)bh * N + qpos], N)) : 0;
@@ -216,8 +216,8 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   const float sl2 = a.scale * kLog2e;
 
   const int nsel = DENSE ? nc
-                  : (a.nsel ? min(max(a.nsel[(int64_t)bh * nc + qa], 0), a.topk) : a.topk);
-  const int32_t* blk = DENSE ? nullptr : a.blocks + ((int64_t)bh * nc + qa) * a.topk;
+                  : (a.nsel ? min(max(a.nsel[(int64_t)bh * nqc + qa], 0), a.topk) : a.topk);
+  const int32_t* blk = DENSE ? nullptr : a.blocks + ((int64_t)bh * nqc + qa) * a.topk;
   // Token sub-tiles of the selected clusters come first; with compensation the
   // centroids follow as ncp / 64 more sub-tiles of 64 (kbar rows as keys,
   // vbar as values) whose logits get + ln n_c, or -inf for a selected or
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
       int j = tile_cluster(t);
       if (j < 0) j = 0;   // any valid tile; its results are not used
       const int part = t % SUB;
-      ks = reinterpret_cast<const u32x4_t*>(a.kc + (((int64_t)bh * nc + j) * C + part * TL::KT) * D);
+      ks = reinterpret_cast<const u32x4_t*>(a.kc + (((int64_t)bh * nc + j) * CK + part * TL::KT) * D);
       vs = reinterpret_cast<const u32x4_t*>(a.vt + (((int64_t)bh * nc + j) * SUB + part) * (int64_t)D * TL::KT);
     } else {
       const int ct = t - Tm;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
   // own; the sub-tiles of the short last cluster, wherever the selection
   // holds it, and the centroid tiles run in loops with the masking code.
   int rpos = -1;   // position of the short cluster in the selection, if any
-  if (N % C != 0) {
+  if (N % CK != 0) {
     if (DENSE) {
       rpos = nc - 1;
     } else {
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(2 * C) __attribute__((amdgpu_waves_per_eu(2))) void
     const int j = cen ? 0 : tile_cluster(t);
     if (j >= 0) {
       const unsigned char* buf = smem + (t & 1) * TL::BYTES;
-      const int nvalid = cen ? TL::KT : min(C, N - j * C) - (t % SUB) * TL::KT;
+      const int nvalid = cen ? TL::KT : min(CK, N - j * CK) - (t % SUB) * TL::KT;
       // two independent accumulation chains (keys 0-31, 32-63) interleaved
       floatx16_t sacc[2] = {zero16(), zero16()};
       {
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
   __shared__ float skv[2][32][D];
   __shared__ uint32_t sSel[8192 / 32];
   const int qa = blockIdx.x, bh = blockIdx.y;
-  const int N = a.N, nc = a.nc, c = a.c;
+  const int N = a.N, nc = a.nc, c = a.c, cq = a.cq, nqc = a.nqc;
   const int tid = threadIdx.x;
   const int qpos = qa * 256 + tid;                   // DENSE: 256 queries per block
   int qtok = 0;
@@ -505,9 +505,9 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
     qvalid = qpos < N;
     qtok = qpos;
   } else {
-    const int nq = min(c, N - qa * c);
+    const int nq = min(cq, N - qa * cq);
     qvalid = tid < nq;
-    if (qvalid) qtok = clamp_tok(a.perm_q[(int64_t)bh * N + qa * c + tid], N);
+    if (qvalid) qtok = clamp_tok(a.perm_q[(int64_t)bh * N + qa * cq + tid], N);
   }
   const float* Qh = (const float*)a.Q + (int64_t)bh * N * D;
   const float* Kh = (const float*)a.K + (int64_t)bh * N * D;
@@ -525,9 +525,9 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
   };
   // key tokens, 32 at a time through LDS
   const int nsel = DENSE ? 1
-                  : (a.nsel ? min(max(a.nsel[(int64_t)bh * nc + qa], 0), a.topk) : a.topk);
+                  : (a.nsel ? min(max(a.nsel[(int64_t)bh * nqc + qa], 0), a.topk) : a.topk);
   for (int bi = 0; bi < nsel; ++bi) {
-    const int j = DENSE ? 0 : a.blocks[((int64_t)bh * nc + qa) * a.topk + bi];
+    const int j = DENSE ? 0 : a.blocks[((int64_t)bh * nqc + qa) * a.topk + bi];
     if (j < 0 || j >= nc) continue;
     const int kbeg = DENSE ? 0 : j * c;
     const int kcnt = DENSE ? N : min(c, N - j * c);
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
     for (int e = tid; e < ncp / 32; e += 256) sSel[e] = 0u;
     __syncthreads();
     for (int e = tid; e < nsel; e += 256) {
-      const int j = a.blocks[((int64_t)bh * nc + qa) * a.topk + e];
+      const int j = a.blocks[((int64_t)bh * nqc + qa) * a.topk + e];
       if (j >= 0 && j < nc) atomicOr(&sSel[j >> 5], 1u << (j & 31));
     }
     __syncthreads();
@@ -577,18 +577,18 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
   if (a.lse) a.lse[(int64_t)bh * N + qtok] = m + logf(lsum);
 }
 
-template <int D, int C, bool DENSE>
+template <int D, int CQ, int CK, bool DENSE>
 void launch_mfma(const AttnArgs& a, hipStream_t st) {
-  const size_t sm = attn_smem<D, C>();
+  const size_t sm = attn_smem<D, CQ>();
   static bool attr_set = false;   // raise the dynamic-LDS limit once per instantiation
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd<D, C, DENSE>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd<D, CQ, CK, DENSE>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     attr_set = true;
   }
-  dim3 g(a.nc, a.BH);
+  dim3 g(a.nqc, a.BH);
   if (a.ev_start) (void)hipEventRecord(a.ev_start, st);
-  attn_fwd<D, C, DENSE><<<g, 2 * C, sm, st>>>(a);
+  attn_fwd<D, CQ, CK, DENSE><<<g, 2 * CQ, sm, st>>>(a);
   if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);
 }
 
@@ -597,13 +597,17 @@ void launch_bf16(const AttnArgs& a, bool dense, hipStream_t st) {
   dim3 gp(attn_ncp(a.nc), a.BH);
   permute_kv<D><<<gp, 256, 0, st>>>(a);
   if (dense) {
-    launch_mfma<D, 128, true>(a, st);
+    launch_mfma<D, 128, 128, true>(a, st);
     return;
   }
-  switch (a.c) {
-    case 64: launch_mfma<D, 64, false>(a, st); break;
-    case 128: launch_mfma<D, 128, false>(a, st); break;
-    default: launch_mfma<D, 256, false>(a, st); break;
+  // (query, key) cluster sizes: equal, or the key clusters larger
+  switch (a.cq * 1000 + a.c) {
+    case 64064: launch_mfma<D, 64, 64, false>(a, st); break;
+    case 64128: launch_mfma<D, 64, 128, false>(a, st); break;
+    case 64256: launch_mfma<D, 64, 256, false>(a, st); break;
+    case 128128: launch_mfma<D, 128, 128, false>(a, st); break;
+    case 128256: launch_mfma<D, 128, 256, false>(a, st); break;
+    default: launch_mfma<D, 256, 256, false>(a, st); break;
   }
 }
 
@@ -618,7 +622,7 @@ void launch_f32(const AttnArgs& a, bool dense, hipStream_t st) {
   }
   dim3 gc(attn_ncp(a.nc), a.BH);
   centroids_kv_f32<D><<<gc, 256, 0, st>>>(a);
-  dim3 g(a.nc, a.BH);
+  dim3 g(a.nqc, a.BH);
   if (a.ev_start) (void)hipEventRecord(a.ev_start, st);
   attn_f32<D, false><<<g, 256, 0, st>>>(a);
   if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);

@@ -197,8 +197,13 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   if (!supported_c(c)) return fail(CA_ERR_UNSUPPORTED, "cluster_size must be 64, 128 or 256");
   if (N < c) return fail(CA_ERR_INVALID_ARG, "N must be >= cluster_size");
   if ((N + c - 1) / c > 8192) return fail(CA_ERR_UNSUPPORTED, "at most 8192 clusters");
-  ca_cluster_opts o = {1, 1, 8, 1, 0, nullptr, nullptr, nullptr, 0, nullptr};
+  ca_cluster_opts o = {1, 1, 8, 1, 0, nullptr, nullptr, nullptr, 0, nullptr, 0};
   if (opts) o = *opts;
+  const int ck = o.cluster_size_k ? o.cluster_size_k : c;   // key cluster size
+  if (!supported_c(ck)) return fail(CA_ERR_UNSUPPORTED, "cluster_size_k must be 0, 64, 128 or 256");
+  if (N < ck) return fail(CA_ERR_INVALID_ARG, "N must be >= cluster_size_k");
+  if (ck != c && (o.trace_perm || o.trace_score || o.trace_dir))
+    return fail(CA_ERR_UNSUPPORTED, "traces need equal query and key cluster sizes");
   if (o.split_mode != 0 && o.split_mode != 1)
     return fail(CA_ERR_INVALID_ARG, "split_mode must be 0 (power iteration) or 1 (diagonalized)");
   if (o.power_iters < 1 || o.power_iters > 1000)
@@ -208,10 +213,9 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   if ((2 * B * H) > 65535) return fail(CA_ERR_UNSUPPORTED, "2*B*H must be <= 65535");
   const int BH = B * H;
   Carver cv(ws);
-  ClusterWs w = plan_cluster(cv, BH, N, D, c, o.split_mode == 1);
+  ClusterWs w = plan_cluster(cv, BH, N, D, c < ck ? c : ck, o.split_mode == 1);
   if (int e = check_ws(ws, ws_bytes, cv.size())) return e;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int L = tree_levels_host(N, c);
   const size_t TN = 2 * (size_t)BH * N;
 
   launch_metric(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, o.transform, o.query_normalize, w.partial,
@@ -225,37 +229,54 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     launch_rotate(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, w.s, w.At, w.At3, w.Y, st);
   }
   launch_perm_init(w.permA, 2 * BH, N, st);
-  int32_t* cur = w.permA;
-  int32_t* nxt = w.permB;
-  uint64_t* hcur = w.hash;
-  uint64_t* hnxt = w.hashB;
-  for (int level = 0; level < L; ++level) {
+  // the split levels of a set of trees (every tree when c_q == c_k, else one
+  // tensor's trees at a time with its own cluster size); returns the
+  // permutation array that holds their final order in `fin`
+  auto run_levels = [&](int ct, int step, int base, int32_t*& fin) -> int {
+    const int L = tree_levels_host(N, ct);
+    int32_t* cur = w.permA;
+    int32_t* nxt = w.permB;
+    uint64_t* hcur = w.hash;
+    uint64_t* hnxt = w.hashB;
+    for (int level = 0; level < L; ++level) {
+      if (o.trace_perm)
+        CA_HIP_CHECK(hipMemcpyAsync(o.trace_perm + level * TN, cur, TN * 4, hipMemcpyDeviceToDevice, st));
+      LevelArgs a;
+      a.Q = Q; a.K = K; a.dtype = dt == CA_BF16 ? 0 : 1;
+      a.BH = BH; a.N = N; a.D = D; a.c = ct; a.level = level;
+      a.transform = o.transform; a.power_iters = o.power_iters; a.sample_factor = o.sample_factor;
+      a.split_mode = o.split_mode; a.basis = w.At; a.Y = w.Y; a.jsel = w.jsel;
+      a.tree_step = step; a.tree_base = base;
+      a.seed = o.seed;
+      a.perm_in = cur; a.perm_out = nxt;
+      a.hpos_in = hcur; a.hpos_out = hnxt; a.s = w.s; a.Mq = w.Mq; a.Mk = w.Mk; a.Mpk = w.Mpk;
+      a.dir_prev = (level & 1) ? w.dirA : w.dirB;
+      a.dir_cur = (level & 1) ? w.dirB : w.dirA;
+      a.nchunks = (N + ct - 1) / ct;
+      a.sample_buf = w.sample; a.chunk_cnt = w.chunk_cnt; a.zbuf_tok = w.stok;
+      a.zbuf = w.zbuf; a.keys = w.keys;
+      a.trace_score = o.trace_score ? o.trace_score + level * TN : nullptr;
+      a.trace_slots = L > 0 ? (1 << (L - 1)) : 1;
+      a.trace_dir = o.trace_dir ? o.trace_dir + (size_t)level * 2 * BH * a.trace_slots * D : nullptr;
+      launch_level(a, st);
+      int32_t* t = cur; cur = nxt; nxt = t;
+      uint64_t* th = hcur; hcur = hnxt; hnxt = th;
+    }
     if (o.trace_perm)
-      CA_HIP_CHECK(hipMemcpyAsync(o.trace_perm + level * TN, cur, TN * 4, hipMemcpyDeviceToDevice, st));
-    LevelArgs a;
-    a.Q = Q; a.K = K; a.dtype = dt == CA_BF16 ? 0 : 1;
-    a.BH = BH; a.N = N; a.D = D; a.c = c; a.level = level;
-    a.transform = o.transform; a.power_iters = o.power_iters; a.sample_factor = o.sample_factor;
-    a.split_mode = o.split_mode; a.basis = w.At; a.Y = w.Y; a.jsel = w.jsel;
-    a.seed = o.seed;
-    a.perm_in = cur; a.perm_out = nxt;
-    a.hpos_in = hcur; a.hpos_out = hnxt; a.s = w.s; a.Mq = w.Mq; a.Mk = w.Mk; a.Mpk = w.Mpk;
-    a.dir_prev = (level & 1) ? w.dirA : w.dirB;
-    a.dir_cur = (level & 1) ? w.dirB : w.dirA;
-    a.nchunks = (N + c - 1) / c;
-    a.sample_buf = w.sample; a.chunk_cnt = w.chunk_cnt; a.zbuf_tok = w.stok;
-    a.zbuf = w.zbuf; a.keys = w.keys;
-    a.trace_score = o.trace_score ? o.trace_score + level * TN : nullptr;
-    a.trace_slots = L > 0 ? (1 << (L - 1)) : 1;
-    a.trace_dir = o.trace_dir ? o.trace_dir + (size_t)level * 2 * BH * a.trace_slots * D : nullptr;
-    launch_level(a, st);
-    int32_t* t = cur; cur = nxt; nxt = t;
-    uint64_t* th = hcur; hcur = hnxt; hnxt = th;
+      CA_HIP_CHECK(hipMemcpyAsync(o.trace_perm + (size_t)L * TN, cur, TN * 4, hipMemcpyDeviceToDevice, st));
+    fin = cur;
+    return 0;
+  };
+  int32_t *fin_q = nullptr, *fin_k = nullptr;
+  if (ck == c) {
+    if (int e = run_levels(c, 1, 0, fin_q)) return e;
+    fin_k = fin_q;
+  } else {
+    if (int e = run_levels(c, 2, 0, fin_q)) return e;
+    if (int e = run_levels(ck, 2, 1, fin_k)) return e;
   }
-  if (o.trace_perm)
-    CA_HIP_CHECK(hipMemcpyAsync(o.trace_perm + (size_t)L * TN, cur, TN * 4, hipMemcpyDeviceToDevice, st));
-  launch_perm_out(cur, BH, N, perm_q, perm_k, st);
-  launch_centroids(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, c, perm_q, perm_k, cent_q, cent_k,
+  launch_perm_out(fin_q, fin_k, BH, N, perm_q, perm_k, st);
+  launch_centroids(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, c, ck, perm_q, perm_k, cent_q, cent_k,
                    counts, st);
   return after_launch();
 }
@@ -309,23 +330,27 @@ int ca_route_adaptive(const float* cent_q, const float* cent_k, const int32_t* c
 
 namespace {
 int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
-                int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
-                const int32_t* blocks, const int32_t* nsel, int topk, int compensate, float scale,
-                void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size_q,
+                int cluster_size_k, const int32_t* blocks, const int32_t* nsel, int topk,
+                int compensate, float scale, void* O, float* lse, void* ws, size_t ws_bytes,
+                void* stream) {
   set_error("");
   if (!Q || !K || !V || !perm_q || !perm_k || !blocks || !O)
     return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
   if (int e = check_common(dt, B, H, N, D)) return e;
-  const int c = cluster_size;
-  if (!supported_c(c)) return fail(CA_ERR_UNSUPPORTED, "cluster_size must be 64, 128 or 256");
-  if (N < c) return fail(CA_ERR_INVALID_ARG, "N must be >= cluster_size");
-  const int nc = (N + c - 1) / c;
-  if (nc > 8192) return fail(CA_ERR_UNSUPPORTED, "at most 8192 clusters");
-  if (topk < 1 || topk > nc) return fail(CA_ERR_INVALID_ARG, "topk must be in [1, n_c]");
+  const int c = cluster_size_k, cq = cluster_size_q;
+  if (!supported_c(c) || !supported_c(cq))
+    return fail(CA_ERR_UNSUPPORTED, "cluster sizes must be 64, 128 or 256");
+  if (cq > c) return fail(CA_ERR_UNSUPPORTED, "the query cluster size must not exceed the key cluster size");
+  if (N < c) return fail(CA_ERR_INVALID_ARG, "N must be >= the cluster sizes");
+  const int nc = (N + c - 1) / c, nqc = (N + cq - 1) / cq;
+  if (nc > 8192) return fail(CA_ERR_UNSUPPORTED, "at most 8192 key clusters");
+  if ((int64_t)nqc * B * H > 0x7FFFFFFF / 2) return fail(CA_ERR_UNSUPPORTED, "too many query clusters");
+  if (topk < 1 || topk > nc) return fail(CA_ERR_INVALID_ARG, "topk must be in [1, n_kc]");
   if (!(scale >= 0.0f) || !std::isfinite(scale)) return fail(CA_ERR_INVALID_ARG, "scale must be finite and >= 0");
   AttnArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : 1;
-  a.BH = B * H; a.N = N; a.D = D; a.c = c; a.nc = nc; a.topk = topk;
+  a.BH = B * H; a.N = N; a.D = D; a.c = c; a.nc = nc; a.cq = cq; a.nqc = nqc; a.topk = topk;
   a.compensate = compensate ? 1 : 0;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
   a.perm_q = perm_q; a.perm_k = perm_k; a.blocks = blocks; a.nsel = nsel; a.O = O; a.lse = lse;
@@ -342,8 +367,8 @@ int ca_attend(const void* Q, const void* K, const void* V, ca_dtype dt, int B, i
               const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
               const int32_t* blocks, int topk, int compensate, float scale, void* O, float* lse,
               void* ws, size_t ws_bytes, void* stream) {
-  return attend_impl(Q, K, V, dt, B, H, N, D, perm_q, perm_k, cluster_size, blocks, nullptr, topk,
-                     compensate, scale, O, lse, ws, ws_bytes, stream);
+  return attend_impl(Q, K, V, dt, B, H, N, D, perm_q, perm_k, cluster_size, cluster_size, blocks,
+                     nullptr, topk, compensate, scale, O, lse, ws, ws_bytes, stream);
 }
 
 int ca_attend_var(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
@@ -354,8 +379,17 @@ int ca_attend_var(const void* Q, const void* K, const void* V, ca_dtype dt, int 
     set_error("");
     return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
   }
-  return attend_impl(Q, K, V, dt, B, H, N, D, perm_q, perm_k, cluster_size, blocks, nsel, max_sel,
-                     compensate, scale, O, lse, ws, ws_bytes, stream);
+  return attend_impl(Q, K, V, dt, B, H, N, D, perm_q, perm_k, cluster_size, cluster_size, blocks,
+                     nsel, max_sel, compensate, scale, O, lse, ws, ws_bytes, stream);
+}
+
+int ca_attend_ex(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
+                 int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size_q,
+                 int cluster_size_k, const int32_t* blocks, const int32_t* nsel, int max_sel,
+                 int compensate, float scale, void* O, float* lse, void* ws, size_t ws_bytes,
+                 void* stream) {
+  return attend_impl(Q, K, V, dt, B, H, N, D, perm_q, perm_k, cluster_size_q, cluster_size_k,
+                     blocks, nsel, max_sel, compensate, scale, O, lse, ws, ws_bytes, stream);
 }
 
 int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N, int D,
@@ -367,6 +401,7 @@ int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, in
   AttnArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : 1;
   a.BH = B * H; a.N = N; a.D = D; a.c = kDenseTile; a.nc = (N + kDenseTile - 1) / kDenseTile;
+  a.cq = a.c; a.nqc = a.nc;
   a.topk = a.nc; a.compensate = 0;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
   a.O = O; a.lse = lse;

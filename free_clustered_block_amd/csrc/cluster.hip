@@ -33,7 +33,7 @@ constexpr int kSampleSpan = 1024;   // positions per workgroup (a multiple of ev
 
 __global__ __launch_bounds__(256) void pddp_sample(LevelArgs a) {
   __shared__ int wcnt[4];
-  const int tree = blockIdx.y;
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base;
   const int tensor = tree & 1;
   const int tid = threadIdx.x, w = tid >> 6;
   uint64_t salt = 0;
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void pddp_dir(LevelArgs a) {
   float* sred = spart + G * D;     // [16]
   int* spre = reinterpret_cast<int*>(sred + 16 + 16);   // chunk prefix sums [nch + 1]
 
-  const int tree = blockIdx.y, slot = blockIdx.x;
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base, slot = blockIdx.x;
   const int bh = tree >> 1, tensor = tree & 1;
   int off, n;
   if (!node_at(a.N, a.c, a.level, slot, &off, &n) || n <= a.c) return;
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256) void pddp_dir_y(LevelArgs a) {
   __shared__ double sp1[G * D], sp2[G * D];
   __shared__ int sred[16];
   extern __shared__ int spre[];   // [nch + 1]
-  const int tree = blockIdx.y, slot = blockIdx.x;
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base, slot = blockIdx.x;
   int off, n;
   if (!node_at(a.N, a.c, a.level, slot, &off, &n) || n <= a.c) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(256) void pddp_dir_y(LevelArgs a) {
 
 // Projection of diagonalized splitting: the chosen coordinate of each member.
 __global__ __launch_bounds__(256) void pddp_project_y(LevelArgs a) {
-  const int tree = blockIdx.y;
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base;
   const int p0 = blockIdx.x * a.c;
   int off, n, idx;
   const int depth = node_of(a.N, a.c, a.level, p0, &off, &n, &idx);
@@ -544,7 +544,7 @@ void pddp_dir_mma(LevelArgs a) {
   __shared__ int ired[NW];
   extern __shared__ int spre[];              // chunk prefix sums [nch + 1]
 
-  const int tree = blockIdx.y, slot = blockIdx.x;
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base, slot = blockIdx.x;
   const int bh = tree >> 1, tensor = tree & 1;
   int off, n;
   if (!node_at(a.N, a.c, a.level, slot, &off, &n) || n <= a.c) return;
@@ -839,7 +839,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void pddp_project(LevelArgs a) {
   constexpr int LPR = 4;                 // lanes per row
   constexpr int EPL = D / LPR;           // elements per lane
-  const int tree = blockIdx.y;
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base;
   const int bh = tree >> 1, tensor = tree & 1;
   const int p0 = blockIdx.x * a.c;
   int off, n, idx;
@@ -912,7 +912,7 @@ __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
   __shared__ int wtot[2][kSplitWaves];
   __shared__ uint32_t sel[4];
 
-  const int tree = blockIdx.y, slot = blockIdx.x;
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base, slot = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   // walk to the slot; find the segment this slot owns
   int o = 0, m = a.N, depth = 0;
@@ -1086,7 +1086,7 @@ CA_DEV void wave_sync() {
 __global__ __launch_bounds__(256) void pddp_split_small(LevelArgs a) {
   constexpr int KPL = kSmallNode / 64;   // keys per lane
   __shared__ int hist[4][256];
-  const int tree = blockIdx.y, w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base, w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int slot = blockIdx.x * 4 + w;
   if (slot >= (1 << a.level)) return;   // the whole wave
   int o = 0, m = a.N, depth = 0;
@@ -1211,12 +1211,13 @@ __global__ void perm_init(int32_t* perm, int trees, int N) {
   if (i < (int64_t)trees * N) perm[i] = (int32_t)(i % N);
 }
 
-__global__ void perm_out(const int32_t* perm, int BH, int N, int32_t* pq, int32_t* pk) {
+__global__ void perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N,
+                         int32_t* pq, int32_t* pk) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)BH * N) return;
   const int64_t bh = i / N, p = i % N;
-  pq[i] = perm[(2 * bh) * N + p];
-  pk[i] = perm[(2 * bh + 1) * N + p];
+  pq[i] = perm_qt[(2 * bh) * N + p];
+  pk[i] = perm_kt[(2 * bh + 1) * N + p];
 }
 
 // Means of the original rows of every cluster. Thread (row slot, group g)
@@ -1224,8 +1225,8 @@ __global__ void perm_out(const int32_t* perm, int BH, int N, int32_t* pq, int32_
 // of a group are then added in slot order.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void centroids_kernel(const T* __restrict__ Q,
-                                                        const T* __restrict__ K, int N, int c,
-                                                        const int32_t* __restrict__ pq,
+                                                        const T* __restrict__ K, int N, int c_q,
+                                                        int c_k, const int32_t* __restrict__ pq,
                                                         const int32_t* __restrict__ pk,
                                                         float* __restrict__ cq,
                                                         float* __restrict__ ck,
@@ -1236,7 +1237,9 @@ __global__ __launch_bounds__(256) void centroids_kernel(const T* __restrict__ Q,
   __shared__ float part[S][D + 1];
   __shared__ int stoks[256];
   const int j = blockIdx.x, bh = blockIdx.y, tensor = blockIdx.z;
+  const int c = tensor == 0 ? c_q : c_k;
   const int nc = (N + c - 1) / c;
+  if (j >= nc) return;
   const int nj = min(c, N - j * c);
   const T* X = (tensor == 0 ? Q : K) + (int64_t)bh * N * D;
   const int32_t* perm = (tensor == 0 ? pq : pk) + (int64_t)bh * N + (int64_t)j * c;
@@ -1270,7 +1273,7 @@ __global__ __launch_bounds__(256) void centroids_kernel(const T* __restrict__ Q,
     for (int q = 0; q < S; ++q) sum += part[q][tid];
     float* out = (tensor == 0 ? cq : ck) + ((int64_t)bh * nc + j) * D;
     out[tid] = sum / (float)nj;
-    if (tid == 0 && tensor == 0 && counts) counts[(int64_t)bh * nc + j] = nj;
+    if (tid == 0 && tensor == 1 && counts) counts[(int64_t)bh * nc + j] = nj;   // key clusters
   }
 }
 
@@ -1281,14 +1284,15 @@ void launch_perm_init(int32_t* perm, int trees, int N, hipStream_t st) {
   perm_init<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm, trees, N);
 }
 
-void launch_perm_out(const int32_t* perm, int BH, int N, int32_t* pq, int32_t* pk, hipStream_t st) {
+void launch_perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N, int32_t* pq,
+                     int32_t* pk, hipStream_t st) {
   const int64_t n = (int64_t)BH * N;
-  perm_out<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm, BH, N, pq, pk);
+  perm_out<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm_qt, perm_kt, BH, N, pq, pk);
 }
 
 template <typename T, int D>
 static void level_impl(const LevelArgs& a, hipStream_t st) {
-  const int trees = 2 * a.BH;
+  const int trees = a.tree_step == 1 ? 2 * a.BH : a.BH;   // every tree, or one tensor's
   dim3 gslots(1u << a.level, trees);
   dim3 gspan((a.N + kSampleSpan - 1) / kSampleSpan, trees);
   pddp_sample<<<gspan, 256, 0, st>>>(a);
@@ -1329,20 +1333,21 @@ void launch_level(const LevelArgs& a, hipStream_t st) {
   }
 }
 
-void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, int D, int c,
-                      const int32_t* pq, const int32_t* pk, float* cq, float* ck,
+void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, int D, int c_q,
+                      int c_k, const int32_t* pq, const int32_t* pk, float* cq, float* ck,
                       int32_t* counts, hipStream_t st) {
-  dim3 g((N + c - 1) / c, BH, 2);
+  const int cmin = c_q < c_k ? c_q : c_k;
+  dim3 g((N + cmin - 1) / cmin, BH, 2);
   if (dtype == 0) {
     const uint16_t* q = (const uint16_t*)Q;
     const uint16_t* k = (const uint16_t*)K;
-    if (D == 64) centroids_kernel<uint16_t, 64><<<g, 256, 0, st>>>(q, k, N, c, pq, pk, cq, ck, counts);
-    else centroids_kernel<uint16_t, 128><<<g, 256, 0, st>>>(q, k, N, c, pq, pk, cq, ck, counts);
+    if (D == 64) centroids_kernel<uint16_t, 64><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts);
+    else centroids_kernel<uint16_t, 128><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts);
   } else {
     const float* q = (const float*)Q;
     const float* k = (const float*)K;
-    if (D == 64) centroids_kernel<float, 64><<<g, 256, 0, st>>>(q, k, N, c, pq, pk, cq, ck, counts);
-    else centroids_kernel<float, 128><<<g, 256, 0, st>>>(q, k, N, c, pq, pk, cq, ck, counts);
+    if (D == 64) centroids_kernel<float, 64><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts);
+    else centroids_kernel<float, 128><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts);
   }
 }
 

@@ -20,6 +20,8 @@ struct LevelArgs {
   int BH, N, D, c, level;
   int transform, power_iters, sample_factor;
   int split_mode;           // 0 = power iteration, 1 = diagonalized (basis below)
+  int tree_step, tree_base; // trees of this launch: blockIdx.y * tree_step + tree_base
+                            // (1, 0: all 2 BH; 2, t: tensor t's BH trees)
   uint64_t seed;
   const int32_t* perm_in;   // [2 BH][N]
   int32_t* perm_out;        // [2 BH][N]
@@ -59,11 +61,15 @@ void launch_basis(const void* Q, int dtype, int BH, int N, int D, int transform,
 void launch_rotate(const void* Q, const void* K, int dtype, int BH, int N, int D, const float* s,
                    const float* At, uint16_t* At3, float* Y, hipStream_t st);
 void launch_perm_init(int32_t* perm, int trees, int N, hipStream_t st);
-void launch_perm_out(const int32_t* perm, int BH, int N, int32_t* perm_q, int32_t* perm_k,
-                     hipStream_t st);
-void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, int D, int c,
-                      const int32_t* perm_q, const int32_t* perm_k, float* cent_q, float* cent_k,
-                      int32_t* counts, hipStream_t st);
+// perm [2 BH][N] tree order -> perm_q, perm_k [BH][N]; the query trees are
+// read from perm_qt, the key trees from perm_kt
+void launch_perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N,
+                     int32_t* perm_q, int32_t* perm_k, hipStream_t st);
+// centroids of query clusters of size c_q and key clusters of size c_k;
+// counts (optional) = key cluster sizes
+void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, int D, int c_q,
+                      int c_k, const int32_t* perm_q, const int32_t* perm_k, float* cent_q,
+                      float* cent_k, int32_t* counts, hipStream_t st);
 
 // route.hip ------------------------------------------------------------------
 void launch_route(const float* cq, const float* ck, int BH, int nq, int nk, int D, int topk,
@@ -80,7 +86,8 @@ struct AttnArgs {
   const void* K;
   const void* V;
   int dtype;
-  int BH, N, D, c, nc, topk, compensate;
+  int BH, N, D, c, nc, topk, compensate;   // c, nc: key cluster size and count
+  int cq, nqc;                             // query cluster size and count
   float scale;
   const int32_t* perm_q;
   const int32_t* perm_k;

@@ -68,7 +68,7 @@ typedef enum {
  * Options of the clustering (v1 §3.2). Pass NULL for the defaults
  * {transform=1, query_normalize=1, power_iters=8, sample_factor=1, seed=0,
  *  trace_perm=NULL, trace_score=NULL, trace_dir=NULL, split_mode=0,
- *  trace_basis=NULL}.
+ *  trace_basis=NULL, cluster_size_k=0}.
  *
  *  transform        1: keys are split under the query metric M_q = Q^T Q / N
  *                   (Eq. 12-14) and queries under the centred key metric
@@ -110,6 +110,11 @@ typedef enum {
  *                   is ignored. trace_dir then holds the chosen a_j.
  *  trace_basis      optional device buffer float [B*H][2][D][D] (split_mode
  *                   1 only): row j of tree (head, tensor) is a_j.
+ *  cluster_size_k   0: keys are clustered with cluster_size like the
+ *                   queries; else the key cluster size c_k in {64, 128, 256}
+ *                   (the pages pair c_q = 64 with c_k = 128, v1 §3.1). Each
+ *                   tensor's tree then follows its own size; the trace
+ *                   buffers need equal sizes (else CA_ERR_UNSUPPORTED).
  */
 typedef struct {
   int transform;
@@ -122,6 +127,7 @@ typedef struct {
   float* trace_dir;
   int split_mode;
   float* trace_basis;
+  int cluster_size_k;
 } ca_cluster_opts;
 
 /* Number of split levels of the data-independent tree for (N, c): the tree
@@ -149,9 +155,13 @@ size_t ca_workspace_size(ca_op op, int B, int H, int N, int D, int cluster_size,
  *           [j c, j c + n_j); every n_j = c except the last, which holds
  *           N - (n_c - 1) c (v1 §3.1). Members of a cluster are in ascending
  *           token order.
- * cent_q, cent_k  out float [B,H,n_c,D], n_c = ceil(N/c): means of the
+ * cent_q, cent_k  out float [B,H,n_qc,D] and [B,H,n_kc,D], n_qc = ceil(N/c_q),
+ *           n_kc = ceil(N/c_k) (c_q = cluster_size, c_k = opts->cluster_size_k
+ *           or c_q; below n_c is either): means of the
  *           original (untransformed) query / key rows of each cluster.
- * counts    out int32 [B,H,n_c] or NULL: n_j.
+ * counts    out int32 [B,H,n_kc] or NULL: n_j of the key clusters.
+ * ws        workspace of ca_workspace_size(CA_OP_CLUSTER (CA_OP_CLUSTER_DIAG
+ *           for split_mode 1), B, H, N, D, min(c_q, c_k), 0).
  */
 int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, int D,
                int cluster_size, const ca_cluster_opts* opts, int32_t* perm_q,
@@ -250,6 +260,28 @@ int ca_attend_var(const void* Q, const void* K, const void* V, ca_dtype dt, int 
                   int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
                   const int32_t* blocks, const int32_t* nsel, int max_sel, int compensate,
                   float scale, void* O, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ca_attend_ex -- ca_attend with query clusters of size cluster_size_q and key
+ * clusters of size cluster_size_k (the pages pair 64-token query clusters with
+ * 128-token key clusters, v1 §3.1) and an optional variable selection.
+ *
+ * perm_q    int32 [B,H,N], clusters of cluster_size_q (n_qc = ceil(N/c_q)).
+ * perm_k    int32 [B,H,N], clusters of cluster_size_k (n_kc = ceil(N/c_k)).
+ * cluster_size_q <= cluster_size_k, both in {64, 128, 256}.
+ * blocks    int32 [B,H,n_qc,max_sel]: key clusters in [0, n_kc) per query
+ *           cluster; with nsel, row a holds nsel[a] of them.
+ * nsel      int32 [B,H,n_qc] (device) or NULL (every row holds max_sel).
+ * max_sel   1 <= max_sel <= n_kc.
+ * Workspace: CA_OP_ATTEND with cluster_size = cluster_size_k. Other
+ * arguments and errors as ca_attend; CA_ERR_UNSUPPORTED for a query cluster
+ * size above the key cluster size.
+ */
+int ca_attend_ex(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
+                 int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size_q,
+                 int cluster_size_k, const int32_t* blocks, const int32_t* nsel, int max_sel,
+                 int compensate, float scale, void* O, float* lse, void* ws, size_t ws_bytes,
+                 void* stream);
 
 /*
  * ca_dense -- dense attention baseline, o_i = sum_j softmax_j(scale q_i.k_j) v_j

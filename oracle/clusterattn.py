@@ -438,11 +438,13 @@ def head_representations(Q: np.ndarray, K: np.ndarray, opts: ClusterOpts):
 
 
 def cluster(Q: np.ndarray, K: np.ndarray, c: int, opts: ClusterOpts | None = None,
-            dtype: str = "bf16", traces: dict | None = None):
+            dtype: str = "bf16", traces: dict | None = None, c_k: int | None = None):
     """Cluster queries and keys of every (batch, head) separately (v1 §3.1).
 
     Q, K: [B, H, N, D]. Returns perm_q, perm_k of shape [B, H, N] (int64).
-    The flattened head index b*H + h keys the random draws.
+    The flattened head index b*H + h keys the random draws. The keys' tree
+    uses cluster size c_k when given (v1 §3.1 pairs 64-token query clusters
+    with 128-token key clusters), else c.
     """
     opts = opts or ClusterOpts()
     B, H, N, D = Q.shape
@@ -457,7 +459,7 @@ def cluster(Q: np.ndarray, K: np.ndarray, c: int, opts: ClusterOpts | None = Non
             tq = TreeTrace() if traces is not None else None
             tk = TreeTrace() if traces is not None else None
             pq[b, h] = cluster_tree(Xq, Gq, hq, c, opts, head, TENSOR_Q, tq)
-            pk[b, h] = cluster_tree(Xk, Gk, hk, c, opts, head, TENSOR_K, tk)
+            pk[b, h] = cluster_tree(Xk, Gk, hk, c_k or c, opts, head, TENSOR_K, tk)
             if traces is not None:
                 traces[(b, h, TENSOR_Q)] = tq
                 traces[(b, h, TENSOR_K)] = tk
@@ -603,7 +605,7 @@ def dense_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float | 
 
 
 def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
-                     scale: float | None = None, clusters=None):
+                     scale: float | None = None, clusters=None, c_k: int | None = None):
     """Block-sparse attention of one head with optional striped
     mean-compensation.
 
@@ -613,22 +615,23 @@ def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
     ln|c| and value vbar_c, which is Eq. 21-22 (the centroid weight w_c
     counted |c| times). Returns O in original token order and LSE.
     ``clusters`` restricts the work to those query clusters (the rows of the
-    other queries are NaN).
+    other queries are NaN). Key clusters have size c_k when given, else c.
     """
     Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
     N, D = Q.shape
     tau = 1.0 / math.sqrt(D) if not scale else float(scale)
+    ck = c_k or c
     qs = leaf_sizes(N, c)
-    ks = leaf_sizes(K.shape[0], c)
-    kbar, cnt = centroids(K, perm_k, c)
-    vbar, _ = centroids(V, perm_k, c)
+    ks = leaf_sizes(K.shape[0], ck)
+    kbar, cnt = centroids(K, perm_k, ck)
+    vbar, _ = centroids(V, perm_k, ck)
     O = np.full((N, V.shape[1]), np.nan)
     L = np.full(N, np.nan)
     for a in (range(len(qs)) if clusters is None else clusters):
         na = qs[a]
         qi = perm_q[a * c:a * c + na]
         sel = np.asarray(blocks[a], np.int64)
-        keys = np.concatenate([perm_k[j * c:j * c + ks[j]] for j in sel])
+        keys = np.concatenate([perm_k[j * ck:j * ck + ks[j]] for j in sel])
         logits = tau * (Q[qi] @ K[keys].T)
         vals = V[keys]
         if compensate:
@@ -645,7 +648,7 @@ def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
     return O, L
 
 
-def attend(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool, scale=None):
+def attend(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool, scale=None, c_k=None):
     """sparse_attention over every (batch, head): Q,K,V [B,H,N,D]."""
     B, H, N, D = Q.shape
     O = np.empty((B, H, N, V.shape[-1]))
@@ -653,7 +656,8 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool, scale=None
     for b in range(B):
         for h in range(H):
             O[b, h], L[b, h] = sparse_attention(Q[b, h], K[b, h], V[b, h], perm_q[b, h],
-                                                perm_k[b, h], c, blocks[b][h], compensate, scale)
+                                                perm_k[b, h], c, blocks[b][h], compensate, scale,
+                                                c_k=c_k)
     return O, L
 
 

@@ -711,6 +711,42 @@ def test_special_cases_equal_dense():
     check_special_cases_equal_dense()
 
 
+def check_unequal_cluster_sizes():
+    # Query clusters of c and key clusters of c_k != c: selecting every key
+    # cluster equals dense; key clusters of one token (c_k = 1) with
+    # compensation equal dense for any selection; one selected key cluster
+    # per query cluster against the logits built by hand from the members
+    r = _rng(17)
+    N, D = 200, 16
+    Q, K, V = (r.standard_normal((N, D)) for _ in range(3))
+    Od, Ld = o.dense_attention(Q, K, V)
+    pq = r.permutation(N)
+    for c, ck in ((32, 64), (16, 64), (64, 32)):
+        pk = r.permutation(N)
+        nq, nk = -(-N // c), -(-N // ck)
+        allb = np.tile(np.arange(nk), (nq, 1))
+        for comp in (False, True):
+            O, L = o.sparse_attention(Q, K, V, pq, pk, c, allb, comp, c_k=ck)
+            assert np.allclose(O, Od, rtol=1e-12, atol=1e-12) and np.allclose(L, Ld, rtol=1e-12)
+        one = r.integers(0, nk, size=(nq, 1))
+        O, _ = o.sparse_attention(Q, K, V, pq, pk, c, one, False, c_k=ck)
+        for a in range(nq):
+            qi = pq[a * c:(a + 1) * c]
+            j = int(one[a, 0])
+            ki = pk[j * ck:(j + 1) * ck]
+            want, _ = o._softmax_combine(Q[qi] @ K[ki].T / math.sqrt(D), V[ki])
+            assert np.allclose(O[qi], want, rtol=1e-12, atol=1e-12)
+    pk = r.permutation(N)
+    for k in (1, 7, 50):
+        sel = np.stack([np.sort(r.choice(N, k, replace=False)) for _ in range(-(-N // 32))])
+        O, _ = o.sparse_attention(Q, K, V, pq, pk, 32, sel, True, c_k=1)
+        assert np.allclose(O, Od, rtol=1e-10, atol=1e-12)
+
+
+def test_unequal_cluster_sizes():
+    check_unequal_cluster_sizes()
+
+
 def check_piecewise_constant_keys():
     # Keys with n_c distinct rows, each repeated c times (shuffled): every split
     # keeps the copies together, so each cluster is one distinct key, delta_c = 0
