@@ -91,6 +91,8 @@ def parse():
                     help="skip the copy and GEMM rate measurements")
     ap.add_argument("--split-mode", choices=["power", "diag"], default="power",
                     help="basic (power iteration) or diagonalized recursive splitting")
+    ap.add_argument("--cq", type=int, default=0,
+                    help="query cluster size when it differs from the key cluster size")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed")
     ap.add_argument("--assign", choices=["topk", "adaptive"], default="topk",
@@ -318,11 +320,14 @@ def main():
     if args.verbose:
         print(f"inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     B, H, N, D = Q.shape
-    c = w.c
+    c = w.c                      # key cluster size
+    cq = args.cq or c            # query cluster size
     op_c = ca.OP_CLUSTER_DIAG if args.split_mode == "diag" else ca.OP_CLUSTER
-    ws_c = torch.empty(ca.workspace_size(op_c, B, H, N, D, c), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(ca.workspace_size(op_c, B, H, N, D, min(c, cq)), dtype=torch.uint8,
+                       device=dev)
     n_c = -(-N // c)
-    ws_r = torch.empty(max(1, ca.workspace_size(ca.OP_ROUTE, B, H, n_c, D, n_c, topk)),
+    n_qc = -(-N // cq)
+    ws_r = torch.empty(max(1, ca.workspace_size(ca.OP_ROUTE, B, H, n_qc, D, n_c, topk)),
                        dtype=torch.uint8, device=dev)
     ws_a = torch.empty(ca.workspace_size(ca.OP_ATTEND, B, H, N, D, c, topk), dtype=torch.uint8,
                        device=dev)
@@ -332,8 +337,9 @@ def main():
     def step(evs=None, kev=None):
         if evs:
             evs[0].record()
-        cr = ca.cluster(Q, K, c, seed=w.cluster_seed, split_mode=args.split_mode,
-                        query_normalize=not adaptive, workspace=ws_c)
+        cr = ca.cluster(Q, K, cq, seed=w.cluster_seed, split_mode=args.split_mode,
+                        query_normalize=not adaptive, cluster_size_k=c if cq != c else 0,
+                        workspace=ws_c)
         if evs:
             evs[1].record()
         if adaptive:
@@ -344,8 +350,8 @@ def main():
         if evs:
             evs[2].record()
             ca.profile_events(kev[0].handle, kev[1].handle)
-        O = ca.attend(Q, K, V, cr.perm_q, cr.perm_k, c, blocks, compensate=w.compensate,
-                      nsel=nsel, workspace=ws_a)
+        O = ca.attend(Q, K, V, cr.perm_q, cr.perm_k, cq, blocks, compensate=w.compensate,
+                      nsel=nsel, c_k=c, workspace=ws_a)
         if evs:
             ca.profile_events(None, None)
             evs[3].record()
@@ -382,8 +388,10 @@ def main():
         ns = nsel.cpu().numpy().astype(np.int64)
     take = np.arange(bl.shape[-1])[None, None, None, :] < ns[..., None]
     sel_sizes = np.where(take, sizes[np.clip(bl, 0, n_c - 1)], 0).sum(-1)
-    tok_inter = float(np.sum(sizes[None, None, :] * sel_sizes))
-    cen_inter = float(np.sum(sizes[None, None, :] * (n_c - ns))) if w.compensate else 0.0
+    qsizes = np.full(n_qc, cq, np.int64)
+    qsizes[-1] = N - (n_qc - 1) * cq
+    tok_inter = float(np.sum(qsizes[None, None, :] * sel_sizes))
+    cen_inter = float(np.sum(qsizes[None, None, :] * (n_c - ns))) if w.compensate else 0.0
     mean_sel = float(ns.mean())
     flops_attn = 4.0 * D * (tok_inter + cen_inter)
     achieved = flops_attn / (t_attn_kernel * 1e-3) / 1e12
@@ -434,7 +442,7 @@ def main():
     clu_gbs = clu_bytes / (clu_ms * 1e-3) / 1e9
 
     traffic = (recorded_traffic(w.name, topk) if B * H == w.B * w.H and not adaptive
-               and args.split_mode == "power" else None)
+               and args.split_mode == "power" and cq == c else None)
     eff = 4.0 * D * N * N * B * H / (wall) / 1e12
     result = {
         "metric": METRIC,
@@ -452,6 +460,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "heads": H, "N": N, "head_dim": D,
                    "cluster_size": c, "topk": topk, "compensate": w.compensate,
                    "split_mode": args.split_mode, "assign": args.assign,
+                   **({"query_cluster_size": cq} if cq != c else {}),
                    **({"recall": args.recall, "min_count": args.min_count,
                        "mean_selected": round(mean_sel, 2)} if adaptive else {})},
         "stage_ms": {"cluster": round(float(st_cluster), 4), "route": round(float(st_route), 4),
