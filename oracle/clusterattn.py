@@ -33,7 +33,12 @@ function that implements it. Summary of those readings:
   the smaller); values equal at the threshold go left in token-id order;
 * top-k selection is exact with ties to the lower key-cluster index;
 * striped mean-compensation is per query, with the cluster's valid count as
-  weight and the original (untransformed) key and value centroids.
+  weight and the original (untransformed) key and value centroids;
+* the optional FP8 Q.K^T operands (OCP E4M3): queries quantized per token,
+  keys per 64 consecutive members of a cluster (per 64 consecutive tokens in
+  dense attention), compensation centroids rounded to bf16 and quantized per
+  64 consecutive clusters; scale amax / 448, codes rounded to nearest even
+  from fp32(x * fp32(448 / amax)); values stay exact.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, invariants, library routines, published generator
@@ -585,6 +590,115 @@ def route_adaptive(cq: np.ndarray, ck: np.ndarray, counts: np.ndarray, tau: floa
 
 
 # ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) operands of the Q.K^T product. The pages run a quantized
+# block-sparse kernel and compare it with quantized dense attention "given
+# equal quantization" (v1 §4.1 "Baselines"; rev §5 "Experiments" and §4
+# "Method" on the kernel); they do not give the scheme. Reading taken here:
+# queries are quantized per token, keys per block of 64 consecutive keys of a
+# cluster's member list (the kernel's key sub-tile), compensation centroids
+# per block of 64 consecutive clusters after rounding to bf16 (the precision
+# in which centroids are streamed); each group has scale amax / 448 and
+# codes e4m3(x * (448 / amax)), both computed in fp32; P.V stays exact.
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3
+    mantissa bits; subnormals at exponent field 0; S.1111.111 is NaN; no
+    infinities; largest finite 448)."""
+    c = np.asarray(codes, np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    E = (c >> 3) & 0xF
+    M = c & 0x7
+    mag = np.where(E == 0, M / 8.0 * 2.0 ** -6, (1.0 + M / 8.0) * np.exp2(E - 7.0))
+    mag = np.where((E == 15) & (M == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each value (ties to the even code), finite values
+    of magnitude >= 464 saturate to +-448, NaN gives 0x7F; the sign of zero
+    is kept. The spacing in binade [2^e, 2^(e+1)) is 2^(e-3), and 2^-9 below
+    2^-6 (the subnormals)."""
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)                          # a = m 2^ex, m in [0.5, 1)
+    e = np.maximum(ex - 1, -6)                   # binade, floored at the subnormals
+    q = np.exp2(e - 3.0)
+    n = np.rint(a / q)                           # round half to even
+    v = np.minimum(n * q, E4M3_MAX)
+    _, ev = np.frexp(v)
+    Ev = ev - 1
+    normal = v >= 2.0 ** -6
+    mant = np.where(normal, v / np.exp2(Ev) * 8.0 - 8.0, 0.0)
+    code = np.where(normal, ((Ev + 7) << 3) + mant, v / 2.0 ** -9).astype(np.int64)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def bf16_nearest(x) -> np.ndarray:
+    """fp32 values rounded to bfloat16 (round to nearest, ties to even on the
+    fp32 bit pattern), returned as fp32."""
+    b = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16 << 16
+    return b.astype(np.uint32).view(np.float32)
+
+
+def quantize_e4m3(X, group: int):
+    """Rows of X in groups of `group` consecutive rows (the last group may be
+    short), one scale per group: amax = max |x| over the group, inv =
+    fp32(448 / amax) (0 for an all-zero group), code = e4m3(fp32(x * inv)),
+    scale = fp32(amax / 448). X holds fp32 values. Returns (codes uint8 like
+    X, scales float32 [ceil(rows / group)])."""
+    X = np.asarray(X, np.float32)
+    R = X.shape[0]
+    ng = (R + group - 1) // group
+    codes = np.empty(X.shape, np.uint8)
+    scales = np.empty(ng, np.float32)
+    for g in range(ng):
+        blk = X[g * group:(g + 1) * group]
+        amax = np.float32(np.max(np.abs(blk))) if blk.size else np.float32(0)
+        inv = np.float32(E4M3_MAX) / amax if amax > 0 else np.float32(0)
+        codes[g * group:(g + 1) * group] = e4m3_encode(blk * np.float32(inv))
+        scales[g] = amax / np.float32(E4M3_MAX)
+    return codes, scales
+
+
+def dequantize_e4m3(codes, scales, group: int) -> np.ndarray:
+    """code value x group scale, exact in fp64."""
+    rows = np.arange(codes.shape[0]) // group
+    return e4m3_decode(codes) * np.asarray(scales, np.float64)[rows][:, None]
+
+
+def fp8_rows(X, group: int) -> np.ndarray:
+    """X after quantization in row groups and dequantization."""
+    return dequantize_e4m3(*quantize_e4m3(X, group), group)
+
+
+def fp8_keys(K, perm_k, ck: int, tile: int = 64) -> np.ndarray:
+    """K (token order) after quantization per block of `tile` consecutive
+    members of each key cluster's member list (a short cluster's last block
+    holds only its valid members)."""
+    K = np.asarray(K, np.float32)
+    out = np.empty(K.shape, np.float64)
+    for j, nj in enumerate(leaf_sizes(K.shape[0], ck)):
+        mem = np.asarray(perm_k[j * ck:j * ck + nj])
+        for p in range(0, nj, tile):
+            rows = mem[p:p + tile]
+            out[rows] = fp8_rows(K[rows], len(rows))
+    return out
+
+
+def fp8_centroids(kbar, tile: int = 64) -> np.ndarray:
+    """Key centroids rounded to bf16, then quantized per block of `tile`
+    consecutive clusters."""
+    return fp8_rows(bf16_nearest(kbar), tile)
+
+
+# ---------------------------------------------------------------------------
 # Attention (v1 §1.2 Eq. 1-2; App. A Eq. 21-22)
 # ---------------------------------------------------------------------------
 
@@ -596,16 +710,21 @@ def _softmax_combine(logits: np.ndarray, values: np.ndarray):
     return o, (m + np.log(l))[:, 0]
 
 
-def dense_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float | None = None):
+def dense_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float | None = None,
+                    qk: str = "exact"):
     """o_i = sum_j softmax_j(tau q_i . k_j) v_j and LSE_i = log sum_j exp(.)
-    for one head (Eq. 1). Q, K, V: [N, D]."""
+    for one head (Eq. 1). Q, K, V: [N, D]. qk="e4m3": the logits use the FP8
+    operands (queries per token, keys per block of 64 consecutive tokens)."""
+    tau = 1.0 / math.sqrt(np.shape(Q)[1]) if not scale else float(scale)
+    if qk == "e4m3":
+        Q, K = fp8_rows(Q, 1), fp8_keys(K, np.arange(np.shape(K)[0]), 64)
     Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
-    tau = 1.0 / math.sqrt(Q.shape[1]) if not scale else float(scale)
     return _softmax_combine(tau * (Q @ K.T), V)
 
 
 def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
-                     scale: float | None = None, clusters=None, c_k: int | None = None):
+                     scale: float | None = None, clusters=None, c_k: int | None = None,
+                     qk: str = "exact"):
     """Block-sparse attention of one head with optional striped
     mean-compensation.
 
@@ -616,15 +735,19 @@ def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
     counted |c| times). Returns O in original token order and LSE.
     ``clusters`` restricts the work to those query clusters (the rows of the
     other queries are NaN). Key clusters have size c_k when given, else c.
+    qk="e4m3": the logits use the FP8 operands (fp8_rows per query, fp8_keys,
+    fp8_centroids); the values and the centroid values stay exact.
     """
-    Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
-    N, D = Q.shape
+    N, D = np.shape(Q)
     tau = 1.0 / math.sqrt(D) if not scale else float(scale)
     ck = c_k or c
     qs = leaf_sizes(N, c)
-    ks = leaf_sizes(K.shape[0], ck)
+    ks = leaf_sizes(np.shape(K)[0], ck)
     kbar, cnt = centroids(K, perm_k, ck)
     vbar, _ = centroids(V, perm_k, ck)
+    if qk == "e4m3":
+        Q, K, kbar = fp8_rows(Q, 1), fp8_keys(K, perm_k, ck), fp8_centroids(kbar)
+    Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
     O = np.full((N, V.shape[1]), np.nan)
     L = np.full(N, np.nan)
     for a in (range(len(qs)) if clusters is None else clusters):
@@ -648,7 +771,8 @@ def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
     return O, L
 
 
-def attend(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool, scale=None, c_k=None):
+def attend(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool, scale=None, c_k=None,
+           qk: str = "exact"):
     """sparse_attention over every (batch, head): Q,K,V [B,H,N,D]."""
     B, H, N, D = Q.shape
     O = np.empty((B, H, N, V.shape[-1]))
@@ -657,18 +781,18 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool, scale=None
         for h in range(H):
             O[b, h], L[b, h] = sparse_attention(Q[b, h], K[b, h], V[b, h], perm_q[b, h],
                                                 perm_k[b, h], c, blocks[b][h], compensate, scale,
-                                                c_k=c_k)
+                                                c_k=c_k, qk=qk)
     return O, L
 
 
-def dense(Q, K, V, scale=None):
+def dense(Q, K, V, scale=None, qk: str = "exact"):
     """dense_attention over every (batch, head)."""
     B, H, N, D = Q.shape
     O = np.empty((B, H, N, V.shape[-1]))
     L = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            O[b, h], L[b, h] = dense_attention(Q[b, h], K[b, h], V[b, h], scale)
+            O[b, h], L[b, h] = dense_attention(Q[b, h], K[b, h], V[b, h], scale, qk)
     return O, L
 
 

@@ -1,0 +1,292 @@
+"""Pins of the oracle's FP8 (OCP E4M3) Q.K^T operands against the format's
+definition, a library conversion, hand-worked values, lossless constructions
+and the quantization error bound. The pages run a quantized kernel and compare
+with quantized dense attention (paper "ClusterAttention: A training-free
+speedup of bidirectional attention", arXiv 2608.26965 v1 §4.1 "Baselines");
+the scheme itself is the oracle's stated reading. ``test_fp8_planted`` plants
+plausible mistakes into the oracle (on the CPU) and requires a pin to fail.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.clusterattn as o
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# The E4M3 format
+# ---------------------------------------------------------------------------
+
+def check_e4m3_decode_library():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = o.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(lib), np.isnan(got))
+    fin = ~np.isnan(lib)
+    assert np.array_equal(lib[fin], got[fin])
+    # facts of the format: largest finite, smallest subnormal and normal, one
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x38] == 1.0
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and np.sum(np.isnan(got)) == 2
+
+
+def check_e4m3_encode_library():
+    import torch
+    r = _rng(1)
+    n = 100000
+    x = np.exp2(r.uniform(-13.0, 8.9, n)) * r.choice([-1.0, 1.0], n)
+    x = np.clip(x, -448.0, 448.0).astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(o.e4m3_encode(x), lib)
+    # every finite code round-trips; midpoints go to the even code
+    codes = np.arange(256, dtype=np.uint8)
+    vals = o.e4m3_decode(codes)
+    fin = ~np.isnan(vals)
+    assert np.array_equal(o.e4m3_encode(vals[fin]), codes[fin])
+    for c in range(0, 0x7E):
+        lo, hi = vals[c], vals[c + 1]
+        mid = (lo + hi) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert o.e4m3_encode(mid) == even, c
+        assert o.e4m3_encode(np.nextafter(mid, 0.0)) == c
+        assert o.e4m3_encode(np.nextafter(mid, 1e9)) == c + 1
+        assert o.e4m3_encode(-mid) == (even | 0x80)
+    # saturation above the largest finite value and the sign of zero
+    assert o.e4m3_encode(500.0) == 0x7E and o.e4m3_encode(-1e6) == 0xFE
+    assert o.e4m3_encode(0.0) == 0x00 and o.e4m3_encode(-0.0) == 0x80
+
+
+def check_bf16_library():
+    import torch
+    r = _rng(2)
+    x = (r.standard_normal(50000) * np.exp2(r.uniform(-20, 20, 50000))).astype(np.float32)
+    lib = torch.from_numpy(x).bfloat16().float().numpy()
+    assert np.array_equal(o.bf16_nearest(x), lib)
+
+
+# ---------------------------------------------------------------------------
+# Group quantization
+# ---------------------------------------------------------------------------
+
+def check_quantize_worked_example():
+    # amax 1: inv = 448; 1 -> 448 (0x7E); -0.5 -> -224 = -1.75 * 2^7 (0xF6);
+    # fp32(0.3 * 448) = 134.4 lies in [128, 256), spacing 16 -> 128 (0x70)
+    codes, scales = o.quantize_e4m3(np.array([[1.0, -0.5, 0.3]], np.float32), 1)
+    assert codes.tolist() == [[0x7E, 0xF6, 0x70]]
+    assert scales.dtype == np.float32 and scales[0] == np.float32(1.0) / np.float32(448.0)
+    # a group of two rows shares one scale; an all-zero group: codes 0, scale 0
+    X = np.array([[2.0, 0.0], [0.0, -1.0], [0.0, 0.0]], np.float32)
+    codes, scales = o.quantize_e4m3(X, 2)
+    assert codes.tolist() == [[0x7E, 0x00], [0x00, 0xF6], [0x00, 0x00]]
+    assert scales.tolist() == [np.float32(2.0) / np.float32(448.0), 0.0]
+
+
+def check_quantize_bounds():
+    r = _rng(3)
+    for R, D, g in [(200, 64, 1), (200, 64, 64), (131, 128, 64), (5, 8, 7)]:
+        X = (r.standard_normal((R, D)) * np.exp2(r.integers(-8, 8, (R, 1)))).astype(np.float32)
+        X[r.random((R, D)) < 0.05] *= 1e-4          # values in the subnormal range
+        codes, scales = o.quantize_e4m3(X, g)
+        assert codes.shape == X.shape and scales.shape == ((R + g - 1) // g,)
+        Xh = o.dequantize_e4m3(codes, scales, g)
+        for k in range(len(scales)):
+            blk = slice(k * g, (k + 1) * g)
+            amax = np.abs(X[blk]).max()
+            # the group's largest magnitude maps to the largest code
+            assert np.abs(o.e4m3_decode(codes[blk])).max() == 448.0
+            assert abs(float(scales[k]) * 448.0 - amax) <= 2 * np.spacing(np.float32(amax))
+            # error: half a spacing, 2^-4 relative in the normal range, 2^-10
+            # code units below it, plus the fp32 rounding of the scales
+            err = np.abs(Xh[blk] - X[blk])
+            bound = np.maximum(2.0 ** -4 * np.abs(X[blk]), 2.0 ** -10 * scales[k]) * (1 + 1e-6) \
+                + 1e-6 * np.abs(X[blk])
+            assert np.all(err <= bound)
+
+
+# ---------------------------------------------------------------------------
+# FP8 attention
+# ---------------------------------------------------------------------------
+
+def _grid_rows(r, n, D, shift):
+    """Rows of e4m3 code values times 2^(shift - 7), each with one element
+    +-448: a group's amax is then 3.5 * 2^max(shift), its scale a power of two
+    and its quantization exact; magnitudes >= 2^-3 keep shifts of a few
+    binades inside a group in the normal range."""
+    codes = r.integers(0x18, 0x7F, (n, D))            # 2^-3 .. 448
+    vals = o.e4m3_decode(codes) * r.choice([-1.0, 1.0], (n, D))
+    vals[np.arange(n), r.integers(0, D, n)] = 448.0 * r.choice([-1.0, 1.0], n)
+    return vals * np.exp2(np.asarray(shift, np.float64) - 7.0)[..., None] \
+        if np.ndim(shift) else vals * 2.0 ** (shift - 7)
+
+
+def check_fp8_attention_lossless():
+    """Operands that every group quantizes exactly: FP8 attention equals the
+    exact one. The two 64-member halves of each 128-key cluster lie 2^12
+    apart in magnitude, and so do the clusters, so a grouping other than per
+    64 members of a cluster, or per-tensor query scaling, loses precision."""
+    r = _rng(4)
+    N, D, c = 640, 16, 128
+    nc = N // c
+    perm_q = r.permutation(N)
+    perm_k = r.permutation(N)
+    Q = np.empty((N, D)); K = np.empty((N, D))
+    Q[:] = _grid_rows(r, N, D, r.integers(-6, 7, N))
+    for j in range(nc):
+        for half in range(2):
+            K[perm_k[j * c + 64 * half:j * c + 64 * half + 64]] = \
+                _grid_rows(r, 64, D, 12 * half + 3 * j - 12)
+    V = r.standard_normal((N, D))
+    blocks = np.array([np.sort(r.choice(nc, 2, replace=False)) for _ in range(nc)])
+    a = o.sparse_attention(Q, K, V, perm_q, perm_k, c, blocks, False, qk="e4m3")
+    b = o.sparse_attention(Q, K, V, perm_q, perm_k, c, blocks, False)
+    assert np.allclose(a[0], b[0], rtol=0, atol=1e-12) and np.allclose(a[1], b[1], rtol=0, atol=1e-9)
+    # compensation: identical rows within a cluster make every centroid a
+    # grid row, and close cluster magnitudes keep the centroid blocks exact
+    for j in range(nc):
+        K[perm_k[j * c:(j + 1) * c]] = _grid_rows(r, 1, D, j % 3 - 1)
+    a = o.sparse_attention(Q, K, V, perm_q, perm_k, c, blocks, True, qk="e4m3")
+    b = o.sparse_attention(Q, K, V, perm_q, perm_k, c, blocks, True)
+    assert np.allclose(a[0], b[0], rtol=0, atol=1e-12) and np.allclose(a[1], b[1], rtol=0, atol=1e-9)
+    # dense: key blocks of 64 consecutive tokens, 2^3 apart
+    Kd = np.concatenate([_grid_rows(r, 64, D, 3 * j - 12) for j in range(N // 64)])
+    a = o.dense_attention(Q, Kd, V, qk="e4m3")
+    b = o.dense_attention(Q, Kd, V)
+    assert np.allclose(a[0], b[0], rtol=0, atol=1e-12) and np.allclose(a[1], b[1], rtol=0, atol=1e-9)
+
+
+def check_fp8_centroid_double_rounding():
+    """Worked example: the excluded cluster's centroid (3.5, x) with
+    x = (1.0625 + 2^-12) / 128 rounds to bf16 (1.0625) / 128, then to the
+    even e4m3 code 1.0 (scale 3.5 / 448 = 2^-7), giving x_hat = 2^-7; the
+    query (3.5, 3.5) is exact. Each query sees 64 keys (3.5, 0) and the
+    centroid with weight 64: LSE = ln(64 e^(12.25 t) + 64 e^((12.25 +
+    3.5 * 2^-7) t)), t = 1 / sqrt(2)."""
+    N, D, c = 128, 2, 64
+    x = (1.0625 + 2.0 ** -12) / 128
+    Q = np.full((N, D), 3.5)
+    K = np.zeros((N, D)); K[:, 0] = 3.5; K[64:, 1] = x
+    V = np.zeros((N, D))
+    perm = np.arange(N)
+    blocks = np.zeros((2, 1), np.int64)
+    _, L = o.sparse_attention(Q, K, V, perm, perm, c, blocks, True, qk="e4m3")
+    t = 1.0 / math.sqrt(2.0)
+    want = math.log(64 * math.exp(12.25 * t) + 64 * math.exp((12.25 + 3.5 * 2.0 ** -7) * t))
+    assert np.allclose(L, want, rtol=0, atol=1e-12)
+
+
+def check_fp8_attention_error_bound():
+    """Random operands: every FP8 logit is within the bound that the group
+    spacings give of the exact logit, so the LSE moves by no more than the
+    largest logit error of its row."""
+    r = _rng(5)
+    N, D, c = 256, 32, 64
+    Q = r.standard_normal((N, D)); K = r.standard_normal((N, D)) + 0.5; V = r.standard_normal((N, D))
+    Q = Q.astype(np.float32).astype(np.float64); K = K.astype(np.float32).astype(np.float64)
+    perm_q = r.permutation(N); perm_k = r.permutation(N)
+    nc = N // c
+    blocks = np.array([np.sort(r.choice(nc, 2, replace=False)) for _ in range(nc)])
+    tau = 1.0 / math.sqrt(D)
+    a = o.sparse_attention(Q, K, V, perm_q, perm_k, c, blocks, False, qk="e4m3")
+    b = o.sparse_attention(Q, K, V, perm_q, perm_k, c, blocks, False)
+    sq = np.abs(Q).max(axis=1) / 448.0
+    sk = np.empty(N)
+    for j in range(nc):
+        mem = perm_k[j * c:(j + 1) * c]
+        sk[mem] = np.abs(K[mem]).max() / 448.0
+    eq = np.maximum(2.0 ** -4 * np.abs(Q), 2.0 ** -10 * sq[:, None]) * 1.001   # |q_hat - q|
+    ek = np.maximum(2.0 ** -4 * np.abs(K), 2.0 ** -10 * sk[:, None]) * 1.001
+    bound = tau * (eq @ (np.abs(K) + ek).T + np.abs(Q) @ ek.T)                  # [query, key]
+    for qa in range(nc):
+        qi = perm_q[qa * c:(qa + 1) * c]
+        keys = np.concatenate([perm_k[j * c:(j + 1) * c] for j in blocks[qa]])
+        lim = bound[np.ix_(qi, keys)].max(axis=1)
+        assert np.all(np.abs(a[1][qi] - b[1][qi]) <= lim)
+    # and the quantized result really differs from the exact one
+    assert np.max(np.abs(a[1] - b[1])) > 1e-6
+
+
+CHECKS = [check_e4m3_decode_library, check_e4m3_encode_library, check_bf16_library,
+          check_quantize_worked_example, check_quantize_bounds, check_fp8_attention_lossless,
+          check_fp8_centroid_double_rounding, check_fp8_attention_error_bound]
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=[f.__name__ for f in CHECKS])
+def test_fp8_pin(check):
+    check()
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes
+# ---------------------------------------------------------------------------
+
+_orig = {n: getattr(o, n) for n in ("e4m3_encode", "fp8_keys", "fp8_rows", "fp8_centroids",
+                                    "quantize_e4m3", "bf16_nearest")}
+
+
+def _encode_truncating(x):
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)
+    q = np.exp2(np.maximum(ex - 1, -6) - 3.0)
+    return _orig["e4m3_encode"](np.copysign(np.floor(a / q) * q, x))
+
+
+def _encode_no_subnormals(x):
+    x = np.asarray(x, np.float64)
+    return _orig["e4m3_encode"](np.where(np.abs(x) < 2.0 ** -6, 0.0 * x, x))
+
+
+def _keys_token_order(K, perm_k, ck, tile=64):
+    return _orig["fp8_keys"](K, np.arange(np.shape(K)[0]), ck, tile)
+
+
+def _keys_per_cluster(K, perm_k, ck, tile=64):
+    return _orig["fp8_keys"](K, perm_k, ck, ck)
+
+
+def _rows_per_tensor(X, group):
+    return _orig["fp8_rows"](X, np.shape(X)[0])
+
+
+def _centroids_without_bf16(kbar, tile=64):
+    return _orig["fp8_rows"](np.asarray(kbar, np.float32), tile)
+
+
+def _quantize_scale_from_inverse(X, group):
+    codes, scales = _orig["quantize_e4m3"](X, group)
+    inv = np.where(scales > 0, np.float32(448.0) / (scales * np.float32(448.0)), 0)
+    return codes, np.where(scales > 0, np.float32(1.0) / inv.astype(np.float32) * np.float32(1.001), 0
+                           ).astype(np.float32)
+
+
+PLANTED = [
+    ("e4m3_encode", _encode_truncating, check_e4m3_encode_library),
+    ("e4m3_encode", _encode_no_subnormals, check_e4m3_encode_library),
+    ("fp8_keys", _keys_token_order, check_fp8_attention_lossless),
+    ("fp8_keys", _keys_per_cluster, check_fp8_attention_lossless),
+    ("fp8_rows", _rows_per_tensor, check_fp8_attention_lossless),
+    ("fp8_centroids", _centroids_without_bf16, check_fp8_centroid_double_rounding),
+    ("quantize_e4m3", _quantize_scale_from_inverse, check_quantize_bounds),
+]
+
+
+def _fails(check):
+    try:
+        check()
+    except AssertionError:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("name,mutant,check", PLANTED,
+                         ids=[f"{p[0]}-{p[1].__name__.lstrip('_')}" for p in PLANTED])
+def test_fp8_planted(monkeypatch, name, mutant, check):
+    check()
+    monkeypatch.setattr(o, name, mutant)
+    assert _fails(check), f"planted mistake in {name} was not caught"
