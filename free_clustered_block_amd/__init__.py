@@ -18,15 +18,16 @@ from dataclasses import dataclass
 __all__ = [
     "CAError", "load", "LIB_PATH", "EXPORTS", "profile_events", "peak_probe", "HipEvent", "tree_levels",
     "workspace_size", "cluster", "route", "route_adaptive", "attend", "dense", "forward",
+    "quantize_e4m3",
     "ClusterResult",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libca.so")
 EXPORTS = ["ca_tree_levels", "ca_workspace_size", "ca_cluster", "ca_route", "ca_route_adaptive",
-           "ca_attend", "ca_attend_var", "ca_attend_ex", "ca_dense", "ca_profile_events", "ca_peak_probe",
-           "ca_status_string", "ca_last_error"]
+           "ca_attend", "ca_attend_var", "ca_attend_ex", "ca_dense", "ca_quantize_e4m3",
+           "ca_profile_events", "ca_peak_probe", "ca_status_string", "ca_last_error"]
 
-CA_BF16, CA_F32 = 0, 1
+CA_BF16, CA_F32, CA_BF16_FP8 = 0, 1, 2
 OP_CLUSTER, OP_ROUTE, OP_ATTEND, OP_DENSE, OP_CLUSTER_DIAG = 0, 1, 2, 3, 4
 
 _lib = None
@@ -76,6 +77,8 @@ def load() -> ctypes.CDLL:
     lib.ca_attend_ex.restype = I
     lib.ca_dense.argtypes = [P, P, P, I, I, I, I, I, F, P, P, P, S, P]
     lib.ca_dense.restype = I
+    lib.ca_quantize_e4m3.argtypes = [P, I, ctypes.c_int64, I, I, P, P, P]
+    lib.ca_quantize_e4m3.restype = I
     lib.ca_peak_probe.argtypes = [I, I, I, P, P]
     lib.ca_peak_probe.restype = I
     lib.ca_profile_events.argtypes = [P, P]
@@ -292,14 +295,25 @@ def route_adaptive(cent_q, cent_k, counts_k, recall: float, *, min_count: int = 
     return (blocks, nsel, scores) if return_scores else (blocks, nsel)
 
 
+def _attn_dtype(Q, fp8: bool) -> int:
+    dt = _dtype_code(Q)
+    if fp8:
+        if dt != CA_BF16:
+            raise TypeError("fp8 attention takes bfloat16 inputs")
+        return CA_BF16_FP8
+    return dt
+
+
 def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
            scale: float = 0.0, return_lse: bool = False, nsel=None, c_k: int = 0,
-           workspace=None):
+           fp8: bool = False, workspace=None):
     """ca_attend: block-sparse attention with optional mean-compensation;
     with `nsel` (selected count per row of `blocks`), ca_attend_var; with key
-    clusters of another size c_k than the query clusters' c, ca_attend_ex."""
+    clusters of another size c_k than the query clusters' c, ca_attend_ex;
+    fp8=True: the Q.K^T product on FP8 (E4M3) operands (dtype CA_BF16_FP8)."""
     torch = _torch()
     _bhnd(Q, K, V)
+    dt = _attn_dtype(Q, fp8)
     B, H, N, D = Q.shape
     dev = Q.device
     O = torch.empty_like(Q)
@@ -309,17 +323,17 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
     nbytes = workspace_size(OP_ATTEND, B, H, N, D, ck, topk)
     ws = _ws(nbytes, dev, workspace)
     if ck != c:
-        st = load().ca_attend_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N,
+        st = load().ca_attend_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, N,
                                  D, perm_q.data_ptr(), perm_k.data_ptr(), c, ck, blocks.data_ptr(),
                                  _ptr(nsel), topk, int(compensate), float(scale), O.data_ptr(),
                                  _ptr(lse), _ptr(ws), nbytes, _stream_ptr(dev))
     elif nsel is None:
-        st = load().ca_attend(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, D,
+        st = load().ca_attend(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, N, D,
                               perm_q.data_ptr(), perm_k.data_ptr(), c, blocks.data_ptr(), topk,
                               int(compensate), float(scale), O.data_ptr(), _ptr(lse), _ptr(ws),
                               nbytes, _stream_ptr(dev))
     else:
-        st = load().ca_attend_var(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N,
+        st = load().ca_attend_var(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, N,
                                   D, perm_q.data_ptr(), perm_k.data_ptr(), c, blocks.data_ptr(),
                                   nsel.data_ptr(), topk, int(compensate), float(scale),
                                   O.data_ptr(), _ptr(lse), _ptr(ws), nbytes, _stream_ptr(dev))
@@ -327,20 +341,37 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
     return (O, lse) if return_lse else O
 
 
-def dense(Q, K, V, *, scale: float = 0.0, return_lse: bool = False, workspace=None):
-    """ca_dense: dense attention baseline."""
+def dense(Q, K, V, *, scale: float = 0.0, return_lse: bool = False, fp8: bool = False,
+          workspace=None):
+    """ca_dense: dense attention baseline (fp8=True: FP8 Q.K^T operands)."""
     torch = _torch()
     _bhnd(Q, K, V)
+    dt = _attn_dtype(Q, fp8)
     B, H, N, D = Q.shape
     dev = Q.device
     O = torch.empty_like(Q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
     nbytes = workspace_size(OP_DENSE, B, H, N, D)
     ws = _ws(nbytes, dev, workspace)
-    st = load().ca_dense(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, D,
+    st = load().ca_dense(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, N, D,
                          float(scale), O.data_ptr(), _ptr(lse), _ptr(ws), nbytes, _stream_ptr(dev))
     _check(st)
     return (O, lse) if return_lse else O
+
+
+def quantize_e4m3(X, group: int):
+    """ca_quantize_e4m3: the rows of a 2-D bf16/fp32 tensor as FP8 (E4M3)
+    codes (uint8, same shape) and one fp32 scale per `group` rows."""
+    torch = _torch()
+    if X.dim() != 2 or not X.is_contiguous():
+        raise ValueError("X must be a contiguous 2-D tensor")
+    R, D = X.shape
+    codes = torch.empty((R, D), dtype=torch.uint8, device=X.device)
+    scales = torch.empty(((R + group - 1) // group,), dtype=torch.float32, device=X.device)
+    st = load().ca_quantize_e4m3(X.data_ptr(), _dtype_code(X), R, D, group, codes.data_ptr(),
+                                 scales.data_ptr(), _stream_ptr(X.device))
+    _check(st)
+    return codes, scales
 
 
 def forward(Q, K, V, c: int, topk: int, *, compensate: bool = True, seed: int = 0,

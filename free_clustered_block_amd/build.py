@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libca.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["metric.hip", "basis.hip", "cluster.hip", "route.hip", "attn.hip", "peak.hip", "ca_api.hip"]
+SOURCES = ["metric.hip", "basis.hip", "cluster.hip", "route.hip", "attn.hip", "quant.hip", "peak.hip", "ca_api.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -18,9 +18,16 @@
 //                kbar rows as keys, vbar as values, logit scale q.kbar +
 //                ln n_c, -inf for selected or padding clusters) in the same
 //                running maximum and sum. O is scattered back to token order.
+// FP8 Q.K^T variant (bf16 inputs): permute_kv writes the key tiles as e4m3
+// codes with one scale per 64-key sub-tile, quant_centroids does the same per
+// 64 key centroids, and attn_fwd quantizes each query row in its prologue; S^T
+// = K Q^T then runs on v_mfma_scale_f32_32x32x64_f8f6f4 and the tile's logit
+// scale becomes scale * s_q * s_k. P.V and everything after it are as in the
+// bf16 path.
 // fp32 path: the same computation on VALU, one thread per query.
 #include <type_traits>
 
+#include "fp8.h"
 #include "kernels.h"
 #include "mfma.h"
 
@@ -50,12 +57,13 @@ CA_HD int vslot(int k) {
 // Cluster-major K / transposed V tiles and centroids (bf16 path)
 // ----------------------------------------------------------------------------
 
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
-  constexpr int RB = 64;                    // rows per LDS block
+  constexpr int RB = 64;                    // rows per LDS block (= one key sub-tile)
   __shared__ __attribute__((aligned(16))) uint16_t skr[RB][D + 8];
   __shared__ __attribute__((aligned(16))) uint16_t sv[RB][D + 8];
   __shared__ float sk[256 / D][D], sm[256 / D][D];
+  __shared__ uint32_t samax[4];
   const int j = blockIdx.x, bh = blockIdx.y;
   const int c = a.c, nc = a.nc, ncp = attn_ncp(nc);
   const int tid = threadIdx.x;
@@ -72,12 +80,14 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
   const int32_t* perm = a.perm_k ? a.perm_k + (int64_t)bh * a.N + (int64_t)j * c : nullptr;
   const uint16_t* K = (const uint16_t*)a.K + (int64_t)bh * a.N * D;
   const uint16_t* V = (const uint16_t*)a.V + (int64_t)bh * a.N * D;
-  uint16_t* kc = a.kc + ((int64_t)bh * nc + j) * c * D;
+  uint16_t* kc = FP8 ? nullptr : a.kc + ((int64_t)bh * nc + j) * c * D;
+  uint8_t* kc8 = FP8 ? a.kc8 + ((int64_t)bh * nc + j) * c * D : nullptr;
   uint16_t* vt = a.vt + ((int64_t)bh * nc + j) * (int64_t)D * c;
 
   // Blocks of 64 rows: the K and V chunks of block b + 1 are loaded while
   // block b is summed and transposed out of LDS. K rows go to kc straight from
-  // registers (zero padded past the cluster's end).
+  // registers (zero padded past the cluster's end); with FP8 they go out as
+  // codes once the block's largest magnitude is known.
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   constexpr int LPT = RB * CPR / 256;       // chunks per thread and block
   constexpr int G = 256 / D;
@@ -101,15 +111,34 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
   load(0);
   for (int b = 0; b < nb; ++b) {
     if (b > 0) __syncthreads();   // the previous block's LDS reads are done
+    uint32_t am = 0;              // FP8: largest |k| bits of this thread's chunks
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int e = i * 256 + tid, r = e / CPR, g = e % CPR;
       *reinterpret_cast<u32x4_t*>(&skr[r][8 * g]) = kr[i];
       *reinterpret_cast<u32x4_t*>(&sv[r][8 * g]) = vr[i];
-      *reinterpret_cast<u32x4_t*>(kc + (int64_t)(b * RB + r) * D + 8 * g) = kr[i];
+      if constexpr (FP8) am = amax_bits_bf16x8(kr[i], am);
+      else *reinterpret_cast<u32x4_t*>(kc + (int64_t)(b * RB + r) * D + 8 * g) = kr[i];
     }
-    if (b + 1 < nb) load(b + 1);
+    if constexpr (FP8) {
+      const float wm = wave_max(bf16_to_f32((uint16_t)am));
+      if ((tid & 63) == 0) samax[tid >> 6] = __float_as_uint(wm);
+    } else {
+      if (b + 1 < nb) load(b + 1);
+    }
     __syncthreads();
+    if constexpr (FP8) {
+      const float amax = fmaxf(fmaxf(__uint_as_float(samax[0]), __uint_as_float(samax[1])),
+                               fmaxf(__uint_as_float(samax[2]), __uint_as_float(samax[3])));
+      const float inv = e4m3_inv(amax);
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int e = i * 256 + tid, r = e / CPR, g = e % CPR;
+        *reinterpret_cast<u32x2_t*>(kc8 + (int64_t)(b * RB + r) * D + 8 * g) = e4m3_pack_bf16x8(kr[i], inv);
+      }
+      if (tid == 0) a.kscale[((int64_t)bh * nc + j) * (c / RB) + b] = e4m3_scale(amax);
+      if (b + 1 < nb) load(b + 1);
+    }
     for (int r = grp; r < RB && b * RB + r < nj; r += G) {
       ksum += bf16_to_f32(skr[r][d]);
       vsum += bf16_to_f32(sv[r][d]);
@@ -148,6 +177,35 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
   }
 }
 
+// FP8: key centroids (bf16, written by permute_kv) as e4m3 codes with one
+// scale per 64 consecutive centroids; one workgroup per 64 centroids.
+template <int D>
+__global__ __launch_bounds__(256) void quant_centroids(AttnArgs a) {
+  constexpr int RB = 64, CPR = D / 8, LPT = RB * CPR / 256;
+  __shared__ uint32_t samax[4];
+  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int ncp = attn_ncp(a.nc);
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.kbar_hi + ((int64_t)bh * ncp + blk * RB) * D);
+  uint8_t* dst = a.kbar8 + ((int64_t)bh * ncp + blk * RB) * D;
+  u32x4_t v[LPT];
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    v[i] = src[i * 256 + tid];
+    am = amax_bits_bf16x8(v[i], am);
+  }
+  const float wm = wave_max(bf16_to_f32((uint16_t)am));
+  if ((tid & 63) == 0) samax[tid >> 6] = __float_as_uint(wm);
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(__uint_as_float(samax[0]), __uint_as_float(samax[1])),
+                           fmaxf(__uint_as_float(samax[2]), __uint_as_float(samax[3])));
+  const float inv = e4m3_inv(amax);
+#pragma unroll
+  for (int i = 0; i < LPT; ++i)
+    *reinterpret_cast<u32x2_t*>(dst + (int64_t)(i * 256 + tid) * 8) = e4m3_pack_bf16x8(v[i], inv);
+  if (tid == 0) a.kbscale[(int64_t)bh * (ncp / RB) + blk] = e4m3_scale(amax);
+}
+
 // ----------------------------------------------------------------------------
 // Attention (bf16 MFMA)
 // ----------------------------------------------------------------------------
@@ -157,15 +215,18 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
 // that the 16 lanes an LDS cycle serves (16 consecutive rows at one 16-byte
 // chunk) fall on distinct banks and every operand read is a per-lane base
 // plus a compile-time offset.
-template <int D>
+// With FP8 keys a K row is D bytes (+16 of padding, which again puts the 16
+// rows an LDS cycle serves on distinct banks).
+template <int D, bool FP8 = false>
 struct AttnTile {
   static constexpr int KT = 64;                           // keys per sub-tile
-  static constexpr int KP = D * 2 + 16;                   // K row pitch (bytes)
+  static constexpr int KE = FP8 ? 1 : 2;                  // bytes per key element
+  static constexpr int KP = D * KE + 16;                  // K row pitch (bytes)
   static constexpr int VP = KT * 2 + 16;                  // V^T row pitch (bytes)
   static constexpr int K_BYTES = KT * KP;
   static constexpr int V_BYTES = D * VP;
   static constexpr int BYTES = K_BYTES + V_BYTES;         // one buffer
-  static constexpr int K_CHUNKS = D / 8;                  // 16-byte chunks per K row
+  static constexpr int K_CHUNKS = D * KE / 16;            // 16-byte chunks per K row
   static constexpr int V_CHUNKS = KT / 8;                 // 16-byte chunks per V^T row
   static constexpr int K_LOADS = KT * K_CHUNKS;           // 16-byte loads per sub-tile
   static constexpr int V_LOADS = D * V_CHUNKS;
@@ -181,9 +242,9 @@ CA_DEV int xcd_logical(int b, int G) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
-template <int D, int CQ, int CK, bool DENSE>
+template <int D, int CQ, int CK, bool DENSE, bool FP8>
 __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd(AttnArgs a) {
-  using TL = AttnTile<D>;
+  using TL = AttnTile<D, FP8>;
   constexpr int NT = 2 * CQ;           // threads (CQ/32 waves of 32 queries)
   constexpr int KS = D / 16;           // k-steps over the head dim
   constexpr int NB = D / 32;           // 32-row blocks of O^T
@@ -202,12 +263,43 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
       qvalid ? (DENSE || !a.perm_q ? qpos : clamp_tok(a.perm_q[(int64_t)bh * N + qpos], N)) : 0;
   const uint16_t* Qh = (const uint16_t*)a.Q + (int64_t)bh * N * D;
 
-  bf16x8_t qf[KS];
+  // Query operand. bf16: step s of the contraction covers dims 16s..16s+15,
+  // lane half h supplying 8 of them. FP8: step s covers dims 64s..64s+63,
+  // lane half h supplying the 32 dims from 64s + 32h as e4m3 codes of the
+  // row quantized with its own scale sq (the halves combine their maxima).
+  constexpr int KS8 = D / 64;
+  bf16x8_t qf[FP8 ? 1 : KS];
+  i32x8_t qf8[FP8 ? KS8 : 1];
+  float sq = 1.0f;
+  if constexpr (FP8) {
+    u32x4_t v[KS8][4];
+    uint32_t am = 0;
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (qvalid) v = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)qtok * D + s * 16 + h * 8);
-    qf[s] = as_bf16x8(v);
+    for (int s = 0; s < KS8; ++s)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        v[s][c4] = u32x4_t{0u, 0u, 0u, 0u};
+        if (qvalid) v[s][c4] = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)qtok * D + s * 64 + h * 32 + c4 * 8);
+        am = amax_bits_bf16x8(v[s][c4], am);
+      }
+    const float amax = max_halves(bf16_to_f32((uint16_t)am));
+    const float inv = e4m3_inv(amax);
+    sq = e4m3_scale(amax);
+#pragma unroll
+    for (int s = 0; s < KS8; ++s)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const u32x2_t w = e4m3_pack_bf16x8(v[s][c4], inv);
+        qf8[s][2 * c4] = (int)w.x;
+        qf8[s][2 * c4 + 1] = (int)w.y;
+      }
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (qvalid) v = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)qtok * D + s * 16 + h * 8);
+      qf[s] = as_bf16x8(v);
+    }
   }
   floatx16_t acc[NB];
 #pragma unroll
@@ -242,8 +334,12 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
     return (j >= 0 && j < nc) ? j : -1;
   };
   // stage: 16-byte global loads into registers, then into an LDS buffer
-  constexpr int KLPT = TL::K_LOADS / NT, VLPT = TL::V_LOADS / NT;
+  // (with FP8 and D = 64 a K sub-tile is 256 loads: fewer than 512 threads)
+  constexpr int KLPT = (TL::K_LOADS + NT - 1) / NT, VLPT = TL::V_LOADS / NT;
+  constexpr bool K_ALL = TL::K_LOADS % NT == 0;
+  static_assert(TL::V_LOADS % NT == 0, "V sub-tile loads must divide evenly");
   u32x4_t kst[KLPT], vst[VLPT];
+  float ksc_cur = 1.0f, ksc_nxt = 1.0f;   // FP8: key scale of the current / next sub-tile
   // Every sub-tile is contiguous in HBM (K rows [64][D], V^T rows [D][64],
   // token and centroid tiles alike), so each thread's 16-byte chunks sit at
   // fixed offsets from a per-tile base.
@@ -254,15 +350,27 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
       int j = tile_cluster(t);
       if (j < 0) j = 0;   // any valid tile; its results are not used
       const int part = t % SUB;
-      ks = reinterpret_cast<const u32x4_t*>(a.kc + (((int64_t)bh * nc + j) * CK + part * TL::KT) * D);
+      const int64_t row = ((int64_t)bh * nc + j) * CK + part * TL::KT;
+      if constexpr (FP8) {
+        ks = reinterpret_cast<const u32x4_t*>(a.kc8 + row * D);
+        ksc_nxt = a.kscale[((int64_t)bh * nc + j) * SUB + part];
+      } else {
+        ks = reinterpret_cast<const u32x4_t*>(a.kc + row * D);
+      }
       vs = reinterpret_cast<const u32x4_t*>(a.vt + (((int64_t)bh * nc + j) * SUB + part) * (int64_t)D * TL::KT);
     } else {
       const int ct = t - Tm;
-      ks = reinterpret_cast<const u32x4_t*>(a.kbar_hi + ((int64_t)bh * ncp + ct * TL::KT) * D);
+      if constexpr (FP8) {
+        ks = reinterpret_cast<const u32x4_t*>(a.kbar8 + ((int64_t)bh * ncp + ct * TL::KT) * D);
+        ksc_nxt = a.kbscale[(int64_t)bh * (ncp / TL::KT) + ct];
+      } else {
+        ks = reinterpret_cast<const u32x4_t*>(a.kbar_hi + ((int64_t)bh * ncp + ct * TL::KT) * D);
+      }
       vs = reinterpret_cast<const u32x4_t*>(a.vbar_t + ((int64_t)bh * (ncp / TL::KT) + ct) * D * TL::KT);
     }
 #pragma unroll
-    for (int i = 0; i < KLPT; ++i) kst[i] = ks[i * NT + tid];
+    for (int i = 0; i < KLPT; ++i)
+      if (K_ALL || i * NT + tid < TL::K_LOADS) kst[i] = ks[i * NT + tid];
 #pragma unroll
     for (int i = 0; i < VLPT; ++i) vst[i] = vs[i * NT + tid];
   };
@@ -271,7 +379,8 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
     for (int i = 0; i < KLPT; ++i) {
       const int e = i * NT + tid;
-      *reinterpret_cast<u32x4_t*>(base + (e / TL::K_CHUNKS) * TL::KP + (e % TL::K_CHUNKS) * 16) = kst[i];
+      if (K_ALL || e < TL::K_LOADS)
+        *reinterpret_cast<u32x4_t*>(base + (e / TL::K_CHUNKS) * TL::KP + (e % TL::K_CHUNKS) * 16) = kst[i];
     }
 #pragma unroll
     for (int i = 0; i < VLPT; ++i) {
@@ -280,14 +389,16 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
                                   (e % TL::V_CHUNKS) * 16) = vst[i];
     }
   };
-  // per-lane LDS read bases: K row r, chunk h; V^T row r, chunk h
-  const int kread = r * TL::KP + h * 16;
+  // per-lane LDS read bases: K row r, chunk h (FP8: 32-byte chunk h); V^T
+  // row r, chunk h
+  const int kread = r * TL::KP + h * (FP8 ? 32 : 16);
   const int vread = TL::K_BYTES + r * TL::VP + h * 16;
   const float* logn = a.logn + (int64_t)bh * ncp;
 
   if (T > 0) {
     fetch(0);
     store(0);
+    ksc_cur = ksc_nxt;
   }
   __syncthreads();
   // Sub-tiles that need no masking (full token tiles) run in loops of their
@@ -316,7 +427,16 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
       const int nvalid = cen ? TL::KT : min(CK, N - j * CK) - (t % SUB) * TL::KT;
       // two independent accumulation chains (keys 0-31, 32-63) interleaved
       floatx16_t sacc[2] = {zero16(), zero16()};
-      {
+      if constexpr (FP8) {
+        // 2 x KS8 products of 32 keys x 64 dims; every operand read issued first
+        constexpr int NQ = 2 * KS8;
+        i32x8_t kf[NQ];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i)
+          kf[i] = *reinterpret_cast<const i32x8_t*>(buf + kread + (i & 1) * 32 * TL::KP + (i >> 1) * 64);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) sacc[i & 1] = mfma32_fp8(kf[i], qf8[i >> 1], sacc[i & 1]);
+      } else {
         // operand reads issued PF ahead of their products (ring of PF
         // registers); the schedule is pinned by scheduling barriers
         constexpr int NQ = 2 * KS, PF = 4;
@@ -337,9 +457,13 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
         __builtin_amdgcn_sched_barrier(0);
       }
       // the exponent below is fma(score, scl, -m): token tiles keep raw q.k
-      // (scl = scale log2 e), centroid tiles are turned into log2 units here
-      float scl = sl2;
+      // (scl = scale log2 e, times s_q s_k with FP8), centroid tiles are
+      // turned into log2 units here
+      // (floored at the smallest normal fp32 so that a zero query or key
+      // block gives logits 0, and masked keys stay at -inf)
+      float scl = FP8 ? fmaxf(sl2 * sq * ksc_cur, __FLT_MIN__) : sl2;
       if (SPECIAL && cen) {
+        const float sc = scl;
         scl = 1.0f;
         const int c0 = (t - Tm) * TL::KT;
 #pragma unroll
@@ -353,7 +477,7 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
             for (int e = 0; e < 4; ++e) {
               const bool excluded = !((selw >> ((k0 + e) & 31)) & 1u);
               const float bias = excluded ? ln[e] * kLog2e : kNegInf;
-              sacc[kb][4 * q + e] = fmaf(sacc[kb][4 * q + e], sl2, bias);
+              sacc[kb][4 * q + e] = fmaf(sacc[kb][4 * q + e], sc, bias);
             }
           }
       } else if (SPECIAL && nvalid < TL::KT) {
@@ -421,6 +545,7 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
     }
     if (t + 1 < T) store((t + 1) & 1);
+    ksc_cur = ksc_nxt;
     __syncthreads();
   };
   auto run = [&](int t0, int t1, auto special_tag) __attribute__((always_inline)) {
@@ -454,9 +579,9 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
   if (a.lse && h == 0) a.lse[(int64_t)bh * N + qtok] = (m + log2f(lsum)) * kLn2;
 }
 
-template <int D, int C>
+template <int D, bool FP8>
 constexpr size_t attn_smem() {
-  return 2 * (size_t)AttnTile<D>::BYTES + 8192 / 8 + 64;   // two buffers, selection bits
+  return 2 * (size_t)AttnTile<D, FP8>::BYTES + 8192 / 8 + 64;   // two buffers, selection bits
 }
 
 // ----------------------------------------------------------------------------
@@ -577,38 +702,48 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
   if (a.lse) a.lse[(int64_t)bh * N + qtok] = m + logf(lsum);
 }
 
-template <int D, int CQ, int CK, bool DENSE>
+template <int D, int CQ, int CK, bool DENSE, bool FP8>
 void launch_mfma(const AttnArgs& a, hipStream_t st) {
-  const size_t sm = attn_smem<D, CQ>();
+  const size_t sm = attn_smem<D, FP8>();
   static bool attr_set = false;   // raise the dynamic-LDS limit once per instantiation
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd<D, CQ, CK, DENSE>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd<D, CQ, CK, DENSE, FP8>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     attr_set = true;
   }
   dim3 g(a.nqc, a.BH);
   if (a.ev_start) (void)hipEventRecord(a.ev_start, st);
-  attn_fwd<D, CQ, CK, DENSE><<<g, 2 * CQ, sm, st>>>(a);
+  attn_fwd<D, CQ, CK, DENSE, FP8><<<g, 2 * CQ, sm, st>>>(a);
   if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);
 }
 
-template <int D>
-void launch_bf16(const AttnArgs& a, bool dense, hipStream_t st) {
+template <int D, bool FP8>
+void launch_tiles(const AttnArgs& a, bool dense, hipStream_t st) {
   dim3 gp(attn_ncp(a.nc), a.BH);
-  permute_kv<D><<<gp, 256, 0, st>>>(a);
+  permute_kv<D, FP8><<<gp, 256, 0, st>>>(a);
+  if (FP8 && !dense && a.compensate) {
+    dim3 gq(attn_ncp(a.nc) / 64, a.BH);
+    quant_centroids<D><<<gq, 256, 0, st>>>(a);
+  }
   if (dense) {
-    launch_mfma<D, 128, 128, true>(a, st);
+    launch_mfma<D, 128, 128, true, FP8>(a, st);
     return;
   }
   // (query, key) cluster sizes: equal, or the key clusters larger
   switch (a.cq * 1000 + a.c) {
-    case 64064: launch_mfma<D, 64, 64, false>(a, st); break;
-    case 64128: launch_mfma<D, 64, 128, false>(a, st); break;
-    case 64256: launch_mfma<D, 64, 256, false>(a, st); break;
-    case 128128: launch_mfma<D, 128, 128, false>(a, st); break;
-    case 128256: launch_mfma<D, 128, 256, false>(a, st); break;
-    default: launch_mfma<D, 256, 256, false>(a, st); break;
+    case 64064: launch_mfma<D, 64, 64, false, FP8>(a, st); break;
+    case 64128: launch_mfma<D, 64, 128, false, FP8>(a, st); break;
+    case 64256: launch_mfma<D, 64, 256, false, FP8>(a, st); break;
+    case 128128: launch_mfma<D, 128, 128, false, FP8>(a, st); break;
+    case 128256: launch_mfma<D, 128, 256, false, FP8>(a, st); break;
+    default: launch_mfma<D, 256, 256, false, FP8>(a, st); break;
   }
+}
+
+template <int D>
+void launch_bf16(const AttnArgs& a, bool dense, hipStream_t st) {
+  if (a.dtype == 2) launch_tiles<D, true>(a, dense, st);
+  else launch_tiles<D, false>(a, dense, st);
 }
 
 template <int D>
@@ -631,7 +766,7 @@ void launch_f32(const AttnArgs& a, bool dense, hipStream_t st) {
 }  // namespace
 
 void launch_attend(const AttnArgs& a, hipStream_t st) {
-  if (a.dtype == 0) {
+  if (a.dtype != 1) {
     if (a.D == 64) launch_bf16<64>(a, false, st); else launch_bf16<128>(a, false, st);
   } else {
     if (a.D == 64) launch_f32<64>(a, false, st); else launch_f32<128>(a, false, st);
@@ -639,7 +774,7 @@ void launch_attend(const AttnArgs& a, hipStream_t st) {
 }
 
 void launch_dense(const AttnArgs& a, hipStream_t st) {
-  if (a.dtype == 0) {
+  if (a.dtype != 1) {
     if (a.D == 64) launch_bf16<64>(a, true, st); else launch_bf16<128>(a, true, st);
   } else {
     if (a.D == 64) launch_f32<64>(a, true, st); else launch_f32<128>(a, true, st);

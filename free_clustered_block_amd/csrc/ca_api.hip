@@ -101,6 +101,16 @@ void plan_attend(Carver& cv, AttnArgs& a, bool with_tiles) {
   a.logn = cv.take<float>(BH * ncp);
   a.kbar32 = cv.take<float>(BH * ncp * D);
   a.vbar32 = cv.take<float>(BH * ncp * D);
+  if (a.dtype == 2 && with_tiles) {
+    // FP8 keys: the codes take the first half of the bf16 key tiles and the
+    // sub-tile scales the second; the centroid codes and scales take the
+    // fp32 centroid arrays, which only the fp32 path uses
+    a.kc8 = reinterpret_cast<uint8_t*>(a.kc);
+    a.kscale = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.kc) + BH * nc * c * D);
+    a.kbar8 = reinterpret_cast<uint8_t*>(a.kbar32);
+    a.kbscale = a.vbar32;
+    a.kc = nullptr;
+  }
 }
 
 constexpr int kDenseTile = 128;
@@ -130,8 +140,9 @@ int after_launch() {
   return CA_OK;
 }
 
-int check_common(int dt, int B, int H, int N, int D) {
-  if (dt != CA_BF16 && dt != CA_F32) return fail(CA_ERR_INVALID_ARG, "unknown dtype");
+int check_common(int dt, int B, int H, int N, int D, bool fp8_ok = false) {
+  if (dt != CA_BF16 && dt != CA_F32 && !(fp8_ok && dt == CA_BF16_FP8))
+    return fail(CA_ERR_INVALID_ARG, fp8_ok ? "unknown dtype" : "unknown dtype (CA_BF16_FP8 is for attention only)");
   if (B < 1 || H < 1 || N < 1 || D < 1) return fail(CA_ERR_INVALID_ARG, "B, H, N, D must be >= 1");
   if ((int64_t)B * H > 32767) return fail(CA_ERR_UNSUPPORTED, "B*H must be <= 32767");
   if ((int64_t)B * H * N >= (int64_t)1 << 31) return fail(CA_ERR_INVALID_ARG, "B*H*N must be < 2^31");
@@ -337,7 +348,7 @@ int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B,
   set_error("");
   if (!Q || !K || !V || !perm_q || !perm_k || !blocks || !O)
     return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
-  if (int e = check_common(dt, B, H, N, D)) return e;
+  if (int e = check_common(dt, B, H, N, D, true)) return e;
   const int c = cluster_size_k, cq = cluster_size_q;
   if (!supported_c(c) || !supported_c(cq))
     return fail(CA_ERR_UNSUPPORTED, "cluster sizes must be 64, 128 or 256");
@@ -349,7 +360,7 @@ int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B,
   if (topk < 1 || topk > nc) return fail(CA_ERR_INVALID_ARG, "topk must be in [1, n_kc]");
   if (!(scale >= 0.0f) || !std::isfinite(scale)) return fail(CA_ERR_INVALID_ARG, "scale must be finite and >= 0");
   AttnArgs a{};
-  a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : 1;
+  a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : (dt == CA_F32 ? 1 : 2);
   a.BH = B * H; a.N = N; a.D = D; a.c = c; a.nc = nc; a.cq = cq; a.nqc = nqc; a.topk = topk;
   a.compensate = compensate ? 1 : 0;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
@@ -396,10 +407,10 @@ int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, in
              float scale, void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
   set_error("");
   if (!Q || !K || !V || !O) return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
-  if (int e = check_common(dt, B, H, N, D)) return e;
+  if (int e = check_common(dt, B, H, N, D, true)) return e;
   if (!(scale >= 0.0f) || !std::isfinite(scale)) return fail(CA_ERR_INVALID_ARG, "scale must be finite and >= 0");
   AttnArgs a{};
-  a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : 1;
+  a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : (dt == CA_F32 ? 1 : 2);
   a.BH = B * H; a.N = N; a.D = D; a.c = kDenseTile; a.nc = (N + kDenseTile - 1) / kDenseTile;
   a.cq = a.c; a.nqc = a.nc;
   a.topk = a.nc; a.compensate = 0;
@@ -410,6 +421,19 @@ int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, in
   plan_attend(cv, a, true);
   if (int e = check_ws(ws, ws_bytes, cv.size())) return e;
   launch_dense(a, static_cast<hipStream_t>(stream));
+  return after_launch();
+}
+
+int ca_quantize_e4m3(const void* X, ca_dtype dt, int64_t rows, int D, int group, uint8_t* codes,
+                     float* scales, void* stream) {
+  set_error("");
+  if (!X || !codes || !scales) return fail(CA_ERR_INVALID_ARG, "null pointer");
+  if (dt != CA_BF16 && dt != CA_F32) return fail(CA_ERR_INVALID_ARG, "dtype must be CA_BF16 or CA_F32");
+  if (rows < 1 || D < 1 || group < 1) return fail(CA_ERR_INVALID_ARG, "rows, D and group must be >= 1");
+  if (rows * (int64_t)D >= ((int64_t)1 << 31) || (int64_t)group * D >= ((int64_t)1 << 31))
+    return fail(CA_ERR_INVALID_ARG, "rows * D and group * D must be < 2^31");
+  launch_quantize_e4m3(X, dt == CA_BF16 ? 0 : 1, rows, D, group, codes, scales,
+                       static_cast<hipStream_t>(stream));
   return after_launch();
 }
 

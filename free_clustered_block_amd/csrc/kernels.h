@@ -85,7 +85,7 @@ struct AttnArgs {
   const void* Q;
   const void* K;
   const void* V;
-  int dtype;
+  int dtype;   // 0 bf16, 1 fp32, 2 bf16 with FP8 (e4m3) Q.K^T operands
   int BH, N, D, c, nc, topk, compensate;   // c, nc: key cluster size and count
   int cq, nqc;                             // query cluster size and count
   float scale;
@@ -103,6 +103,11 @@ struct AttnArgs {
   float* logn;        // [BH][ncp]
   float* kbar32;      // [BH][ncp][D]
   float* vbar32;      // [BH][ncp][D]
+  // scratch of the FP8 variant (carved from kc, kbar32 and vbar32)
+  uint8_t* kc8;       // [BH][nc][c][D]   key codes, cluster-major, zero padded
+  float* kscale;      // [BH][nc][c/64]   one scale per 64-key sub-tile
+  uint8_t* kbar8;     // [BH][ncp][D]     key-centroid codes
+  float* kbscale;     // [BH][ncp/64]     one scale per 64 centroids
   // optional events recorded around the main attention kernel
   hipEvent_t ev_start;
   hipEvent_t ev_stop;
@@ -115,5 +120,8 @@ void launch_attend(const AttnArgs& a, hipStream_t st);
 void launch_peak_mfma(int blocks, int iters, float* out, hipStream_t st);
 void launch_peak_lds(int blocks, int iters, float* out, hipStream_t st);
 void launch_dense(const AttnArgs& a, hipStream_t st);
+// quant.hip ------------------------------------------------------------------
+void launch_quantize_e4m3(const void* X, int dtype, int64_t rows, int D, int group, uint8_t* codes,
+                          float* scales, hipStream_t st);
 
 }  // namespace ca

@@ -53,7 +53,10 @@ typedef enum {
 
 typedef enum {
   CA_BF16 = 0,             /* bfloat16 inputs and outputs, fp32 accumulation */
-  CA_F32 = 1               /* float32 throughout                             */
+  CA_F32 = 1,              /* float32 throughout                             */
+  CA_BF16_FP8 = 2          /* attention only (ca_attend*, ca_dense): bfloat16
+                              inputs and outputs, the Q.K^T product on FP8
+                              (OCP E4M3) operands, P.V as with CA_BF16       */
 } ca_dtype;
 
 typedef enum {
@@ -282,6 +285,37 @@ int ca_attend_ex(const void* Q, const void* K, const void* V, ca_dtype dt, int B
                  int cluster_size_k, const int32_t* blocks, const int32_t* nsel, int max_sel,
                  int compensate, float scale, void* O, float* lse, void* ws, size_t ws_bytes,
                  void* stream);
+
+/*
+ * FP8 attention (dtype CA_BF16_FP8 in ca_attend, ca_attend_var, ca_attend_ex
+ * and ca_dense). The pages' kernel is quantized and is compared with
+ * quantized dense attention (v1 §4.1 "Baselines"); the scheme is not given
+ * there, so this one is stated: each query row is one group, the keys of a
+ * cluster form groups of 64 consecutive members of its permutation (a short
+ * cluster's last group holds its valid members; ca_dense: 64 consecutive
+ * tokens), and with compensation the key centroids, rounded to bf16, form
+ * groups of 64 consecutive clusters. A group is quantized as by
+ * ca_quantize_e4m3; the logit is scale * s_q * s_k * sum(code_q * code_k)
+ * accumulated in fp32. Values, P.V and the output are as with CA_BF16. The
+ * workspace is that of CA_BF16.
+ */
+
+/*
+ * ca_quantize_e4m3 -- rows to FP8 (OCP E4M3) codes, one scale per group of
+ * `group` consecutive rows (the last group may be short): amax = max |x| over
+ * the group, inv = fp32(448 / amax) (0 for an all-zero group), code =
+ * e4m3(fp32(x * inv)) rounded to nearest even (sign kept, so -0 gives 0x80),
+ * scale = fp32(amax / 448); x is recovered as code value * scale. The
+ * attention's FP8 operands are made by the same device code.
+ *
+ * X       [rows, D] of type dt (CA_BF16 or CA_F32; device, read only).
+ * codes   out uint8 [rows, D] (device).
+ * scales  out float [ceil(rows / group)] (device).
+ * Errors: CA_ERR_INVALID_ARG for null pointers, another dtype, rows, D or
+ * group < 1, rows * D or group * D >= 2^31. Inputs must be finite.
+ */
+int ca_quantize_e4m3(const void* X, ca_dtype dt, int64_t rows, int D, int group, uint8_t* codes,
+                     float* scales, void* stream);
 
 /*
  * ca_dense -- dense attention baseline, o_i = sum_j softmax_j(scale q_i.k_j) v_j

@@ -22,7 +22,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ca_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ca_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -152,3 +152,23 @@ def test_peak_probe_rejects_bad_arguments(lib):
     assert lib.ca_peak_probe(0, 0, 1, FAKE, None) == 1
     assert lib.ca_peak_probe(1, 1, 0, FAKE, None) == 1
     assert lib.ca_peak_probe(0, 1, 1, None, None) == 1
+
+
+def test_fp8_dtype_and_quantize_reject_bad_arguments(lib):
+    # CA_BF16_FP8 (2) is for attention only: ca_cluster rejects it, ca_dense
+    # and ca_attend take it (then fail here on the workspace, nothing launched)
+    assert _cluster(lib, dt=2) == 1
+    assert b"attention only" in lib.ca_last_error()
+    assert lib.ca_dense(FAKE, FAKE, FAKE, 2, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 8, None) == 3
+    assert lib.ca_dense(FAKE, FAKE, FAKE, 3, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 8, None) == 1
+    assert _attend(lib, dt=2, ws_bytes=10) == 3
+    q = lib.ca_quantize_e4m3
+    # X, dt, rows, D, group, codes, scales, stream
+    assert q(None, 0, 4, 64, 1, FAKE, FAKE, None) == 1
+    assert q(FAKE, 0, 4, 64, 1, None, FAKE, None) == 1
+    assert q(FAKE, 0, 4, 64, 1, FAKE, None, None) == 1
+    assert q(FAKE, 2, 4, 64, 1, FAKE, FAKE, None) == 1
+    assert q(FAKE, 0, 0, 64, 1, FAKE, FAKE, None) == 1
+    assert q(FAKE, 0, 4, 0, 1, FAKE, FAKE, None) == 1
+    assert q(FAKE, 0, 4, 64, 0, FAKE, FAKE, None) == 1
+    assert q(FAKE, 1, 1 << 25, 64, 1, FAKE, FAKE, None) == 1
