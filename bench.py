@@ -40,12 +40,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "ClusterAttention fwd latency, eff. TFLOP/s & speedup vs dense at N=32k, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+# FP8 Q.K^T with bf16 P.V: half the FLOPs at each rate, so the bound on the
+# whole count is 4 / (2 / 5000 + 2 / 2500) TFLOP/s
+PEAK_FP8QK_TFLOPS = 4.0 / (2.0 / PEAK_FP8_TFLOPS + 2.0 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 # HBM bytes per attention launch from rocprofv3 FETCH_SIZE + WRITE_SIZE runs,
 # scaled by the same counters on a plain copy; valid only for the kernel
 # sources whose digest the file records.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_video_32760_traffic.txt")
-ATTN_SOURCES = ["attn.hip", "mfma.h", "common.h", "kernels.h"]
+TRAFFIC_FILE_FP8 = os.path.join(ROOT, "profiles", "attn_fwd_fp8_video_32760_traffic.txt")
+ATTN_SOURCES = ["attn.hip", "fp8.h", "mfma.h", "common.h", "kernels.h"]
 
 
 def attn_source_digest() -> str:
@@ -56,12 +61,12 @@ def attn_source_digest() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str, topk: int):
+def recorded_traffic(workload: str, topk: int, fp8: bool = False):
     """HBM bytes per attention launch recorded for this workload and these
     kernel sources, or None."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as fh:
+        with open(TRAFFIC_FILE_FP8 if fp8 else TRAFFIC_FILE) as fh:
             for line in fh:
                 if ":" in line and not line.startswith(("#", " ", "|")):
                     k, v = line.split(":", 1)
@@ -99,6 +104,9 @@ def parse():
                     help="top-k selection, or adaptive selection to a mass recall")
     ap.add_argument("--recall", type=float, default=0.9, help="mass recall of --assign adaptive")
     ap.add_argument("--min-count", type=int, default=16, help="minimum count of --assign adaptive")
+    ap.add_argument("--fp8", action="store_true",
+                    help="Q.K^T on FP8 (E4M3) operands in the attention and in the dense "
+                         "baseline (dtype CA_BF16_FP8); P.V stays bf16")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="quality/latency sweep over cluster size, selected fraction, SMC and "
@@ -117,7 +125,7 @@ def gen_inputs(w):
 
 
 def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power", assign="topk", recall=0.9,
-                 min_count=16):
+                 min_count=16, qk="exact"):
     """The oracle, untuned, on the first `heads` heads of the same input."""
     import oracle.clusterattn as o
     try:
@@ -129,7 +137,8 @@ def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power", assign="topk", rec
                          query_normalize=assign == "topk")
     t0 = time.perf_counter()
     if assign == "topk":
-        o.forward(Q[:, :heads], K[:, :heads], V[:, :heads], w.c, topk, w.compensate, opts, w.dtype)
+        o.forward(Q[:, :heads], K[:, :heads], V[:, :heads], w.c, topk, w.compensate, opts, w.dtype,
+                  qk=qk)
     else:
         Qs, Ks, Vs = Q[:, :heads], K[:, :heads], V[:, :heads]
         pq, pk = o.cluster(Qs, Ks, w.c, opts, w.dtype)
@@ -140,7 +149,7 @@ def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power", assign="topk", rec
                 cq, _ = o.centroids(Qs[b, h], pq[b, h], w.c)
                 ck, cnt = o.centroids(Ks[b, h], pk[b, h], w.c)
                 sel[b][h] = o.route_adaptive(cq, ck, cnt, tau, recall, min_count)
-        o.attend(Qs, Ks, Vs, pq, pk, w.c, sel, w.compensate)
+        o.attend(Qs, Ks, Vs, pq, pk, w.c, sel, w.compensate, qk=qk)
     t = time.perf_counter() - t0
     flops = 4.0 * w.D * w.N * w.N * heads * w.B
     return {
@@ -149,7 +158,8 @@ def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power", assign="topk", rec
         "cores": int(cores),
         "kind": "oracle",
         "sample": f"{heads} of {w.H} heads of the same workload, full N={w.N}; "
-                  f"{t:.2f} s wall for cluster+route+attend in fp64 NumPy "
+                  f"{t:.2f} s wall for cluster+route+attend in fp64 NumPy"
+                  f"{' (FP8 Q.K^T operands)' if qk == 'e4m3' else ''} "
                   f"(BLAS threads={cores}; PDDP and top-k loops single-threaded Python)",
         "seconds": t,
     }
@@ -351,7 +361,7 @@ def main():
             evs[2].record()
             ca.profile_events(kev[0].handle, kev[1].handle)
         O = ca.attend(Q, K, V, cr.perm_q, cr.perm_k, cq, blocks, compensate=w.compensate,
-                      nsel=nsel, c_k=c, workspace=ws_a)
+                      nsel=nsel, c_k=c, fp8=args.fp8, workspace=ws_a)
         if evs:
             ca.profile_events(None, None)
             evs[3].record()
@@ -441,8 +451,9 @@ def main():
     clu_ms = float(st_cluster + st_route)
     clu_gbs = clu_bytes / (clu_ms * 1e-3) / 1e9
 
-    traffic = (recorded_traffic(w.name, topk) if B * H == w.B * w.H and not adaptive
+    traffic = (recorded_traffic(w.name, topk, args.fp8) if B * H == w.B * w.H and not adaptive
                and args.split_mode == "power" and cq == c else None)
+    peak = PEAK_FP8QK_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     eff = 4.0 * D * N * N * B * H / (wall) / 1e12
     result = {
         "metric": METRIC,
@@ -455,11 +466,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": ("fp8e4m3 (Q.K^T) + bf16 (P.V)" if args.fp8
+                  else "bf16" if w.dtype == "bf16" else "f32"),
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "N": N, "head_dim": D,
                    "cluster_size": c, "topk": topk, "compensate": w.compensate,
                    "split_mode": args.split_mode, "assign": args.assign,
+                   **({"qk_operands": "fp8 e4m3, per-token query / per-64-key scales"}
+                      if args.fp8 else {}),
                    **({"query_cluster_size": cq} if cq != c else {}),
                    **({"recall": args.recall, "min_count": args.min_count,
                        "mean_selected": round(mean_sel, 2)} if adaptive else {})},
@@ -476,9 +490,11 @@ def main():
             "kernel": "attn_fwd (block-sparse attention + SMC)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": round(peak, 1),
+            **({"peak_note": "half the FLOPs (Q.K^T) at the fp8 5.0 PFLOP/s peak, half "
+                             "(P.V) at the bf16 2.5 PFLOP/s peak"} if args.fp8 else {}),
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "flops_per_launch": flops_attn,
         },
@@ -490,21 +506,36 @@ def main():
 
     if not args.no_dense:
         ws_d = torch.empty(ca.workspace_size(ca.OP_DENSE, B, H, N, D), dtype=torch.uint8, device=dev)
-        Od = ca.dense(Q, K, V, workspace=ws_d)
-        torch.cuda.synchronize()
-        de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.dense_steps)]
-        for a, b in de:
-            a.record()
-            Od = ca.dense(Q, K, V, workspace=ws_d)
-            b.record()
-        torch.cuda.synchronize()
-        dense_ms = float(np.mean([a.elapsed_time(b) for a, b in de]))
-        cos = torch.nn.functional.cosine_similarity(O.float(), Od.float(), dim=-1).mean().item()
+
+        def time_dense(fp8):
+            Od = ca.dense(Q, K, V, fp8=fp8, workspace=ws_d)
+            torch.cuda.synchronize()
+            de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.dense_steps)]
+            for a, b in de:
+                a.record()
+                Od = ca.dense(Q, K, V, fp8=fp8, workspace=ws_d)
+                b.record()
+            torch.cuda.synchronize()
+            return Od, float(np.mean([a.elapsed_time(b) for a, b in de]))
+
+        def cosine(x, y):
+            return torch.nn.functional.cosine_similarity(x.float(), y.float(), dim=-1).mean().item()
+
+        # the dense baseline in the path's own precision ("given equal
+        # quantization"); with --fp8 the bf16 dense output is the reference of
+        # both cosines
+        Od, dense_ms = time_dense(args.fp8)
         result["dense_ms"] = round(dense_ms, 4)
         result["speedup_vs_dense"] = round(dense_ms / (wall * 1e3), 3)
         result["dense_tflops"] = round(4.0 * D * N * N * B * H / (dense_ms * 1e-3) / 1e12, 2)
-        result["cos_vs_dense"] = round(cos, 5)
+        if args.fp8:
+            Ob, dense_bf16_ms = time_dense(False)
+            result["dense_bf16_ms"] = round(dense_bf16_ms, 4)
+            result["cos_vs_dense"] = round(cosine(O, Ob), 5)
+            result["cos_dense_fp8_vs_dense_bf16"] = round(cosine(Od, Ob), 5)
+        else:
+            result["cos_vs_dense"] = round(cosine(O, Od), 5)
 
     if not args.no_peaks:
         result["measured_peaks"] = measure_peaks(torch, dev)
@@ -512,7 +543,8 @@ def main():
     if not args.no_cpu_baseline:
         heads = max(1, min(args.cpu_heads, H))
         result["cpu_baseline"] = cpu_baseline(w, Qn, Kn, Vn, topk, heads, args.split_mode,
-                                              args.assign, args.recall, args.min_count)
+                                              args.assign, args.recall, args.min_count,
+                                              "e4m3" if args.fp8 else "exact")
 
     print(json.dumps(result), flush=True)
 
