@@ -242,10 +242,15 @@ CA_DEV int xcd_logical(int b, int G) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
-template <int D, int CQ, int CK, bool DENSE, bool FP8>
-__global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd(AttnArgs a) {
+// KSPL = 2 (64-query clusters): the workgroup has two waves per 32 queries,
+// each taking one 32-key half of every sub-tile with its own running maximum,
+// sum and accumulators, merged through LDS at the end. This keeps four waves
+// (and the per-thread share of the tile loads) of a 128-query workgroup.
+template <int D, int CQ, int CK, bool DENSE, bool FP8, int KSPL>
+__global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd(AttnArgs a) {
   using TL = AttnTile<D, FP8>;
-  constexpr int NT = 2 * CQ;           // threads (CQ/32 waves of 32 queries)
+  constexpr int NT = 2 * CQ * KSPL;    // threads: CQ/32 query groups x KSPL key halves
+  constexpr int NKB = 2 / KSPL;        // 32-key blocks of a sub-tile per wave
   constexpr int KS = D / 16;           // k-steps over the head dim
   constexpr int NB = D / 32;           // 32-row blocks of O^T
   constexpr int SUB = CK / TL::KT;     // sub-tiles per key cluster
@@ -257,7 +262,9 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int nc = a.nc, nqc = a.nqc, N = a.N;   // key clusters, query clusters
   const int qa = lg % nqc, bh = lg / nqc;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
-  const int qpos = qa * CQ + w * 32 + r;
+  const int qg = w % (CQ / 32);                                             // query group
+  const int kh = KSPL == 1 ? 0 : __builtin_amdgcn_readfirstlane(w / (CQ / 32));   // key half
+  const int qpos = qa * CQ + qg * 32 + r;
   const bool qvalid = qpos < N;
   const int qtok =
       qvalid ? (DENSE || !a.perm_q ? qpos : clamp_tok(a.perm_q[(int64_t)bh * N + qpos], N)) : 0;
@@ -425,36 +432,42 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (j >= 0) {
       const unsigned char* buf = smem + (t & 1) * TL::BYTES;
       const int nvalid = cen ? TL::KT : min(CK, N - j * CK) - (t % SUB) * TL::KT;
-      // two independent accumulation chains (keys 0-31, 32-63) interleaved
+      // two independent accumulation chains interleaved: the two 32-key
+      // blocks, or (KSPL = 2) the even and odd k-steps of the wave's block,
+      // added afterwards. Product i covers key block kbg(i) and k-step s(i).
       floatx16_t sacc[2] = {zero16(), zero16()};
+      auto kblk = [&](int i) { return KSPL == 1 ? (i & 1) : kh; };
       if constexpr (FP8) {
-        // 2 x KS8 products of 32 keys x 64 dims; every operand read issued first
-        constexpr int NQ = 2 * KS8;
+        // NKB x KS8 products of 32 keys x 64 dims; every operand read issued first
+        constexpr int NQ = NKB * KS8;
         i32x8_t kf[NQ];
 #pragma unroll
         for (int i = 0; i < NQ; ++i)
-          kf[i] = *reinterpret_cast<const i32x8_t*>(buf + kread + (i & 1) * 32 * TL::KP + (i >> 1) * 64);
+          kf[i] = *reinterpret_cast<const i32x8_t*>(buf + kread + kblk(i) * 32 * TL::KP + (i / NKB) * 64);
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) sacc[i & 1] = mfma32_fp8(kf[i], qf8[i >> 1], sacc[i & 1]);
+        for (int i = 0; i < NQ; ++i) sacc[i & 1] = mfma32_fp8(kf[i], qf8[i / NKB], sacc[i & 1]);
       } else {
         // operand reads issued PF ahead of their products (ring of PF
         // registers); the schedule is pinned by scheduling barriers
-        constexpr int NQ = 2 * KS, PF = 4;
+        constexpr int NQ = NKB * KS, PF = 4;
         bf16x8_t ring[PF];
 #pragma unroll
         for (int i = 0; i < PF; ++i)
-          ring[i] = *reinterpret_cast<const bf16x8_t*>(buf + kread + (i & 1) * 32 * TL::KP + (i >> 1) * 32);
+          ring[i] = *reinterpret_cast<const bf16x8_t*>(buf + kread + kblk(i) * 32 * TL::KP + (i / NKB) * 32);
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
           __builtin_amdgcn_sched_barrier(0);
-          const int kb = i & 1, s = i >> 1;
-          sacc[kb] = mfma32(ring[i % PF], qf[s], sacc[kb]);
+          sacc[i & 1] = mfma32(ring[i % PF], qf[i / NKB], sacc[i & 1]);
           if (i + PF < NQ) {
             const int j = i + PF;
-            ring[i % PF] = *reinterpret_cast<const bf16x8_t*>(buf + kread + (j & 1) * 32 * TL::KP + (j >> 1) * 32);
+            ring[i % PF] = *reinterpret_cast<const bf16x8_t*>(buf + kread + kblk(j) * 32 * TL::KP + (j / NKB) * 32);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (KSPL == 2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[0][i] += sacc[1][i];
       }
       // the exponent below is fma(score, scl, -m): token tiles keep raw q.k
       // (scl = scale log2 e, times s_q s_k with FP8), centroid tiles are
@@ -467,10 +480,10 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
         scl = 1.0f;
         const int c0 = (t - Tm) * TL::KT;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int k0 = c0 + kb * 32 + 8 * q + 4 * h;
+            const int k0 = c0 + (KSPL == 1 ? kb : kh) * 32 + 8 * q + 4 * h;
             const floatx4_t ln = *reinterpret_cast<const floatx4_t*>(logn + k0);
             const uint32_t selw = sSel[k0 >> 5];
 #pragma unroll
@@ -482,10 +495,10 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
           }
       } else if (SPECIAL && nvalid < TL::KT) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const bool out = kb * 32 + c_row(i, h) >= nvalid;
+            const bool out = (KSPL == 1 ? kb : kh) * 32 + c_row(i, h) >= nvalid;
             sacc[kb][i] = out ? kNegInf : sacc[kb][i];
           }
       }
@@ -495,7 +508,7 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
       // l, which uses the same m)
       float bm = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) bm = fmaxf(bm, sacc[i >> 4][i & 15]);
+      for (int i = 0; i < 16 * NKB; ++i) bm = fmaxf(bm, sacc[i >> 4][i & 15]);
       bm = max_halves(bm) * scl;
       const bool grow = bm > m + kLazy;
       if (__ballot(grow)) [[unlikely]] {
@@ -509,28 +522,29 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
         m = mn;
       }
       const float nm = m == kNegInf ? 0.0f : -m;   // nothing valid yet: P = 0
-      float tv[32];
+      float tv[16 * NKB];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) tv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 4][i & 15], scl, nm));
+      for (int i = 0; i < 16 * NKB; ++i) tv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 4][i & 15], scl, nm));
       // P enters the P.V product as bf16; the denominator sums the same
       // rounded values, so the output stays a convex combination of values
-      bf16x8_t pk[4];
+      bf16x8_t pk[2 * NKB];
       float ps = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 2 * NKB; ++q) {
         const u32x4_t u = pack8(tv + 8 * q);
         ps = sum_bf16x8(u, ps);
         pk[q] = as_bf16x8(u);
       }
       lsum += ps;   // this lane's keys; the halves are added at the end
       {
-        // keys 16q .. 16q+15 of the sub-tile: V^T chunk 2q + h; reads issued
-        // PF ahead of their products
-        constexpr int NV = 4 * NB, PF = 4;
+        // keys 16q .. 16q+15 of the sub-tile: V^T chunk 2q + h (q counted
+        // from the wave's key half); reads issued PF ahead of their products
+        constexpr int NV = 2 * NKB * NB, PF = 4;
+        const int vq0 = 2 * kh;
         bf16x8_t ring[PF];
 #pragma unroll
         for (int i = 0; i < PF; ++i)
-          ring[i] = *reinterpret_cast<const bf16x8_t*>(buf + vread + (i % NB) * 32 * TL::VP + (i / NB) * 32);
+          ring[i] = *reinterpret_cast<const bf16x8_t*>(buf + vread + (i % NB) * 32 * TL::VP + (vq0 + i / NB) * 32);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
           __builtin_amdgcn_sched_barrier(0);
@@ -538,7 +552,7 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
           acc[nb] = mfma32(ring[i % PF], pk[q], acc[nb]);
           if (i + PF < NV) {
             const int j = i + PF;
-            ring[i % PF] = *reinterpret_cast<const bf16x8_t*>(buf + vread + (j % NB) * 32 * TL::VP + (j / NB) * 32);
+            ring[i % PF] = *reinterpret_cast<const bf16x8_t*>(buf + vread + (j % NB) * 32 * TL::VP + (vq0 + j / NB) * 32);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -562,6 +576,34 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
   run(Tm, T, std::true_type{});
 
   lsum = sum_halves(lsum);
+  if constexpr (KSPL == 2) {
+    // merge the key halves: the second wave of each query group leaves its
+    // maximum, sum and accumulators in LDS (the tile buffers are free after
+    // the last barrier), the first rescales both to the larger maximum
+    constexpr int XE = 16 * NB + 2;   // floats per lane
+    static_assert((CQ / 32) * XE * 64 * 4 <= 2 * TL::BYTES, "exchange fits the tile buffers");
+    float* xch = reinterpret_cast<float*>(smem) + (size_t)qg * XE * 64 + l;
+    if (kh == 1) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[(nb * 16 + i) * 64] = acc[nb][i];
+      xch[16 * NB * 64] = m;
+      xch[(16 * NB + 1) * 64] = lsum;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = xch[16 * NB * 64], l1 = xch[(16 * NB + 1) * 64];
+    const float mn = fmaxf(m, m1);
+    const float a0 = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+    const float a1 = m1 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m1 - mn);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[nb][i] = fmaf(acc[nb][i], a0, xch[(nb * 16 + i) * 64] * a1);
+    lsum = fmaf(lsum, a0, l1 * a1);
+    m = mn;
+  }
   if (!qvalid) return;
   const float inv = 1.0f / lsum;
   uint16_t* Oh = (uint16_t*)a.O + ((int64_t)bh * N + qtok) * D;
@@ -704,16 +746,17 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
 
 template <int D, int CQ, int CK, bool DENSE, bool FP8>
 void launch_mfma(const AttnArgs& a, hipStream_t st) {
+  constexpr int KSPL = CQ == 64 ? 2 : 1;
   const size_t sm = attn_smem<D, FP8>();
   static bool attr_set = false;   // raise the dynamic-LDS limit once per instantiation
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd<D, CQ, CK, DENSE, FP8>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd<D, CQ, CK, DENSE, FP8, KSPL>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     attr_set = true;
   }
   dim3 g(a.nqc, a.BH);
   if (a.ev_start) (void)hipEventRecord(a.ev_start, st);
-  attn_fwd<D, CQ, CK, DENSE, FP8><<<g, 2 * CQ, sm, st>>>(a);
+  attn_fwd<D, CQ, CK, DENSE, FP8, KSPL><<<g, 2 * CQ * KSPL, sm, st>>>(a);
   if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);
 }
 
