@@ -45,7 +45,7 @@ class _Opts(ctypes.Structure):
                 ("seed", ctypes.c_uint64), ("trace_perm", ctypes.c_void_p),
                 ("trace_score", ctypes.c_void_p), ("trace_dir", ctypes.c_void_p),
                 ("split_mode", ctypes.c_int), ("trace_basis", ctypes.c_void_p),
-                ("cluster_size_k", ctypes.c_int)]
+                ("cluster_size_k", ctypes.c_int), ("kv_heads", ctypes.c_int)]
 
 _SPLIT_MODES = {"power": 0, "diag": 1}
 
@@ -73,7 +73,7 @@ def load() -> ctypes.CDLL:
     lib.ca_attend.restype = I
     lib.ca_attend_var.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I, I, F, P, P, P, S, P]
     lib.ca_attend_var.restype = I
-    lib.ca_attend_ex.argtypes = [P, P, P, I, I, I, I, I, P, P, I, I, P, P, I, I, F, P, P, P, S, P]
+    lib.ca_attend_ex.argtypes = [P, P, P, I, I, I, I, I, I, P, P, I, I, P, P, I, I, F, P, P, P, S, P]
     lib.ca_attend_ex.restype = I
     lib.ca_dense.argtypes = [P, P, P, I, I, I, I, I, F, P, P, P, S, P]
     lib.ca_dense.restype = I
@@ -197,6 +197,17 @@ def _bhnd(*ts):
             raise ValueError("tensors must be contiguous [B, H, N, D] device tensors")
 
 
+def _kv_heads(Q, *kv) -> int:
+    """Head count of K (and V) when it differs from Q's (grouped- or
+    multi-query attention), else 0."""
+    B, H, N, D = Q.shape
+    for t in kv:
+        if t.shape[0] != B or t.shape[2:] != Q.shape[2:] or t.shape[1] != kv[0].shape[1]:
+            raise ValueError("K and V must be [B, kv_heads, N, D] like Q")
+    h = kv[0].shape[1]
+    return 0 if h == H else h
+
+
 @dataclass
 class ClusterResult:
     perm_q: object
@@ -219,12 +230,15 @@ def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = Tru
     split_mode "power" is basic recursive splitting (power iteration per node),
     "diag" diagonalized recursive splitting (one principal-component basis per
     tree, each node splits along its highest-variance coordinate).
-    cluster_size_k (0: c) clusters the keys with their own size."""
+    cluster_size_k (0: c) clusters the keys with their own size. K may have
+    fewer heads than Q (grouped- or multi-query attention): every query head
+    then clusters its key/value head's rows under its own metric."""
     if split_mode not in _SPLIT_MODES:
         raise ValueError(f"split_mode must be one of {sorted(_SPLIT_MODES)}")
     torch = _torch()
     _bhnd(Q, K)
     B, H, N, D = Q.shape
+    kvh = _kv_heads(Q, K)
     dev = Q.device
     ck = cluster_size_k or c
     n_c, n_kc = -(-N // c), -(-N // ck)
@@ -244,7 +258,7 @@ def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = Tru
             tb = torch.full((B * H, 2, D, D), float("nan"), dtype=torch.float32, device=dev)
     opts = _Opts(int(transform), int(query_normalize), power_iters, sample_factor,
                  seed & ((1 << 64) - 1), _ptr(tp), _ptr(ts), _ptr(td),
-                 _SPLIT_MODES[split_mode], _ptr(tb), int(cluster_size_k))
+                 _SPLIT_MODES[split_mode], _ptr(tb), int(cluster_size_k), kvh)
     nbytes = workspace_size(OP_CLUSTER_DIAG if split_mode == "diag" else OP_CLUSTER, B, H, N, D,
                             min(c, ck))
     ws = _ws(nbytes, dev, workspace)
@@ -309,11 +323,13 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
            fp8: bool = False, workspace=None):
     """ca_attend: block-sparse attention with optional mean-compensation;
     with `nsel` (selected count per row of `blocks`), ca_attend_var; with key
-    clusters of another size c_k than the query clusters' c, ca_attend_ex;
+    clusters of another size c_k than the query clusters' c, or K and V with
+    fewer heads than Q (grouped- or multi-query attention), ca_attend_ex;
     fp8=True: the Q.K^T product on FP8 (E4M3) operands (dtype CA_BF16_FP8)."""
     torch = _torch()
     _bhnd(Q, K, V)
     dt = _attn_dtype(Q, fp8)
+    kvh = _kv_heads(Q, K, V)
     B, H, N, D = Q.shape
     dev = Q.device
     O = torch.empty_like(Q)
@@ -322,8 +338,8 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
     ck = c_k or c
     nbytes = workspace_size(OP_ATTEND, B, H, N, D, ck, topk)
     ws = _ws(nbytes, dev, workspace)
-    if ck != c:
-        st = load().ca_attend_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, N,
+    if ck != c or kvh:
+        st = load().ca_attend_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, kvh, N,
                                  D, perm_q.data_ptr(), perm_k.data_ptr(), c, ck, blocks.data_ptr(),
                                  _ptr(nsel), topk, int(compensate), float(scale), O.data_ptr(),
                                  _ptr(lse), _ptr(ws), nbytes, _stream_ptr(dev))
@@ -346,6 +362,8 @@ def dense(Q, K, V, *, scale: float = 0.0, return_lse: bool = False, fp8: bool = 
     """ca_dense: dense attention baseline (fp8=True: FP8 Q.K^T operands)."""
     torch = _torch()
     _bhnd(Q, K, V)
+    if _kv_heads(Q, K, V):
+        raise ValueError("dense() takes K and V with the head count of Q")
     dt = _attn_dtype(Q, fp8)
     B, H, N, D = Q.shape
     dev = Q.device

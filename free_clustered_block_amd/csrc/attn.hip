@@ -78,8 +78,8 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
   }
   const int nj = min(c, a.N - j * c);
   const int32_t* perm = a.perm_k ? a.perm_k + (int64_t)bh * a.N + (int64_t)j * c : nullptr;
-  const uint16_t* K = (const uint16_t*)a.K + (int64_t)bh * a.N * D;
-  const uint16_t* V = (const uint16_t*)a.V + (int64_t)bh * a.N * D;
+  const uint16_t* K = (const uint16_t*)a.K + (int64_t)(bh / a.kvg) * a.N * D;
+  const uint16_t* V = (const uint16_t*)a.V + (int64_t)(bh / a.kvg) * a.N * D;
   uint16_t* kc = FP8 ? nullptr : a.kc + ((int64_t)bh * nc + j) * c * D;
   uint8_t* kc8 = FP8 ? a.kc8 + ((int64_t)bh * nc + j) * c * D : nullptr;
   uint16_t* vt = a.vt + ((int64_t)bh * nc + j) * (int64_t)D * c;
@@ -645,8 +645,8 @@ __global__ __launch_bounds__(256) void centroids_kv_f32(AttnArgs a) {
   }
   const int nj = min(a.c, a.N - j * a.c);
   const int32_t* perm = a.perm_k + (int64_t)bh * a.N + (int64_t)j * a.c;
-  const float* K = (const float*)a.K + (int64_t)bh * a.N * D;
-  const float* V = (const float*)a.V + (int64_t)bh * a.N * D;
+  const float* K = (const float*)a.K + (int64_t)(bh / a.kvg) * a.N * D;
+  const float* V = (const float*)a.V + (int64_t)(bh / a.kvg) * a.N * D;
   float ks = 0.0f, vs = 0.0f;
   for (int r = 0; r < nj; ++r) {
     const int tok = clamp_tok(perm[r], a.N);
@@ -677,8 +677,8 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
     if (qvalid) qtok = clamp_tok(a.perm_q[(int64_t)bh * N + qa * cq + tid], N);
   }
   const float* Qh = (const float*)a.Q + (int64_t)bh * N * D;
-  const float* Kh = (const float*)a.K + (int64_t)bh * N * D;
-  const float* Vh = (const float*)a.V + (int64_t)bh * N * D;
+  const float* Kh = (const float*)a.K + (int64_t)(bh / a.kvg) * N * D;
+  const float* Vh = (const float*)a.V + (int64_t)(bh / a.kvg) * N * D;
   float q[D], o[D];
   for (int d = 0; d < D; ++d) { q[d] = qvalid ? Qh[(int64_t)qtok * D + d] : 0.0f; o[d] = 0.0f; }
   float m = kNegInf, lsum = 0.0f;

@@ -881,7 +881,7 @@ __global__ __launch_bounds__(kRotThreads) void rotate_bf16(const uint16_t* __res
                                                            const uint16_t* __restrict__ K,
                                                            const float* __restrict__ s,
                                                            const uint16_t* __restrict__ At3, int N,
-                                                           float* __restrict__ Y) {
+                                                           float* __restrict__ Y, int kvg) {
   constexpr int NB = D / 32, KS = D / 16, PB = D + 8, NW = kRotThreads / 64;
   extern __shared__ __attribute__((aligned(16))) uint16_t sb[];   // [3 D][PB]
   const int tree = blockIdx.y, bh = tree >> 1, tensor = tree & 1;
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(kRotThreads) void rotate_bf16(const uint16_t* __res
     }
   }
   __syncthreads();
-  const uint16_t* X = (tensor == 0 ? Q : K) + (int64_t)bh * N * D;
+  const uint16_t* X = tensor == 0 ? Q + (int64_t)bh * N * D : K + (int64_t)(bh / kvg) * N * D;
   const float* sv = tensor == 0 ? s + (int64_t)bh * N : nullptr;
   float* Yt = Y + (int64_t)tree * N * D;
   const int tend = min(N, (blockIdx.x + 1) * kRotTokens);
@@ -955,12 +955,12 @@ __global__ __launch_bounds__(256) void rotate_f32(const float* __restrict__ Q,
                                                   const float* __restrict__ K,
                                                   const float* __restrict__ s,
                                                   const float* __restrict__ At, int N,
-                                                  float* __restrict__ Y) {
+                                                  float* __restrict__ Y, int kvg) {
   constexpr int G = 256 / D, TT = 32;
   __shared__ float sx[TT][D + 1];
   const int tree = blockIdx.y, bh = tree >> 1, tensor = tree & 1;
   const int tid = threadIdx.x, j = tid % D, g = tid / D;
-  const float* X = (tensor == 0 ? Q : K) + (int64_t)bh * N * D;
+  const float* X = tensor == 0 ? Q + (int64_t)bh * N * D : K + (int64_t)(bh / kvg) * N * D;
   const float* sv = tensor == 0 ? s + (int64_t)bh * N : nullptr;
   float aj[D];
 #pragma unroll
@@ -982,7 +982,7 @@ __global__ __launch_bounds__(256) void rotate_f32(const float* __restrict__ Q,
 
 template <int D>
 void launch_rotate_d(const void* Q, const void* K, int dtype, int BH, int N, const float* s,
-                     const float* At, uint16_t* At3, float* Y, hipStream_t st) {
+                     const float* At, uint16_t* At3, float* Y, int kvg, hipStream_t st) {
   const int trees = 2 * BH;
   if (dtype == 0) {
     basis_split<D><<<(unsigned)(((int64_t)trees * D * D + 255) / 256), 256, 0, st>>>(At, trees, At3);
@@ -994,10 +994,10 @@ void launch_rotate_d(const void* Q, const void* K, int dtype, int BH, int N, con
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
       attr_set = true;
     }
-    rotate_bf16<D><<<g, kRotThreads, sm, st>>>((const uint16_t*)Q, (const uint16_t*)K, s, At3, N, Y);
+    rotate_bf16<D><<<g, kRotThreads, sm, st>>>((const uint16_t*)Q, (const uint16_t*)K, s, At3, N, Y, kvg);
   } else {
     dim3 g((N + 31) / 32, trees);
-    rotate_f32<D><<<g, 256, 0, st>>>((const float*)Q, (const float*)K, s, At, N, Y);
+    rotate_f32<D><<<g, 256, 0, st>>>((const float*)Q, (const float*)K, s, At, N, Y, kvg);
   }
 }
 
@@ -1011,9 +1011,9 @@ void launch_basis(const void* Q, int dtype, int BH, int N, int D, int transform,
 }
 
 void launch_rotate(const void* Q, const void* K, int dtype, int BH, int N, int D, const float* s,
-                   const float* At, uint16_t* At3, float* Y, hipStream_t st) {
-  if (D == 64) launch_rotate_d<64>(Q, K, dtype, BH, N, s, At, At3, Y, st);
-  else launch_rotate_d<128>(Q, K, dtype, BH, N, s, At, At3, Y, st);
+                   const float* At, uint16_t* At3, float* Y, int kvg, hipStream_t st) {
+  if (D == 64) launch_rotate_d<64>(Q, K, dtype, BH, N, s, At, At3, Y, kvg, st);
+  else launch_rotate_d<128>(Q, K, dtype, BH, N, s, At, At3, Y, kvg, st);
 }
 
 }  // namespace ca

@@ -208,8 +208,12 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   if (!supported_c(c)) return fail(CA_ERR_UNSUPPORTED, "cluster_size must be 64, 128 or 256");
   if (N < c) return fail(CA_ERR_INVALID_ARG, "N must be >= cluster_size");
   if ((N + c - 1) / c > 8192) return fail(CA_ERR_UNSUPPORTED, "at most 8192 clusters");
-  ca_cluster_opts o = {1, 1, 8, 1, 0, nullptr, nullptr, nullptr, 0, nullptr, 0};
+  ca_cluster_opts o = {1, 1, 8, 1, 0, nullptr, nullptr, nullptr, 0, nullptr, 0, 0};
   if (opts) o = *opts;
+  const int kvh = o.kv_heads ? o.kv_heads : H;   // key/value heads
+  if (kvh < 1 || kvh > H || H % kvh != 0)
+    return fail(CA_ERR_INVALID_ARG, "kv_heads must be 0 or divide H");
+  const int kvg = H / kvh;
   const int ck = o.cluster_size_k ? o.cluster_size_k : c;   // key cluster size
   if (!supported_c(ck)) return fail(CA_ERR_UNSUPPORTED, "cluster_size_k must be 0, 64, 128 or 256");
   if (N < ck) return fail(CA_ERR_INVALID_ARG, "N must be >= cluster_size_k");
@@ -230,14 +234,14 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   const size_t TN = 2 * (size_t)BH * N;
 
   launch_metric(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, o.transform, o.query_normalize, w.partial,
-                w.hash, w.Mq, w.Mk, w.kbar, w.gsplit, w.s, w.Mpk, st);
+                w.hash, w.Mq, w.Mk, w.kbar, w.gsplit, w.s, w.Mpk, kvg, st);
   if (o.split_mode == 1) {
     launch_basis(Q, dt == CA_BF16 ? 0 : 1, BH, N, D, o.transform, w.s, w.Mq, w.Mk, w.partial, w.Cq,
                  w.Rbuf, w.Zbuf, w.At, st);
     if (o.trace_basis)
       CA_HIP_CHECK(hipMemcpyAsync(o.trace_basis, w.At, 2 * (size_t)BH * D * D * 4,
                                   hipMemcpyDeviceToDevice, st));
-    launch_rotate(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, w.s, w.At, w.At3, w.Y, st);
+    launch_rotate(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, w.s, w.At, w.At3, w.Y, kvg, st);
   }
   launch_perm_init(w.permA, 2 * BH, N, st);
   // the split levels of a set of trees (every tree when c_q == c_k, else one
@@ -254,7 +258,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
         CA_HIP_CHECK(hipMemcpyAsync(o.trace_perm + level * TN, cur, TN * 4, hipMemcpyDeviceToDevice, st));
       LevelArgs a;
       a.Q = Q; a.K = K; a.dtype = dt == CA_BF16 ? 0 : 1;
-      a.BH = BH; a.N = N; a.D = D; a.c = ct; a.level = level;
+      a.BH = BH; a.N = N; a.D = D; a.c = ct; a.level = level; a.kvg = kvg;
       a.transform = o.transform; a.power_iters = o.power_iters; a.sample_factor = o.sample_factor;
       a.split_mode = o.split_mode; a.basis = w.At; a.Y = w.Y; a.jsel = w.jsel;
       a.tree_step = step; a.tree_base = base;
@@ -288,7 +292,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   }
   launch_perm_out(fin_q, fin_k, BH, N, perm_q, perm_k, st);
   launch_centroids(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, c, ck, perm_q, perm_k, cent_q, cent_k,
-                   counts, st);
+                   counts, kvg, st);
   return after_launch();
 }
 
@@ -340,8 +344,9 @@ int ca_route_adaptive(const float* cent_q, const float* cent_k, const int32_t* c
 }
 
 namespace {
-int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
-                int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size_q,
+int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H,
+                int kv_heads, int N, int D, const int32_t* perm_q, const int32_t* perm_k,
+                int cluster_size_q,
                 int cluster_size_k, const int32_t* blocks, const int32_t* nsel, int topk,
                 int compensate, float scale, void* O, float* lse, void* ws, size_t ws_bytes,
                 void* stream) {
@@ -359,8 +364,11 @@ int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B,
   if ((int64_t)nqc * B * H > 0x7FFFFFFF / 2) return fail(CA_ERR_UNSUPPORTED, "too many query clusters");
   if (topk < 1 || topk > nc) return fail(CA_ERR_INVALID_ARG, "topk must be in [1, n_kc]");
   if (!(scale >= 0.0f) || !std::isfinite(scale)) return fail(CA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (kv_heads < 1 || kv_heads > H || H % kv_heads != 0)
+    return fail(CA_ERR_INVALID_ARG, "kv_heads must divide H");
   AttnArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : (dt == CA_F32 ? 1 : 2);
+  a.kvg = H / kv_heads;
   a.BH = B * H; a.N = N; a.D = D; a.c = c; a.nc = nc; a.cq = cq; a.nqc = nqc; a.topk = topk;
   a.compensate = compensate ? 1 : 0;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
@@ -378,7 +386,7 @@ int ca_attend(const void* Q, const void* K, const void* V, ca_dtype dt, int B, i
               const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
               const int32_t* blocks, int topk, int compensate, float scale, void* O, float* lse,
               void* ws, size_t ws_bytes, void* stream) {
-  return attend_impl(Q, K, V, dt, B, H, N, D, perm_q, perm_k, cluster_size, cluster_size, blocks,
+  return attend_impl(Q, K, V, dt, B, H, H, N, D, perm_q, perm_k, cluster_size, cluster_size, blocks,
                      nullptr, topk, compensate, scale, O, lse, ws, ws_bytes, stream);
 }
 
@@ -390,17 +398,19 @@ int ca_attend_var(const void* Q, const void* K, const void* V, ca_dtype dt, int 
     set_error("");
     return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
   }
-  return attend_impl(Q, K, V, dt, B, H, N, D, perm_q, perm_k, cluster_size, cluster_size, blocks,
+  return attend_impl(Q, K, V, dt, B, H, H, N, D, perm_q, perm_k, cluster_size, cluster_size, blocks,
                      nsel, max_sel, compensate, scale, O, lse, ws, ws_bytes, stream);
 }
 
-int ca_attend_ex(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
-                 int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size_q,
-                 int cluster_size_k, const int32_t* blocks, const int32_t* nsel, int max_sel,
-                 int compensate, float scale, void* O, float* lse, void* ws, size_t ws_bytes,
-                 void* stream) {
-  return attend_impl(Q, K, V, dt, B, H, N, D, perm_q, perm_k, cluster_size_q, cluster_size_k,
-                     blocks, nsel, max_sel, compensate, scale, O, lse, ws, ws_bytes, stream);
+int ca_attend_ex(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H,
+                 int kv_heads, int N, int D, const int32_t* perm_q, const int32_t* perm_k,
+                 int cluster_size_q, int cluster_size_k, const int32_t* blocks,
+                 const int32_t* nsel, int max_sel, int compensate, float scale, void* O,
+                 float* lse, void* ws, size_t ws_bytes, void* stream) {
+  set_error("");
+  return attend_impl(Q, K, V, dt, B, H, kv_heads ? kv_heads : H, N, D, perm_q, perm_k,
+                     cluster_size_q, cluster_size_k, blocks, nsel, max_sel, compensate, scale, O,
+                     lse, ws, ws_bytes, stream);
 }
 
 int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N, int D,
@@ -412,7 +422,7 @@ int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, in
   AttnArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : (dt == CA_F32 ? 1 : 2);
   a.BH = B * H; a.N = N; a.D = D; a.c = kDenseTile; a.nc = (N + kDenseTile - 1) / kDenseTile;
-  a.cq = a.c; a.nqc = a.nc;
+  a.cq = a.c; a.nqc = a.nc; a.kvg = 1;
   a.topk = a.nc; a.compensate = 0;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
   a.O = O; a.lse = lse;

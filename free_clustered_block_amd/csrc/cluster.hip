@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void pddp_dir(LevelArgs a) {
   int off, n;
   if (!node_at(a.N, a.c, a.level, slot, &off, &n) || n <= a.c) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const T* X = reinterpret_cast<const T*>(tensor == 0 ? a.Q : a.K) + (int64_t)bh * a.N * D;
+  const T* X = reinterpret_cast<const T*>(tensor == 0 ? a.Q : a.K) + (int64_t)(tensor == 0 ? bh : bh / a.kvg) * a.N * D;
   const float* svec = tensor == 0 ? a.s + (int64_t)bh * a.N : nullptr;
   const int32_t* perm = a.perm_in + (int64_t)tree * a.N + off;
   int32_t* stok = a.zbuf_tok + (int64_t)tree * a.N + off;   // the node's sample tokens
@@ -549,7 +549,7 @@ void pddp_dir_mma(LevelArgs a) {
   int off, n;
   if (!node_at(a.N, a.c, a.level, slot, &off, &n) || n <= a.c) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 31, h = l >> 5;
-  const uint16_t* X = reinterpret_cast<const uint16_t*>(tensor == 0 ? a.Q : a.K) + (int64_t)bh * a.N * D;
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(tensor == 0 ? a.Q : a.K) + (int64_t)(tensor == 0 ? bh : bh / a.kvg) * a.N * D;
   const float* svec = tensor == 0 ? a.s + (int64_t)bh * a.N : nullptr;
   const int32_t* perm = a.perm_in + (int64_t)tree * a.N + off;
   int32_t* stok = a.zbuf_tok + (int64_t)tree * a.N + off;
@@ -851,7 +851,7 @@ __global__ __launch_bounds__(256) void pddp_project(LevelArgs a) {
   float ur[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) ur[e] = u[e];
-  const T* X = reinterpret_cast<const T*>(tensor == 0 ? a.Q : a.K) + (int64_t)bh * a.N * D;
+  const T* X = reinterpret_cast<const T*>(tensor == 0 ? a.Q : a.K) + (int64_t)(tensor == 0 ? bh : bh / a.kvg) * a.N * D;
   const int32_t* perm = a.perm_in + (int64_t)tree * a.N;
   const float* svec = tensor == 0 ? a.s + (int64_t)bh * a.N : nullptr;
   uint32_t* keys = a.keys + (int64_t)tree * a.N;
@@ -1230,7 +1230,7 @@ __global__ __launch_bounds__(256) void centroids_kernel(const T* __restrict__ Q,
                                                         const int32_t* __restrict__ pk,
                                                         float* __restrict__ cq,
                                                         float* __restrict__ ck,
-                                                        int32_t* __restrict__ counts) {
+                                                        int32_t* __restrict__ counts, int kvg) {
   constexpr int EPG = 16 / (int)sizeof(T);   // elements per 16-byte group
   constexpr int NG = D / EPG;                // groups per row
   constexpr int S = 256 / NG;                // row slots
@@ -1241,7 +1241,7 @@ __global__ __launch_bounds__(256) void centroids_kernel(const T* __restrict__ Q,
   const int nc = (N + c - 1) / c;
   if (j >= nc) return;
   const int nj = min(c, N - j * c);
-  const T* X = (tensor == 0 ? Q : K) + (int64_t)bh * N * D;
+  const T* X = tensor == 0 ? Q + (int64_t)bh * N * D : K + (int64_t)(bh / kvg) * N * D;
   const int32_t* perm = (tensor == 0 ? pq : pk) + (int64_t)bh * N + (int64_t)j * c;
   const int tid = threadIdx.x;
   if (tid < nj) stoks[tid] = perm[tid];
@@ -1335,19 +1335,19 @@ void launch_level(const LevelArgs& a, hipStream_t st) {
 
 void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, int D, int c_q,
                       int c_k, const int32_t* pq, const int32_t* pk, float* cq, float* ck,
-                      int32_t* counts, hipStream_t st) {
+                      int32_t* counts, int kvg, hipStream_t st) {
   const int cmin = c_q < c_k ? c_q : c_k;
   dim3 g((N + cmin - 1) / cmin, BH, 2);
   if (dtype == 0) {
     const uint16_t* q = (const uint16_t*)Q;
     const uint16_t* k = (const uint16_t*)K;
-    if (D == 64) centroids_kernel<uint16_t, 64><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts);
-    else centroids_kernel<uint16_t, 128><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts);
+    if (D == 64) centroids_kernel<uint16_t, 64><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg);
+    else centroids_kernel<uint16_t, 128><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg);
   } else {
     const float* q = (const float*)Q;
     const float* k = (const float*)K;
-    if (D == 64) centroids_kernel<float, 64><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts);
-    else centroids_kernel<float, 128><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts);
+    if (D == 64) centroids_kernel<float, 64><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg);
+    else centroids_kernel<float, 128><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg);
   }
 }
 

@@ -10,7 +10,9 @@ int metric_rows_per_chunk(int N, int BH);
 // dtype: 0 = bf16, 1 = fp32. partial: [BH][nchunks][2 D D + D] fp32 scratch.
 void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D, int transform,
                    int query_normalize, float* partial, uint64_t* hash, float* Mq, float* Mk,
-                   float* kbar, uint16_t* gsplit, float* s, float* Mpk, hipStream_t st);
+                   float* kbar, uint16_t* gsplit, float* s, float* Mpk, int kvg, hipStream_t st);
+// kvg: query heads per key/value head (1 = multi-head attention); the key
+// rows of query head bh are those of key/value head bh / kvg (every call).
 
 // cluster.hip ----------------------------------------------------------------
 struct LevelArgs {
@@ -18,6 +20,7 @@ struct LevelArgs {
   const void* K;
   int dtype;
   int BH, N, D, c, level;
+  int kvg;                  // query heads per key/value head (key rows of tree 2 bh + 1: head bh / kvg)
   int transform, power_iters, sample_factor;
   int split_mode;           // 0 = power iteration, 1 = diagonalized (basis below)
   int tree_step, tree_base; // trees of this launch: blockIdx.y * tree_step + tree_base
@@ -59,7 +62,7 @@ void launch_basis(const void* Q, int dtype, int BH, int N, int D, int transform,
 // Y [2 BH][N][D] = coordinates of every query (s q) and key in its tree's
 // basis At; At3 [2 BH][3][D][D] bf16 scratch (bf16 inputs).
 void launch_rotate(const void* Q, const void* K, int dtype, int BH, int N, int D, const float* s,
-                   const float* At, uint16_t* At3, float* Y, hipStream_t st);
+                   const float* At, uint16_t* At3, float* Y, int kvg, hipStream_t st);
 void launch_perm_init(int32_t* perm, int trees, int N, hipStream_t st);
 // perm [2 BH][N] tree order -> perm_q, perm_k [BH][N]; the query trees are
 // read from perm_qt, the key trees from perm_kt
@@ -69,7 +72,7 @@ void launch_perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int
 // counts (optional) = key cluster sizes
 void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, int D, int c_q,
                       int c_k, const int32_t* perm_q, const int32_t* perm_k, float* cent_q,
-                      float* cent_k, int32_t* counts, hipStream_t st);
+                      float* cent_k, int32_t* counts, int kvg, hipStream_t st);
 
 // route.hip ------------------------------------------------------------------
 void launch_route(const float* cq, const float* ck, int BH, int nq, int nk, int D, int topk,
@@ -87,6 +90,7 @@ struct AttnArgs {
   const void* V;
   int dtype;   // 0 bf16, 1 fp32, 2 bf16 with FP8 (e4m3) Q.K^T operands
   int BH, N, D, c, nc, topk, compensate;   // c, nc: key cluster size and count
+  int kvg;                                 // query heads per key/value head (K, V rows of head bh / kvg)
   int cq, nqc;                             // query cluster size and count
   float scale;
   const int32_t* perm_q;

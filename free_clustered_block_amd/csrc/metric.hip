@@ -39,7 +39,7 @@ CA_DEV uint64_t hash_word(uint32_t j, uint32_t w) { return (uint64_t)w * kHashPo
 template <int D>
 __global__ __launch_bounds__(256) void metric_partial_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int N, int rows_per_chunk,
-    int nchunks, float* __restrict__ partial, uint64_t* __restrict__ hash) {
+    int nchunks, float* __restrict__ partial, uint64_t* __restrict__ hash, int kvg) {
   constexpr int TT = kMetricTile;
   constexpr int NB = D / 32;
   constexpr int BPW = NB * NB / 4;          // 32x32 blocks per wave
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void metric_partial_bf16(
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
   // thread (tp, gi): tokens 2 tp, 2 tp + 1 of each tile, groups gi + GI k
   const int tp = tid % TP, gi = tid / TP;
-  const uint16_t* X = (t == 0 ? Q : K) + (int64_t)bh * N * D;
+  const uint16_t* X = t == 0 ? Q + (int64_t)bh * N * D : K + (int64_t)(bh / kvg) * N * D;
   uint64_t hpow[GPT][4];
 #pragma unroll
   for (int k = 0; k < GPT; ++k)
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void metric_partial_bf16(
 template <typename T, int D>
 __global__ __launch_bounds__(256) void metric_partial_f32(
     const T* __restrict__ Q, const T* __restrict__ K, int N, int rows_per_chunk, int nchunks,
-    float* __restrict__ partial, uint64_t* __restrict__ hash) {
+    float* __restrict__ partial, uint64_t* __restrict__ hash, int kvg) {
   // Plain VALU path: thread e accumulates entries e, e+256, ... of Q^T Q and K^T K.
   constexpr int TT = 32;
   __shared__ float sx[2][TT][D];
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void metric_partial_f32(
   const int r0 = chunk * rows_per_chunk;
   const int r1 = min(N, r0 + rows_per_chunk);
   const int tid = threadIdx.x;
-  const T* X[2] = {Q + (int64_t)bh * N * D, K + (int64_t)bh * N * D};
+  const T* X[2] = {Q + (int64_t)bh * N * D, K + (int64_t)(bh / kvg) * N * D};
   constexpr int PER = (D * D + 255) / 256;
   float aq[PER], ak[PER];
   for (int i = 0; i < PER; ++i) aq[i] = ak[i] = 0.0f;
@@ -390,7 +390,7 @@ int metric_rows_per_chunk(int N, int BH) {
 
 void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D, int transform,
                    int query_normalize, float* partial, uint64_t* hash, float* Mq, float* Mk,
-                   float* kbar, uint16_t* gsplit, float* s, float* Mpk, hipStream_t st) {
+                   float* kbar, uint16_t* gsplit, float* s, float* Mpk, int kvg, hipStream_t st) {
   const int rows = metric_rows_per_chunk(N, BH);
   const int nchunks = (N + rows - 1) / rows;
   dim3 gp(nchunks, BH);
@@ -398,13 +398,13 @@ void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D
     const uint16_t* q = (const uint16_t*)Q;
     const uint16_t* k = (const uint16_t*)K;
     gp.z = 2;
-    if (D == 64) metric_partial_bf16<64><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash);
-    else metric_partial_bf16<128><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash);
+    if (D == 64) metric_partial_bf16<64><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash, kvg);
+    else metric_partial_bf16<128><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash, kvg);
   } else {
     const float* q = (const float*)Q;
     const float* k = (const float*)K;
-    if (D == 64) metric_partial_f32<float, 64><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash);
-    else metric_partial_f32<float, 128><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash);
+    if (D == 64) metric_partial_f32<float, 64><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash, kvg);
+    else metric_partial_f32<float, 128><<<gp, 256, 0, st>>>(q, k, N, rows, nchunks, partial, hash, kvg);
   }
   dim3 gr((D * D + 255) / 256, BH);
   if (D == 64) metric_reduce<64><<<gr, 256, 0, st>>>(partial, nchunks, N, transform, Mq, Mk, kbar, gsplit, Mpk);

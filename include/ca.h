@@ -71,7 +71,7 @@ typedef enum {
  * Options of the clustering (v1 §3.2). Pass NULL for the defaults
  * {transform=1, query_normalize=1, power_iters=8, sample_factor=1, seed=0,
  *  trace_perm=NULL, trace_score=NULL, trace_dir=NULL, split_mode=0,
- *  trace_basis=NULL, cluster_size_k=0}.
+ *  trace_basis=NULL, cluster_size_k=0, kv_heads=0}.
  *
  *  transform        1: keys are split under the query metric M_q = Q^T Q / N
  *                   (Eq. 12-14) and queries under the centred key metric
@@ -118,6 +118,15 @@ typedef enum {
  *                   (the pages pair c_q = 64 with c_k = 128, v1 §3.1). Each
  *                   tensor's tree then follows its own size; the trace
  *                   buffers need equal sizes (else CA_ERR_UNSUPPORTED).
+ *  kv_heads         0: K has H heads (multi-head attention). Else K is
+ *                   [B, kv_heads, N, D] with kv_heads dividing H (grouped- or
+ *                   multi-query attention): query head h shares the key rows
+ *                   of head h / (H / kv_heads), and every query head still
+ *                   clusters those keys under its own metric, so perm_k,
+ *                   cent_k and counts stay per query head (the pages' option
+ *                   of one key clustering per associated query head, v1 §6.2
+ *                   "Extension beyond MHA"). CA_ERR_INVALID_ARG if kv_heads
+ *                   does not divide H.
  */
 typedef struct {
   int transform;
@@ -131,6 +140,7 @@ typedef struct {
   int split_mode;
   float* trace_basis;
   int cluster_size_k;
+  int kv_heads;
 } ca_cluster_opts;
 
 /* Number of split levels of the data-independent tree for (N, c): the tree
@@ -267,8 +277,14 @@ int ca_attend_var(const void* Q, const void* K, const void* V, ca_dtype dt, int 
 /*
  * ca_attend_ex -- ca_attend with query clusters of size cluster_size_q and key
  * clusters of size cluster_size_k (the pages pair 64-token query clusters with
- * 128-token key clusters, v1 §3.1) and an optional variable selection.
+ * 128-token key clusters, v1 §3.1), an optional variable selection and
+ * shared key/value heads.
  *
+ * kv_heads  0 or H: K and V are [B,H,N,D]. Else K and V are [B,kv_heads,N,D]
+ *           with kv_heads dividing H, and query head h reads the rows of head
+ *           h / (H / kv_heads) (grouped- or multi-query attention; perm_k and
+ *           blocks stay per query head, as ca_cluster with the same kv_heads
+ *           produces them). CA_ERR_INVALID_ARG if kv_heads does not divide H.
  * perm_q    int32 [B,H,N], clusters of cluster_size_q (n_qc = ceil(N/c_q)).
  * perm_k    int32 [B,H,N], clusters of cluster_size_k (n_kc = ceil(N/c_k)).
  * cluster_size_q <= cluster_size_k, both in {64, 128, 256}.
@@ -280,11 +296,11 @@ int ca_attend_var(const void* Q, const void* K, const void* V, ca_dtype dt, int 
  * arguments and errors as ca_attend; CA_ERR_UNSUPPORTED for a query cluster
  * size above the key cluster size.
  */
-int ca_attend_ex(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H, int N,
-                 int D, const int32_t* perm_q, const int32_t* perm_k, int cluster_size_q,
-                 int cluster_size_k, const int32_t* blocks, const int32_t* nsel, int max_sel,
-                 int compensate, float scale, void* O, float* lse, void* ws, size_t ws_bytes,
-                 void* stream);
+int ca_attend_ex(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H,
+                 int kv_heads, int N, int D, const int32_t* perm_q, const int32_t* perm_k,
+                 int cluster_size_q, int cluster_size_k, const int32_t* blocks,
+                 const int32_t* nsel, int max_sel, int compensate, float scale, void* O,
+                 float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * FP8 attention (dtype CA_BF16_FP8 in ca_attend, ca_attend_var, ca_attend_ex

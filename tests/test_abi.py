@@ -172,3 +172,20 @@ def test_fp8_dtype_and_quantize_reject_bad_arguments(lib):
     assert q(FAKE, 0, 4, 0, 1, FAKE, FAKE, None) == 1
     assert q(FAKE, 0, 4, 64, 0, FAKE, FAKE, None) == 1
     assert q(FAKE, 1, 1 << 25, 64, 1, FAKE, FAKE, None) == 1
+
+
+def test_kv_heads_rejected_unless_dividing_h(lib):
+    import free_clustered_block_amd as ca
+    opts = ca._Opts(1, 1, 8, 1, 0, None, None, None, 0, None, 0, 3)
+    assert _cluster(lib, H=4, opts=ctypes.byref(opts)) == 1
+    assert b"kv_heads" in lib.ca_last_error()
+    opts = ca._Opts(1, 1, 8, 1, 0, None, None, None, 0, None, 0, 8)
+    assert _cluster(lib, H=4, opts=ctypes.byref(opts)) == 1
+    ex = lib.ca_attend_ex
+    # Q, K, V, dt, B, H, kv_heads, N, D, perm_q, perm_k, c_q, c_k, blocks, nsel, max_sel, comp,
+    # scale, O, lse, ws, ws_bytes, stream
+    assert ex(FAKE, FAKE, FAKE, 0, 1, 4, 3, 1024, 64, FAKE, FAKE, 64, 64, FAKE, None, 4, 1, 0.0,
+              FAKE, None, FAKE, 1 << 30, None) == 1
+    assert b"kv_heads" in lib.ca_last_error()
+    assert ex(FAKE, FAKE, FAKE, 0, 1, 4, 2, 1024, 64, FAKE, FAKE, 64, 64, FAKE, None, 4, 1, 0.0,
+              FAKE, None, FAKE, 10, None) == 3
