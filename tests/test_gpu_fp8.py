@@ -226,3 +226,31 @@ def test_fp8_full_size_sampled(ca):
         print(f"head {h}: sparse {len(rows)} rows max|O-oracle|={err:.2e} max|LSE-oracle|={lerr:.2e}; "
               f"dense 256 rows max|O-oracle|={derr:.2e} max|LSE-oracle|={dlerr:.2e}", flush=True)
         assert err <= TOL_O and lerr <= TOL_L and derr <= TOL_O and dlerr <= TOL_L
+
+
+def test_zero_queries_and_key_blocks(ca):
+    """Groups whose largest magnitude is 0 (scale 0): zero query rows and a
+    whole key cluster of zero rows, including the short last cluster, so the
+    masked keys of that tile meet a zero logit scale. Against the oracle,
+    sparse and dense, compensation on."""
+    w = synth.WORKLOADS["video_32760"]
+    Q, K, V = synth.generate(w, heads=slice(0, 2), N=1000)
+    B, H, N, D = Q.shape
+    c, topk = 128, 3
+    pq = np.stack([np.random.default_rng(h).permutation(N) for h in range(H)])[None]
+    pk = np.stack([np.random.default_rng(10 + h).permutation(N) for h in range(H)])[None]
+    Q[0, :, pq[0, 0, :40]] = 0.0                          # zero query rows
+    nc = -(-N // c)
+    for h in range(H):
+        K[0, h, pk[0, h, 2 * c:3 * c]] = 0.0              # a full zero cluster
+        K[0, h, pk[0, h, (nc - 1) * c:]] = 0.0            # the short last cluster
+    blocks = np.stack([np.stack([np.array([0, 2, nc - 1]) for _ in range(nc)])
+                       for _ in range(H)])[None].astype(np.int32)
+    O, L = ca.attend(_dev(Q), _dev(K), _dev(V), _i32(pq), _i32(pk), c, _i32(blocks),
+                     compensate=True, return_lse=True, fp8=True)
+    Oo, Lo = o.attend(Q, K, V, pq, pk, c, blocks, True, qk="e4m3")
+    assert np.all(np.isfinite(_np(O))) and np.all(np.isfinite(_np(L)))
+    assert np.max(np.abs(_np(O) - Oo)) <= TOL_O and np.max(np.abs(_np(L) - Lo)) <= TOL_L
+    Od, Ld = ca.dense(_dev(Q), _dev(K), _dev(V), return_lse=True, fp8=True)
+    Odo, Ldo = o.dense(Q, K, V, qk="e4m3")
+    assert np.max(np.abs(_np(Od) - Odo)) <= TOL_O and np.max(np.abs(_np(Ld) - Ldo)) <= TOL_L
