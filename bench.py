@@ -107,6 +107,10 @@ def parse():
     ap.add_argument("--fp8", action="store_true",
                     help="Q.K^T on FP8 (E4M3) operands in the attention and in the dense "
                          "baseline (dtype CA_BF16_FP8); P.V stays bf16")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="shared key/value heads (grouped- or multi-query attention): K and V "
+                         "keep the workload's first KV heads; every query head clusters its "
+                         "KV head's keys under its own metric")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="quality/latency sweep over cluster size, selected fraction, SMC and "
@@ -325,6 +329,14 @@ def main():
     Qn, Kn, Vn = gen_inputs(w)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     Q = torch.from_numpy(Qn).to(tdt).to(dev).contiguous()
+    kvh = args.kv_heads or w.H
+    if w.H % kvh != 0:
+        print("--kv-heads must divide the workload's head count", file=sys.stderr)
+        sys.exit(2)
+    if kvh != w.H:
+        # the first kvh heads' keys and values, shared by H / kvh query heads each
+        Kn = np.ascontiguousarray(Kn[:, :kvh])
+        Vn = np.ascontiguousarray(Vn[:, :kvh])
     K = torch.from_numpy(Kn).to(tdt).to(dev).contiguous()
     V = torch.from_numpy(Vn).to(tdt).to(dev).contiguous()
     if args.verbose:
@@ -452,7 +464,7 @@ def main():
     clu_gbs = clu_bytes / (clu_ms * 1e-3) / 1e9
 
     traffic = (recorded_traffic(w.name, topk, args.fp8) if B * H == w.B * w.H and not adaptive
-               and args.split_mode == "power" and cq == c else None)
+               and args.split_mode == "power" and cq == c and kvh == w.H else None)
     peak = PEAK_FP8QK_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     eff = 4.0 * D * N * N * B * H / (wall) / 1e12
     result = {
@@ -475,6 +487,7 @@ def main():
                    **({"qk_operands": "fp8 e4m3, per-token query / per-64-key scales"}
                       if args.fp8 else {}),
                    **({"query_cluster_size": cq} if cq != c else {}),
+                   **({"kv_heads": kvh} if kvh != w.H else {}),
                    **({"recall": args.recall, "min_count": args.min_count,
                        "mean_selected": round(mean_sel, 2)} if adaptive else {})},
         "stage_ms": {"cluster": round(float(st_cluster), 4), "route": round(float(st_route), 4),
@@ -507,14 +520,18 @@ def main():
     if not args.no_dense:
         ws_d = torch.empty(ca.workspace_size(ca.OP_DENSE, B, H, N, D), dtype=torch.uint8, device=dev)
 
+        # the dense baseline takes the key/value heads repeated per query head
+        Kd = K.repeat_interleave(w.H // kvh, dim=1).contiguous() if kvh != w.H else K
+        Vd = V.repeat_interleave(w.H // kvh, dim=1).contiguous() if kvh != w.H else V
+
         def time_dense(fp8):
-            Od = ca.dense(Q, K, V, fp8=fp8, workspace=ws_d)
+            Od = ca.dense(Q, Kd, Vd, fp8=fp8, workspace=ws_d)
             torch.cuda.synchronize()
             de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(args.dense_steps)]
             for a, b in de:
                 a.record()
-                Od = ca.dense(Q, K, V, fp8=fp8, workspace=ws_d)
+                Od = ca.dense(Q, Kd, Vd, fp8=fp8, workspace=ws_d)
                 b.record()
             torch.cuda.synchronize()
             return Od, float(np.mean([a.elapsed_time(b) for a, b in de]))
@@ -542,6 +559,9 @@ def main():
 
     if not args.no_cpu_baseline:
         heads = max(1, min(args.cpu_heads, H))
+        if kvh != w.H:
+            Kn = np.repeat(Kn, w.H // kvh, axis=1)
+            Vn = np.repeat(Vn, w.H // kvh, axis=1)
         result["cpu_baseline"] = cpu_baseline(w, Qn, Kn, Vn, topk, heads, args.split_mode,
                                               args.assign, args.recall, args.min_count,
                                               "e4m3" if args.fp8 else "exact")
