@@ -797,7 +797,7 @@ def dense(Q, K, V, scale=None, qk: str = "exact"):
 
 
 def forward(Q, K, V, c: int, topk: int, compensate: bool = True, opts: ClusterOpts | None = None,
-            dtype: str = "bf16", scale=None):
+            dtype: str = "bf16", scale=None, qk: str = "exact"):
     """The whole path: cluster -> centroids -> route -> attend (v1 §1.1)."""
     pq, pk = cluster(Q, K, c, opts, dtype)
     B, H, N, D = Q.shape
@@ -807,7 +807,7 @@ def forward(Q, K, V, c: int, topk: int, compensate: bool = True, opts: ClusterOp
             cq, _ = centroids(Q[b, h], pq[b, h], c)
             ck, _ = centroids(K[b, h], pk[b, h], c)
             blocks[b, h] = route(cq, ck, topk)
-    O, L = attend(Q, K, V, pq, pk, c, blocks, compensate, scale)
+    O, L = attend(Q, K, V, pq, pk, c, blocks, compensate, scale, qk=qk)
     return O, L, pq, pk, blocks
 
 
