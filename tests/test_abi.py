@@ -189,3 +189,23 @@ def test_kv_heads_rejected_unless_dividing_h(lib):
     assert b"kv_heads" in lib.ca_last_error()
     assert ex(FAKE, FAKE, FAKE, 0, 1, 4, 2, 1024, 64, FAKE, FAKE, 64, 64, FAKE, None, 4, 1, 0.0,
               FAKE, None, FAKE, 10, None) == 3
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """The product path has no fallback: without libca.so every call raises."""
+    import free_clustered_block_amd as ca
+    monkeypatch.setattr(ca, "LIB_PATH", str(tmp_path / "missing" / "libca.so"))
+    monkeypatch.setattr(ca, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        ca.load()
+    with pytest.raises(RuntimeError, match="not built"):
+        ca.workspace_size(ca.OP_ATTEND, 1, 1, 1024, 64, 64)
+
+
+def test_product_path_does_not_import_the_oracle():
+    """Only tests, the smoke check and the bench's CPU leg may use the oracle."""
+    import pathlib
+    pkg = pathlib.Path(ROOT) / "free_clustered_block_amd"
+    for f in list(pkg.rglob("*.py")) + list(pkg.rglob("*.hip")) + list(pkg.rglob("*.h")):
+        text = f.read_text()
+        assert "oracle" not in text, f
