@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--topk", type=int, default=0, help="override top-k")
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-sdpa", action="store_true",
+                    help="skip the torch scaled_dot_product_attention (flash backend) reference")
     ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=5,
@@ -553,6 +555,29 @@ def main():
             result["cos_dense_fp8_vs_dense_bf16"] = round(cosine(Od, Ob), 5)
         else:
             result["cos_vs_dense"] = round(cosine(O, Od), 5)
+
+        # reference only: torch's fused dense attention (flash backend) on the
+        # same bf16 inputs, 3 timed calls
+        if not args.no_sdpa and w.dtype == "bf16":
+            try:
+                from torch.nn.attention import SDPBackend, sdpa_kernel
+                with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                    torch.nn.functional.scaled_dot_product_attention(Q, Kd, Vd)
+                    torch.cuda.synchronize()
+                    se = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                          for _ in range(3)]
+                    for a, b in se:
+                        a.record()
+                        torch.nn.functional.scaled_dot_product_attention(Q, Kd, Vd)
+                        b.record()
+                    torch.cuda.synchronize()
+                sdpa_ms = float(np.median([a.elapsed_time(b) for a, b in se]))
+                result["torch_sdpa_flash_ms"] = round(sdpa_ms, 4)
+                result["speedup_vs_torch_sdpa"] = round(sdpa_ms / (wall * 1e3), 3)
+            except Exception as e:   # not available on this build: reported as absent
+                result["torch_sdpa_flash_ms"] = None
+                if args.verbose:
+                    print(f"torch SDPA reference unavailable: {e}", file=sys.stderr)
 
     if not args.no_peaks:
         result["measured_peaks"] = measure_peaks(torch, dev)
