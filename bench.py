@@ -226,7 +226,9 @@ def sweep(args, torch, synth, ca):
     selected fraction k/n_c in {1/4, 1/8, 1/16}, SMC off/on, for the learned
     (PDDP) clusters and for seeded random clusters of the same sizes; then
     adaptive selection at mass recalls {0.6, 0.8, 0.9, 0.95, 0.99} (minimum
-    count 16), SMC off/on."""
+    count 16), SMC off/on. With --fp8 the attention takes FP8 Q.K^T operands,
+    the latency is compared with FP8 dense attention and the error with bf16
+    dense attention."""
     dev = torch.device("cuda:0")
 
     def timed(fn, reps=3):
@@ -245,7 +247,9 @@ def sweep(args, torch, synth, ca):
         Qn, Kn, Vn = gen_inputs(w)
         Q, K, V = (torch.from_numpy(x).to(torch.bfloat16).to(dev).contiguous() for x in (Qn, Kn, Vn))
         B, H, N, D = Q.shape
-        Od, dense_ms = timed(lambda: ca.dense(Q, K, V))
+        Od, dense_ms = timed(lambda: ca.dense(Q, K, V, fp8=args.fp8))
+        if args.fp8:
+            Od = ca.dense(Q, K, V)   # the error reference stays bf16 dense attention
         Odf = Od.float()
         nd = torch.linalg.vector_norm(Odf).item()
         for c in (64, 128, 256):
@@ -266,14 +270,15 @@ def sweep(args, torch, synth, ca):
                             if kind == "pddp":
                                 cr = ca.cluster(Q, K, c, seed=w.cluster_seed)
                                 bl = ca.route(cr.cent_q, cr.cent_k, k)
-                                return ca.attend(Q, K, V, cr.perm_q, cr.perm_k, c, bl, compensate=smc)
+                                return ca.attend(Q, K, V, cr.perm_q, cr.perm_k, c, bl, compensate=smc,
+                                                 fp8=args.fp8)
                             bl = ca.route(rq, rk, k)
-                            return ca.attend(Q, K, V, pq, pk, c, bl, compensate=smc)
+                            return ca.attend(Q, K, V, pq, pk, c, bl, compensate=smc, fp8=args.fp8)
                         O, ms = timed(run)
                         Of = O.float()
                         rel = torch.linalg.vector_norm(Of - Odf).item() / nd
                         cos = torch.nn.functional.cosine_similarity(Of, Odf, dim=-1).mean().item()
-                        print(json.dumps({"sweep": w.name, "clusters": kind, "c": c, "k": k,
+                        print(json.dumps({"sweep": w.name, "fp8": args.fp8, "clusters": kind, "c": c, "k": k,
                                           "fraction": f"1/{f}", "smc": smc,
                                           "rel_err_vs_dense": round(rel, 5),
                                           "cos_vs_dense": round(cos, 5), "ms": round(ms, 4),
@@ -290,13 +295,13 @@ def sweep(args, torch, synth, ca):
                                                    min_count=16)
                         sel["n"] = ns
                         return ca.attend(Q, K, V, cr.perm_q, cr.perm_k, c, bl, compensate=smc,
-                                         nsel=ns)
+                                         nsel=ns, fp8=args.fp8)
                     O, ms = timed(run_ada)
                     Of = O.float()
                     rel = torch.linalg.vector_norm(Of - Odf).item() / nd
                     cos = torch.nn.functional.cosine_similarity(Of, Odf, dim=-1).mean().item()
                     frac = sel["n"].float().mean().item() / n_c
-                    print(json.dumps({"sweep": w.name, "clusters": "pddp", "assign": "adaptive",
+                    print(json.dumps({"sweep": w.name, "fp8": args.fp8, "clusters": "pddp", "assign": "adaptive",
                                       "c": c, "recall": recall, "selected_fraction": round(frac, 4),
                                       "smc": smc, "rel_err_vs_dense": round(rel, 5),
                                       "cos_vs_dense": round(cos, 5), "ms": round(ms, 4),
