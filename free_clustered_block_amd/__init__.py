@@ -45,7 +45,8 @@ class _Opts(ctypes.Structure):
                 ("seed", ctypes.c_uint64), ("trace_perm", ctypes.c_void_p),
                 ("trace_score", ctypes.c_void_p), ("trace_dir", ctypes.c_void_p),
                 ("split_mode", ctypes.c_int), ("trace_basis", ctypes.c_void_p),
-                ("cluster_size_k", ctypes.c_int), ("kv_heads", ctypes.c_int)]
+                ("cluster_size_k", ctypes.c_int), ("kv_heads", ctypes.c_int),
+                ("kv_share", ctypes.c_int)]
 
 _SPLIT_MODES = {"power": 0, "diag": 1}
 
@@ -224,7 +225,7 @@ class ClusterResult:
 def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = True,
             power_iters: int = 8, sample_factor: int = 1, seed: int = 0,
             split_mode: str = "power", cluster_size_k: int = 0, trace: bool = False,
-            workspace=None) -> ClusterResult:
+            kv_share: bool = False, workspace=None) -> ClusterResult:
     """ca_cluster: permutations into clusters of size c and the cluster centroids.
 
     split_mode "power" is basic recursive splitting (power iteration per node),
@@ -232,7 +233,9 @@ def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = Tru
     tree, each node splits along its highest-variance coordinate).
     cluster_size_k (0: c) clusters the keys with their own size. K may have
     fewer heads than Q (grouped- or multi-query attention): every query head
-    then clusters its key/value head's rows under its own metric."""
+    then clusters its key/value head's rows under its own metric, or, with
+    kv_share, each key/value head's keys are clustered once under the mean
+    of its query heads' metrics (and copied to every head of the group)."""
     if split_mode not in _SPLIT_MODES:
         raise ValueError(f"split_mode must be one of {sorted(_SPLIT_MODES)}")
     torch = _torch()
@@ -258,7 +261,7 @@ def cluster(Q, K, c: int, *, transform: bool = True, query_normalize: bool = Tru
             tb = torch.full((B * H, 2, D, D), float("nan"), dtype=torch.float32, device=dev)
     opts = _Opts(int(transform), int(query_normalize), power_iters, sample_factor,
                  seed & ((1 << 64) - 1), _ptr(tp), _ptr(ts), _ptr(td),
-                 _SPLIT_MODES[split_mode], _ptr(tb), int(cluster_size_k), kvh)
+                 _SPLIT_MODES[split_mode], _ptr(tb), int(cluster_size_k), kvh, int(kv_share))
     nbytes = workspace_size(OP_CLUSTER_DIAG if split_mode == "diag" else OP_CLUSTER, B, H, N, D,
                             min(c, ck))
     ws = _ws(nbytes, dev, workspace)

@@ -208,12 +208,14 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   if (!supported_c(c)) return fail(CA_ERR_UNSUPPORTED, "cluster_size must be 64, 128 or 256");
   if (N < c) return fail(CA_ERR_INVALID_ARG, "N must be >= cluster_size");
   if ((N + c - 1) / c > 8192) return fail(CA_ERR_UNSUPPORTED, "at most 8192 clusters");
-  ca_cluster_opts o = {1, 1, 8, 1, 0, nullptr, nullptr, nullptr, 0, nullptr, 0, 0};
+  ca_cluster_opts o = {1, 1, 8, 1, 0, nullptr, nullptr, nullptr, 0, nullptr, 0, 0, 0};
   if (opts) o = *opts;
   const int kvh = o.kv_heads ? o.kv_heads : H;   // key/value heads
   if (kvh < 1 || kvh > H || H % kvh != 0)
     return fail(CA_ERR_INVALID_ARG, "kv_heads must be 0 or divide H");
   const int kvg = H / kvh;
+  if (o.kv_share != 0 && o.kv_share != 1) return fail(CA_ERR_INVALID_ARG, "kv_share must be 0 or 1");
+  const int kshare = o.kv_share ? kvg : 1;   // query heads per shared key tree
   const int ck = o.cluster_size_k ? o.cluster_size_k : c;   // key cluster size
   if (!supported_c(ck)) return fail(CA_ERR_UNSUPPORTED, "cluster_size_k must be 0, 64, 128 or 256");
   if (N < ck) return fail(CA_ERR_INVALID_ARG, "N must be >= cluster_size_k");
@@ -235,6 +237,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
 
   launch_metric(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, o.transform, o.query_normalize, w.partial,
                 w.hash, w.Mq, w.Mk, w.kbar, w.gsplit, w.s, w.Mpk, kvg, st);
+  if (kshare > 1) launch_pool_key_metric(w.Mq, w.Mpk, BH, D, kshare, st);
   if (o.split_mode == 1) {
     launch_basis(Q, dt == CA_BF16 ? 0 : 1, BH, N, D, o.transform, w.s, w.Mq, w.Mk, w.partial, w.Cq,
                  w.Rbuf, w.Zbuf, w.At, st);
@@ -253,9 +256,17 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     int32_t* nxt = w.permB;
     uint64_t* hcur = w.hash;
     uint64_t* hnxt = w.hashB;
+    // trace copies of this run's trees only (rows base, base + step, ...)
+    const int ntrees = (2 * BH - base + step - 1) / step;
+    auto trace_copy = [&](int32_t* dst, const int32_t* src) -> int {
+      CA_HIP_CHECK(hipMemcpy2DAsync(dst + (size_t)base * N, (size_t)step * N * 4, src + (size_t)base * N,
+                                    (size_t)step * N * 4, (size_t)N * 4, ntrees,
+                                    hipMemcpyDeviceToDevice, st));
+      return 0;
+    };
     for (int level = 0; level < L; ++level) {
       if (o.trace_perm)
-        CA_HIP_CHECK(hipMemcpyAsync(o.trace_perm + level * TN, cur, TN * 4, hipMemcpyDeviceToDevice, st));
+        if (int e = trace_copy(o.trace_perm + level * TN, cur)) return e;
       LevelArgs a;
       a.Q = Q; a.K = K; a.dtype = dt == CA_BF16 ? 0 : 1;
       a.BH = BH; a.N = N; a.D = D; a.c = ct; a.level = level; a.kvg = kvg;
@@ -278,19 +289,21 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
       uint64_t* th = hcur; hcur = hnxt; hnxt = th;
     }
     if (o.trace_perm)
-      CA_HIP_CHECK(hipMemcpyAsync(o.trace_perm + (size_t)L * TN, cur, TN * 4, hipMemcpyDeviceToDevice, st));
+      if (int e = trace_copy(o.trace_perm + (size_t)L * TN, cur)) return e;
     fin = cur;
     return 0;
   };
   int32_t *fin_q = nullptr, *fin_k = nullptr;
-  if (ck == c) {
+  if (ck == c && kshare == 1) {
     if (int e = run_levels(c, 1, 0, fin_q)) return e;
     fin_k = fin_q;
   } else {
+    // query trees, then the key trees (of the first head of each group when
+    // the key clustering is shared)
     if (int e = run_levels(c, 2, 0, fin_q)) return e;
-    if (int e = run_levels(ck, 2, 1, fin_k)) return e;
+    if (int e = run_levels(ck, 2 * kshare, 1, fin_k)) return e;
   }
-  launch_perm_out(fin_q, fin_k, BH, N, perm_q, perm_k, st);
+  launch_perm_out(fin_q, fin_k, BH, N, kshare, perm_q, perm_k, st);
   launch_centroids(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, c, ck, perm_q, perm_k, cent_q, cent_k,
                    counts, kvg, st);
   return after_launch();

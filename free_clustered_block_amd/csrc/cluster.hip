@@ -1211,13 +1211,13 @@ __global__ void perm_init(int32_t* perm, int trees, int N) {
   if (i < (int64_t)trees * N) perm[i] = (int32_t)(i % N);
 }
 
-__global__ void perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N,
+__global__ void perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N, int kshare,
                          int32_t* pq, int32_t* pk) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)BH * N) return;
   const int64_t bh = i / N, p = i % N;
   pq[i] = perm_qt[(2 * bh) * N + p];
-  pk[i] = perm_kt[(2 * bh + 1) * N + p];
+  pk[i] = perm_kt[(2 * (bh - bh % kshare) + 1) * N + p];   // the group's first head's key tree
 }
 
 // Means of the original rows of every cluster. Thread (row slot, group g)
@@ -1284,15 +1284,16 @@ void launch_perm_init(int32_t* perm, int trees, int N, hipStream_t st) {
   perm_init<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm, trees, N);
 }
 
-void launch_perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N, int32_t* pq,
-                     int32_t* pk, hipStream_t st) {
+void launch_perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N, int kshare,
+                     int32_t* pq, int32_t* pk, hipStream_t st) {
   const int64_t n = (int64_t)BH * N;
-  perm_out<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm_qt, perm_kt, BH, N, pq, pk);
+  perm_out<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm_qt, perm_kt, BH, N, kshare, pq, pk);
 }
 
 template <typename T, int D>
 static void level_impl(const LevelArgs& a, hipStream_t st) {
-  const int trees = a.tree_step == 1 ? 2 * a.BH : a.BH;   // every tree, or one tensor's
+  // the trees tree_base, tree_base + tree_step, ... below 2 BH
+  const int trees = (2 * a.BH - a.tree_base + a.tree_step - 1) / a.tree_step;
   dim3 gslots(1u << a.level, trees);
   dim3 gspan((a.N + kSampleSpan - 1) / kSampleSpan, trees);
   pddp_sample<<<gspan, 256, 0, st>>>(a);

@@ -66,8 +66,13 @@ void launch_rotate(const void* Q, const void* K, int dtype, int BH, int N, int D
 void launch_perm_init(int32_t* perm, int trees, int N, hipStream_t st);
 // perm [2 BH][N] tree order -> perm_q, perm_k [BH][N]; the query trees are
 // read from perm_qt, the key trees from perm_kt
-void launch_perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N,
+// (kshare > 1: the key trees of heads bh - bh % kshare serve their whole group)
+void launch_perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N, int kshare,
                      int32_t* perm_q, int32_t* perm_k, hipStream_t st);
+// Shared key clustering of groups of g query heads: the key-tree metric of
+// the group's first head (Mq and its packed copy in Mpk) becomes the mean of
+// the group's query metrics.
+void launch_pool_key_metric(float* Mq, float* Mpk, int BH, int D, int g, hipStream_t st);
 // centroids of query clusters of size c_q and key clusters of size c_k;
 // counts (optional) = key cluster sizes
 void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, int D, int c_q,

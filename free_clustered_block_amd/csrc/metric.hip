@@ -388,6 +388,29 @@ int metric_rows_per_chunk(int N, int BH) {
   return (int)((rows + kMetricTile - 1) / kMetricTile * kMetricTile);
 }
 
+// Mean of the query metrics of each group of g heads, into the slots of the
+// group's first head (in place: every thread reads all of its element's
+// inputs before writing). Mpk's packing is an element permutation, so the
+// packed copy is averaged the same way.
+__global__ __launch_bounds__(256) void pool_key_metric(float* __restrict__ Mq, float* __restrict__ Mpk,
+                                                       int DD, int g) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int lead = blockIdx.y * g;
+  if (e >= DD) return;
+  float a = 0.0f, b = 0.0f;
+  for (int i = 0; i < g; ++i) {
+    a += Mq[(int64_t)(lead + i) * DD + e];
+    b += Mpk[(int64_t)(2 * (lead + i) + 1) * DD + e];
+  }
+  Mq[(int64_t)lead * DD + e] = a / (float)g;
+  Mpk[(int64_t)(2 * lead + 1) * DD + e] = b / (float)g;
+}
+
+void launch_pool_key_metric(float* Mq, float* Mpk, int BH, int D, int g, hipStream_t st) {
+  dim3 grid((D * D + 255) / 256, BH / g);
+  pool_key_metric<<<grid, 256, 0, st>>>(Mq, Mpk, D * D, g);
+}
+
 void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D, int transform,
                    int query_normalize, float* partial, uint64_t* hash, float* Mq, float* Mk,
                    float* kbar, uint16_t* gsplit, float* s, float* Mpk, int kvg, hipStream_t st) {

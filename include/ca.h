@@ -71,7 +71,7 @@ typedef enum {
  * Options of the clustering (v1 §3.2). Pass NULL for the defaults
  * {transform=1, query_normalize=1, power_iters=8, sample_factor=1, seed=0,
  *  trace_perm=NULL, trace_score=NULL, trace_dir=NULL, split_mode=0,
- *  trace_basis=NULL, cluster_size_k=0, kv_heads=0}.
+ *  trace_basis=NULL, cluster_size_k=0, kv_heads=0, kv_share=0}.
  *
  *  transform        1: keys are split under the query metric M_q = Q^T Q / N
  *                   (Eq. 12-14) and queries under the centred key metric
@@ -127,6 +127,13 @@ typedef enum {
  *                   of one key clustering per associated query head, v1 §6.2
  *                   "Extension beyond MHA"). CA_ERR_INVALID_ARG if kv_heads
  *                   does not divide H.
+ *  kv_share         0: as above. 1 (with kv_heads): the pages' other option,
+ *                   one key clustering per key/value head under the mean of
+ *                   its query heads' metrics M_q; it takes the random draws
+ *                   of the group's first query head, and its permutation,
+ *                   centroids and counts are written to every query head of
+ *                   the group (identical rows), so routing and attention are
+ *                   called as before.
  */
 typedef struct {
   int transform;
@@ -141,6 +148,7 @@ typedef struct {
   float* trace_basis;
   int cluster_size_k;
   int kv_heads;
+  int kv_share;
 } ca_cluster_opts;
 
 /* Number of split levels of the data-independent tree for (N, c): the tree

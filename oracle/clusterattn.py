@@ -443,13 +443,19 @@ def head_representations(Q: np.ndarray, K: np.ndarray, opts: ClusterOpts):
 
 
 def cluster(Q: np.ndarray, K: np.ndarray, c: int, opts: ClusterOpts | None = None,
-            dtype: str = "bf16", traces: dict | None = None, c_k: int | None = None):
+            dtype: str = "bf16", traces: dict | None = None, c_k: int | None = None,
+            key_share: int = 1):
     """Cluster queries and keys of every (batch, head) separately (v1 §3.1).
 
     Q, K: [B, H, N, D]. Returns perm_q, perm_k of shape [B, H, N] (int64).
     The flattened head index b*H + h keys the random draws. The keys' tree
     uses cluster size c_k when given (v1 §3.1 pairs 64-token query clusters
-    with 128-token key clusters), else c.
+    with 128-token key clusters), else c. key_share = g > 1: the heads form
+    groups of g consecutive query heads over one key/value head (K holds
+    that head's rows repeated per query head), and each group's keys are
+    clustered once, under the mean of the group's query metrics (v1 §6.2
+    "Extension beyond MHA", its first option), with the random draws of the
+    group's first head; every head of the group gets that permutation.
     """
     opts = opts or ClusterOpts()
     B, H, N, D = Q.shape
@@ -464,6 +470,12 @@ def cluster(Q: np.ndarray, K: np.ndarray, c: int, opts: ClusterOpts | None = Non
             tq = TreeTrace() if traces is not None else None
             tk = TreeTrace() if traces is not None else None
             pq[b, h] = cluster_tree(Xq, Gq, hq, c, opts, head, TENSOR_Q, tq)
+            if key_share > 1:
+                if h % key_share:
+                    pk[b, h] = pk[b, h - h % key_share]
+                    continue
+                Gk = np.mean([head_representations(Q[b, h + i], K[b, h + i], opts)[3]
+                              for i in range(key_share)], axis=0)
             pk[b, h] = cluster_tree(Xk, Gk, hk, c_k or c, opts, head, TENSOR_K, tk)
             if traces is not None:
                 traces[(b, h, TENSOR_Q)] = tq

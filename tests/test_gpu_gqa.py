@@ -89,3 +89,41 @@ def test_attend_shared_heads_equal_repeated_and_oracle(ca, name, fp8):
     tol = 2e-2 if dt == "bf16" else 1e-4
     print(f"{name} fp8={fp8}: max|O-oracle|={err:.2e} max|LSE-oracle|={lerr:.2e}")
     assert err <= tol and lerr <= (1e-2 if dt == "bf16" else 1e-4)
+
+
+@pytest.mark.parametrize("split_mode", ["power", "diag"])
+def test_shared_key_clustering(ca, split_mode):
+    """kv_share: one key clustering per key/value head under the mean of its
+    query heads' metrics (v1 §6.2, the first option). Every head of a group
+    gets the same key permutation, centroids and counts; with identical query
+    heads in a group of two (the mean of two equal fp32 metrics is exact) it
+    equals the per-head clustering; against the oracle's shared trees the
+    key clusters agree."""
+    import torch
+    w, Q, K, V, G, dt, cq, ck = _inputs("video_gqa4to2_bf16")
+    tq, tk = _dev(Q, dt), _dev(K, dt)
+    kw = dict(seed=w.cluster_seed, split_mode=split_mode)
+    sh = ca.cluster(tq, tk, cq, kv_share=True, **kw)
+    for g0 in range(0, Q.shape[1], G):
+        for i in range(1, G):
+            assert torch.equal(sh.perm_k[:, g0 + i], sh.perm_k[:, g0])
+            assert torch.equal(sh.cent_k[:, g0 + i], sh.cent_k[:, g0])
+            assert torch.equal(sh.counts[:, g0 + i], sh.counts[:, g0])
+    # queries are clustered per head exactly as without sharing
+    own = ca.cluster(tq, tk, cq, **kw)
+    assert torch.equal(sh.perm_q, own.perm_q) and torch.equal(sh.cent_q, own.cent_q)
+    # identical query heads within each group: the shared tree is the first head's own
+    Qd = Q.copy()
+    Qd[:, 1::2] = Qd[:, 0::2]
+    tqd = _dev(Qd, dt)
+    a = ca.cluster(tqd, tk, cq, kv_share=True, **kw)
+    b = ca.cluster(tqd, tk, cq, **kw)
+    assert torch.equal(a.perm_k[:, 0::2], b.perm_k[:, 0::2])
+    if split_mode == "power":
+        opts = o.ClusterOpts(seed=w.cluster_seed)
+        Krep = np.repeat(K, G, axis=1)
+        _, pko = o.cluster(Q, Krep, cq, opts, dt, key_share=G)
+        pk = _np(sh.perm_k)
+        ag = np.mean([o.cluster_agreement(pk[0, h], pko[0, h], cq) for h in range(0, Q.shape[1], G)])
+        print(f"shared key clusters: agreement with the oracle {ag:.5f}")
+        assert ag >= 0.95
