@@ -181,6 +181,9 @@ def test_kv_heads_rejected_unless_dividing_h(lib):
     assert b"kv_heads" in lib.ca_last_error()
     opts = ca._Opts(1, 1, 8, 1, 0, None, None, None, 0, None, 0, 8)
     assert _cluster(lib, H=4, opts=ctypes.byref(opts)) == 1
+    opts = ca._Opts(1, 1, 8, 1, 0, None, None, None, 0, None, 0, 2, 2)
+    assert _cluster(lib, H=4, opts=ctypes.byref(opts)) == 1
+    assert b"kv_share" in lib.ca_last_error()
     ex = lib.ca_attend_ex
     # Q, K, V, dt, B, H, kv_heads, N, D, perm_q, perm_k, c_q, c_k, blocks, nsel, max_sel, comp,
     # scale, O, lse, ws, ws_bytes, stream
