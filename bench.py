@@ -113,6 +113,9 @@ def parse():
                     help="shared key/value heads (grouped- or multi-query attention): K and V "
                          "keep the workload's first KV heads; every query head clusters its "
                          "KV head's keys under its own metric")
+    ap.add_argument("--kv-share", action="store_true",
+                    help="with --kv-heads: one key clustering per KV head under the mean of its "
+                         "query heads' metrics")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="quality/latency sweep over cluster size, selected fraction, SMC and "
@@ -368,7 +371,7 @@ def main():
             evs[0].record()
         cr = ca.cluster(Q, K, cq, seed=w.cluster_seed, split_mode=args.split_mode,
                         query_normalize=not adaptive, cluster_size_k=c if cq != c else 0,
-                        workspace=ws_c)
+                        kv_share=args.kv_share, workspace=ws_c)
         if evs:
             evs[1].record()
         if adaptive:
@@ -494,7 +497,7 @@ def main():
                    **({"qk_operands": "fp8 e4m3, per-token query / per-64-key scales"}
                       if args.fp8 else {}),
                    **({"query_cluster_size": cq} if cq != c else {}),
-                   **({"kv_heads": kvh} if kvh != w.H else {}),
+                   **({"kv_heads": kvh, "kv_share": bool(args.kv_share)} if kvh != w.H else {}),
                    **({"recall": args.recall, "min_count": args.min_count,
                        "mean_selected": round(mean_sel, 2)} if adaptive else {})},
         "stage_ms": {"cluster": round(float(st_cluster), 4), "route": round(float(st_route), 4),
