@@ -42,7 +42,10 @@ function that implements it. Summary of those readings:
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, invariants, library routines, published generator
-outputs or brute force, except ``cluster_agreement`` (a reporting helper).
+outputs or brute force (the query and key representations and the whole
+clustering against textbook PDDP on explicitly transformed vectors, the warm
+start against its geometric characterisation), except ``cluster_agreement``
+(a reporting helper).
 """
 from __future__ import annotations
 
@@ -284,6 +287,23 @@ def sample_members(members: np.ndarray, hashes: np.ndarray, level: int, tensor: 
     return T
 
 
+def warm_start(seed: int, head: int, tensor: int, level: int, index: int, d: int,
+               parent: np.ndarray | None) -> np.ndarray:
+    """Start vector of the power iteration at node (level, index) (v1 §3.2.1
+    "Basic recursive splitting": the estimate starts from the parent's
+    principal-component estimate averaged with a random normal vector of about
+    the same norm). Read as u0 = normalise(u_parent + r / |r|), u_parent the
+    parent's unit direction; at the root (no parent) u0 = r / |r|. r is
+    warm_vector of the node; if the sum vanishes, r / |r| is kept."""
+    r = warm_vector(seed, head, tensor, level, index, d)
+    r = r / np.linalg.norm(r)
+    if parent is None:
+        return r
+    s = parent + r
+    ns = np.linalg.norm(s)
+    return s / ns if ns > 0 else r
+
+
 def principal_direction(Xs: np.ndarray, M: np.ndarray, u0: np.ndarray, p: int) -> np.ndarray:
     """p power iterations u <- M C u / |M C u| from u0, C the centred sample
     covariance. With M = R^T R this is the power iteration on R C R^T written
@@ -397,15 +417,8 @@ def cluster_tree(X: np.ndarray, M: np.ndarray, hashes: np.ndarray, c: int, opts:
             if diag:
                 _, u = diag_direction(X[T], basis)
             else:
-                r = warm_vector(opts.seed, head, tensor, level, nd.index, d)
-                r = r / np.linalg.norm(r)
                 par = parent_dir.get((level - 1, nd.index // 2))
-                if par is None:
-                    u0 = r
-                else:
-                    s = par + r
-                    ns = np.linalg.norm(s)
-                    u0 = s / ns if ns > 0 else r
+                u0 = warm_start(opts.seed, head, tensor, level, nd.index, d, par)
                 u = principal_direction(X[T], M, u0, opts.power_iters)
             parent_dir[(level, nd.index)] = u
             scores = X[members] @ u
@@ -470,15 +483,19 @@ def cluster(Q: np.ndarray, K: np.ndarray, c: int, opts: ClusterOpts | None = Non
             tq = TreeTrace() if traces is not None else None
             tk = TreeTrace() if traces is not None else None
             pq[b, h] = cluster_tree(Xq, Gq, hq, c, opts, head, TENSOR_Q, tq)
+            if traces is not None:
+                traces[(b, h, TENSOR_Q)] = tq
             if key_share > 1:
                 if h % key_share:
-                    pk[b, h] = pk[b, h - h % key_share]
+                    lead = h - h % key_share
+                    pk[b, h] = pk[b, lead]
+                    if traces is not None:        # the group's one key tree
+                        traces[(b, h, TENSOR_K)] = traces[(b, lead, TENSOR_K)]
                     continue
                 Gk = np.mean([head_representations(Q[b, h + i], K[b, h + i], opts)[3]
                               for i in range(key_share)], axis=0)
             pk[b, h] = cluster_tree(Xk, Gk, hk, c_k or c, opts, head, TENSOR_K, tk)
             if traces is not None:
-                traces[(b, h, TENSOR_Q)] = tq
                 traces[(b, h, TENSOR_K)] = tk
     return pq, pk
 

@@ -117,9 +117,7 @@ def test_full_size_sampled(ca, wname):
                     if k in replay:
                         par = td[lvl - 1, tree, nd.index // 2].astype(np.float64) if lvl else None
                         T = o.sample_members(mem, hs, lvl, tensor, D, opts.sample_factor, opts.seed)
-                        r = o.warm_vector(opts.seed, head, tensor, lvl, nd.index, D)
-                        r = r / np.linalg.norm(r)
-                        u0 = r if par is None else (par + r) / np.linalg.norm(par + r)
+                        u0 = o.warm_start(opts.seed, head, tensor, lvl, nd.index, D, par)
                         u = o.principal_direction(X[T], G, u0, opts.power_iters)
                         ug = td[lvl, tree, nd.index].astype(np.float64)
                         assert 1 - abs(u @ ug) / np.linalg.norm(ug) <= 1e-9, (wname, h, lvl, tensor)

@@ -79,13 +79,7 @@ def _gpu_cluster(ca, name, trace=False):
 def _replay_direction(X, M, hashes, members, level, tensor, head, slot, d, opts, parent):
     """The oracle's direction for one node, on a given membership."""
     T = o.sample_members(members, hashes, level, tensor, d, opts.sample_factor, opts.seed)
-    r = o.warm_vector(opts.seed, head, tensor, level, slot, d)
-    r = r / np.linalg.norm(r)
-    if parent is None:
-        u0 = r
-    else:
-        s = parent + r
-        u0 = s / np.linalg.norm(s)
+    u0 = o.warm_start(opts.seed, head, tensor, level, slot, d, parent)
     return o.principal_direction(X[T], M, u0, opts.power_iters)
 
 

@@ -185,6 +185,114 @@ def test_query_normalisers():
     check_query_normalisers()
 
 
+def _keys_with_known_covariance(U, sig, kbar):
+    """Key rows kbar +- sqrt(d) sig_j u_j (j = 1..d, N = 2d): their mean is
+    exactly kbar and their centred second moment is exactly U diag(sig^2) U^T,
+    while the uncentred one adds kbar kbar^T."""
+    d = len(sig)
+    E = np.sqrt(d) * (U * np.asarray(sig)[None, :]).T          # row j: sqrt(d) sig_j u_j
+    return np.concatenate([kbar + E, kbar - E]), (U * np.asarray(sig) ** 2) @ U.T
+
+
+def check_head_representations():
+    """The vectors and geometries each tensor is split under (v1 §3.2.2 "Key
+    clustering", Eq. 10-14, and "Query clustering", Eq. 15-16): keys are the
+    raw key rows under the geometry whose quadratic form on a key difference
+    is the mean squared logit difference over the queries; queries are s q
+    with s > 0 under the centred key covariance, normalised so that the
+    root of that covariance maps each to a unit vector."""
+    r = _rng(41)
+    d = 6
+    U = _orthonormal(r, d, d)
+    sig = np.array([3.0, 2.0, 1.5, 1.0, 0.5, 0.25])
+    kbar = np.array([4.0, -3.0, 2.5, 1.0, -2.0, 3.5])
+    K, Sigma = _keys_with_known_covariance(U, sig, kbar)
+    N = K.shape[0]
+    Q = r.standard_normal((N, d)) + np.linspace(-2.0, 2.0, d)
+    Xq, Gq, Xk, Gk = o.head_representations(Q, K, o.ClusterOpts())
+    # query geometry: the centred key covariance built above
+    assert np.allclose(Gq, Sigma, rtol=1e-12, atol=1e-12), "query geometry"
+    # key geometry: Eq. 10-11 on every pair of keys, brute force over queries
+    for a in range(N):
+        for b in range(N):
+            dk = K[a] - K[b]
+            want = np.mean((Q @ K[a] - Q @ K[b]) ** 2)
+            assert math.isclose(dk @ Gk @ dk, want, rel_tol=1e-10, abs_tol=1e-10), "key geometry"
+    assert np.array_equal(Xk, K), "keys are split untransformed"
+    # queries: x_i = s_i q_i with s_i > 0 and |R x_i| = 1 for the known root
+    R = (U * sig[None, :]) @ U.T                               # R^T R = Sigma
+    ratio = np.einsum("ij,ij->i", Xq, Q) / np.einsum("ij,ij->i", Q, Q)
+    assert np.all(ratio > 0)
+    assert np.allclose(Xq, ratio[:, None] * Q, rtol=1e-12, atol=1e-14), "queries are scaled q"
+    assert np.allclose(np.linalg.norm(Xq @ R.T, axis=1), 1.0, rtol=1e-12), "Eq. 16 normaliser"
+    # without the transform: identity geometries, unit-length queries
+    Xq0, Gq0, Xk0, Gk0 = o.head_representations(Q, K, o.ClusterOpts(transform=False))
+    assert np.array_equal(Gq0, np.eye(d)) and np.array_equal(Gk0, np.eye(d))
+    assert np.allclose(np.linalg.norm(Xq0, axis=1), 1.0, rtol=1e-12)
+    # without the query normalisation (adaptive mode, v1 §6): raw queries
+    Xq1, Gq1, _, _ = o.head_representations(Q, K, o.ClusterOpts(query_normalize=False))
+    assert np.array_equal(Xq1, Q) and np.allclose(Gq1, Sigma, rtol=1e-12, atol=1e-12)
+
+
+def test_head_representations():
+    check_head_representations()
+
+
+def _textbook_pddp(Z, c):
+    """Boley's PDDP on explicit vectors: split every node larger than c along
+    the top eigenvector (numpy.linalg.eigh) of its members' centred
+    covariance, at the median. Returns the leaves as a set of frozensets and
+    the largest lambda_2 / lambda_1 met (the power iteration's rate)."""
+    leaves, worst = set(), 0.0
+    stack = [np.arange(Z.shape[0])]
+    while stack:
+        m = stack.pop()
+        if len(m) <= c:
+            leaves.add(frozenset(m.tolist()))
+            continue
+        Zc = Z[m] - Z[m].mean(0)
+        w, V = np.linalg.eigh(Zc.T @ Zc / len(m))
+        worst = max(worst, w[-2] / w[-1])
+        sc = Z[m] @ V[:, -1]
+        order = np.argsort(sc, kind="stable")
+        stack += [m[order[:len(m) // 2]], m[order[len(m) // 2:]]]
+    return leaves, worst
+
+
+def check_cluster_matches_textbook_pddp():
+    """cluster() run to convergence on the whole node (no subsample) splits
+    like textbook PDDP on the explicitly transformed vectors of v1 §3.2.2:
+    keys as R_q k (Eq. 14, R_q^T R_q = Q^T Q / N), queries as R_k q / |R_k q|
+    (Eq. 16, R_k^T R_k the centred key covariance). N = 4c, so every split is
+    at the exact median and the leaves do not depend on the eigenvectors'
+    signs; compared as sets of leaves."""
+    r = _rng(44)
+    N, d, c = 64, 4, 16
+    Q = r.standard_normal((N, d)) @ np.diag([3.0, 1.5, 0.8, 0.3]) + 0.5
+    K = r.standard_normal((N, d)) @ np.diag([0.4, 2.5, 1.0, 3.0]) - 1.0
+    Q4, K4 = Q[None, None], K[None, None]
+    pq, pk = o.cluster(Q4, K4, c, o.ClusterOpts(power_iters=400, sample_factor=N, seed=9), "f32")
+
+    def sym_root(S):
+        w, V = np.linalg.eigh(S)
+        return (V * np.sqrt(np.clip(w, 0, None))) @ V.T
+
+    Rq = sym_root(Q.T @ Q / N)
+    Kc = K - K.mean(0)
+    Rk = sym_root(Kc.T @ Kc / N)
+    zq = Q @ Rk.T
+    zq = zq / np.linalg.norm(zq, axis=1, keepdims=True)
+    for perm, Z in ((pq[0, 0], zq), (pk[0, 0], K @ Rq.T)):
+        want, worst = _textbook_pddp(Z, c)
+        assert worst < 0.9, worst           # every node's eigengap makes p = 400 converge
+        got = {frozenset(perm[j * c:(j + 1) * c].tolist()) for j in range(N // c)}
+        assert got == want
+
+
+def test_cluster_matches_textbook_pddp():
+    check_cluster_matches_textbook_pddp()
+
+
 # ---------------------------------------------------------------------------
 # Principal direction with the metric injected (v1 §3.2.1, §3.2.2, §6.1)
 # ---------------------------------------------------------------------------
@@ -216,6 +324,70 @@ def check_power_iteration_matches_eigh():
 
 def test_power_iteration_matches_eigh():
     check_power_iteration_matches_eigh()
+
+
+def check_warm_start_composition():
+    """Warm start of the power iteration (v1 §3.2.1 "Basic recursive
+    splitting": the parent's estimate averaged with a random normal vector of
+    about the same norm). With no power iterations the traced direction of
+    every node is its start: at the root the node's unit random vector, below
+    it the bisector of the parent's unit direction and the node's unit random
+    vector (unit length, equal cosine to both, in their span)."""
+    r = _rng(42)
+    N, d, c = 200, 5, 16
+    X = r.standard_normal((N, d)) @ r.standard_normal((d, d))
+    hashes = o.row_hash(o.row_words(X.astype(np.float32), "f32"))
+    seed, head, tensor = 77, 3, o.TENSOR_K
+    opts = o.ClusterOpts(power_iters=0, seed=seed)
+    tr = o.TreeTrace()
+    o.cluster_tree(X, np.eye(d), hashes, c, opts, head, tensor, tr)
+    want = {}
+    for level, nodes in enumerate(o.tree_levels(N, c)):
+        for nd in nodes:
+            if nd.n <= c:
+                continue
+            rv = o.warm_vector(seed, head, tensor, level, nd.index, d)
+            rh = rv / np.linalg.norm(rv)
+            u = tr.dirs[(level, nd.index)]
+            assert math.isclose(np.linalg.norm(u), 1.0, rel_tol=1e-12)
+            if level == 0:
+                assert np.allclose(u, rh, rtol=0, atol=1e-14), "root starts at r/|r|"
+            else:
+                par = want[(level - 1, nd.index // 2)]
+                assert math.isclose(u @ par, u @ rh, rel_tol=1e-10) and u @ rh > 0, "bisector"
+                B = np.stack([par, rh], axis=1)
+                res = u - B @ np.linalg.lstsq(B, u, rcond=None)[0]
+                assert np.linalg.norm(res) < 1e-12, "in span(parent, r)"
+            want[(level, nd.index)] = u
+    assert len(want) == sum(nd.n > c for lv in o.tree_levels(N, c) for nd in lv)
+    # p = 8 power iterations on a node whose centred covariance is isotropic
+    # (M = I, whole node sampled): the start is already a fixed point
+    Xi = np.concatenate([np.eye(d), -np.eye(d)]) * 2.0 + 0.75
+    hi = o.row_hash(o.row_words(Xi.astype(np.float32), "f32"))
+    tr8 = o.TreeTrace()
+    o.cluster_tree(Xi, np.eye(d), hi, d, o.ClusterOpts(power_iters=8, seed=seed, sample_factor=2),
+                   head, tensor, tr8)
+    rv = o.warm_vector(seed, head, tensor, 0, 0, d)
+    assert np.allclose(tr8.dirs[(0, 0)], rv / np.linalg.norm(rv), rtol=0, atol=1e-12)
+
+
+def test_warm_start_composition():
+    check_warm_start_composition()
+
+
+def test_key_share_traces():
+    # every head's query tree is traced; the heads of a group share the key tree
+    r = _rng(43)
+    B, H, N, D, c = 1, 4, 96, 8, 16
+    Q = r.standard_normal((B, H, N, D)).astype(np.float32)
+    K = np.repeat(r.standard_normal((B, 1, N, D)).astype(np.float32), H, axis=1)
+    traces = {}
+    pq, pk = o.cluster(Q, K, c, o.ClusterOpts(seed=5), "f32", traces=traces, key_share=2)
+    for h in range(H):
+        assert np.array_equal(traces[(0, h, o.TENSOR_Q)].perms[-1], pq[0, h])
+        assert np.array_equal(traces[(0, h, o.TENSOR_K)].perms[-1], pk[0, h])
+        assert traces[(0, h, o.TENSOR_K)] is traces[(0, h - h % 2, o.TENSOR_K)]
+    assert not np.array_equal(pk[0, 0], pk[0, 2])
 
 
 def test_power_iteration_zero_covariance_keeps_warm_start():
@@ -841,7 +1013,8 @@ def _no_log_count(Q, K, V, perm_q, perm_k, c, blocks, compensate, scale=None):
 _orig = {name: getattr(o, name) for name in
          ["sparse_attention", "split_size", "metric_matrices", "principal_direction", "topk_row",
           "centroids", "dense_attention", "split_by_scores", "fmix64", "pc_basis",
-          "diag_direction", "adaptive_row", "cluster_masses"]}
+          "diag_direction", "adaptive_row", "cluster_masses", "head_representations",
+          "warm_start"]}
 
 
 def _basis_ascending(X, M):
@@ -939,6 +1112,41 @@ def _fmix_wrong_shift(z):
     return _orig["fmix64"](z)
 
 
+def _repr_no_normaliser(Q, K, opts):
+    # queries split as raw q (the Eq. 16 normaliser dropped)
+    Xq, Gq, Xk, Gk = _orig["head_representations"](Q, K, opts)
+    return np.asarray(Q, np.float64), Gq, Xk, Gk
+
+
+def _repr_uncentred_query_geometry(Q, K, opts):
+    # queries under K^T K / N instead of the centred K_c^T K_c / N
+    Xq, Gq, Xk, Gk = _orig["head_representations"](Q, K, opts)
+    K = np.asarray(K, np.float64)
+    G = K.T @ K / K.shape[0] if opts.transform else Gq
+    s = o.query_normalisers(Q, G) if opts.query_normalize else np.ones(len(Q))
+    return s[:, None] * np.asarray(Q, np.float64), G, Xk, Gk
+
+
+def _repr_swapped_geometries(Q, K, opts):
+    Xq, Gq, Xk, Gk = _orig["head_representations"](Q, K, opts)
+    s = o.query_normalisers(Q, Gk) if opts.query_normalize else np.ones(len(Q))
+    return s[:, None] * np.asarray(Q, np.float64), Gk, Xk, Gq
+
+
+def _warm_start_no_parent(seed, head, tensor, level, index, d, parent):
+    return _orig["warm_start"](seed, head, tensor, level, index, d, None)
+
+
+def _warm_start_unnormalised(seed, head, tensor, level, index, d, parent):
+    u = _orig["warm_start"](seed, head, tensor, level, index, d, None)
+    return u if parent is None else parent + u
+
+
+def _warm_start_parent_only(seed, head, tensor, level, index, d, parent):
+    u = _orig["warm_start"](seed, head, tensor, level, index, d, None)
+    return u if parent is None else parent.copy()
+
+
 PLANTED = [
     ("sparse_attention", _no_log_count, check_smc_error_identity),
     ("split_size", _split_size_larger, check_tree_layout),
@@ -956,6 +1164,15 @@ PLANTED = [
     ("diag_direction", _direction_uncentred, check_diag_direction_bruteforce),
     ("adaptive_row", _adaptive_higher_cutoff, check_adaptive_guarantees),
     ("cluster_masses", _masses_without_counts, check_adaptive_direct_cutoff),
+    ("head_representations", _repr_no_normaliser, check_head_representations),
+    ("head_representations", _repr_uncentred_query_geometry, check_head_representations),
+    ("head_representations", _repr_swapped_geometries, check_head_representations),
+    ("head_representations", _repr_no_normaliser, check_cluster_matches_textbook_pddp),
+    ("head_representations", _repr_uncentred_query_geometry, check_cluster_matches_textbook_pddp),
+    ("head_representations", _repr_swapped_geometries, check_cluster_matches_textbook_pddp),
+    ("warm_start", _warm_start_no_parent, check_warm_start_composition),
+    ("warm_start", _warm_start_unnormalised, check_warm_start_composition),
+    ("warm_start", _warm_start_parent_only, check_warm_start_composition),
 ]
 
 
