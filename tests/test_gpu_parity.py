@@ -21,6 +21,7 @@ import pytest
 
 import oracle.clusterattn as o
 import synth
+from tie_check import check_tree
 
 pytestmark = pytest.mark.gpu
 
@@ -159,24 +160,23 @@ def test_cluster_against_oracle_per_level(ca, name):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_cluster_end_to_end_agreement(ca, name):
-    """Agreement of the whole GPU tree with the oracle's own fp64 tree.
-
-    Informational beyond a floor: the warm-started power iteration carries
-    last-bit differences of the metrics and directions down the tree (a
-    relative perturbation of 1e-6 in fp64 alone moves up to a few percent of
-    tokens on these inputs), so exact end-to-end agreement is not a property
-    of the method; the node-by-node test above is the parity check.
-    """
+    """The whole GPU tree against the oracle's own fp64 tree: at least 99.9 %
+    of tokens in the same cluster, and every token that differs left the
+    oracle's path at a median tie (its oracle score within 1e-3 of the node's
+    interquartile range from the split threshold; tests/tie_check.py). The
+    node-by-node test above is the stage-isolated parity check."""
     w, Q, K, V, c, topk = _inputs(name)
+    B, H, N, D = Q.shape
     res = _gpu_cluster(ca, name)
-    pq, pk = o.cluster(Q, K, c, _opts(w), w.dtype)
-    B, H = Q.shape[:2]
-    agq = np.mean([o.cluster_agreement(_np(res.perm_q)[b, h], pq[b, h], c)
-                   for b in range(B) for h in range(H)])
-    agk = np.mean([o.cluster_agreement(_np(res.perm_k)[b, h], pk[b, h], c)
-                   for b in range(B) for h in range(H)])
-    print(f"{name}: end-to-end cluster agreement q={agq:.5f} k={agk:.5f}")
-    assert agq >= 0.95 and agk >= 0.95
+    traces = {}
+    pq, pk = o.cluster(Q, K, c, _opts(w), w.dtype, traces=traces)
+    for tensor, gp, op in ((o.TENSOR_Q, _np(res.perm_q), pq), (o.TENSOR_K, _np(res.perm_k), pk)):
+        for b in range(B):
+            for h in range(H):
+                ag, worst = check_tree(gp[b, h], op[b, h], traces[(b, h, tensor)], N, c,
+                                       (name, b, h, tensor))
+                print(f"{name}: head {h} tensor {tensor}: agreement {ag:.5f}, "
+                      f"largest tie distance {worst:.2e} IQR")
 
 
 @pytest.mark.parametrize("name", list(CASES))

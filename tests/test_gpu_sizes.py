@@ -19,6 +19,7 @@ import numpy as np
 import pytest
 
 import oracle.clusterattn as o
+from tie_check import check_tree
 import synth
 
 pytestmark = pytest.mark.gpu
@@ -68,13 +69,17 @@ def test_cluster_sizes_match_single_size_runs(ca, name):
     assert torch.equal(both.perm_k, krun.perm_k) and torch.equal(both.cent_k, krun.cent_k)
     assert torch.equal(both.counts, krun.counts)
     B, H = Q.shape[:2]
-    pq, pk = o.cluster(Q, K, cq, o.ClusterOpts(seed=w.cluster_seed), w.dtype, c_k=ck)
-    agq = np.mean([o.cluster_agreement(_np(both.perm_q)[b, h], pq[b, h], cq)
-                   for b in range(B) for h in range(H)])
-    agk = np.mean([o.cluster_agreement(_np(both.perm_k)[b, h], pk[b, h], ck)
-                   for b in range(B) for h in range(H)])
-    print(f"{name}: end-to-end cluster agreement q={agq:.5f} k={agk:.5f}")
-    assert agq >= 0.95 and agk >= 0.95
+    N = Q.shape[2]
+    traces = {}
+    pq, pk = o.cluster(Q, K, cq, o.ClusterOpts(seed=w.cluster_seed), w.dtype, traces=traces, c_k=ck)
+    for tensor, gp, op, cc in ((o.TENSOR_Q, _np(both.perm_q), pq, cq),
+                               (o.TENSOR_K, _np(both.perm_k), pk, ck)):
+        for b in range(B):
+            for h in range(H):
+                ag, worst = check_tree(gp[b, h], op[b, h], traces[(b, h, tensor)], N, cc,
+                                       (name, b, h, tensor))
+                print(f"{name}: head {h} tensor {tensor}: agreement {ag:.5f}, "
+                      f"largest tie distance {worst:.2e} IQR")
 
 
 @pytest.mark.parametrize("compensate", [True, False])
