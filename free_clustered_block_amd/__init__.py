@@ -17,13 +17,14 @@ from dataclasses import dataclass
 
 __all__ = [
     "CAError", "load", "LIB_PATH", "EXPORTS", "profile_events", "peak_probe", "HipEvent", "tree_levels",
-    "workspace_size", "cluster", "route", "route_adaptive", "attend", "dense", "forward",
+    "workspace_size", "cluster", "route", "route_noalloc", "route_adaptive", "attend", "dense", "forward",
     "quantize_e4m3",
     "ClusterResult",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libca.so")
-EXPORTS = ["ca_tree_levels", "ca_workspace_size", "ca_cluster", "ca_route", "ca_route_adaptive",
+EXPORTS = ["ca_tree_levels", "ca_workspace_size", "ca_cluster", "ca_route", "ca_route_noalloc",
+           "ca_route_adaptive",
            "ca_attend", "ca_attend_var", "ca_attend_ex", "ca_dense", "ca_quantize_e4m3",
            "ca_profile_events", "ca_peak_probe", "ca_status_string", "ca_last_error"]
 
@@ -68,6 +69,8 @@ def load() -> ctypes.CDLL:
     lib.ca_cluster.restype = I
     lib.ca_route.argtypes = [P, P, I, I, I, I, I, I, P, P, P, S, P]
     lib.ca_route.restype = I
+    lib.ca_route_noalloc.argtypes = [P, P, I, I, I, I, I, I, P, P]
+    lib.ca_route_noalloc.restype = I
     lib.ca_route_adaptive.argtypes = [P, P, P, I, I, I, I, I, F, F, I, P, P, P, P, S, P]
     lib.ca_route_adaptive.restype = I
     lib.ca_attend.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, I, I, F, P, P, P, S, P]
@@ -287,6 +290,24 @@ def route(cent_q, cent_k, topk: int, *, return_scores: bool = False, workspace=N
                          blocks.data_ptr(), _ptr(scores), _ptr(ws), nbytes, _stream_ptr(dev))
     _check(st)
     return (blocks, scores) if return_scores else blocks
+
+
+def route_noalloc(cent_q, cent_k, topk: int, *, blocks=None):
+    """ca_route_noalloc: top-k key clusters per query cluster without a
+    workspace (the library's scratch array holds the scores). ``blocks``, if
+    given, is the int32 output tensor [B,H,n_qc,topk]; nothing is allocated
+    then."""
+    torch = _torch()
+    B, H, nq, D = cent_q.shape
+    nk = cent_k.shape[2]
+    if blocks is None:
+        blocks = torch.empty((B, H, nq, topk), dtype=torch.int32, device=cent_q.device)
+    elif blocks.dtype != torch.int32 or tuple(blocks.shape) != (B, H, nq, topk) or not blocks.is_contiguous():
+        raise ValueError("blocks must be a contiguous int32 tensor [B,H,n_qc,topk]")
+    st = load().ca_route_noalloc(cent_q.data_ptr(), cent_k.data_ptr(), B, H, nq, nk, D, topk,
+                                 blocks.data_ptr(), _stream_ptr(cent_q.device))
+    _check(st)
+    return blocks
 
 
 def route_adaptive(cent_q, cent_k, counts_k, recall: float, *, min_count: int = 16,

@@ -329,6 +329,25 @@ int ca_route(const float* cent_q, const float* cent_k, int B, int H, int n_qc, i
   return after_launch();
 }
 
+int ca_route_noalloc(const float* cent_q, const float* cent_k, int B, int H, int n_qc, int n_kc,
+                     int D, int topk, int32_t* blocks, void* stream) {
+  set_error("");
+  if (!cent_q || !cent_k || !blocks) return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
+  if (B < 1 || H < 1 || n_qc < 1 || n_kc < 1) return fail(CA_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (!supported_d(D)) return fail(CA_ERR_UNSUPPORTED, "D must be 64 or 128");
+  if (topk < 1 || topk > n_kc) return fail(CA_ERR_INVALID_ARG, "topk must be in [1, n_kc]");
+  if (n_kc > 8192) return fail(CA_ERR_UNSUPPORTED, "n_kc must be <= 8192");
+  if ((int64_t)B * H > 32767 || n_qc > 65535) return fail(CA_ERR_UNSUPPORTED, "too many heads or query clusters");
+  if ((uint64_t)B * H * n_qc * n_kc > kRouteScratchFloats)
+    return fail(CA_ERR_UNSUPPORTED, "B*H*n_qc*n_kc exceeds the " + std::to_string(kRouteScratchFloats) +
+                                        " scores (32 MiB) of the allocation-free scratch; use ca_route");
+  float* sc = nullptr;
+  const char* err = "";
+  if (route_scratch(&sc, &err)) return fail(CA_ERR_HIP, std::string("scratch address: ") + err);
+  launch_route(cent_q, cent_k, B * H, n_qc, n_kc, D, topk, sc, blocks, static_cast<hipStream_t>(stream));
+  return after_launch();
+}
+
 int ca_route_adaptive(const float* cent_q, const float* cent_k, const int32_t* counts_k, int B,
                       int H, int n_qc, int n_kc, int D, float scale, float recall, int min_count,
                       int32_t* blocks, int32_t* nsel, float* scores, void* ws, size_t ws_bytes,

@@ -82,6 +82,12 @@ void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, in
 // route.hip ------------------------------------------------------------------
 void launch_route(const float* cq, const float* ck, int BH, int nq, int nk, int D, int topk,
                   float* scores, int32_t* blocks, hipStream_t st);
+// Scratch of the allocation-free routing call: at most kRouteScratchFloats
+// scores (B H n_qc n_kc), 32 MiB per device. route_scratch gives the device
+// address of that array on the current device (looked up once per device,
+// thread-safe); nonzero with *err set if the lookup fails.
+constexpr size_t kRouteScratchFloats = (size_t)8 << 20;
+int route_scratch(float** out, const char** err);
 // adaptive selection: blocks [BH][nq][nk] (the first nsel entries of a row
 // are the selected clusters, ascending; the rest -1), nsel [BH][nq]
 void launch_route_adaptive(const float* cq, const float* ck, const int32_t* counts, int BH, int nq,

@@ -3,9 +3,41 @@
 // then keep the top-k key clusters per query cluster (§3.3.2), ties to the
 // lower index, written in ascending order; or, adaptively, the clusters above
 // a histogram cutoff that meets a minimum count and a mass recall.
+#include <mutex>
+
 #include "kernels.h"
 
 namespace ca {
+
+// Score matrix of ca_route_noalloc: a file-scope device array instead of a
+// caller workspace. Every GPU the library runs on holds its own copy until
+// the process ends; host code must use the address hipGetSymbolAddress
+// returns for the current device, never the array's name (in host code that
+// name is only a stand-in for the symbol).
+static __device__ __align__(256) float scratch[kRouteScratchFloats];
+
+int route_scratch(float** out, const char** err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = "no usable current HIP device";
+    return 1;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = hipGetErrorString(e);
+      return 1;
+    }
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return 0;
+}
 
 namespace {
 

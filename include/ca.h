@@ -204,6 +204,29 @@ int ca_route(const float* cent_q, const float* cent_k, int B, int H, int n_qc, i
              void* stream);
 
 /*
+ * ca_route_noalloc -- ca_route for callers that cannot allocate memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same centroid scores and top-k selection as ca_route with
+ * scores = NULL, bit for bit, but the score matrix lives in a scratch array
+ * inside the library instead of a caller workspace, so neither the caller
+ * nor the library allocates anything.
+ *
+ * Arguments as ca_route (cent_q, cent_k, B, H, n_qc, n_kc, D, topk, blocks,
+ * stream); the stream's device must be the current device.
+ * Limit: B*H*n_qc*n_kc <= 8388608 scores (32 MiB of fp32; e.g. 40 heads of
+ * 256 x 256 clusters, or 8 heads of 1024 x 1024); larger calls return
+ * CA_ERR_UNSUPPORTED before launching anything (use ca_route).
+ * The scratch is one device array per GPU, held from the first call on that
+ * GPU until the process ends and shared by every call on it: calls that
+ * overlap on one GPU (concurrent streams or threads) race on it and must be
+ * serialised by the caller. Nothing in it needs to start at zero (every
+ * score is written before it is read). CA_ERR_HIP if the array's device
+ * address cannot be obtained.
+ */
+int ca_route_noalloc(const float* cent_q, const float* cent_k, int B, int H, int n_qc, int n_kc,
+                     int D, int topk, int32_t* blocks, void* stream);
+
+/*
  * ca_route_adaptive -- centroid scoring and adaptive selection (v1 §3.3.2
  * "Selection"; later revision §4.2): for each query cluster, the key
  * clusters of highest score until both min_count clusters and a fraction

@@ -123,6 +123,18 @@ def test_route_and_dense_reject_bad_arguments(lib):
     assert lib.ca_dense(FAKE, FAKE, FAKE, 0, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 8, None) == 3
 
 
+def test_route_noalloc_rejects_bad_arguments(lib):
+    # cent_q, cent_k, B, H, n_qc, n_kc, D, topk, blocks, stream
+    nr = lib.ca_route_noalloc
+    assert nr(FAKE, FAKE, 1, 1, 8, 8, 64, 4, None, None) == 1
+    assert nr(FAKE, FAKE, 1, 1, 8, 8, 64, 9, FAKE, None) == 1
+    assert nr(FAKE, FAKE, 1, 1, 8, 8, 96, 4, FAKE, None) == 2
+    # beyond the 8388608-score scratch: refused on the host, before any HIP call
+    assert nr(FAKE, FAKE, 1, 9, 1024, 1024, 64, 4, FAKE, None) == 2
+    assert b"scratch" in lib.ca_last_error()
+    assert nr(FAKE, FAKE, 2, 4, 1024, 1025, 64, 4, FAKE, None) == 2
+
+
 def test_adaptive_route_and_ragged_attend_reject_bad_arguments(lib):
     ra = lib.ca_route_adaptive
     # cent_q, cent_k, counts, B, H, n_qc, n_kc, D, scale, recall, min_count, blocks, nsel, scores, ws
