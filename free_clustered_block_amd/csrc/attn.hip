@@ -748,12 +748,7 @@ template <int D, int CQ, int CK, bool DENSE, bool FP8>
 void launch_mfma(const AttnArgs& a, hipStream_t st) {
   constexpr int KSPL = CQ == 64 ? 2 : 1;
   const size_t sm = attn_smem<D, FP8>();
-  static bool attr_set = false;   // raise the dynamic-LDS limit once per instantiation
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd<D, CQ, CK, DENSE, FP8, KSPL>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-    attr_set = true;
-  }
+  CA_MAX_LDS_ONCE((&attn_fwd<D, CQ, CK, DENSE, FP8, KSPL>), sm);
   dim3 g(a.nqc, a.BH);
   if (a.ev_start) (void)hipEventRecord(a.ev_start, st);
   attn_fwd<D, CQ, CK, DENSE, FP8, KSPL><<<g, 2 * CQ * KSPL, sm, st>>>(a);

@@ -833,12 +833,7 @@ void launch_basis_d(const void* Q, int dtype, int BH, int N, int transform, cons
   dim3 gr((D * D + 255) / 256, BH);
   qmoment_reduce<D><<<gr, 256, 0, st>>>(partial, nchunks, N, Cq);
   constexpr size_t sm = BasisLds<D>::bytes;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&basis_kernel<D>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-    attr_set = true;
-  }
+  CA_MAX_LDS_ONCE(&basis_kernel<D>, sm);
   basis_kernel<D><<<2 * BH, 256, sm, st>>>(Mq, Mk, Cq, transform, Rbuf, Zbuf, At);
 }
 
@@ -988,12 +983,7 @@ void launch_rotate_d(const void* Q, const void* K, int dtype, int BH, int N, con
     basis_split<D><<<(unsigned)(((int64_t)trees * D * D + 255) / 256), 256, 0, st>>>(At, trees, At3);
     dim3 g((N + kRotTokens - 1) / kRotTokens, trees);
     constexpr size_t sm = (size_t)3 * D * (D + 8) * 2;
-    static bool attr_set = false;
-    if (!attr_set) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rotate_bf16<D>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-      attr_set = true;
-    }
+    CA_MAX_LDS_ONCE(&rotate_bf16<D>, sm);
     rotate_bf16<D><<<g, kRotThreads, sm, st>>>((const uint16_t*)Q, (const uint16_t*)K, s, At3, N, Y, kvg);
   } else {
     dim3 g((N + 31) / 32, trees);

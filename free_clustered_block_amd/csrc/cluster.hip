@@ -1307,11 +1307,15 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
     pddp_dir_mma<D><<<gslots, DirMma<D>::NT, lds, st>>>(a);
   } else {
     const size_t lds = dir_smem<T, D>(a.N, a.c, a.level);
-    static size_t lds_allowed = 0;   // raise the dynamic-LDS limit when a level needs more
-    if (lds > lds_allowed) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&pddp_dir<T, D>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      lds_allowed = lds;
+    {   // raise the dynamic-LDS limit when a level needs more (host threads serialised)
+      static std::mutex mu;
+      static size_t lds_allowed = 0;
+      std::lock_guard<std::mutex> lock(mu);
+      if (lds > lds_allowed) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&pddp_dir<T, D>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        lds_allowed = lds;
+      }
     }
     pddp_dir<T, D><<<gslots, 256, lds, st>>>(a);
   }

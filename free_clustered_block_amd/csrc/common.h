@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <string>
 
 #define CA_DEV __device__ __forceinline__
@@ -188,4 +189,15 @@ void set_error(const std::string& s);
       ::ca::set_error(std::string(#expr) + ": " + hipGetErrorString(e_));    \
       return 4;                                                              \
     }                                                                        \
+  } while (0)
+
+// Raises a kernel's dynamic-LDS limit to `bytes` once per process (per call
+// site; std::call_once makes the first launch from several host threads safe).
+#define CA_MAX_LDS_ONCE(kernel_ptr, bytes)                                                 \
+  do {                                                                                     \
+    static std::once_flag once_;                                                           \
+    std::call_once(once_, [&] {                                                            \
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel_ptr),                 \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)(bytes)); \
+    });                                                                                    \
   } while (0)

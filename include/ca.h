@@ -18,7 +18,12 @@
  *  - Every pointer argument is a device pointer owned by the caller unless it
  *    is documented as a host pointer. The library never allocates device or
  *    host memory, never frees caller memory and keeps no state between calls
- *    except a thread-local error string.
+ *    except a thread-local error string, with three stated exceptions: the
+ *    per-thread profiling events of ca_profile_events (a timing hook outside
+ *    the computation, off unless set), the scratch array of ca_route_noalloc
+ *    (one per GPU, for callers that cannot allocate), and a once-per-process,
+ *    thread-safe raise of some kernels' dynamic LDS limit at their first
+ *    launch.
  *  - Scratch memory is passed in as `ws` (device, 256-byte aligned) of
  *    `ws_bytes` bytes; ca_workspace_size() gives the bytes a call needs.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
@@ -378,6 +383,9 @@ int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, in
  * `start` on their stream immediately before their main attention kernel and
  * `stop` immediately after it, so the caller can time that kernel alone with
  * hipEventElapsedTime. Pass NULL, NULL to switch it off. Returns CA_OK.
+ * This is per-thread state outside the stateless contract above: while it is
+ * set, ca_attend* and ca_dense enqueue the two event records besides their
+ * kernels (their results are unchanged). It is off by default.
  */
 int ca_profile_events(void* start, void* stop);
 

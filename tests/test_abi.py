@@ -235,3 +235,33 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_calls_from_several_threads(lib):
+    """The host side keeps no shared state on these paths: workspace sizing
+    and argument validation from eight threads at once give each thread its
+    own results and its own ca_last_error string."""
+    import threading
+    import free_clustered_block_amd as ca
+    want_ws = ca.workspace_size(ca.OP_ATTEND, 1, 8, 65536, 64, 128, 64)
+    errors = []
+
+    def work(k):
+        try:
+            for i in range(200):
+                assert ca.workspace_size(ca.OP_ATTEND, 1, 8, 65536, 64, 128, 64) == want_ws
+                if (i + k) % 2:
+                    assert _attend(lib, D=32) == 2
+                    assert b"D must be" in lib.ca_last_error()
+                else:
+                    assert _cluster(lib, c=100) == 2
+                    assert b"cluster_size" in lib.ca_last_error()
+        except AssertionError as e:      # pragma: no cover - reported below
+            errors.append((k, e))
+
+    ts = [threading.Thread(target=work, args=(k,)) for k in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors
