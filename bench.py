@@ -17,10 +17,14 @@ Prints one JSON line:
              counting 4 d FLOP per performed token or centroid interaction,
              timed with HIP events recorded around that kernel alone
   cpu_baseline  the CPU oracle on a bounded sample of heads of the same input
-Also reported: per-step median/p10/p90 from HIP events, the same steps with
-the caches flushed before each one (cold), and the measured HBM copy and bf16
-GEMM rates of the box (a 1 GiB torch copy, which also serves as the plain-copy
-calibration of the HBM byte counters, and an 8192^3 torch.matmul).
+The headline (value, ms_per_step) is the median of the K timed steps, each
+run after a 512 MiB write that flushes the L2 caches and the 256 MB MALL
+(cold), timed by HIP events around the step; the same K steps run back to back
+(warm) are reported beside it with per-stage times. Also reported: the
+measured HBM copy and bf16 GEMM rates of the box (a 1 GiB torch copy, which
+also serves as the plain-copy calibration of the HBM byte counters, and an
+8192^3 torch.matmul), and the same forward on the tabular workloads
+(8 x 65536 and 8 x 262144 tokens, d 64) under "other_workloads".
 """
 from __future__ import annotations
 
@@ -92,8 +96,9 @@ def parse():
                     help="skip the torch scaled_dot_product_attention (flash backend) reference")
     ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=5,
-                    help="steps timed one by one after a 512 MiB cache flush")
+    ap.add_argument("--others", default="tabular_64k,tabular_256k",
+                    help="further workloads timed in the same run (comma-separated; '' for none)")
+    ap.add_argument("--other-steps", type=int, default=5)
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the copy and GEMM rate measurements")
     ap.add_argument("--split-mode", choices=["power", "diag"], default="power",
@@ -133,15 +138,56 @@ def gen_inputs(w):
     return Q, K, V
 
 
+def host_info():
+    """CPU model and the BLAS numpy runs on (vendor, version, threads)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = {}
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = {"vendor": i.get("internal_api"), "version": i.get("version"),
+                        "threads": i.get("num_threads"), "arch": i.get("architecture")}
+                break
+    except Exception:
+        pass
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "blas": blas}
+
+
+def oracle_small_case(synth):
+    """The oracle on the whole 1024-token fp32 workload (1 head, d 64, c 64,
+    top 4), with the BLAS threads as set and with one thread."""
+    import oracle.clusterattn as o
+    from threadpoolctl import threadpool_limits
+    w = synth.WORKLOADS["small_gmm_1k"]
+    Q, K, V = synth.generate(w)
+    opts = o.ClusterOpts(seed=w.cluster_seed)
+    out = {"workload": w.name}
+    for label, limit in (("all_threads_s", None), ("one_thread_s", 1)):
+        ts = []
+        for _ in range(3):
+            with threadpool_limits(limits=limit):
+                t0 = time.perf_counter()
+                o.forward(Q, K, V, w.c, w.topk, w.compensate, opts, w.dtype)
+                ts.append(time.perf_counter() - t0)
+        out[label] = round(float(np.median(ts)), 4)
+    return out
+
+
 def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power", assign="topk", recall=0.9,
                  min_count=16, qk="exact"):
     """The oracle, untuned, on the first `heads` heads of the same input."""
     import oracle.clusterattn as o
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
+    info = host_info()
+    cores = int(info["blas"].get("threads") or 1)
     opts = o.ClusterOpts(seed=w.cluster_seed, split_mode=split_mode,
                          query_normalize=assign == "topk")
     t0 = time.perf_counter()
@@ -171,6 +217,7 @@ def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power", assign="topk", rec
                   f"{' (FP8 Q.K^T operands)' if qk == 'e4m3' else ''} "
                   f"(BLAS threads={cores}; PDDP and top-k loops single-threaded Python)",
         "seconds": t,
+        **info,
     }
 
 
@@ -312,34 +359,17 @@ def sweep(args, torch, synth, ca):
                                       "speedup_vs_dense": round(dense_ms / ms, 3)}), flush=True)
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads would shard across GPUs with no communication); run with --gpus 1",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import synth
-    import free_clustered_block_amd as ca
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    ca.load()
-    if args.sweep:
-        sweep(args, torch, synth, ca)
-        return
-    w = synth.WORKLOADS[args.workload]
-    topk = args.topk or w.topk
-    dev = torch.device("cuda:0")
+def run_workload(args, wname, torch, synth, ca, dev, steps, warmup, full=True):
+    """Times the forward on one workload; returns the result dict (the JSON
+    line's fields). full=False skips the torch SDPA reference, the peaks and
+    the CPU baseline (the extra workloads of one run)."""
+    w = synth.WORKLOADS[wname]
+    topk = (args.topk or w.topk) if full else w.topk
     t_gen = time.perf_counter()
     Qn, Kn, Vn = gen_inputs(w)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     Q = torch.from_numpy(Qn).to(tdt).to(dev).contiguous()
-    kvh = args.kv_heads or w.H
+    kvh = (args.kv_heads or w.H) if full else w.H
     if w.H % kvh != 0:
         print("--kv-heads must divide the workload's head count", file=sys.stderr)
         sys.exit(2)
@@ -350,11 +380,16 @@ def main():
     K = torch.from_numpy(Kn).to(tdt).to(dev).contiguous()
     V = torch.from_numpy(Vn).to(tdt).to(dev).contiguous()
     if args.verbose:
-        print(f"inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+        print(f"{wname}: inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
+              flush=True)
     B, H, N, D = Q.shape
-    c = w.c                      # key cluster size
-    cq = args.cq or c            # query cluster size
-    op_c = ca.OP_CLUSTER_DIAG if args.split_mode == "diag" else ca.OP_CLUSTER
+    c = w.c                                  # key cluster size
+    cq = (args.cq or c) if full else c       # query cluster size
+    split_mode = args.split_mode if full else "power"
+    adaptive = full and args.assign == "adaptive"
+    fp8 = full and args.fp8
+    kv_share = full and args.kv_share
+    op_c = ca.OP_CLUSTER_DIAG if split_mode == "diag" else ca.OP_CLUSTER
     ws_c = torch.empty(ca.workspace_size(op_c, B, H, N, D, min(c, cq)), dtype=torch.uint8,
                        device=dev)
     n_c = -(-N // c)
@@ -364,14 +399,12 @@ def main():
     ws_a = torch.empty(ca.workspace_size(ca.OP_ATTEND, B, H, N, D, c, topk), dtype=torch.uint8,
                        device=dev)
 
-    adaptive = args.assign == "adaptive"
-
     def step(evs=None, kev=None):
         if evs:
             evs[0].record()
-        cr = ca.cluster(Q, K, cq, seed=w.cluster_seed, split_mode=args.split_mode,
+        cr = ca.cluster(Q, K, cq, seed=w.cluster_seed, split_mode=split_mode,
                         query_normalize=not adaptive, cluster_size_k=c if cq != c else 0,
-                        kv_share=args.kv_share, workspace=ws_c)
+                        kv_share=kv_share, workspace=ws_c)
         if evs:
             evs[1].record()
         if adaptive:
@@ -381,27 +414,50 @@ def main():
             blocks, nsel = ca.route(cr.cent_q, cr.cent_k, topk, workspace=ws_r), None
         if evs:
             evs[2].record()
-            ca.profile_events(kev[0].handle, kev[1].handle)
+            if kev is not None:
+                ca.profile_events(kev[0].handle, kev[1].handle)
         O = ca.attend(Q, K, V, cr.perm_q, cr.perm_k, cq, blocks, compensate=w.compensate,
-                      nsel=nsel, c_k=c, fp8=args.fp8, workspace=ws_a)
+                      nsel=nsel, c_k=c, fp8=fp8, workspace=ws_a)
         if evs:
-            ca.profile_events(None, None)
+            if kev is not None:
+                ca.profile_events(None, None)
             evs[3].record()
         return O, cr, (blocks, nsel)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    kevs = [(ca.HipEvent(), ca.HipEvent()) for _ in range(args.steps)]
+
+    # headline: K steps, each after a 512 MiB write that flushes the L2 caches
+    # and the MALL; HIP events around the step alone
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(steps)]
+    torch.cuda.synchronize()
+    tc = time.perf_counter()
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        cold[i][0].record()
+        step()
+        cold[i][1].record()
+    torch.cuda.synchronize()
+    cold_wall = (time.perf_counter() - tc) / steps
+    del flush
+    cold_ms = np.array([a.elapsed_time(b) for a, b in cold])
+
+    # warm: the same K steps back to back, with per-stage events and the
+    # attention kernel's own events
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    kevs = [(ca.HipEvent(), ca.HipEvent()) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         O, cr, blocks = step(evs[i], kevs[i])
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / args.steps
+    wall = (time.perf_counter() - t0) / steps
     if args.verbose:
-        print(f"timed {args.steps} steps: {wall * 1e3:.3f} ms/step", file=sys.stderr, flush=True)
+        print(f"{wname}: cold median {np.median(cold_ms):.3f} ms, warm {wall * 1e3:.3f} ms/step",
+              file=sys.stderr, flush=True)
     step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     st_cluster = np.mean([e[0].elapsed_time(e[1]) for e in evs])
     st_route = np.mean([e[1].elapsed_time(e[2]) for e in evs])
@@ -430,7 +486,7 @@ def main():
 
     # the same step captured once in a HIP graph (fixed shapes) and replayed
     graph_ms = None
-    if args.graph:
+    if full and args.graph:
         gs = torch.cuda.Stream()
         gs.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(gs):
@@ -443,63 +499,64 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
         tg = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             graph.replay()
         torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - tg) / args.steps * 1e3
+        graph_ms = (time.perf_counter() - tg) / steps * 1e3
         del graph
 
-    # the same step with every cache flushed first (HIP events around the step only)
-    cold_ms = []
-    if args.cold_steps > 0:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        for i in range(args.cold_steps):
-            flush.fill_(i & 0xFF)
-            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a_ev.record()
-            step()
-            b_ev.record()
-            torch.cuda.synchronize()
-            cold_ms.append(a_ev.elapsed_time(b_ev))
-        del flush
-
-    # clustering + routing against the HBM roofline: algorithmic bytes are, per
-    # split level, tensor and token, the row read for the projection plus the
-    # index read and write (2 D e + 8 B, e = element size), plus the
-    # compulsory metric pass (Q and K rows) and centroid pass (Q, K, V rows)
+    # clustering + routing against the HBM roofline. Algorithmic bytes: per
+    # tree actually built, per split level and token, the row read for the
+    # projection plus the index read and write (2 D e + 8 B, e = element
+    # size); plus the compulsory metric pass (every query row and every key
+    # row of the key/value heads) and centroid pass (query rows per head, key
+    # and value rows per key tree).
     esz = 2 if w.dtype == "bf16" else 4
-    n_levels = ca.tree_levels(N, c)
-    clu_bytes = float(B * H) * (n_levels * 2 * N * (D * esz + 8) + 5 * N * D * esz)
+    row = N * D * esz
+    key_trees = B * (H // (H // kvh) if kv_share else H)
+    q_trees = B * H
+    clu_bytes = float(q_trees * ca.tree_levels(N, cq) * N * (D * esz + 8)
+                      + key_trees * ca.tree_levels(N, c) * N * (D * esz + 8)
+                      + (q_trees + B * kvh) * row + (q_trees + 2 * key_trees) * row)
     clu_ms = float(st_cluster + st_route)
     clu_gbs = clu_bytes / (clu_ms * 1e-3) / 1e9
 
-    traffic = (recorded_traffic(w.name, topk, args.fp8) if B * H == w.B * w.H and not adaptive
-               and args.split_mode == "power" and cq == c and kvh == w.H else None)
-    peak = PEAK_FP8QK_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
-    eff = 4.0 * D * N * N * B * H / (wall) / 1e12
+    traffic = (recorded_traffic(w.name, topk, fp8) if B * H == w.B * w.H and not adaptive
+               and split_mode == "power" and cq == c and kvh == w.H else None)
+    peak = PEAK_FP8QK_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    dense_eq = 4.0 * D * N * N * B * H
+    head_ms = float(np.median(cold_ms))
     result = {
         "metric": METRIC,
-        "value": round(eff, 3),
+        "value": round(dense_eq / (head_ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s (dense-equivalent, 4 d N^2 H per step)",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3, 4),
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(head_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8e4m3 (Q.K^T) + bf16 (P.V)" if args.fp8
+        "dtype": ("fp8e4m3 (Q.K^T) + bf16 (P.V)" if fp8
                   else "bf16" if w.dtype == "bf16" else "f32"),
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "N": N, "head_dim": D,
                    "cluster_size": c, "topk": topk, "compensate": w.compensate,
-                   "split_mode": args.split_mode, "assign": args.assign,
+                   "split_mode": split_mode, "assign": "adaptive" if adaptive else "topk",
                    **({"qk_operands": "fp8 e4m3, per-token query / per-64-key scales"}
-                      if args.fp8 else {}),
+                      if fp8 else {}),
                    **({"query_cluster_size": cq} if cq != c else {}),
-                   **({"kv_heads": kvh, "kv_share": bool(args.kv_share)} if kvh != w.H else {}),
+                   **({"kv_heads": kvh, "kv_share": bool(kv_share)} if kvh != w.H else {}),
                    **({"recall": args.recall, "min_count": args.min_count,
                        "mean_selected": round(mean_sel, 2)} if adaptive else {})},
+        "timing": ("value and ms_per_step: median of the K timed steps, each after a 512 MiB "
+                   "cache flush (cold), HIP events around the step; warm: the same K steps "
+                   "back to back"),
+        "cold": {"ms_median": round(head_ms, 4), "ms_p10": round(float(np.percentile(cold_ms, 10)), 4),
+                 "ms_p90": round(float(np.percentile(cold_ms, 90)), 4),
+                 "wall_ms_per_step_with_flush": round(cold_wall * 1e3, 4)},
+        "warm": {"ms_per_step": round(wall * 1e3, 4),
+                 "value": round(dense_eq / wall / 1e12, 3)},
         "stage_ms": {"cluster": round(float(st_cluster), 4), "route": round(float(st_route), 4),
                      "attend": round(float(st_attend), 4),
                      "attend_kernel": round(float(t_attn_kernel), 4),
@@ -507,7 +564,6 @@ def main():
                      "step_median": round(float(np.median(step_ms)), 4),
                      "step_p10": round(float(np.percentile(step_ms, 10)), 4),
                      "step_p90": round(float(np.percentile(step_ms, 90)), 4),
-                     "cold_step_median": round(float(np.median(cold_ms)), 4) if cold_ms else None,
                      "graph_replay": round(graph_ms, 4) if graph_ms is not None else None},
         "roofline": {
             "kernel": "attn_fwd (block-sparse attention + SMC)",
@@ -515,7 +571,7 @@ def main():
             "achieved": round(achieved, 2),
             "peak": round(peak, 1),
             **({"peak_note": "half the FLOPs (Q.K^T) at the fp8 5.0 PFLOP/s peak, half "
-                             "(P.V) at the bf16 2.5 PFLOP/s peak"} if args.fp8 else {}),
+                             "(P.V) at the bf16 2.5 PFLOP/s peak"} if fp8 else {}),
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
@@ -534,14 +590,14 @@ def main():
         Kd = K.repeat_interleave(w.H // kvh, dim=1).contiguous() if kvh != w.H else K
         Vd = V.repeat_interleave(w.H // kvh, dim=1).contiguous() if kvh != w.H else V
 
-        def time_dense(fp8):
-            Od = ca.dense(Q, Kd, Vd, fp8=fp8, workspace=ws_d)
+        def time_dense(use_fp8):
+            Od = ca.dense(Q, Kd, Vd, fp8=use_fp8, workspace=ws_d)
             torch.cuda.synchronize()
             de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(args.dense_steps)]
             for a, b in de:
                 a.record()
-                Od = ca.dense(Q, Kd, Vd, fp8=fp8, workspace=ws_d)
+                Od = ca.dense(Q, Kd, Vd, fp8=use_fp8, workspace=ws_d)
                 b.record()
             torch.cuda.synchronize()
             return Od, float(np.mean([a.elapsed_time(b) for a, b in de]))
@@ -552,21 +608,23 @@ def main():
         # the dense baseline in the path's own precision ("given equal
         # quantization"); with --fp8 the bf16 dense output is the reference of
         # both cosines
-        Od, dense_ms = time_dense(args.fp8)
+        Od, dense_ms = time_dense(fp8)
         result["dense_ms"] = round(dense_ms, 4)
-        result["speedup_vs_dense"] = round(dense_ms / (wall * 1e3), 3)
-        result["dense_tflops"] = round(4.0 * D * N * N * B * H / (dense_ms * 1e-3) / 1e12, 2)
-        if args.fp8:
+        result["speedup_vs_dense"] = round(dense_ms / head_ms, 3)
+        result["speedup_vs_dense_warm"] = round(dense_ms / (wall * 1e3), 3)
+        result["dense_tflops"] = round(dense_eq / (dense_ms * 1e-3) / 1e12, 2)
+        if fp8:
             Ob, dense_bf16_ms = time_dense(False)
             result["dense_bf16_ms"] = round(dense_bf16_ms, 4)
             result["cos_vs_dense"] = round(cosine(O, Ob), 5)
             result["cos_dense_fp8_vs_dense_bf16"] = round(cosine(Od, Ob), 5)
         else:
             result["cos_vs_dense"] = round(cosine(O, Od), 5)
+        del Od
 
         # reference only: torch's fused dense attention (flash backend) on the
         # same bf16 inputs, 3 timed calls
-        if not args.no_sdpa and w.dtype == "bf16":
+        if full and not args.no_sdpa and w.dtype == "bf16":
             try:
                 from torch.nn.attention import SDPBackend, sdpa_kernel
                 with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
@@ -581,24 +639,63 @@ def main():
                     torch.cuda.synchronize()
                 sdpa_ms = float(np.median([a.elapsed_time(b) for a, b in se]))
                 result["torch_sdpa_flash_ms"] = round(sdpa_ms, 4)
-                result["speedup_vs_torch_sdpa"] = round(sdpa_ms / (wall * 1e3), 3)
+                result["speedup_vs_torch_sdpa"] = round(sdpa_ms / head_ms, 3)
             except Exception as e:   # not available on this build: reported as absent
                 result["torch_sdpa_flash_ms"] = None
                 if args.verbose:
                     print(f"torch SDPA reference unavailable: {e}", file=sys.stderr)
 
-    if not args.no_peaks:
+    if full and not args.no_peaks:
         result["measured_peaks"] = measure_peaks(torch, dev)
 
-    if not args.no_cpu_baseline:
+    if full and not args.no_cpu_baseline:
         heads = max(1, min(args.cpu_heads, H))
         if kvh != w.H:
             Kn = np.repeat(Kn, w.H // kvh, axis=1)
             Vn = np.repeat(Vn, w.H // kvh, axis=1)
-        result["cpu_baseline"] = cpu_baseline(w, Qn, Kn, Vn, topk, heads, args.split_mode,
-                                              args.assign, args.recall, args.min_count,
-                                              "e4m3" if args.fp8 else "exact")
+        result["cpu_baseline"] = cpu_baseline(w, Qn, Kn, Vn, topk, heads, split_mode,
+                                              "adaptive" if adaptive else "topk", args.recall,
+                                              args.min_count, "e4m3" if fp8 else "exact")
+        result["cpu_baseline"]["small_fp32_case"] = oracle_small_case(synth)
+    return result
 
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no communication); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import free_clustered_block_amd as ca
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ca.load()
+    if args.sweep:
+        sweep(args, torch, synth, ca)
+        return
+    dev = torch.device("cuda:0")
+    result = run_workload(args, args.workload, torch, synth, ca, dev, args.steps, args.warmup)
+    torch.cuda.empty_cache()
+    others = {}
+    for name in [x for x in args.others.split(",") if x and x != args.workload]:
+        r = run_workload(args, name, torch, synth, ca, dev, args.other_steps, 2, full=False)
+        torch.cuda.empty_cache()
+        others[name] = {k: r[k] for k in ("config", "ms_per_step", "value", "warm", "stage_ms",
+                                          "dense_ms", "speedup_vs_dense", "cos_vs_dense")
+                        if k in r}
+        others[name]["roofline_frac"] = r["roofline"]["frac"]
+        others[name]["cluster_route_hbm_frac"] = r["cluster_route_hbm"]["frac"]
+        if args.verbose:
+            print(f"{name}: {others[name]['ms_per_step']} ms", file=sys.stderr, flush=True)
+    if others:
+        result["other_workloads"] = others
     print(json.dumps(result), flush=True)
 
 
