@@ -267,7 +267,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     for (int level = 0; level < L; ++level) {
       if (o.trace_perm)
         if (int e = trace_copy(o.trace_perm + level * TN, cur)) return e;
-      LevelArgs a;
+      LevelArgs a{};
       a.Q = Q; a.K = K; a.dtype = dt == CA_BF16 ? 0 : 1;
       a.BH = BH; a.N = N; a.D = D; a.c = ct; a.level = level; a.kvg = kvg;
       a.transform = o.transform; a.power_iters = o.power_iters; a.sample_factor = o.sample_factor;

@@ -14,6 +14,9 @@
 //                 partition of the node's permutation slice.
 // The node layout depends only on (N, c) and is recomputed on the device, so
 // no host synchronisation is needed between levels.
+#include <algorithm>
+#include <utility>
+
 #include "kernels.h"
 #include "mfma.h"
 
@@ -515,6 +518,26 @@ size_t dir_smem(int N, int c, int level) {
 // a time in one round trip and stored transposed (dimension-major) in LDS.
 // ----------------------------------------------------------------------------
 
+// Matrix-vector step of the power iteration with the vector broadcast across
+// lanes instead of re-read from LDS by every lane. The 16 lanes of a DPP row
+// (one lane half) need the same 64 vector entries; lane j of the row holds
+// entries 32 (j >> 2) + 8 (j & 3) + 4 h + 0..3, and row_newbcast:k hands lane
+// k's four values to the whole row, fused into the multiply-add.
+template <int K>
+CA_DEV void fmac_row_bcast(float& acc, float u, float c) {
+  asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+               : "+v"(acc)
+               : "v"(u), "v"(c), "i"(K));
+}
+// t4[e] += sum over k of m[4 k + e] * (entry e of row lane k's vector values)
+template <int... K>
+CA_DEV void matvec_row_bcast(float (&t4)[4], const floatx4_t& uv, const float* m,
+                             std::integer_sequence<int, K...>) {
+  ((fmac_row_bcast<K>(t4[0], uv[0], m[4 * K]), fmac_row_bcast<K>(t4[1], uv[1], m[4 * K + 1]),
+    fmac_row_bcast<K>(t4[2], uv[2], m[4 * K + 2]), fmac_row_bcast<K>(t4[3], uv[3], m[4 * K + 3])),
+   ...);
+}
+
 template <int D>
 struct DirMma {
   static constexpr int NW = D / 32;          // waves; wave w owns columns [32w, 32w + 32)
@@ -539,7 +562,8 @@ void pddp_dir_mma(LevelArgs a) {
   __shared__ __attribute__((aligned(16))) float xbar[D];
   __shared__ __attribute__((aligned(16))) float su0[D];
   __shared__ __attribute__((aligned(16))) float tbuf[D];
-  __shared__ __attribute__((aligned(16))) float vbuf[D];
+  __shared__ __attribute__((aligned(16))) float vbuf[2][D];   // by iteration parity
+  __shared__ float nred[2][NW];                               // |v|^2 per wave, by parity
   __shared__ float red[3][NW];
   __shared__ int ired[NW];
   extern __shared__ int spre[];              // chunk prefix sums [nch + 1]
@@ -572,15 +596,42 @@ void pddp_dir_mma(LevelArgs a) {
     rj -= 2.0f;
   }
 
-  // sample size: prefix over the node's chunk counts
+  // Sample size. Chunk-list mode: prefix over the node's chunk counts (lists
+  // written by pddp_sample). Inline mode (nodes of at most 32 NT members, so
+  // a thread's positions fit one 32-bit mask): thread tid tests the content hashes of positions
+  // [tid per, tid per + per) itself, so the sample comes out in position
+  // order, as the concatenated chunk lists would.
+  const bool inl = a.sample_inline != 0;
   const int ch0 = off / a.c;
   const int nch = (n + a.c - 1) / a.c;
   const int32_t* cnt = a.chunk_cnt + (int64_t)tree * a.nchunks + ch0;
-  const int per = (nch + NT - 1) / NT;
+  const int per = inl ? (n + NT - 1) / NT : (nch + NT - 1) / NT;
   const int g0 = tid * per;
   int gs = 0;
-  for (int k = 0; k < per; ++k)
-    if (g0 + k < nch) gs += cnt[g0 + k];
+  uint32_t sbits = 0;   // inline mode: sampled positions g0 + k of this thread
+  int ptok[4] = {0, 0, 0, 0};   // inline mode, per <= 4: their tokens, read with the hashes
+  if (inl) {
+    uint64_t salt = 0;
+    salt = chain_step(salt, a.seed);
+    salt = chain_step(salt, kDomainSample);
+    salt = chain_step(salt, (uint64_t)tensor);
+    salt = chain_step(salt, (uint64_t)a.level);
+    const uint64_t ad = (uint64_t)a.sample_factor * D;
+    const bool take_all = ad >= (uint64_t)n;
+    const uint64_t thr = take_all ? 0 : ((ad << 32) / (uint64_t)n);
+    const uint64_t* hpos = a.hpos_in + (int64_t)tree * a.N + off;
+    if (per <= 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k < per && g0 + k < n) ptok[k] = perm[g0 + k];
+    }
+    for (int k = 0; k < per; ++k)
+      if (g0 + k < n && (take_all || (fmix64(hpos[g0 + k] ^ salt) >> 32) < thr)) sbits |= 1u << k;
+    gs = __popc(sbits);
+  } else {
+    for (int k = 0; k < per; ++k)
+      if (g0 + k < nch) gs += cnt[g0 + k];
+  }
   {
     const float srr = wave_sum(rj * rj), srp = wave_sum(rj * pj), spp = wave_sum(pj * pj);
     if (l == 0) { red[0][w] = srr; red[1][w] = srp; red[2][w] = spp; }
@@ -593,12 +644,18 @@ void pddp_dir_mma(LevelArgs a) {
   }
   if (l == 63) ired[w] = inc;
   __syncthreads();
+  int srun = 0;   // inline mode: sample rows before this thread's positions
   {
     int run = inc - gs;
     for (int q = 0; q < w; ++q) run += ired[q];
-    for (int k = 0; k < per; ++k)
-      if (g0 + k < nch) { spre[g0 + k] = run; run += cnt[g0 + k]; }
-    if (tid == NT - 1) spre[nch] = run;
+    if (inl) {
+      srun = run;
+      if (tid == NT - 1) spre[0] = run + gs;
+    } else {
+      for (int k = 0; k < per; ++k)
+        if (g0 + k < nch) { spre[g0 + k] = run; run += cnt[g0 + k]; }
+      if (tid == NT - 1) spre[nch] = run;
+    }
     // u0 = normalise(parent + r / |r|), or r / |r| at the root
     float srr = 0.0f, srp = 0.0f, spp = 0.0f;
 #pragma unroll
@@ -612,23 +669,40 @@ void pddp_dir_mma(LevelArgs a) {
     if (tid < D) su0[tid] = u0;
   }
   __syncthreads();
-  int m = spre[nch];
+  int m = spre[inl ? 0 : nch];
   const bool whole = m < 2;     // fewer than two sampled rows: the whole node
   if (whole) m = n;
-  const int32_t* lists = a.sample_buf + (int64_t)tree * a.N;
-  for (int rr = tid; rr < m; rr += NT) {
-    int tok;
-    if (whole) {
-      tok = perm[rr];
-    } else {
-      int lo = 0, hi = nch - 1;     // last chunk k with spre[k] <= rr
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (spre[mid] <= rr) lo = mid; else hi = mid - 1;
+  if (inl && !whole) {
+    // this thread's sampled positions, in order, at rows srun, srun + 1, ...
+    for (uint32_t b = sbits; b; b &= b - 1) {
+      const int k = __builtin_ctz(b);
+      int tok;
+      if (per <= 4) {
+        tok = ptok[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) tok = k == q ? ptok[q] : tok;
+      } else {
+        tok = perm[g0 + k];
       }
-      tok = lists[(int64_t)(ch0 + lo) * a.c + (rr - spre[lo])];
+      if (srun < TOKCAP) tokl[srun] = tok; else stok[srun] = tok;
+      ++srun;
     }
-    if (rr < TOKCAP) tokl[rr] = tok; else stok[rr] = tok;
+  } else {
+    const int32_t* lists = a.sample_buf + (int64_t)tree * a.N;
+    for (int rr = tid; rr < m; rr += NT) {
+      int tok;
+      if (whole) {
+        tok = perm[rr];
+      } else {
+        int lo = 0, hi = nch - 1;     // last chunk k with spre[k] <= rr
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (spre[mid] <= rr) lo = mid; else hi = mid - 1;
+        }
+        tok = lists[(int64_t)(ch0 + lo) * a.c + (rr - spre[lo])];
+      }
+      if (rr < TOKCAP) tokl[rr] = tok; else stok[rr] = tok;
+    }
   }
   __syncthreads();
 
@@ -773,59 +847,59 @@ void pddp_dir_mma(LevelArgs a) {
   }
 
   // --- power iterations -------------------------------------------------------
-  // Each iteration reads the previous v (the warm start first) once: t = C v
-  // and |v|^2 come from the same values, then t is scaled by 1/|v| (u = v/|v|).
-  // vbuf is rewritten only after the next barrier.
+  // Iteration it reads v of iteration it - 1 (the warm start first) once and
+  // forms t = C v / |v|; |v|^2 is the sum, in wave order, of the per-wave
+  // sums of squares its writers left beside it. v and those sums are double
+  // buffered by iteration parity: a buffer is rewritten two iterations later,
+  // after every wave has passed the barrier that follows its last read.
   bool fallback = false;
   float inv_norm = 1.0f;
+  int last = 0;   // buffer holding the final v
+  // vector entries this lane holds for its DPP row (lanes past RT * 4 repeat row lane 0's)
+  const int j16 = (l & 15) < RT * 4 ? (l & 15) : 0;
+  const int vsel = 32 * (j16 >> 2) + 8 * (j16 & 3) + 4 * h;
   for (int it = 0;; ++it) {
-    const float* usrc = it == 0 ? su0 : vbuf;
-    floatx4_t ub[RT * 4];
+    const float* usrc = it == 0 ? su0 : vbuf[(it - 1) & 1];
+    const floatx4_t uv = *reinterpret_cast<const floatx4_t*>(&usrc[vsel]);
+    float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    {
+      float cf[RT * 16];   // the C strip in matvec order: element 4 k + e
 #pragma unroll
-    for (int k = 0; k < RT * 4; ++k)
-      ub[k] = *reinterpret_cast<const floatx4_t*>(&usrc[32 * (k >> 2) + 8 * (k & 3) + 4 * h]);
-    __builtin_amdgcn_sched_barrier(0);
-    float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, n4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int k = 0; k < RT * 4; ++k)
 #pragma unroll
-    for (int k = 0; k < RT * 4; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        t4[e] = fmaf(acc[k >> 2][4 * (k & 3) + e], ub[k][e], t4[e]);
-        n4[e] = fmaf(ub[k][e], ub[k][e], n4[e]);
-      }
+        for (int e = 0; e < 4; ++e) cf[4 * k + e] = acc[k >> 2][4 * (k & 3) + e];
+      matvec_row_bcast(t4, uv, cf, std::make_integer_sequence<int, RT * 4>{});
+    }
     float tp = (t4[0] + t4[1]) + (t4[2] + t4[3]);
-    float nn = (n4[0] + n4[1]) + (n4[2] + n4[3]);
     tp = sum_halves(tp);
-    nn = sum_halves(nn);   // the two half-waves' rows cover every index once
     if (it > 0) {
+      float nn = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) nn += nred[(it - 1) & 1][q];
       if (nn == 0.0f) { fallback = true; break; }
       inv_norm = 1.0f / sqrtf(nn);
-      if (it == a.power_iters) break;
+      if (it == a.power_iters) { last = (it - 1) & 1; break; }
       tp *= inv_norm;
     }
     float vp = tp;
     if (a.transform) {
       if (h == 0) tbuf[32 * w + r] = tp;
       __syncthreads();
-      floatx4_t tb[RT * 4];
-#pragma unroll
-      for (int k = 0; k < RT * 4; ++k)
-        tb[k] = *reinterpret_cast<const floatx4_t*>(&tbuf[32 * (k >> 2) + 8 * (k & 3) + 4 * h]);
-      __builtin_amdgcn_sched_barrier(0);
+      const floatx4_t tv = *reinterpret_cast<const floatx4_t*>(&tbuf[vsel]);
       float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int k = 0; k < RT * 4; ++k)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = fmaf(mr[4 * k + e], tb[k][e], v4[e]);
+      matvec_row_bcast(v4, tv, mr, std::make_integer_sequence<int, RT * 4>{});
       vp = (v4[0] + v4[1]) + (v4[2] + v4[3]);
       vp = sum_halves(vp);
     }
-    if (h == 0) vbuf[32 * w + r] = vp;
+    // both lane halves hold v[32 w + r]: the first half's squares are the wave's share
+    const float sq = wave_sum(h == 0 ? vp * vp : 0.0f);
+    if (h == 0) vbuf[it & 1][32 * w + r] = vp;
+    if (l == 0) nred[it & 1][w] = sq;
     __syncthreads();
   }
   float* out = a.dir_cur + ((int64_t)tree * (1 << a.level) + slot) * D;
   if (tid < D) {
-    const float v = fallback ? su0[tid] : vbuf[tid] * inv_norm;
+    const float v = fallback ? su0[tid] : vbuf[last][tid] * inv_norm;
     out[tid] = v;
     if (a.trace_dir) a.trace_dir[((int64_t)tree * a.trace_slots + slot) * D + tid] = v;
   }
@@ -895,7 +969,7 @@ __global__ __launch_bounds__(256) void pddp_project(LevelArgs a) {
 
 constexpr int kSplitThreads = 512;
 constexpr int kSplitWaves = kSplitThreads / 64;
-constexpr int kSplitCache = 16384;           // keys kept in LDS
+constexpr int kSplitCacheMax = 32768;        // keys kept in LDS at most (128 KiB)
 
 CA_DEV int wave_sum_int(int v) {
 #pragma unroll
@@ -907,7 +981,7 @@ CA_DEV int wave_sum_int(int v) {
 // the first t go left and the rest right, both keeping position order (a
 // stable partition). The token's content hash moves with it.
 __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t skeys[kSplitCache];
+  extern __shared__ __attribute__((aligned(16))) uint32_t skeys[];   // a.split_cache keys
   __shared__ int hist[kSplitWaves][256];
   __shared__ int wtot[2][kSplitWaves];
   __shared__ uint32_t sel[4];
@@ -942,7 +1016,7 @@ __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
   // radix select of the rank-t key over LDS histograms, 8-bit digits from the
   // highest bit in which the node's keys differ (the bits above it are common
   // to every key and would put every member in one bucket)
-  const bool cached = n <= kSplitCache;
+  const bool cached = n <= a.split_cache;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int i = tid; i < n; i += kSplitThreads) {
     const uint32_t k = gkeys[i];
@@ -1296,7 +1370,12 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
   const int trees = (2 * a.BH - a.tree_base + a.tree_step - 1) / a.tree_step;
   dim3 gslots(1u << a.level, trees);
   dim3 gspan((a.N + kSampleSpan - 1) / kSampleSpan, trees);
-  pddp_sample<<<gspan, 256, 0, st>>>(a);
+  // bf16 power-iteration levels whose nodes are small draw the sample inside
+  // the direction kernel; the others take the per-chunk lists
+  LevelArgs la = a;
+  la.sample_inline = (sizeof(T) == 2 && a.split_mode == 0 &&
+                      max_split_node(a.N, a.c, a.level) <= 32 * DirMma<D>::NT) ? 1 : 0;
+  if (!la.sample_inline) pddp_sample<<<gspan, 256, 0, st>>>(la);
   if (a.split_mode == 1) {
     const int64_t nmax = ((int64_t)a.N >> a.level) + 2 * (int64_t)a.c;   // bounds every node
     const size_t lds = (size_t)((nmax + a.c - 1) / a.c + 2) * 4;
@@ -1304,7 +1383,7 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
   } else if constexpr (sizeof(T) == 2) {
     const int64_t nmax = ((int64_t)a.N >> a.level) + 2 * (int64_t)a.c;   // bounds every node
     const size_t lds = (size_t)((nmax + a.c - 1) / a.c + 2) * 4;
-    pddp_dir_mma<D><<<gslots, DirMma<D>::NT, lds, st>>>(a);
+    pddp_dir_mma<D><<<gslots, DirMma<D>::NT, lds, st>>>(la);
   } else {
     const size_t lds = dir_smem<T, D>(a.N, a.c, a.level);
     {   // raise the dynamic-LDS limit when a level needs more (host threads serialised)
@@ -1326,7 +1405,13 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
     dim3 gsmall(((1u << a.level) + 3) / 4, trees);
     pddp_split_small<<<gsmall, 256, 0, st>>>(a);
   } else {
-    pddp_split<<<gslots, kSplitThreads, 0, st>>>(a);
+    // the level's largest node in LDS when it fits (the top levels have few,
+    // large nodes: one workgroup per CU is enough there)
+    LevelArgs ls = a;
+    ls.split_cache = std::min(max_split_node(a.N, a.c, a.level), kSplitCacheMax);
+    const size_t lds = (size_t)ls.split_cache * 4;
+    CA_MAX_LDS_ONCE(&pddp_split, (size_t)kSplitCacheMax * 4);
+    pddp_split<<<gslots, kSplitThreads, lds, st>>>(ls);
   }
 }
 

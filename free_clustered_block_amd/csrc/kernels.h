@@ -41,6 +41,8 @@ struct LevelArgs {
   const float* dir_prev;    // [2 BH][slots/2][D]
   float* dir_cur;           // [2 BH][slots][D]
   int nchunks;              // ceil(N / c)
+  int sample_inline;        // set by launch_level: the direction kernel draws the subsample itself
+  int split_cache;          // set by launch_level: keys a split workgroup keeps in LDS
   int32_t* sample_buf;      // [2 BH][N]   per-chunk sample lists
   int32_t* chunk_cnt;       // [2 BH][nchunks]
   int32_t* zbuf_tok;        // [2 BH][N]   a node's gathered sample tokens
