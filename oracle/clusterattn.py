@@ -727,6 +727,74 @@ def fp8_centroids(kbar, tile: int = 64) -> np.ndarray:
     return fp8_rows(bf16_nearest(kbar), tile)
 
 
+# FP8 (OCP E4M3) value operands of the P.V product (reading, as for Q.K^T:
+# the pages give no scheme). Values are grouped per head dimension over 32
+# consecutive members of a key cluster's member list (32 consecutive tokens in
+# dense attention, 32 consecutive key centroids after rounding to bf16 for
+# compensation), and a group shares a power-of-two scale 2^e: the block scale
+# of the OCP microscaling formats (an E8M0 exponent per 32 elements), with e
+# the smallest integer such that amax <= 448 * 2^e (e >= -127; e = 0 for an
+# all-zero group), codes e4m3(x * 2^-e). The attention weights P multiply
+# these dequantized values; P itself is kept exact here (the kernel rounds P
+# to E4M3 against its running maximum, so the tests bound that rounding
+# instead of reproducing it).
+
+def e8m0_exponent(amax: float) -> int:
+    """Smallest integer e with amax <= 448 * 2^e, at least -127; 0 when
+    amax == 0. With amax = m 2^x (m in [0.5, 1)) and 448 = 0.875 2^9:
+    e = x - 9 if m <= 0.875 else x - 8."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    m, x = math.frexp(amax)
+    return max(-127, x - 9 if m <= 0.875 else x - 8)
+
+
+def quantize_mx_e4m3(X, block: int):
+    """Columns of X in groups of `block` consecutive rows (the last group may
+    be short), one power-of-two scale per (group, column): returns codes
+    (uint8, like X) and exponents (int64 [ceil(rows / block), columns])."""
+    X = np.asarray(X, np.float64)
+    R, D = X.shape
+    ng = (R + block - 1) // block
+    codes = np.empty(X.shape, np.uint8)
+    expo = np.zeros((ng, D), np.int64)
+    for g in range(ng):
+        blk = X[g * block:(g + 1) * block]
+        for d in range(D):
+            e = e8m0_exponent(np.max(np.abs(blk[:, d])) if blk.size else 0.0)
+            expo[g, d] = e
+            codes[g * block:(g + 1) * block, d] = e4m3_encode(blk[:, d] * 2.0 ** -e)
+    return codes, expo
+
+
+def fp8_value_rows(X, block: int) -> np.ndarray:
+    """X after quantize_mx_e4m3 and dequantization (exact in fp64)."""
+    codes, expo = quantize_mx_e4m3(X, block)
+    rows = np.arange(codes.shape[0]) // block
+    return e4m3_decode(codes) * np.exp2(expo[rows].astype(np.float64))
+
+
+def fp8_values(V, perm_k, ck: int, block: int = 32) -> np.ndarray:
+    """V (token order) after quantization per dimension over each block of
+    `block` consecutive members of a key cluster's member list (a short
+    cluster's last block holds only its valid members)."""
+    V = np.asarray(V, np.float64)
+    out = np.empty(V.shape, np.float64)
+    for j, nj in enumerate(leaf_sizes(V.shape[0], ck)):
+        mem = np.asarray(perm_k[j * ck:j * ck + nj])
+        for p in range(0, nj, block):
+            rows = mem[p:p + block]
+            out[rows] = fp8_value_rows(V[rows], len(rows))
+    return out
+
+
+def fp8_value_centroids(vbar, block: int = 32) -> np.ndarray:
+    """Value centroids rounded to bf16, then quantized per dimension over
+    blocks of `block` consecutive clusters."""
+    return fp8_value_rows(bf16_nearest(vbar).astype(np.float64), block)
+
+
 # ---------------------------------------------------------------------------
 # Attention (v1 §1.2 Eq. 1-2; App. A Eq. 21-22)
 # ---------------------------------------------------------------------------
@@ -740,20 +808,24 @@ def _softmax_combine(logits: np.ndarray, values: np.ndarray):
 
 
 def dense_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float | None = None,
-                    qk: str = "exact"):
+                    qk: str = "exact", pv: str = "exact"):
     """o_i = sum_j softmax_j(tau q_i . k_j) v_j and LSE_i = log sum_j exp(.)
     for one head (Eq. 1). Q, K, V: [N, D]. qk="e4m3": the logits use the FP8
-    operands (queries per token, keys per block of 64 consecutive tokens)."""
+    operands (queries per token, keys per block of 64 consecutive tokens).
+    pv="e4m3": the values are the FP8 ones (per dimension over blocks of 32
+    consecutive tokens); the weights stay exact."""
     tau = 1.0 / math.sqrt(np.shape(Q)[1]) if not scale else float(scale)
     if qk == "e4m3":
         Q, K = fp8_rows(Q, 1), fp8_keys(K, np.arange(np.shape(K)[0]), 64)
+    if pv == "e4m3":
+        V = fp8_values(V, np.arange(np.shape(V)[0]), np.shape(V)[0])
     Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
     return _softmax_combine(tau * (Q @ K.T), V)
 
 
 def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
                      scale: float | None = None, clusters=None, c_k: int | None = None,
-                     qk: str = "exact"):
+                     qk: str = "exact", pv: str = "exact"):
     """Block-sparse attention of one head with optional striped
     mean-compensation.
 
@@ -765,7 +837,8 @@ def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
     ``clusters`` restricts the work to those query clusters (the rows of the
     other queries are NaN). Key clusters have size c_k when given, else c.
     qk="e4m3": the logits use the FP8 operands (fp8_rows per query, fp8_keys,
-    fp8_centroids); the values and the centroid values stay exact.
+    fp8_centroids); the values and the centroid values stay exact unless
+    pv="e4m3" (fp8_values, fp8_value_centroids; the weights stay exact).
     """
     N, D = np.shape(Q)
     tau = 1.0 / math.sqrt(D) if not scale else float(scale)
@@ -776,6 +849,8 @@ def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
     vbar, _ = centroids(V, perm_k, ck)
     if qk == "e4m3":
         Q, K, kbar = fp8_rows(Q, 1), fp8_keys(K, perm_k, ck), fp8_centroids(kbar)
+    if pv == "e4m3":
+        V, vbar = fp8_values(V, perm_k, ck), fp8_value_centroids(vbar)
     Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
     O = np.full((N, V.shape[1]), np.nan)
     L = np.full(N, np.nan)
@@ -801,7 +876,7 @@ def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
 
 
 def attend(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool, scale=None, c_k=None,
-           qk: str = "exact"):
+           qk: str = "exact", pv: str = "exact"):
     """sparse_attention over every (batch, head): Q,K,V [B,H,N,D]."""
     B, H, N, D = Q.shape
     O = np.empty((B, H, N, V.shape[-1]))
@@ -810,18 +885,18 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool, scale=None
         for h in range(H):
             O[b, h], L[b, h] = sparse_attention(Q[b, h], K[b, h], V[b, h], perm_q[b, h],
                                                 perm_k[b, h], c, blocks[b][h], compensate, scale,
-                                                c_k=c_k, qk=qk)
+                                                c_k=c_k, qk=qk, pv=pv)
     return O, L
 
 
-def dense(Q, K, V, scale=None, qk: str = "exact"):
+def dense(Q, K, V, scale=None, qk: str = "exact", pv: str = "exact"):
     """dense_attention over every (batch, head)."""
     B, H, N, D = Q.shape
     O = np.empty((B, H, N, V.shape[-1]))
     L = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            O[b, h], L[b, h] = dense_attention(Q[b, h], K[b, h], V[b, h], scale, qk)
+            O[b, h], L[b, h] = dense_attention(Q[b, h], K[b, h], V[b, h], scale, qk, pv)
     return O, L
 
 

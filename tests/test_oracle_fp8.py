@@ -211,9 +211,120 @@ def check_fp8_attention_error_bound():
     assert np.max(np.abs(a[1] - b[1])) > 1e-6
 
 
+# ---------------------------------------------------------------------------
+# FP8 value operands (P.V): power-of-two scales per dimension and 32 members
+# ---------------------------------------------------------------------------
+
+def check_e8m0_bruteforce():
+    """The scale exponent is the smallest e with amax <= 448 * 2^e (searched
+    directly), floored at -127, and 0 for an all-zero group."""
+    r = _rng(6)
+    vals = np.concatenate([np.exp2(r.uniform(-140.0, 120.0, 4000)),
+                           448.0 * np.exp2(np.arange(-130, 100, dtype=np.float64)),
+                           np.nextafter(448.0 * np.exp2(np.arange(-20, 20.0)), np.inf),
+                           np.array([1.0, 3.0, 224.0, 448.0, 449.0, 2.0 ** -149])])
+    for a in vals:
+        e = -200
+        while a > 448.0 * 2.0 ** e:
+            e += 1
+        assert o.e8m0_exponent(a) == max(e, -127), a
+    assert o.e8m0_exponent(0.0) == 0
+
+
+def check_mx_quantize_worked_example():
+    # amax 3: e = -7 (448 * 2^-7 = 3.5 >= 3 > 1.75); 3 * 128 = 384 = 1.5 * 2^8 (0x7C);
+    # 0.3 * 128 = 38.4 in [32, 64), spacing 4 -> 40 (0x62), i.e. 0.3125; -128 (0xF0)
+    X = np.array([[3.0, 0.0], [0.3, 0.0], [-1.0, 0.0]])
+    codes, expo = o.quantize_mx_e4m3(X, 32)
+    assert codes[:, 0].tolist() == [0x7C, 0x62, 0xF0] and codes[:, 1].tolist() == [0, 0, 0]
+    assert expo.tolist() == [[-7, 0]]
+    assert o.fp8_value_rows(X, 32)[:, 0].tolist() == [3.0, 0.3125, -1.0]
+    # two groups of two rows: per column and per group
+    Y = np.array([[1.0, 448.0], [-2.0, 1.0], [0.25, 0.0], [0.0, 900.0]])
+    codes, expo = o.quantize_mx_e4m3(Y, 2)
+    assert expo.tolist() == [[-7, 0], [-10, 2]]
+
+
+def check_mx_quantize_bounds():
+    r = _rng(7)
+    for R, D, g in [(256, 64, 32), (100, 16, 32), (33, 8, 32), (64, 4, 7)]:
+        X = r.standard_normal((R, D)) * np.exp2(r.integers(-10, 10, (1, D)))
+        X[r.random((R, D)) < 0.05] *= 1e-4
+        codes, expo = o.quantize_mx_e4m3(X, g)
+        Xh = o.fp8_value_rows(X, g)
+        for k in range(expo.shape[0]):
+            blk = slice(k * g, (k + 1) * g)
+            amax = np.abs(X[blk]).max(axis=0)
+            sc = np.exp2(expo[k].astype(np.float64))
+            # the group's largest magnitude lands in (224, 448] code units
+            assert np.all((amax / sc > 224.0) & (amax / sc <= 448.0))
+            err = np.abs(Xh[blk] - X[blk])
+            assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(X[blk]), 2.0 ** -10 * sc))
+
+
+def _value_grid(r, n, D, shift):
+    """Rows of e4m3 code values times 2^(shift - 7): every per-dimension group
+    with a fixed shift quantizes exactly under a power-of-two scale."""
+    codes = r.integers(0x18, 0x7F, (n, D))
+    vals = o.e4m3_decode(codes) * r.choice([-1.0, 1.0], (n, D))
+    return vals * 2.0 ** (shift - 7)
+
+
+def check_fp8_values_lossless():
+    """Values that every group (one dimension, 32 consecutive members of a
+    cluster) quantizes exactly give the exact attention. The two 32-member
+    halves of each 64-member block, the dimensions and the clusters lie 2^12
+    apart, so per-64-member, per-token or token-order grouping loses
+    precision."""
+    r = _rng(8)
+    N, D, c = 512, 8, 128
+    nc = N // c
+    perm_q = r.permutation(N); perm_k = r.permutation(N)
+    Q = r.standard_normal((N, D)); K = r.standard_normal((N, D))
+    V = np.empty((N, D))
+    dshift = 12 * (np.arange(D) % 3) - 12
+    for j in range(nc):
+        for b in range(c // 32):
+            mem = perm_k[j * c + 32 * b:j * c + 32 * b + 32]
+            V[mem] = _value_grid(r, 32, D, 0) * np.exp2(dshift + 12.0 * (b % 2) + j)[None, :]
+    blocks = np.array([np.sort(r.choice(nc, 2, replace=False)) for _ in range(nc)])
+    assert np.array_equal(o.fp8_values(V, perm_k, c), V)
+    a = o.sparse_attention(Q, K, V, perm_q, perm_k, c, blocks, False, pv="e4m3")
+    b = o.sparse_attention(Q, K, V, perm_q, perm_k, c, blocks, False)
+    assert np.allclose(a[0], b[0], rtol=1e-13, atol=0) and np.array_equal(a[1], b[1])
+    # dense: groups of 32 consecutive tokens
+    Vd = np.concatenate([_value_grid(r, 32, D, 0) * np.exp2(dshift + 12.0 * (k % 2))[None, :]
+                         for k in range(N // 32)])
+    a = o.dense_attention(Q, K, Vd, pv="e4m3")
+    b = o.dense_attention(Q, K, Vd)
+    assert np.allclose(a[0], b[0], rtol=1e-13, atol=0)
+
+
+def check_fp8_value_centroid_double_rounding():
+    """Worked example: the excluded cluster's value centroid x = (1.0625 +
+    2^-12) / 128 rounds to bf16 (1.0625 / 128); its group (32 centroids, the
+    others 0) has amax 1.0625 / 128, e = -15 (448 * 2^-15 = 0.0137 >= x), and
+    x * 2^15 = 272 is the midpoint of the codes 256 and 288, so it rounds to
+    the even 256: x_hat = 2^-7. With the selected cluster's values 0 and
+    weights 64 : 64 e^0, the output is x_hat / 2 = 2^-8 (without the bf16
+    rounding, 272.0625 would round up to 288)."""
+    N, D, c = 128, 1, 64
+    x = (1.0625 + 2.0 ** -12) / 128
+    Q = np.zeros((N, D)); K = np.zeros((N, D))
+    V = np.zeros((N, D)); V[64:, 0] = x
+    perm = np.arange(N)
+    blocks = np.array([[0], [0]])
+    O, _ = o.sparse_attention(Q, K, V, perm, perm, c, blocks, True, pv="e4m3")
+    assert np.allclose(O[:, 0], 2.0 ** -8, rtol=0, atol=1e-15)
+    Oe, _ = o.sparse_attention(Q, K, V, perm, perm, c, blocks, True)
+    assert abs(Oe[0, 0] - x / 2) < 1e-15 and abs(Oe[0, 0] - O[0, 0]) > 1e-7
+
+
 CHECKS = [check_e4m3_decode_library, check_e4m3_encode_library, check_bf16_library,
           check_quantize_worked_example, check_quantize_bounds, check_fp8_attention_lossless,
-          check_fp8_centroid_double_rounding, check_fp8_attention_error_bound]
+          check_fp8_centroid_double_rounding, check_fp8_attention_error_bound,
+          check_e8m0_bruteforce, check_mx_quantize_worked_example, check_mx_quantize_bounds,
+          check_fp8_values_lossless, check_fp8_value_centroid_double_rounding]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[f.__name__ for f in CHECKS])
@@ -226,7 +337,8 @@ def test_fp8_pin(check):
 # ---------------------------------------------------------------------------
 
 _orig = {n: getattr(o, n) for n in ("e4m3_encode", "fp8_keys", "fp8_rows", "fp8_centroids",
-                                    "quantize_e4m3", "bf16_nearest")}
+                                    "quantize_e4m3", "bf16_nearest", "e8m0_exponent",
+                                    "fp8_values", "fp8_value_rows", "fp8_value_centroids")}
 
 
 def _encode_truncating(x):
@@ -265,7 +377,45 @@ def _quantize_scale_from_inverse(X, group):
                            ).astype(np.float32)
 
 
+def _e8m0_one_too_low(amax):
+    e = _orig["e8m0_exponent"](amax)
+    return e - 1 if amax > 0 else e
+
+
+def _values_per_64(V, perm_k, ck, block=32):
+    return _orig["fp8_values"](V, perm_k, ck, 64)
+
+
+def _values_token_order(V, perm_k, ck, block=32):
+    return _orig["fp8_values"](V, np.arange(np.shape(V)[0]), ck, block)
+
+
+def _value_rows_not_power_of_two(X, block):
+    X = np.asarray(X, np.float64)
+    out = np.empty_like(X)
+    for g in range(0, X.shape[0], block):
+        blk = X[g:g + block]
+        amax = np.abs(blk).max(axis=0)
+        sc = np.where(amax > 0, amax / 448.0, 1.0)
+        out[g:g + block] = o.e4m3_decode(o.e4m3_encode(blk / sc)) * sc
+    return out
+
+
+def _value_rows_per_token(X, block):
+    return _orig["fp8_value_rows"](np.asarray(X).T, np.shape(X)[1]).T
+
+
+def _value_centroids_without_bf16(vbar, block=32):
+    return _orig["fp8_value_rows"](np.asarray(vbar, np.float64), block)
+
+
 PLANTED = [
+    ("e8m0_exponent", _e8m0_one_too_low, check_e8m0_bruteforce),
+    ("fp8_values", _values_per_64, check_fp8_values_lossless),
+    ("fp8_values", _values_token_order, check_fp8_values_lossless),
+    ("fp8_value_rows", _value_rows_not_power_of_two, check_fp8_values_lossless),
+    ("fp8_value_rows", _value_rows_per_token, check_fp8_values_lossless),
+    ("fp8_value_centroids", _value_centroids_without_bf16, check_fp8_value_centroid_double_rounding),
     ("e4m3_encode", _encode_truncating, check_e4m3_encode_library),
     ("e4m3_encode", _encode_no_subnormals, check_e4m3_encode_library),
     ("fp8_keys", _keys_token_order, check_fp8_attention_lossless),
