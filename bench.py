@@ -114,6 +114,9 @@ def parse():
     ap.add_argument("--fp8", action="store_true",
                     help="Q.K^T on FP8 (E4M3) operands in the attention and in the dense "
                          "baseline (dtype CA_BF16_FP8); P.V stays bf16")
+    ap.add_argument("--fp8-pv", action="store_true",
+                    help="Q.K^T and P.V on FP8 (E4M3) operands (dtype CA_BF16_FP8_PV), in the "
+                         "attention and in the dense baseline")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="shared key/value heads (grouped- or multi-query attention): K and V "
                          "keep the workload's first KV heads; every query head clusters its "
@@ -183,7 +186,7 @@ def oracle_small_case(synth):
 
 
 def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power", assign="topk", recall=0.9,
-                 min_count=16, qk="exact"):
+                 min_count=16, qk="exact", pv="exact"):
     """The oracle, untuned, on the first `heads` heads of the same input."""
     import oracle.clusterattn as o
     info = host_info()
@@ -193,7 +196,7 @@ def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power", assign="topk", rec
     t0 = time.perf_counter()
     if assign == "topk":
         o.forward(Q[:, :heads], K[:, :heads], V[:, :heads], w.c, topk, w.compensate, opts, w.dtype,
-                  qk=qk)
+                  qk=qk, pv=pv)
     else:
         Qs, Ks, Vs = Q[:, :heads], K[:, :heads], V[:, :heads]
         pq, pk = o.cluster(Qs, Ks, w.c, opts, w.dtype)
@@ -204,7 +207,7 @@ def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power", assign="topk", rec
                 cq, _ = o.centroids(Qs[b, h], pq[b, h], w.c)
                 ck, cnt = o.centroids(Ks[b, h], pk[b, h], w.c)
                 sel[b][h] = o.route_adaptive(cq, ck, cnt, tau, recall, min_count)
-        o.attend(Qs, Ks, Vs, pq, pk, w.c, sel, w.compensate, qk=qk)
+        o.attend(Qs, Ks, Vs, pq, pk, w.c, sel, w.compensate, qk=qk, pv=pv)
     t = time.perf_counter() - t0
     flops = 4.0 * w.D * w.N * w.N * heads * w.B
     return {
@@ -214,7 +217,8 @@ def cpu_baseline(w, Q, K, V, topk, heads, split_mode="power", assign="topk", rec
         "kind": "oracle",
         "sample": f"{heads} of {w.H} heads of the same workload, full N={w.N}; "
                   f"{t:.2f} s wall for cluster+route+attend in fp64 NumPy"
-                  f"{' (FP8 Q.K^T operands)' if qk == 'e4m3' else ''} "
+                  f"{' (FP8 Q.K^T operands)' if qk == 'e4m3' and pv != 'e4m3' else ''}"
+                  f"{' (FP8 Q.K^T and P.V operands)' if pv == 'e4m3' else ''} "
                   f"(BLAS threads={cores}; PDDP and top-k loops single-threaded Python)",
         "seconds": t,
         **info,
@@ -387,7 +391,7 @@ def run_workload(args, wname, torch, synth, ca, dev, steps, warmup, full=True):
     cq = (args.cq or c) if full else c       # query cluster size
     split_mode = args.split_mode if full else "power"
     adaptive = full and args.assign == "adaptive"
-    fp8 = full and args.fp8
+    fp8 = ("qkpv" if args.fp8_pv else args.fp8) if full else False
     kv_share = full and args.kv_share
     op_c = ca.OP_CLUSTER_DIAG if split_mode == "diag" else ca.OP_CLUSTER
     ws_c = torch.empty(ca.workspace_size(op_c, B, H, N, D, min(c, cq)), dtype=torch.uint8,
@@ -521,9 +525,9 @@ def run_workload(args, wname, torch, synth, ca, dev, steps, warmup, full=True):
     clu_ms = float(st_cluster + st_route)
     clu_gbs = clu_bytes / (clu_ms * 1e-3) / 1e9
 
-    traffic = (recorded_traffic(w.name, topk, fp8) if B * H == w.B * w.H and not adaptive
-               and split_mode == "power" and cq == c and kvh == w.H else None)
-    peak = PEAK_FP8QK_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    traffic = (recorded_traffic(w.name, topk, bool(fp8)) if B * H == w.B * w.H and not adaptive
+               and split_mode == "power" and cq == c and kvh == w.H and fp8 != "qkpv" else None)
+    peak = (PEAK_FP8_TFLOPS if fp8 == "qkpv" else PEAK_FP8QK_TFLOPS if fp8 else PEAK_BF16_TFLOPS)
     dense_eq = 4.0 * D * N * N * B * H
     head_ms = float(np.median(cold_ms))
     result = {
@@ -537,7 +541,7 @@ def run_workload(args, wname, torch, synth, ca, dev, steps, warmup, full=True):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8e4m3 (Q.K^T) + bf16 (P.V)" if fp8
+        "dtype": ("fp8e4m3 (Q.K^T and P.V)" if fp8 == "qkpv" else "fp8e4m3 (Q.K^T) + bf16 (P.V)" if fp8
                   else "bf16" if w.dtype == "bf16" else "f32"),
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "N": N, "head_dim": D,
@@ -545,6 +549,9 @@ def run_workload(args, wname, torch, synth, ca, dev, steps, warmup, full=True):
                    "split_mode": split_mode, "assign": "adaptive" if adaptive else "topk",
                    **({"qk_operands": "fp8 e4m3, per-token query / per-64-key scales"}
                       if fp8 else {}),
+                   **({"pv_operands": "fp8 e4m3, values with a power-of-two scale per "
+                                      "dimension and 32 keys, weights unscaled"}
+                      if fp8 == "qkpv" else {}),
                    **({"query_cluster_size": cq} if cq != c else {}),
                    **({"kv_heads": kvh, "kv_share": bool(kv_share)} if kvh != w.H else {}),
                    **({"recall": args.recall, "min_count": args.min_count,
@@ -571,7 +578,7 @@ def run_workload(args, wname, torch, synth, ca, dev, steps, warmup, full=True):
             "achieved": round(achieved, 2),
             "peak": round(peak, 1),
             **({"peak_note": "half the FLOPs (Q.K^T) at the fp8 5.0 PFLOP/s peak, half "
-                             "(P.V) at the bf16 2.5 PFLOP/s peak"} if fp8 else {}),
+                             "(P.V) at the bf16 2.5 PFLOP/s peak"} if fp8 is True else {}),
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
@@ -655,7 +662,8 @@ def run_workload(args, wname, torch, synth, ca, dev, steps, warmup, full=True):
             Vn = np.repeat(Vn, w.H // kvh, axis=1)
         result["cpu_baseline"] = cpu_baseline(w, Qn, Kn, Vn, topk, heads, split_mode,
                                               "adaptive" if adaptive else "topk", args.recall,
-                                              args.min_count, "e4m3" if fp8 else "exact")
+                                              args.min_count, "e4m3" if fp8 else "exact",
+                                              "e4m3" if fp8 == "qkpv" else "exact")
         result["cpu_baseline"]["small_fp32_case"] = oracle_small_case(synth)
     return result
 

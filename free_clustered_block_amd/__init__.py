@@ -28,7 +28,7 @@ EXPORTS = ["ca_tree_levels", "ca_workspace_size", "ca_cluster", "ca_route", "ca_
            "ca_attend", "ca_attend_var", "ca_attend_ex", "ca_dense", "ca_quantize_e4m3",
            "ca_profile_events", "ca_peak_probe", "ca_status_string", "ca_last_error"]
 
-CA_BF16, CA_F32, CA_BF16_FP8 = 0, 1, 2
+CA_BF16, CA_F32, CA_BF16_FP8, CA_BF16_FP8_PV = 0, 1, 2, 3
 OP_CLUSTER, OP_ROUTE, OP_ATTEND, OP_DENSE, OP_CLUSTER_DIAG = 0, 1, 2, 3, 4
 
 _lib = None
@@ -333,23 +333,30 @@ def route_adaptive(cent_q, cent_k, counts_k, recall: float, *, min_count: int = 
     return (blocks, nsel, scores) if return_scores else (blocks, nsel)
 
 
-def _attn_dtype(Q, fp8: bool) -> int:
+def _attn_dtype(Q, fp8) -> int:
+    """fp8: False, True / "qk" (FP8 Q.K^T, CA_BF16_FP8) or "qkpv" (FP8 Q.K^T
+    and P.V, CA_BF16_FP8_PV)."""
     dt = _dtype_code(Q)
     if fp8:
         if dt != CA_BF16:
             raise TypeError("fp8 attention takes bfloat16 inputs")
-        return CA_BF16_FP8
+        if fp8 == "qkpv":
+            return CA_BF16_FP8_PV
+        if fp8 is True or fp8 == "qk":
+            return CA_BF16_FP8
+        raise ValueError("fp8 must be False, True, 'qk' or 'qkpv'")
     return dt
 
 
 def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
            scale: float = 0.0, return_lse: bool = False, nsel=None, c_k: int = 0,
-           fp8: bool = False, workspace=None):
+           fp8=False, workspace=None):
     """ca_attend: block-sparse attention with optional mean-compensation;
     with `nsel` (selected count per row of `blocks`), ca_attend_var; with key
     clusters of another size c_k than the query clusters' c, or K and V with
     fewer heads than Q (grouped- or multi-query attention), ca_attend_ex;
-    fp8=True: the Q.K^T product on FP8 (E4M3) operands (dtype CA_BF16_FP8)."""
+    fp8=True (or "qk"): the Q.K^T product on FP8 (E4M3) operands (dtype
+    CA_BF16_FP8); fp8="qkpv": P.V on FP8 operands too (CA_BF16_FP8_PV)."""
     torch = _torch()
     _bhnd(Q, K, V)
     dt = _attn_dtype(Q, fp8)
@@ -381,9 +388,10 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
     return (O, lse) if return_lse else O
 
 
-def dense(Q, K, V, *, scale: float = 0.0, return_lse: bool = False, fp8: bool = False,
+def dense(Q, K, V, *, scale: float = 0.0, return_lse: bool = False, fp8=False,
           workspace=None):
-    """ca_dense: dense attention baseline (fp8=True: FP8 Q.K^T operands)."""
+    """ca_dense: dense attention baseline (fp8=True / "qk": FP8 Q.K^T operands;
+    "qkpv": FP8 P.V operands too)."""
     torch = _torch()
     _bhnd(Q, K, V)
     if _kv_heads(Q, K, V):

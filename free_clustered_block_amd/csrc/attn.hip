@@ -24,6 +24,13 @@
 // = K Q^T then runs on v_mfma_scale_f32_32x32x64_f8f6f4 and the tile's logit
 // scale becomes scale * s_q * s_k. P.V and everything after it are as in the
 // bf16 path.
+// FP8 Q.K^T and P.V variant: in addition, the values enter P.V as e4m3
+// codes with a power-of-two scale per head dimension and 32 keys (the OCP
+// microscaling block scale, applied by v_mfma_scale_f32_32x32x64_f8f6f4 to
+// its A operand), written by permute_kv (quant_vcentroids for the value
+// centroids), and the attention weights are rounded to e4m3 (they are at
+// most 2^8 by the lazy running maximum, inside the format's range) before
+// the product; the softmax denominator sums the fp32 weights.
 // fp32 path: the same computation on VALU, one thread per query.
 #include <type_traits>
 
@@ -53,11 +60,43 @@ CA_HD int vslot(int k) {
   return (k & ~15) | (qs << 2) | (k & 3);
 }
 
+// FP8 value sub-tile (64 keys), in HBM and in LDS: D rows of 64 code bytes,
+// then the scale bytes [2][32][4] (key block kb of 32 keys, dimension
+// 32 nb + r at [kb][r][nb], byte = exponent + 127). Byte 32 h + 16 kb + j
+// of a row holds key 32 kb + 16 h + j: the matrix core takes the 32 bytes
+// of lane half h as its operand and scales bytes 16 kb .. 16 kb + 15 of both
+// halves with the scale that lane half kb supplies, so each scale block is
+// 32 consecutive keys; attn_fwd holds the weights in the same order.
+template <int D>
+constexpr int vt8_bytes() { return D * 64 + 256; }
+
+// Codes and scale of dimension dd, key half hb of a 64-key block whose bf16
+// values val(k) (k = key within the block) are given; dst is the sub-tile.
+template <int D, typename F>
+CA_DEV void write_vt8(uint8_t* dst, int dd, int hb, F val) {
+  uint32_t am = 0;
+#pragma unroll 8
+  for (int k = 0; k < 32; ++k) am = max(am, (uint32_t)(val(32 * hb + k) & 0x7FFFu));
+  const int ex = e8m0_exponent(bf16_to_f32((uint16_t)am));
+  const float sc = ldexpf(1.0f, -ex);   // exact: a power of two
+  uint32_t wv[8];   // keys 32 hb + 4 i + 0..3
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k0 = 32 * hb + 4 * i;
+    wv[i] = e4m3_pack4_raw(bf16_to_f32(val(k0)) * sc, bf16_to_f32(val(k0 + 1)) * sc,
+                           bf16_to_f32(val(k0 + 2)) * sc, bf16_to_f32(val(k0 + 3)) * sc);
+  }
+  // keys 32 hb + 16 h + j at byte 32 h + 16 hb + j
+  *reinterpret_cast<u32x4_t*>(dst + dd * 64 + 16 * hb) = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
+  *reinterpret_cast<u32x4_t*>(dst + dd * 64 + 32 + 16 * hb) = u32x4_t{wv[4], wv[5], wv[6], wv[7]};
+  dst[D * 64 + (hb * 32 + (dd & 31)) * 4 + (dd >> 5)] = (uint8_t)(ex + 127);
+}
+
 // ----------------------------------------------------------------------------
 // Cluster-major K / transposed V tiles and centroids (bf16 path)
 // ----------------------------------------------------------------------------
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool FP8PV>
 __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
   constexpr int RB = 64;                    // rows per LDS block (= one key sub-tile)
   __shared__ __attribute__((aligned(16))) uint16_t skr[RB][D + 8];
@@ -143,9 +182,15 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
       ksum += bf16_to_f32(skr[r][d]);
       vsum += bf16_to_f32(sv[r][d]);
     }
+    if constexpr (FP8PV) {
+      // FP8 values: thread (dim, key half) writes its 32 codes and scale
+      uint8_t* vt8 = a.vt8 + (((int64_t)bh * nc + j) * (c / RB) + b) * vt8_bytes<D>();
+      for (int e = tid; e < 2 * D; e += 256)
+        write_vt8<D>(vt8, e % D, e / D, [&](int k) { return sv[k][e % D]; });
+    }
     // V written transposed [D][64] per block: each thread writes 8
     // consecutive storage slots of one dim
-    for (int e = tid; e < D * (RB / 8); e += 256) {
+    for (int e = tid; e < (FP8PV ? 0 : D * (RB / 8)); e += 256) {
       const int dd = e / (RB / 8), s8 = e % (RB / 8);
       uint16_t vals[8];
 #pragma unroll
@@ -206,6 +251,20 @@ __global__ __launch_bounds__(256) void quant_centroids(AttnArgs a) {
   if (tid == 0) a.kbscale[(int64_t)bh * (ncp / RB) + blk] = e4m3_scale(amax);
 }
 
+// FP8 P.V: value centroids (bf16, written by permute_kv as transposed
+// sub-tiles) as FP8 value sub-tiles; one workgroup per 64 centroids.
+template <int D>
+__global__ __launch_bounds__(256) void quant_vcentroids(AttnArgs a) {
+  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int ncp = attn_ncp(a.nc);
+  const uint16_t* src = a.vbar_t + ((int64_t)bh * (ncp / 64) + blk) * D * 64;
+  uint8_t* dst = a.vbar8 + ((int64_t)bh * (ncp / 64) + blk) * vt8_bytes<D>();
+  for (int e = tid; e < 2 * D; e += 256) {
+    const int dd = e % D;
+    write_vt8<D>(dst, dd, e / D, [&](int k) { return src[dd * 64 + vslot(k)]; });
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Attention (bf16 MFMA)
 // ----------------------------------------------------------------------------
@@ -217,19 +276,21 @@ __global__ __launch_bounds__(256) void quant_centroids(AttnArgs a) {
 // plus a compile-time offset.
 // With FP8 keys a K row is D bytes (+16 of padding, which again puts the 16
 // rows an LDS cycle serves on distinct banks).
-template <int D, bool FP8 = false>
+// With FP8 values a V^T row is 64 code bytes (+16 of padding: conflict-free
+// 32-byte operand reads) and the sub-tile's 256 scale bytes follow the rows.
+template <int D, bool FP8 = false, bool FP8PV = false>
 struct AttnTile {
   static constexpr int KT = 64;                           // keys per sub-tile
   static constexpr int KE = FP8 ? 1 : 2;                  // bytes per key element
   static constexpr int KP = D * KE + 16;                  // K row pitch (bytes)
-  static constexpr int VP = KT * 2 + 16;                  // V^T row pitch (bytes)
+  static constexpr int VP = FP8PV ? KT + 16 : KT * 2 + 16;   // V^T row pitch (bytes)
   static constexpr int K_BYTES = KT * KP;
-  static constexpr int V_BYTES = D * VP;
+  static constexpr int V_BYTES = D * VP + (FP8PV ? 256 : 0);
   static constexpr int BYTES = K_BYTES + V_BYTES;         // one buffer
   static constexpr int K_CHUNKS = D * KE / 16;            // 16-byte chunks per K row
-  static constexpr int V_CHUNKS = KT / 8;                 // 16-byte chunks per V^T row
+  static constexpr int V_CHUNKS = FP8PV ? KT / 16 : KT / 8;   // 16-byte chunks per V^T row
   static constexpr int K_LOADS = KT * K_CHUNKS;           // 16-byte loads per sub-tile
-  static constexpr int V_LOADS = D * V_CHUNKS;
+  static constexpr int V_LOADS = D * V_CHUNKS + (FP8PV ? 16 : 0);
 };
 
 // Workgroup order: consecutive logical workgroups (adjacent query clusters of
@@ -246,9 +307,10 @@ CA_DEV int xcd_logical(int b, int G) {
 // each taking one 32-key half of every sub-tile with its own running maximum,
 // sum and accumulators, merged through LDS at the end. This keeps four waves
 // (and the per-thread share of the tile loads) of a 128-query workgroup.
-template <int D, int CQ, int CK, bool DENSE, bool FP8, int KSPL>
+template <int D, int CQ, int CK, bool DENSE, bool FP8, int KSPL, bool FP8PV>
 __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd(AttnArgs a) {
-  using TL = AttnTile<D, FP8>;
+  using TL = AttnTile<D, FP8, FP8PV>;
+  static_assert(!FP8PV || (FP8 && KSPL == 1), "FP8 values need FP8 keys and whole 64-key sub-tiles per wave");
   constexpr int NT = 2 * CQ * KSPL;    // threads: CQ/32 query groups x KSPL key halves
   constexpr int NKB = 2 / KSPL;        // 32-key blocks of a sub-tile per wave
   constexpr int KS = D / 16;           // k-steps over the head dim
@@ -342,9 +404,8 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
   };
   // stage: 16-byte global loads into registers, then into an LDS buffer
   // (with FP8 and D = 64 a K sub-tile is 256 loads: fewer than 512 threads)
-  constexpr int KLPT = (TL::K_LOADS + NT - 1) / NT, VLPT = TL::V_LOADS / NT;
-  constexpr bool K_ALL = TL::K_LOADS % NT == 0;
-  static_assert(TL::V_LOADS % NT == 0, "V sub-tile loads must divide evenly");
+  constexpr int KLPT = (TL::K_LOADS + NT - 1) / NT, VLPT = (TL::V_LOADS + NT - 1) / NT;
+  constexpr bool K_ALL = TL::K_LOADS % NT == 0, V_ALL = TL::V_LOADS % NT == 0;
   u32x4_t kst[KLPT], vst[VLPT];
   float ksc_cur = 1.0f, ksc_nxt = 1.0f;   // FP8: key scale of the current / next sub-tile
   // Every sub-tile is contiguous in HBM (K rows [64][D], V^T rows [D][64],
@@ -364,7 +425,10 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
       } else {
         ks = reinterpret_cast<const u32x4_t*>(a.kc + row * D);
       }
-      vs = reinterpret_cast<const u32x4_t*>(a.vt + (((int64_t)bh * nc + j) * SUB + part) * (int64_t)D * TL::KT);
+      if constexpr (FP8PV)
+        vs = reinterpret_cast<const u32x4_t*>(a.vt8 + (((int64_t)bh * nc + j) * SUB + part) * vt8_bytes<D>());
+      else
+        vs = reinterpret_cast<const u32x4_t*>(a.vt + (((int64_t)bh * nc + j) * SUB + part) * (int64_t)D * TL::KT);
     } else {
       const int ct = t - Tm;
       if constexpr (FP8) {
@@ -373,13 +437,17 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
       } else {
         ks = reinterpret_cast<const u32x4_t*>(a.kbar_hi + ((int64_t)bh * ncp + ct * TL::KT) * D);
       }
-      vs = reinterpret_cast<const u32x4_t*>(a.vbar_t + ((int64_t)bh * (ncp / TL::KT) + ct) * D * TL::KT);
+      if constexpr (FP8PV)
+        vs = reinterpret_cast<const u32x4_t*>(a.vbar8 + ((int64_t)bh * (ncp / TL::KT) + ct) * vt8_bytes<D>());
+      else
+        vs = reinterpret_cast<const u32x4_t*>(a.vbar_t + ((int64_t)bh * (ncp / TL::KT) + ct) * D * TL::KT);
     }
 #pragma unroll
     for (int i = 0; i < KLPT; ++i)
       if (K_ALL || i * NT + tid < TL::K_LOADS) kst[i] = ks[i * NT + tid];
 #pragma unroll
-    for (int i = 0; i < VLPT; ++i) vst[i] = vs[i * NT + tid];
+    for (int i = 0; i < VLPT; ++i)
+      if (V_ALL || i * NT + tid < TL::V_LOADS) vst[i] = vs[i * NT + tid];
   };
   auto store = [&](int buf) {
     unsigned char* base = smem + buf * TL::BYTES;
@@ -392,14 +460,19 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int i = 0; i < VLPT; ++i) {
       const int e = i * NT + tid;
-      *reinterpret_cast<u32x4_t*>(base + TL::K_BYTES + (e / TL::V_CHUNKS) * TL::VP +
-                                  (e % TL::V_CHUNKS) * 16) = vst[i];
+      if (V_ALL || e < TL::V_LOADS) {
+        // FP8 values: the chunks past the D rows are the scale bytes
+        const int off = (FP8PV && e >= D * TL::V_CHUNKS)
+                            ? D * TL::VP + (e - D * TL::V_CHUNKS) * 16
+                            : (e / TL::V_CHUNKS) * TL::VP + (e % TL::V_CHUNKS) * 16;
+        *reinterpret_cast<u32x4_t*>(base + TL::K_BYTES + off) = vst[i];
+      }
     }
   };
   // per-lane LDS read bases: K row r, chunk h (FP8: 32-byte chunk h); V^T
   // row r, chunk h
   const int kread = r * TL::KP + h * (FP8 ? 32 : 16);
-  const int vread = TL::K_BYTES + r * TL::VP + h * 16;
+  const int vread = TL::K_BYTES + r * TL::VP + h * (FP8PV ? 32 : 16);
   const float* logn = a.logn + (int64_t)bh * ncp;
 
   if (T > 0) {
@@ -525,6 +598,48 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
       float tv[16 * NKB];
 #pragma unroll
       for (int i = 0; i < 16 * NKB; ++i) tv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 4][i & 15], scl, nm));
+      if constexpr (FP8PV) {
+        // P as e4m3 codes (P <= 2^8: inside the format's range, no scale).
+        // Word q of key block kb holds keys 32 kb + 8 q + 4 h + 0..3 in lane
+        // half h; swapping words q = 0, 1 of the upper half with words 2, 3
+        // of the lower half gives lane half h keys 32 kb + 16 h + 0..15 of
+        // both blocks, in the byte order of the FP8 value rows.
+        uint32_t wk[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            wk[kb][q] = e4m3_pack4_raw(tv[16 * kb + 4 * q], tv[16 * kb + 4 * q + 1],
+                                       tv[16 * kb + 4 * q + 2], tv[16 * kb + 4 * q + 3]);
+        i32x8_t pb;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(wk[kb][q], wk[kb][q + 2], false, false);
+            pb[4 * kb + 2 * q] = (int)sw[0];
+            pb[4 * kb + 2 * q + 1] = (int)sw[1];
+          }
+        float ps4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) ps4[i & 3] += tv[i];
+        lsum += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);   // this lane's keys, fp32 weights
+        // O^T block nb += V^T rows 32 nb + r (bytes 32 h .. 32 h + 31) x P^T;
+        // this lane half supplies the scales of key block h of rows 32 nb + r
+        // (byte nb of one word)
+        const int sword = *reinterpret_cast<const int*>(buf + TL::K_BYTES + D * TL::VP + (h * 32 + r) * 4);
+        auto vrow = [&](int nb) {
+          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(buf + vread + nb * 32 * TL::VP);
+          const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(buf + vread + nb * 32 * TL::VP + 16);
+          return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        };
+        acc[0] = mfma32_fp8_scale_a<0>(vrow(0), pb, acc[0], sword);
+        acc[1] = mfma32_fp8_scale_a<1>(vrow(1), pb, acc[1], sword);
+        if constexpr (NB > 2) {
+          acc[2] = mfma32_fp8_scale_a<2>(vrow(2), pb, acc[2], sword);
+          acc[3] = mfma32_fp8_scale_a<3>(vrow(3), pb, acc[3], sword);
+        }
+      } else {
       // P enters the P.V product as bf16; the denominator sums the same
       // rounded values, so the output stays a convex combination of values
       bf16x8_t pk[2 * NKB];
@@ -557,6 +672,7 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      }   // bf16 P.V
     }
     if (t + 1 < T) store((t + 1) & 1);
     ksc_cur = ksc_nxt;
@@ -621,9 +737,9 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
   if (a.lse && h == 0) a.lse[(int64_t)bh * N + qtok] = (m + log2f(lsum)) * kLn2;
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool FP8PV>
 constexpr size_t attn_smem() {
-  return 2 * (size_t)AttnTile<D, FP8>::BYTES + 8192 / 8 + 64;   // two buffers, selection bits
+  return 2 * (size_t)AttnTile<D, FP8, FP8PV>::BYTES + 8192 / 8 + 64;   // two buffers, selection bits
 }
 
 // ----------------------------------------------------------------------------
@@ -744,44 +860,55 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
   if (a.lse) a.lse[(int64_t)bh * N + qtok] = m + logf(lsum);
 }
 
-template <int D, int CQ, int CK, bool DENSE, bool FP8>
+template <int D, int CQ, int CK, bool DENSE, bool FP8, bool FP8PV>
 void launch_mfma(const AttnArgs& a, hipStream_t st) {
   constexpr int KSPL = CQ == 64 ? 2 : 1;
-  const size_t sm = attn_smem<D, FP8>();
-  CA_MAX_LDS_ONCE((&attn_fwd<D, CQ, CK, DENSE, FP8, KSPL>), sm);
+  const size_t sm = attn_smem<D, FP8, FP8PV>();
+  CA_MAX_LDS_ONCE((&attn_fwd<D, CQ, CK, DENSE, FP8, KSPL, FP8PV>), sm);
   dim3 g(a.nqc, a.BH);
   if (a.ev_start) (void)hipEventRecord(a.ev_start, st);
-  attn_fwd<D, CQ, CK, DENSE, FP8, KSPL><<<g, 2 * CQ * KSPL, sm, st>>>(a);
+  attn_fwd<D, CQ, CK, DENSE, FP8, KSPL, FP8PV><<<g, 2 * CQ * KSPL, sm, st>>>(a);
   if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool FP8PV>
 void launch_tiles(const AttnArgs& a, bool dense, hipStream_t st) {
   dim3 gp(attn_ncp(a.nc), a.BH);
-  permute_kv<D, FP8><<<gp, 256, 0, st>>>(a);
+  permute_kv<D, FP8, FP8PV><<<gp, 256, 0, st>>>(a);
   if (FP8 && !dense && a.compensate) {
     dim3 gq(attn_ncp(a.nc) / 64, a.BH);
     quant_centroids<D><<<gq, 256, 0, st>>>(a);
+    if (FP8PV) quant_vcentroids<D><<<gq, 256, 0, st>>>(a);
   }
   if (dense) {
-    launch_mfma<D, 128, 128, true, FP8>(a, st);
+    launch_mfma<D, 128, 128, true, FP8, FP8PV>(a, st);
     return;
   }
-  // (query, key) cluster sizes: equal, or the key clusters larger
-  switch (a.cq * 1000 + a.c) {
-    case 64064: launch_mfma<D, 64, 64, false, FP8>(a, st); break;
-    case 64128: launch_mfma<D, 64, 128, false, FP8>(a, st); break;
-    case 64256: launch_mfma<D, 64, 256, false, FP8>(a, st); break;
-    case 128128: launch_mfma<D, 128, 128, false, FP8>(a, st); break;
-    case 128256: launch_mfma<D, 128, 256, false, FP8>(a, st); break;
-    default: launch_mfma<D, 256, 256, false, FP8>(a, st); break;
+  // (query, key) cluster sizes: equal, or the key clusters larger (FP8
+  // values: query clusters of at least 128, checked on the host)
+  if constexpr (FP8PV) {
+    switch (a.cq * 1000 + a.c) {
+      case 128128: launch_mfma<D, 128, 128, false, FP8, FP8PV>(a, st); break;
+      case 128256: launch_mfma<D, 128, 256, false, FP8, FP8PV>(a, st); break;
+      default: launch_mfma<D, 256, 256, false, FP8, FP8PV>(a, st); break;
+    }
+  } else {
+    switch (a.cq * 1000 + a.c) {
+      case 64064: launch_mfma<D, 64, 64, false, FP8, FP8PV>(a, st); break;
+      case 64128: launch_mfma<D, 64, 128, false, FP8, FP8PV>(a, st); break;
+      case 64256: launch_mfma<D, 64, 256, false, FP8, FP8PV>(a, st); break;
+      case 128128: launch_mfma<D, 128, 128, false, FP8, FP8PV>(a, st); break;
+      case 128256: launch_mfma<D, 128, 256, false, FP8, FP8PV>(a, st); break;
+      default: launch_mfma<D, 256, 256, false, FP8, FP8PV>(a, st); break;
+    }
   }
 }
 
 template <int D>
 void launch_bf16(const AttnArgs& a, bool dense, hipStream_t st) {
-  if (a.dtype == 2) launch_tiles<D, true>(a, dense, st);
-  else launch_tiles<D, false>(a, dense, st);
+  if (a.dtype == 3) launch_tiles<D, true, true>(a, dense, st);
+  else if (a.dtype == 2) launch_tiles<D, true, false>(a, dense, st);
+  else launch_tiles<D, false, false>(a, dense, st);
 }
 
 template <int D>

@@ -101,7 +101,14 @@ void plan_attend(Carver& cv, AttnArgs& a, bool with_tiles) {
   a.logn = cv.take<float>(BH * ncp);
   a.kbar32 = cv.take<float>(BH * ncp * D);
   a.vbar32 = cv.take<float>(BH * ncp * D);
-  if (a.dtype == 2 && with_tiles) {
+  if (a.dtype == 3 && with_tiles) {
+    // FP8 values: the value sub-tiles take the bf16 value tiles' region (half
+    // its size and the scales), the centroid sub-tiles the fp32 value
+    // centroids past the key-centroid scales
+    a.vt8 = reinterpret_cast<uint8_t*>(a.vt);
+    a.vbar8 = reinterpret_cast<uint8_t*>(a.vbar32) + (BH * (ncp / 64) * 4 + 255) / 256 * 256;
+  }
+  if (a.dtype >= 2 && with_tiles) {
     // FP8 keys: the codes take the first half of the bf16 key tiles and the
     // sub-tile scales the second; the centroid codes and scales take the
     // fp32 centroid arrays, which only the fp32 path uses
@@ -114,6 +121,10 @@ void plan_attend(Carver& cv, AttnArgs& a, bool with_tiles) {
 }
 
 constexpr int kDenseTile = 128;
+
+int attn_dtype(int dt) {
+  return dt == CA_BF16 ? 0 : dt == CA_F32 ? 1 : dt == CA_BF16_FP8 ? 2 : 3;
+}
 
 bool supported_c(int c) { return c == 64 || c == 128 || c == 256; }
 bool supported_d(int d) { return d == 64 || d == 128; }
@@ -141,8 +152,8 @@ int after_launch() {
 }
 
 int check_common(int dt, int B, int H, int N, int D, bool fp8_ok = false) {
-  if (dt != CA_BF16 && dt != CA_F32 && !(fp8_ok && dt == CA_BF16_FP8))
-    return fail(CA_ERR_INVALID_ARG, fp8_ok ? "unknown dtype" : "unknown dtype (CA_BF16_FP8 is for attention only)");
+  if (dt != CA_BF16 && dt != CA_F32 && !(fp8_ok && (dt == CA_BF16_FP8 || dt == CA_BF16_FP8_PV)))
+    return fail(CA_ERR_INVALID_ARG, fp8_ok ? "unknown dtype" : "unknown dtype (CA_BF16_FP8 and CA_BF16_FP8_PV are for attention only)");
   if (B < 1 || H < 1 || N < 1 || D < 1) return fail(CA_ERR_INVALID_ARG, "B, H, N, D must be >= 1");
   if ((int64_t)B * H > 32767) return fail(CA_ERR_UNSUPPORTED, "B*H must be <= 32767");
   if ((int64_t)B * H * N >= (int64_t)1 << 31) return fail(CA_ERR_INVALID_ARG, "B*H*N must be < 2^31");
@@ -390,6 +401,8 @@ int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B,
   if (!supported_c(c) || !supported_c(cq))
     return fail(CA_ERR_UNSUPPORTED, "cluster sizes must be 64, 128 or 256");
   if (cq > c) return fail(CA_ERR_UNSUPPORTED, "the query cluster size must not exceed the key cluster size");
+  if (dt == CA_BF16_FP8_PV && cq < 128)
+    return fail(CA_ERR_UNSUPPORTED, "CA_BF16_FP8_PV needs query clusters of 128 or 256");
   if (N < c) return fail(CA_ERR_INVALID_ARG, "N must be >= the cluster sizes");
   const int nc = (N + c - 1) / c, nqc = (N + cq - 1) / cq;
   if (nc > 8192) return fail(CA_ERR_UNSUPPORTED, "at most 8192 key clusters");
@@ -399,7 +412,7 @@ int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B,
   if (kv_heads < 1 || kv_heads > H || H % kv_heads != 0)
     return fail(CA_ERR_INVALID_ARG, "kv_heads must divide H");
   AttnArgs a{};
-  a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : (dt == CA_F32 ? 1 : 2);
+  a.Q = Q; a.K = K; a.V = V; a.dtype = attn_dtype(dt);
   a.kvg = H / kv_heads;
   a.BH = B * H; a.N = N; a.D = D; a.c = c; a.nc = nc; a.cq = cq; a.nqc = nqc; a.topk = topk;
   a.compensate = compensate ? 1 : 0;
@@ -452,7 +465,7 @@ int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, in
   if (int e = check_common(dt, B, H, N, D, true)) return e;
   if (!(scale >= 0.0f) || !std::isfinite(scale)) return fail(CA_ERR_INVALID_ARG, "scale must be finite and >= 0");
   AttnArgs a{};
-  a.Q = Q; a.K = K; a.V = V; a.dtype = dt == CA_BF16 ? 0 : (dt == CA_F32 ? 1 : 2);
+  a.Q = Q; a.K = K; a.V = V; a.dtype = attn_dtype(dt);
   a.BH = B * H; a.N = N; a.D = D; a.c = kDenseTile; a.nc = (N + kDenseTile - 1) / kDenseTile;
   a.cq = a.c; a.nqc = a.nc; a.kvg = 1;
   a.topk = a.nc; a.compensate = 0;

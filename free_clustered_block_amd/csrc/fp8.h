@@ -31,6 +31,35 @@ CA_DEV floatx16_t mfma32_fp8(const i32x8_t& a, const i32x8_t& b, const floatx16_
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// FP8 value operands of P.V: a block of 32 values of one head dimension shares
+// a power-of-two scale 2^e (the OCP microscaling E8M0 block scale, byte
+// e + 127), e the smallest integer with amax <= 448 * 2^e (at least -127; 0
+// for an all-zero block): with amax = m 2^x, m in [0.5, 1), and 448 = 0.875
+// 2^9, e = x - 9 if m <= 0.875 else x - 8. The MFMA applies the scale of
+// operand A per row and 32-element block of the contraction (opsel picks the
+// byte of the scale register); operand B (the attention weights, <= 256 by
+// the lazy running maximum, exact in range) takes scale byte 127 (2^0).
+CA_DEV int e8m0_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int x;
+  const float m = frexpf(amax, &x);
+  const int e = m <= 0.875f ? x - 9 : x - 8;
+  return e < -127 ? -127 : e;
+}
+
+template <int OPSEL_A>
+CA_DEV floatx16_t mfma32_fp8_scale_a(const i32x8_t& a, const i32x8_t& b, const floatx16_t& c,
+                                     int scale_a) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL_A, scale_a, 0, 0x7F);
+}
+
+// Four values (already in range) as four e4m3 codes, byte i = value i.
+CA_DEV uint32_t e4m3_pack4_raw(float x0, float x1, float x2, float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return (uint32_t)w;
+}
+
 // inv = 448 / amax (0 for amax == 0) and the dequantization scale amax / 448,
 // both rounded to nearest in fp32.
 CA_DEV float e4m3_inv(float amax) { return amax > 0.0f ? __fdiv_rn(kE4m3Max, amax) : 0.0f; }

@@ -101,7 +101,7 @@ struct AttnArgs {
   const void* Q;
   const void* K;
   const void* V;
-  int dtype;   // 0 bf16, 1 fp32, 2 bf16 with FP8 (e4m3) Q.K^T operands
+  int dtype;   // 0 bf16, 1 fp32, 2 bf16 with FP8 (e4m3) Q.K^T operands, 3 FP8 Q.K^T and P.V
   int BH, N, D, c, nc, topk, compensate;   // c, nc: key cluster size and count
   int kvg;                                 // query heads per key/value head (K, V rows of head bh / kvg)
   int cq, nqc;                             // query cluster size and count
@@ -125,6 +125,10 @@ struct AttnArgs {
   float* kscale;      // [BH][nc][c/64]   one scale per 64-key sub-tile
   uint8_t* kbar8;     // [BH][ncp][D]     key-centroid codes
   float* kbscale;     // [BH][ncp/64]     one scale per 64 centroids
+  // FP8 values (dtype 3; carved from vt and from vbar32 past kbscale): per
+  // 64-key sub-tile D rows of 64 codes and 256 scale bytes
+  uint8_t* vt8;       // [BH][nc][c/64] sub-tiles
+  uint8_t* vbar8;     // [BH][ncp/64]   sub-tiles of the value centroids
   // optional events recorded around the main attention kernel
   hipEvent_t ev_start;
   hipEvent_t ev_stop;

@@ -59,9 +59,11 @@ typedef enum {
 typedef enum {
   CA_BF16 = 0,             /* bfloat16 inputs and outputs, fp32 accumulation */
   CA_F32 = 1,              /* float32 throughout                             */
-  CA_BF16_FP8 = 2          /* attention only (ca_attend*, ca_dense): bfloat16
+  CA_BF16_FP8 = 2,         /* attention only (ca_attend*, ca_dense): bfloat16
                               inputs and outputs, the Q.K^T product on FP8
                               (OCP E4M3) operands, P.V as with CA_BF16       */
+  CA_BF16_FP8_PV = 3       /* attention only: as CA_BF16_FP8, and P.V on FP8
+                              operands too (query clusters of 128 or 256)    */
 } ca_dtype;
 
 typedef enum {
@@ -350,6 +352,19 @@ int ca_attend_ex(const void* Q, const void* K, const void* V, ca_dtype dt, int B
  * ca_quantize_e4m3; the logit is scale * s_q * s_k * sum(code_q * code_k)
  * accumulated in fp32. Values, P.V and the output are as with CA_BF16. The
  * workspace is that of CA_BF16.
+ *
+ * With CA_BF16_FP8_PV the P.V product runs on FP8 operands as well (the
+ * pages compare "given equal quantization", v1 §4.1; the scheme is again
+ * stated here). Values are grouped per head dimension over 32 consecutive
+ * members of a key cluster (ca_dense: 32 consecutive tokens; compensation:
+ * 32 consecutive value centroids rounded to bf16); a group shares the scale
+ * 2^e, e the smallest integer with max|v| <= 448 * 2^e (at least -127, 0 for
+ * an all-zero group), codes e4m3(v * 2^-e) rounded to nearest even (the OCP
+ * microscaling E8M0 block scale, applied by the matrix core). The attention
+ * weights exp(logit - m) against the kernel's running maximum m (at most
+ * 2^8) are rounded to e4m3 before the product; the denominator sums them in
+ * fp32 before that rounding. Query clusters must be 128 or 256
+ * (CA_ERR_UNSUPPORTED otherwise). The workspace is that of CA_BF16.
  */
 
 /*

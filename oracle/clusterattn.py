@@ -823,23 +823,15 @@ def dense_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float | 
     return _softmax_combine(tau * (Q @ K.T), V)
 
 
-def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
-                     scale: float | None = None, clusters=None, c_k: int | None = None,
-                     qk: str = "exact", pv: str = "exact"):
-    """Block-sparse attention of one head with optional striped
-    mean-compensation.
-
-    Query i of cluster a attends with token resolution to every key of the
-    selected clusters Sel(a) (Eq. 2). With compensation, every excluded key
-    cluster enters once through its centroid: logit tau q_i . kbar_c +
-    ln|c| and value vbar_c, which is Eq. 21-22 (the centroid weight w_c
-    counted |c| times). Returns O in original token order and LSE.
-    ``clusters`` restricts the work to those query clusters (the rows of the
-    other queries are NaN). Key clusters have size c_k when given, else c.
-    qk="e4m3": the logits use the FP8 operands (fp8_rows per query, fp8_keys,
-    fp8_centroids); the values and the centroid values stay exact unless
-    pv="e4m3" (fp8_values, fp8_value_centroids; the weights stay exact).
-    """
+def attention_terms(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
+                    scale: float | None = None, clusters=None, c_k: int | None = None,
+                    qk: str = "exact", pv: str = "exact"):
+    """The terms sparse_attention combines, per query cluster a: yields
+    (a, query tokens, logits [n_a, terms], values [terms, D]). Query i of
+    cluster a has one term per key of the selected clusters Sel(a), logit
+    tau q_i . k_j and value v_j (Eq. 2), and with compensation one term per
+    excluded key cluster, logit tau q_i . kbar_c + ln|c| and value vbar_c
+    (Eq. 21-22, the centroid weight counted |c| times)."""
     N, D = np.shape(Q)
     tau = 1.0 / math.sqrt(D) if not scale else float(scale)
     ck = c_k or c
@@ -852,8 +844,6 @@ def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
     if pv == "e4m3":
         V, vbar = fp8_values(V, perm_k, ck), fp8_value_centroids(vbar)
     Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
-    O = np.full((N, V.shape[1]), np.nan)
-    L = np.full(N, np.nan)
     for a in (range(len(qs)) if clusters is None else clusters):
         na = qs[a]
         qi = perm_q[a * c:a * c + na]
@@ -869,6 +859,32 @@ def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
                 cl = tau * (Q[qi] @ kbar[ex].T) + np.log(cnt[ex].astype(np.float64))[None, :]
                 logits = np.concatenate([logits, cl], axis=1)
                 vals = np.concatenate([vals, vbar[ex]], axis=0)
+        yield a, qi, logits, vals
+
+
+def sparse_attention(Q, K, V, perm_q, perm_k, c: int, blocks, compensate: bool,
+                     scale: float | None = None, clusters=None, c_k: int | None = None,
+                     qk: str = "exact", pv: str = "exact"):
+    """Block-sparse attention of one head with optional striped
+    mean-compensation.
+
+    Query i of cluster a attends with token resolution to every key of the
+    selected clusters Sel(a) (Eq. 2). With compensation, every excluded key
+    cluster enters once through its centroid: logit tau q_i . kbar_c +
+    ln|c| and value vbar_c, which is Eq. 21-22 (the centroid weight w_c
+    counted |c| times); attention_terms lists these terms. Returns O in
+    original token order and LSE. ``clusters`` restricts the work to those
+    query clusters (the rows of the other queries are NaN). Key clusters have
+    size c_k when given, else c.
+    qk="e4m3": the logits use the FP8 operands (fp8_rows per query, fp8_keys,
+    fp8_centroids); the values and the centroid values stay exact unless
+    pv="e4m3" (fp8_values, fp8_value_centroids; the weights stay exact).
+    """
+    N = np.shape(Q)[0]
+    O = np.full((N, np.shape(V)[1]), np.nan)
+    L = np.full(N, np.nan)
+    for _, qi, logits, vals in attention_terms(Q, K, V, perm_q, perm_k, c, blocks, compensate,
+                                               scale, clusters, c_k, qk, pv):
         o, lse = _softmax_combine(logits, vals)
         O[qi] = o
         L[qi] = lse
@@ -901,7 +917,7 @@ def dense(Q, K, V, scale=None, qk: str = "exact", pv: str = "exact"):
 
 
 def forward(Q, K, V, c: int, topk: int, compensate: bool = True, opts: ClusterOpts | None = None,
-            dtype: str = "bf16", scale=None, qk: str = "exact"):
+            dtype: str = "bf16", scale=None, qk: str = "exact", pv: str = "exact"):
     """The whole path: cluster -> centroids -> route -> attend (v1 §1.1)."""
     pq, pk = cluster(Q, K, c, opts, dtype)
     B, H, N, D = Q.shape
@@ -911,7 +927,7 @@ def forward(Q, K, V, c: int, topk: int, compensate: bool = True, opts: ClusterOp
             cq, _ = centroids(Q[b, h], pq[b, h], c)
             ck, _ = centroids(K[b, h], pk[b, h], c)
             blocks[b, h] = route(cq, ck, topk)
-    O, L = attend(Q, K, V, pq, pk, c, blocks, compensate, scale, qk=qk)
+    O, L = attend(Q, K, V, pq, pk, c, blocks, compensate, scale, qk=qk, pv=pv)
     return O, L, pq, pk, blocks
 
 

@@ -172,7 +172,13 @@ def test_fp8_dtype_and_quantize_reject_bad_arguments(lib):
     assert _cluster(lib, dt=2) == 1
     assert b"attention only" in lib.ca_last_error()
     assert lib.ca_dense(FAKE, FAKE, FAKE, 2, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 8, None) == 3
-    assert lib.ca_dense(FAKE, FAKE, FAKE, 3, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 8, None) == 1
+    # CA_BF16_FP8_PV (3): attention only, query clusters of 128 or 256
+    assert lib.ca_dense(FAKE, FAKE, FAKE, 3, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 8, None) == 3
+    assert lib.ca_dense(FAKE, FAKE, FAKE, 4, 1, 1, 128, 64, 0.0, FAKE, None, FAKE, 8, None) == 1
+    assert _cluster(lib, dt=3) == 1
+    assert _attend(lib, dt=3, c=64) == 2
+    assert b"CA_BF16_FP8_PV" in lib.ca_last_error()
+    assert _attend(lib, dt=3, c=128, topk=2, ws_bytes=10) == 3
     assert _attend(lib, dt=2, ws_bytes=10) == 3
     q = lib.ca_quantize_e4m3
     # X, dt, rows, D, group, codes, scales, stream

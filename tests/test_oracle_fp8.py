@@ -320,11 +320,48 @@ def check_fp8_value_centroid_double_rounding():
     assert abs(Oe[0, 0] - x / 2) < 1e-15 and abs(Oe[0, 0] - O[0, 0]) > 1e-7
 
 
+def check_pv_rounding_bound():
+    """The bound tests/fp8_bound.py gives holds for the kernel's algorithm run
+    in fp64: sub-tiles of 64 terms, a running maximum that moves only when a
+    sub-tile's maximum exceeds it by more than 8 (log2 units), weights
+    2^(l - m) rounded to E4M3, accumulators rescaled when m moves, the
+    denominator over the unrounded weights. And the rounding is visible."""
+    from fp8_bound import pv_rounding_bound
+    r = _rng(9)
+    worst = 0.0
+    for trial in range(40):
+        T, D = int(r.integers(64, 600)), 8
+        spread = [0.5, 3.0, 12.0][trial % 3]
+        L2 = r.standard_normal((4, T)) * spread + r.standard_normal((4, 1)) * 20   # log2 units
+        Vh = o.fp8_value_rows(r.standard_normal((T, D)), 32)
+        want = (np.exp2(L2 - L2.max(1, keepdims=True)) @ Vh) / np.exp2(
+            L2 - L2.max(1, keepdims=True)).sum(1, keepdims=True)
+        for i in range(4):
+            m, acc, den = -np.inf, np.zeros(D), 0.0
+            for t0 in range(0, T, 64):
+                blk = L2[i, t0:t0 + 64]
+                bm = blk.max()
+                if bm > m + 8:
+                    alpha = np.exp2(m - bm) if m > -np.inf else 0.0
+                    acc, den, m = acc * alpha, den * alpha, bm
+                P = np.exp2(blk - m)
+                assert P.max() <= 256.0
+                Ph = o.e4m3_decode(o.e4m3_encode(P))
+                acc = acc + Ph @ Vh[t0:t0 + 64]
+                den += P.sum()
+            got = acc / den
+            b = pv_rounding_bound(L2[i:i + 1] * np.log(2.0), Vh)[0]
+            assert np.all(np.abs(got - want[i]) <= b * (1 + 1e-9) + 1e-12)
+            worst = max(worst, float(np.max(np.abs(got - want[i]))))
+    assert worst > 1e-4
+
+
 CHECKS = [check_e4m3_decode_library, check_e4m3_encode_library, check_bf16_library,
           check_quantize_worked_example, check_quantize_bounds, check_fp8_attention_lossless,
           check_fp8_centroid_double_rounding, check_fp8_attention_error_bound,
           check_e8m0_bruteforce, check_mx_quantize_worked_example, check_mx_quantize_bounds,
-          check_fp8_values_lossless, check_fp8_value_centroid_double_rounding]
+          check_fp8_values_lossless, check_fp8_value_centroid_double_rounding,
+          check_pv_rounding_bound]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[f.__name__ for f in CHECKS])
