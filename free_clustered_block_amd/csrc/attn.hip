@@ -32,6 +32,7 @@
 // most 2^8 by the lazy running maximum, inside the format's range) before
 // the product; the softmax denominator sums the fp32 weights.
 // fp32 path: the same computation on VALU, one thread per query.
+#include <algorithm>
 #include <type_traits>
 
 #include "fp8.h"
@@ -737,6 +738,382 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
   if (a.lse && h == 0) a.lse[(int64_t)bh * N + qtok] = (m + log2f(lsum)) * kLn2;
 }
 
+// ----------------------------------------------------------------------------
+// Attention, bf16, software-pipelined (query clusters of 128 or 256)
+// ----------------------------------------------------------------------------
+
+// 16 bytes per lane from global memory straight into LDS (lane l's bytes land
+// at lds + 16 l; lds is wave-uniform). Written out so that the compiler,
+// which would otherwise wait for the transfer before every later LDS read,
+// leaves the wait to the caller (s_waitcnt vmcnt before the barrier that
+// publishes the buffer). M0 is restored after the issue.
+CA_DEV void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+// Same work as attn_fwd<D, CQ, CK, DENSE, false, 1>, scheduled as a pipeline:
+// iteration t computes the softmax of sub-tile t while the matrix cores run
+// the Q.K^T products of sub-tile t + 1 and the P.V products of sub-tile
+// t - 1. K and V^T sub-tiles are moved into LDS by direct global-to-LDS loads
+// (no register staging), double buffered: K of sub-tile t + 2 and V^T of
+// sub-tile t are issued at the top of iteration t and waited for at its end,
+// one barrier per iteration. LDS rows are unpadded with their 16-byte chunks
+// XOR-swizzled by the row index (conflict-free operand reads). The running
+// maximum is lazy as in attn_fwd (it moves only when a sub-tile exceeds it by
+// more than kLazy); the sub-tile's maximum is taken first, so the weights are
+// formed once, against the final value.
+//
+// LDS of attn_fwd2 past the K and V double buffers: the selected clusters
+// (up to kBlkCache entries), and with compensation the centroid logit bias
+// (ln n_c in log2 units, -inf for selected or padding clusters).
+constexpr int kBlkCache = 1024;
+struct Attn2Lds {
+  int blk_off, bias_off, bytes;
+};
+template <int D>
+Attn2Lds attn2_lds(int nc, int topk, bool comp) {
+  Attn2Lds r;
+  r.blk_off = 2 * (64 * 2 * D) + 2 * (D * 2 * 64);
+  r.bias_off = r.blk_off + 4 * std::min(topk, kBlkCache);
+  r.bytes = r.bias_off + (comp ? 4 * attn_ncp(nc) : 0);
+  return r;
+}
+
+template <int D, int CQ, int CK, bool DENSE>
+__global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd2(AttnArgs a, Attn2Lds lay) {
+  constexpr int NT = 2 * CQ, NW = NT / 64;
+  constexpr int KT = 64, KS = D / 16, NB = D / 32, SUB = CK / KT;
+  constexpr int KROW = 2 * D, CPRK = KROW / 16;       // K row bytes, 16-byte chunks per row
+  constexpr int KBUF = KT * KROW;
+  constexpr int VROW = 2 * KT, CPRV = VROW / 16;      // V^T row bytes (64 keys), chunks
+  constexpr int VBUF = D * VROW;
+  constexpr int KPW = KBUF / 1024 / NW, VPW = VBUF / 1024 / NW;   // 1 KB transfers per wave
+  static_assert(KBUF % (1024 * NW) == 0 && VBUF % (1024 * NW) == 0, "whole transfers per wave");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int* sBlk = reinterpret_cast<int*>(smem + lay.blk_off);
+  float* sBias = reinterpret_cast<float*>(smem + lay.bias_off);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+  const int G = gridDim.x * gridDim.y;
+  const int lg = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, G);
+  const int nc = a.nc, nqc = a.nqc, N = a.N;
+  const int qa = lg % nqc, bh = lg / nqc;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
+  const int qpos = qa * CQ + w * 32 + r;
+  const bool qvalid = qpos < N;
+  const int qtok =
+      qvalid ? (DENSE || !a.perm_q ? qpos : clamp_tok(a.perm_q[(int64_t)bh * N + qpos], N)) : 0;
+  const uint16_t* Qh = (const uint16_t*)a.Q + (int64_t)bh * N * D;
+
+  bf16x8_t qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (qvalid) v = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)qtok * D + s * 16 + h * 8);
+    qf[s] = as_bf16x8(v);
+  }
+  floatx16_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = zero16();
+  float m = kNegInf, lsum = 0.0f;
+  const float sl2 = a.scale * kLog2e;
+
+  const int nsel = DENSE ? nc
+                  : (a.nsel ? min(max(a.nsel[(int64_t)bh * nqc + qa], 0), a.topk) : a.topk);
+  const int32_t* blk = DENSE ? nullptr : a.blocks + ((int64_t)bh * nqc + qa) * a.topk;
+  const int Tm = nsel * SUB;
+  const int ncp = attn_ncp(nc);
+  const bool comp = !DENSE && a.compensate;
+  const int T = Tm + (comp ? ncp / KT : 0);
+  const int ncache = min(nsel, kBlkCache);
+  if (!DENSE) {
+    for (int e = tid; e < ncache; e += NT) sBlk[e] = blk[e];
+    if (comp) {
+      // bias of centroid c: ln n_c (log2 units) if c is not selected, else -inf
+      const float* logn = a.logn + (int64_t)bh * ncp;
+      for (int e = tid; e < ncp; e += NT) sBias[e] = logn[e] * kLog2e;
+      __syncthreads();
+      for (int e = tid; e < nsel; e += NT) {
+        const int j = blk[e];
+        if (j >= 0 && j < nc) sBias[j] = kNegInf;
+      }
+    }
+    __syncthreads();
+  }
+
+  // cluster of token sub-tile t, uniform (-1: an out-of-range entry, skipped)
+  auto tile_cluster = [&](int t) -> int {
+    if (DENSE) return t / SUB;
+    const int e = t / SUB;
+    const int j = __builtin_amdgcn_readfirstlane(e < kBlkCache ? sBlk[e] : blk[e]);
+    return (j >= 0 && j < nc) ? j : -1;
+  };
+  auto uniform_ptr = [](const void* p) -> const unsigned char* {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const unsigned char*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+  };
+  auto k_src = [&](int t, int j) -> const unsigned char* {
+    if (t < Tm)
+      return uniform_ptr(a.kc + (((int64_t)bh * nc + max(j, 0)) * CK + (t % SUB) * KT) * D);
+    return uniform_ptr(a.kbar_hi + ((int64_t)bh * ncp + (t - Tm) * KT) * D);
+  };
+  auto v_src = [&](int t, int j) -> const unsigned char* {
+    if (t < Tm)
+      return uniform_ptr(a.vt + (((int64_t)bh * nc + max(j, 0)) * SUB + t % SUB) * (int64_t)D * KT);
+    return uniform_ptr(a.vbar_t + ((int64_t)bh * (ncp / KT) + (t - Tm)) * D * KT);
+  };
+  // per-lane source offsets of this wave's transfers: LDS chunk q = 64 (i NW + w) + l
+  // holds row q / CPR, source chunk (q % CPR) ^ (row % CPR)
+  uint32_t koff[KPW], voff[VPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int q = 64 * (i * NW + w) + l, row = q / CPRK, pos = q % CPRK;
+    koff[i] = row * KROW + (pos ^ (row % CPRK)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < VPW; ++i) {
+    const int q = 64 * (i * NW + w) + l, row = q / CPRV, pos = q % CPRV;
+    voff[i] = row * VROW + (pos ^ (row % CPRV)) * 16;
+  }
+  const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds0 + 1024 * w);
+  auto load_k = [&](int t, int slot) {
+    const unsigned char* src = k_src(t, t < Tm ? tile_cluster(t) : 0);
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) dma16(koff[i], src, wlds + slot * KBUF + 1024 * NW * i);
+  };
+  auto load_v = [&](int t, int slot) {
+    const unsigned char* src = v_src(t, t < Tm ? tile_cluster(t) : 0);
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) dma16(voff[i], src, wlds + 2 * KBUF + slot * VBUF + 1024 * NW * i);
+  };
+  // per-lane operand read offsets: K row 32 kb + r chunk 2 s + h; V^T row 32 nb + r chunk 2 q + h
+  int kro[KS], vro[4];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) kro[s] = r * KROW + (((2 * s + h) ^ (r % CPRK)) * 16);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) vro[q] = 2 * KBUF + r * VROW + (((2 * q + h) ^ (r % CPRV)) * 16);
+
+  // Q.K^T of the sub-tile in K slot `slot` into s2 (two 32-key blocks)
+  auto qk = [&](int slot, floatx16_t (&s2)[2]) __attribute__((always_inline)) {
+    s2[0] = zero16();
+    s2[1] = zero16();
+    const unsigned char* base = smem + slot * KBUF;
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(base + kro[i >> 1] + (i & 1) * 32 * KROW);
+      s2[i & 1] = mfma32(kv, qf[i >> 1], s2[i & 1]);
+    }
+  };
+  // O^T += V^T P^T of the sub-tile in V slot `slot`, weights pk
+  auto pv = [&](int slot, const bf16x8_t (&pk)[4]) __attribute__((always_inline)) {
+    const unsigned char* base = smem + slot * VBUF;
+#pragma unroll
+    for (int i = 0; i < 4 * NB; ++i) {
+      const int nb = i % NB, q = i / NB;
+      const bf16x8_t vv = *reinterpret_cast<const bf16x8_t*>(base + vro[q] + nb * 32 * VROW);
+      acc[nb] = mfma32(vv, pk[q], acc[nb]);
+    }
+  };
+  // the short last cluster's sub-tiles need key masking
+  int rpos = -1;
+  if (N % CK != 0) {
+    if (DENSE) {
+      rpos = nc - 1;
+    } else {
+      int mine = -1;
+      for (int e = l; e < nsel; e += 64)
+        if ((e < kBlkCache ? sBlk[e] : blk[e]) == nc - 1) mine = e;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mine = max(mine, __shfl_xor(mine, o, 64));
+      rpos = __builtin_amdgcn_readfirstlane(mine);
+    }
+  }
+  // Logits of sub-tile t in log2 units (token tiles: masked past the
+  // cluster's end; centroid tiles: + the bias); returns the factor still to
+  // apply (the scale for token tiles, 1 for centroid tiles).
+  auto logits = [&](int t, int j, floatx16_t (&s2)[2]) __attribute__((always_inline)) -> float {
+    if (t >= Tm) {
+      const int c0 = (t - Tm) * KT;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const floatx4_t bias = *reinterpret_cast<const floatx4_t*>(sBias + c0 + kb * 32 + 8 * q + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s2[kb][4 * q + e] = fmaf(s2[kb][4 * q + e], sl2, bias[e]);
+        }
+      return 1.0f;
+    }
+    if (rpos >= 0 && t / SUB == rpos) {
+      const int nvalid = min(CK, N - j * CK) - (t % SUB) * KT;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s2[kb][i] = kb * 32 + c_row(i, h) >= nvalid ? kNegInf : s2[kb][i];
+    }
+    return sl2;
+  };
+
+  floatx16_t scur[2], snext[2];
+  bf16x8_t pkold[4];
+  // prologue: K of sub-tiles 0 and 1, Q.K^T of sub-tile 0
+  if (T > 0) load_k(0, 0);
+  if (T > 1) load_k(1, 1);
+  __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
+  __syncthreads();
+  if (T > 0) qk(0, scur);
+  __syncthreads();   // every wave has read K slot 0 before it is refilled
+
+  // Iteration t: transfers for later sub-tiles, then one straight-line
+  // region holding the P.V products of t - 1 (PV), the Q.K^T products of
+  // t + 1 (QK) and the softmax of t, interleaved by scheduling groups (one
+  // operand read, one product, four vector instructions), then the rare
+  // rescale, the wait for the transfers and the barrier.
+  auto iter = [&](int t, auto pv_tag, auto qk_tag) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
+    const int ks = t & 1;
+    const int jt = t < Tm ? tile_cluster(t) : 0;
+    const bool skip = jt < 0;
+    if (t + 2 < T) load_k(t + 2, ks);
+    {
+      const unsigned char* src = v_src(t, jt);
+#pragma unroll
+      for (int i = 0; i < VPW; ++i) dma16(voff[i], src, wlds + 2 * KBUF + ks * VBUF + 1024 * NW * i);
+    }
+    const float scl = logits(t, jt, scur);
+    // One instruction stream in a fixed order (scheduling barriers between
+    // steps): step i issues product i (the 4 NB P.V products of t - 1, then
+    // the 2 KS Q.K^T products of t + 1) and the LDS read of product i + PF's
+    // operand, beside the softmax of sub-tile t: its maximum over the first
+    // MS steps, then (branch-free, per lane) the new running maximum, and in
+    // the remaining steps the weights against it, packed to bf16 and summed
+    // 8 at a time. Nothing of sub-tile t's logits is needed afterwards.
+    constexpr int NPV = PV ? 4 * NB : 0, NM = NPV + (QK ? 2 * KS : 0);
+    constexpr int PF = 4;
+    constexpr int NSTEP = NM > 0 ? NM : 1;
+    constexpr int MS = NSTEP >= 4 ? NSTEP / 4 : 1;        // steps of the maximum
+    constexpr int E0 = NSTEP > 1 ? MS : 0, NE = NSTEP - E0;   // steps of the weights
+    const unsigned char* vbase = smem + (ks ^ 1) * VBUF;
+    const unsigned char* kbase = smem + (ks ^ 1) * KBUF;
+    auto operand = [&](int i) -> bf16x8_t {
+      if (i < NPV) {
+        const int nb = i % NB, q = i / NB;
+        return *reinterpret_cast<const bf16x8_t*>(vbase + vro[q] + nb * 32 * VROW);
+      }
+      const int k = i - NPV;
+      return *reinterpret_cast<const bf16x8_t*>(kbase + kro[k >> 1] + (k & 1) * 32 * KROW);
+    };
+    if constexpr (QK) {
+      snext[0] = zero16();
+      snext[1] = zero16();
+    }
+    bf16x8_t ring[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      if (i < NM) ring[i] = operand(i);
+    bf16x8_t pk[4];
+    float ps = 0.0f, tv[8], bm = kNegInf, mn = m, nm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < NM) {
+        if (i < NPV) {
+          const int nb = i % NB, q = i / NB;
+          acc[nb] = mfma32(ring[i % PF], pkold[q], acc[nb]);
+        } else {
+          const int k = i - NPV;
+          snext[k & 1] = mfma32(ring[i % PF], qf[k >> 1], snext[k & 1]);
+        }
+        if (i + PF < NM) ring[i % PF] = operand(i + PF);
+      }
+#pragma unroll
+      for (int el = 0; el < 32; ++el)
+        if (el * MS / 32 == i) bm = fmaxf(bm, scur[el >> 4][el & 15]);
+      if (i == MS - 1) {
+        // the lazy maximum: it moves only when the sub-tile exceeds it by
+        // more than kLazy (always for the first sub-tile with keys); a
+        // skipped sub-tile gets weight 0 through the offset -inf
+        bm = max_halves(bm) * scl;
+        mn = ((bm > m + kLazy) & !skip) ? bm : m;
+        nm = skip ? kNegInf : (mn == kNegInf ? 0.0f : -mn);
+      }
+#pragma unroll
+      for (int el = 0; el < 32; ++el)
+        if (i >= E0 && E0 + el * NE / 32 == i) {
+          tv[el & 7] = __builtin_amdgcn_exp2f(fmaf(scur[el >> 4][el & 15], scl, nm));
+          if ((el & 7) == 7) {
+            u32x4_t u = pack8(tv);
+            ps = sum_bf16x8(u, ps);
+            // pinned here: left free, the weights sink past the rescale
+            // branch, out of the interleaved region
+            asm volatile("" : "+v"(u), "+v"(ps));
+            pk[el >> 3] = as_bf16x8(u);
+          }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (__ballot(mn != m)) [[unlikely]] {
+      // the maximum moved: rescale what is accumulated (the P.V products of
+      // t - 1 are in)
+      const float alpha = mn != m ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
+      lsum *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
+      m = mn;
+    }
+    lsum += ps;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pkold[q] = pk[q];
+    if constexpr (QK) {
+      scur[0] = snext[0];
+      scur[1] = snext[1];
+    }
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this iteration's transfers
+    __syncthreads();
+  };
+  if (T == 1) {
+    iter(0, std::false_type{}, std::false_type{});
+  } else if (T > 1) {
+    iter(0, std::false_type{}, std::true_type{});
+#pragma unroll 1
+    for (int t = 1; t < T - 1; ++t) iter(t, std::true_type{}, std::true_type{});
+    iter(T - 1, std::true_type{}, std::false_type{});
+  }
+  if (T > 0) pv((T - 1) & 1, pkold);
+
+  lsum = sum_halves(lsum);
+  if (!qvalid) return;
+  const float inv = 1.0f / lsum;
+  uint16_t* Oh = (uint16_t*)a.O + ((int64_t)bh * N + qtok) * D;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = nb * 32 + 8 * g + 4 * h;
+      u32x2_t v;
+      v.x = pack_bf16x2(acc[nb][4 * g] * inv, acc[nb][4 * g + 1] * inv);
+      v.y = pack_bf16x2(acc[nb][4 * g + 2] * inv, acc[nb][4 * g + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(Oh + d0) = v;
+    }
+  }
+  if (a.lse && h == 0) a.lse[(int64_t)bh * N + qtok] = (m + log2f(lsum)) * kLn2;
+}
+
+
 template <int D, bool FP8, bool FP8PV>
 constexpr size_t attn_smem() {
   return 2 * (size_t)AttnTile<D, FP8, FP8PV>::BYTES + 8192 / 8 + 64;   // two buffers, selection bits
@@ -871,6 +1248,17 @@ void launch_mfma(const AttnArgs& a, hipStream_t st) {
   if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);
 }
 
+// bf16 without FP8 operands, query clusters of 128 or 256: the pipelined kernel
+template <int D, int CQ, int CK, bool DENSE>
+void launch_mfma2(const AttnArgs& a, hipStream_t st) {
+  const Attn2Lds lay = attn2_lds<D>(a.nc, DENSE ? 0 : a.topk, !DENSE && a.compensate);
+  CA_MAX_LDS_ONCE((&attn_fwd2<D, CQ, CK, DENSE>), 160 * 1024);
+  dim3 g(a.nqc, a.BH);
+  if (a.ev_start) (void)hipEventRecord(a.ev_start, st);
+  attn_fwd2<D, CQ, CK, DENSE><<<g, 2 * CQ, (size_t)lay.bytes, st>>>(a, lay);
+  if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);
+}
+
 template <int D, bool FP8, bool FP8PV>
 void launch_tiles(const AttnArgs& a, bool dense, hipStream_t st) {
   dim3 gp(attn_ncp(a.nc), a.BH);
@@ -881,7 +1269,8 @@ void launch_tiles(const AttnArgs& a, bool dense, hipStream_t st) {
     if (FP8PV) quant_vcentroids<D><<<gq, 256, 0, st>>>(a);
   }
   if (dense) {
-    launch_mfma<D, 128, 128, true, FP8, FP8PV>(a, st);
+    if constexpr (!FP8) launch_mfma2<D, 128, 128, true>(a, st);
+    else launch_mfma<D, 128, 128, true, FP8, FP8PV>(a, st);
     return;
   }
   // (query, key) cluster sizes: equal, or the key clusters larger (FP8
@@ -891,6 +1280,15 @@ void launch_tiles(const AttnArgs& a, bool dense, hipStream_t st) {
       case 128128: launch_mfma<D, 128, 128, false, FP8, FP8PV>(a, st); break;
       case 128256: launch_mfma<D, 128, 256, false, FP8, FP8PV>(a, st); break;
       default: launch_mfma<D, 256, 256, false, FP8, FP8PV>(a, st); break;
+    }
+  } else if constexpr (!FP8) {
+    switch (a.cq * 1000 + a.c) {
+      case 64064: launch_mfma<D, 64, 64, false, FP8, FP8PV>(a, st); break;
+      case 64128: launch_mfma<D, 64, 128, false, FP8, FP8PV>(a, st); break;
+      case 64256: launch_mfma<D, 64, 256, false, FP8, FP8PV>(a, st); break;
+      case 128128: launch_mfma2<D, 128, 128, false>(a, st); break;
+      case 128256: launch_mfma2<D, 128, 256, false>(a, st); break;
+      default: launch_mfma2<D, 256, 256, false>(a, st); break;
     }
   } else {
     switch (a.cq * 1000 + a.c) {
