@@ -34,6 +34,7 @@
 // fp32 path: the same computation on VALU, one thread per query.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "fp8.h"
 #include "kernels.h"
@@ -742,6 +743,18 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
 // Attention, bf16, software-pipelined (query clusters of 128 or 256)
 // ----------------------------------------------------------------------------
 
+// f(std::integral_constant<int, i>) for i = 0 .. N - 1, expanded at compile
+// time (a loop the unroller may decline to flatten is not acceptable inside a
+// hand-scheduled region)
+template <class F, int... I>
+CA_DEV void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+CA_DEV void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 // 16 bytes per lane from global memory straight into LDS (lane l's bytes land
 // at lds + 16 l; lds is wave-uniform). Written out so that the compiler,
 // which would otherwise wait for the transfer before every later LDS read,
@@ -800,6 +813,7 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
   static_assert(KBUF % (1024 * NW) == 0 && VBUF % (1024 * NW) == 0, "whole transfers per wave");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int* sBlk = reinterpret_cast<int*>(smem + lay.blk_off);
+  const __attribute__((address_space(3))) int* sBlkL = (const __attribute__((address_space(3))) int*)sBlk;
   float* sBias = reinterpret_cast<float*>(smem + lay.bias_off);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
@@ -854,7 +868,10 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
   auto tile_cluster = [&](int t) -> int {
     if (DENSE) return t / SUB;
     const int e = t / SUB;
-    const int j = __builtin_amdgcn_readfirstlane(e < kBlkCache ? sBlk[e] : blk[e]);
+    int j;
+    if (e < kBlkCache) j = sBlkL[e];   // an LDS read, not a generic one
+    else j = blk[e];
+    j = __builtin_amdgcn_readfirstlane(j);
     return (j >= 0 && j < nc) ? j : -1;
   };
   auto uniform_ptr = [](const void* p) -> const unsigned char* {
@@ -874,54 +891,55 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
     return uniform_ptr(a.vbar_t + ((int64_t)bh * (ncp / KT) + (t - Tm)) * D * KT);
   };
   // per-lane source offsets of this wave's transfers: LDS chunk q = 64 (i NW + w) + l
-  // holds row q / CPR, source chunk (q % CPR) ^ (row % CPR)
-  uint32_t koff[KPW], voff[VPW];
-#pragma unroll
-  for (int i = 0; i < KPW; ++i) {
-    const int q = 64 * (i * NW + w) + l, row = q / CPRK, pos = q % CPRK;
-    koff[i] = row * KROW + (pos ^ (row % CPRK)) * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < VPW; ++i) {
-    const int q = 64 * (i * NW + w) + l, row = q / CPRV, pos = q % CPRV;
-    voff[i] = row * VROW + (pos ^ (row % CPRV)) * 16;
+  // holds row q / CPR, source chunk (q % CPR) ^ (row % CPR). Transfer i is
+  // transfer 0 moved by 1024 NW bytes at both ends: 64 NW chunks are a whole
+  // number of rows, and a multiple of CPR rows (row % CPR does not change).
+  static_assert((64 * NW) % (CPRK * CPRK) == 0 && (64 * NW) % (CPRV * CPRV) == 0, "transfer stride");
+  uint32_t koff, voff;
+  {
+    const int q = 64 * w + l;
+    koff = (q / CPRK) * KROW + ((q % CPRK) ^ ((q / CPRK) % CPRK)) * 16;
+    voff = (q / CPRV) * VROW + ((q % CPRV) ^ ((q / CPRV) % CPRV)) * 16;
   }
   const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds0 + 1024 * w);
   auto load_k = [&](int t, int slot) {
     const unsigned char* src = k_src(t, t < Tm ? tile_cluster(t) : 0);
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) dma16(koff[i], src, wlds + slot * KBUF + 1024 * NW * i);
-  };
-  auto load_v = [&](int t, int slot) {
-    const unsigned char* src = v_src(t, t < Tm ? tile_cluster(t) : 0);
-#pragma unroll
-    for (int i = 0; i < VPW; ++i) dma16(voff[i], src, wlds + 2 * KBUF + slot * VBUF + 1024 * NW * i);
+    for (int i = 0; i < KPW; ++i) dma16(koff, src + 1024 * NW * i, wlds + slot * KBUF + 1024 * NW * i);
   };
   // per-lane operand read offsets: K row 32 kb + r chunk 2 s + h; V^T row 32 nb + r chunk 2 q + h
-  int kro[KS], vro[4];
+  // (LDS addresses: the slot and block offsets of a read are then immediates)
+  // K: chunk (2 s + h) ^ x of row r, x = r % CPRK, is at byte
+  // 32 (s ^ (x >> 1)) + 16 (h ^ (x & 1)) of the row: kbase + (32 s ^ kx).
+  // The per-read XOR (one v_xad with the add) replaces eight address
+  // registers that would be loop-invariant and, at this register budget,
+  // spilled.
+  const uint32_t kbase = lds0 + r * KROW + 16 * (h ^ (r & 1));
+  const uint32_t kx = 32 * ((r % CPRK) >> 1);
+  auto kro_at = [&](uint32_t kxv, int s) -> uint32_t { return kbase + ((32u * s) ^ kxv); };
+  uint32_t vro[4];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) kro[s] = r * KROW + (((2 * s + h) ^ (r % CPRK)) * 16);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) vro[q] = 2 * KBUF + r * VROW + (((2 * q + h) ^ (r % CPRV)) * 16);
+  for (int q = 0; q < 4; ++q) vro[q] = lds0 + 2 * KBUF + r * VROW + (((2 * q + h) ^ (r % CPRV)) * 16);
+  auto lds16 = [](uint32_t addr) -> bf16x8_t {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>((uintptr_t)addr);
+  };
 
   // Q.K^T of the sub-tile in K slot `slot` into s2 (two 32-key blocks)
   auto qk = [&](int slot, floatx16_t (&s2)[2]) __attribute__((always_inline)) {
     s2[0] = zero16();
     s2[1] = zero16();
-    const unsigned char* base = smem + slot * KBUF;
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
-      const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(base + kro[i >> 1] + (i & 1) * 32 * KROW);
+      const bf16x8_t kv = lds16(kro_at(kx, i >> 1) + slot * KBUF + (i & 1) * 32 * KROW);
       s2[i & 1] = mfma32(kv, qf[i >> 1], s2[i & 1]);
     }
   };
   // O^T += V^T P^T of the sub-tile in V slot `slot`, weights pk
   auto pv = [&](int slot, const bf16x8_t (&pk)[4]) __attribute__((always_inline)) {
-    const unsigned char* base = smem + slot * VBUF;
 #pragma unroll
     for (int i = 0; i < 4 * NB; ++i) {
       const int nb = i % NB, q = i / NB;
-      const bf16x8_t vv = *reinterpret_cast<const bf16x8_t*>(base + vro[q] + nb * 32 * VROW);
+      const bf16x8_t vv = lds16(vro[q] + slot * VBUF + nb * 32 * VROW);
       acc[nb] = mfma32(vv, pk[q], acc[nb]);
     }
   };
@@ -966,33 +984,45 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
     return sl2;
   };
 
-  floatx16_t scur[2], snext[2];
-  bf16x8_t pkold[4];
+  // Logits (two 32-key blocks) and bf16 weights of sub-tile t live in
+  // S[t & 1] and PK[t & 1]: with the parity of t known at compile time, each
+  // iteration reads one set and writes the other (no copies), and every LDS
+  // slot offset is an immediate.
+  floatx16_t S[2][2];
+  bf16x8_t PK[2][4];
+  // clusters of sub-tiles t, t + 1 and t + 2 (uniform; -1 for a skipped
+  // entry, 0 for centroid sub-tiles and past the end), read one iteration
+  // ahead so that the region waits for no LDS read of its own
+  auto cl = [&](int t) -> int { return t < Tm ? tile_cluster(t) : 0; };
+  int jc0 = cl(0), jc1 = cl(1), jc2 = cl(2);
   // prologue: K of sub-tiles 0 and 1, Q.K^T of sub-tile 0
   if (T > 0) load_k(0, 0);
   if (T > 1) load_k(1, 1);
   __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
   __syncthreads();
-  if (T > 0) qk(0, scur);
+  if (T > 0) qk(0, S[0]);
   __syncthreads();   // every wave has read K slot 0 before it is refilled
 
-  // Iteration t: transfers for later sub-tiles, then one straight-line
-  // region holding the P.V products of t - 1 (PV), the Q.K^T products of
-  // t + 1 (QK) and the softmax of t, interleaved by scheduling groups (one
-  // operand read, one product, four vector instructions), then the rare
-  // rescale, the wait for the transfers and the barrier.
-  auto iter = [&](int t, auto pv_tag, auto qk_tag) __attribute__((always_inline)) {
+  // Iteration t (parity P = t & 1): one straight-line region holding the
+  // transfers for later sub-tiles, the P.V products of t - 1 (PV), the Q.K^T
+  // products of t + 1 (QK) and the softmax of t, then the rare rescale, the
+  // wait for the transfers and the barrier.
+  auto iter = [&](int t, auto parity, auto pv_tag, auto qk_tag) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
     constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
-    const int ks = t & 1;
-    const int jt = t < Tm ? tile_cluster(t) : 0;
-    const bool skip = jt < 0;
-    if (t + 2 < T) load_k(t + 2, ks);
-    {
-      const unsigned char* src = v_src(t, jt);
-#pragma unroll
-      for (int i = 0; i < VPW; ++i) dma16(voff[i], src, wlds + 2 * KBUF + ks * VBUF + 1024 * NW * i);
-    }
-    const float scl = logits(t, jt, scur);
+    floatx16_t (&scur)[2] = S[P];
+    floatx16_t (&snext)[2] = S[P ^ 1];
+    const bf16x8_t (&pkold)[4] = PK[P ^ 1];
+    bf16x8_t (&pk)[4] = PK[P];
+    const bool skip = jc0 < 0;
+    // transfers of this iteration (issued inside the region below): V^T of
+    // sub-tile t into V slot P and K of sub-tile t + 2 into K slot P. Past
+    // the last sub-tile the K transfer repeats V^T's 16 KB source (K slot P
+    // is not read again), which keeps the region free of branches.
+    const unsigned char* vsrc = v_src(t, jc0);
+    const unsigned char* ksrc = t + 2 < T ? k_src(t + 2, jc2) : vsrc;
+    const float skipoff = skip ? kNegInf : 0.0f;   // uniform: no branch in the region
+    const float scl = logits(t, jc0, scur);
     // One instruction stream in a fixed order (scheduling barriers between
     // steps): step i issues product i (the 4 NB P.V products of t - 1, then
     // the 2 KS Q.K^T products of t + 1) and the LDS read of product i + PF's
@@ -1005,15 +1035,15 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int NSTEP = NM > 0 ? NM : 1;
     constexpr int MS = NSTEP >= 4 ? NSTEP / 4 : 1;        // steps of the maximum
     constexpr int E0 = NSTEP > 1 ? MS : 0, NE = NSTEP - E0;   // steps of the weights
-    const unsigned char* vbase = smem + (ks ^ 1) * VBUF;
-    const unsigned char* kbase = smem + (ks ^ 1) * KBUF;
+    uint32_t kxo = kx;
+    asm volatile("" : "+v"(kxo));   // opaque: the K read addresses stay in the loop
     auto operand = [&](int i) -> bf16x8_t {
       if (i < NPV) {
         const int nb = i % NB, q = i / NB;
-        return *reinterpret_cast<const bf16x8_t*>(vbase + vro[q] + nb * 32 * VROW);
+        return lds16(vro[q] + (P ^ 1) * VBUF + nb * 32 * VROW);
       }
       const int k = i - NPV;
-      return *reinterpret_cast<const bf16x8_t*>(kbase + kro[k >> 1] + (k & 1) * 32 * KROW);
+      return lds16(kro_at(kxo, k >> 1) + (P ^ 1) * KBUF + (k & 1) * 32 * KROW);
     };
     if constexpr (QK) {
       snext[0] = zero16();
@@ -1023,37 +1053,42 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
     for (int i = 0; i < PF; ++i)
       if (i < NM) ring[i] = operand(i);
-    bf16x8_t pk[4];
     float ps = 0.0f, tv[8], bm = kNegInf, mn = m, nm = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
+    static_for<NSTEP>([&](auto step) __attribute__((always_inline)) {
+      constexpr int i = decltype(step)::value;
       __builtin_amdgcn_sched_barrier(0);
-      if (i < NM) {
-        if (i < NPV) {
-          const int nb = i % NB, q = i / NB;
-          acc[nb] = mfma32(ring[i % PF], pkold[q], acc[nb]);
-        } else {
-          const int k = i - NPV;
-          snext[k & 1] = mfma32(ring[i % PF], qf[k >> 1], snext[k & 1]);
+      // one transfer per step from the first (V^T first: it is needed sooner)
+      static_for<VPW + KPW>([&](auto xc) __attribute__((always_inline)) {
+        constexpr int x = decltype(xc)::value;
+        if constexpr ((x < NSTEP ? x : NSTEP - 1) == i) {
+          if constexpr (x < VPW) dma16(voff, vsrc + 1024 * NW * x, wlds + 2 * KBUF + P * VBUF + 1024 * NW * x);
+          else dma16(koff, ksrc + 1024 * NW * (x - VPW), wlds + P * KBUF + 1024 * NW * (x - VPW));
         }
-        if (i + PF < NM) ring[i % PF] = operand(i + PF);
+      });
+      if constexpr (i < NPV) {
+        acc[i % NB] = mfma32(ring[i % PF], pkold[i / NB], acc[i % NB]);
+      } else if constexpr (i < NM) {
+        constexpr int k = i - NPV;
+        snext[k & 1] = mfma32(ring[i % PF], qf[k >> 1], snext[k & 1]);
       }
-#pragma unroll
-      for (int el = 0; el < 32; ++el)
-        if (el * MS / 32 == i) bm = fmaxf(bm, scur[el >> 4][el & 15]);
-      if (i == MS - 1) {
+      if constexpr (i + PF < NM) ring[i % PF] = operand(i + PF);
+      static_for<32>([&](auto ec) __attribute__((always_inline)) {
+        constexpr int el = decltype(ec)::value;
+        if constexpr (el * MS / 32 == i) bm = fmaxf(bm, scur[el >> 4][el & 15]);
+      });
+      if constexpr (i == MS - 1) {
         // the lazy maximum: it moves only when the sub-tile exceeds it by
         // more than kLazy (always for the first sub-tile with keys); a
         // skipped sub-tile gets weight 0 through the offset -inf
         bm = max_halves(bm) * scl;
         mn = ((bm > m + kLazy) & !skip) ? bm : m;
-        nm = skip ? kNegInf : (mn == kNegInf ? 0.0f : -mn);
+        nm = (mn == kNegInf ? 0.0f : -mn) + skipoff;
       }
-#pragma unroll
-      for (int el = 0; el < 32; ++el)
-        if (i >= E0 && E0 + el * NE / 32 == i) {
+      static_for<32>([&](auto ec) __attribute__((always_inline)) {
+        constexpr int el = decltype(ec)::value;
+        if constexpr (i >= E0 && E0 + el * NE / 32 == i) {
           tv[el & 7] = __builtin_amdgcn_exp2f(fmaf(scur[el >> 4][el & 15], scl, nm));
-          if ((el & 7) == 7) {
+          if constexpr ((el & 7) == 7) {
             u32x4_t u = pack8(tv);
             ps = sum_bf16x8(u, ps);
             // pinned here: left free, the weights sink past the rescale
@@ -1062,7 +1097,8 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
             pk[el >> 3] = as_bf16x8(u);
           }
         }
-    }
+      });
+    });
     __builtin_amdgcn_sched_barrier(0);
     if (__ballot(mn != m)) [[unlikely]] {
       // the maximum moved: rescale what is accumulated (the P.V products of
@@ -1076,24 +1112,37 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
       m = mn;
     }
     lsum += ps;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) pkold[q] = pk[q];
-    if constexpr (QK) {
-      scur[0] = snext[0];
-      scur[1] = snext[1];
-    }
+    jc0 = jc1;
+    jc1 = jc2;
+    jc2 = cl(t + 3);
     __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this iteration's transfers
     __syncthreads();
   };
+  using F_ = std::false_type;
+  using T_ = std::true_type;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   if (T == 1) {
-    iter(0, std::false_type{}, std::false_type{});
+    iter(0, P0{}, F_{}, F_{});
   } else if (T > 1) {
-    iter(0, std::false_type{}, std::true_type{});
+    iter(0, P0{}, F_{}, T_{});
+    int t = 1;
 #pragma unroll 1
-    for (int t = 1; t < T - 1; ++t) iter(t, std::true_type{}, std::true_type{});
-    iter(T - 1, std::true_type{}, std::false_type{});
+    for (; t + 2 < T; t += 2) {
+      iter(t, P1{}, T_{}, T_{});
+      iter(t + 1, P0{}, T_{}, T_{});
+    }
+    if (t + 1 < T) {
+      iter(t, P1{}, T_{}, T_{});
+      iter(t + 1, P0{}, T_{}, F_{});
+    } else {
+      iter(t, P1{}, T_{}, F_{});
+    }
   }
-  if (T > 0) pv((T - 1) & 1, pkold);
+  if (T > 0) {
+    if ((T - 1) & 1) pv(1, PK[1]);
+    else pv(0, PK[0]);
+  }
 
   lsum = sum_halves(lsum);
   if (!qvalid) return;
