@@ -911,9 +911,18 @@ void pddp_dir_mma(LevelArgs a) {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pddp_project(LevelArgs a) {
-  constexpr int LPR = 4;                 // lanes per row
+  // bf16: 8 lanes per row (each load instruction takes whole 128-byte lines)
+  // and two rows per lane group with both rows' loads in flight together;
+  // fp32: 4 lanes per row, one row at a time
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int LPR = BF ? 8 : 4;        // lanes per row
   constexpr int EPL = D / LPR;           // elements per lane
-  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base;
+  constexpr int RPG = BF ? 2 : 1;        // rows per lane group and pass
+  constexpr int RPP = 256 / LPR;         // lane groups per workgroup
+  // Trees in reverse order on odd levels: the trees the previous level read
+  // last are read first, while they are still in the last-level cache.
+  const int ty = (a.level & 1) ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int tree = ty * a.tree_step + a.tree_base;
   const int bh = tree >> 1, tensor = tree & 1;
   const int p0 = blockIdx.x * a.c;
   int off, n, idx;
@@ -930,35 +939,65 @@ __global__ __launch_bounds__(256) void pddp_project(LevelArgs a) {
   const float* svec = tensor == 0 ? a.s + (int64_t)bh * a.N : nullptr;
   uint32_t* keys = a.keys + (int64_t)tree * a.N;
   const int pend = min(a.N, p0 + a.c);
-  for (int pb = p0; pb < pend; pb += 256 / LPR) {
-    const int p = pb + tid / LPR;
-    float acc = 0.0f;
-    int tok = 0;
-    if (p < pend) {
-      tok = perm[p];
-      const T* row = X + (int64_t)tok * D + q * EPL;
-      if constexpr (sizeof(T) == 2) {
+  for (int pb = p0; pb < pend; pb += RPG * RPP) {
+    int tok[RPG];
 #pragma unroll
-        for (int g = 0; g < EPL / 8; ++g) {
-          const u32x4_t v = reinterpret_cast<const u32x4_t*>(row)[g];
-          const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+    for (int k = 0; k < RPG; ++k) {
+      const int p = pb + k * RPP + tid / LPR;
+      tok[k] = p < pend ? perm[p] : -1;
+    }
+    float acc[RPG];
+    float sc[RPG];
+    if constexpr (BF) {
+      u32x4_t v[RPG][EPL / 8];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            acc += bf16_to_f32((uint16_t)(ws[k] & 0xFFFFu)) * ur[g * 8 + 2 * k];
-            acc += bf16_to_f32((uint16_t)(ws[k] >> 16)) * ur[g * 8 + 2 * k + 1];
+      for (int k = 0; k < RPG; ++k) {
+        sc[k] = 1.0f;
+        if (tok[k] >= 0) {
+          const u32x4_t* row = reinterpret_cast<const u32x4_t*>(X + (int64_t)tok[k] * D + q * EPL);
+#pragma unroll
+          for (int g = 0; g < EPL / 8; ++g) v[k][g] = row[g];
+          if (svec) sc[k] = svec[tok[k]];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < RPG; ++k) {
+        acc[k] = 0.0f;
+        if (tok[k] >= 0) {
+#pragma unroll
+          for (int g = 0; g < EPL / 8; ++g) {
+            const uint32_t ws[4] = {v[k][g].x, v[k][g].y, v[k][g].z, v[k][g].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[k] += bf16_to_f32((uint16_t)(ws[e] & 0xFFFFu)) * ur[g * 8 + 2 * e];
+              acc[k] += bf16_to_f32((uint16_t)(ws[e] >> 16)) * ur[g * 8 + 2 * e + 1];
+            }
           }
         }
-      } else {
+      }
+    } else {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc += load_elem(row, e) * ur[e];
+      for (int k = 0; k < RPG; ++k) {
+        acc[k] = 0.0f;
+        sc[k] = 1.0f;
+        if (tok[k] >= 0) {
+          const T* row = X + (int64_t)tok[k] * D + q * EPL;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[k] += load_elem(row, e) * ur[e];
+          if (svec) sc[k] = svec[tok[k]];
+        }
       }
     }
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    if (p < pend && q == 0) {
-      const float score = svec ? svec[tok] * acc : acc;
-      keys[p] = order_key(score);
-      if (a.trace_score) a.trace_score[(int64_t)tree * a.N + p] = score;
+#pragma unroll
+    for (int k = 0; k < RPG; ++k) {
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) acc[k] += __shfl_xor(acc[k], o, 64);
+      const int p = pb + k * RPP + tid / LPR;
+      if (tok[k] >= 0 && q == 0) {
+        const float score = svec ? sc[k] * acc[k] : acc[k];
+        keys[p] = order_key(score);
+        if (a.trace_score) a.trace_score[(int64_t)tree * a.N + p] = score;
+      }
     }
   }
 }
