@@ -5,6 +5,9 @@
 // node subsamples. Second moments and q^T G q run on bf16 MFMA with fp32
 // accumulation (G is split into three bf16 terms so q^T G q keeps fp32
 // accuracy); fp32 inputs take a VALU path.
+#include <algorithm>
+#include <type_traits>
+
 #include "kernels.h"
 #include "mfma.h"
 
@@ -257,7 +260,13 @@ __global__ __launch_bounds__(256) void metric_reduce(const float* __restrict__ p
   gs[2 * D * D + e] = lo;
 }
 
-constexpr int kQnormSpan = 1024;   // queries per workgroup of qnorm_bf16
+// queries per workgroup of qnorm_bf16: the fewest that keep every workgroup
+// resident at once (three per CU at its register count), whole 32-query tiles
+int qnorm_span(int N, int BH) {
+  const int per_head = std::max(1, 768 / BH);
+  const int span = (N + per_head - 1) / per_head;
+  return (span + 31) / 32 * 32;
+}
 
 // s_i = (q_i^T G q_i)^{-1/2} (0 if q^T G q <= 0). Y^T = G Q^T on the matrix
 // cores with G as hi + mid + lo bf16 terms held as A operands for the block's
@@ -265,7 +274,7 @@ constexpr int kQnormSpan = 1024;   // queries per workgroup of qnorm_bf16
 // then t_i = sum_n Y^T[n][i] q_i[n] from the accumulator rows. Wave w computes
 // rows [32 (w % NB), +32) of Y^T for query group w / NB of each tile.
 template <int D>
-__global__ __launch_bounds__(256) void qnorm_bf16(const uint16_t* __restrict__ Q, int N,
+__global__ __launch_bounds__(256) void qnorm_bf16(const uint16_t* __restrict__ Q, int N, int span,
                                                   const uint16_t* __restrict__ gsplit,
                                                   float* __restrict__ s_out) {
   constexpr int NB = D / 32;                 // 32-row blocks of Y^T
@@ -281,26 +290,29 @@ __global__ __launch_bounds__(256) void qnorm_bf16(const uint16_t* __restrict__ Q
   const int bn = w % NB, qg = w / NB;
   const uint16_t* Qh = Q + (int64_t)bh * N * D;
   const uint16_t* G = gsplit + (int64_t)bh * 3 * D * D;
-  const int q0 = blockIdx.x * kQnormSpan;
-  const int qend = min(N, q0 + kQnormSpan);
+  const int q0 = blockIdx.x * span;
+  const int qend = min(N, q0 + span);
 
-  u32x4_t st[PPT];
-  auto load_tile = [&](int t0) {
+  // register staging of two tiles: tile t + 1 is stored to LDS while tile t
+  // is in the matrix cores, and tile t + 3 is requested in its place
+  u32x4_t st[2][PPT];
+  auto load_tile = [&](u32x4_t (&dst)[PPT], int t0) {
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
       const int idx = tid + 256 * k, row = idx / (D / 8), pc = idx % (D / 8);
-      st[k] = u32x4_t{0u, 0u, 0u, 0u};
-      if (t0 + row < qend) st[k] = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)(t0 + row) * D + 8 * pc);
+      dst[k] = u32x4_t{0u, 0u, 0u, 0u};
+      if (t0 + row < qend) dst[k] = *reinterpret_cast<const u32x4_t*>(Qh + (int64_t)(t0 + row) * D + 8 * pc);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](const u32x4_t (&src)[PPT], int buf) {
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
       const int idx = tid + 256 * k, row = idx / (D / 8), pc = idx % (D / 8);
-      *reinterpret_cast<u32x4_t*>(&sq[buf][row][8 * pc]) = st[k];
+      *reinterpret_cast<u32x4_t*>(&sq[buf][row][8 * pc]) = src[k];
     }
   };
-  load_tile(q0);
+  load_tile(st[0], q0);
+  if (q0 + TILE < qend) load_tile(st[1], q0 + TILE);
   // A operands: rows [32 bn, 32 bn + 32) of the three parts of G
   bf16x8_t ga[3][KS];
 #pragma unroll
@@ -309,12 +321,12 @@ __global__ __launch_bounds__(256) void qnorm_bf16(const uint16_t* __restrict__ Q
     for (int s = 0; s < KS; ++s)
       ga[p][s] = *reinterpret_cast<const bf16x8_t*>(G + (int64_t)p * D * D +
                                                     (int64_t)(32 * bn + r) * D + 16 * s + 8 * h);
-  store_tile(0);
+  store_tile(st[0], 0);
+  if (q0 + 2 * TILE < qend) load_tile(st[0], q0 + 2 * TILE);
   __syncthreads();
-  int buf = 0;
-  for (int t0 = q0; t0 < qend; t0 += TILE) {
-    const bool more = t0 + TILE < qend;
-    if (more) load_tile(t0 + TILE);
+  // one tile: Y^T block on the matrix cores, t_i, then the next tile's store
+  auto step = [&](int t0, auto parity) __attribute__((always_inline)) {
+    constexpr int buf = decltype(parity)::value;
     floatx16_t y = zero16();
     const uint16_t* qrow = &sq[buf][32 * qg + r][0];
 #pragma unroll
@@ -335,7 +347,12 @@ __global__ __launch_bounds__(256) void qnorm_bf16(const uint16_t* __restrict__ Q
     }
     tp = sum_halves(tp);
     if (h == 0) tred[buf][bn][32 * qg + r] = tp;
-    if (more) store_tile(buf ^ 1);
+    // tile t + 1 (staged in slot buf ^ 1) into the other LDS buffer, and
+    // tile t + 3 requested into that slot
+    if (t0 + TILE < qend) {
+      store_tile(st[buf ^ 1], buf ^ 1);
+      if (t0 + 3 * TILE < qend) load_tile(st[buf ^ 1], t0 + 3 * TILE);
+    }
     __syncthreads();
     if (tid < TILE && t0 + tid < qend) {
       float t = 0.0f;
@@ -343,7 +360,10 @@ __global__ __launch_bounds__(256) void qnorm_bf16(const uint16_t* __restrict__ Q
       for (int b = 0; b < NB; ++b) t += tred[buf][b][tid];
       s_out[(int64_t)bh * N + t0 + tid] = t > 0.0f ? 1.0f / sqrtf(t) : 0.0f;
     }
-    buf ^= 1;
+  };
+  for (int t0 = q0; t0 < qend; t0 += 2 * TILE) {
+    step(t0, std::integral_constant<int, 0>{});
+    if (t0 + TILE < qend) step(t0 + TILE, std::integral_constant<int, 1>{});
   }
 }
 
@@ -378,10 +398,10 @@ __global__ void fill_f32(float* p, int64_t n, float v) {
 }  // namespace
 
 int metric_rows_per_chunk(int N, int BH) {
-  // about 384 chunks over all heads (768 workgroups with the two tensors,
-  // three per CU), at least 256 rows each,
-  // a multiple of the 64-token tile
-  const int64_t want = (384 + BH - 1) / BH;
+  // as many chunks as keep every workgroup of the pass resident at once (two
+  // per CU at the bf16 kernel's register count: 512 workgroups with the two
+  // tensors), at least 256 rows each, a multiple of the 128-token tile
+  const int64_t want = std::max<int64_t>(1, 256 / BH);
   const int64_t most = ((int64_t)N + 255) / 256;
   const int64_t chunks = want < most ? want : most;
   const int64_t rows = ((int64_t)N + chunks - 1) / chunks;
@@ -438,9 +458,10 @@ void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D
     return;
   }
   if (dtype == 0) {
-    dim3 gq((N + kQnormSpan - 1) / kQnormSpan, BH);
-    if (D == 64) qnorm_bf16<64><<<gq, 256, 0, st>>>((const uint16_t*)Q, N, gsplit, s);
-    else qnorm_bf16<128><<<gq, 256, 0, st>>>((const uint16_t*)Q, N, gsplit, s);
+    const int span = qnorm_span(N, BH);
+    dim3 gq((N + span - 1) / span, BH);
+    if (D == 64) qnorm_bf16<64><<<gq, 256, 0, st>>>((const uint16_t*)Q, N, span, gsplit, s);
+    else qnorm_bf16<128><<<gq, 256, 0, st>>>((const uint16_t*)Q, N, span, gsplit, s);
   } else {
     dim3 gq((N + 255) / 256, BH);
     if (D == 64) qnorm_f32<float, 64><<<gq, 256, 0, st>>>((const float*)Q, N, Mk, transform, s);
