@@ -890,16 +890,25 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
       return uniform_ptr(a.vt + (((int64_t)bh * nc + max(j, 0)) * SUB + t % SUB) * (int64_t)D * KT);
     return uniform_ptr(a.vbar_t + ((int64_t)bh * (ncp / KT) + (t - Tm)) * D * KT);
   };
+  // LDS rows keep their 16-byte chunks XOR-swizzled: chunk c of row `row`
+  // sits at position c ^ swz(row), swz(row) = (row / RPB) % CPR with RPB the
+  // rows per 256 bytes (one pass of the 64 four-byte banks). The 16 lanes that
+  // one ds_read_b128 pass serves read rows r .. r + 15 at one chunk, and hit
+  // 16 distinct 16-byte bank groups.
+  constexpr int RPBK = 256 / KROW > 0 ? 256 / KROW : 1, RPBV = 256 / VROW > 0 ? 256 / VROW : 1;
+  auto swz_k = [](int row) { return (row / RPBK) % CPRK; };
+  auto swz_v = [](int row) { return (row / RPBV) % CPRV; };
   // per-lane source offsets of this wave's transfers: LDS chunk q = 64 (i NW + w) + l
-  // holds row q / CPR, source chunk (q % CPR) ^ (row % CPR). Transfer i is
+  // holds row q / CPR, source chunk (q % CPR) ^ swz(row). Transfer i is
   // transfer 0 moved by 1024 NW bytes at both ends: 64 NW chunks are a whole
-  // number of rows, and a multiple of CPR rows (row % CPR does not change).
-  static_assert((64 * NW) % (CPRK * CPRK) == 0 && (64 * NW) % (CPRV * CPRV) == 0, "transfer stride");
+  // number of rows, and swz does not change over that many rows.
+  static_assert((64 * NW / CPRK) % (RPBK * CPRK) == 0 && (64 * NW / CPRV) % (RPBV * CPRV) == 0,
+                "transfer stride");
   uint32_t koff, voff;
   {
     const int q = 64 * w + l;
-    koff = (q / CPRK) * KROW + ((q % CPRK) ^ ((q / CPRK) % CPRK)) * 16;
-    voff = (q / CPRV) * VROW + ((q % CPRV) ^ ((q / CPRV) % CPRV)) * 16;
+    koff = (q / CPRK) * KROW + ((q % CPRK) ^ swz_k(q / CPRK)) * 16;
+    voff = (q / CPRV) * VROW + ((q % CPRV) ^ swz_v(q / CPRV)) * 16;
   }
   const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds0 + 1024 * w);
   auto load_k = [&](int t, int slot) {
@@ -909,17 +918,19 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
   };
   // per-lane operand read offsets: K row 32 kb + r chunk 2 s + h; V^T row 32 nb + r chunk 2 q + h
   // (LDS addresses: the slot and block offsets of a read are then immediates)
-  // K: chunk (2 s + h) ^ x of row r, x = r % CPRK, is at byte
+  // K: chunk (2 s + h) ^ x of row r, x = swz_k(r), is at byte
   // 32 (s ^ (x >> 1)) + 16 (h ^ (x & 1)) of the row: kbase + (32 s ^ kx).
   // The per-read XOR (one v_xad with the add) replaces eight address
   // registers that would be loop-invariant and, at this register budget,
-  // spilled.
-  const uint32_t kbase = lds0 + r * KROW + 16 * (h ^ (r & 1));
-  const uint32_t kx = 32 * ((r % CPRK) >> 1);
+  // spilled. (Rows 32 kb + r have the swizzle of row r: 32 is a multiple of
+  // RPB * CPR.)
+  static_assert(32 % (RPBK * CPRK) == 0 && 32 % (RPBV * CPRV) == 0, "block rows keep the swizzle");
+  const uint32_t kbase = lds0 + r * KROW + 16 * (h ^ (swz_k(r) & 1));
+  const uint32_t kx = 32 * (swz_k(r) >> 1);
   auto kro_at = [&](uint32_t kxv, int s) -> uint32_t { return kbase + ((32u * s) ^ kxv); };
   uint32_t vro[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) vro[q] = lds0 + 2 * KBUF + r * VROW + (((2 * q + h) ^ (r % CPRV)) * 16);
+  for (int q = 0; q < 4; ++q) vro[q] = lds0 + 2 * KBUF + r * VROW + (((2 * q + h) ^ swz_v(r)) * 16);
   auto lds16 = [](uint32_t addr) -> bf16x8_t {
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>((uintptr_t)addr);
   };
