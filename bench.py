@@ -573,7 +573,9 @@ def run_workload(args, wname, torch, synth, ca, dev, steps, warmup, full=True):
                      "step_p90": round(float(np.percentile(step_ms, 90)), 4),
                      "graph_replay": round(graph_ms, 4) if graph_ms is not None else None},
         "roofline": {
-            "kernel": "attn_fwd (block-sparse attention + SMC)",
+            "kernel": ("attn_fwd2 (pipelined block-sparse attention + SMC)"
+                       if not fp8 and w.dtype == "bf16" and cq in (128, 256)
+                       else "attn_fwd (block-sparse attention + SMC)"),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": round(peak, 1),
