@@ -421,7 +421,7 @@ def run_workload(args, wname, torch, synth, ca, dev, steps, warmup, full=True):
             if kev is not None:
                 ca.profile_events(kev[0].handle, kev[1].handle)
         O = ca.attend(Q, K, V, cr.perm_q, cr.perm_k, cq, blocks, compensate=w.compensate,
-                      nsel=nsel, c_k=c, fp8=fp8, workspace=ws_a)
+                      nsel=nsel, c_k=c, fp8=fp8, kv_shared=kv_share, workspace=ws_a)
         if evs:
             if kev is not None:
                 ca.profile_events(None, None)

@@ -77,7 +77,7 @@ def load() -> ctypes.CDLL:
     lib.ca_attend.restype = I
     lib.ca_attend_var.argtypes = [P, P, P, I, I, I, I, I, P, P, I, P, P, I, I, F, P, P, P, S, P]
     lib.ca_attend_var.restype = I
-    lib.ca_attend_ex.argtypes = [P, P, P, I, I, I, I, I, I, P, P, I, I, P, P, I, I, F, P, P, P, S, P]
+    lib.ca_attend_ex.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, I, I, P, P, I, I, F, P, P, P, S, P]
     lib.ca_attend_ex.restype = I
     lib.ca_dense.argtypes = [P, P, P, I, I, I, I, I, F, P, P, P, S, P]
     lib.ca_dense.restype = I
@@ -350,13 +350,16 @@ def _attn_dtype(Q, fp8) -> int:
 
 def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
            scale: float = 0.0, return_lse: bool = False, nsel=None, c_k: int = 0,
-           fp8=False, workspace=None):
+           fp8=False, kv_shared: bool = False, workspace=None):
     """ca_attend: block-sparse attention with optional mean-compensation;
     with `nsel` (selected count per row of `blocks`), ca_attend_var; with key
     clusters of another size c_k than the query clusters' c, or K and V with
     fewer heads than Q (grouped- or multi-query attention), ca_attend_ex;
-    fp8=True (or "qk"): the Q.K^T product on FP8 (E4M3) operands (dtype
-    CA_BF16_FP8); fp8="qkpv": P.V on FP8 operands too (CA_BF16_FP8_PV)."""
+    kv_shared=True (with fewer K/V heads): perm_k's rows are identical within
+    each group of query heads (cluster(..., kv_share=True)), so the key tiles
+    are built once per group; fp8=True (or "qk"): the Q.K^T product on FP8
+    (E4M3) operands (dtype CA_BF16_FP8); fp8="qkpv": P.V on FP8 operands too
+    (CA_BF16_FP8_PV)."""
     torch = _torch()
     _bhnd(Q, K, V)
     dt = _attn_dtype(Q, fp8)
@@ -370,8 +373,9 @@ def attend(Q, K, V, perm_q, perm_k, c: int, blocks, *, compensate: bool = True,
     nbytes = workspace_size(OP_ATTEND, B, H, N, D, ck, topk)
     ws = _ws(nbytes, dev, workspace)
     if ck != c or kvh:
-        st = load().ca_attend_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, kvh, N,
-                                 D, perm_q.data_ptr(), perm_k.data_ptr(), c, ck, blocks.data_ptr(),
+        st = load().ca_attend_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, kvh,
+                                 int(bool(kv_shared)), N, D, perm_q.data_ptr(), perm_k.data_ptr(),
+                                 c, ck, blocks.data_ptr(),
                                  _ptr(nsel), topk, int(compensate), float(scale), O.data_ptr(),
                                  _ptr(lse), _ptr(ws), nbytes, _stream_ptr(dev))
     elif nsel is None:

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void permute_kv(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sv[RB][D + 8];
   __shared__ float sk[256 / D][D], sm[256 / D][D];
   __shared__ uint32_t samax[4];
-  const int j = blockIdx.x, bh = blockIdx.y;
+  const int j = blockIdx.x, bh = blockIdx.y * (a.kshare > 1 ? a.kshare : 1);   // heads that build tiles
   const int c = a.c, nc = a.nc, ncp = attn_ncp(nc);
   const int tid = threadIdx.x;
   if (j >= nc) {
@@ -230,7 +230,7 @@ template <int D>
 __global__ __launch_bounds__(256) void quant_centroids(AttnArgs a) {
   constexpr int RB = 64, CPR = D / 8, LPT = RB * CPR / 256;
   __shared__ uint32_t samax[4];
-  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int blk = blockIdx.x, bh = blockIdx.y * (a.kshare > 1 ? a.kshare : 1), tid = threadIdx.x;
   const int ncp = attn_ncp(a.nc);
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.kbar_hi + ((int64_t)bh * ncp + blk * RB) * D);
   uint8_t* dst = a.kbar8 + ((int64_t)bh * ncp + blk * RB) * D;
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void quant_centroids(AttnArgs a) {
 // sub-tiles) as FP8 value sub-tiles; one workgroup per 64 centroids.
 template <int D>
 __global__ __launch_bounds__(256) void quant_vcentroids(AttnArgs a) {
-  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int blk = blockIdx.x, bh = blockIdx.y * (a.kshare > 1 ? a.kshare : 1), tid = threadIdx.x;
   const int ncp = attn_ncp(a.nc);
   const uint16_t* src = a.vbar_t + ((int64_t)bh * (ncp / 64) + blk) * D * 64;
   uint8_t* dst = a.vbar8 + ((int64_t)bh * (ncp / 64) + blk) * vt8_bytes<D>();
@@ -325,6 +325,7 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
   const int lg = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, G);
   const int nc = a.nc, nqc = a.nqc, N = a.N;   // key clusters, query clusters
   const int qa = lg % nqc, bh = lg / nqc;
+  const int bt = attn_kt(a, bh);   // the head whose key tiles and centroids bh reads
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
   const int qg = w % (CQ / 32);                                             // query group
   const int kh = KSPL == 1 ? 0 : __builtin_amdgcn_readfirstlane(w / (CQ / 32));   // key half
@@ -420,29 +421,29 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
       int j = tile_cluster(t);
       if (j < 0) j = 0;   // any valid tile; its results are not used
       const int part = t % SUB;
-      const int64_t row = ((int64_t)bh * nc + j) * CK + part * TL::KT;
+      const int64_t row = ((int64_t)bt * nc + j) * CK + part * TL::KT;
       if constexpr (FP8) {
         ks = reinterpret_cast<const u32x4_t*>(a.kc8 + row * D);
-        ksc_nxt = a.kscale[((int64_t)bh * nc + j) * SUB + part];
+        ksc_nxt = a.kscale[((int64_t)bt * nc + j) * SUB + part];
       } else {
         ks = reinterpret_cast<const u32x4_t*>(a.kc + row * D);
       }
       if constexpr (FP8PV)
-        vs = reinterpret_cast<const u32x4_t*>(a.vt8 + (((int64_t)bh * nc + j) * SUB + part) * vt8_bytes<D>());
+        vs = reinterpret_cast<const u32x4_t*>(a.vt8 + (((int64_t)bt * nc + j) * SUB + part) * vt8_bytes<D>());
       else
-        vs = reinterpret_cast<const u32x4_t*>(a.vt + (((int64_t)bh * nc + j) * SUB + part) * (int64_t)D * TL::KT);
+        vs = reinterpret_cast<const u32x4_t*>(a.vt + (((int64_t)bt * nc + j) * SUB + part) * (int64_t)D * TL::KT);
     } else {
       const int ct = t - Tm;
       if constexpr (FP8) {
-        ks = reinterpret_cast<const u32x4_t*>(a.kbar8 + ((int64_t)bh * ncp + ct * TL::KT) * D);
-        ksc_nxt = a.kbscale[(int64_t)bh * (ncp / TL::KT) + ct];
+        ks = reinterpret_cast<const u32x4_t*>(a.kbar8 + ((int64_t)bt * ncp + ct * TL::KT) * D);
+        ksc_nxt = a.kbscale[(int64_t)bt * (ncp / TL::KT) + ct];
       } else {
-        ks = reinterpret_cast<const u32x4_t*>(a.kbar_hi + ((int64_t)bh * ncp + ct * TL::KT) * D);
+        ks = reinterpret_cast<const u32x4_t*>(a.kbar_hi + ((int64_t)bt * ncp + ct * TL::KT) * D);
       }
       if constexpr (FP8PV)
-        vs = reinterpret_cast<const u32x4_t*>(a.vbar8 + ((int64_t)bh * (ncp / TL::KT) + ct) * vt8_bytes<D>());
+        vs = reinterpret_cast<const u32x4_t*>(a.vbar8 + ((int64_t)bt * (ncp / TL::KT) + ct) * vt8_bytes<D>());
       else
-        vs = reinterpret_cast<const u32x4_t*>(a.vbar_t + ((int64_t)bh * (ncp / TL::KT) + ct) * D * TL::KT);
+        vs = reinterpret_cast<const u32x4_t*>(a.vbar_t + ((int64_t)bt * (ncp / TL::KT) + ct) * D * TL::KT);
     }
 #pragma unroll
     for (int i = 0; i < KLPT; ++i)
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(2 * CQ * KSPL) __attribute__((amdgpu_waves_per_eu(2
   // row r, chunk h
   const int kread = r * TL::KP + h * (FP8 ? 32 : 16);
   const int vread = TL::K_BYTES + r * TL::VP + h * (FP8PV ? 32 : 16);
-  const float* logn = a.logn + (int64_t)bh * ncp;
+  const float* logn = a.logn + (int64_t)bt * ncp;
 
   if (T > 0) {
     fetch(0);
@@ -821,6 +822,7 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int lg = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, G);
   const int nc = a.nc, nqc = a.nqc, N = a.N;
   const int qa = lg % nqc, bh = lg / nqc;
+  const int bt = attn_kt(a, bh);   // the head whose key tiles and centroids bh reads
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
   const int qpos = qa * CQ + w * 32 + r;
   const bool qvalid = qpos < N;
@@ -853,7 +855,7 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int e = tid; e < ncache; e += NT) sBlk[e] = blk[e];
     if (comp) {
       // bias of centroid c: ln n_c (log2 units) if c is not selected, else -inf
-      const float* logn = a.logn + (int64_t)bh * ncp;
+      const float* logn = a.logn + (int64_t)bt * ncp;
       for (int e = tid; e < ncp; e += NT) sBias[e] = logn[e] * kLog2e;
       __syncthreads();
       for (int e = tid; e < nsel; e += NT) {
@@ -882,13 +884,13 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
   };
   auto k_src = [&](int t, int j) -> const unsigned char* {
     if (t < Tm)
-      return uniform_ptr(a.kc + (((int64_t)bh * nc + max(j, 0)) * CK + (t % SUB) * KT) * D);
-    return uniform_ptr(a.kbar_hi + ((int64_t)bh * ncp + (t - Tm) * KT) * D);
+      return uniform_ptr(a.kc + (((int64_t)bt * nc + max(j, 0)) * CK + (t % SUB) * KT) * D);
+    return uniform_ptr(a.kbar_hi + ((int64_t)bt * ncp + (t - Tm) * KT) * D);
   };
   auto v_src = [&](int t, int j) -> const unsigned char* {
     if (t < Tm)
-      return uniform_ptr(a.vt + (((int64_t)bh * nc + max(j, 0)) * SUB + t % SUB) * (int64_t)D * KT);
-    return uniform_ptr(a.vbar_t + ((int64_t)bh * (ncp / KT) + (t - Tm)) * D * KT);
+      return uniform_ptr(a.vt + (((int64_t)bt * nc + max(j, 0)) * SUB + t % SUB) * (int64_t)D * KT);
+    return uniform_ptr(a.vbar_t + ((int64_t)bt * (ncp / KT) + (t - Tm)) * D * KT);
   };
   // LDS rows keep their 16-byte chunks XOR-swizzled: chunk c of row `row`
   // sits at position c ^ swz(row), swz(row) = (row / RPB) % CPR with RPB the
@@ -1185,7 +1187,7 @@ constexpr size_t attn_smem() {
 
 template <int D>
 __global__ __launch_bounds__(256) void centroids_kv_f32(AttnArgs a) {
-  const int j = blockIdx.x, bh = blockIdx.y;
+  const int j = blockIdx.x, bh = blockIdx.y * (a.kshare > 1 ? a.kshare : 1);   // heads that build tiles
   const int ncp = attn_ncp(a.nc);
   const int d = threadIdx.x;
   if (d >= D) return;
@@ -1216,6 +1218,7 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
   __shared__ float skv[2][32][D];
   __shared__ uint32_t sSel[8192 / 32];
   const int qa = blockIdx.x, bh = blockIdx.y;
+  const int bt = attn_kt(a, bh);   // the head whose key clusters and centroids bh reads
   const int N = a.N, nc = a.nc, c = a.c, cq = a.cq, nqc = a.nqc;
   const int tid = threadIdx.x;
   const int qpos = qa * 256 + tid;                   // DENSE: 256 queries per block
@@ -1257,7 +1260,7 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
         const int rr = e / D, d = e % D;
         if (k0 + rr < kcnt) {
           const int pos = kbeg + k0 + rr;
-          const int tok = DENSE ? pos : clamp_tok(a.perm_k[(int64_t)bh * N + pos], N);
+          const int tok = DENSE ? pos : clamp_tok(a.perm_k[(int64_t)bt * N + pos], N);
           skv[0][rr][d] = Kh[(int64_t)tok * D + d];
           skv[1][rr][d] = Vh[(int64_t)tok * D + d];
         }
@@ -1283,11 +1286,11 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
     __syncthreads();
     for (int j = 0; j < nc; ++j) {
       if ((sSel[j >> 5] >> (j & 31)) & 1u) continue;
-      const float* kb = a.kbar32 + ((int64_t)bh * ncp + j) * D;
-      const float* vb = a.vbar32 + ((int64_t)bh * ncp + j) * D;
+      const float* kb = a.kbar32 + ((int64_t)bt * ncp + j) * D;
+      const float* vb = a.vbar32 + ((int64_t)bt * ncp + j) * D;
       float s = 0.0f;
       for (int d = 0; d < D; ++d) s += q[d] * kb[d];
-      absorb(s * a.scale + a.logn[(int64_t)bh * ncp + j], vb);
+      absorb(s * a.scale + a.logn[(int64_t)bt * ncp + j], vb);
     }
   }
   if (!qvalid) return;
@@ -1321,10 +1324,13 @@ void launch_mfma2(const AttnArgs& a, hipStream_t st) {
 
 template <int D, bool FP8, bool FP8PV>
 void launch_tiles(const AttnArgs& a, bool dense, hipStream_t st) {
-  dim3 gp(attn_ncp(a.nc), a.BH);
+  // tiles of the heads that build them (every head, or each key-sharing
+  // group's first head)
+  const int tile_heads = a.BH / (a.kshare > 1 ? a.kshare : 1);
+  dim3 gp(attn_ncp(a.nc), tile_heads);
   permute_kv<D, FP8, FP8PV><<<gp, 256, 0, st>>>(a);
   if (FP8 && !dense && a.compensate) {
-    dim3 gq(attn_ncp(a.nc) / 64, a.BH);
+    dim3 gq(attn_ncp(a.nc) / 64, tile_heads);
     quant_centroids<D><<<gq, 256, 0, st>>>(a);
     if (FP8PV) quant_vcentroids<D><<<gq, 256, 0, st>>>(a);
   }
@@ -1378,7 +1384,7 @@ void launch_f32(const AttnArgs& a, bool dense, hipStream_t st) {
     if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);
     return;
   }
-  dim3 gc(attn_ncp(a.nc), a.BH);
+  dim3 gc(attn_ncp(a.nc), a.BH / (a.kshare > 1 ? a.kshare : 1));   // the centroid-building heads
   centroids_kv_f32<D><<<gc, 256, 0, st>>>(a);
   dim3 g(a.nqc, a.BH);
   if (a.ev_start) (void)hipEventRecord(a.ev_start, st);

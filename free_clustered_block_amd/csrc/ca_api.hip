@@ -388,7 +388,7 @@ int ca_route_adaptive(const float* cent_q, const float* cent_k, const int32_t* c
 
 namespace {
 int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H,
-                int kv_heads, int N, int D, const int32_t* perm_q, const int32_t* perm_k,
+                int kv_heads, int kv_shared, int N, int D, const int32_t* perm_q, const int32_t* perm_k,
                 int cluster_size_q,
                 int cluster_size_k, const int32_t* blocks, const int32_t* nsel, int topk,
                 int compensate, float scale, void* O, float* lse, void* ws, size_t ws_bytes,
@@ -411,9 +411,11 @@ int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B,
   if (!(scale >= 0.0f) || !std::isfinite(scale)) return fail(CA_ERR_INVALID_ARG, "scale must be finite and >= 0");
   if (kv_heads < 1 || kv_heads > H || H % kv_heads != 0)
     return fail(CA_ERR_INVALID_ARG, "kv_heads must divide H");
+  if (kv_shared != 0 && kv_shared != 1) return fail(CA_ERR_INVALID_ARG, "kv_shared must be 0 or 1");
   AttnArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.dtype = attn_dtype(dt);
   a.kvg = H / kv_heads;
+  a.kshare = kv_shared ? a.kvg : 1;
   a.BH = B * H; a.N = N; a.D = D; a.c = c; a.nc = nc; a.cq = cq; a.nqc = nqc; a.topk = topk;
   a.compensate = compensate ? 1 : 0;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
@@ -431,7 +433,7 @@ int ca_attend(const void* Q, const void* K, const void* V, ca_dtype dt, int B, i
               const int32_t* perm_q, const int32_t* perm_k, int cluster_size,
               const int32_t* blocks, int topk, int compensate, float scale, void* O, float* lse,
               void* ws, size_t ws_bytes, void* stream) {
-  return attend_impl(Q, K, V, dt, B, H, H, N, D, perm_q, perm_k, cluster_size, cluster_size, blocks,
+  return attend_impl(Q, K, V, dt, B, H, H, 0, N, D, perm_q, perm_k, cluster_size, cluster_size, blocks,
                      nullptr, topk, compensate, scale, O, lse, ws, ws_bytes, stream);
 }
 
@@ -443,17 +445,17 @@ int ca_attend_var(const void* Q, const void* K, const void* V, ca_dtype dt, int 
     set_error("");
     return fail(CA_ERR_INVALID_ARG, "null tensor pointer");
   }
-  return attend_impl(Q, K, V, dt, B, H, H, N, D, perm_q, perm_k, cluster_size, cluster_size, blocks,
+  return attend_impl(Q, K, V, dt, B, H, H, 0, N, D, perm_q, perm_k, cluster_size, cluster_size, blocks,
                      nsel, max_sel, compensate, scale, O, lse, ws, ws_bytes, stream);
 }
 
 int ca_attend_ex(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H,
-                 int kv_heads, int N, int D, const int32_t* perm_q, const int32_t* perm_k,
-                 int cluster_size_q, int cluster_size_k, const int32_t* blocks,
-                 const int32_t* nsel, int max_sel, int compensate, float scale, void* O,
-                 float* lse, void* ws, size_t ws_bytes, void* stream) {
+                 int kv_heads, int kv_shared, int N, int D, const int32_t* perm_q,
+                 const int32_t* perm_k, int cluster_size_q, int cluster_size_k,
+                 const int32_t* blocks, const int32_t* nsel, int max_sel, int compensate,
+                 float scale, void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
   set_error("");
-  return attend_impl(Q, K, V, dt, B, H, kv_heads ? kv_heads : H, N, D, perm_q, perm_k,
+  return attend_impl(Q, K, V, dt, B, H, kv_heads ? kv_heads : H, kv_shared, N, D, perm_q, perm_k,
                      cluster_size_q, cluster_size_k, blocks, nsel, max_sel, compensate, scale, O,
                      lse, ws, ws_bytes, stream);
 }
@@ -467,7 +469,7 @@ int ca_dense(const void* Q, const void* K, const void* V, ca_dtype dt, int B, in
   AttnArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.dtype = attn_dtype(dt);
   a.BH = B * H; a.N = N; a.D = D; a.c = kDenseTile; a.nc = (N + kDenseTile - 1) / kDenseTile;
-  a.cq = a.c; a.nqc = a.nc; a.kvg = 1;
+  a.cq = a.c; a.nqc = a.nc; a.kvg = 1; a.kshare = 1;
   a.topk = a.nc; a.compensate = 0;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
   a.O = O; a.lse = lse;

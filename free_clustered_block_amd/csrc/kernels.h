@@ -104,6 +104,9 @@ struct AttnArgs {
   int dtype;   // 0 bf16, 1 fp32, 2 bf16 with FP8 (e4m3) Q.K^T operands, 3 FP8 Q.K^T and P.V
   int BH, N, D, c, nc, topk, compensate;   // c, nc: key cluster size and count
   int kvg;                                 // query heads per key/value head (K, V rows of head bh / kvg)
+  int kshare;                              // query heads sharing one key clustering: the key
+                                           // tiles and centroids of head bh are those built
+                                           // for head kt(bh) = (bh / kshare) * kshare (1: own)
   int cq, nqc;                             // query cluster size and count
   float scale;
   const int32_t* perm_q;
@@ -135,6 +138,8 @@ struct AttnArgs {
 };
 // centroid count padded to whole 64-centroid sub-tiles
 CA_HD int attn_ncp(int nc) { return (nc + 63) / 64 * 64; }
+// head whose key tiles and centroids head bh reads
+CA_HD int attn_kt(const AttnArgs& a, int bh) { return a.kshare > 1 ? bh / a.kshare * a.kshare : bh; }
 void launch_attend(const AttnArgs& a, hipStream_t st);
 
 // peak.hip -------------------------------------------------------------------

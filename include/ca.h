@@ -140,7 +140,8 @@ typedef enum {
  *                   of the group's first query head, and its permutation,
  *                   centroids and counts are written to every query head of
  *                   the group (identical rows), so routing and attention are
- *                   called as before.
+ *                   called as before (ca_attend_ex with kv_shared = 1 then
+ *                   builds the key tiles once per group).
  */
 typedef struct {
   int transform;
@@ -323,6 +324,13 @@ int ca_attend_var(const void* Q, const void* K, const void* V, ca_dtype dt, int 
  *           h / (H / kv_heads) (grouped- or multi-query attention; perm_k and
  *           blocks stay per query head, as ca_cluster with the same kv_heads
  *           produces them). CA_ERR_INVALID_ARG if kv_heads does not divide H.
+ * kv_shared 0, or 1 when perm_k's rows are identical within each group of
+ *           H / kv_heads query heads (ca_cluster with kv_share = 1 produces
+ *           that; v1 §6.2 "Extension beyond MHA"): the cluster-major key and
+ *           value tiles and the centroids are then built once per group, from
+ *           the group's first head, and every head of the group reads them.
+ *           The output is that of kv_shared = 0 on the same inputs.
+ *           CA_ERR_INVALID_ARG for other values.
  * perm_q    int32 [B,H,N], clusters of cluster_size_q (n_qc = ceil(N/c_q)).
  * perm_k    int32 [B,H,N], clusters of cluster_size_k (n_kc = ceil(N/c_k)).
  * cluster_size_q <= cluster_size_k, both in {64, 128, 256}.
@@ -335,7 +343,7 @@ int ca_attend_var(const void* Q, const void* K, const void* V, ca_dtype dt, int 
  * size above the key cluster size.
  */
 int ca_attend_ex(const void* Q, const void* K, const void* V, ca_dtype dt, int B, int H,
-                 int kv_heads, int N, int D, const int32_t* perm_q, const int32_t* perm_k,
+                 int kv_heads, int kv_shared, int N, int D, const int32_t* perm_q, const int32_t* perm_k,
                  int cluster_size_q, int cluster_size_k, const int32_t* blocks,
                  const int32_t* nsel, int max_sel, int compensate, float scale, void* O,
                  float* lse, void* ws, size_t ws_bytes, void* stream);

@@ -203,12 +203,15 @@ def test_kv_heads_rejected_unless_dividing_h(lib):
     assert _cluster(lib, H=4, opts=ctypes.byref(opts)) == 1
     assert b"kv_share" in lib.ca_last_error()
     ex = lib.ca_attend_ex
-    # Q, K, V, dt, B, H, kv_heads, N, D, perm_q, perm_k, c_q, c_k, blocks, nsel, max_sel, comp,
-    # scale, O, lse, ws, ws_bytes, stream
-    assert ex(FAKE, FAKE, FAKE, 0, 1, 4, 3, 1024, 64, FAKE, FAKE, 64, 64, FAKE, None, 4, 1, 0.0,
+    # Q, K, V, dt, B, H, kv_heads, kv_shared, N, D, perm_q, perm_k, c_q, c_k, blocks, nsel,
+    # max_sel, comp, scale, O, lse, ws, ws_bytes, stream
+    assert ex(FAKE, FAKE, FAKE, 0, 1, 4, 3, 0, 1024, 64, FAKE, FAKE, 64, 64, FAKE, None, 4, 1, 0.0,
               FAKE, None, FAKE, 1 << 30, None) == 1
     assert b"kv_heads" in lib.ca_last_error()
-    assert ex(FAKE, FAKE, FAKE, 0, 1, 4, 2, 1024, 64, FAKE, FAKE, 64, 64, FAKE, None, 4, 1, 0.0,
+    assert ex(FAKE, FAKE, FAKE, 0, 1, 4, 2, 2, 1024, 64, FAKE, FAKE, 64, 64, FAKE, None, 4, 1, 0.0,
+              FAKE, None, FAKE, 1 << 30, None) == 1
+    assert b"kv_shared" in lib.ca_last_error()
+    assert ex(FAKE, FAKE, FAKE, 0, 1, 4, 2, 1, 1024, 64, FAKE, FAKE, 64, 64, FAKE, None, 4, 1, 0.0,
               FAKE, None, FAKE, 10, None) == 3
 
 

@@ -131,3 +131,28 @@ def test_shared_key_clustering(ca, split_mode):
                                    ("kv_share", h))
             print(f"shared key clusters, head {h}: agreement with the oracle {ag:.5f}, "
                   f"largest tie distance {worst:.2e} IQR")
+
+
+@pytest.mark.parametrize("fp8", [False, True, "qkpv"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_attend_kv_shared_equals_per_head(ca, name, fp8):
+    """ca_attend_ex with kv_shared = 1 on a shared key clustering (every head
+    of a group holds the same perm_k rows) builds the key tiles once per
+    group and must give, bit for bit, the output and LSE of kv_shared = 0 on
+    the same inputs (bf16 with query clusters of 128 and of 64, FP8 Q.K^T,
+    FP8 P.V, fp32)."""
+    import torch
+    w, Q, K, V, G, dt, cq, ck = _inputs(name)
+    if fp8 and dt != "bf16":
+        pytest.skip("FP8 attention takes bf16 inputs")
+    if fp8 == "qkpv" and cq < 128:
+        pytest.skip("FP8 P.V needs query clusters of 128 or 256")
+    tq, tk, tv = _dev(Q, dt), _dev(K, dt), _dev(V, dt)
+    cr = ca.cluster(tq, tk, cq, seed=w.cluster_seed, cluster_size_k=ck if ck != cq else 0,
+                    kv_share=True)
+    blocks = ca.route(cr.cent_q, cr.cent_k, 4)
+    for comp in (True, False):
+        kw = dict(compensate=comp, return_lse=True, fp8=fp8, c_k=ck)
+        O, L = ca.attend(tq, tk, tv, cr.perm_q, cr.perm_k, cq, blocks, kv_shared=True, **kw)
+        Or, Lr = ca.attend(tq, tk, tv, cr.perm_q, cr.perm_k, cq, blocks, **kw)
+        assert torch.equal(O, Or) and torch.equal(L, Lr), (name, fp8, comp)
