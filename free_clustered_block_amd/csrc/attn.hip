@@ -947,15 +947,6 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
       s2[i & 1] = mfma32(kv, qf[i >> 1], s2[i & 1]);
     }
   };
-  // O^T += V^T P^T of the sub-tile in V slot `slot`, weights pk
-  auto pv = [&](int slot, const bf16x8_t (&pk)[4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4 * NB; ++i) {
-      const int nb = i % NB, q = i / NB;
-      const bf16x8_t vv = lds16(vro[q] + slot * VBUF + nb * 32 * VROW);
-      acc[nb] = mfma32(vv, pk[q], acc[nb]);
-    }
-  };
   // the short last cluster's sub-tiles need key masking
   int rpos = -1;
   if (N % CK != 0) {
@@ -974,6 +965,7 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
   // cluster's end; centroid tiles: + the bias); returns the factor still to
   // apply (the scale for token tiles, 1 for centroid tiles).
   auto logits = [&](int t, int j, floatx16_t (&s2)[2]) __attribute__((always_inline)) -> float {
+    if (t >= T) return sl2;   // a skipped drain sub-tile
     if (t >= Tm) {
       const int c0 = (t - Tm) * KT;
 #pragma unroll
@@ -1008,9 +1000,17 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
   // ahead so that the region waits for no LDS read of its own
   auto cl = [&](int t) -> int { return t < Tm ? tile_cluster(t) : 0; };
   int jc0 = cl(0), jc1 = cl(1), jc2 = cl(2);
-  // prologue: K of sub-tiles 0 and 1, Q.K^T of sub-tile 0
-  if (T > 0) load_k(0, 0);
-  if (T > 1) load_k(1, 1);
+  const int jc_last = T > 0 ? cl(T - 1) : 0;
+  // prologue: K of sub-tiles 0 and 1, Q.K^T of sub-tile 0; zero weights and
+  // a zeroed V^T slot 1 for the P.V products of iteration 0
+  if (T > 0) {
+    load_k(0, 0);
+    load_k(T > 1 ? 1 : 0, 1);   // finite data in slot 1 even for a single sub-tile
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) PK[1][q] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+  for (int e = tid; e < VBUF / 16; e += NT)
+    *reinterpret_cast<u32x4_t*>(smem + 2 * KBUF + VBUF + 16 * e) = u32x4_t{0u, 0u, 0u, 0u};
   __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
   __syncthreads();
   if (T > 0) qk(0, S[0]);
@@ -1027,12 +1027,13 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
     floatx16_t (&snext)[2] = S[P ^ 1];
     const bf16x8_t (&pkold)[4] = PK[P ^ 1];
     bf16x8_t (&pk)[4] = PK[P];
-    const bool skip = jc0 < 0;
+    const bool skip = t >= T || jc0 < 0;
     // transfers of this iteration (issued inside the region below): V^T of
     // sub-tile t into V slot P and K of sub-tile t + 2 into K slot P. Past
-    // the last sub-tile the K transfer repeats V^T's 16 KB source (K slot P
-    // is not read again), which keeps the region free of branches.
-    const unsigned char* vsrc = v_src(t, jc0);
+    // the last sub-tile both repeat the last V^T tile's 16 KB source (the
+    // slots are read again only by products whose results are discarded or
+    // multiplied by zero weights), which keeps the region free of branches.
+    const unsigned char* vsrc = t < T ? v_src(t, jc0) : v_src(T - 1, max(jc_last, 0));
     const unsigned char* ksrc = t + 2 < T ? k_src(t + 2, jc2) : vsrc;
     const float skipoff = skip ? kNegInf : 0.0f;   // uniform: no branch in the region
     const float scl = logits(t, jc0, scur);
@@ -1131,30 +1132,22 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
     __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this iteration's transfers
     __syncthreads();
   };
-  using F_ = std::false_type;
+  // Iterations t = 0 .. T: every one runs the whole pipeline. Iteration 0's
+  // P.V products multiply zero weights with a zeroed V^T slot; sub-tiles from
+  // T on are skipped (weight 0) and their Q.K^T products discarded, so
+  // iteration T only completes the P.V products of T - 1 (and one more
+  // padding iteration follows when T is odd). With no remainder variants of
+  // the iteration every value stays in registers.
   using T_ = std::true_type;
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  if (T == 1) {
-    iter(0, P0{}, F_{}, F_{});
-  } else if (T > 1) {
-    iter(0, P0{}, F_{}, T_{});
-    int t = 1;
+  if (T > 0) {
+    iter(0, P0{}, T_{}, T_{});
 #pragma unroll 1
-    for (; t + 2 < T; t += 2) {
+    for (int t = 1; t <= T; t += 2) {
       iter(t, P1{}, T_{}, T_{});
       iter(t + 1, P0{}, T_{}, T_{});
     }
-    if (t + 1 < T) {
-      iter(t, P1{}, T_{}, T_{});
-      iter(t + 1, P0{}, T_{}, F_{});
-    } else {
-      iter(t, P1{}, T_{}, F_{});
-    }
-  }
-  if (T > 0) {
-    if ((T - 1) & 1) pv(1, PK[1]);
-    else pv(0, PK[0]);
   }
 
   lsum = sum_halves(lsum);
