@@ -37,8 +37,8 @@ CA_DEV uint64_t hash_word(uint32_t j, uint32_t w) { return (uint64_t)w * kHashPo
 
 // One workgroup per (chunk of rows, head, tensor): tiles of 128 tokens are
 // read one round trip ahead as token pairs, stored transposed in LDS and fed
-// to the matrix cores; the row hashes come from the same registers, the key
-// sums from the transposed tile (one dimension per thread).
+// to the matrix cores; the row hashes and the key sums come from the same
+// registers.
 template <int D>
 __global__ __launch_bounds__(256) void metric_partial_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int N, int rows_per_chunk,
@@ -59,9 +59,7 @@ __global__ __launch_bounds__(256) void metric_partial_bf16(
   const int r1 = min(N, r0 + rows_per_chunk);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
   // thread (tp, gi): tokens 2 tp, 2 tp + 1 of each tile, groups gi + GI k
-  // (gi is the wave index when a wave holds TP threads: uniform, so the hash
-  // powers below are scalar loads into SGPRs)
-  const int tp = tid % TP, gi = TP == 64 ? __builtin_amdgcn_readfirstlane(tid / TP) : tid / TP;
+  const int tp = tid % TP, gi = tid / TP;
   const uint16_t* X = t == 0 ? Q + (int64_t)bh * N * D : K + (int64_t)(bh / kvg) * N * D;
   uint64_t hpow[GPT][4];
 #pragma unroll
@@ -72,7 +70,11 @@ __global__ __launch_bounds__(256) void metric_partial_bf16(
   floatx16_t acc[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) acc[i] = zero16();
-  float ksum = 0.0f;   // key sums: thread d < D sums dimension d over the transposed tiles
+  float ksum[GPT][8];
+#pragma unroll
+  for (int k = 0; k < GPT; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ksum[k][e] = 0.0f;
 
   u32x4_t pre[GPT][2];
   auto fetch = [&](int base) {
@@ -100,24 +102,16 @@ __global__ __launch_bounds__(256) void metric_partial_bf16(
         // dims 8g + 2q (low halves) and 8g + 2q + 1 (high halves) of the two tokens
         *reinterpret_cast<uint32_t*>(&sx[8 * g + 2 * q][2 * tp]) = (a0[q] & 0xFFFFu) | (a1[q] << 16);
         *reinterpret_cast<uint32_t*>(&sx[8 * g + 2 * q + 1][2 * tp]) = (a0[q] >> 16) | (a1[q] & 0xFFFF0000u);
+        if (t == 1) {
+          ksum[k][2 * q] += bf16_to_f32((uint16_t)(a0[q] & 0xFFFFu)) + bf16_to_f32((uint16_t)(a1[q] & 0xFFFFu));
+          ksum[k][2 * q + 1] += bf16_to_f32((uint16_t)(a0[q] >> 16)) + bf16_to_f32((uint16_t)(a1[q] >> 16));
+        }
       }
     }
     shash[gi][2 * tp] = hp0;
     shash[gi][2 * tp + 1] = hp1;
     __syncthreads();
     if (base + TT < r1) fetch(base + TT);   // next tile in flight during the products
-    if (t == 1 && tid < D) {
-      // dimension tid over the tile's tokens (rows past r1 are zero)
-      const uint16_t* row = &sx[tid][0];
-#pragma unroll
-      for (int g = 0; g < TT / 8; ++g) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + 8 * g);
-        const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          ksum += bf16_to_f32((uint16_t)(ws[e] & 0xFFFFu)) + bf16_to_f32((uint16_t)(ws[e] >> 16));
-      }
-    }
     if (tid < TT && base + tid < r1) {
       uint64_t s = 0;
 #pragma unroll
@@ -145,7 +139,18 @@ __global__ __launch_bounds__(256) void metric_partial_bf16(
     for (int e = 0; e < 16; ++e)
       out[t * D * D + (bm * 32 + c_row(e, h)) * D + bn * 32 + r] = acc[i][e];
   }
-  if (t == 1 && tid < D) out[2 * D * D + tid] = ksum;
+  if (t == 1) {
+    // key sums: the TP token-pair lanes of a group (fixed butterfly order)
+#pragma unroll
+    for (int k = 0; k < GPT; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = ksum[k][e];
+#pragma unroll
+        for (int o = 1; o < TP; o <<= 1) v += __shfl_xor(v, o, 64);
+        if (tp == 0) out[2 * D * D + 8 * (gi + GI * k) + e] = v;
+      }
+  }
 }
 
 template <typename T, int D>
@@ -393,10 +398,10 @@ __global__ void fill_f32(float* p, int64_t n, float v) {
 }  // namespace
 
 int metric_rows_per_chunk(int N, int BH) {
-  // as many chunks as keep every workgroup of the pass resident at once (three
-  // per CU at the bf16 kernel's register count: 768 workgroups with the two
+  // as many chunks as keep every workgroup of the pass resident at once (two
+  // per CU at the bf16 kernel's register count: 512 workgroups with the two
   // tensors), at least 256 rows each, a multiple of the 128-token tile
-  const int64_t want = std::max<int64_t>(1, 384 / BH);
+  const int64_t want = std::max<int64_t>(1, 256 / BH);
   const int64_t most = ((int64_t)N + 255) / 256;
   const int64_t chunks = want < most ? want : most;
   const int64_t rows = ((int64_t)N + chunks - 1) / chunks;
