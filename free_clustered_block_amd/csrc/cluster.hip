@@ -1006,8 +1006,8 @@ __global__ __launch_bounds__(256) void pddp_project(LevelArgs a) {
 // Radix select + stable partition of every splitting node; leaves are copied.
 // ----------------------------------------------------------------------------
 
-constexpr int kSplitThreads = 512;
-constexpr int kSplitWaves = kSplitThreads / 64;
+constexpr int kSplitThreads = 512;          // threads per node below the top levels
+constexpr int kSplitThreadsTop = 1024;      // threads per node at the two top levels
 constexpr int kSplitCacheMax = 32768;        // keys kept in LDS at most (128 KiB)
 
 CA_DEV int wave_sum_int(int v) {
@@ -1019,10 +1019,12 @@ CA_DEV int wave_sum_int(int v) {
 // Split of one node: the members are ordered by (key, position), strictly;
 // the first t go left and the rest right, both keeping position order (a
 // stable partition). The token's content hash moves with it.
-__global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
+template <int NT>
+__global__ __launch_bounds__(NT) void pddp_split(LevelArgs a) {
+  constexpr int NW = NT / 64;
   extern __shared__ __attribute__((aligned(16))) uint32_t skeys[];   // a.split_cache keys
-  __shared__ int hist[kSplitWaves][256];
-  __shared__ int wtot[2][kSplitWaves];
+  __shared__ int hist[NW][256];
+  __shared__ int wtot[2][NW];
   __shared__ uint32_t sel[4];
 
   const int tree = (int)blockIdx.y * a.tree_step + a.tree_base, slot = blockIdx.x;
@@ -1042,7 +1044,7 @@ __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
     // leaf: copied once, by the slot whose remaining path bits are all zero
     const int below = a.level - depth;
     if (below > 0 && (slot & ((1 << below) - 1)) != 0) return;
-    for (int i = tid; i < m; i += kSplitThreads) {
+    for (int i = tid; i < m; i += NT) {
       pout[o + i] = pin[o + i];
       hout[o + i] = hin[o + i];
     }
@@ -1057,11 +1059,26 @@ __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
   // to every key and would put every member in one bucket)
   const bool cached = n <= a.split_cache;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int i = tid; i < n; i += kSplitThreads) {
-    const uint32_t k = gkeys[i];
-    if (cached) skeys[i] = k;
-    kmin = min(kmin, k);
-    kmax = max(kmax, k);
+  {
+    // LB loads in flight per thread (one round trip per LB keys, not per key)
+    constexpr int LB = 16;
+    for (int i0 = tid; i0 < n; i0 += LB * NT) {
+      uint32_t kv[LB];
+#pragma unroll
+      for (int b = 0; b < LB; ++b) {
+        const int i = i0 + b * NT;
+        kv[b] = i < n ? gkeys[i] : 0u;
+      }
+#pragma unroll
+      for (int b = 0; b < LB; ++b) {
+        const int i = i0 + b * NT;
+        if (i < n) {
+          if (cached) skeys[i] = kv[b];
+          kmin = min(kmin, kv[b]);
+          kmax = max(kmax, kv[b]);
+        }
+      }
+    }
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
@@ -1072,7 +1089,7 @@ __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
   __syncthreads();
   kmin = (uint32_t)wtot[0][0];
   kmax = (uint32_t)wtot[1][0];
-  for (int q = 1; q < kSplitWaves; ++q) {
+  for (int q = 1; q < NW; ++q) {
     kmin = min(kmin, (uint32_t)wtot[0][q]);
     kmax = max(kmax, (uint32_t)wtot[1][q]);
   }
@@ -1087,10 +1104,10 @@ __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
     const uint32_t dmask = (2u << (hi - lo)) - 1u;
     const uint32_t hmask = hi == 31 ? 0u : (0xFFFFFFFFu << (hi + 1));
     __syncthreads();   // the previous round's reads of hist and sel are done
-    for (int i = tid; i < kSplitWaves * 256; i += kSplitThreads) (&hist[0][0])[i] = 0;
+    for (int i = tid; i < NW * 256; i += NT) (&hist[0][0])[i] = 0;
     __syncthreads();
 #pragma unroll 8
-    for (int i = tid; i < n; i += kSplitThreads) {
+    for (int i = tid; i < n; i += NT) {
       const uint32_t k = key_at(i);
       if ((k & hmask) == (prefix & hmask)) atomicAdd(&hist[w][(k >> lo) & dmask], 1);
     }
@@ -1100,7 +1117,7 @@ __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         int tot = 0;
-        for (int q = 0; q < kSplitWaves; ++q) tot += hist[q][4 * l + j];
+        for (int q = 0; q < NW; ++q) tot += hist[q][4 * l + j];
         v[j] = tot;
         s += tot;
       }
@@ -1133,7 +1150,7 @@ __global__ __launch_bounds__(kSplitThreads) void pddp_split(LevelArgs a) {
   // stable partition: wave w owns a contiguous region of positions; the
   // regions' counts give each wave its starting ranks, then each wave walks
   // its region 64 members at a time with ballot prefixes
-  const int per_w = (n + kSplitWaves - 1) / kSplitWaves;
+  const int per_w = (n + NW - 1) / NW;
   const int r0 = min(n, w * per_w), r1 = min(n, r0 + per_w);
   int cl = 0, ce = 0;
 #pragma unroll 8
@@ -1449,8 +1466,13 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
     LevelArgs ls = a;
     ls.split_cache = std::min(max_split_node(a.N, a.c, a.level), kSplitCacheMax);
     const size_t lds = (size_t)ls.split_cache * 4;
-    CA_MAX_LDS_ONCE(&pddp_split, (size_t)kSplitCacheMax * 4);
-    pddp_split<<<gslots, kSplitThreads, lds, st>>>(ls);
+    if (a.level <= 1) {
+      CA_MAX_LDS_ONCE(&pddp_split<kSplitThreadsTop>, (size_t)kSplitCacheMax * 4);
+      pddp_split<kSplitThreadsTop><<<gslots, kSplitThreadsTop, lds, st>>>(ls);
+    } else {
+      CA_MAX_LDS_ONCE(&pddp_split<kSplitThreads>, (size_t)kSplitCacheMax * 4);
+      pddp_split<kSplitThreads><<<gslots, kSplitThreads, lds, st>>>(ls);
+    }
   }
 }
 
