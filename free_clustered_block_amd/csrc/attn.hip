@@ -802,9 +802,13 @@ Attn2Lds attn2_lds(int nc, int topk, bool comp) {
   return r;
 }
 
-template <int D, int CQ, int CK, bool DENSE>
-__global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd2(AttnArgs a, Attn2Lds lay) {
-  constexpr int NT = 2 * CQ, NW = NT / 64;
+// QS workgroups share a query cluster, each taking CQ / QS of its queries
+// (d = 64 with 256-query clusters: two four-wave workgroups instead of one
+// of eight, so that three of them fit a CU at three waves per SIMD).
+template <int D, int CQ, int CK, bool DENSE, int QS>
+__global__ __launch_bounds__(2 * CQ / QS) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2)))
+void attn_fwd2(AttnArgs a, Attn2Lds lay) {
+  constexpr int NT = 2 * CQ / QS, NW = NT / 64;
   constexpr int KT = 64, KS = D / 16, NB = D / 32, SUB = CK / KT;
   constexpr int KROW = 2 * D, CPRK = KROW / 16;       // K row bytes, 16-byte chunks per row
   constexpr int KBUF = KT * KROW;
@@ -821,10 +825,10 @@ __global__ __launch_bounds__(2 * CQ) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int G = gridDim.x * gridDim.y;
   const int lg = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, G);
   const int nc = a.nc, nqc = a.nqc, N = a.N;
-  const int qa = lg % nqc, bh = lg / nqc;
+  const int qa = lg / QS % nqc, bh = lg / QS / nqc, qpart = lg % QS;
   const int bt = attn_kt(a, bh);   // the head whose key tiles and centroids bh reads
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, r = l & 31;
-  const int qpos = qa * CQ + w * 32 + r;
+  const int qpos = qa * CQ + qpart * (CQ / QS) + w * 32 + r;
   const bool qvalid = qpos < N;
   const int qtok =
       qvalid ? (DENSE || !a.perm_q ? qpos : clamp_tok(a.perm_q[(int64_t)bh * N + qpos], N)) : 0;
@@ -1307,11 +1311,12 @@ void launch_mfma(const AttnArgs& a, hipStream_t st) {
 // bf16 without FP8 operands, query clusters of 128 or 256: the pipelined kernel
 template <int D, int CQ, int CK, bool DENSE>
 void launch_mfma2(const AttnArgs& a, hipStream_t st) {
+  constexpr int QS = (D == 64 && CQ == 256) ? 2 : 1;
   const Attn2Lds lay = attn2_lds<D>(a.nc, DENSE ? 0 : a.topk, !DENSE && a.compensate);
-  CA_MAX_LDS_ONCE((&attn_fwd2<D, CQ, CK, DENSE>), 160 * 1024);
-  dim3 g(a.nqc, a.BH);
+  CA_MAX_LDS_ONCE((&attn_fwd2<D, CQ, CK, DENSE, QS>), 160 * 1024);
+  dim3 g(a.nqc * QS, a.BH);
   if (a.ev_start) (void)hipEventRecord(a.ev_start, st);
-  attn_fwd2<D, CQ, CK, DENSE><<<g, 2 * CQ, (size_t)lay.bytes, st>>>(a, lay);
+  attn_fwd2<D, CQ, CK, DENSE, QS><<<g, 2 * CQ / QS, (size_t)lay.bytes, st>>>(a, lay);
   if (a.ev_stop) (void)hipEventRecord(a.ev_stop, st);
 }
 
