@@ -787,18 +787,21 @@ CA_DEV void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
 // formed once, against the final value.
 //
 // LDS of attn_fwd2 past the K and V double buffers: the selected clusters
-// (up to kBlkCache entries), and with compensation the centroid logit bias
-// (ln n_c in log2 units, -inf for selected or padding clusters).
+// (up to kBlkCache entries), then the key bias rows that the Q.K^T
+// accumulators start from (in units of the raw score q.k): a zero row for
+// whole token sub-tiles, one row per sub-tile of the last, short cluster
+// (0, or -inf past its end), and with compensation the centroid bias
+// (ln n_c / scale, -inf for selected or padding clusters).
 constexpr int kBlkCache = 1024;
 struct Attn2Lds {
   int blk_off, bias_off, bytes;
 };
 template <int D>
-Attn2Lds attn2_lds(int nc, int topk, bool comp) {
+Attn2Lds attn2_lds(int nc, int topk, bool comp, int sub) {
   Attn2Lds r;
   r.blk_off = 2 * (64 * 2 * D) + 2 * (D * 2 * 64);
-  r.bias_off = r.blk_off + 4 * std::min(topk, kBlkCache);
-  r.bytes = r.bias_off + (comp ? 4 * attn_ncp(nc) : 0);
+  r.bias_off = (r.blk_off + 4 * std::min(topk, kBlkCache) + 15) / 16 * 16;
+  r.bytes = r.bias_off + 4 * 64 * (1 + sub) + (comp ? 4 * attn_ncp(nc) : 0);
   return r;
 }
 
@@ -819,7 +822,8 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int* sBlk = reinterpret_cast<int*>(smem + lay.blk_off);
   const __attribute__((address_space(3))) int* sBlkL = (const __attribute__((address_space(3))) int*)sBlk;
-  float* sBias = reinterpret_cast<float*>(smem + lay.bias_off);
+  float* sKB = reinterpret_cast<float*>(smem + lay.bias_off);   // key bias rows
+  float* sBias = sKB + 64 * (1 + SUB);                           // centroid bias
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int G = gridDim.x * gridDim.y;
@@ -858,17 +862,28 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
   if (!DENSE) {
     for (int e = tid; e < ncache; e += NT) sBlk[e] = blk[e];
     if (comp) {
-      // bias of centroid c: ln n_c (log2 units) if c is not selected, else -inf
+      // bias of centroid c: ln n_c / scale if c is not selected, else -inf
+      // (the logit scale * (q.kbar_c + bias) is then scale q.kbar_c + ln n_c)
       const float* logn = a.logn + (int64_t)bt * ncp;
-      for (int e = tid; e < ncp; e += NT) sBias[e] = logn[e] * kLog2e;
+      const float inv_scale = 1.0f / a.scale;
+      for (int e = tid; e < ncp; e += NT) sBias[e] = logn[e] * inv_scale;
       __syncthreads();
       for (int e = tid; e < nsel; e += NT) {
         const int j = blk[e];
         if (j >= 0 && j < nc) sBias[j] = kNegInf;
       }
     }
-    __syncthreads();
   }
+  {
+    // the zero row, and the rows of the last cluster's sub-tiles: key k of
+    // sub-tile u is past the cluster's end when k >= its valid count
+    const int last_valid = N - (nc - 1) * CK;   // members of the last cluster
+    for (int e = tid; e < 64 * (1 + SUB); e += NT) {
+      const int u = e / 64 - 1, k = e % 64;
+      sKB[e] = (u < 0 || k < last_valid - u * KT) ? 0.0f : kNegInf;
+    }
+  }
+  __syncthreads();
 
   // cluster of token sub-tile t, uniform (-1: an out-of-range entry, skipped)
   auto tile_cluster = [&](int t) -> int {
@@ -941,18 +956,39 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>((uintptr_t)addr);
   };
 
-  // Q.K^T of the sub-tile in K slot `slot` into s2 (two 32-key blocks)
-  auto qk = [&](int slot, floatx16_t (&s2)[2]) __attribute__((always_inline)) {
-    s2[0] = zero16();
-    s2[1] = zero16();
+  // accumulator start of sub-tile u's logits: its key bias row (uniform
+  // offset in floats into the rows; rpos is set below, before any call)
+  int rpos = -1;
+  auto kb_row = [&](int u) -> int {
+    if (u >= T) return 0;
+    if (u >= Tm) return 64 * (1 + SUB) + (u - Tm) * KT;
+    if (rpos >= 0 && u / SUB == rpos) return 64 * (1 + u % SUB);
+    return 0;
+  };
+  auto kb_init = [&](int u, floatx16_t (&s2)[2]) __attribute__((always_inline)) {
+    const __attribute__((address_space(3))) float* row =
+        (const __attribute__((address_space(3))) float*)sKB + kb_row(u);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4_t v = *reinterpret_cast<const __attribute__((address_space(3))) floatx4_t*>(
+            row + kb * 32 + 8 * q + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s2[kb][4 * q + e] = v[e];
+      }
+  };
+  // Q.K^T of sub-tile u in K slot `slot` into s2 (two 32-key blocks)
+  auto qk = [&](int u, int slot, floatx16_t (&s2)[2]) __attribute__((always_inline)) {
+    kb_init(u, s2);
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
       const bf16x8_t kv = lds16(kro_at(kx, i >> 1) + slot * KBUF + (i & 1) * 32 * KROW);
       s2[i & 1] = mfma32(kv, qf[i >> 1], s2[i & 1]);
     }
   };
-  // the short last cluster's sub-tiles need key masking
-  int rpos = -1;
+  // the short last cluster's sub-tiles need key masking: rpos is its entry in
+  // the selection (every entry of the dense pass)
   if (N % CK != 0) {
     if (DENSE) {
       rpos = nc - 1;
@@ -965,34 +1001,6 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
       rpos = __builtin_amdgcn_readfirstlane(mine);
     }
   }
-  // Logits of sub-tile t in log2 units (token tiles: masked past the
-  // cluster's end; centroid tiles: + the bias); returns the factor still to
-  // apply (the scale for token tiles, 1 for centroid tiles).
-  auto logits = [&](int t, int j, floatx16_t (&s2)[2]) __attribute__((always_inline)) -> float {
-    if (t >= T) return sl2;   // a skipped drain sub-tile
-    if (t >= Tm) {
-      const int c0 = (t - Tm) * KT;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const floatx4_t bias = *reinterpret_cast<const floatx4_t*>(sBias + c0 + kb * 32 + 8 * q + 4 * h);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s2[kb][4 * q + e] = fmaf(s2[kb][4 * q + e], sl2, bias[e]);
-        }
-      return 1.0f;
-    }
-    if (rpos >= 0 && t / SUB == rpos) {
-      const int nvalid = min(CK, N - j * CK) - (t % SUB) * KT;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          s2[kb][i] = kb * 32 + c_row(i, h) >= nvalid ? kNegInf : s2[kb][i];
-    }
-    return sl2;
-  };
-
   // Logits (two 32-key blocks) and bf16 weights of sub-tile t live in
   // S[t & 1] and PK[t & 1]: with the parity of t known at compile time, each
   // iteration reads one set and writes the other (no copies), and every LDS
@@ -1017,7 +1025,7 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
     *reinterpret_cast<u32x4_t*>(smem + 2 * KBUF + VBUF + 16 * e) = u32x4_t{0u, 0u, 0u, 0u};
   __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
   __syncthreads();
-  if (T > 0) qk(0, S[0]);
+  if (T > 0) qk(0, 0, S[0]);
   __syncthreads();   // every wave has read K slot 0 before it is refilled
 
   // Iteration t (parity P = t & 1): one straight-line region holding the
@@ -1040,7 +1048,7 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
     const unsigned char* vsrc = t < T ? v_src(t, jc0) : v_src(T - 1, max(jc_last, 0));
     const unsigned char* ksrc = t + 2 < T ? k_src(t + 2, jc2) : vsrc;
     const float skipoff = skip ? kNegInf : 0.0f;   // uniform: no branch in the region
-    const float scl = logits(t, jc0, scur);
+    const float scl = sl2;
     // One instruction stream in a fixed order (scheduling barriers between
     // steps): step i issues product i (the 4 NB P.V products of t - 1, then
     // the 2 KS Q.K^T products of t + 1) and the LDS read of product i + PF's
@@ -1063,10 +1071,7 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
       const int k = i - NPV;
       return lds16(kro_at(kxo, k >> 1) + (P ^ 1) * KBUF + (k & 1) * 32 * KROW);
     };
-    if constexpr (QK) {
-      snext[0] = zero16();
-      snext[1] = zero16();
-    }
+    if constexpr (QK) kb_init(t + 1, snext);   // the products of t + 1 accumulate onto it
     bf16x8_t ring[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i)
@@ -1312,7 +1317,7 @@ void launch_mfma(const AttnArgs& a, hipStream_t st) {
 template <int D, int CQ, int CK, bool DENSE>
 void launch_mfma2(const AttnArgs& a, hipStream_t st) {
   constexpr int QS = (D == 64 && CQ == 256) ? 2 : 1;
-  const Attn2Lds lay = attn2_lds<D>(a.nc, DENSE ? 0 : a.topk, !DENSE && a.compensate);
+  const Attn2Lds lay = attn2_lds<D>(a.nc, DENSE ? 0 : a.topk, !DENSE && a.compensate, CK / 64);
   CA_MAX_LDS_ONCE((&attn_fwd2<D, CQ, CK, DENSE, QS>), 160 * 1024);
   dim3 g(a.nqc * QS, a.BH);
   if (a.ev_start) (void)hipEventRecord(a.ev_start, st);

@@ -409,6 +409,8 @@ int attend_impl(const void* Q, const void* K, const void* V, ca_dtype dt, int B,
   if ((int64_t)nqc * B * H > 0x7FFFFFFF / 2) return fail(CA_ERR_UNSUPPORTED, "too many query clusters");
   if (topk < 1 || topk > nc) return fail(CA_ERR_INVALID_ARG, "topk must be in [1, n_kc]");
   if (!(scale >= 0.0f) || !std::isfinite(scale)) return fail(CA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (compensate && scale > 0.0f && scale < 1e-30f)
+    return fail(CA_ERR_INVALID_ARG, "with compensation a positive scale must be >= 1e-30");
   if (kv_heads < 1 || kv_heads > H || H % kv_heads != 0)
     return fail(CA_ERR_INVALID_ARG, "kv_heads must divide H");
   if (kv_shared != 0 && kv_shared != 1) return fail(CA_ERR_INVALID_ARG, "kv_shared must be 0 or 1");

@@ -285,7 +285,9 @@ int ca_route_adaptive(const float* cent_q, const float* cent_k, const int32_t* c
  * compensate  nonzero: every key cluster not selected by a query's cluster
  *           enters the query's softmax once, with logit scale*q.kbar_c +
  *           ln n_c and value vbar_c (centroids of the original K and V rows).
- * scale     softmax temperature; 0 means 1/sqrt(D).
+ * scale     softmax temperature; 0 means 1/sqrt(D). With compensate a
+ *           positive scale must be at least 1e-30 (the centroid term is
+ *           carried as ln n_c / scale inside the score accumulation).
  * O         out [B,H,N,D] of type dt, original token order.
  * lse       out float [B,H,N] or NULL: natural log of the softmax denominator
  *           (the "attention denominator" of v1 §3.1) including the running

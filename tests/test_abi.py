@@ -108,6 +108,7 @@ def test_attend_rejects_bad_arguments(lib):
     assert _attend(lib, topk=17) == 1          # n_c = 16
     assert _attend(lib, scale=-1.0) == 1
     assert _attend(lib, scale=float("nan")) == 1
+    assert _attend(lib, scale=1e-35) == 1          # compensation carries ln n_c / scale
     assert _attend(lib, D=32) == 2
     assert _attend(lib, c=32) == 2
     assert _attend(lib, ws_bytes=10) == 3
