@@ -550,8 +550,12 @@ struct DirMma {
   static constexpr int TOKCAP = 4 * SC;      // sample tokens kept in LDS (whole rounds)
 };
 
-template <int D>
-__global__ __launch_bounds__(DirMma<D>::NT) __attribute__((amdgpu_waves_per_eu(2)))
+// TS: the trees of the launch are query trees only (0), key trees only (1),
+// or both (-1: tensor = tree & 1). Key rows enter the Gram matrix as they
+// are, which needs fewer registers than the three-term query split: the
+// key-only version runs three workgroups per CU.
+template <int D, int TS>
+__global__ __launch_bounds__(DirMma<D>::NT) __attribute__((amdgpu_waves_per_eu(TS == 1 ? 3 : 2)))
 void pddp_dir_mma(LevelArgs a) {
   using Cf = DirMma<D>;
   constexpr int NW = Cf::NW, NT = Cf::NT, RT = Cf::RT, SC = Cf::SC, XP = Cf::XP, RPT = Cf::RPT;
@@ -569,7 +573,8 @@ void pddp_dir_mma(LevelArgs a) {
   extern __shared__ int spre[];              // chunk prefix sums [nch + 1]
 
   const int tree = (int)blockIdx.y * a.tree_step + a.tree_base, slot = blockIdx.x;
-  const int bh = tree >> 1, tensor = tree & 1;
+  const int bh = tree >> 1;
+  const int tensor = TS >= 0 ? TS : (tree & 1);
   int off, n;
   if (!node_at(a.N, a.c, a.level, slot, &off, &n) || n <= a.c) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 31, h = l >> 5;
@@ -769,7 +774,7 @@ void pddp_dir_mma(LevelArgs a) {
     for (int ks = 0; ks < nks; ++ks) {
       const int k0 = 16 * ks + 8 * h;
       const u32x4_t bw = *reinterpret_cast<const u32x4_t*>(&xt[32 * w + r][k0]);
-      if (tensor == 1) {
+      if (TS == 1 || (TS < 0 && tensor == 1)) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const u32x4_t aw = *reinterpret_cast<const u32x4_t*>(&xt[32 * rt + r][k0]);
@@ -1420,6 +1425,8 @@ void launch_perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int
   perm_out<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm_qt, perm_kt, BH, N, kshare, pq, pk);
 }
 
+constexpr int64_t kDirSplitNodes = 2048;   // node slots of a level from which tensors launch apart
+
 template <typename T, int D>
 static void level_impl(const LevelArgs& a, hipStream_t st) {
   // the trees tree_base, tree_base + tree_step, ... below 2 BH
@@ -1439,7 +1446,29 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
   } else if constexpr (sizeof(T) == 2) {
     const int64_t nmax = ((int64_t)a.N >> a.level) + 2 * (int64_t)a.c;   // bounds every node
     const size_t lds = (size_t)((nmax + a.c - 1) / a.c + 2) * 4;
-    pddp_dir_mma<D><<<gslots, DirMma<D>::NT, lds, st>>>(la);
+    // levels with many nodes: one launch per tensor, so that the key trees
+    // run at three workgroups per CU (the trees of a launch alternate between
+    // query and key trees when its step is odd); levels with few nodes: one
+    // launch (two would add a launch latency each)
+    auto dir_launch = [&](const LevelArgs& l) {
+      const int tr = (2 * a.BH - l.tree_base + l.tree_step - 1) / l.tree_step;
+      if (tr <= 0) return;
+      dim3 g(1u << a.level, tr);
+      if ((l.tree_base & 1) == 0) pddp_dir_mma<D, 0><<<g, DirMma<D>::NT, lds, st>>>(l);
+      else pddp_dir_mma<D, 1><<<g, DirMma<D>::NT, lds, st>>>(l);
+    };
+    const bool many = (int64_t)trees << a.level >= kDirSplitNodes;
+    if (!many && la.tree_step % 2 == 1) {
+      pddp_dir_mma<D, -1><<<gslots, DirMma<D>::NT, lds, st>>>(la);
+    } else if (la.tree_step % 2 == 0) {
+      dir_launch(la);
+    } else {
+      LevelArgs l0 = la, l1 = la;
+      l0.tree_step = l1.tree_step = 2 * la.tree_step;
+      l1.tree_base = la.tree_base + la.tree_step;
+      dir_launch(l0);
+      dir_launch(l1);
+    }
   } else {
     const size_t lds = dir_smem<T, D>(a.N, a.c, a.level);
     {   // raise the dynamic-LDS limit when a level needs more (host threads serialised)
