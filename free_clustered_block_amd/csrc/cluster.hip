@@ -538,26 +538,35 @@ CA_DEV void matvec_row_bcast(float (&t4)[4], const floatx4_t& uv, const float* m
    ...);
 }
 
-template <int D>
+template <int D, int SCR = 160>
 struct DirMma {
   static constexpr int NW = D / 32;          // waves; wave w owns columns [32w, 32w + 32)
   static constexpr int NT = 64 * NW;         // threads
   static constexpr int RT = D / 32;          // 32-row tiles of C per column strip
-  static constexpr int SC = 160;             // sample rows per gather round (the sample
+  static constexpr int SC = SCR;             // sample rows per gather round (the sample
                                              // averages a D rows; 160 covers it at +3 sd)
+  static_assert(SC % 32 == 0, "whole row pairs per thread and round");
   static constexpr int RPT = SC / 16;        // rows per thread and round
-  static constexpr int XP = SC + 8;          // padded transposed row (bf16): 336 B apart
+  static constexpr int XP = SC + 8;          // padded transposed row (bf16): 16 k + 4 dwords
+                                             // apart, so 16 lanes' 16-byte reads hit
+                                             // distinct banks
   static constexpr int TOKCAP = 4 * SC;      // sample tokens kept in LDS (whole rounds)
 };
+// Rows per gather round of a launch: the top levels (few nodes, latency bound)
+// take a whole sample in one round; the levels with many nodes, which launch
+// per tensor, gather 128 rows a round, which needs fewer registers in flight,
+// so that three workgroups fit on a CU for query trees as well as key trees.
+template <int TS>
+constexpr int dir_rows_per_round() { return TS == 0 ? 96 : TS == 1 ? 128 : 160; }
 
 // TS: the trees of the launch are query trees only (0), key trees only (1),
 // or both (-1: tensor = tree & 1). Key rows enter the Gram matrix as they
 // are, which needs fewer registers than the three-term query split: the
 // key-only version runs three workgroups per CU.
 template <int D, int TS>
-__global__ __launch_bounds__(DirMma<D>::NT) __attribute__((amdgpu_waves_per_eu(TS == 1 ? 3 : 2)))
+__global__ __launch_bounds__(DirMma<D>::NT) __attribute__((amdgpu_waves_per_eu(TS >= 0 ? 3 : 2)))
 void pddp_dir_mma(LevelArgs a) {
-  using Cf = DirMma<D>;
+  using Cf = DirMma<D, dir_rows_per_round<TS>()>;
   constexpr int NW = Cf::NW, NT = Cf::NT, RT = Cf::RT, SC = Cf::SC, XP = Cf::XP, RPT = Cf::RPT;
   constexpr int TOKCAP = Cf::TOKCAP;
   __shared__ __attribute__((aligned(16))) uint16_t xt[D][XP];
@@ -864,6 +873,14 @@ void pddp_dir_mma(LevelArgs a) {
   const int j16 = (l & 15) < RT * 4 ? (l & 15) : 0;
   const int vsel = 32 * (j16 >> 2) + 8 * (j16 & 3) + 4 * h;
   for (int it = 0;; ++it) {
+    if (it > 0) {
+      float nn = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) nn += nred[(it - 1) & 1][q];
+      if (nn == 0.0f) { fallback = true; break; }
+      inv_norm = 1.0f / sqrtf(nn);
+      if (it == a.power_iters) { last = (it - 1) & 1; break; }
+    }
     const float* usrc = it == 0 ? su0 : vbuf[(it - 1) & 1];
     const floatx4_t uv = *reinterpret_cast<const floatx4_t*>(&usrc[vsel]);
     float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -877,15 +894,7 @@ void pddp_dir_mma(LevelArgs a) {
     }
     float tp = (t4[0] + t4[1]) + (t4[2] + t4[3]);
     tp = sum_halves(tp);
-    if (it > 0) {
-      float nn = 0.0f;
-#pragma unroll
-      for (int q = 0; q < NW; ++q) nn += nred[(it - 1) & 1][q];
-      if (nn == 0.0f) { fallback = true; break; }
-      inv_norm = 1.0f / sqrtf(nn);
-      if (it == a.power_iters) { last = (it - 1) & 1; break; }
-      tp *= inv_norm;
-    }
+    if (it > 0) tp *= inv_norm;
     float vp = tp;
     if (a.transform) {
       if (h == 0) tbuf[32 * w + r] = tp;
