@@ -821,7 +821,6 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
   static_assert(KBUF % (1024 * NW) == 0 && VBUF % (1024 * NW) == 0, "whole transfers per wave");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int* sBlk = reinterpret_cast<int*>(smem + lay.blk_off);
-  const __attribute__((address_space(3))) int* sBlkL = (const __attribute__((address_space(3))) int*)sBlk;
   float* sKB = reinterpret_cast<float*>(smem + lay.bias_off);   // key bias rows
   float* sBias = sKB + 64 * (1 + SUB);                           // centroid bias
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
@@ -885,16 +884,15 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
   }
   __syncthreads();
 
-  // cluster of token sub-tile t, uniform (-1: an out-of-range entry, skipped)
-  auto tile_cluster = [&](int t) -> int {
-    if (DENSE) return t / SUB;
-    const int e = t / SUB;
-    int j;
-    if (e < kBlkCache) j = sBlkL[e];   // an LDS read, not a generic one
-    else j = blk[e];
-    j = __builtin_amdgcn_readfirstlane(j);
-    return (j >= 0 && j < nc) ? j : -1;
-  };
+  // cluster of token sub-tile t, uniform (-1: an out-of-range entry, skipped).
+  // The selection is read-only and its address uniform, so the entry comes
+  // through the scalar cache into a scalar register: no LDS read, no
+  // readfirstlane, and no wait that joins the vector-memory counter.
+  const __attribute__((address_space(4))) int32_t* blk4 =
+      (const __attribute__((address_space(4))) int32_t*)(uintptr_t)(DENSE ? a.blocks : blk);
+  auto valid_cluster = [&](int j) -> int { return (j >= 0 && j < nc) ? j : -1; };
+  auto raw_cluster = [&](int t) -> int { return DENSE ? t / SUB : blk4[t / SUB]; };
+  auto tile_cluster = [&](int t) -> int { return valid_cluster(raw_cluster(t)); };
   auto uniform_ptr = [](const void* p) -> const unsigned char* {
     const uint64_t v = (uint64_t)(uintptr_t)p;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -1007,12 +1005,14 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
   // slot offset is an immediate.
   floatx16_t S[2][2];
   bf16x8_t PK[2][4];
-  // clusters of sub-tiles t, t + 1 and t + 2 (uniform; -1 for a skipped
-  // entry, 0 for centroid sub-tiles and past the end), read one iteration
-  // ahead so that the region waits for no LDS read of its own
-  auto cl = [&](int t) -> int { return t < Tm ? tile_cluster(t) : 0; };
+  // clusters of sub-tiles t, t + 1 and t + 2 (uniform; 0 for centroid
+  // sub-tiles and past the end), read one iteration ahead as they are stored
+  // in the selection and checked where they are used (-1 for an entry out of
+  // range: a skipped sub-tile), so that the scalar load of an iteration's
+  // last entry completes during its transfer wait and barrier
+  auto cl = [&](int t) -> int { return t < Tm ? raw_cluster(t) : 0; };
   int jc0 = cl(0), jc1 = cl(1), jc2 = cl(2);
-  const int jc_last = T > 0 ? cl(T - 1) : 0;
+  const int jc_last = T > 0 ? valid_cluster(cl(T - 1)) : 0;
   // prologue: K of sub-tiles 0 and 1, Q.K^T of sub-tile 0; zero weights and
   // a zeroed V^T slot 1 for the P.V products of iteration 0
   if (T > 0) {
@@ -1039,14 +1039,15 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
     floatx16_t (&snext)[2] = S[P ^ 1];
     const bf16x8_t (&pkold)[4] = PK[P ^ 1];
     bf16x8_t (&pk)[4] = PK[P];
-    const bool skip = t >= T || jc0 < 0;
+    const int j0 = valid_cluster(jc0);
+    const bool skip = t >= T || j0 < 0;
     // transfers of this iteration (issued inside the region below): V^T of
     // sub-tile t into V slot P and K of sub-tile t + 2 into K slot P. Past
     // the last sub-tile both repeat the last V^T tile's 16 KB source (the
     // slots are read again only by products whose results are discarded or
     // multiplied by zero weights), which keeps the region free of branches.
-    const unsigned char* vsrc = t < T ? v_src(t, jc0) : v_src(T - 1, max(jc_last, 0));
-    const unsigned char* ksrc = t + 2 < T ? k_src(t + 2, jc2) : vsrc;
+    const unsigned char* vsrc = t < T ? v_src(t, j0) : v_src(T - 1, max(jc_last, 0));
+    const unsigned char* ksrc = t + 2 < T ? k_src(t + 2, valid_cluster(jc2)) : vsrc;
     const float skipoff = skip ? kNegInf : 0.0f;   // uniform: no branch in the region
     const float scl = sl2;
     // One instruction stream in a fixed order (scheduling barriers between
@@ -1071,11 +1072,14 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
       const int k = i - NPV;
       return lds16(kro_at(kxo, k >> 1) + (P ^ 1) * KBUF + (k & 1) * 32 * KROW);
     };
-    if constexpr (QK) kb_init(t + 1, snext);   // the products of t + 1 accumulate onto it
     bf16x8_t ring[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i)
       if (i < NM) ring[i] = operand(i);
+    // the products of t + 1 accumulate onto the bias row; its reads go after
+    // the first operands (LDS reads return in order, and the Q.K^T products
+    // come after the P.V ones), so the first product waits for its operand only
+    if constexpr (QK) kb_init(t + 1, snext);
     float ps = 0.0f, tv[8], bm = kNegInf, mn = m, nm = 0.0f;
     static_for<NSTEP>([&](auto step) __attribute__((always_inline)) {
       constexpr int i = decltype(step)::value;
