@@ -760,18 +760,16 @@ CA_DEV void static_for(F&& f) {
 // at lds + 16 l; lds is wave-uniform). Written out so that the compiler,
 // which would otherwise wait for the transfer before every later LDS read,
 // leaves the wait to the caller (s_waitcnt vmcnt before the barrier that
-// publishes the buffer). M0 is restored after the issue.
+// publishes the buffer). M0, which holds the LDS address, is declared
+// clobbered: nothing else in the kernels that use this keeps a value in it.
 CA_DEV void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-  uint32_t keep;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
+      "global_load_lds_dwordx4 %0, %1"
+      :
       : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
+      : "memory", "m0");
 }
 
 // Same work as attn_fwd<D, CQ, CK, DENSE, false, 1>, scheduled as a pipeline:
