@@ -19,6 +19,7 @@
 
 #include "kernels.h"
 #include "mfma.h"
+#include "wave_select.h"
 
 namespace ca {
 
@@ -1217,18 +1218,10 @@ __global__ __launch_bounds__(NT) void pddp_split(LevelArgs a) {
 }
 
 // Split of nodes of at most kSmallNode members: one wave per node (four per
-// workgroup), the same radix select and stable partition with wave-wide
-// ballots and a per-wave LDS histogram, no workgroup barriers.
-constexpr int kSmallNode = 1024;
-
-CA_DEV void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+// workgroup), the one-wave selection of wave_select.h; leaves are copied.
+constexpr int kSmallNode = kWaveSelMax;
 
 __global__ __launch_bounds__(256) void pddp_split_small(LevelArgs a) {
-  constexpr int KPL = kSmallNode / 64;   // keys per lane
   __shared__ int hist[4][256];
   const int tree = (int)blockIdx.y * a.tree_step + a.tree_base, w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int slot = blockIdx.x * 4 + w;
@@ -1255,85 +1248,13 @@ __global__ __launch_bounds__(256) void pddp_split_small(LevelArgs a) {
   const int off = o, n = m;   // n <= kSmallNode (checked by the launch)
   const int t = split_size(n, a.c);
   const uint32_t* gkeys = a.keys + (int64_t)tree * a.N + off;
-  uint32_t k[KPL];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-  for (int q = 0; q < KPL; ++q) {
-    const int i = l + 64 * q;
-    k[q] = i < n ? gkeys[i] : 0u;
-    if (i < n) { kmin = min(kmin, k[q]); kmax = max(kmax, k[q]); }
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d, 64));
-  }
-  const uint32_t diff = kmin ^ kmax;
-  const int hb = diff ? 31 - __builtin_clz(diff) : -1;
-  uint32_t prefix = hb < 0 ? kmin : (hb == 31 ? 0u : kmin & (0xFFFFFFFFu << (hb + 1)));
-  int want = t;
-  int* hw = hist[w];
-  for (int hi = hb; hi >= 0;) {
-    const int lo = hi >= 7 ? hi - 7 : 0;
-    const uint32_t dmask = (2u << (hi - lo)) - 1u;
-    const uint32_t hmask = hi == 31 ? 0u : (0xFFFFFFFFu << (hi + 1));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hw[4 * l + j] = 0;
-    wave_sync();
-#pragma unroll
-    for (int q = 0; q < KPL; ++q)
-      if (l + 64 * q < n && (k[q] & hmask) == (prefix & hmask)) atomicAdd(&hw[(k[q] >> lo) & dmask], 1);
-    wave_sync();
-    int v[4], s = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { v[j] = hw[4 * l + j]; s += v[j]; }
-    int inc = s;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(inc, d, 64);
-      if (l >= d) inc += y;
+  wave_select(l, n, t, [&](int i) { return gkeys[i]; }, hist[w], [&](int i, bool left, int lrank) {
+    const int dest = left ? off + lrank : off + t + (i - lrank);
+    if (dest < off + n) {
+      pout[dest] = pin[off + i];
+      hout[dest] = hin[off + i];
     }
-    int before = inc - s, bsel = 0, bbefore = 0;
-    bool mine = false;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (before < want && want <= before + v[j]) { mine = true; bsel = 4 * l + j; bbefore = before; }
-      before += v[j];
-    }
-    const uint64_t owner = __ballot(mine);
-    const int src = owner ? __builtin_ctzll(owner) : 0;   // one lane owns rank `want`
-    bsel = __shfl(bsel, src, 64);
-    bbefore = __shfl(bbefore, src, 64);
-    prefix |= (uint32_t)bsel << lo;
-    want -= bbefore;
-    hi = lo - 1;
-    wave_sync();   // every lane has read the histogram before it is cleared again
-  }
-  const uint32_t kstar = prefix;
-  const int eq_take = want;
-  int erun = 0, lrun = 0;
-#pragma unroll
-  for (int q = 0; q < KPL; ++q) {
-    const int i = l + 64 * q;
-    if (64 * q >= n) break;   // uniform
-    const bool valid = i < n;
-    const bool less = valid && k[q] < kstar;
-    const bool eq = valid && k[q] == kstar;
-    uint64_t bal_e, bal_l;
-    const int eqpre = lane_prefix(eq, &bal_e);
-    const bool left = less || (eq && erun + eqpre < eq_take);
-    const int lpre = lane_prefix(left, &bal_l);
-    const int lrank = lrun + lpre;
-    if (valid) {
-      const int dest = left ? off + lrank : off + t + (i - lrank);
-      if (dest < off + n) {
-        pout[dest] = pin[off + i];
-        hout[dest] = hin[off + i];
-      }
-    }
-    erun += __popcll(bal_e);
-    lrun += __popcll(bal_l);
-  }
+  });
 }
 
 // Largest node that splits at a level (host).

@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include "kernels.h"
+#include "wave_select.h"
 
 namespace ca {
 
@@ -186,6 +187,24 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
   }
 }
 
+// Rows of at most kWaveSelMax key clusters: one wave per (head, query
+// cluster), four per workgroup, the one-wave selection of the k smallest
+// (~order_key(score), index) pairs; the taken indices are visited in
+// ascending order with their rank, which is their output slot.
+__global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ A, int nq, int nk,
+                                                        int k, int32_t* __restrict__ blocks) {
+  __shared__ int hist[4][256];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + w, bh = blockIdx.y;
+  if (row >= nq) return;   // the whole wave
+  const float* a = A + ((int64_t)bh * nq + row) * nk;
+  int32_t* out = blocks + ((int64_t)bh * nq + row) * k;
+  wave_select(l, nk, k, [&](int i) { return ~order_key(a[i]); }, hist[w],
+              [&](int i, bool take, int rank) {
+                if (take && rank < k) out[rank] = i;
+              });
+}
+
 // ----------------------------------------------------------------------------
 // Adaptive selection (v1 §3.3.2 "Selection"; later revision §4.2): per query
 // cluster, the key clusters of highest score until both a minimum count and
@@ -362,8 +381,13 @@ void launch_route(const float* cq, const float* ck, int BH, int nq, int nk, int 
                   float* scores, int32_t* blocks, hipStream_t st) {
   dim3 gs((nk + kTile - 1) / kTile, (nq + kTile - 1) / kTile, BH);
   scores_kernel<<<gs, 256, 0, st>>>(cq, ck, nq, nk, D, scores);
-  dim3 gt(nq, BH);
-  topk_kernel<<<gt, kSelThreads, 0, st>>>(scores, nq, nk, topk, blocks);
+  if (nk <= kWaveSelMax) {
+    dim3 gw((nq + 3) / 4, BH);
+    topk_wave_kernel<<<gw, 256, 0, st>>>(scores, nq, nk, topk, blocks);
+  } else {
+    dim3 gt(nq, BH);
+    topk_kernel<<<gt, kSelThreads, 0, st>>>(scores, nq, nk, topk, blocks);
+  }
 }
 
 }  // namespace ca
