@@ -61,13 +61,27 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ c
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+  // the next d chunk is staged in registers while the current one is in use
+  constexpr int EPT = kTile * kDChunk / 256;   // elements per thread and chunk
+  float ra[EPT], rb[EPT];
+  auto fetch = [&](int d0) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = (int)threadIdx.x + 256 * k, rr = e / kDChunk, dd = e % kDChunk;
+      ra[k] = (i0 + rr < nq) ? Q[(int64_t)(i0 + rr) * D + d0 + dd] : 0.0f;
+      rb[k] = (j0 + rr < nk) ? K[(int64_t)(j0 + rr) * D + d0 + dd] : 0.0f;
+    }
+  };
+  fetch(0);
   for (int d0 = 0; d0 < D; d0 += kDChunk) {
-    for (int e = threadIdx.x; e < kTile * kDChunk; e += 256) {
-      const int rr = e / kDChunk, dd = e % kDChunk;
-      sa[rr][dd] = (i0 + rr < nq) ? Q[(int64_t)(i0 + rr) * D + d0 + dd] : 0.0f;
-      sb[rr][dd] = (j0 + rr < nk) ? K[(int64_t)(j0 + rr) * D + d0 + dd] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = (int)threadIdx.x + 256 * k, rr = e / kDChunk, dd = e % kDChunk;
+      sa[rr][dd] = ra[k];
+      sb[rr][dd] = rb[k];
     }
     __syncthreads();
+    if (d0 + kDChunk < D) fetch(d0 + kDChunk);
 #pragma unroll 8
     for (int dd = 0; dd < kDChunk; ++dd) {
       float av[4], bv[4];
