@@ -555,19 +555,22 @@ struct DirMma {
 };
 // Rows per gather round of a launch: the top levels (few nodes, latency bound)
 // take a whole sample in one round; the levels with many nodes, which launch
-// per tensor, gather 128 rows a round, which needs fewer registers in flight,
-// so that three workgroups fit on a CU for query trees as well as key trees.
-template <int TS>
-constexpr int dir_rows_per_round() { return TS == 0 ? 96 : TS == 1 ? 128 : 160; }
+// per tensor, gather fewer rows a round, which needs fewer registers in
+// flight: at D = 128 three waves per SIMD for query trees as well as key
+// trees (96 and 128 rows), at D = 64 four (64 and 96 rows).
+template <int D, int TS>
+constexpr int dir_rows_per_round() {
+  return TS < 0 ? 160 : D == 64 ? (TS == 0 ? 64 : 96) : (TS == 0 ? 96 : 128);
+}
 
 // TS: the trees of the launch are query trees only (0), key trees only (1),
 // or both (-1: tensor = tree & 1). Key rows enter the Gram matrix as they
 // are, which needs fewer registers than the three-term query split: the
 // key-only version runs three workgroups per CU.
 template <int D, int TS>
-__global__ __launch_bounds__(DirMma<D>::NT) __attribute__((amdgpu_waves_per_eu(TS >= 0 ? 3 : 2)))
+__global__ __launch_bounds__(DirMma<D>::NT) __attribute__((amdgpu_waves_per_eu(TS < 0 ? 2 : D == 64 ? 4 : 3)))
 void pddp_dir_mma(LevelArgs a) {
-  using Cf = DirMma<D, dir_rows_per_round<TS>()>;
+  using Cf = DirMma<D, dir_rows_per_round<D, TS>()>;
   constexpr int NW = Cf::NW, NT = Cf::NT, RT = Cf::RT, SC = Cf::SC, XP = Cf::XP, RPT = Cf::RPT;
   constexpr int TOKCAP = Cf::TOKCAP;
   __shared__ __attribute__((aligned(16))) uint16_t xt[D][XP];
