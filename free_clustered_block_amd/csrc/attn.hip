@@ -927,11 +927,19 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
     koff = (q / CPRK) * KROW + ((q % CPRK) ^ swz_k(q / CPRK)) * 16;
     voff = (q / CPRV) * VROW + ((q % CPRV) ^ swz_v(q / CPRV)) * 16;
   }
+  // transfer i's per-lane source offsets, loop-invariant: the source base
+  // of a sub-tile is then one scalar pair for all of its transfers (no 64-bit
+  // scalar add per transfer)
+  uint32_t koffs[KPW], voffs[VPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) koffs[i] = koff + 1024 * NW * i;
+#pragma unroll
+  for (int i = 0; i < VPW; ++i) voffs[i] = voff + 1024 * NW * i;
   const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds0 + 1024 * w);
   auto load_k = [&](int t, int slot) {
     const unsigned char* src = k_src(t, t < Tm ? tile_cluster(t) : 0);
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) dma16(koff, src + 1024 * NW * i, wlds + slot * KBUF + 1024 * NW * i);
+    for (int i = 0; i < KPW; ++i) dma16(koffs[i], src, wlds + slot * KBUF + 1024 * NW * i);
   };
   // per-lane operand read offsets: K row 32 kb + r chunk 2 s + h; V^T row 32 nb + r chunk 2 q + h
   // (LDS addresses: the slot and block offsets of a read are then immediates)
@@ -1086,8 +1094,8 @@ void attn_fwd2(AttnArgs a, Attn2Lds lay) {
       static_for<VPW + KPW>([&](auto xc) __attribute__((always_inline)) {
         constexpr int x = decltype(xc)::value;
         if constexpr ((x < NSTEP ? x : NSTEP - 1) == i) {
-          if constexpr (x < VPW) dma16(voff, vsrc + 1024 * NW * x, wlds + 2 * KBUF + P * VBUF + 1024 * NW * x);
-          else dma16(koff, ksrc + 1024 * NW * (x - VPW), wlds + P * KBUF + 1024 * NW * (x - VPW));
+          if constexpr (x < VPW) dma16(voffs[x], vsrc, wlds + 2 * KBUF + P * VBUF + 1024 * NW * x);
+          else dma16(koffs[x - VPW], ksrc, wlds + P * KBUF + 1024 * NW * (x - VPW));
         }
       });
       if constexpr (i < NPV) {
