@@ -51,6 +51,7 @@ struct ClusterWs {
   uint16_t* At3;                  // its three-term bf16 split
   int32_t* jsel;                  // chosen coordinate per node
   float* Y;                       // coordinates of every vector (diagonalized only)
+  int32_t* wide;                  // wide split of the large-node levels (or null)
 };
 
 ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c, bool diag) {
@@ -85,6 +86,8 @@ ClusterWs plan_cluster(Carver& cv, int BH, int N, int D, int c, bool diag) {
   w.At3 = cv.take<uint16_t>(T * 3 * D * D);
   w.jsel = cv.take<int32_t>(T * slots);
   w.Y = diag ? cv.take<float>(T * N * D) : nullptr;
+  const size_t ww = wide_split_words(BH, N, c);
+  w.wide = ww ? cv.take<int32_t>(ww) : nullptr;
   return w;
 }
 
@@ -291,7 +294,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
       a.dir_cur = (level & 1) ? w.dirB : w.dirA;
       a.nchunks = (N + ct - 1) / ct;
       a.sample_buf = w.sample; a.chunk_cnt = w.chunk_cnt; a.zbuf_tok = w.stok;
-      a.zbuf = w.zbuf; a.keys = w.keys;
+      a.zbuf = w.zbuf; a.keys = w.keys; a.wide = w.wide;
       a.trace_score = o.trace_score ? o.trace_score + level * TN : nullptr;
       a.trace_slots = L > 0 ? (1 << (L - 1)) : 1;
       a.trace_dir = o.trace_dir ? o.trace_dir + (size_t)level * 2 * BH * a.trace_slots * D : nullptr;

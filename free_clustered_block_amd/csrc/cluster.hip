@@ -1220,6 +1220,287 @@ __global__ __launch_bounds__(NT) void pddp_split(LevelArgs a) {
   }
 }
 
+// ----------------------------------------------------------------------------
+// Wide split of the levels whose nodes are too large for one workgroup to
+// move quickly (a node of 2^18 members read through one CU several times):
+// every node's positions are cut into chunks of kWideChunk, one workgroup per
+// chunk. The same selection as pddp_split (the rank-t key by 8-bit radix
+// digits from the highest bit in which the node's keys differ, position
+// tie-break), with the node's digit histogram summed from per-chunk LDS
+// histograms by integer atomics (exact, order-free) and each digit picked by
+// one small workgroup per node; then per-chunk counts and a stable scatter
+// whose starting ranks are the counts of the node's earlier chunks.
+// Per node the workspace holds: [0] kmin, [1] kmax, [2] prefix, [3] want
+// (rank still to locate), [4] hi (top bit of the next digit, -1 when done),
+// then 256 histogram words; per chunk two counts (less, equal).
+// ----------------------------------------------------------------------------
+
+constexpr int kWideChunk = 4096;               // positions per workgroup
+constexpr int kWideNode = 65536;               // levels whose largest node is this big go wide
+constexpr int kWideSlots = 8;                  // ... and have at most this many node slots
+constexpr int kWideState = 8 + 256;            // words of per-node state
+
+// node of slot `slot` at the level: (o, m, depth) as in the split kernels
+CA_DEV void wide_node(const LevelArgs& a, int slot, int* o, int* m, int* depth) {
+  int oo = 0, mm = a.N, d = 0;
+  for (; d < a.level; ++d) {
+    if (mm <= a.c) break;
+    const int t = split_size(mm, a.c);
+    if ((slot >> (a.level - 1 - d)) & 1) { oo += t; mm -= t; } else { mm = t; }
+  }
+  *o = oo; *m = mm; *depth = d;
+}
+
+CA_DEV int32_t* wide_state(const LevelArgs& a, int tree, int slot) {
+  return a.wide + ((int64_t)tree * kWideSlots + slot) * kWideState;
+}
+CA_DEV int32_t* wide_counts(const LevelArgs& a, int tree, int slot, int chunk) {
+  return a.wide + (int64_t)2 * a.BH * kWideSlots * kWideState +
+         (((int64_t)tree * kWideSlots + slot) * a.wide_cpn + chunk) * 2;
+}
+
+// grid (slots * cpn, trees): per chunk of a splitting node, min and max key
+__global__ __launch_bounds__(256) void wide_minmax(LevelArgs a) {
+  __shared__ uint32_t red[2][4];
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base;
+  const int slot = blockIdx.x / a.wide_cpn, chunk = blockIdx.x % a.wide_cpn;
+  int o, n, depth;
+  wide_node(a, slot, &o, &n, &depth);
+  if (depth < a.level || n <= a.c || chunk * kWideChunk >= n) return;
+  const uint32_t* keys = a.keys + (int64_t)tree * a.N + o;
+  const int i0 = chunk * kWideChunk, i1 = min(n, i0 + kWideChunk);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int i = i0 + tid; i < i1; i += 256) { const uint32_t k = keys[i]; kmin = min(kmin, k); kmax = max(kmax, k); }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d, 64));
+  }
+  if (l == 0) { red[0][w] = kmin; red[1][w] = kmax; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int q = 1; q < 4; ++q) { kmin = min(kmin, red[0][q]); kmax = max(kmax, red[1][q]); }
+    int32_t* st = wide_state(a, tree, slot);
+    atomicMin(reinterpret_cast<unsigned int*>(&st[0]), kmin);
+    atomicMax(reinterpret_cast<unsigned int*>(&st[1]), kmax);
+  }
+}
+
+// grid (slots, trees): state of each splitting node before the first digit
+// (mode 0: reset min/max and histogram; mode 1: digits from the min/max)
+__global__ __launch_bounds__(256) void wide_init(LevelArgs a, int mode) {
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base, slot = blockIdx.x;
+  int o, n, depth;
+  wide_node(a, slot, &o, &n, &depth);
+  if (depth < a.level || n <= a.c) return;
+  int32_t* st = wide_state(a, tree, slot);
+  if (mode == 0) {
+    if (threadIdx.x == 0) { st[0] = (int32_t)0xFFFFFFFFu; st[1] = 0; }
+    for (int i = threadIdx.x; i < 256; i += 256) st[8 + i] = 0;
+    return;
+  }
+  if (threadIdx.x != 0) return;
+  const uint32_t kmin = (uint32_t)st[0], kmax = (uint32_t)st[1];
+  const uint32_t diff = kmin ^ kmax;
+  const int hb = diff ? 31 - __builtin_clz(diff) : -1;   // highest differing bit
+  st[2] = (int32_t)(hb < 0 ? kmin : (hb == 31 ? 0u : kmin & (0xFFFFFFFFu << (hb + 1))));
+  st[3] = split_size(n, a.c);
+  st[4] = hb;
+}
+
+// grid (slots * cpn, trees): the chunk's histogram of the current digit over
+// the keys that share the prefix, added to the node's histogram
+__global__ __launch_bounds__(256) void wide_hist(LevelArgs a) {
+  __shared__ int hist[4][256];
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base;
+  const int slot = blockIdx.x / a.wide_cpn, chunk = blockIdx.x % a.wide_cpn;
+  int o, n, depth;
+  wide_node(a, slot, &o, &n, &depth);
+  if (depth < a.level || n <= a.c || chunk * kWideChunk >= n) return;
+  int32_t* st = wide_state(a, tree, slot);
+  const int hi = st[4];
+  if (hi < 0) return;   // uniform: the node's rank-t key is known
+  const int lo = hi >= 7 ? hi - 7 : 0;
+  const uint32_t dmask = (2u << (hi - lo)) - 1u;
+  const uint32_t hmask = hi == 31 ? 0u : (0xFFFFFFFFu << (hi + 1));
+  const uint32_t prefix = (uint32_t)st[2];
+  const int tid = threadIdx.x, w = tid >> 6;
+  for (int i = tid; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  const uint32_t* keys = a.keys + (int64_t)tree * a.N + o;
+  const int i0 = chunk * kWideChunk, i1 = min(n, i0 + kWideChunk);
+#pragma unroll 4
+  for (int i = i0 + tid; i < i1; i += 256) {
+    const uint32_t k = keys[i];
+    if ((k & hmask) == (prefix & hmask)) atomicAdd(&hist[w][(k >> lo) & dmask], 1);
+  }
+  __syncthreads();
+  const int v = hist[0][tid] + hist[1][tid] + hist[2][tid] + hist[3][tid];
+  if (v) atomicAdd(&st[8 + tid], v);
+}
+
+// grid (slots, trees), 64 threads: the bucket that holds rank `want`, then the
+// next digit; the histogram is cleared for it
+__global__ __launch_bounds__(64) void wide_pick(LevelArgs a) {
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base, slot = blockIdx.x;
+  int o, n, depth;
+  wide_node(a, slot, &o, &n, &depth);
+  if (depth < a.level || n <= a.c) return;
+  int32_t* st = wide_state(a, tree, slot);
+  const int hi = st[4];
+  if (hi < 0) return;
+  const int lo = hi >= 7 ? hi - 7 : 0;
+  const int l = threadIdx.x;
+  const int want = st[3];
+  int v[4], s = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { v[j] = st[8 + 4 * l + j]; s += v[j]; }
+  int inc = s;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d, 64);
+    if (l >= d) inc += y;
+  }
+  int before = inc - s, bsel = 0, bbefore = 0;
+  bool mine = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (before < want && want <= before + v[j]) { mine = true; bsel = 4 * l + j; bbefore = before; }
+    before += v[j];
+  }
+  const uint64_t owner = __ballot(mine);
+  const int src = owner ? __builtin_ctzll(owner) : 0;   // one lane owns rank `want`
+  bsel = __shfl(bsel, src, 64);
+  bbefore = __shfl(bbefore, src, 64);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) st[8 + 4 * l + j] = 0;
+  if (l == 0) {
+    st[2] = (int32_t)((uint32_t)st[2] | ((uint32_t)bsel << lo));
+    st[3] = want - bbefore;
+    st[4] = lo - 1;
+  }
+}
+
+// grid (slots * cpn, trees): members of the chunk below and equal to the
+// node's rank-t key
+__global__ __launch_bounds__(256) void wide_count(LevelArgs a) {
+  __shared__ int red[2][4];
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base;
+  const int slot = blockIdx.x / a.wide_cpn, chunk = blockIdx.x % a.wide_cpn;
+  int o, n, depth;
+  wide_node(a, slot, &o, &n, &depth);
+  if (depth < a.level || n <= a.c || chunk * kWideChunk >= n) return;
+  const uint32_t kstar = (uint32_t)wide_state(a, tree, slot)[2];
+  const uint32_t* keys = a.keys + (int64_t)tree * a.N + o;
+  const int i0 = chunk * kWideChunk, i1 = min(n, i0 + kWideChunk);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  int cl = 0, ce = 0;
+#pragma unroll 4
+  for (int i = i0 + tid; i < i1; i += 256) {
+    const uint32_t k = keys[i];
+    cl += k < kstar;
+    ce += k == kstar;
+  }
+  cl = wave_sum_int(cl);
+  ce = wave_sum_int(ce);
+  if (l == 0) { red[0][w] = cl; red[1][w] = ce; }
+  __syncthreads();
+  if (tid == 0) {
+    int32_t* cc = wide_counts(a, tree, slot, chunk);
+    cc[0] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    cc[1] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  }
+}
+
+// grid (slots * cpn, trees): stable partition of the chunk (wave w walks the
+// chunk's quarter w in steps of 64 with ballot prefixes, starting from the
+// counts of the node's earlier chunks and of the chunk's earlier quarters);
+// the chunks of leaves are copied
+__global__ __launch_bounds__(256) void wide_scatter(LevelArgs a) {
+  __shared__ int wt[2][4];
+  const int tree = (int)blockIdx.y * a.tree_step + a.tree_base;
+  const int slot = blockIdx.x / a.wide_cpn, chunk = blockIdx.x % a.wide_cpn;
+  int o, n, depth;
+  wide_node(a, slot, &o, &n, &depth);
+  const int32_t* pin = a.perm_in + (int64_t)tree * a.N;
+  int32_t* pout = a.perm_out + (int64_t)tree * a.N;
+  const uint64_t* hin = a.hpos_in + (int64_t)tree * a.N;
+  uint64_t* hout = a.hpos_out + (int64_t)tree * a.N;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int i0 = chunk * kWideChunk, i1 = min(n, i0 + kWideChunk);
+  if (depth < a.level || n <= a.c) {
+    // leaf: copied once, by the slot whose remaining path bits are all zero
+    const int below = a.level - depth;
+    if (below > 0 && (slot & ((1 << below) - 1)) != 0) return;
+    for (int i = i0 + tid; i < i1; i += 256) {
+      pout[o + i] = pin[o + i];
+      hout[o + i] = hin[o + i];
+    }
+    return;
+  }
+  if (i0 >= n) return;
+  const int32_t* st = wide_state(a, tree, slot);
+  const uint32_t kstar = (uint32_t)st[2];
+  const int eq_take = st[3];   // members equal to kstar that go left (lowest positions)
+  const int t = split_size(n, a.c);
+  int lb = 0, eb = 0;   // members of the node's earlier chunks below / equal to kstar
+  for (int q = 0; q < chunk; ++q) {
+    const int32_t* cc = wide_counts(a, tree, slot, q);
+    lb += cc[0];
+    eb += cc[1];
+  }
+  const uint32_t* keys = a.keys + (int64_t)tree * a.N + o;
+  const int per_w = kWideChunk / 4;
+  const int r0 = min(i1, i0 + w * per_w), r1 = min(i1, r0 + per_w);
+  int cl = 0, ce = 0;
+  for (int i = r0 + l; i < r1; i += 64) {
+    const uint32_t k = keys[i];
+    cl += k < kstar;
+    ce += k == kstar;
+  }
+  cl = wave_sum_int(cl);
+  ce = wave_sum_int(ce);
+  if (l == 0) { wt[0][w] = cl; wt[1][w] = ce; }
+  __syncthreads();
+  for (int q = 0; q < w; ++q) { lb += wt[0][q]; eb += wt[1][q]; }
+  int erun = eb;                        // equal members before the current step
+  int lrun = lb + min(eb, eq_take);     // left members before the current step
+  constexpr int BATCH = 4;
+  for (int base = r0; base < r1; base += 64 * BATCH) {
+    uint32_t k[BATCH];
+    int pv[BATCH];
+    uint64_t hv[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int i = base + 64 * b + l;
+      k[b] = 0u; pv[b] = 0; hv[b] = 0;
+      if (i < r1) { k[b] = keys[i]; pv[b] = pin[o + i]; hv[b] = hin[o + i]; }
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int i = base + 64 * b + l;
+      const bool valid = i < r1;
+      const bool less = valid && k[b] < kstar;
+      const bool eq = valid && k[b] == kstar;
+      uint64_t bal_e, bal_l;
+      const int eqpre = lane_prefix(eq, &bal_e);
+      const bool left = less || (eq && erun + eqpre < eq_take);
+      const int lpre = lane_prefix(left, &bal_l);
+      const int lrank = lrun + lpre;
+      if (valid) {
+        const int dest = left ? o + lrank : o + t + (i - lrank);
+        if (dest < o + n) {   // holds by construction; guards the slice
+          pout[dest] = pv[b];
+          hout[dest] = hv[b];
+        }
+      }
+      erun += __popcll(bal_e);
+      lrun += __popcll(bal_l);
+    }
+  }
+}
+
 // Split of nodes of at most kSmallNode members: one wave per node (four per
 // workgroup), the one-wave selection of wave_select.h; leaves are copied.
 constexpr int kSmallNode = kWaveSelMax;
@@ -1419,7 +1700,24 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
   dim3 gproj((a.N + a.c - 1) / a.c, trees);
   if (a.split_mode == 1) pddp_project_y<<<gproj, 256, 0, st>>>(a);
   else pddp_project<T, D><<<gproj, 256, 0, st>>>(a);
-  if (max_split_node(a.N, a.c, a.level) <= kSmallNode) {
+  const int maxn = max_split_node(a.N, a.c, a.level);
+  if (a.wide && maxn >= kWideNode && (1 << a.level) <= kWideSlots) {
+    // wide split: every node in chunks of kWideChunk positions
+    LevelArgs lw = a;
+    lw.wide_cpn = (maxn + kWideChunk - 1) / kWideChunk;
+    dim3 gs(1u << a.level, trees), gc((1u << a.level) * lw.wide_cpn, trees);
+    wide_init<<<gs, 256, 0, st>>>(lw, 0);
+    wide_minmax<<<gc, 256, 0, st>>>(lw);
+    wide_init<<<gs, 256, 0, st>>>(lw, 1);
+    for (int r = 0; r < 4; ++r) {   // at most four 8-bit digits; finished nodes skip the rest
+      wide_hist<<<gc, 256, 0, st>>>(lw);
+      wide_pick<<<gs, 64, 0, st>>>(lw);
+    }
+    wide_count<<<gc, 256, 0, st>>>(lw);
+    wide_scatter<<<gc, 256, 0, st>>>(lw);
+    return;
+  }
+  if (maxn <= kSmallNode) {
     dim3 gsmall(((1u << a.level) + 3) / 4, trees);
     pddp_split_small<<<gsmall, 256, 0, st>>>(a);
   } else {
@@ -1436,6 +1734,17 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
       pddp_split<kSplitThreads><<<gslots, kSplitThreads, lds, st>>>(ls);
     }
   }
+}
+
+// Workspace words of the wide split for trees of N tokens (0 if no level of
+// such a tree goes wide).
+size_t wide_split_words(int BH, int N, int c) {
+  const int L = tree_levels_host(N, c);
+  bool any = false;
+  for (int l = 0; l < L && (1 << l) <= kWideSlots; ++l) any |= max_split_node(N, c, l) >= kWideNode;
+  if (!any) return 0;
+  const size_t cpn = ((size_t)N + kWideChunk - 1) / kWideChunk;
+  return 2 * (size_t)BH * kWideSlots * (kWideState + 2 * cpn);
 }
 
 void launch_level(const LevelArgs& a, hipStream_t st) {

@@ -43,6 +43,8 @@ struct LevelArgs {
   int nchunks;              // ceil(N / c)
   int sample_inline;        // set by launch_level: the direction kernel draws the subsample itself
   int split_cache;          // set by launch_level: keys a split workgroup keeps in LDS
+  int32_t* wide;            // wide split of the large-node levels: per-node state, per-chunk counts
+  int wide_cpn;             // set by launch_level: chunks per node of a wide level
   int32_t* sample_buf;      // [2 BH][N]   per-chunk sample lists
   int32_t* chunk_cnt;       // [2 BH][nchunks]
   int32_t* zbuf_tok;        // [2 BH][N]   a node's gathered sample tokens
@@ -53,6 +55,8 @@ struct LevelArgs {
   int trace_slots;
 };
 void launch_level(const LevelArgs& a, hipStream_t st);
+// workspace words (int32) of the wide split of the large-node levels (0: none)
+size_t wide_split_words(int BH, int N, int c);
 
 // basis.hip ------------------------------------------------------------------
 // Principal-component basis of each tree for diagonalized splitting: At
