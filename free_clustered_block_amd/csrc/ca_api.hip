@@ -2,6 +2,7 @@
 // workspace layout and launch sequencing. No call allocates memory or
 // synchronises with the device.
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "ca.h"
@@ -164,6 +165,34 @@ int check_common(int dt, int B, int H, int N, int D, bool fp8_ok = false) {
   return 0;
 }
 
+// The key trees' split levels run on a side stream beside the query trees':
+// at the top levels every direction and split launch is latency-bound and
+// fills few CUs, so each tensor's launches overlap the other's projection.
+// The side stream is forked from the caller's stream and joined back to it
+// by events, so the call stays ordered on the caller's stream (and a graph
+// captured there takes both branches). One side stream per GPU (non-blocking,
+// default priority) and one event pair per host thread and GPU, each created
+// at its first use and kept until the process ends.
+constexpr int kMaxDevices = 64;
+int side_stream(hipStream_t* side, hipEvent_t* fork, hipEvent_t* join) {
+  int dev = 0;
+  CA_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(CA_ERR_UNSUPPORTED, "device index must be < 64");
+  static std::mutex mu;
+  static hipStream_t streams[kMaxDevices] = {};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!streams[dev]) CA_HIP_CHECK(hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking));
+    *side = streams[dev];
+  }
+  thread_local hipEvent_t ev[kMaxDevices][2] = {};
+  for (int i = 0; i < 2; ++i)
+    if (!ev[dev][i]) CA_HIP_CHECK(hipEventCreateWithFlags(&ev[dev][i], hipEventDisableTiming));
+  *fork = ev[dev][0];
+  *join = ev[dev][1];
+  return 0;
+}
+
 }  // namespace
 }  // namespace ca
 
@@ -264,7 +293,13 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   // the split levels of a set of trees (every tree when c_q == c_k, else one
   // tensor's trees at a time with its own cluster size); returns the
   // permutation array that holds their final order in `fin`
-  auto run_levels = [&](int ct, int step, int base, int32_t*& fin) -> int {
+  // per-tree row strides of the level buffers, the same for every level and
+  // both tensors (the workspace's sizes, from the smaller cluster size)
+  const int cmin = c < ck ? c : ck;
+  const int nch_all = (N + cmin - 1) / cmin;
+  const int lmax = tree_levels_host(N, cmin);
+  const int node_slots = lmax > 0 ? 1 << (lmax - 1) : 1;
+  auto run_levels = [&](int ct, int step, int base, int32_t*& fin, hipStream_t rs) -> int {
     const int L = tree_levels_host(N, ct);
     int32_t* cur = w.permA;
     int32_t* nxt = w.permB;
@@ -275,7 +310,7 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     auto trace_copy = [&](int32_t* dst, const int32_t* src) -> int {
       CA_HIP_CHECK(hipMemcpy2DAsync(dst + (size_t)base * N, (size_t)step * N * 4, src + (size_t)base * N,
                                     (size_t)step * N * 4, (size_t)N * 4, ntrees,
-                                    hipMemcpyDeviceToDevice, st));
+                                    hipMemcpyDeviceToDevice, rs));
       return 0;
     };
     for (int level = 0; level < L; ++level) {
@@ -292,13 +327,14 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
       a.hpos_in = hcur; a.hpos_out = hnxt; a.s = w.s; a.Mq = w.Mq; a.Mk = w.Mk; a.Mpk = w.Mpk;
       a.dir_prev = (level & 1) ? w.dirA : w.dirB;
       a.dir_cur = (level & 1) ? w.dirB : w.dirA;
-      a.nchunks = (N + ct - 1) / ct;
+      a.nchunks = nch_all;
+      a.node_slots = node_slots;
       a.sample_buf = w.sample; a.chunk_cnt = w.chunk_cnt; a.zbuf_tok = w.stok;
       a.zbuf = w.zbuf; a.keys = w.keys; a.wide = w.wide;
       a.trace_score = o.trace_score ? o.trace_score + level * TN : nullptr;
       a.trace_slots = L > 0 ? (1 << (L - 1)) : 1;
       a.trace_dir = o.trace_dir ? o.trace_dir + (size_t)level * 2 * BH * a.trace_slots * D : nullptr;
-      launch_level(a, st);
+      launch_level(a, rs);
       int32_t* t = cur; cur = nxt; nxt = t;
       uint64_t* th = hcur; hcur = hnxt; hnxt = th;
     }
@@ -307,16 +343,22 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     fin = cur;
     return 0;
   };
+  // query trees on the caller's stream, beside them the key trees (of the
+  // first head of each group when the key clustering is shared) on the side
+  // stream; the two touch disjoint rows of every per-tree buffer
   int32_t *fin_q = nullptr, *fin_k = nullptr;
-  if (ck == c && kshare == 1) {
-    if (int e = run_levels(c, 1, 0, fin_q)) return e;
-    fin_k = fin_q;
-  } else {
-    // query trees, then the key trees (of the first head of each group when
-    // the key clustering is shared)
-    if (int e = run_levels(c, 2, 0, fin_q)) return e;
-    if (int e = run_levels(ck, 2 * kshare, 1, fin_k)) return e;
-  }
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  if (int e = side_stream(&side, &ev_fork, &ev_join)) return e;
+  CA_HIP_CHECK(hipEventRecord(ev_fork, st));
+  CA_HIP_CHECK(hipStreamWaitEvent(side, ev_fork, 0));
+  const int eq = run_levels(c, 2, 0, fin_q, st);
+  const int ek = run_levels(ck, 2 * kshare, 1, fin_k, side);
+  // join even after a failed enqueue, so the side stream never runs ahead
+  CA_HIP_CHECK(hipEventRecord(ev_join, side));
+  CA_HIP_CHECK(hipStreamWaitEvent(st, ev_join, 0));
+  if (eq) return eq;
+  if (ek) return ek;
   launch_perm_out(fin_q, fin_k, BH, N, kshare, perm_q, perm_k, st);
   launch_centroids(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, c, ck, perm_q, perm_k, cent_q, cent_k,
                    counts, kvg, st);

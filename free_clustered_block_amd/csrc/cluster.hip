@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void pddp_dir(LevelArgs a) {
     const float nr = sqrtf(block_sum(r * r));
     float rh = r / nr;
     if (a.level > 0) {
-      const float* par = a.dir_prev + ((int64_t)tree * (1 << (a.level - 1)) + (slot >> 1)) * D;
+      const float* par = a.dir_prev + ((int64_t)tree * a.node_slots + (slot >> 1)) * D;
       const float sv = tid < D ? par[tid] + rh : 0.0f;
       const float ns = sqrtf(block_sum(sv * sv));
       if (ns > 0.0f) rh = sv / ns;
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void pddp_dir(LevelArgs a) {
     __syncthreads();
   }
   __syncthreads();
-  float* out = a.dir_cur + ((int64_t)tree * (1 << a.level) + slot) * D;
+  float* out = a.dir_cur + ((int64_t)tree * a.node_slots + slot) * D;
   if (tid < D) {
     const float v = fallback ? su0[tid] : su[tid];
     out[tid] = v;
@@ -471,11 +471,11 @@ __global__ __launch_bounds__(256) void pddp_dir_y(LevelArgs a) {
     for (int j = 1; j < D; ++j)
       if (sp1[j] > best) { best = sp1[j]; jb = j; }
     sred[0] = jb;
-    a.jsel[(int64_t)tree * (1 << a.level) + slot] = jb;
+    a.jsel[(int64_t)tree * a.node_slots + slot] = jb;
   }
   __syncthreads();
   const int jb = sred[0];
-  float* out = a.dir_cur + ((int64_t)tree * (1 << a.level) + slot) * D;
+  float* out = a.dir_cur + ((int64_t)tree * a.node_slots + slot) * D;
   if (tid < D) {
     const float v = a.basis[((int64_t)tree * D + jb) * D + tid];
     out[tid] = v;
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(256) void pddp_project_y(LevelArgs a) {
   int off, n, idx;
   const int depth = node_of(a.N, a.c, a.level, p0, &off, &n, &idx);
   if (depth < a.level || n <= a.c) return;   // inside a leaf
-  const int j = a.jsel[(int64_t)tree * (1 << a.level) + idx];
+  const int j = a.jsel[(int64_t)tree * a.node_slots + idx];
   const int p = p0 + (int)threadIdx.x;
   if (p >= min(a.N, p0 + a.c)) return;
   const int tok = a.perm_in[(int64_t)tree * a.N + p];
@@ -600,7 +600,7 @@ void pddp_dir_mma(LevelArgs a) {
   float rj = 0.0f, pj = 0.0f;
   if (tid < D) {
     if (a.level > 0)
-      pj = a.dir_prev[((int64_t)tree * (1 << (a.level - 1)) + (slot >> 1)) * D + tid];
+      pj = a.dir_prev[((int64_t)tree * a.node_slots + (slot >> 1)) * D + tid];
     uint64_t base = 0;
     base = chain_step(base, a.seed);
     base = chain_step(base, kDomainWarm);
@@ -915,7 +915,7 @@ void pddp_dir_mma(LevelArgs a) {
     if (l == 0) nred[it & 1][w] = sq;
     __syncthreads();
   }
-  float* out = a.dir_cur + ((int64_t)tree * (1 << a.level) + slot) * D;
+  float* out = a.dir_cur + ((int64_t)tree * a.node_slots + slot) * D;
   if (tid < D) {
     const float v = fallback ? su0[tid] : vbuf[last][tid] * inv_norm;
     out[tid] = v;
@@ -948,7 +948,7 @@ __global__ __launch_bounds__(256) void pddp_project(LevelArgs a) {
   if (depth < a.level || n <= a.c) return;   // inside a leaf
 
   const int tid = threadIdx.x, q = tid & (LPR - 1);
-  const float* u = a.dir_cur + ((int64_t)tree * (1 << a.level) + idx) * D + q * EPL;
+  const float* u = a.dir_cur + ((int64_t)tree * a.node_slots + idx) * D + q * EPL;
   float ur[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) ur[e] = u[e];
@@ -1256,7 +1256,7 @@ CA_DEV int32_t* wide_state(const LevelArgs& a, int tree, int slot) {
 }
 CA_DEV int32_t* wide_counts(const LevelArgs& a, int tree, int slot, int chunk) {
   return a.wide + (int64_t)2 * a.BH * kWideSlots * kWideState +
-         (((int64_t)tree * kWideSlots + slot) * a.wide_cpn + chunk) * 2;
+         (((int64_t)tree * kWideSlots + slot) * ((a.N + kWideChunk - 1) / kWideChunk) + chunk) * 2;
 }
 
 // grid (slots * cpn, trees): per chunk of a splitting node, min and max key
@@ -1671,8 +1671,10 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
       if ((l.tree_base & 1) == 0) pddp_dir_mma<D, 0><<<g, DirMma<D>::NT, lds, st>>>(l);
       else pddp_dir_mma<D, 1><<<g, DirMma<D>::NT, lds, st>>>(l);
     };
-    const bool many = (int64_t)trees << a.level >= kDirSplitNodes;
-    if (!many && la.tree_step % 2 == 1) {
+    // (a launch of one tensor's trees counts its nodes double: the other
+    // tensor's level runs beside it on the other stream)
+    const bool many = ((int64_t)trees << a.level) * (la.tree_step % 2 == 0 ? 2 : 1) >= kDirSplitNodes;
+    if (!many) {
       pddp_dir_mma<D, -1><<<gslots, DirMma<D>::NT, lds, st>>>(la);
     } else if (la.tree_step % 2 == 0) {
       dir_launch(la);

@@ -37,9 +37,12 @@ struct LevelArgs {
                             // keys) packed in the per-lane order of the direction kernel
   const float* basis;       // [2 BH][D][D]: row j = basis direction a_j (diagonalized)
   const float* Y;           // [2 BH][N][D]: coordinates x . a_j of every token (diagonalized)
-  int32_t* jsel;            // [2 BH][slots]: chosen coordinate of each node (diagonalized)
-  const float* dir_prev;    // [2 BH][slots/2][D]
-  float* dir_cur;           // [2 BH][slots][D]
+  int32_t* jsel;            // [2 BH][node_slots]: chosen coordinate of each node (diagonalized)
+  const float* dir_prev;    // [2 BH][node_slots][D], slots of the previous level
+  float* dir_cur;           // [2 BH][node_slots][D]
+  int node_slots;           // per-tree row stride of jsel and the direction arrays: the
+                            // deepest level's slot count, the same at every level so that
+                            // trees at different levels (two streams) never share a row
   int nchunks;              // ceil(N / c)
   int sample_inline;        // set by launch_level: the direction kernel draws the subsample itself
   int split_cache;          // set by launch_level: keys a split workgroup keeps in LDS

@@ -18,12 +18,13 @@
  *  - Every pointer argument is a device pointer owned by the caller unless it
  *    is documented as a host pointer. The library never allocates device or
  *    host memory, never frees caller memory and keeps no state between calls
- *    except a thread-local error string, with three stated exceptions: the
+ *    except a thread-local error string, with four stated exceptions: the
  *    per-thread profiling events of ca_profile_events (a timing hook outside
  *    the computation, off unless set), the scratch array of ca_route_noalloc
- *    (one per GPU, for callers that cannot allocate), and a once-per-process,
+ *    (one per GPU, for callers that cannot allocate), a once-per-process,
  *    thread-safe raise of some kernels' dynamic LDS limit at their first
- *    launch.
+ *    launch, and the side stream of ca_cluster (one per GPU, with one pair of
+ *    fork/join events per host thread and GPU, created at first use).
  *  - Scratch memory is passed in as `ws` (device, 256-byte aligned) of
  *    `ws_bytes` bytes; ca_workspace_size() gives the bytes a call needs.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
@@ -191,6 +192,16 @@ size_t ca_workspace_size(ca_op op, int B, int H, int N, int D, int cluster_size,
  * counts    out int32 [B,H,n_kc] or NULL: n_j of the key clusters.
  * ws        workspace of ca_workspace_size(CA_OP_CLUSTER (CA_OP_CLUSTER_DIAG
  *           for split_mode 1), B, H, N, D, min(c_q, c_k), 0).
+ * stream    the query trees' split levels run on `stream`; the key trees'
+ *           run beside them on a library-owned side stream of the current
+ *           GPU (non-blocking, default priority), which waits for `stream`
+ *           at the call's start (an event) and which `stream` waits for
+ *           before the centroids (another event). The call is therefore
+ *           ordered on `stream` as a whole, and a HIP graph captured on
+ *           `stream` holds both branches. Calls from several host threads
+ *           share the side stream (correct, but they serialise there); a
+ *           capture on one thread must not overlap a ca_cluster call of
+ *           another thread on the same GPU.
  */
 int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, int D,
                int cluster_size, const ca_cluster_opts* opts, int32_t* perm_q,
