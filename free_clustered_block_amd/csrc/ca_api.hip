@@ -167,9 +167,10 @@ int check_common(int dt, int B, int H, int N, int D, bool fp8_ok = false) {
 
 // The key trees' split levels run on a side stream beside the query trees':
 // at the top levels every direction and split launch is latency-bound and
-// fills few CUs, so each tensor's launches overlap the other's projection.
-// The side stream is forked from the caller's stream and joined back to it
-// by events, so the call stays ordered on the caller's stream (and a graph
+// fills few CUs, so each tensor's launches overlap the other's projection
+// (splitting each tensor's trees over more streams measured no faster). The
+// side stream is forked from the caller's stream and joined back to it by
+// events, so the call stays ordered on the caller's stream (and a graph
 // captured there takes both branches). One side stream per GPU (non-blocking,
 // default priority) and one event pair per host thread and GPU, each created
 // at its first use and kept until the process ends.
@@ -278,10 +279,17 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t TN = 2 * (size_t)BH * N;
 
-  launch_metric(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, o.transform, o.query_normalize, w.partial,
-                w.hash, w.Mq, w.Mk, w.kbar, w.gsplit, w.s, w.Mpk, kvg, st);
+  const int dti = dt == CA_BF16 ? 0 : 1;
+  launch_metric(Q, K, dti, BH, N, D, o.transform, w.partial, w.hash, w.Mq, w.Mk, w.kbar, w.gsplit,
+                w.Mpk, kvg, st);
   if (kshare > 1) launch_pool_key_metric(w.Mq, w.Mpk, BH, D, kshare, st);
+  // the query normalisers: before the basis (which weights the queries by
+  // them), else on the query trees' stream only (the key trees do not read them)
+  auto qnorm = [&] {
+    launch_qnorm(Q, dti, BH, N, D, o.transform, o.query_normalize, w.gsplit, w.Mk, w.s, st);
+  };
   if (o.split_mode == 1) {
+    qnorm();
     launch_basis(Q, dt == CA_BF16 ? 0 : 1, BH, N, D, o.transform, w.s, w.Mq, w.Mk, w.partial, w.Cq,
                  w.Rbuf, w.Zbuf, w.At, st);
     if (o.trace_basis)
@@ -290,9 +298,9 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     launch_rotate(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, w.s, w.At, w.At3, w.Y, kvg, st);
   }
   launch_perm_init(w.permA, 2 * BH, N, st);
-  // the split levels of a set of trees (every tree when c_q == c_k, else one
-  // tensor's trees at a time with its own cluster size); returns the
-  // permutation array that holds their final order in `fin`
+  // the split levels of one tensor's trees (rows base, base + step, ...) with
+  // cluster size ct, enqueued on stream rs; returns the permutation array
+  // that holds their final order in `fin`
   // per-tree row strides of the level buffers, the same for every level and
   // both tensors (the workspace's sizes, from the smaller cluster size)
   const int cmin = c < ck ? c : ck;
@@ -343,25 +351,37 @@ int ca_cluster(const void* Q, const void* K, ca_dtype dt, int B, int H, int N, i
     fin = cur;
     return 0;
   };
-  // query trees on the caller's stream, beside them the key trees (of the
+  // query trees on the caller's stream; beside them the key trees (of the
   // first head of each group when the key clustering is shared) on the side
-  // stream; the two touch disjoint rows of every per-tree buffer
-  int32_t *fin_q = nullptr, *fin_k = nullptr;
+  // stream. The two touch disjoint rows of every per-tree buffer; each ends
+  // with its own permutation output and centroids.
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   if (int e = side_stream(&side, &ev_fork, &ev_join)) return e;
   CA_HIP_CHECK(hipEventRecord(ev_fork, st));
   CA_HIP_CHECK(hipStreamWaitEvent(side, ev_fork, 0));
-  const int eq = run_levels(c, 2, 0, fin_q, st);
-  const int ek = run_levels(ck, 2 * kshare, 1, fin_k, side);
+  int32_t *fin_q = nullptr, *fin_k = nullptr;
+  int err = 0;
+  if (o.split_mode == 0) qnorm();
+  if (int e = run_levels(c, 2, 0, fin_q, st)) {
+    err = e;
+  } else {
+    launch_perm_out(fin_q, 0, BH, N, kshare, perm_q, st);
+    launch_centroids(Q, K, dti, BH, N, D, c, ck, perm_q, perm_k, cent_q, cent_k, counts, kvg, 0, 1, st);
+  }
+  if (!err) {
+    if (int e = run_levels(ck, 2 * kshare, 1, fin_k, side)) {
+      err = e;
+    } else {
+      launch_perm_out(fin_k, 1, BH, N, kshare, perm_k, side);
+      launch_centroids(Q, K, dti, BH, N, D, c, ck, perm_q, perm_k, cent_q, cent_k, counts, kvg, 1, 1,
+                       side);
+    }
+  }
   // join even after a failed enqueue, so the side stream never runs ahead
   CA_HIP_CHECK(hipEventRecord(ev_join, side));
   CA_HIP_CHECK(hipStreamWaitEvent(st, ev_join, 0));
-  if (eq) return eq;
-  if (ek) return ek;
-  launch_perm_out(fin_q, fin_k, BH, N, kshare, perm_q, perm_k, st);
-  launch_centroids(Q, K, dt == CA_BF16 ? 0 : 1, BH, N, D, c, ck, perm_q, perm_k, cent_q, cent_k,
-                   counts, kvg, st);
+  if (err) return err;
   return after_launch();
 }
 

@@ -1560,13 +1560,13 @@ __global__ void perm_init(int32_t* perm, int trees, int N) {
   if (i < (int64_t)trees * N) perm[i] = (int32_t)(i % N);
 }
 
-__global__ void perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N, int kshare,
-                         int32_t* pq, int32_t* pk) {
+__global__ void perm_out(const int32_t* perm_t, int tensor, int BH, int N, int kshare,
+                         int32_t* perm) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)BH * N) return;
   const int64_t bh = i / N, p = i % N;
-  pq[i] = perm_qt[(2 * bh) * N + p];
-  pk[i] = perm_kt[(2 * (bh - bh % kshare) + 1) * N + p];   // the group's first head's key tree
+  if (tensor == 0) perm[i] = perm_t[(2 * bh) * N + p];
+  else perm[i] = perm_t[(2 * (bh - bh % kshare) + 1) * N + p];   // the group's first head's key tree
 }
 
 // Means of the original rows of every cluster. Thread (row slot, group g)
@@ -1579,13 +1579,14 @@ __global__ __launch_bounds__(256) void centroids_kernel(const T* __restrict__ Q,
                                                         const int32_t* __restrict__ pk,
                                                         float* __restrict__ cq,
                                                         float* __restrict__ ck,
-                                                        int32_t* __restrict__ counts, int kvg) {
+                                                        int32_t* __restrict__ counts, int kvg,
+                                                        int t0) {
   constexpr int EPG = 16 / (int)sizeof(T);   // elements per 16-byte group
   constexpr int NG = D / EPG;                // groups per row
   constexpr int S = 256 / NG;                // row slots
   __shared__ float part[S][D + 1];
   __shared__ int stoks[256];
-  const int j = blockIdx.x, bh = blockIdx.y, tensor = blockIdx.z;
+  const int j = blockIdx.x, bh = blockIdx.y, tensor = (int)blockIdx.z + t0;
   const int c = tensor == 0 ? c_q : c_k;
   const int nc = (N + c - 1) / c;
   if (j >= nc) return;
@@ -1633,10 +1634,10 @@ void launch_perm_init(int32_t* perm, int trees, int N, hipStream_t st) {
   perm_init<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm, trees, N);
 }
 
-void launch_perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N, int kshare,
-                     int32_t* pq, int32_t* pk, hipStream_t st) {
+void launch_perm_out(const int32_t* perm_t, int tensor, int BH, int N, int kshare, int32_t* perm,
+                     hipStream_t st) {
   const int64_t n = (int64_t)BH * N;
-  perm_out<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm_qt, perm_kt, BH, N, kshare, pq, pk);
+  perm_out<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm_t, tensor, BH, N, kshare, perm);
 }
 
 constexpr int64_t kDirSplitNodes = 2048;   // node slots of a level from which tensors launch apart
@@ -1671,9 +1672,9 @@ static void level_impl(const LevelArgs& a, hipStream_t st) {
       if ((l.tree_base & 1) == 0) pddp_dir_mma<D, 0><<<g, DirMma<D>::NT, lds, st>>>(l);
       else pddp_dir_mma<D, 1><<<g, DirMma<D>::NT, lds, st>>>(l);
     };
-    // (a launch of one tensor's trees counts its nodes double: the other
-    // tensor's level runs beside it on the other stream)
-    const bool many = ((int64_t)trees << a.level) * (la.tree_step % 2 == 0 ? 2 : 1) >= kDirSplitNodes;
+    // (counted over every tree of both tensors: the other trees' levels run
+    // beside this launch on the other streams)
+    const bool many = ((int64_t)2 * a.BH << a.level) >= kDirSplitNodes;
     if (!many) {
       pddp_dir_mma<D, -1><<<gslots, DirMma<D>::NT, lds, st>>>(la);
     } else if (la.tree_step % 2 == 0) {
@@ -1759,19 +1760,19 @@ void launch_level(const LevelArgs& a, hipStream_t st) {
 
 void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, int D, int c_q,
                       int c_k, const int32_t* pq, const int32_t* pk, float* cq, float* ck,
-                      int32_t* counts, int kvg, hipStream_t st) {
+                      int32_t* counts, int kvg, int t0, int nt, hipStream_t st) {
   const int cmin = c_q < c_k ? c_q : c_k;
-  dim3 g((N + cmin - 1) / cmin, BH, 2);
+  dim3 g((N + cmin - 1) / cmin, BH, nt);
   if (dtype == 0) {
     const uint16_t* q = (const uint16_t*)Q;
     const uint16_t* k = (const uint16_t*)K;
-    if (D == 64) centroids_kernel<uint16_t, 64><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg);
-    else centroids_kernel<uint16_t, 128><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg);
+    if (D == 64) centroids_kernel<uint16_t, 64><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg, t0);
+    else centroids_kernel<uint16_t, 128><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg, t0);
   } else {
     const float* q = (const float*)Q;
     const float* k = (const float*)K;
-    if (D == 64) centroids_kernel<float, 64><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg);
-    else centroids_kernel<float, 128><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg);
+    if (D == 64) centroids_kernel<float, 64><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg, t0);
+    else centroids_kernel<float, 128><<<g, 256, 0, st>>>(q, k, N, c_q, c_k, pq, pk, cq, ck, counts, kvg, t0);
   }
 }
 

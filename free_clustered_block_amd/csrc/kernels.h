@@ -8,9 +8,14 @@ namespace ca {
 // metric.hip -----------------------------------------------------------------
 int metric_rows_per_chunk(int N, int BH);
 // dtype: 0 = bf16, 1 = fp32. partial: [BH][nchunks][2 D D + D] fp32 scratch.
+// M_q, M_k, kbar, the query geometry's bf16 split and the row hashes
 void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D, int transform,
-                   int query_normalize, float* partial, uint64_t* hash, float* Mq, float* Mk,
-                   float* kbar, uint16_t* gsplit, float* s, float* Mpk, int kvg, hipStream_t st);
+                   float* partial, uint64_t* hash, float* Mq, float* Mk, float* kbar,
+                   uint16_t* gsplit, float* Mpk, int kvg, hipStream_t st);
+// the query normalisers s [BH][N] (1 without query normalisation), after launch_metric
+void launch_qnorm(const void* Q, int dtype, int BH, int N, int D, int transform,
+                  int query_normalize, const uint16_t* gsplit, const float* Mk, float* s,
+                  hipStream_t st);
 // kvg: query heads per key/value head (1 = multi-head attention); the key
 // rows of query head bh are those of key/value head bh / kvg (every call).
 
@@ -76,17 +81,18 @@ void launch_perm_init(int32_t* perm, int trees, int N, hipStream_t st);
 // perm [2 BH][N] tree order -> perm_q, perm_k [BH][N]; the query trees are
 // read from perm_qt, the key trees from perm_kt
 // (kshare > 1: the key trees of heads bh - bh % kshare serve their whole group)
-void launch_perm_out(const int32_t* perm_qt, const int32_t* perm_kt, int BH, int N, int kshare,
-                     int32_t* perm_q, int32_t* perm_k, hipStream_t st);
+// (tensor 0: perm_q from the query trees, 1: perm_k from the key trees)
+void launch_perm_out(const int32_t* perm_t, int tensor, int BH, int N, int kshare, int32_t* perm,
+                     hipStream_t st);
 // Shared key clustering of groups of g query heads: the key-tree metric of
 // the group's first head (Mq and its packed copy in Mpk) becomes the mean of
 // the group's query metrics.
 void launch_pool_key_metric(float* Mq, float* Mpk, int BH, int D, int g, hipStream_t st);
 // centroids of query clusters of size c_q and key clusters of size c_k;
-// counts (optional) = key cluster sizes
+// counts (optional) = key cluster sizes; tensors t0 .. t0 + nt - 1 (0 = queries, 1 = keys)
 void launch_centroids(const void* Q, const void* K, int dtype, int BH, int N, int D, int c_q,
                       int c_k, const int32_t* perm_q, const int32_t* perm_k, float* cent_q,
-                      float* cent_k, int32_t* counts, int kvg, hipStream_t st);
+                      float* cent_k, int32_t* counts, int kvg, int t0, int nt, hipStream_t st);
 
 // route.hip ------------------------------------------------------------------
 void launch_route(const float* cq, const float* ck, int BH, int nq, int nk, int D, int topk,

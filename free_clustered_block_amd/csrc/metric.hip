@@ -432,8 +432,8 @@ void launch_pool_key_metric(float* Mq, float* Mpk, int BH, int D, int g, hipStre
 }
 
 void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D, int transform,
-                   int query_normalize, float* partial, uint64_t* hash, float* Mq, float* Mk,
-                   float* kbar, uint16_t* gsplit, float* s, float* Mpk, int kvg, hipStream_t st) {
+                   float* partial, uint64_t* hash, float* Mq, float* Mk, float* kbar,
+                   uint16_t* gsplit, float* Mpk, int kvg, hipStream_t st) {
   const int rows = metric_rows_per_chunk(N, BH);
   const int nchunks = (N + rows - 1) / rows;
   dim3 gp(nchunks, BH);
@@ -452,6 +452,11 @@ void launch_metric(const void* Q, const void* K, int dtype, int BH, int N, int D
   dim3 gr((D * D + 255) / 256, BH);
   if (D == 64) metric_reduce<64><<<gr, 256, 0, st>>>(partial, nchunks, N, transform, Mq, Mk, kbar, gsplit, Mpk);
   else metric_reduce<128><<<gr, 256, 0, st>>>(partial, nchunks, N, transform, Mq, Mk, kbar, gsplit, Mpk);
+}
+
+void launch_qnorm(const void* Q, int dtype, int BH, int N, int D, int transform,
+                  int query_normalize, const uint16_t* gsplit, const float* Mk, float* s,
+                  hipStream_t st) {
   if (!query_normalize) {
     int64_t n = (int64_t)BH * N;
     fill_f32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(s, n, 1.0f);
