@@ -268,18 +268,57 @@ int qnorm_span(int N, int BH) {
   return (span + 31) / 32 * 32;
 }
 
-// s_i = (q_i^T G q_i)^{-1/2} (0 if q^T G q <= 0). Y^T = G Q^T on the matrix
-// cores with G as hi + mid + lo bf16 terms held as A operands for the block's
-// lifetime; query tiles stream through LDS (double-buffered) as B operands,
-// then t_i = sum_n Y^T[n][i] q_i[n] from the accumulator rows. Wave w computes
-// rows [32 (w % NB), +32) of Y^T for query group w / NB of each tile.
+// Upper block triangle of the symmetric query geometry G, in 16-wide k-steps
+// of 32-row blocks: q^T G q = sum_I q_I^T (G_II q_I + sum_{J > I} 2 G_IJ q_J),
+// so block row I covers k-steps [2 I, D / 16), and the blocks right of the
+// diagonal enter doubled (exact in bf16). The k-steps are dealt to the waves
+// of a query group in at most two segments (block row, first, end) each, the
+// same number of k-steps per wave: at D = 128, 20 k-steps over 4 waves
+// (10 of the 16 blocks), at D = 64, 6 over 2 waves.
+struct QnSeg {
+  int row, s0, s1;
+};
+template <int D>
+struct QnPlan;
+template <>
+struct QnPlan<128> {
+  static constexpr int KMAX = 5;
+  static constexpr QnSeg seg[4][2] = {{{0, 0, 5}, {0, 0, 0}},
+                                      {{0, 5, 8}, {3, 6, 8}},
+                                      {{1, 2, 7}, {1, 0, 0}},
+                                      {{1, 7, 8}, {2, 4, 8}}};
+};
+template <>
+struct QnPlan<64> {
+  static constexpr int KMAX = 3;
+  static constexpr QnSeg seg[2][2] = {{{0, 0, 3}, {0, 0, 0}}, {{0, 3, 4}, {1, 2, 4}}};
+};
+
+CA_DEV bf16x8_t bf16x8_times2(const bf16x8_t& v) {
+  const u32x4_t u = __builtin_bit_cast(u32x4_t, v);
+  u32x4_t o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = f32_to_bf16(2.0f * bf16_to_f32((uint16_t)(u[k] & 0xFFFFu)));
+    const uint32_t hi = f32_to_bf16(2.0f * bf16_to_f32((uint16_t)(u[k] >> 16)));
+    o[k] = lo | (hi << 16);
+  }
+  return as_bf16x8(o);
+}
+
+// s_i = (q_i^T G q_i)^{-1/2} (0 if q^T G q <= 0). The products run on the
+// matrix cores with G as hi + mid + lo bf16 terms held as A operands for the
+// block's lifetime (the wave's k-steps of the upper block triangle, see
+// QnPlan); query tiles stream through LDS (double-buffered) as B operands,
+// then each wave dots its accumulator rows with the query and the waves'
+// partial sums are added in wave order.
 template <int D>
 __global__ __launch_bounds__(256) void qnorm_bf16(const uint16_t* __restrict__ Q, int N, int span,
                                                   const uint16_t* __restrict__ gsplit,
                                                   float* __restrict__ s_out) {
-  constexpr int NB = D / 32;                 // 32-row blocks of Y^T
+  constexpr int NB = D / 32;                 // waves per query group
   constexpr int QG = 4 / NB;                 // query groups of 32 per tile
-  constexpr int KS = D / 16;                 // MFMA k-steps
+  constexpr int KMAX = QnPlan<D>::KMAX;
   constexpr int QP = D + 8;                  // padded query row (bf16)
   constexpr int TILE = 32 * QG;              // queries per step
   constexpr int PPT = TILE * D / 8 / 256;    // 16-byte pieces per thread per tile
@@ -313,38 +352,59 @@ __global__ __launch_bounds__(256) void qnorm_bf16(const uint16_t* __restrict__ Q
   };
   load_tile(st[0], q0);
   if (q0 + TILE < qend) load_tile(st[1], q0 + TILE);
-  // A operands: rows [32 bn, 32 bn + 32) of the three parts of G
-  bf16x8_t ga[3][KS];
+  // A operands of the wave's k-steps, in segment order: rows [32 row, +32)
+  // of the three parts of G, doubled right of the diagonal block
+  const QnSeg sg0 = QnPlan<D>::seg[bn][0], sg1 = QnPlan<D>::seg[bn][1];
+  const int n0 = sg0.s1 - sg0.s0, n1 = sg1.s1 - sg1.s0;
+  bf16x8_t ga[3][KMAX];
 #pragma unroll
-  for (int p = 0; p < 3; ++p)
+  for (int k = 0; k < KMAX; ++k) {
+    const bool first = k < n0;
+    const int row = first ? sg0.row : sg1.row;
+    const int sk = first ? sg0.s0 + k : sg1.s0 + (k - n0);
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      ga[p][s] = *reinterpret_cast<const bf16x8_t*>(G + (int64_t)p * D * D +
-                                                    (int64_t)(32 * bn + r) * D + 16 * s + 8 * h);
+    for (int p = 0; p < 3; ++p) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(G + (int64_t)p * D * D +
+                                                      (int64_t)(32 * row + r) * D + 16 * sk + 8 * h);
+      if ((sk >> 1) > row) v = bf16x8_times2(v);
+      ga[p][k] = v;
+    }
+  }
   store_tile(st[0], 0);
   if (q0 + 2 * TILE < qend) load_tile(st[0], q0 + 2 * TILE);
   __syncthreads();
-  // one tile: Y^T block on the matrix cores, t_i, then the next tile's store
+  // one tile: the wave's segments on the matrix cores, its partial
+  // sum_I q_I^T y_I, then the next tile's store
   auto step = [&](int t0, auto parity) __attribute__((always_inline)) {
     constexpr int buf = decltype(parity)::value;
-    floatx16_t y = zero16();
     const uint16_t* qrow = &sq[buf][32 * qg + r][0];
+    // lane (r, h) holds y[32 row + c_row(i, h)][query r] of a segment
+    auto dot = [&](const floatx16_t& y, int row, float tp) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8_t bq = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s + 8 * h);
-#pragma unroll
-      for (int p = 0; p < 3; ++p) y = mfma32(ga[p][s], bq, y);
-    }
-    // lane (r, h) holds Y^T[32 bn + c_row(i, h)][query r]
+      for (int jq = 0; jq < 4; ++jq) {
+        const u32x2_t qv = *reinterpret_cast<const u32x2_t*>(qrow + 32 * row + 8 * jq + 4 * h);
+        tp = fmaf(y[4 * jq + 0], bf16_to_f32((uint16_t)(qv.x & 0xFFFFu)), tp);
+        tp = fmaf(y[4 * jq + 1], bf16_to_f32((uint16_t)(qv.x >> 16)), tp);
+        tp = fmaf(y[4 * jq + 2], bf16_to_f32((uint16_t)(qv.y & 0xFFFFu)), tp);
+        tp = fmaf(y[4 * jq + 3], bf16_to_f32((uint16_t)(qv.y >> 16)), tp);
+      }
+      return tp;
+    };
+    // the segments one after the other through one accumulator
     float tp = 0.0f;
+    floatx16_t y = zero16();
 #pragma unroll
-    for (int jq = 0; jq < 4; ++jq) {
-      const u32x2_t qv = *reinterpret_cast<const u32x2_t*>(qrow + 32 * bn + 8 * jq + 4 * h);
-      tp = fmaf(y[4 * jq + 0], bf16_to_f32((uint16_t)(qv.x & 0xFFFFu)), tp);
-      tp = fmaf(y[4 * jq + 1], bf16_to_f32((uint16_t)(qv.x >> 16)), tp);
-      tp = fmaf(y[4 * jq + 2], bf16_to_f32((uint16_t)(qv.y & 0xFFFFu)), tp);
-      tp = fmaf(y[4 * jq + 3], bf16_to_f32((uint16_t)(qv.y >> 16)), tp);
+    for (int k = 0; k < KMAX; ++k) {
+      if (k == n0) {   // the first segment is complete
+        tp = dot(y, sg0.row, tp);
+        y = zero16();
+      }
+      const int sk = k < n0 ? sg0.s0 + k : sg1.s0 + (k - n0);
+      const bf16x8_t bq = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * sk + 8 * h);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) y = mfma32(ga[p][k], bq, y);
     }
+    tp = dot(y, n1 > 0 ? sg1.row : sg0.row, tp);
     tp = sum_halves(tp);
     if (h == 0) tred[buf][bn][32 * qg + r] = tp;
     // tile t + 1 (staged in slot buf ^ 1) into the other LDS buffer, and
