@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/ca.h: argument validation,
 // workspace layout and launch sequencing. No call allocates memory or
-// synchronises with the device.
+// synchronises with the device; ca_cluster creates its side stream (one per
+// GPU) and its fork/join events (per host thread and GPU) once, at first use.
 #include <cmath>
 #include <mutex>
 #include <string>
